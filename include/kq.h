@@ -1,0 +1,210 @@
+/*
+ * kq.h -- C ABI of libkq, an INT8 quantized linear layer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * What the library computes (one linear layer, y = x W^T + bias, with both
+ * operands quantized):
+ *   - activations x (bf16, [M,K], one row per token) are quantized per token
+ *     to int8 with an fp32 scale, inside the linear call;
+ *   - weights W ([N,K], one row per output channel) are quantized offline,
+ *     either to int8 with one fp32 scale per output channel, or to packed
+ *     unsigned int4 with an fp16 scale and an fp16 offset per group of 64
+ *     consecutive K;
+ *   - an INT8 x INT8 -> INT32 matrix product runs on the MFMA units, and the
+ *     dequantization (token scale x channel or group scale) and the bias add
+ *     are fused into the same kernel's epilogue.
+ *
+ * Sources of the method (the pages are cited by title and section):
+ *   [qlip]   "qlip-mlx" README (TheStageAI), the w8a8_linear / w4a8_linear
+ *            feature bullets and "Quick start": W8A8 GEMM with per-token
+ *            activation quantization inside the kernel, INT8xINT8->INT32
+ *            matmul, dequant+bias fused into one node; quantize_weight_int8
+ *            maps [N,K] fp weights to int8 plus fp32 scales; W4A8 keeps the
+ *            same INT8 compute with weights stored as packed int4; calls with
+ *            M <= 16 take a register-dequant GEMV.
+ *   [mlx4722] MLX pull request 4722 (staged int8 affine quantized matmul),
+ *            "Selector rules": affine weights, 2-D transposed [N,K] weight
+ *            layout, K % 64 == 0, K/64 <= 1024, non-batched operands, group
+ *            sizes 32/64/128 (this library: 64).
+ *   [kquant] mlx-kquant pull request 89 commit list: routes must not round
+ *            beyond one weight and one output rounding; errors other than a
+ *            declined route raise; the route decision is one tested function.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensors are dense, row-major, non-batched (callers flatten [B,L,K]
+ *     to [M,K]).  Device pointers must be 16-byte aligned.
+ *   - "device" pointers are HIP device allocations on the current device;
+ *     "host" pointers are ordinary process memory.
+ *   - The caller owns every buffer, the workspace included.  The library
+ *     allocates no memory, keeps no pointer after a call returns, and never
+ *     synchronizes: work is enqueued on `stream` (a hipStream_t; NULL means
+ *     the null stream) and buffers must stay alive until it completes.
+ *   - Every call returns a kq_status.  On failure nothing is enqueued (except
+ *     KQ_ERR_LAUNCH) and kq_last_error() returns a message of the form
+ *     "[kq_w4a8_linear] K=100 must be a multiple of 64".  No C++ exception
+ *     and no abort crosses the ABI.
+ *   - Shapes with M == 0 or N == 0 are valid and enqueue nothing.
+ *   - Inputs must be finite.  Weights must satisfy |w| < 65504 for the int4
+ *     format (its scale and offset are fp16).
+ */
+#ifndef KQ_H
+#define KQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kq_status {
+    KQ_SUCCESS = 0,
+    KQ_ERR_INVALID_VALUE = 1, /* null pointer, negative size, misalignment */
+    KQ_ERR_UNSUPPORTED = 2,   /* valid request outside the supported envelope */
+    KQ_ERR_NO_DEVICE = 3,     /* no gfx950 device current */
+    KQ_ERR_WORKSPACE = 4,     /* workspace missing or smaller than required */
+    KQ_ERR_LAUNCH = 5         /* the HIP runtime rejected a kernel launch */
+} kq_status;
+
+typedef enum kq_wformat {
+    /* int8 codes [N,K], fp32 scale [N]; w ~= scale[n] * q[n,k]. */
+    KQ_W8_PER_CHANNEL = 0,
+    /* uint8 [N,K/2] with two 4-bit codes per byte (low nibble = even k),
+     * fp16 scale [N,K/64] and fp16 offset [N,K/64];
+     * w ~= scale[n,g] * q[n,k] + offset[n,g] with g = k / 64, q in [0,15]. */
+    KQ_W4_AFFINE_G64 = 1
+} kq_wformat;
+
+typedef enum kq_dtype {
+    KQ_DTYPE_F32 = 0,  /* fp32 output, rounded once from the exact result */
+    KQ_DTYPE_BF16 = 1, /* bf16 output: the fp32 result rounded to nearest even */
+    /* Debug output of the integer accumulators.  W8A8: int32 [M,N] holding
+     * sum_k a[m,k]*q[n,k].  W4A8 / GEMV: int32 [K/64, M, N] holding, per
+     * 64-wide K group g, P[g,m,n] = sum_{k in g} a[m,k]*q[n,k]. */
+    KQ_DTYPE_I32 = 2
+} kq_dtype;
+
+typedef enum kq_route_kind {
+    KQ_ROUTE_GEMM = 0, /* LDS-tiled MFMA GEMM */
+    KQ_ROUTE_GEMV = 1  /* weight-streaming register-dequant kernel, M <= 16 */
+} kq_route_kind;
+
+/* Launch plan chosen for one linear call (see kq_route). */
+typedef struct kq_route_info {
+    int32_t kind;     /* kq_route_kind */
+    int32_t tile_m;   /* output rows per workgroup */
+    int32_t tile_n;   /* output columns per workgroup */
+    int32_t threads;  /* threads per workgroup */
+    int64_t grid;     /* workgroups in the main kernel */
+} kq_route_info;
+
+/* Largest K the linears accept: 65536 * 127 * 127 < 2^31, so the int32
+ * accumulator cannot overflow ([mlx4722] "Selector rules": K/64 <= 1024). */
+#define KQ_MAX_K 65536
+/* Largest M of the GEMV route ([qlip] W4A8 bullet: M <= 16). */
+#define KQ_GEMV_MAX_M 16
+
+/* 1 if the current HIP device is a gfx950 (MI355X class) GPU, else 0.
+ * [qlip] "Key features": the package is a clean no-op where the INT8 matrix
+ * hardware is missing (is_available() -> False).  Never fails. */
+int kq_is_available(void);
+
+/* Message of the last failed call on this thread ("" if none).  The string
+ * is owned by the library and valid until the next call on this thread. */
+const char* kq_last_error(void);
+
+/* Bytes of device workspace a linear call with this M, K and weight format
+ * needs: int8 activation codes (M*K), fp32 token scales (4*M), and for the
+ * int4 format the per-group code sums (4*M*K/64), each region 256-byte
+ * aligned.  Returns 0 for M == 0.  Pure host function. */
+size_t kq_workspace_bytes(int64_t M, int64_t K, kq_wformat fmt);
+
+/* Launch plan of a linear call; pure host function, no device access.
+ * [kquant]: the route decision is one tested function.  Routing: M <= 16
+ * takes the GEMV unless the environment variable KQ_FORCE_ROUTE=gemm;
+ * KQ_FORCE_ROUTE=gemv forces the GEMV whenever M <= 16 allows it.
+ * Returns KQ_ERR_INVALID_VALUE / KQ_ERR_UNSUPPORTED for shapes the linears
+ * reject, with the same messages. */
+kq_status kq_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
+                   kq_dtype y_dtype, kq_route_info* out /* host */);
+
+/* Offline weight quantization ([qlip] "Quick start": quantize_weight_int8
+ * maps [N,K] weights to int8 plus fp32 scales; [mlx4722]: affine 4-bit
+ * weights with per-group scale and bias, group 64).
+ *   w      device fp32 [N,K]
+ *   KQ_W8_PER_CHANNEL: wq = int8 [N,K]; scale = fp32 [N]; gbias must be NULL.
+ *     Per row n: amax = max_k |w|; if 127/amax overflows (amax == 0 or
+ *     tiny) the row is all zero with scale 0; else inv = fp32(127/amax),
+ *     q = clamp(rint(fp32(w*inv)), -127, 127), scale = fp32(amax/127).
+ *   KQ_W4_AFFINE_G64: wq = uint8 [N,K/2]; scale = fp16 [N,K/64];
+ *     gbias = fp16 [N,K/64]; K % 64 == 0.  Per group: lo = min, hi = max,
+ *     scale = fp16(fp32((hi-lo)/15)), offset = fp16(lo); if scale == 0 the
+ *     codes are 0, else q = clamp(rint(fp32(fp32(w-offset) * fp32(1/scale))),
+ *     0, 15).
+ * Rounding is IEEE round-to-nearest-even throughout; results are bit-exact
+ * and deterministic. */
+kq_status kq_quantize_weights(const float* w, int64_t N, int64_t K,
+                              kq_wformat fmt, void* wq, void* scale,
+                              void* gbias, void* stream);
+
+/* Per-token activation quantization ([qlip] w8a8_linear bullet: activations
+ * quantize dynamically per token; [mlx4722]: the activation-quantize kernel
+ * handles K that is not a multiple of 32).
+ *   x     device bf16 [M,K] (raw bf16 bit patterns), any K >= 1
+ *   a     device int8 [M,K] codes      (output)
+ *   sx    device fp32 [M] token scales (output)
+ *   gsum  device int32 [M,K/64] sums of the codes of each 64-wide K group,
+ *         or NULL; non-NULL requires K % 64 == 0 (output)
+ * Same rule as the int8 weight rows: amax over the row, inv = fp32(127/amax),
+ * codes = clamp(rint(fp32(x*inv)), -127, 127), sx = fp32(amax/127), and an
+ * all-zero row (sx = 0) when 127/amax overflows.  Bit-exact. */
+kq_status kq_quantize_act(const void* x, int64_t M, int64_t K, int8_t* a,
+                          float* sx, int32_t* gsum, void* stream);
+
+/* W8A8 linear ([qlip] w8a8_linear: per-token activation quantization,
+ * INT8xINT8->INT32 matmul, dequant+bias fused).
+ *   x     device bf16 [M,K]
+ *   wq    device int8 [N,K], sw device fp32 [N] (from kq_quantize_weights)
+ *   bias  device fp32 [N] or NULL
+ *   y     device [M,N] of y_dtype:
+ *           F32/BF16: y = sx[m]*sw[n]*acc[m,n] + bias[n], acc = sum_k a*q,
+ *           computed in fp32 and rounded to y_dtype;
+ *           I32: acc itself.
+ *   ws    device workspace of at least kq_workspace_bytes(M,K,KQ_W8_...)
+ * Requires 64 <= K <= KQ_MAX_K and K % 64 == 0.  M <= 16 routes to the GEMV
+ * kernel (see kq_route). */
+kq_status kq_w8a8_linear(const void* x, int64_t M, int64_t K, int64_t N,
+                         const int8_t* wq, const float* sw, const float* bias,
+                         void* y, kq_dtype y_dtype, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* W4A8 linear ([qlip] w4a8_linear: the same INT8 compute with weights
+ * stored as packed int4; [mlx4722]: stage weights and activations as int8
+ * instead of dequantizing).  Arguments as kq_w8a8_linear, with the int4
+ * weights of kq_quantize_weights(KQ_W4_AFFINE_G64):
+ *   wq4   device uint8 [N,K/2]; gscale, gbias device fp16 [N,K/64]
+ *   y (F32/BF16) = sx[m] * sum_g (gscale[n,g]*P[g,m,n] + gbias[n,g]*A[m,g])
+ *                  + bias[n], with P the per-group int8 products and A the
+ *                  per-group code sums; y (I32) = P as int32 [K/64,M,N]. */
+kq_status kq_w4a8_linear(const void* x, int64_t M, int64_t K, int64_t N,
+                         const uint8_t* wq4, const void* gscale,
+                         const void* gbias, const float* bias, void* y,
+                         kq_dtype y_dtype, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Small-M GEMV ([qlip] w4a8_linear bullet: a register-dequant GEMV path for
+ * M <= 16 runs decode-style calls at weight-bandwidth speed).  Same math and
+ * arguments as kq_w4a8_linear (fmt = KQ_W4_AFFINE_G64: wq, scale, gbias as
+ * there) or kq_w8a8_linear (fmt = KQ_W8_PER_CHANNEL: wq int8, scale fp32 [N],
+ * gbias NULL), always on the GEMV kernel.  Requires 1 <= M <= 16. */
+kq_status kq_gemv_small_m(kq_wformat fmt, const void* x, int64_t M, int64_t K,
+                          int64_t N, const void* wq, const void* scale,
+                          const void* gbias, const float* bias, void* y,
+                          kq_dtype y_dtype, void* ws, size_t ws_bytes,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KQ_H */
