@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Throughput of the INT8 quantized linear on one MI355X.
+
+A step is one full linear call -- per-token activation quantization, the
+INT8 MFMA GEMM and its fused dequant+bias epilogue -- on the DiT
+attention-projection workload (W8A8, M=4096 tokens, K=N=3072, bf16 out),
+with the offline weight quantization done once before timing.  Inputs are
+seeded synthetic draws (the pages' models and prompts are not available),
+resident in HBM before the timed region, rotated over enough independent
+copies (>= 512 MB) that the 256 MB Infinity Cache cannot hold them.
+
+Timing: W eager warmup steps; the K timed steps are captured in one HIP
+graph (so host launch overhead does not bound microsecond-scale calls),
+replayed once untimed, then replayed once between synchronizations and
+events on the capturing stream.  The GEMM kernel alone is timed the same
+way through kq_w8a8_gemm on the same pre-quantized activations, for the
+roofline figure.  The CPU oracle is timed on the host on the same
+workload.
+
+Prints ONE JSON line (rank 0, N=1).  `--gpus N` with N > 1 exits: this
+build targets one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0   # MI355X dense INT8 MFMA, tera-ops/s
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, GB/s
+ROTATE_BYTES = 512 << 20  # working set rotated per timed pass
+METRIC = "W8A8/W4A8 GEMM INT8 TOPS + % of INT8 MFMA peak; GEMV GB/s at M≤16"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ workloads
+def algorithmic_bytes(wl, M=None) -> int:
+    """Compulsory HBM bytes of one linear call: bf16 x, the weights (int8 +
+    fp32 scale, or int4 + fp16 scale and offset per 64-group = 0.5625 B per
+    weight), the fp32 bias and y."""
+    M = wl.M if M is None else M
+    x = 2 * M * wl.K
+    if wl.fmt == "w8":
+        w = wl.N * wl.K + 4 * wl.N
+    else:
+        w = wl.N * wl.K // 2 + 4 * wl.N * (wl.K // 64)
+    y = (4 if wl.out == "f32" else 2) * M * wl.N
+    return x + w + 4 * wl.N + y
+
+
+class Prepared:
+    """Device-resident inputs of one workload, in R rotation copies."""
+
+    def __init__(self, wl, seed=0, x_override=None):
+        import torch
+        import synth
+        import w8a8_gemm_dit_amd as kq
+        from tests.parity import dev, dev_bf16
+
+        self.wl = wl
+        self.kq = kq
+        self.out_dtype = torch.float32 if wl.out == "f32" else torch.bfloat16
+        x0 = dev_bf16(synth.activations(wl, seed)) if x_override is None else x_override
+        wd = dev(synth.weights(wl, seed))
+        b0 = dev(synth.bias(wl, seed))
+        fmt = kq.KQ_W8_PER_CHANNEL if wl.fmt == "w8" else kq.KQ_W4_AFFINE_G64
+        self.fmt = fmt
+        wq, sc, gb = kq.kq_quantize_weights(wd, fmt)
+        del wd
+        ws_bytes = kq.kq_workspace_bytes(wl.M, wl.K, fmt)
+        ysz = wl.M * wl.N * (4 if wl.out == "f32" else 2)
+        per_copy = (x0.numel() * 2 + wq.numel() + sc.numel() * sc.element_size()
+                    + (0 if gb is None else gb.numel() * 2) + 4 * wl.N + ysz + ws_bytes)
+        self.R = max(1, min(16, math.ceil(ROTATE_BYTES / per_copy)))
+        self.copies = []
+        for r in range(self.R):
+            c = {
+                "x": x0 if r == 0 else x0.clone(),
+                "wq": wq if r == 0 else wq.clone(),
+                "sc": sc if r == 0 else sc.clone(),
+                "gb": None if gb is None else (gb if r == 0 else gb.clone()),
+                "b": b0 if r == 0 else b0.clone(),
+                "y": torch.empty((wl.M, wl.N), dtype=self.out_dtype, device="cuda"),
+                "ws": torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device="cuda"),
+            }
+            a, sx, gs = kq.kq_quantize_act(c["x"], group_sums=(fmt == kq.KQ_W4_AFFINE_G64))
+            c.update(a=a, sx=sx, gs=gs)
+            self.copies.append(c)
+        torch.cuda.synchronize()
+
+    def step(self, i: int) -> None:
+        c = self.copies[i % self.R]
+        kq = self.kq
+        if self.fmt == kq.KQ_W8_PER_CHANNEL:
+            kq.kq_w8a8_linear(c["x"], c["wq"], c["sc"], c["b"], out_dtype=self.out_dtype,
+                              out=c["y"], workspace=c["ws"])
+        else:
+            kq.kq_w4a8_linear(c["x"], c["wq"], c["sc"], c["gb"], c["b"], out_dtype=self.out_dtype,
+                              out=c["y"], workspace=c["ws"])
+
+    def gemm(self, i: int) -> None:
+        c = self.copies[i % self.R]
+        kq = self.kq
+        if self.fmt == kq.KQ_W8_PER_CHANNEL:
+            kq.kq_w8a8_gemm(c["a"], c["sx"], c["wq"], c["sc"], c["b"], out_dtype=self.out_dtype,
+                            out=c["y"])
+        else:
+            kq.kq_w4a8_gemm(c["a"], c["sx"], c["gs"], c["wq"], c["sc"], c["gb"], c["b"],
+                            out_dtype=self.out_dtype, out=c["y"])
+
+
+def graph_time(fn, steps: int) -> float:
+    """Capture `steps` calls of fn(i) in one HIP graph, replay once untimed,
+    then time one replay; returns ms per call."""
+    import torch
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0)                         # touch everything once outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    g.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def eager_time(fn, steps: int) -> float:
+    import torch
+
+    st = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for i in range(steps):
+        fn(i)
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+# ------------------------------------------------------------ CPU baseline
+def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
+    """The oracle as it stands (numpy; fp32 quantizers, fp64 product), on the
+    full headline workload, repeated until about `budget_s` of CPU time."""
+    import numpy as np
+    import oracle
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    xb, w, b = synth.activations(wl), synth.weights(wl), synth.bias(wl)
+    q8, sw = oracle.quantize_w8(w)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        y = oracle.w8a8_linear_exact(xb, q8, sw, b)
+        oracle.round_bf16_bits(oracle.round_f32(y))
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 50:
+            break
+    med = statistics.median(times)
+    return {
+        "value": round(wl.ops / med / 1e12, 4),
+        "unit": "TOPS",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"full {wl.name} linear (per-token quantize + fp64 product + bf16 rounding), "
+                   f"median of {len(times)} runs, {med:.3f} s each; host {platform.processor() or platform.machine()}, "
+                   f"{len(os.sched_getaffinity(0))} cores visible"),
+    }
+
+
+# ------------------------------------------------------------ traffic
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm_w8a8.hip", "kq_common.hpp"):
+        with open(os.path.join(ROOT, "w8a8_gemm_dit_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None if absent or taken on a different kernel source."""
+    p = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(kernel)
+    except Exception:
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------ main
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--quick", action="store_true", help="headline only, no extra workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="few eager steps of every workload, for profiler runs")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; this build runs on one GPU "
+              "(the linear would shard by output rows or columns with no collective).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    import w8a8_gemm_dit_amd as kq
+
+    torch.cuda.set_device(0)
+    if not kq.kq_is_available():
+        print("bench.py: device 0 is not a gfx950 GPU", file=sys.stderr)
+        return 1
+    log(f"device {torch.cuda.get_device_name(0)}")
+
+    if args.profile:
+        for name, wl in synth.WORKLOADS.items():
+            p = Prepared(wl)
+            for i in range(max(args.steps, 1)):
+                p.step(i)
+            for i in range(max(args.steps, 1)):
+                p.gemm(i)
+            torch.cuda.synchronize()
+            log(f"profiled {name}")
+            del p
+            torch.cuda.empty_cache()
+        return 0
+
+    wl = synth.WORKLOADS[synth.HEADLINE]
+    p = Prepared(wl)
+    log(f"{wl.name}: {p.R} rotation copies")
+    for i in range(args.warmup):
+        p.step(i)
+    torch.cuda.synchronize()
+    ms = graph_time(p.step, args.steps)
+    ms_eager = eager_time(p.step, args.steps)
+    ms_gemm = graph_time(p.gemm, args.steps)
+    log(f"step {ms * 1e3:.2f} us (eager {ms_eager * 1e3:.2f} us), gemm {ms_gemm * 1e3:.2f} us")
+    route = kq.kq_route(wl.M, wl.N, wl.K, kq.KQ_W8_PER_CHANNEL)
+    gemm_name = f"gemm_w8a8_{route['tile_m']}x{route['tile_n']}"
+    tops = wl.ops / (ms * 1e-3) / 1e12
+    gemm_tops = wl.ops / (ms_gemm * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(tops, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N,
+                   "weights": "int8 per output channel", "activations": "bf16 -> int8 per token",
+                   "out": wl.out, "pct_of_int8_peak": round(100 * tops / PEAK_INT8_TOPS, 2),
+                   "eager_ms_per_step": round(ms_eager, 6), "rotation_copies": p.R},
+        "roofline": {
+            "kernel": gemm_name,
+            "bound": "mfma",
+            "achieved": round(gemm_tops, 2),
+            "peak": PEAK_INT8_TOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+            "traffic": recorded_traffic(gemm_name),
+            "avg_launch_us": round(ms_gemm * 1e3, 3),
+        },
+    }
+    del p
+    torch.cuda.empty_cache()
+
+    if not args.quick:
+        extra = {}
+        steps_x = max(20, args.steps // 5)
+        for name, w in synth.WORKLOADS.items():
+            if name == synth.HEADLINE:
+                continue
+            pw = Prepared(w)
+            for i in range(3):
+                pw.step(i)
+            t = graph_time(pw.step, steps_x)
+            tg = graph_time(pw.gemm, steps_x)
+            gbs = algorithmic_bytes(w) / (t * 1e-3) / 1e9
+            r = kq.kq_route(w.M, w.N, w.K, pw.fmt)
+            extra[name] = {
+                "ms_per_call": round(t, 5), "kernel_ms": round(tg, 5),
+                "route": r["kind"], "tile": f"{r['tile_m']}x{r['tile_n']}",
+                "tops": round(w.ops / (t * 1e-3) / 1e12, 2),
+                "pct_int8_peak": round(100 * w.ops / (t * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2),
+                "kernel_tops": round(w.ops / (tg * 1e-3) / 1e12, 2),
+                "gbs": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+            }
+            log(f"{name}: {t * 1e3:.2f} us/call ({extra[name]['tops']} TOPS, {gbs:.0f} GB/s)")
+            del pw
+            torch.cuda.empty_cache()
+        result["extra"] = extra
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

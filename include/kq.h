@@ -192,6 +192,26 @@ kq_status kq_w4a8_linear(const void* x, int64_t M, int64_t K, int64_t N,
                          kq_dtype y_dtype, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* Linears on activations already quantized by kq_quantize_act: the same
+ * kernels, routes and results as kq_w8a8_linear / kq_w4a8_linear, without
+ * the activation pass.  One quantization can then feed several linears that
+ * read the same activations (a DiT block's q/k/v projections, or its
+ * modulation fan-out).
+ *   a     device int8 [M,K] codes, sx device fp32 [M] scales
+ *   gsum  device int32 [M,K/64] group sums (int4 weights only)
+ * Other arguments, constraints and outputs as the corresponding linear; no
+ * workspace is needed. */
+kq_status kq_w8a8_gemm(const int8_t* a, const float* sx, int64_t M, int64_t K,
+                       int64_t N, const int8_t* wq, const float* sw,
+                       const float* bias, void* y, kq_dtype y_dtype,
+                       void* stream);
+
+kq_status kq_w4a8_gemm(const int8_t* a, const float* sx, const int32_t* gsum,
+                       int64_t M, int64_t K, int64_t N, const uint8_t* wq4,
+                       const void* gscale, const void* gbias,
+                       const float* bias, void* y, kq_dtype y_dtype,
+                       void* stream);
+
 /* Small-M GEMV ([qlip] w4a8_linear bullet: a register-dequant GEMV path for
  * M <= 16 runs decode-style calls at weight-bandwidth speed).  Same math and
  * arguments as kq_w4a8_linear (fmt = KQ_W4_AFFINE_G64: wq, scale, gbias as

@@ -1,0 +1,170 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol the header
+declares, and its host logic (validation, routing, workspace sizing, error
+messages) behaves as documented.  No call here reaches the device: each one
+fails validation, or is a no-op, before any device access."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import w8a8_gemm_dit_amd as kq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kq.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|kq_status|size_t|const char\*)\s+(kq_\w+)\s*\(",
+                                 src, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    L = kq.lib()
+    declared = _declared_functions()
+    assert len(declared) == 11, declared
+    assert sorted(kq.exported_symbols) == declared
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_is_available_false_without_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    assert kq.kq_is_available() is False
+
+
+def test_workspace_layout():
+    al = lambda v: (v + 255) // 256 * 256
+    M, K = 4096, 3072
+    assert kq.kq_workspace_bytes(M, K, kq.KQ_W8_PER_CHANNEL) == al(M * K) + al(4 * M)
+    assert kq.kq_workspace_bytes(M, K, kq.KQ_W4_AFFINE_G64) == al(M * K) + al(4 * M) + al(4 * M * K // 64)
+    assert kq.kq_workspace_bytes(0, K, kq.KQ_W8_PER_CHANNEL) == 0
+    assert kq.kq_workspace_bytes(3, 64, kq.KQ_W8_PER_CHANNEL) == 256 + 256
+
+
+@pytest.mark.parametrize("M,N,K,fmt,kind,tile,grid", [
+    (1, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 32), 432),
+    (16, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 32), 432),
+    (17, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemm", None, None),
+    (4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 128), 384),
+    (16384, 12288, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 256), 3072),
+    (2048, 12288, 4096, kq.KQ_W4_AFFINE_G64, "gemm", (256, 128), 768),
+    (2048, 4096, 12288, kq.KQ_W4_AFFINE_G64, "gemm", (256, 128), 256),
+    (2048, 48, 5120, kq.KQ_W8_PER_CHANNEL, "gemm", (64, 64), 32),
+])
+def test_route_decisions(M, N, K, fmt, kind, tile, grid, kq_env):
+    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None)
+    r = kq.kq_route(M, N, K, fmt)
+    assert r["kind"] == kind
+    if tile is not None:
+        assert (r["tile_m"], r["tile_n"]) == tile
+        assert r["grid"] == grid
+
+
+def test_route_levers(kq_env):
+    kq_env(KQ_FORCE_ROUTE="gemm")
+    assert kq.kq_route(4, 512, 512, kq.KQ_W4_AFFINE_G64)["kind"] == "gemm"
+    kq_env(KQ_FORCE_ROUTE="gemv")
+    assert kq.kq_route(4, 512, 512, kq.KQ_W8_PER_CHANNEL)["kind"] == "gemv"
+    with pytest.raises(ValueError, match=r"\[kq_route\] M=32 exceeds the GEMV limit 16"):
+        kq.kq_route(32, 512, 512, kq.KQ_W8_PER_CHANNEL)
+    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE="128x128")
+    r = kq.kq_route(4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL)
+    assert (r["tile_m"], r["tile_n"], r["grid"]) == (128, 128, 32 * 24)
+    kq_env(KQ_TILE="256x256")
+    r = kq.kq_route(4096, 3072, 3072, kq.KQ_W4_AFFINE_G64)
+    assert (r["tile_m"], r["tile_n"]) == (256, 128)     # int4 caps at 256x128
+
+
+@pytest.mark.parametrize("K,msg", [
+    (100, r"\[kq_route\] K=100 must be a positive multiple of 64"),
+    (0, r"K=0 must be a positive multiple of 64"),
+    (65536 + 64, r"K=65600 exceeds 65536"),
+])
+def test_route_rejects_unsupported_k(K, msg):
+    with pytest.raises(ValueError, match=msg):
+        kq.kq_route(64, 64, K, kq.KQ_W8_PER_CHANNEL)
+
+
+def test_route_rejects_bad_enums_and_sizes():
+    with pytest.raises(ValueError, match="unknown weight format 7"):
+        kq.kq_route(64, 64, 64, 7)
+    with pytest.raises(ValueError, match="unknown output dtype 9"):
+        kq.kq_route(64, 64, 64, kq.KQ_W8_PER_CHANNEL, 9)
+    with pytest.raises(ValueError, match="negative size"):
+        kq.kq_route(-1, 64, 64, kq.KQ_W8_PER_CHANNEL)
+
+
+# Raw C-ABI calls with fake (never dereferenced) device addresses.
+P = ctypes.c_void_p
+
+
+def _w8(M, K, N, x=16, w=32, sw=48, y=64, ws=80, wsb=1 << 30, dtype=kq.KQ_DTYPE_BF16):
+    return kq.lib().kq_w8a8_linear(P(x), M, K, N, P(w), P(sw), None, P(y), dtype, P(ws), wsb, None)
+
+
+def test_linear_validation_without_device():
+    L = kq.lib()
+    assert _w8(64, 100, 64) == kq.KQ_ERR_UNSUPPORTED
+    assert "[kq_w8a8_linear] K=100 must be a positive multiple of 64" in kq.kq_last_error()
+    assert _w8(0, 128, 64) == kq.KQ_SUCCESS          # empty: nothing enqueued
+    assert _w8(64, 128, 0) == kq.KQ_SUCCESS
+    assert _w8(64, 128, 64, x=0) == kq.KQ_ERR_INVALID_VALUE
+    assert "null tensor pointer" in kq.kq_last_error()
+    assert _w8(64, 128, 64, x=17) == kq.KQ_ERR_INVALID_VALUE
+    assert "16-byte aligned" in kq.kq_last_error()
+    assert _w8(64, 128, 64, wsb=100) == kq.KQ_ERR_WORKSPACE
+    assert "smaller than the" in kq.kq_last_error()
+    assert _w8(64, 128, 64, dtype=5) == kq.KQ_ERR_INVALID_VALUE
+    # int4 needs the group offsets
+    st = L.kq_w4a8_linear(P(16), 64, 128, 64, P(32), P(48), None, None, P(64),
+                          kq.KQ_DTYPE_BF16, P(80), 1 << 30, None)
+    assert st == kq.KQ_ERR_INVALID_VALUE and "group offsets" in kq.kq_last_error()
+    # GEMV limit
+    st = L.kq_gemv_small_m(kq.KQ_W4_AFFINE_G64, P(16), 17, 128, 64, P(32), P(48), P(64), None,
+                           P(80), kq.KQ_DTYPE_BF16, P(96), 1 << 30, None)
+    assert st == kq.KQ_ERR_UNSUPPORTED and "exceeds the GEMV limit 16" in kq.kq_last_error()
+    st = L.kq_gemv_small_m(kq.KQ_W8_PER_CHANNEL, P(16), 4, 128, 64, P(32), P(48), P(64), None,
+                           P(80), kq.KQ_DTYPE_BF16, P(96), 1 << 30, None)
+    assert st == kq.KQ_ERR_INVALID_VALUE and "gbias must be NULL" in kq.kq_last_error()
+
+
+def test_quantizer_validation_without_device():
+    L = kq.lib()
+    assert L.kq_quantize_act(P(16), 4, 0, P(32), P(48), None, None) == kq.KQ_ERR_UNSUPPORTED
+    assert L.kq_quantize_act(P(16), 4, 100, P(32), P(48), P(64), None) == kq.KQ_ERR_UNSUPPORTED
+    assert "group sums need K % 64 == 0" in kq.kq_last_error()
+    assert L.kq_quantize_act(P(16), 0, 100, P(32), P(48), None, None) == kq.KQ_SUCCESS
+    assert L.kq_quantize_act(None, 4, 64, P(32), P(48), None, None) == kq.KQ_ERR_INVALID_VALUE
+    assert L.kq_quantize_weights(P(16), 4, 100, kq.KQ_W4_AFFINE_G64, P(32), P(48), P(64),
+                                 None) == kq.KQ_ERR_UNSUPPORTED
+    assert L.kq_quantize_weights(P(16), 4, 64, kq.KQ_W8_PER_CHANNEL, P(32), P(48), P(64),
+                                 None) == kq.KQ_ERR_INVALID_VALUE
+    assert L.kq_quantize_weights(P(16), 4, 64, 3, P(32), P(48), None, None) == kq.KQ_ERR_INVALID_VALUE
+    assert L.kq_quantize_weights(P(16), 0, 64, kq.KQ_W8_PER_CHANNEL, P(32), P(48), None,
+                                 None) == kq.KQ_SUCCESS
+
+
+def test_last_error_is_per_thread():
+    import threading
+    _w8(64, 100, 64)
+    seen = {}
+
+    def other():
+        seen["msg"] = kq.kq_last_error()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "K=100" in kq.kq_last_error()
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(kq, "_lib", None)
+    monkeypatch.setattr(kq, "_LIB_PATH", "/nonexistent/libkq.so")
+    with pytest.raises(kq.KqError, match="not built"):
+        kq.lib()

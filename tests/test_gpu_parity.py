@@ -1,0 +1,296 @@
+"""GPU parity: libkq (through its C ABI and the thin binding) against the
+CPU oracle on identical seeded inputs."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import w8a8_gemm_dit_amd as kq
+from tests.parity import check_bf16, check_f32, dev, dev_bf16, host, host_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    print(f"[parity] device: {torch.cuda.get_device_name(0)}", flush=True)
+    assert kq.kq_is_available(), "libkq reports no gfx950 device"
+
+
+# -------------------------------------------------------------- quantizers
+K_SWEEP = [1, 7, 8, 31, 33, 63, 64, 65, 127, 128, 511, 512, 520, 3072, 4096, 5120,
+           12288, 16384, 20000, 20001]
+
+
+@pytest.mark.parametrize("K", K_SWEEP)
+@pytest.mark.parametrize("M", [1, 5])
+def test_quantize_act_k_sweep(M, K):
+    xb = synth.random_bf16((M, K), seed=1000 + K + M, scale=2.0, dist="student_t4")
+    a_ref, sx_ref, g_ref = oracle.quantize_act(xb)
+    a, sx, g = kq.kq_quantize_act(dev_bf16(xb), group_sums=(K % 64 == 0))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(a), a_ref)
+    assert np.array_equal(host(sx).view(np.uint32), sx_ref.view(np.uint32))
+    if K % 64 == 0:
+        assert np.array_equal(host(g), g_ref)
+
+
+def test_quantize_act_special_rows():
+    K = 3072
+    x = synth.bf16_bits_to_f32(synth.random_bf16((8, K), seed=7)).copy()
+    x[0] = 0.0                               # zero row
+    x[1] = 0.0
+    x[1, 17] = 1e-38                         # 127/amax overflows -> zero row
+    x[2] *= np.float32(1e-36)                # tiny, still quantizes
+    x[3] = 0.0
+    x[3, ::7] = np.float32(2.0 ** -130)      # subnormal values (bf16 keeps them)
+    x[4, 5] = np.float32(3.0e38)             # huge outlier
+    x[5] = np.round(x[5] * 40)               # ties at .5 after scaling
+    x[6] *= np.float32(-1.0)
+    xb = synth.to_bf16_bits(x)
+    a_ref, sx_ref, g_ref = oracle.quantize_act(xb)
+    a, sx, g = kq.kq_quantize_act(dev_bf16(xb), group_sums=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(a), a_ref)
+    assert np.array_equal(host(sx).view(np.uint32), sx_ref.view(np.uint32))
+    assert np.array_equal(host(g), g_ref)
+
+
+@pytest.mark.parametrize("N,K", [(1, 64), (33, 192), (257, 3072), (48, 5120), (130, 12288)])
+def test_quantize_weights_bit_exact(N, K):
+    w = synth.random_f32((N, K), seed=N + K, scale=0.02)
+    w[0, :64] = 0.0                           # degenerate group / row part
+    if N > 2:
+        w[2] = 0.0                            # zero row -> scale 0
+    wd = dev(w)
+    q8, sw, none = kq.kq_quantize_weights(wd, kq.KQ_W8_PER_CHANNEL)
+    q4, gs, gb = kq.kq_quantize_weights(wd, kq.KQ_W4_AFFINE_G64)
+    torch.cuda.synchronize()
+    assert none is None
+    q8_ref, sw_ref = oracle.quantize_w8(w)
+    assert np.array_equal(host(q8), q8_ref)
+    assert np.array_equal(host(sw).view(np.uint32), sw_ref.view(np.uint32))
+    p_ref, gs_ref, gb_ref, _ = oracle.quantize_w4(w)
+    assert np.array_equal(host(q4), p_ref)
+    assert np.array_equal(host(gs).view(np.uint16), gs_ref.view(np.uint16))
+    assert np.array_equal(host(gb).view(np.uint16), gb_ref.view(np.uint16))
+
+
+# ---------------------------------------------------------------- linears
+def _problem(M, K, N, seed, dist="normal", with_bias=True):
+    xb = synth.random_bf16((M, K), seed=seed, dist=dist)
+    w = synth.random_f32((N, K), seed=seed + 1, scale=0.02)
+    b = synth.random_f32((N,), seed=seed + 2, scale=0.1) if with_bias else None
+    return xb, w, b
+
+
+SHAPES = [(64, 512, 512), (1, 64, 16), (17, 64, 33), (100, 192, 200), (257, 128, 129),
+          (300, 256, 48), (64, 1024, 1000), (513, 320, 260)]
+TILES = [None, "256x256", "256x128", "128x128", "64x64"]
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_w8a8_accumulators_bit_exact(M, K, N, tile, kq_env):
+    kq_env(KQ_TILE=tile, KQ_FORCE_ROUTE="gemm")
+    xb, w, _ = _problem(M, K, N, seed=M * 7 + K + N)
+    q8, sw = oracle.quantize_w8(w)
+    a, _, _ = oracle.quantize_act(xb)
+    acc = kq.kq_w8a8_linear(dev_bf16(xb), dev(q8), dev(sw), out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(acc), oracle.w8a8_acc(a, q8))
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("tile", [None, "256x256", "64x64"])
+@pytest.mark.parametrize("M,K,N", SHAPES[:6])
+def test_w8a8_outputs(M, K, N, tile, out, kq_env):
+    kq_env(KQ_TILE=tile, KQ_FORCE_ROUTE="gemm")
+    xb, w, b = _problem(M, K, N, seed=M + 3 * K + N, with_bias=(M % 2 == 0))
+    q8, sw = oracle.quantize_w8(w)
+    y64 = oracle.w8a8_linear_exact(xb, q8, sw, b)
+    T = oracle.w8a8_magnitude(xb, q8, sw, b)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    y = kq.kq_w8a8_linear(dev_bf16(xb), dev(q8), dev(sw), None if b is None else dev(b), out_dtype=dt)
+    torch.cuda.synchronize()
+    if out == "f32":
+        check_f32(host(y), y64, T, f"w8a8 {M}x{K}x{N}")
+    else:
+        check_bf16(host_bf16_bits(y), y64, T, f"w8a8 {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("tile", [None, "256x128", "128x128", "64x64"])
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_w4a8_group_products_bit_exact(M, K, N, tile, kq_env):
+    kq_env(KQ_TILE=tile, KQ_FORCE_ROUTE="gemm")
+    xb, w, _ = _problem(M, K, N, seed=M + K * 5 + N)
+    p, gs, gb, q = oracle.quantize_w4(w)
+    a, _, _ = oracle.quantize_act(xb)
+    P = kq.kq_w4a8_linear(dev_bf16(xb), dev(p), dev(gs), dev(gb), out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(P), oracle.w4a8_group_acc(a, q))
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("tile", [None, "128x128", "64x64"])
+@pytest.mark.parametrize("M,K,N", SHAPES[:6])
+def test_w4a8_outputs(M, K, N, tile, out, kq_env):
+    kq_env(KQ_TILE=tile, KQ_FORCE_ROUTE="gemm")
+    xb, w, b = _problem(M, K, N, seed=2 * M + K + N, with_bias=(M % 2 == 1))
+    p, gs, gb, q = oracle.quantize_w4(w)
+    y64 = oracle.w4a8_linear_exact(xb, q, gs, gb, b)
+    T = oracle.w4a8_magnitude(xb, q, gs, gb, b)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    y = kq.kq_w4a8_linear(dev_bf16(xb), dev(p), dev(gs), dev(gb), None if b is None else dev(b),
+                          out_dtype=dt)
+    torch.cuda.synchronize()
+    if out == "f32":
+        check_f32(host(y), y64, T, f"w4a8 {M}x{K}x{N}")
+    else:
+        check_bf16(host_bf16_bits(y), y64, T, f"w4a8 {M}x{K}x{N}")
+
+
+# ------------------------------------------------------------------ GEMV
+@pytest.mark.parametrize("M", [1, 2, 4, 7, 16])
+@pytest.mark.parametrize("K,N", [(64, 16), (320, 100), (5120, 256), (4160, 33)])
+def test_gemv_w4_bit_exact_and_outputs(M, K, N):
+    xb, w, b = _problem(M, K, N, seed=M + K + 11 * N)
+    p, gs, gb, q = oracle.quantize_w4(w)
+    a, _, _ = oracle.quantize_act(xb)
+    args = (kq.KQ_W4_AFFINE_G64, dev_bf16(xb), dev(p), dev(gs), dev(gb))
+    P = kq.kq_gemv_small_m(*args, out_dtype=torch.int32)
+    yf = kq.kq_gemv_small_m(*args, bias=dev(b), out_dtype=torch.float32)
+    yb = kq.kq_gemv_small_m(*args, bias=dev(b), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(P), oracle.w4a8_group_acc(a, q))
+    y64 = oracle.w4a8_linear_exact(xb, q, gs, gb, b)
+    T = oracle.w4a8_magnitude(xb, q, gs, gb, b)
+    check_f32(host(yf), y64, T, "gemv w4 f32")
+    check_bf16(host_bf16_bits(yb), y64, T, "gemv w4 bf16")
+
+
+@pytest.mark.parametrize("M", [1, 3, 16])
+@pytest.mark.parametrize("K,N", [(64, 16), (5120, 300)])
+def test_gemv_w8(M, K, N):
+    xb, w, b = _problem(M, K, N, seed=M + K + 13 * N)
+    q8, sw = oracle.quantize_w8(w)
+    a, _, _ = oracle.quantize_act(xb)
+    args = (kq.KQ_W8_PER_CHANNEL, dev_bf16(xb), dev(q8), dev(sw), None)
+    acc = kq.kq_gemv_small_m(*args, out_dtype=torch.int32)
+    yf = kq.kq_gemv_small_m(*args, bias=dev(b), out_dtype=torch.float32)
+    yb = kq.kq_gemv_small_m(*args, bias=dev(b), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(acc), oracle.w8a8_acc(a, q8))
+    y64 = oracle.w8a8_linear_exact(xb, q8, sw, b)
+    T = oracle.w8a8_magnitude(xb, q8, sw, b)
+    check_f32(host(yf), y64, T, "gemv w8 f32")
+    check_bf16(host_bf16_bits(yb), y64, T, "gemv w8 bf16")
+
+
+def test_gemv_and_gemm_routes_agree_bitwise(kq_env):
+    # The same per-group products whichever kernel runs (decode steps stay
+    # bit-identical across routes, as MLX pull request 4722 checks).
+    M, K, N = 8, 1024, 200
+    xb, w, b = _problem(M, K, N, seed=99)
+    p, gs, gb, q = oracle.quantize_w4(w)
+    args = (dev_bf16(xb), dev(p), dev(gs), dev(gb))
+    kq_env(KQ_FORCE_ROUTE="gemv")
+    P1 = host(kq.kq_w4a8_linear(*args, out_dtype=torch.int32))
+    kq_env(KQ_FORCE_ROUTE="gemm")
+    P2 = host(kq.kq_w4a8_linear(*args, out_dtype=torch.int32))
+    assert np.array_equal(P1, P2)
+
+
+# ------------------------------------------------------------- behaviour
+def test_route_log_names_kernels(kq_env, capfd):
+    kq_env(KQ_LOG="1", KQ_FORCE_ROUTE=None, KQ_TILE=None)
+    xb, w, b = _problem(4, 256, 64, seed=5)
+    p, gs, gb, _ = oracle.quantize_w4(w)
+    kq.kq_w4a8_linear(dev_bf16(xb), dev(p), dev(gs), dev(gb))
+    xb2 = synth.random_bf16((300, 256), seed=6)
+    kq.kq_w4a8_linear(dev_bf16(xb2), dev(p), dev(gs), dev(gb))
+    torch.cuda.synchronize()
+    err = capfd.readouterr().err
+    assert "kq_w4a8_linear M=4" in err and "route=gemv" in err and "gemv_w4a8" in err
+    assert "kq_w4a8_linear M=300" in err and "route=gemm" in err and "gemm_w4a8_" in err
+
+
+def test_empty_and_error_paths():
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    wq = torch.zeros((64, 128), dtype=torch.int8, device="cuda")
+    sw = torch.ones((64,), dtype=torch.float32, device="cuda")
+    y = kq.kq_w8a8_linear(x, wq, sw)
+    assert y.shape == (0, 64)
+    xb = torch.zeros((4, 100), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="K=100 must be a positive multiple of 64"):
+        kq.kq_w8a8_linear(xb, torch.zeros((64, 100), dtype=torch.int8, device="cuda"), sw)
+    # a misaligned x (an offset view of a larger buffer)
+    big = torch.zeros((4 * 128 + 8,), dtype=torch.bfloat16, device="cuda")
+    xm = big[1:1 + 4 * 128].view(4, 128)
+    with pytest.raises(ValueError, match="16-byte aligned"):
+        kq.kq_w8a8_linear(xm, wq, sw)
+
+
+def test_deterministic_bits():
+    M, K, N = 512, 1024, 768
+    xb, w, b = _problem(M, K, N, seed=42)
+    q8, sw = oracle.quantize_w8(w)
+    p, gs, gb, _ = oracle.quantize_w4(w)
+    x = dev_bf16(xb)
+    r1 = kq.kq_w8a8_linear(x, dev(q8), dev(sw), dev(b)).clone()
+    r2 = kq.kq_w8a8_linear(x, dev(q8), dev(sw), dev(b)).clone()
+    s1 = kq.kq_w4a8_linear(x, dev(p), dev(gs), dev(gb), dev(b)).clone()
+    s2 = kq.kq_w4a8_linear(x, dev(p), dev(gs), dev(gb), dev(b)).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(r1.view(torch.int16), r2.view(torch.int16))
+    assert torch.equal(s1.view(torch.int16), s2.view(torch.int16))
+
+
+# ------------------------------------------------------ full-size workloads
+def _sample_rows(M, rng):
+    rows = {0, 1, M // 2, M - 2, M - 1}
+    rows.update(int(r) for r in rng.integers(0, M, size=4))
+    return np.array(sorted(r for r in rows if 0 <= r < M))
+
+
+@pytest.mark.parametrize("name", [n for n in synth.WORKLOADS])
+def test_workload_full_size_sampled_rows(name):
+    """Full-size launch (as the benchmark runs it); the weights are checked
+    bit-exact in full and the outputs on sampled rows, which the oracle can
+    compute on their own because quantization is per row."""
+    wl = synth.WORKLOADS[name]
+    print(f"[parity] workload {name}", flush=True)
+    xb = synth.activations(wl)
+    w = synth.weights(wl)
+    b = synth.bias(wl)
+    rows = _sample_rows(wl.M, np.random.default_rng(0))
+    wd = dev(w)
+    out_dt = torch.float32 if wl.out == "f32" else torch.bfloat16
+    x = dev_bf16(xb)
+    if wl.fmt == "w8":
+        q8, sw, _ = kq.kq_quantize_weights(wd, kq.KQ_W8_PER_CHANNEL)
+        del wd
+        y = kq.kq_w8a8_linear(x, q8, sw, dev(b), out_dtype=out_dt)
+        q8_ref, sw_ref = oracle.quantize_w8(w)
+        assert np.array_equal(host(q8), q8_ref)
+        assert np.array_equal(host(sw).view(np.uint32), sw_ref.view(np.uint32))
+        y64 = oracle.w8a8_linear_exact(xb[rows], q8_ref, sw_ref, b)
+        T = oracle.w8a8_magnitude(xb[rows], q8_ref, sw_ref, b)
+    else:
+        p, gs, gb = kq.kq_quantize_weights(wd, kq.KQ_W4_AFFINE_G64)
+        del wd
+        y = kq.kq_w4a8_linear(x, p, gs, gb, dev(b), out_dtype=out_dt)
+        p_ref, gs_ref, gb_ref, q_ref = oracle.quantize_w4(w)
+        assert np.array_equal(host(p), p_ref)
+        assert np.array_equal(host(gs).view(np.uint16), gs_ref.view(np.uint16))
+        assert np.array_equal(host(gb).view(np.uint16), gb_ref.view(np.uint16))
+        y64 = oracle.w4a8_linear_exact(xb[rows], q_ref, gs_ref, gb_ref, b)
+        T = oracle.w4a8_magnitude(xb[rows], q_ref, gs_ref, gb_ref, b)
+    ys = y[torch.from_numpy(rows).cuda()]
+    torch.cuda.synchronize()
+    if wl.out == "f32":
+        check_f32(host(ys), y64, T, name)
+    else:
+        check_bf16(host_bf16_bits(ys), y64, T, name)

@@ -1,0 +1,326 @@
+// C ABI of libkq: argument checks, routing and kernel launches.
+//
+// Every entry point validates its arguments on the host before touching the
+// device, records a "[op] message" on failure (the MLX "[op] ... not
+// supported" invalid_argument convention, MLX pull request 3026's fast.cpp
+// checks) and returns a status; no exception crosses the ABI.  A declined
+// route is not an error (mlx-kquant pull request 89 commit list: raise on
+// errors other than a declined route).  Launches are asynchronous on the
+// caller's stream; nothing here allocates device memory or synchronizes.
+//
+// Environment levers, read on every call:
+//   KQ_LOG=1            one stderr line per call: op, route, kernels, grid
+//   KQ_FORCE_ROUTE=gemm|gemv   override the M <= 16 GEMV routing
+//   KQ_TILE=256x256|256x128|128x128|64x64   pin the GEMM tile (A/B runs)
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "kq.h"
+#include "kq_launch.hpp"
+#include "kq_route.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kq_status fail(kq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+int env_force_route() {
+  const char* v = getenv("KQ_FORCE_ROUTE");
+  if (!v) return 0;
+  if (!strcmp(v, "gemm")) return 1;
+  if (!strcmp(v, "gemv")) return 2;
+  return 0;
+}
+
+int env_tile() {
+  const char* v = getenv("KQ_TILE");
+  if (!v) return -1;
+  if (!strcmp(v, "256x256")) return kq::kTile256x256;
+  if (!strcmp(v, "256x128")) return kq::kTile256x128;
+  if (!strcmp(v, "128x128")) return kq::kTile128x128;
+  if (!strcmp(v, "64x64")) return kq::kTile64x64;
+  return -1;
+}
+
+bool env_log() {
+  const char* v = getenv("KQ_LOG");
+  return v && v[0] && strcmp(v, "0");
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Checks that the current device is gfx950 (cached per device).
+kq_status check_device(const char* op) {
+  static int cache[64];  // 0 unknown, 1 gfx950, 2 other
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(KQ_ERR_NO_DEVICE, "[%s] no HIP device", op);
+  if (dev < 64 && cache[dev] == 1) return KQ_SUCCESS;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+    return fail(KQ_ERR_NO_DEVICE, "[%s] cannot query device %d", op, dev);
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) cache[dev] = ok ? 1 : 2;
+  if (!ok) return fail(KQ_ERR_NO_DEVICE, "[%s] device %d is %s, not gfx950", op, dev, prop.gcnArchName);
+  return KQ_SUCCESS;
+}
+
+kq_status check_launch(const char* op) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KQ_ERR_LAUNCH, "[%s] launch failed: %s", op, hipGetErrorString(e));
+  return KQ_SUCCESS;
+}
+
+int out_kind(kq_dtype d) {
+  return d == KQ_DTYPE_F32 ? kq::kOutF32 : d == KQ_DTYPE_BF16 ? kq::kOutBF16 : kq::kOutI32;
+}
+
+const char* dtype_name(kq_dtype d) {
+  return d == KQ_DTYPE_F32 ? "f32" : d == KQ_DTYPE_BF16 ? "bf16" : "i32";
+}
+
+// Launches the GEMM/GEMV stage of a validated linear on quantized
+// activations (codes, scales and, for int4 weights, group sums).
+kq_status launch_main(const char* op, int force, kq_wformat fmt, const int8_t* codes,
+                      const float* sx, const int32_t* gsum, int64_t M, int64_t K, int64_t N,
+                      const void* wq, const void* scale, const void* gbias, const float* bias,
+                      void* y, kq_dtype y_dtype, hipStream_t s, const char* kq_name) {
+  const kq_route_info r = kq::choose_route(M, N, K, fmt, force, env_tile());
+  const int out = out_kind(y_dtype);
+  const char* k2;
+  if (r.kind == KQ_ROUTE_GEMV) {
+    k2 = kq::launch_gemv(fmt == KQ_W4_AFFINE_G64, codes, sx, gsum, wq, scale, gbias, bias, y, out,
+                         (int)M, (int)N, (int)K, s);
+  } else {
+    int tile = 0;
+    for (int t = 0; t <= kq::kTile64x64; ++t)
+      if (kq::tile_shape(t).bm == r.tile_m && kq::tile_shape(t).bn == r.tile_n) tile = t;
+    if (fmt == KQ_W8_PER_CHANNEL)
+      k2 = kq::launch_gemm_w8a8(tile, codes, sx, reinterpret_cast<const int8_t*>(wq),
+                                reinterpret_cast<const float*>(scale), bias, y, out, (int)M,
+                                (int)N, (int)K, s);
+    else
+      k2 = kq::launch_gemm_w4a8(tile, codes, sx, gsum, reinterpret_cast<const uint8_t*>(wq),
+                                scale, gbias, bias, y, out, (int)M, (int)N, (int)K, s);
+  }
+  const kq_status st = check_launch(op);
+  if (st != KQ_SUCCESS) return st;
+  if (env_log())
+    fprintf(stderr, "[kq] %s M=%lld N=%lld K=%lld out=%s route=%s kernels=%s%s%s tile=%dx%d grid=%lld\n",
+            op, (long long)M, (long long)N, (long long)K, dtype_name(y_dtype),
+            r.kind == KQ_ROUTE_GEMV ? "gemv" : "gemm", kq_name ? kq_name : "",
+            kq_name ? "," : "", k2, r.tile_m, r.tile_n, (long long)r.grid);
+  return KQ_SUCCESS;
+}
+
+// Checks shared by every linear entry point (scalars, pointers, alignment).
+kq_status check_linear_args(const char* op, int force, kq_wformat fmt, int64_t M, int64_t K,
+                            int64_t N, kq_dtype y_dtype, const void* x, const void* wq,
+                            const void* scale, const void* gbias, const void* y) {
+  std::string err;
+  kq_status st = kq::validate_linear(op, M, K, N, fmt, y_dtype, err);
+  if (st != KQ_SUCCESS) return fail(st, "%s", err.c_str());
+  if (M == 0 || N == 0) return KQ_SUCCESS;
+  if (!x || !wq || !scale || !y) return fail(KQ_ERR_INVALID_VALUE, "[%s] null tensor pointer", op);
+  if (fmt == KQ_W4_AFFINE_G64 && !gbias)
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] int4 weights need the group offsets", op);
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(y))
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] x, weights, y and workspace must be 16-byte aligned", op);
+  if (force == 2 && M > KQ_GEMV_MAX_M)
+    return fail(KQ_ERR_UNSUPPORTED, "[%s] M=%lld exceeds the GEMV limit %d", op, (long long)M,
+                KQ_GEMV_MAX_M);
+  return KQ_SUCCESS;
+}
+
+// Shared body of the three linear entry points that quantize x themselves.
+kq_status run_linear(const char* op, int force, kq_wformat fmt, const void* x, int64_t M,
+                     int64_t K, int64_t N, const void* wq, const void* scale, const void* gbias,
+                     const float* bias, void* y, kq_dtype y_dtype, void* ws, size_t ws_bytes,
+                     void* stream) {
+  kq_status st = check_linear_args(op, force, fmt, M, K, N, y_dtype, x, wq, scale, gbias, y);
+  if (st != KQ_SUCCESS || M == 0 || N == 0) return st;
+  if (!aligned16(ws))
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] x, weights, y and workspace must be 16-byte aligned", op);
+  const kq::WorkspaceLayout wl = kq::workspace_layout(M, K, fmt);
+  if (!ws || ws_bytes < wl.total)
+    return fail(KQ_ERR_WORKSPACE, "[%s] workspace of %zu bytes is smaller than the %zu required", op,
+                ws_bytes, wl.total);
+  st = check_device(op);
+  if (st != KQ_SUCCESS) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* wsb = reinterpret_cast<char*>(ws);
+  int8_t* codes = reinterpret_cast<int8_t*>(wsb + wl.codes_off);
+  float* sx = reinterpret_cast<float*>(wsb + wl.scale_off);
+  int32_t* gsum = fmt == KQ_W4_AFFINE_G64 ? reinterpret_cast<int32_t*>(wsb + wl.gsum_off) : nullptr;
+  const char* kq_name = kq::launch_quant_act(reinterpret_cast<const uint16_t*>(x), M, (int)K, codes,
+                                             sx, gsum, s);
+  st = check_launch(op);
+  if (st != KQ_SUCCESS) return st;
+  return launch_main(op, force, fmt, codes, sx, gsum, M, K, N, wq, scale, gbias, bias, y, y_dtype,
+                     s, kq_name);
+}
+
+// Shared body of the entry points on pre-quantized activations.
+kq_status run_gemm(const char* op, kq_wformat fmt, const int8_t* a, const float* sx,
+                   const int32_t* gsum, int64_t M, int64_t K, int64_t N, const void* wq,
+                   const void* scale, const void* gbias, const float* bias, void* y,
+                   kq_dtype y_dtype, void* stream) {
+  const int force = env_force_route();
+  kq_status st = check_linear_args(op, force, fmt, M, K, N, y_dtype, a, wq, scale, gbias, y);
+  if (st != KQ_SUCCESS || M == 0 || N == 0) return st;
+  if (!sx || (fmt == KQ_W4_AFFINE_G64 && !gsum))
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] null scale or group-sum pointer", op);
+  st = check_device(op);
+  if (st != KQ_SUCCESS) return st;
+  return launch_main(op, force, fmt, a, sx, gsum, M, K, N, wq, scale, gbias, bias, y, y_dtype,
+                     reinterpret_cast<hipStream_t>(stream), nullptr);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kq_is_available(void) {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+  return strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+}
+
+const char* kq_last_error(void) { return g_last_error.c_str(); }
+
+size_t kq_workspace_bytes(int64_t M, int64_t K, kq_wformat fmt) {
+  return kq::workspace_layout(M, K, fmt).total;
+}
+
+kq_status kq_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt, kq_dtype y_dtype,
+                   kq_route_info* out) {
+  std::string err;
+  kq_status st = kq::validate_linear("kq_route", M, K, N, fmt, y_dtype, err);
+  if (st != KQ_SUCCESS) return fail(st, "%s", err.c_str());
+  if (!out) return fail(KQ_ERR_INVALID_VALUE, "[kq_route] null output");
+  const int force = env_force_route();
+  if (force == 2 && M > KQ_GEMV_MAX_M)
+    return fail(KQ_ERR_UNSUPPORTED, "[kq_route] M=%lld exceeds the GEMV limit %d", (long long)M,
+                KQ_GEMV_MAX_M);
+  *out = kq::choose_route(M, N, K, fmt, force, env_tile());
+  return KQ_SUCCESS;
+}
+
+kq_status kq_quantize_weights(const float* w, int64_t N, int64_t K, kq_wformat fmt, void* wq,
+                              void* scale, void* gbias, void* stream) {
+  const char* op = "kq_quantize_weights";
+  if (N < 0 || K < 0) return fail(KQ_ERR_INVALID_VALUE, "[%s] negative size", op);
+  if (fmt != KQ_W8_PER_CHANNEL && fmt != KQ_W4_AFFINE_G64)
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] unknown weight format %d", op, (int)fmt);
+  if (K == 0) return fail(KQ_ERR_UNSUPPORTED, "[%s] K must be positive", op);
+  if (K > INT32_MAX / 2) return fail(KQ_ERR_UNSUPPORTED, "[%s] K=%lld too large", op, (long long)K);
+  if (fmt == KQ_W4_AFFINE_G64 && K % 64)
+    return fail(KQ_ERR_UNSUPPORTED, "[%s] K=%lld must be a multiple of 64 for int4 weights", op,
+                (long long)K);
+  if (fmt == KQ_W8_PER_CHANNEL && gbias)
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] int8 weights take no group offsets (gbias must be NULL)", op);
+  if (N == 0) return KQ_SUCCESS;
+  if (!w || !wq || !scale || (fmt == KQ_W4_AFFINE_G64 && !gbias))
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] null tensor pointer", op);
+  if (!aligned16(w) || !aligned16(wq))
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] w and wq must be 16-byte aligned", op);
+  kq_status st = check_device(op);
+  if (st != KQ_SUCCESS) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const char* name;
+  if (fmt == KQ_W8_PER_CHANNEL)
+    name = kq::launch_quant_w8(w, N, (int)K, reinterpret_cast<int8_t*>(wq),
+                               reinterpret_cast<float*>(scale), s);
+  else
+    name = kq::launch_quant_w4(w, N, (int)K, reinterpret_cast<uint8_t*>(wq), scale, gbias, s);
+  st = check_launch(op);
+  if (st == KQ_SUCCESS && env_log())
+    fprintf(stderr, "[kq] %s N=%lld K=%lld kernel=%s\n", op, (long long)N, (long long)K, name);
+  return st;
+}
+
+kq_status kq_quantize_act(const void* x, int64_t M, int64_t K, int8_t* a, float* sx,
+                          int32_t* gsum, void* stream) {
+  const char* op = "kq_quantize_act";
+  if (M < 0 || K < 0) return fail(KQ_ERR_INVALID_VALUE, "[%s] negative size", op);
+  if (K == 0) return fail(KQ_ERR_UNSUPPORTED, "[%s] K must be positive", op);
+  if (K > INT32_MAX / 2) return fail(KQ_ERR_UNSUPPORTED, "[%s] K=%lld too large", op, (long long)K);
+  if (gsum && K % 64)
+    return fail(KQ_ERR_UNSUPPORTED, "[%s] group sums need K %% 64 == 0 (K=%lld)", op, (long long)K);
+  if (M == 0) return KQ_SUCCESS;
+  if (!x || !a || !sx) return fail(KQ_ERR_INVALID_VALUE, "[%s] null tensor pointer", op);
+  if (K % 8 == 0 && (!aligned16(x) || ((uintptr_t)a & 7)))
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] x must be 16-byte and a 8-byte aligned", op);
+  kq_status st = check_device(op);
+  if (st != KQ_SUCCESS) return st;
+  const char* name = kq::launch_quant_act(reinterpret_cast<const uint16_t*>(x), M, (int)K, a, sx,
+                                          gsum, reinterpret_cast<hipStream_t>(stream));
+  st = check_launch(op);
+  if (st == KQ_SUCCESS && env_log())
+    fprintf(stderr, "[kq] %s M=%lld K=%lld kernel=%s\n", op, (long long)M, (long long)K, name);
+  return st;
+}
+
+kq_status kq_w8a8_linear(const void* x, int64_t M, int64_t K, int64_t N, const int8_t* wq,
+                         const float* sw, const float* bias, void* y, kq_dtype y_dtype, void* ws,
+                         size_t ws_bytes, void* stream) {
+  return run_linear("kq_w8a8_linear", env_force_route(), KQ_W8_PER_CHANNEL, x, M, K, N, wq, sw,
+                    nullptr, bias, y, y_dtype, ws, ws_bytes, stream);
+}
+
+kq_status kq_w4a8_linear(const void* x, int64_t M, int64_t K, int64_t N, const uint8_t* wq4,
+                         const void* gscale, const void* gbias, const float* bias, void* y,
+                         kq_dtype y_dtype, void* ws, size_t ws_bytes, void* stream) {
+  return run_linear("kq_w4a8_linear", env_force_route(), KQ_W4_AFFINE_G64, x, M, K, N, wq4, gscale,
+                    gbias, bias, y, y_dtype, ws, ws_bytes, stream);
+}
+
+kq_status kq_w8a8_gemm(const int8_t* a, const float* sx, int64_t M, int64_t K, int64_t N,
+                       const int8_t* wq, const float* sw, const float* bias, void* y,
+                       kq_dtype y_dtype, void* stream) {
+  return run_gemm("kq_w8a8_gemm", KQ_W8_PER_CHANNEL, a, sx, nullptr, M, K, N, wq, sw, nullptr, bias,
+                  y, y_dtype, stream);
+}
+
+kq_status kq_w4a8_gemm(const int8_t* a, const float* sx, const int32_t* gsum, int64_t M, int64_t K,
+                       int64_t N, const uint8_t* wq4, const void* gscale, const void* gbias,
+                       const float* bias, void* y, kq_dtype y_dtype, void* stream) {
+  return run_gemm("kq_w4a8_gemm", KQ_W4_AFFINE_G64, a, sx, gsum, M, K, N, wq4, gscale, gbias, bias,
+                  y, y_dtype, stream);
+}
+
+kq_status kq_gemv_small_m(kq_wformat fmt, const void* x, int64_t M, int64_t K, int64_t N,
+                          const void* wq, const void* scale, const void* gbias, const float* bias,
+                          void* y, kq_dtype y_dtype, void* ws, size_t ws_bytes, void* stream) {
+  const char* op = "kq_gemv_small_m";
+  if (M > KQ_GEMV_MAX_M)
+    return fail(KQ_ERR_UNSUPPORTED, "[%s] M=%lld exceeds the GEMV limit %d", op, (long long)M,
+                KQ_GEMV_MAX_M);
+  if (fmt == KQ_W8_PER_CHANNEL && gbias)
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] int8 weights take no group offsets (gbias must be NULL)", op);
+  return run_linear(op, 2, fmt, x, M, K, N, wq, scale, gbias, bias, y, y_dtype, ws, ws_bytes,
+                    stream);
+}
+
+}  // extern "C"

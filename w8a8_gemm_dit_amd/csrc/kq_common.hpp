@@ -1,0 +1,79 @@
+// Device-side helpers shared by the libkq kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+// bf16 bit pattern -> fp32 (exact).
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float v) {
+  uint32_t u = __float_as_uint(v);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two fp32 -> packed bf16x2 (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+}
+
+// Wave-wide reductions over all 64 lanes (result in every lane).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fminf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// int8 code of one value: clamp(rint(v * inv), -127, 127).  The product is a
+// single IEEE multiply (no contraction possible), rintf is round-half-even.
+__device__ __forceinline__ int quant_code(float v, float inv) {
+  float t = rintf(v * inv);
+  t = fminf(fmaxf(t, -127.0f), 127.0f);
+  return (int)t;
+}
+
+// Pack four int8 codes into one dword (byte i = code i).
+__device__ __forceinline__ uint32_t pack4_i8(int c0, int c1, int c2, int c3) {
+  return (uint32_t)(c0 & 0xFF) | ((uint32_t)(c1 & 0xFF) << 8) |
+         ((uint32_t)(c2 & 0xFF) << 16) | ((uint32_t)(c3 & 0xFF) << 24);
+}
+
+// Unpack 8 int4 codes (one dword, low nibble of byte j = code 2j, high
+// nibble = code 2j+1) into 8 int8 codes in k order, as two dwords.
+__device__ __forceinline__ void unpack8_u4(uint32_t d, uint32_t& lo4, uint32_t& hi4) {
+  const uint32_t lo = d & 0x0F0F0F0Fu;          // codes 0,2,4,6
+  const uint32_t hi = (d >> 4) & 0x0F0F0F0Fu;   // codes 1,3,5,7
+  // v_perm_b32: bytes 0-3 select from the second operand, 4-7 from the first.
+  lo4 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // codes 0,1,2,3
+  hi4 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // codes 4,5,6,7
+}
+
+// Map a linear workgroup id onto a tile id so that the workgroups one XCD
+// runs (ids congruent mod 8 are dispatched to the same XCD) get a
+// contiguous range of tiles, which share operand panels in that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  constexpr int kXcds = 8;
+  if (nblocks % kXcds != 0) return bid;
+  const int per = nblocks / kXcds;
+  return (bid % kXcds) * per + bid / kXcds;
+}
+
+}  // namespace kq

@@ -1,0 +1,38 @@
+// Host-side launchers of the libkq kernels (internal interface between the
+// C ABI in kq_api.cpp and the kernel translation units).  Each launcher
+// enqueues on `s` without synchronizing and returns the kernel's name (for
+// the KQ_LOG route log); launch errors are read by the caller with
+// hipGetLastError.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kq {
+
+enum OutKind : int { kOutF32 = 0, kOutBF16 = 1, kOutI32 = 2 };
+
+const char* launch_quant_act(const uint16_t* x, int64_t M, int K, int8_t* a, float* sx,
+                             int32_t* gsum, hipStream_t s);
+const char* launch_quant_w8(const float* w, int64_t N, int K, int8_t* q, float* sw,
+                            hipStream_t s);
+const char* launch_quant_w4(const float* w, int64_t N, int K, uint8_t* q4, void* gs, void* gb,
+                            hipStream_t s);
+
+// W8A8 GEMM on quantized activations: y = sx*sw*(a . q^T) + bias.
+const char* launch_gemm_w8a8(int tile, const int8_t* a, const float* sx, const int8_t* q,
+                             const float* sw, const float* bias, void* y, int out, int M,
+                             int N, int K, hipStream_t s);
+
+// W4A8 GEMM: y = sx * sum_g (gs*P + gb*A) + bias (or P per group for I32).
+const char* launch_gemm_w4a8(int tile, const int8_t* a, const float* sx, const int32_t* gsum,
+                             const uint8_t* q4, const void* gs, const void* gb,
+                             const float* bias, void* y, int out, int M, int N, int K,
+                             hipStream_t s);
+
+// GEMV for 1 <= M <= 16 (w4: q is packed int4 with gs/gb; w8: q int8, gs = fp32 [N]).
+const char* launch_gemv(bool w4, const int8_t* a, const float* sx, const int32_t* gsum,
+                        const void* q, const void* gs, const void* gb, const float* bias,
+                        void* y, int out, int M, int N, int K, hipStream_t s);
+
+}  // namespace kq

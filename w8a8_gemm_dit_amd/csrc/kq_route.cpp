@@ -1,0 +1,129 @@
+// Argument validation and route selection (pure host code, no HIP).
+//
+// The envelope follows MLX pull request 4722, "Selector rules" (2-D [N,K]
+// weights, K % 64 == 0, K/64 <= 1024, non-batched), without its M >= 64
+// gate, which the pull request calls a coverage choice; M <= 16 takes the
+// GEMV ("qlip-mlx" README, w4a8_linear bullet).  The decision is one tested
+// function (mlx-kquant pull request 89 commit list).
+#include "kq_route.hpp"
+
+#include <cstdio>
+
+namespace kq {
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+TileShape tile_shape(int32_t tile) {
+  switch (tile) {
+    case kTile256x256: return {256, 256, 256};
+    case kTile256x128: return {256, 128, 256};
+    case kTile128x128: return {128, 128, 256};
+    default: return {64, 64, 256};
+  }
+}
+
+kq_status validate_linear(const char* op, int64_t M, int64_t K, int64_t N,
+                          kq_wformat fmt, kq_dtype y_dtype, std::string& err) {
+  char buf[256];
+  if (M < 0 || N < 0 || K < 0) {
+    snprintf(buf, sizeof buf, "[%s] negative size (M=%lld, N=%lld, K=%lld)", op,
+             (long long)M, (long long)N, (long long)K);
+    err = buf;
+    return KQ_ERR_INVALID_VALUE;
+  }
+  if (fmt != KQ_W8_PER_CHANNEL && fmt != KQ_W4_AFFINE_G64) {
+    snprintf(buf, sizeof buf, "[%s] unknown weight format %d", op, (int)fmt);
+    err = buf;
+    return KQ_ERR_INVALID_VALUE;
+  }
+  if (y_dtype != KQ_DTYPE_F32 && y_dtype != KQ_DTYPE_BF16 && y_dtype != KQ_DTYPE_I32) {
+    snprintf(buf, sizeof buf, "[%s] unknown output dtype %d", op, (int)y_dtype);
+    err = buf;
+    return KQ_ERR_INVALID_VALUE;
+  }
+  if (K % 64 != 0 || K == 0) {
+    snprintf(buf, sizeof buf, "[%s] K=%lld must be a positive multiple of 64", op,
+             (long long)K);
+    err = buf;
+    return KQ_ERR_UNSUPPORTED;
+  }
+  if (K > KQ_MAX_K) {
+    snprintf(buf, sizeof buf, "[%s] K=%lld exceeds %d (int32 accumulator bound)", op,
+             (long long)K, KQ_MAX_K);
+    err = buf;
+    return KQ_ERR_UNSUPPORTED;
+  }
+  if (M > (int64_t)1 << 31 || N > (int64_t)1 << 30 || M * K > ((int64_t)1 << 40)) {
+    snprintf(buf, sizeof buf, "[%s] shape too large (M=%lld, N=%lld)", op,
+             (long long)M, (long long)N);
+    err = buf;
+    return KQ_ERR_UNSUPPORTED;
+  }
+  return KQ_SUCCESS;
+}
+
+kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
+                           int force, int tile_override) {
+  (void)K;
+  kq_route_info r{};
+  const bool gemv = (force == 2) ? (M <= KQ_GEMV_MAX_M)
+                    : (force == 1) ? false
+                                   : (M >= 1 && M <= KQ_GEMV_MAX_M);
+  if (gemv) {
+    r.kind = KQ_ROUTE_GEMV;
+    r.tile_m = KQ_GEMV_MAX_M;
+    r.tile_n = kGemvCols;
+    r.threads = kGemvThreads;
+    r.grid = (N + kGemvCols - 1) / kGemvCols;
+    return r;
+  }
+  int32_t tile;
+  if (tile_override >= 0 && tile_override <= kTile64x64) {
+    tile = (fmt == KQ_W4_AFFINE_G64 && tile_override == kTile256x256) ? kTile256x128 : tile_override;
+  } else {
+    // Pick the largest tile that still gives every CU (256) work; thin
+    // problems fall back to small tiles.
+    auto tiles = [&](int32_t t) {
+      TileShape s = tile_shape(t);
+      return ((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
+    };
+    // The int4 GEMM keeps fp32 accumulators plus per-group int32 products,
+    // so its largest tile is 256x128.
+    if (fmt == KQ_W8_PER_CHANNEL && tiles(kTile256x256) >= 256)
+      tile = kTile256x256;
+    else if (tiles(kTile256x128) >= 256)
+      tile = kTile256x128;
+    else if (tiles(kTile128x128) >= 256)
+      tile = kTile128x128;
+    else
+      tile = kTile64x64;
+  }
+  TileShape s = tile_shape(tile);
+  r.kind = KQ_ROUTE_GEMM;
+  r.tile_m = s.bm;
+  r.tile_n = s.bn;
+  r.threads = s.threads;
+  r.grid = ((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
+  return r;
+}
+
+WorkspaceLayout workspace_layout(int64_t M, int64_t K, kq_wformat fmt) {
+  WorkspaceLayout w{};
+  if (M <= 0 || K <= 0) return w;
+  size_t off = 0;
+  w.codes_off = off;
+  w.codes_bytes = (size_t)M * (size_t)K;
+  off = align256(off + w.codes_bytes);
+  w.scale_off = off;
+  w.scale_bytes = 4 * (size_t)M;
+  off = align256(off + w.scale_bytes);
+  if (fmt == KQ_W4_AFFINE_G64) {
+    w.gsum_off = off;
+    w.gsum_bytes = 4 * (size_t)M * (size_t)(K / 64);
+    off = align256(off + w.gsum_bytes);
+  }
+  w.total = off;
+  return w;
+}
+
+}  // namespace kq

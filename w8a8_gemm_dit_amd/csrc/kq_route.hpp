@@ -1,0 +1,51 @@
+// Argument validation and route selection for the libkq linears.
+// Pure host code with no HIP dependency, so it is testable without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "kq.h"
+
+namespace kq {
+
+// Tile configurations of the W8A8/W4A8 GEMM kernels.
+enum GemmTile : int32_t {
+  kTile256x256 = 0,  // 256 rows x 256 columns, 4 waves of 128x128
+  kTile256x128 = 1,  // 256 x 128, 4 waves of 128x64 (2x2)
+  kTile128x128 = 2,  // 128 x 128, 4 waves of 64x64
+  kTile64x64 = 3,    // 64 x 64, 4 waves of 32x32 (thin shapes)
+};
+
+struct TileShape {
+  int32_t bm, bn, threads;
+};
+
+TileShape tile_shape(int32_t tile);
+
+// Validates a linear call's scalar arguments; on failure writes the message
+// (with the "[op] " prefix) to err and returns the status.
+kq_status validate_linear(const char* op, int64_t M, int64_t K, int64_t N,
+                          kq_wformat fmt, kq_dtype y_dtype, std::string& err);
+
+// Route of a validated linear call.  force: 0 = automatic, 1 = GEMM, 2 = GEMV.
+// tile_override: -1 = automatic, else a GemmTile.
+kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
+                           int force, int tile_override);
+
+// Workspace layout of one linear call.
+struct WorkspaceLayout {
+  size_t codes_off, codes_bytes;   // int8 [M,K]
+  size_t scale_off, scale_bytes;   // fp32 [M]
+  size_t gsum_off, gsum_bytes;     // int32 [M,K/64] (int4 format only)
+  size_t total;
+};
+WorkspaceLayout workspace_layout(int64_t M, int64_t K, kq_wformat fmt);
+
+// GEMV route geometry.
+constexpr int kGemvCols = 32;     // output columns per workgroup
+constexpr int kGemvThreads = 256;
+
+}  // namespace kq

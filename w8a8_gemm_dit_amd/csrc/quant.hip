@@ -1,0 +1,259 @@
+// Quantization kernels of libkq.
+//
+// Activation rule ("qlip-mlx" README, w8a8_linear bullet: per-token
+// activation quantization inside the kernel, no calibration), applied per
+// row: amax = max |x|; inv = fp32(127/amax); codes = clamp(rint(x*inv),
+// -127, 127); scale = fp32(amax/127); rows whose 127/amax overflows become
+// zero with scale 0.  The same rule quantizes int8 weight rows ("qlip-mlx"
+// README, "Quick start": quantize_weight_int8 gives int8 codes and fp32
+// per-output-channel scales).  Int4 weights are min-max affine per 64-wide
+// K group with fp16 scale and offset (MLX pull request 4722: affine 4-bit
+// g64).  All arithmetic is IEEE fp32 with round-to-nearest-even and
+// correctly rounded division, so results are bit-exact and deterministic.
+//
+// The activation kernel is HBM-bound (2 bytes in, 1 byte out per element):
+// one wavefront per row, 16-byte coalesced loads kept in registers, a
+// wavefront max-reduction, then 8-byte code stores from the same registers.
+#include <float.h>
+
+#include "kq_common.hpp"
+#include "kq_launch.hpp"
+
+namespace kq {
+
+namespace {
+
+constexpr int kRowsPerBlock = 4;  // one wavefront per row, 4 waves per block
+
+__device__ __forceinline__ float row_inv(float amax, float& scale) {
+  const float inv = 127.0f / amax;
+  const bool ok = inv <= FLT_MAX;  // false for +inf (amax 0 or tiny)
+  scale = ok ? amax / 127.0f : 0.0f;
+  return ok ? inv : 0.0f;
+}
+
+// Quantize 8 bf16 values held in a uint4; returns 8 codes as uint2 and their sum.
+__device__ __forceinline__ uint2 quant8(const uint4 v, float inv, int& sum) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  int c[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[2 * i] = quant_code(bf16_to_f32(w[i] & 0xFFFFu), inv);
+    c[2 * i + 1] = quant_code(bf16_to_f32(w[i] >> 16), inv);
+  }
+  sum = c[0] + c[1] + c[2] + c[3] + c[4] + c[5] + c[6] + c[7];
+  return make_uint2(pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7]));
+}
+
+__device__ __forceinline__ float absmax8(const uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = fmaxf(m, fabsf(bf16_to_f32(w[i] & 0xFFFFu)));
+    m = fmaxf(m, fabsf(bf16_to_f32(w[i] >> 16)));
+  }
+  return m;
+}
+
+// Sum over the 8 aligned lanes of a group (lanes 8q..8q+7).
+__device__ __forceinline__ int group8_sum(int v) {
+  v += __shfl_xor(v, 1, kWave);
+  v += __shfl_xor(v, 2, kWave);
+  v += __shfl_xor(v, 4, kWave);
+  return v;
+}
+
+// K % 8 == 0 and K <= 512*CH: the row stays in registers (CH chunks of 8
+// values per lane; chunk c = lane + 64*j covers elements 8c..8c+7).
+template <int CH>
+__global__ __launch_bounds__(256) void quant_act_regs(
+    const uint16_t* __restrict__ x, int64_t M, int K, int8_t* __restrict__ a,
+    float* __restrict__ sx, int32_t* __restrict__ gsum) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int nch = K >> 3;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + row * (int64_t)K);
+  uint4 v[CH];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int c = lane + 64 * j;
+    v[j] = (c < nch) ? xr[c] : make_uint4(0, 0, 0, 0);
+    amax = fmaxf(amax, absmax8(v[j]));
+  }
+  amax = wave_max(amax);
+  float scale;
+  const float inv = row_inv(amax, scale);
+  if (lane == 0) sx[row] = scale;
+  uint2* ar = reinterpret_cast<uint2*>(a + row * (int64_t)K);
+  const int G = K >> 6;
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int c = lane + 64 * j;
+    int s;
+    const uint2 codes = quant8(v[j], inv, s);
+    if (c < nch) ar[c] = codes;
+    if (gsum != nullptr) {
+      s = group8_sum(s);
+      if ((lane & 7) == 0 && c < nch) gsum[row * G + (c >> 3)] = s;
+    }
+  }
+}
+
+// K % 8 == 0, any K: two passes over the row (the second hits the cache).
+__global__ __launch_bounds__(256) void quant_act_stream(
+    const uint16_t* __restrict__ x, int64_t M, int K, int8_t* __restrict__ a,
+    float* __restrict__ sx, int32_t* __restrict__ gsum) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int nch = K >> 3;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + row * (int64_t)K);
+  float amax = 0.0f;
+  for (int c = lane; c < nch; c += 64) amax = fmaxf(amax, absmax8(xr[c]));
+  amax = wave_max(amax);
+  float scale;
+  const float inv = row_inv(amax, scale);
+  if (lane == 0) sx[row] = scale;
+  uint2* ar = reinterpret_cast<uint2*>(a + row * (int64_t)K);
+  const int G = K >> 6;
+  for (int c0 = 0; c0 < nch; c0 += 64) {
+    const int c = c0 + lane;
+    int s = 0;
+    uint2 codes = make_uint2(0, 0);
+    if (c < nch) codes = quant8(xr[c], inv, s);
+    if (c < nch) ar[c] = codes;
+    if (gsum != nullptr) {
+      s = group8_sum(s);
+      if ((lane & 7) == 0 && c < nch) gsum[row * G + (c >> 3)] = s;
+    }
+  }
+}
+
+// Any K (not a multiple of 8): element-wise two-pass fallback, no group sums.
+__global__ __launch_bounds__(256) void quant_act_scalar(
+    const uint16_t* __restrict__ x, int64_t M, int K, int8_t* __restrict__ a,
+    float* __restrict__ sx) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const uint16_t* xr = x + row * (int64_t)K;
+  float amax = 0.0f;
+  for (int k = lane; k < K; k += 64) amax = fmaxf(amax, fabsf(bf16_to_f32(xr[k])));
+  amax = wave_max(amax);
+  float scale;
+  const float inv = row_inv(amax, scale);
+  if (lane == 0) sx[row] = scale;
+  int8_t* ar = a + row * (int64_t)K;
+  for (int k = lane; k < K; k += 64) ar[k] = (int8_t)quant_code(bf16_to_f32(xr[k]), inv);
+}
+
+// int8 weight rows from fp32: one wavefront per output channel.
+__global__ __launch_bounds__(256) void quant_w8_rows(const float* __restrict__ w, int64_t N,
+                                                     int K, int8_t* __restrict__ q,
+                                                     float* __restrict__ sw) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= N) return;
+  const float* wr = w + row * (int64_t)K;
+  float amax = 0.0f;
+  for (int k = lane; k < K; k += 64) amax = fmaxf(amax, fabsf(wr[k]));
+  amax = wave_max(amax);
+  float scale;
+  const float inv = row_inv(amax, scale);
+  if (lane == 0) sw[row] = scale;
+  int8_t* qr = q + row * (int64_t)K;
+  for (int k = lane; k < K; k += 64) qr[k] = (int8_t)quant_code(wr[k], inv);
+}
+
+// Affine int4 weights: one thread per (row n, 64-wide group g).
+__global__ __launch_bounds__(256) void quant_w4_groups(const float* __restrict__ w, int64_t N,
+                                                       int K, uint8_t* __restrict__ q4,
+                                                       __half* __restrict__ gs,
+                                                       __half* __restrict__ gb) {
+  const int G = K >> 6;
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= N * (int64_t)G) return;
+  const int64_t n = id / G;
+  const int g = (int)(id - n * G);
+  const float4* src = reinterpret_cast<const float4*>(w + n * (int64_t)K + 64 * g);
+  float v[64];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float4 t = src[i];
+    v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+  }
+  float lo = v[0], hi = v[0];
+#pragma unroll
+  for (int i = 1; i < 64; ++i) { lo = fminf(lo, v[i]); hi = fmaxf(hi, v[i]); }
+  const __half s = __float2half_rn((hi - lo) / 15.0f);
+  const __half b = __float2half_rn(lo);
+  gs[id] = s;
+  gb[id] = b;
+  const float sf = __half2float(s);
+  const float bf = __half2float(b);
+  const float inv = (sf != 0.0f) ? 1.0f / sf : 0.0f;
+  uint32_t out[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float t = rintf((v[8 * d + j] - bf) * inv);
+      t = fminf(fmaxf(t, 0.0f), 15.0f);
+      word |= ((uint32_t)t) << (4 * j);
+    }
+    out[d] = word;
+  }
+  uint4* dst = reinterpret_cast<uint4*>(q4 + n * (int64_t)(K / 2) + 32 * g);
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+}
+
+template <int CH>
+void launch_regs(const uint16_t* x, int64_t M, int K, int8_t* a, float* sx, int32_t* gsum,
+                 hipStream_t s, dim3 grid) {
+  hipLaunchKernelGGL(quant_act_regs<CH>, grid, dim3(256), 0, s, x, M, K, a, sx, gsum);
+}
+
+}  // namespace
+
+const char* launch_quant_act(const uint16_t* x, int64_t M, int K, int8_t* a, float* sx,
+                             int32_t* gsum, hipStream_t s) {
+  const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock));
+  if (K % 8 != 0) {
+    hipLaunchKernelGGL(quant_act_scalar, grid, dim3(256), 0, s, x, M, K, a, sx);
+    return "quant_act_scalar";
+  }
+  const int need = (K / 8 + 63) / 64;  // chunks per lane
+  if (need <= 1) { launch_regs<1>(x, M, K, a, sx, gsum, s, grid); return "quant_act_regs1"; }
+  if (need <= 2) { launch_regs<2>(x, M, K, a, sx, gsum, s, grid); return "quant_act_regs2"; }
+  if (need <= 4) { launch_regs<4>(x, M, K, a, sx, gsum, s, grid); return "quant_act_regs4"; }
+  if (need <= 6) { launch_regs<6>(x, M, K, a, sx, gsum, s, grid); return "quant_act_regs6"; }
+  if (need <= 8) { launch_regs<8>(x, M, K, a, sx, gsum, s, grid); return "quant_act_regs8"; }
+  if (need <= 12) { launch_regs<12>(x, M, K, a, sx, gsum, s, grid); return "quant_act_regs12"; }
+  if (need <= 16) { launch_regs<16>(x, M, K, a, sx, gsum, s, grid); return "quant_act_regs16"; }
+  if (need <= 24) { launch_regs<24>(x, M, K, a, sx, gsum, s, grid); return "quant_act_regs24"; }
+  hipLaunchKernelGGL(quant_act_stream, grid, dim3(256), 0, s, x, M, K, a, sx, gsum);
+  return "quant_act_stream";
+}
+
+const char* launch_quant_w8(const float* w, int64_t N, int K, int8_t* q, float* sw,
+                            hipStream_t s) {
+  const dim3 grid((unsigned)((N + kRowsPerBlock - 1) / kRowsPerBlock));
+  hipLaunchKernelGGL(quant_w8_rows, grid, dim3(256), 0, s, w, N, K, q, sw);
+  return "quant_w8_rows";
+}
+
+const char* launch_quant_w4(const float* w, int64_t N, int K, uint8_t* q4, void* gs, void* gb,
+                            hipStream_t s) {
+  const int64_t items = N * (int64_t)(K / 64);
+  const dim3 grid((unsigned)((items + 255) / 256));
+  hipLaunchKernelGGL(quant_w4_groups, grid, dim3(256), 0, s, w, N, K, q4,
+                     reinterpret_cast<__half*>(gs), reinterpret_cast<__half*>(gb));
+  return "quant_w4_groups";
+}
+
+}  // namespace kq
