@@ -22,6 +22,7 @@ from .kq_oracle import (  # noqa: F401
     w4a8_group_acc,
     w8a8_linear_exact,
     w4a8_linear_exact,
+    linear_dequantized_fp64,
     w8a8_magnitude,
     w4a8_magnitude,
     round_f32,

@@ -176,23 +176,53 @@ def w4a8_group_acc(a, q) -> np.ndarray:
 
 
 # ------------------------------------------------------------------ linears
+# y = x_hat . w_hat^T + bias for the dequantized operands.  The scales are
+# factored out of the exact integer sums (the same algebra), so the float64
+# result is within a few roundings (2^-52 relative) of the exact value; a
+# float64 product of the dequantized operands would instead carry an error
+# proportional to sum |x_hat||w_hat|, which need not vanish where the exact
+# result is 0.
 def w8a8_linear_exact(x_bf16_bits, q8, sw, bias=None) -> np.ndarray:
-    """y = x_hat . w_hat^T + bias in float64 for int8 weights, where
-    x_hat = sx * a from the per-token quantizer and w_hat = sw * q8."""
+    """y[m,n] = sx[m] * sw[n] * acc[m,n] + bias[n] in float64, with
+    acc = sum_k a*q8 exact (x_hat = sx*a, w_hat = sw*q8)."""
     a, sx, _ = quantize_act(x_bf16_bits, with_group_sums=False)
-    xh = np.asarray(sx, np.float64)[:, None] * a.astype(np.float64)
-    y = xh @ dequant_w8(q8, sw).T
+    acc = w8a8_acc(a, q8).astype(np.float64)
+    s = np.asarray(sx, np.float64)[:, None] * np.asarray(sw, np.float64)[None, :]  # exact
+    y = s * acc
     if bias is not None:
         y = y + np.asarray(bias, np.float64)[None, :]
     return y
 
 
 def w4a8_linear_exact(x_bf16_bits, q, gs, gb, bias=None) -> np.ndarray:
-    """y = x_hat . w_hat^T + bias in float64 for affine int4 weights, where
-    w_hat = gs * q + gb per 64-group (q unpacked codes [N,K])."""
+    """y[m,n] = sx[m] * sum_g (gs[n,g]*P[g,m,n] + gb[n,g]*A[m,g]) + bias[n]
+    in float64, with P and A exact integers (x_hat = sx*a, w_hat = gs*q + gb
+    per 64-group: sum_k x_hat*w_hat = sx * sum_g (gs*P + gb*A)).  Each
+    gs*P and gb*A is exact in float64."""
+    a, sx, A = quantize_act(x_bf16_bits, with_group_sums=True)
+    if A is None:
+        raise ValueError("K must be a multiple of 64")
+    a64 = a.astype(np.float64)
+    q64 = np.asarray(q, np.float64)
+    gs64 = np.asarray(gs, np.float64)
+    gb64 = np.asarray(gb, np.float64)
+    s = np.zeros((a.shape[0], q64.shape[0]))
+    for g in range(a.shape[1] // 64):
+        sl = slice(64 * g, 64 * g + 64)
+        P = a64[:, sl] @ q64[:, sl].T                         # exact integers
+        s += gs64[None, :, g] * P + gb64[None, :, g] * A[:, g, None].astype(np.float64)
+    y = np.asarray(sx, np.float64)[:, None] * s
+    if bias is not None:
+        y = y + np.asarray(bias, np.float64)[None, :]
+    return y
+
+
+def linear_dequantized_fp64(x_bf16_bits, w_hat, bias=None) -> np.ndarray:
+    """The plain definition: float64 product of the dequantized operands,
+    x_hat . w_hat^T + bias (used to cross-check the factored forms)."""
     a, sx, _ = quantize_act(x_bf16_bits, with_group_sums=False)
     xh = np.asarray(sx, np.float64)[:, None] * a.astype(np.float64)
-    y = xh @ dequant_w4(q, gs, gb).T
+    y = xh @ np.asarray(w_hat, np.float64).T
     if bias is not None:
         y = y + np.asarray(bias, np.float64)[None, :]
     return y
@@ -213,11 +243,15 @@ def w4a8_magnitude(x_bf16_bits, q, gs, gb, bias=None) -> np.ndarray:
     """T[m,n] = sx * sum_g (|gs*P| + |gb*A|) + |bias|: the scale against which
     an fp32 per-group evaluation of the int4 epilogue is accurate."""
     a, sx, A = quantize_act(x_bf16_bits, with_group_sums=True)
-    P = w4a8_group_acc(a, q).astype(np.float64)              # [G,M,N]
-    gs64 = np.asarray(gs, np.float64).T[:, None, :]          # [G,1,N]
-    gb64 = np.asarray(gb, np.float64).T[:, None, :]
-    A64 = A.astype(np.float64).T[:, :, None]                 # [G,M,1]
-    s = np.sum(np.abs(gs64 * P) + np.abs(gb64 * A64), axis=0)
+    a64 = a.astype(np.float64)
+    q64 = np.asarray(q, np.float64)
+    gs64 = np.asarray(gs, np.float64)
+    gb64 = np.asarray(gb, np.float64)
+    s = np.zeros((a.shape[0], q64.shape[0]))
+    for g in range(a.shape[1] // 64):
+        sl = slice(64 * g, 64 * g + 64)
+        P = a64[:, sl] @ q64[:, sl].T
+        s += np.abs(gs64[None, :, g] * P) + np.abs(gb64[None, :, g] * A[:, g, None].astype(np.float64))
     t = np.asarray(sx, np.float64)[:, None] * s
     if bias is not None:
         t = t + np.abs(np.asarray(bias, np.float64))[None, :]

@@ -290,6 +290,43 @@ def test_quantization_error_bound_against_fp64_gemm(fmt):
     assert rel < (0.02 if fmt == "w8" else 0.1)
 
 
+@pytest.mark.parametrize("fmt", ["w8", "w4"])
+def test_factored_forms_match_plain_dequantized_product(fmt):
+    # The oracle factors the scales out of exact integer sums; the plain
+    # definition (float64 product of dequantized operands) must agree to
+    # within that product's own rounding, K * 2^-52 * sum |x_hat||w_hat|.
+    m, k, n = 24, 448, 40
+    xb = synth.random_bf16((m, k), 29, dist="student_t4")
+    w = synth.random_f32((n, k), 30, scale=0.02)
+    bias = synth.random_f32((n,), 31, scale=0.1)
+    a, sx, _ = oracle.quantize_act(xb)
+    xh = sx.astype(np.float64)[:, None] * a
+    if fmt == "w8":
+        q8, sw = oracle.quantize_w8(w)
+        wh = oracle.dequant_w8(q8, sw)
+        y = oracle.w8a8_linear_exact(xb, q8, sw, bias)
+    else:
+        _, gs, gb, q = oracle.quantize_w4(w)
+        wh = oracle.dequant_w4(q, gs, gb)
+        y = oracle.w4a8_linear_exact(xb, q, gs, gb, bias)
+    plain = oracle.linear_dequantized_fp64(xb, wh, bias)
+    bound = k * 2.0 ** -52 * (np.abs(xh) @ np.abs(wh).T + np.abs(bias))
+    assert np.all(np.abs(y - plain) <= bound)
+
+
+def test_exact_zero_results_are_zero():
+    # rows whose int8 products cancel exactly give exactly the bias
+    k = 128
+    x = np.zeros((1, k), np.float32)
+    x[0, 0], x[0, 1] = 1.0, -1.0
+    w = np.zeros((2, k), np.float32)
+    w[:, 0] = w[:, 1] = 0.5
+    w[1, 5] = 1.0
+    q8, sw = oracle.quantize_w8(w)
+    y = oracle.w8a8_linear_exact(_bits(x), q8, sw)
+    assert np.all(y == 0.0)
+
+
 def test_transposed_weight_is_caught():
     # a plausible slip (using w instead of w^T) must break the fp64 check
     m, k = 16, 64
