@@ -50,7 +50,7 @@ def test_workspace_layout():
     (1, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 32), 432),
     (16, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 32), 432),
     (17, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemm", None, None),
-    (4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 128), 384),
+    (4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 192), 256),
     (16384, 12288, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 256), 3072),
     (2048, 12288, 4096, kq.KQ_W4_AFFINE_G64, "gemm", (256, 128), 768),
     (2048, 4096, 12288, kq.KQ_W4_AFFINE_G64, "gemm", (256, 128), 256),

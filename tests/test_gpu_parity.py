@@ -86,8 +86,10 @@ def _problem(M, K, N, seed, dist="normal", with_bias=True):
     return xb, w, b
 
 
+# K covers both GEMM loop variants (K % 256 == 0, and 1-3 trailing 64-steps)
 SHAPES = [(64, 512, 512), (1, 64, 16), (17, 64, 33), (100, 192, 200), (257, 128, 129),
-          (300, 256, 48), (64, 1024, 1000), (513, 320, 260)]
+          (300, 256, 48), (64, 1024, 1000), (513, 320, 260), (300, 448, 200), (130, 576, 72),
+          (70, 640, 70)]
 TILES = [None, "256x256", "256x128", "128x128", "64x64"]
 
 

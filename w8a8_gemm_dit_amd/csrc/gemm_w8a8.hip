@@ -6,22 +6,33 @@
 // transposed weights).
 //
 // gfx950 design:
-//   - a workgroup computes a BM x BN output tile with 4 wavefronts in a 2x2
-//     grid; each wavefront owns a (BM/2) x (BN/2) tile of int32
-//     accumulators built from v_mfma_i32_16x16x64_i8 (16x16 outputs, K=64
-//     per instruction);
-//   - the weights are the MFMA "A" operand and the activations the "B"
-//     operand, so each lane ends with 4 consecutive output columns of one
-//     row (one 8- or 16-byte store per 16x16 tile);
-//   - K advances 64 bytes per stage; both operand tiles are staged in LDS,
-//     double buffered, rows of 64 bytes with the 16-byte chunk index XORed
-//     with (row/4)%4 so that the 16 lanes of each ds_read_b128 phase hit 16
-//     distinct bank groups;
+//   - a workgroup of 4 wavefronts (2x2) computes a BM x BN output tile; each
+//     wavefront owns (BM/2) x (BN/2) int32 accumulators built from
+//     v_mfma_i32_16x16x64_i8 (16x16 outputs, K = 64 per instruction);
+//   - K advances 64 bytes per step.  Operand tiles move global -> LDS with
+//     buffer_load_dwordx4 ... lds (no staging registers): 64 lanes write
+//     1 KB of LDS per instruction, each lane fetching the global 16-byte
+//     chunk that belongs at its LDS slot, so the tile lands with 64-byte
+//     rows whose 16-byte chunk index is XORed with (row/4)%4 and every
+//     16-lane phase of the fragment ds_read_b128 hits 16 distinct banks;
+//   - a 4-slot LDS ring keeps 3 steps of loads in flight, and fragments are
+//     software-pipelined: step k reads step k+1's fragments while its MFMAs
+//     run on step k's, then refills the slot step k was read from.  Each
+//     step costs one s_waitcnt of known depth and one barrier without a
+//     memory fence.  Each ring slot is its own LDS array (the compiler
+//     tracks the asynchronous LDS writes per array, so reads of one slot
+//     never wait for loads landing in another), the K loop is unrolled by
+//     4, and scheduling barriers between steps keep the accumulators in
+//     place in AGPRs;
+//   - no data-dependent branches: buffer descriptors are rebased per
+//     workgroup so rows past M or N read as zero, and loads past the last
+//     K step re-load the final slice into slots that are never read;
+//   - the weights are the MFMA A operand and the activations the B operand,
+//     so each lane ends with 4 consecutive output columns of one row;
 //   - workgroup ids are remapped so each XCD (ids congruent mod 8) works on
-//     a contiguous block of tiles, keeping operand panels in its own L2;
-//   - the epilogue converts the accumulator to fp32, multiplies by
-//     sx[m]*sw[n], adds the bias with one fma and rounds once to the output
-//     type (fp32, or bf16 round-to-nearest-even).
+//     a contiguous block of tiles that share operand panels in its L2;
+//   - epilogue: fp32 acc * (sx[m]*sw[n]) + bias[n] with one fma, rounded
+//     once to fp32 or bf16 (round-to-nearest-even).
 #include "kq_common.hpp"
 #include "kq_launch.hpp"
 #include "kq_route.hpp"
@@ -33,54 +44,93 @@ namespace {
 template <int BM, int BN>
 struct Cfg {
   static constexpr int kThreads = 256;
-  static constexpr int kWavesM = 2, kWavesN = 2;
-  static constexpr int kWTM = BM / kWavesM;  // wave tile: rows (m)
-  static constexpr int kWTN = BN / kWavesN;  // wave tile: columns (n)
+  static constexpr int kWTM = BM / 2;  // wave tile rows (m)
+  static constexpr int kWTN = BN / 2;  // wave tile columns (n)
   static constexpr int kTM = kWTM / 16;
   static constexpr int kTN = kWTN / 16;
-  static constexpr int kChA = BM * 4;  // 16-byte chunks of one stage
-  static constexpr int kChB = BN * 4;
-  static constexpr int kLdA = (kChA + kThreads - 1) / kThreads;
-  static constexpr int kLdB = (kChB + kThreads - 1) / kThreads;
+  static constexpr int kRows = BM + BN;            // LDS rows per step (A rows, then W rows)
+  static constexpr int kSlots = kRows * 4;         // 16-byte slots per step
+  static constexpr int kLPW = kRows / 64;          // 1 KB DMA blocks per wave per step
+  static_assert(kRows % 64 == 0 && BM % 64 == 0 && BN % 32 == 0, "tile shape");
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 2) & 3)); }
+// LDS row swizzle: the 16-byte chunk index of row r is XORed with
+// ((r/2)%4) ^ ((r/8)%2).  A fragment read (16 consecutive rows, one chunk)
+// then touches 16 distinct 16-byte bank groups per 16 lanes and 8 distinct
+// ones per 8 lanes, so it is conflict-free whether the LDS serves 8 or 16
+// lanes of a ds_read_b128 per clock.  The value depends on r % 16 only.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+
+__device__ __forceinline__ int slot_of(int row, int chunk) { return row * 4 + (chunk ^ swz(row)); }
+
+// s_waitcnt with vmcnt = N (compile-time) and lgkmcnt = 0 (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt bits 6:4 left at
+// "no wait", lgkmcnt bits 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0 << 8));
+}
+
+// Workgroup barrier without a memory fence (a fence would wait for the
+// loads still in flight); the empty asm statements keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Instruction interleave of one K step: NV groups of [MFMA x a, DS read x b,
+// MFMA x a, VMEM x 1], then the leftovers, so the MFMA pipe stays busy while
+// the fragment reads and the LDS DMA loads issue (sched_group_barrier mask
+// bits: 0x008 MFMA, 0x100 DS read, 0x020 VMEM read).
+template <int NM, int ND, int NV>
+__device__ __forceinline__ void interleave_step() {
+  constexpr int a = NM / (2 * NV);
+  constexpr int b = ND / NV;
+#pragma unroll
+  for (int g = 0; g < NV; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x008, a, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, b, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, a, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, ND - b * NV, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, NM - 2 * a * NV, 0);
+}
 
 template <int OUT>
-__device__ __forceinline__ void store_out(void* y, int64_t idx, const float v[4], const int32_t iv[4],
-                                          int valid, bool vec_ok) {
+__device__ __forceinline__ void store4(void* y, int64_t idx, const float v[4], const int32_t iv[4],
+                                       int valid, bool vec_ok) {
   if (OUT == kOutI32) {
     int32_t* p = reinterpret_cast<int32_t*>(y) + idx;
-    if (vec_ok && valid == 4) {
-      *reinterpret_cast<int4*>(p) = make_int4(iv[0], iv[1], iv[2], iv[3]);
-    } else {
-      for (int i = 0; i < valid; ++i) p[i] = iv[i];
-    }
+    if (vec_ok && valid == 4) *reinterpret_cast<int4*>(p) = make_int4(iv[0], iv[1], iv[2], iv[3]);
+    else for (int i = 0; i < valid; ++i) p[i] = iv[i];
   } else if (OUT == kOutF32) {
     float* p = reinterpret_cast<float*>(y) + idx;
-    if (vec_ok && valid == 4) {
-      *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-    } else {
-      for (int i = 0; i < valid; ++i) p[i] = v[i];
-    }
+    if (vec_ok && valid == 4) *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    else for (int i = 0; i < valid; ++i) p[i] = v[i];
   } else {
     uint16_t* p = reinterpret_cast<uint16_t*>(y) + idx;
-    if (vec_ok && valid == 4) {
+    if (vec_ok && valid == 4)
       *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-    } else {
-      for (int i = 0; i < valid; ++i) p[i] = (uint16_t)f32_to_bf16_rne(v[i]);
-    }
+    else for (int i = 0; i < valid; ++i) p[i] = (uint16_t)f32_to_bf16_rne(v[i]);
   }
 }
 
-template <int BM, int BN, int OUT>
+// REM: K % 256 != 0, so up to 3 K steps follow the 4-step loop.  The
+// conditional tail makes the register allocator copy accumulators at the
+// loop back-edge, so it is compiled only into the variant that needs it.
+template <int BM, int BN, int OUT, bool REM>
 __global__ __launch_bounds__(256) void gemm_w8a8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int8_t* __restrict__ W,
     const float* __restrict__ sw, const float* __restrict__ bias, void* __restrict__ y, int M,
     int N, int K) {
   using C = Cfg<BM, BN>;
-  __shared__ int4 lds_a[2][C::kChA];
-  __shared__ int4 lds_b[2][C::kChB];
+  __shared__ int4 lds0[C::kSlots], lds1[C::kSlots], lds2[C::kSlots], lds3[C::kSlots];
 
   const int tiles_n = (N + BN - 1) / BN;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
@@ -88,31 +138,36 @@ __global__ __launch_bounds__(256) void gemm_w8a8_kernel(
   const int n0 = (tile % tiles_n) * BN;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave % C::kWavesM;
-  const int wn = wave / C::kWavesM;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA bases stay scalar
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
 
-  // Global source of each 16-byte chunk this thread stages (rows past the
-  // edge re-read the last row; their results are never stored).
-  const int8_t* src_a[C::kLdA];
-  const int8_t* src_b[C::kLdB];
-  int dst_a[C::kLdA], dst_b[C::kLdB];
+  // Buffer descriptors rebased on this tile's first row: rows past the
+  // matrix edge fall outside num_records and read as zero.
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(A + (int64_t)m0 * K), 0, min(BM, M - m0) * K, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(W + (int64_t)n0 * K), 0, min(BN, N - n0) * K, 0x00020000);
+
+  // DMA plan: wave w moves 1 KB blocks b = w + 4*i (rows 16b..16b+15);
+  // lane l fills slot 64*b + l: row r = 16*b + l/4, physical chunk l%4,
+  // holding logical chunk (l%4) ^ swz(r).  swz(r) does not depend on i, so
+  // block i reads at the thread's base offset plus 64*i rows.  Blocks
+  // i < BM/64 are activation rows, the rest weight rows.
+  const int rb = 16 * wave + (lane >> 2);
+  const uint32_t voff = (uint32_t)(rb * K + (((lane & 3) ^ swz(rb)) * 16));
+  const int KT = K / 64;
+  auto issue = [&](int4* slot, int kt) {
+    const int ks = min(kt, KT - 1) * 64;  // steps past the end re-load the last slice
 #pragma unroll
-  for (int i = 0; i < C::kLdA; ++i) {
-    const int q = tid + i * C::kThreads;
-    const int row = q >> 2, ch = q & 3;
-    const int gr = min(m0 + row, M - 1);
-    src_a[i] = A + (int64_t)gr * K + ch * 16;
-    dst_a[i] = (q < C::kChA) ? swz(row, ch) : -1;
-  }
-#pragma unroll
-  for (int i = 0; i < C::kLdB; ++i) {
-    const int q = tid + i * C::kThreads;
-    const int row = q >> 2, ch = q & 3;
-    const int gr = min(n0 + row, N - 1);
-    src_b[i] = W + (int64_t)gr * K + ch * 16;
-    dst_b[i] = (q < C::kChB) ? swz(row, ch) : -1;
-  }
+    for (int i = 0; i < C::kLPW; ++i) {
+      lds_ptr_t dst = (lds_ptr_t)(slot + 64 * (wave + 4 * i));
+      if (i < BM / 64)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, voff, ks + 64 * i * K, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, voff, ks + (64 * i - BM) * K, 0, 0);
+    }
+  };
 
   v4i acc[C::kTN][C::kTM];
 #pragma unroll
@@ -120,97 +175,129 @@ __global__ __launch_bounds__(256) void gemm_w8a8_kernel(
 #pragma unroll
     for (int j = 0; j < C::kTM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-  int4 ra[C::kLdA], rb[C::kLdB];
-  auto gload = [&](int kt) {
-    const int64_t off = (int64_t)kt * 64;
-#pragma unroll
-    for (int i = 0; i < C::kLdA; ++i)
-      if (dst_a[i] >= 0) ra[i] = *reinterpret_cast<const int4*>(src_a[i] + off);
-#pragma unroll
-    for (int i = 0; i < C::kLdB; ++i)
-      if (dst_b[i] >= 0) rb[i] = *reinterpret_cast<const int4*>(src_b[i] + off);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::kLdA; ++i)
-      if (dst_a[i] >= 0) lds_a[buf][dst_a[i]] = ra[i];
-#pragma unroll
-    for (int i = 0; i < C::kLdB; ++i)
-      if (dst_b[i] >= 0) lds_b[buf][dst_b[i]] = rb[i];
-  };
-
   const int fr = lane & 15;  // fragment row within a 16-row tile
   const int fc = lane >> 4;  // fragment 16-byte chunk
-  const int KT = K / 64;
+  // Fragment slots: 16-row tile j sits 64 slots after tile j-1.
+  const int a_slot0 = slot_of(wm * C::kWTM + fr, fc);
+  const int w_slot0 = slot_of(BM + wn * C::kWTN + fr, fc);
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    v4i fa[C::kTM], fw[C::kTN];
+  struct Frags {
+    v4i a[C::kTM], w[C::kTN];
+  };
+  auto read_frags = [&](Frags& f, const int4* slot) {
 #pragma unroll
     for (int j = 0; j < C::kTM; ++j) {
-      const int row = wm * C::kWTM + j * 16 + fr;
-      const int4 t = lds_a[buf][swz(row, fc)];
-      fa[j] = v4i{t.x, t.y, t.z, t.w};
+      const int4 t = slot[a_slot0 + 64 * j];
+      f.a[j] = v4i{t.x, t.y, t.z, t.w};
     }
 #pragma unroll
     for (int i = 0; i < C::kTN; ++i) {
-      const int row = wn * C::kWTN + i * 16 + fr;
-      const int4 t = lds_b[buf][swz(row, fc)];
-      fw[i] = v4i{t.x, t.y, t.z, t.w};
+      const int4 t = slot[w_slot0 + 64 * i];
+      f.w[i] = v4i{t.x, t.y, t.z, t.w};
     }
+  };
+  auto mfmas = [&](const Frags& f) {
 #pragma unroll
     for (int i = 0; i < C::kTN; ++i)
 #pragma unroll
       for (int j = 0; j < C::kTM; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fw[i], fa[j], acc[i][j], 0, 0, 0);
-    if (kt + 1 < KT) lstore(buf ^ 1);
-    __syncthreads();
-  }
+        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.w[i], f.a[j], acc[i][j], 0, 0, 0);
+  };
+  // One step: (1) wait until step kt+1 has landed (at most 2 later steps of
+  // this wave's loads in flight) and this wave's reads of step kt's slot are
+  // done, then barrier; (2) issue the reads of step kt+1's fragments and
+  // refill step kt's slot with step kt+4, interleaved with (3) the MFMAs on
+  // step kt's fragments, so all three overlap.  The scheduling
+  // groups spread the reads and loads between the MFMAs.
+  auto step = [&](Frags& cur, Frags& nxt, int4* cur_slot, const int4* nxt_slot, int kt) {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm_lgkm0<2 * C::kLPW>();
+    barrier_nofence();
+    read_frags(nxt, nxt_slot);
+    issue(cur_slot, kt + 4);
+    mfmas(cur);
+    interleave_step<C::kTM * C::kTN, C::kTM + C::kTN, C::kLPW>();
+  };
 
-  // Epilogue: lane holds D[n = nb + 4*(lane/16) + r][m = mb + lane%16], r = 0..3.
+  Frags f0, f1;
+  issue(lds0, 0);
+  issue(lds1, 1);
+  issue(lds2, 2);
+  issue(lds3, 3);
+  wait_vm_lgkm0<3 * C::kLPW>();
+  barrier_nofence();
+  read_frags(f0, lds0);
+  int kt = 0;
+  for (; kt + 4 <= KT; kt += 4) {
+    step(f0, f1, lds0, lds1, kt);
+    step(f1, f0, lds1, lds2, kt + 1);
+    step(f0, f1, lds2, lds3, kt + 2);
+    step(f1, f0, lds3, lds0, kt + 3);
+  }
+  if (REM) {  // K steps beyond a multiple of 4
+    if (kt < KT) step(f0, f1, lds0, lds1, kt);
+    if (kt + 1 < KT) step(f1, f0, lds1, lds2, kt + 1);
+    if (kt + 2 < KT) step(f0, f1, lds2, lds3, kt + 2);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm_lgkm0<0>();  // drain the dead loads before the workgroup exits
+
+  // Epilogue: lane holds D[n = nb + 4*(lane/16) + r][m = mb + lane%16].
   const bool vec_ok = (N % 4) == 0;
+  float s_m[C::kTM];
 #pragma unroll
   for (int j = 0; j < C::kTM; ++j) {
-    const int m = m0 + wm * C::kWTM + j * 16 + fr;
-    if (m >= M) continue;
-    const float s_m = (OUT == kOutI32) ? 0.0f : sx[m];
+    const int m = min(m0 + wm * C::kWTM + j * 16 + fr, M - 1);
+    s_m[j] = (OUT == kOutI32) ? 0.0f : sx[m];
+  }
 #pragma unroll
-    for (int i = 0; i < C::kTN; ++i) {
-      const int n = n0 + wn * C::kWTN + i * 16 + fc * 4;
-      if (n >= N) continue;
-      const int valid = min(4, N - n);
+  for (int i = 0; i < C::kTN; ++i) {
+    const int n = n0 + wn * C::kWTN + i * 16 + fc * 4;
+    float swv[4], bv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int nn = min(n + r, N - 1);
+      swv[r] = (OUT == kOutI32) ? 0.f : sw[nn];
+      bv[r] = (OUT == kOutI32 || bias == nullptr) ? 0.f : bias[nn];
+    }
+    if (n >= N) continue;
+#pragma unroll
+    for (int j = 0; j < C::kTM; ++j) {
+      const int m = m0 + wm * C::kWTM + j * 16 + fr;
+      if (m >= M) continue;
       float v[4];
       int32_t iv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         iv[r] = acc[i][j][r];
-        if (OUT != kOutI32) {
-          const int nn = min(n + r, N - 1);
-          const float b = bias ? bias[nn] : 0.0f;
-          v[r] = fmaf(s_m * sw[nn], (float)iv[r], b);
-        }
+        v[r] = fmaf(s_m[j] * swv[r], (float)iv[r], bv[r]);
       }
-      store_out<OUT>(y, (int64_t)m * N + n, v, iv, valid, vec_ok);
+      store4<OUT>(y, (int64_t)m * N + n, v, iv, min(4, N - n), vec_ok);
     }
   }
+}
+
+template <int BM, int BN, bool REM>
+void launch_rem(const int8_t* a, const float* sx, const int8_t* q, const float* sw,
+                const float* bias, void* y, int out, int M, int N, int K, hipStream_t s) {
+  const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const dim3 grid((unsigned)tiles), block(256);
+  if (out == kOutF32)
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, kOutF32, REM>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
+  else if (out == kOutBF16)
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, kOutBF16, REM>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
+  else
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, kOutI32, REM>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
 }
 
 template <int BM, int BN>
 const char* launch_tile(const int8_t* a, const float* sx, const int8_t* q, const float* sw,
                         const float* bias, void* y, int out, int M, int N, int K,
                         hipStream_t s, const char* name) {
-  const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const dim3 grid((unsigned)tiles), block(256);
-  if (out == kOutF32)
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, kOutF32>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
-  else if (out == kOutBF16)
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, kOutBF16>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
+  if (K % 256 == 0)
+    launch_rem<BM, BN, false>(a, sx, q, sw, bias, y, out, M, N, K, s);
   else
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, kOutI32>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
+    launch_rem<BM, BN, true>(a, sx, q, sw, bias, y, out, M, N, K, s);
   return name;
 }
 
@@ -222,6 +309,8 @@ const char* launch_gemm_w8a8(int tile, const int8_t* a, const float* sx, const i
   switch (tile) {
     case kTile256x256:
       return launch_tile<256, 256>(a, sx, q, sw, bias, y, out, M, N, K, s, "gemm_w8a8_256x256");
+    case kTile256x192:
+      return launch_tile<256, 192>(a, sx, q, sw, bias, y, out, M, N, K, s, "gemm_w8a8_256x192");
     case kTile256x128:
       return launch_tile<256, 128>(a, sx, q, sw, bias, y, out, M, N, K, s, "gemm_w8a8_256x128");
     case kTile128x128:

@@ -11,7 +11,7 @@
 // Environment levers, read on every call:
 //   KQ_LOG=1            one stderr line per call: op, route, kernels, grid
 //   KQ_FORCE_ROUTE=gemm|gemv   override the M <= 16 GEMV routing
-//   KQ_TILE=256x256|256x128|128x128|64x64   pin the GEMM tile (A/B runs)
+//   KQ_TILE=256x256|256x192|256x128|128x128|64x64   pin the GEMM tile (A/B runs)
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -46,15 +46,7 @@ int env_force_route() {
   return 0;
 }
 
-int env_tile() {
-  const char* v = getenv("KQ_TILE");
-  if (!v) return -1;
-  if (!strcmp(v, "256x256")) return kq::kTile256x256;
-  if (!strcmp(v, "256x128")) return kq::kTile256x128;
-  if (!strcmp(v, "128x128")) return kq::kTile128x128;
-  if (!strcmp(v, "64x64")) return kq::kTile64x64;
-  return -1;
-}
+int env_tile() { return kq::tile_from_name(getenv("KQ_TILE")); }
 
 bool env_log() {
   const char* v = getenv("KQ_LOG");
@@ -107,7 +99,7 @@ kq_status launch_main(const char* op, int force, kq_wformat fmt, const int8_t* c
                          (int)M, (int)N, (int)K, s);
   } else {
     int tile = 0;
-    for (int t = 0; t <= kq::kTile64x64; ++t)
+    for (int t = 0; t < kq::kNumTiles; ++t)
       if (kq::tile_shape(t).bm == r.tile_m && kq::tile_shape(t).bn == r.tile_n) tile = t;
     if (fmt == KQ_W8_PER_CHANNEL)
       k2 = kq::launch_gemm_w8a8(tile, codes, sx, reinterpret_cast<const int8_t*>(wq),

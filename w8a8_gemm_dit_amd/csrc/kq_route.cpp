@@ -16,10 +16,25 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 TileShape tile_shape(int32_t tile) {
   switch (tile) {
     case kTile256x256: return {256, 256, 256};
+    case kTile256x192: return {256, 192, 256};
     case kTile256x128: return {256, 128, 256};
     case kTile128x128: return {128, 128, 256};
     default: return {64, 64, 256};
   }
+}
+
+static const char* const kTileNames[kNumTiles] = {"256x256", "256x192", "256x128", "128x128",
+                                                  "64x64"};
+
+const char* tile_name(int32_t tile) {
+  return (tile >= 0 && tile < kNumTiles) ? kTileNames[tile] : "?";
+}
+
+int32_t tile_from_name(const char* name) {
+  if (!name) return -1;
+  for (int32_t t = 0; t < kNumTiles; ++t)
+    if (std::string(name) == kTileNames[t]) return t;
+  return -1;
 }
 
 kq_status validate_linear(const char* op, int64_t M, int64_t K, int64_t N,
@@ -77,26 +92,35 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
     r.grid = (N + kGemvCols - 1) / kGemvCols;
     return r;
   }
-  int32_t tile;
-  if (tile_override >= 0 && tile_override <= kTile64x64) {
-    tile = (fmt == KQ_W4_AFFINE_G64 && tile_override == kTile256x256) ? kTile256x128 : tile_override;
+  // Tiles each kernel offers; the int4 GEMM keeps fp32 accumulators and
+  // per-group int32 products, so its largest tile is 256x128.
+  static const int32_t kW8Tiles[] = {kTile256x256, kTile256x192, kTile256x128, kTile128x128,
+                                     kTile64x64};
+  static const int32_t kW4Tiles[] = {kTile256x128, kTile128x128, kTile64x64};
+  const bool w8 = fmt == KQ_W8_PER_CHANNEL;
+  const int32_t* cand = w8 ? kW8Tiles : kW4Tiles;
+  const int ncand = w8 ? 5 : 3;
+  int32_t tile = -1;
+  if (tile_override >= 0 && tile_override < kNumTiles) {
+    for (int i = 0; i < ncand; ++i)
+      if (cand[i] == tile_override) tile = tile_override;
+    if (tile < 0) tile = cand[0];  // a tile this kernel lacks: its largest
   } else {
-    // Pick the largest tile that still gives every CU (256) work; thin
-    // problems fall back to small tiles.
-    auto tiles = [&](int32_t t) {
-      TileShape s = tile_shape(t);
-      return ((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
-    };
-    // The int4 GEMM keeps fp32 accumulators plus per-group int32 products,
-    // so its largest tile is 256x128.
-    if (fmt == KQ_W8_PER_CHANNEL && tiles(kTile256x256) >= 256)
-      tile = kTile256x256;
-    else if (tiles(kTile256x128) >= 256)
-      tile = kTile256x128;
-    else if (tiles(kTile128x128) >= 256)
-      tile = kTile128x128;
-    else
-      tile = kTile64x64;
+    // Minimize (waves of 256 workgroups) x (tile area / relative tile
+    // efficiency): larger tiles reuse operands better, but a partial last
+    // wave leaves CUs idle.
+    double best = 0;
+    for (int i = 0; i < ncand; ++i) {
+      const TileShape s = tile_shape(cand[i]);
+      const int64_t tiles = ((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
+      const int64_t waves = (tiles + 255) / 256;
+      static const double kEff[kNumTiles] = {1.0, 0.97, 0.9, 0.75, 0.45};
+      const double cost = (double)waves * s.bm * s.bn / kEff[cand[i]];
+      if (tile < 0 || cost < best) {
+        best = cost;
+        tile = cand[i];
+      }
+    }
   }
   TileShape s = tile_shape(tile);
   r.kind = KQ_ROUTE_GEMM;
