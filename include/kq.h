@@ -103,6 +103,8 @@ typedef struct kq_route_info {
 #define KQ_MAX_K 65536
 /* Largest M of the GEMV route ([qlip] W4A8 bullet: M <= 16). */
 #define KQ_GEMV_MAX_M 16
+/* Largest K of the GEMV route. */
+#define KQ_GEMV_MAX_K 16384
 
 /* 1 if the current HIP device is a gfx950 (MI355X class) GPU, else 0.
  * [qlip] "Key features": the package is a clean no-op where the INT8 matrix
@@ -121,8 +123,9 @@ size_t kq_workspace_bytes(int64_t M, int64_t K, kq_wformat fmt);
 
 /* Launch plan of a linear call; pure host function, no device access.
  * [kquant]: the route decision is one tested function.  Routing: M <= 16
- * takes the GEMV unless the environment variable KQ_FORCE_ROUTE=gemm;
- * KQ_FORCE_ROUTE=gemv forces the GEMV whenever M <= 16 allows it.
+ * with K <= KQ_GEMV_MAX_K takes the GEMV unless the environment variable
+ * KQ_FORCE_ROUTE=gemm; KQ_FORCE_ROUTE=gemv forces the GEMV (and fails for
+ * shapes it cannot take).
  * Returns KQ_ERR_INVALID_VALUE / KQ_ERR_UNSUPPORTED for shapes the linears
  * reject, with the same messages. */
 kq_status kq_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
@@ -216,7 +219,9 @@ kq_status kq_w4a8_gemm(const int8_t* a, const float* sx, const int32_t* gsum,
  * M <= 16 runs decode-style calls at weight-bandwidth speed).  Same math and
  * arguments as kq_w4a8_linear (fmt = KQ_W4_AFFINE_G64: wq, scale, gbias as
  * there) or kq_w8a8_linear (fmt = KQ_W8_PER_CHANNEL: wq int8, scale fp32 [N],
- * gbias NULL), always on the GEMV kernel.  Requires 1 <= M <= 16. */
+ * gbias NULL), always on the GEMV kernel.  Requires 1 <= M <= 16 and
+ * K <= KQ_GEMV_MAX_K (each wavefront keeps its K slice of the activations in
+ * registers); the linears route larger K to the GEMM. */
 kq_status kq_gemv_small_m(kq_wformat fmt, const void* x, int64_t M, int64_t K,
                           int64_t N, const void* wq, const void* scale,
                           const void* gbias, const float* bias, void* y,

@@ -47,8 +47,10 @@ def test_workspace_layout():
 
 
 @pytest.mark.parametrize("M,N,K,fmt,kind,tile,grid", [
-    (1, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 32), 432),
-    (16, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 32), 432),
+    (1, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 864),
+    (16, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 864),
+    (4, 512, 16384, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 32),
+    (4, 512, 16448, kq.KQ_W8_PER_CHANNEL, "gemm", None, None),
     (17, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemm", None, None),
     (4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 192), 256),
     (16384, 12288, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 256), 3072),
@@ -72,6 +74,8 @@ def test_route_levers(kq_env):
     assert kq.kq_route(4, 512, 512, kq.KQ_W8_PER_CHANNEL)["kind"] == "gemv"
     with pytest.raises(ValueError, match=r"\[kq_route\] M=32 exceeds the GEMV limit 16"):
         kq.kq_route(32, 512, 512, kq.KQ_W8_PER_CHANNEL)
+    with pytest.raises(ValueError, match=r"\[kq_route\] K=16448 exceeds the GEMV limit 16384"):
+        kq.kq_route(4, 512, 16448, kq.KQ_W8_PER_CHANNEL)
     kq_env(KQ_FORCE_ROUTE=None, KQ_TILE="128x128")
     r = kq.kq_route(4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL)
     assert (r["tile_m"], r["tile_n"], r["grid"]) == (128, 128, 32 * 24)

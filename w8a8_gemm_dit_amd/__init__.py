@@ -31,6 +31,7 @@ KQ_DTYPE_F32, KQ_DTYPE_BF16, KQ_DTYPE_I32 = 0, 1, 2
 KQ_ROUTE_GEMM, KQ_ROUTE_GEMV = 0, 1
 KQ_MAX_K = 65536
 KQ_GEMV_MAX_M = 16
+KQ_GEMV_MAX_K = 16384
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkq.so")

@@ -63,25 +63,6 @@ __device__ __forceinline__ int swz(int row) { return ((row >> 1) & 3) ^ ((row >>
 
 __device__ __forceinline__ int slot_of(int row, int chunk) { return row * 4 + (chunk ^ swz(row)); }
 
-// s_waitcnt with vmcnt = N (compile-time) and lgkmcnt = 0 (gfx9 encoding:
-// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt bits 6:4 left at
-// "no wait", lgkmcnt bits 11:8).
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0 << 8));
-}
-
-// Workgroup barrier without a memory fence (a fence would wait for the
-// loads still in flight); the empty asm statements keep the compiler from
-// moving memory accesses across it.
-__device__ __forceinline__ void barrier_nofence() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Instruction interleave of one K step: NV groups of [MFMA x a, DS read x b,
 // MFMA x a, VMEM x 1], then the leftovers, so the MFMA pipe stays busy while

@@ -1,21 +1,28 @@
 // Small-M GEMV of libkq (1 <= M <= 16): "qlip-mlx" README, w4a8_linear
 // bullet -- a register-dequant GEMV path for small batches, so decode-style
 // calls run at weight-bandwidth speed.  Same math as the GEMM routes:
-//   int4: y = sx * sum_g (gs*P + gb*A) + bias,  int8: y = sx*sw*acc + bias.
+//   int4: y = sx * sum_g (gs*P + gb*A) + bias,  int8: y = sx*sw*acc + bias,
+// with P the exact int32 dot product of one 64-wide group and A the group
+// sum of the activation codes.
 //
 // gfx950 design (HBM-bound: every weight byte is read once):
-//   - a workgroup owns 32 output columns (two 16-column MFMA tiles) and its
-//     4 wavefronts split the K groups between them (group g goes to wave
-//     g % 4), so many independent weight loads are in flight per CU;
-//   - weights go straight from global memory into MFMA operand registers
-//     (8 bytes of packed int4 = 16 codes per lane per group, unpacked in
-//     registers; or 16 int8 bytes), with no LDS staging; the M <= 16
-//     activation rows ride in the MFMA's 16 columns (rows >= M read as 0);
-//   - the group scales/offsets and code sums of the workgroup's columns and
-//     rows are staged in LDS in 64-group chunks, transposed so that each
-//     lane reads its 4 consecutive columns with one 16-byte LDS read;
-//   - the 4 wavefronts' partial accumulators are summed through LDS, then
-//     one wavefront applies the epilogue.
+//   - a workgroup owns 16 output columns and its 8 wavefronts split the K
+//     groups into 8 contiguous slices (rounded to whole 128-byte lines);
+//   - each wavefront streams its slice through a private LDS chunk with
+//     direct global->LDS buffer loads: one load instruction moves 8 rows x
+//     one full 128-byte line, and the LDS layout is the MFMA fragment order,
+//     so the fragment reads are contiguous and conflict-free.  A small chunk
+//     (4 groups) keeps the LDS per workgroup low, so several workgroups per
+//     CU keep loads in flight;
+//   - the 16 columns' fp16 group scales and offsets are one contiguous run
+//     per array; the workgroup stages them in LDS with coalesced loads
+//     issued before the weight loads;
+//   - v_mfma_i32_16x16x64_i8 with the activation codes as the A operand
+//     (rows >= M zero) and the weights as B; a second MFMA against an
+//     all-ones B gives the group sums A exactly, so no group-sum input is
+//     read;
+//   - the 8 partial sums are reduced through LDS (fp32 for int4 weights,
+//     exact int32 for int8) and one wavefront applies the epilogue.
 #include "kq_common.hpp"
 #include "kq_launch.hpp"
 #include "kq_route.hpp"
@@ -24,194 +31,220 @@ namespace kq {
 
 namespace {
 
-constexpr int kCols = kGemvCols;  // 32
-constexpr int kGC = 64;           // groups per LDS chunk
-constexpr int kUnroll = 4;        // groups in flight per wave iteration
+constexpr int kWaves = 8;         // K slices per workgroup
+constexpr int kChunk = 4;         // groups per LDS chunk of one wavefront
+constexpr int kMaxG = kGemvMaxK / 64;
 
 template <bool W4, int OUT>
-__global__ __launch_bounds__(256) void gemv_kernel(
-    const int8_t* __restrict__ A, const float* __restrict__ sx, const int32_t* __restrict__ gsum,
+__global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
+    const int8_t* __restrict__ A, const float* __restrict__ sx,
     const void* __restrict__ Wq, const void* __restrict__ gsv, const void* __restrict__ gbv,
     const float* __restrict__ bias, void* __restrict__ y, int M, int N, int K) {
-  __shared__ float lds_gs[kGC][kCols];
-  __shared__ float lds_gb[kGC][kCols];
-  __shared__ float lds_as[kGC][16];
-  __shared__ float lds_red[3][2][4][64];
+  constexpr int UB = W4 ? 32 : 64;          // bytes of one weight row per group
+  constexpr int LPR = UB / 16;              // DMA lanes per (row, group)
+  constexpr int GPB = 128 / UB;             // groups per 128-byte line (one DMA block)
+  constexpr int WLDS = kChunk * 16 * UB;    // LDS bytes of one wavefront's chunk
+  constexpr bool kScales = W4 && OUT != kOutI32;
+  static_assert(kChunk % GPB == 0, "a chunk is whole DMA blocks");
+  __shared__ __attribute__((aligned(16))) int8_t lds_w[kWaves][WLDS];
+  __shared__ float lds_red[kWaves - 1][4][64];
+  extern __shared__ uint32_t lds_sb[];      // [G][16]: scale | offset << 16 (int4 only)
 
   const int G = K / 64;
-  const int n0 = blockIdx.x * kCols;
+  const int RB = W4 ? K / 2 : K;            // bytes per weight row
+  const int n0 = blockIdx.x * 16;
+  const int rows = min(16, N - n0);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int fr = lane & 15;
-  const int fc = lane >> 4;
+  // Wave-uniform (readfirstlane): slice guards are scalar branches, the
+  // LDS DMA bases stay scalar and every MFMA runs with the full EXEC mask.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fr = lane & 15;  // MFMA A row m / B column of this lane
+  const int fc = lane >> 4;  // MFMA 16-wide k chunk / output row block
+  const int per = ((G + kWaves - 1) / kWaves + GPB - 1) / GPB * GPB;
+  const int g0 = min(wave * per, G);
+  const int gn = min(per, G - g0);  // 0 for trailing wavefronts of short K
 
-  // Operand rows of this lane: weight rows n0 + 16*t + fr, activation row fr.
-  const int ar = fr;
-  const bool a_ok = ar < M;
-  const int8_t* a_row = A + (int64_t)(a_ok ? ar : 0) * K + fc * 16;
-  const uint8_t* w4_row[2];
-  const int8_t* w8_row[2];
+  // 1. Scale/offset staging loads: rows n0..n0+rows-1 of the [N, G] arrays
+  //    are one contiguous run of rows*G halves; issued first so that the LDS
+  //    writes below wait for these loads only.
+  constexpr int kSL = kScales ? kMaxG * 16 / (kWaves * 64) : 1;
+  uint32_t sreg[kSL];
+  if (kScales) {
+    const uint16_t* hs = reinterpret_cast<const uint16_t*>(gsv) + (int64_t)n0 * G;
+    const uint16_t* hb = reinterpret_cast<const uint16_t*>(gbv) + (int64_t)n0 * G;
+    const int lim = rows * G;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int n = min(n0 + 16 * t + fr, N - 1);
-    w4_row[t] = reinterpret_cast<const uint8_t*>(Wq) + (int64_t)n * (K / 2) + fc * 8;
-    w8_row[t] = reinterpret_cast<const int8_t*>(Wq) + (int64_t)n * K + fc * 16;
+    for (int j = 0; j < kSL; ++j) {
+      const int e = tid + j * kWaves * 64;
+      uint32_t v = 0;
+      if (e < lim) v = (uint32_t)hs[e] | ((uint32_t)hb[e] << 16);
+      sreg[j] = v;
+    }
   }
 
-  v4f facc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-  v4i iacc[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
-
-  for (int gc0 = 0; gc0 < G; gc0 += kGC) {
-    const int gcn = min(kGC, G - gc0);
-    if (W4) {
-      __syncthreads();
-      const __half* hs = reinterpret_cast<const __half*>(gsv);
-      const __half* hb = reinterpret_cast<const __half*>(gbv);
-      for (int e = tid; e < gcn * kCols; e += 256) {
-        const int c = e / gcn, gl = e - c * gcn;  // consecutive threads walk one column's groups
-        const int n = min(n0 + c, N - 1);
-        lds_gs[gl][c] = __half2float(hs[(int64_t)n * G + gc0 + gl]);
-        lds_gb[gl][c] = __half2float(hb[(int64_t)n * G + gc0 + gl]);
-      }
-      for (int e = tid; e < gcn * 16; e += 256) {
-        const int r = e / gcn, gl = e - r * gcn;
-        lds_as[gl][r] = (r < M) ? (float)gsum[(int64_t)r * G + gc0 + gl] : 0.0f;
-      }
-      __syncthreads();
-    }
-    for (int gb0 = wave; gb0 < gcn; gb0 += 4 * kUnroll) {
-      v4i fa[kUnroll], fw[kUnroll][2];
+  // 2. Weight DMA.  The descriptor is rebased on row n0 with num_records =
+  //    rows*RB: rows past N and groups past the matrix end read as zero.
+  //    Block (r8, blk) = rows 8*r8..8*r8+7 x groups blk*GPB.. of the chunk;
+  //    lane l moves 16 bytes: group l/(8*LPR), row (l/LPR)%8, piece l%LPR,
+  //    into LDS byte 16*l of the block, which puts (row r, chunk group i) at
+  //    (r/8)*kChunk*8*UB + i*8*UB + (r%8)*UB -- the fragment order.
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(reinterpret_cast<const int8_t*>(Wq) + (int64_t)n0 * RB), 0,
+      rows * RB, 0x00020000);
+  const int d_gg = lane / (8 * LPR), d_rr = (lane / LPR) & 7, d_pc = lane % LPR;
+  const int voff = d_rr * RB + d_gg * UB + d_pc * 16;
+  auto issue = [&](int gs, int gc) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int gl = gb0 + 4 * u;
-        const int g = gc0 + (gl < gcn ? gl : 0);
-        const int4 t = a_ok ? *reinterpret_cast<const int4*>(a_row + (int64_t)g * 64)
-                            : make_int4(0, 0, 0, 0);
-        fa[u] = v4i{t.x, t.y, t.z, t.w};
+    for (int blk = 0; blk < kChunk / GPB; ++blk) {
+      if (blk * GPB < gc) {
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          if (W4) {
-            const uint2 p = *reinterpret_cast<const uint2*>(w4_row[t2] + (int64_t)g * 32);
-            uint32_t u0, u1, u2, u3;
-            unpack8_u4(p.x, u0, u1);
-            unpack8_u4(p.y, u2, u3);
-            fw[u][t2] = v4i{(int)u0, (int)u1, (int)u2, (int)u3};
-          } else {
-            const int4 w = *reinterpret_cast<const int4*>(w8_row[t2] + (int64_t)g * 64);
-            fw[u][t2] = v4i{w.x, w.y, w.z, w.w};
-          }
+        for (int r8 = 0; r8 < 2; ++r8) {
+          lds_ptr_t dst = (lds_ptr_t)(&lds_w[wave][r8 * (kChunk * 8 * UB) + blk * 1024]);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, voff,
+                                                   r8 * 8 * RB + (gs + blk * GPB) * UB, 0, 0);
         }
       }
+    }
+  };
+  // 3. Activation fragments of a chunk: A row fr (< M), k chunk fc.
+  v4i fa[kChunk];
+  const int8_t* arow = A + (int64_t)fr * K + fc * 16;
+  auto load_a = [&](int gs, int gc) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int gl = gb0 + 4 * u;
-        if (gl >= gcn) break;
-        const int g = gc0 + gl;
+    for (int i = 0; i < kChunk; ++i) {
+      int4 t = make_int4(0, 0, 0, 0);
+      if (i < gc && fr < M) t = *reinterpret_cast<const int4*>(arow + (gs + i) * 64);
+      fa[i] = v4i{t.x, t.y, t.z, t.w};
+    }
+  };
+  issue(g0, min(gn, kChunk));
+  load_a(g0, min(gn, kChunk));
+
+  // Epilogue operands, loaded while the weights stream.
+  const int nn = n0 + fr;
+  const int nc = min(nn, N - 1);
+  const float bv = bias ? bias[nc] : 0.0f;
+  const float swn = (!W4 && OUT != kOutI32) ? reinterpret_cast<const float*>(gsv)[nc] : 0.0f;
+  float sxm[4];
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          if (W4) {
-            const v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(fw[u][t2], fa[u], v4i{0, 0, 0, 0}, 0, 0, 0);
-            if (OUT == kOutI32) {
-              const int n = n0 + 16 * t2 + 4 * fc;
-              if (fr < M) {
-                int32_t* dst = reinterpret_cast<int32_t*>(y) + ((int64_t)g * M + fr) * N;
+  for (int r = 0; r < 4; ++r) sxm[r] = (OUT != kOutI32) ? sx[min(4 * fc + r, M - 1)] : 0.0f;
+
+  if (kScales) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                  if (n + r < N) dst[n + r] = p[r];
-              }
-            } else {
-              const float4 s4 = *reinterpret_cast<const float4*>(&lds_gs[gl][16 * t2 + 4 * fc]);
-              const float4 b4 = *reinterpret_cast<const float4*>(&lds_gb[gl][16 * t2 + 4 * fc]);
-              const float af = lds_as[gl][fr];
-              const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
-              const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+    for (int j = 0; j < kSL; ++j) {
+      const int e = tid + j * kWaves * 64;
+      if (e < 16 * G) {
+        const int r = e / G, g = e - r * G;
+        lds_sb[g * 16 + r] = sreg[j];
+      }
+    }
+    wait_vm_lgkm0<63>();
+    barrier_nofence();
+  }
+
+  v4f facc = v4f{0.f, 0.f, 0.f, 0.f};
+  v4i iacc = v4i{0, 0, 0, 0};
+  const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
+  const int8_t* wl = &lds_w[wave][(fr >> 3) * (kChunk * 8 * UB) + (fr & 7) * UB + fc * (UB / 4)];
+  for (int c0 = 0; c0 < gn; c0 += kChunk) {
+    const int gc = min(kChunk, gn - c0);
+    if (c0 > 0) {
+      wait_vm_lgkm0<63>();  // fragment reads of the last chunk done before the DMA reuses it
+      issue(g0 + c0, gc);
+      load_a(g0 + c0, gc);
+    }
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      if (i < gc) {
+        const int g = g0 + c0 + i;
+        if (W4) {
+          const uint2 wv = *reinterpret_cast<const uint2*>(wl + i * 8 * UB);
+          uint32_t u0, u1, u2, u3;
+          unpack8_u4(wv.x, u0, u1);
+          unpack8_u4(wv.y, u2, u3);
+          const v4i fw = v4i{(int)u0, (int)u1, (int)u2, (int)u3};
+          const v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fw, v4i{0, 0, 0, 0}, 0, 0, 0);
+          if (OUT == kOutI32) {
+            // debug output: P of every group, [G, M, N]; p[r] = P[g, 4*fc + r, n]
+            if (nn < N) {
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
-                const float t = fmaf(sv[r], (float)p[r], facc[t2][r]);
-                facc[t2][r] = fmaf(bv[r], af, t);
+                const int m = 4 * fc + r;
+                if (m < M) reinterpret_cast<int32_t*>(y)[((int64_t)g * M + m) * N + nn] = p[r];
               }
             }
           } else {
-            iacc[t2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fw[u][t2], fa[u], iacc[t2], 0, 0, 0);
+            const v4i as = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], ones, v4i{0, 0, 0, 0}, 0, 0, 0);
+            const uint32_t sb = lds_sb[g * 16 + fr];
+            const float s = __half2float(__ushort_as_half((unsigned short)(sb & 0xffff)));
+            const float b = __half2float(__ushort_as_half((unsigned short)(sb >> 16)));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) facc[r] = fmaf(b, (float)as[r], fmaf(s, (float)p[r], facc[r]));
           }
+        } else {
+          const int4 wv = *reinterpret_cast<const int4*>(wl + i * 8 * UB);
+          iacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], v4i{wv.x, wv.y, wv.z, wv.w}, iacc,
+                                                       0, 0, 0);
         }
       }
     }
   }
   if (W4 && OUT == kOutI32) return;
 
-  // Sum the 4 wavefronts' partials (fp32 for int4, exact int32 for int8).
+  // Reduce the 8 partials: fp32 for int4 weights, exact int32 for int8.
   if (wave > 0) {
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        lds_red[wave - 1][t2][r][lane] = W4 ? facc[t2][r] : __int_as_float(iacc[t2][r]);
+    for (int r = 0; r < 4; ++r)
+      lds_red[wave - 1][r][lane] = W4 ? facc[r] : __int_as_float(iacc[r]);
   }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int w = 0; w < 3; ++w) {
-        if (W4) facc[t2][r] += lds_red[w][t2][r][lane];
-        else iacc[t2][r] += __float_as_int(lds_red[w][t2][r][lane]);
-      }
-
-  const int m = fr;
-  if (m >= M) return;
-  const float s_m = (OUT == kOutI32) ? 0.f : sx[m];
-#pragma unroll
-  for (int t2 = 0; t2 < 2; ++t2) {
-    const int n = n0 + 16 * t2 + 4 * fc;
-    if (n >= N) continue;
-    const int valid = min(4, N - n);
-    const int64_t idx = (int64_t)m * N + n;
-    float v[4];
+  for (int w = 0; w < kWaves - 1; ++w)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int nn = min(n + r, N - 1);
-      const float b = bias ? bias[nn] : 0.0f;
-      if (W4) v[r] = fmaf(s_m, facc[t2][r], b);
-      else if (OUT != kOutI32) v[r] = fmaf(s_m * reinterpret_cast<const float*>(gsv)[nn], (float)iacc[t2][r], b);
+      if (W4) facc[r] += lds_red[w][r][lane];
+      else iacc[r] += __float_as_int(lds_red[w][r][lane]);
     }
+  if (nn >= N) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * fc + r;
+    if (m >= M) continue;
+    const int64_t idx = (int64_t)m * N + nn;
     if (OUT == kOutI32) {
-      int32_t* p = reinterpret_cast<int32_t*>(y) + idx;
-      for (int r = 0; r < valid; ++r) p[r] = iacc[t2][r];
-    } else if (OUT == kOutF32) {
-      float* p = reinterpret_cast<float*>(y) + idx;
-      for (int r = 0; r < valid; ++r) p[r] = v[r];
+      reinterpret_cast<int32_t*>(y)[idx] = iacc[r];
     } else {
-      uint16_t* p = reinterpret_cast<uint16_t*>(y) + idx;
-      for (int r = 0; r < valid; ++r) p[r] = (uint16_t)f32_to_bf16_rne(v[r]);
+      const float v = W4 ? fmaf(sxm[r], facc[r], bv) : fmaf(sxm[r] * swn, (float)iacc[r], bv);
+      if (OUT == kOutF32) reinterpret_cast<float*>(y)[idx] = v;
+      else reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)f32_to_bf16_rne(v);
     }
   }
 }
 
 template <bool W4>
-const char* launch_fmt(const int8_t* a, const float* sx, const int32_t* gsum, const void* q,
-                       const void* gs, const void* gb, const float* bias, void* y, int out, int M,
-                       int N, int K, hipStream_t s) {
-  const dim3 grid((unsigned)((N + kCols - 1) / kCols)), block(256);
+const char* launch_fmt(const int8_t* a, const float* sx, const void* q, const void* gs,
+                       const void* gb, const float* bias, void* y, int out, int M, int N, int K,
+                       hipStream_t s) {
+  const dim3 grid((unsigned)((N + 15) / 16)), block(kWaves * 64);
+  const size_t sb = (W4 && out != kOutI32) ? (size_t)16 * (K / 64) * sizeof(uint32_t) : 0;
   if (out == kOutF32)
-    hipLaunchKernelGGL((gemv_kernel<W4, kOutF32>), grid, block, 0, s, a, sx, gsum, q, gs, gb, bias, y, M, N, K);
+    hipLaunchKernelGGL((gemv_kernel<W4, kOutF32>), grid, block, sb, s, a, sx, q, gs, gb, bias, y, M, N, K);
   else if (out == kOutBF16)
-    hipLaunchKernelGGL((gemv_kernel<W4, kOutBF16>), grid, block, 0, s, a, sx, gsum, q, gs, gb, bias, y, M, N, K);
+    hipLaunchKernelGGL((gemv_kernel<W4, kOutBF16>), grid, block, sb, s, a, sx, q, gs, gb, bias, y, M, N, K);
   else
-    hipLaunchKernelGGL((gemv_kernel<W4, kOutI32>), grid, block, 0, s, a, sx, gsum, q, gs, gb, bias, y, M, N, K);
+    hipLaunchKernelGGL((gemv_kernel<W4, kOutI32>), grid, block, sb, s, a, sx, q, gs, gb, bias, y, M, N, K);
   return W4 ? "gemv_w4a8" : "gemv_w8a8";
 }
 
 }  // namespace
 
-const char* launch_gemv(bool w4, const int8_t* a, const float* sx, const int32_t* gsum,
+const char* launch_gemv(bool w4, const int8_t* a, const float* sx, const int32_t* /*gsum*/,
                         const void* q, const void* gs, const void* gb, const float* bias,
                         void* y, int out, int M, int N, int K, hipStream_t s) {
-  return w4 ? launch_fmt<true>(a, sx, gsum, q, gs, gb, bias, y, out, M, N, K, s)
-            : launch_fmt<false>(a, sx, gsum, q, gs, gb, bias, y, out, M, N, K, s);
+  return w4 ? launch_fmt<true>(a, sx, q, gs, gb, bias, y, out, M, N, K, s)
+            : launch_fmt<false>(a, sx, q, gs, gb, bias, y, out, M, N, K, s);
 }
 
 }  // namespace kq

@@ -135,6 +135,9 @@ kq_status check_linear_args(const char* op, int force, kq_wformat fmt, int64_t M
   if (force == 2 && M > KQ_GEMV_MAX_M)
     return fail(KQ_ERR_UNSUPPORTED, "[%s] M=%lld exceeds the GEMV limit %d", op, (long long)M,
                 KQ_GEMV_MAX_M);
+  if (force == 2 && K > kq::kGemvMaxK)
+    return fail(KQ_ERR_UNSUPPORTED, "[%s] K=%lld exceeds the GEMV limit %lld", op, (long long)K,
+                (long long)kq::kGemvMaxK);
   return KQ_SUCCESS;
 }
 
@@ -215,6 +218,9 @@ kq_status kq_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt, kq_dtype y_d
   if (force == 2 && M > KQ_GEMV_MAX_M)
     return fail(KQ_ERR_UNSUPPORTED, "[kq_route] M=%lld exceeds the GEMV limit %d", (long long)M,
                 KQ_GEMV_MAX_M);
+  if (force == 2 && K > kq::kGemvMaxK)
+    return fail(KQ_ERR_UNSUPPORTED, "[kq_route] K=%lld exceeds the GEMV limit %lld", (long long)K,
+                (long long)kq::kGemvMaxK);
   *out = kq::choose_route(M, N, K, fmt, force, env_tile());
   return KQ_SUCCESS;
 }

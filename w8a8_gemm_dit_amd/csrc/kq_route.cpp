@@ -79,11 +79,9 @@ kq_status validate_linear(const char* op, int64_t M, int64_t K, int64_t N,
 
 kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
                            int force, int tile_override) {
-  (void)K;
   kq_route_info r{};
-  const bool gemv = (force == 2) ? (M <= KQ_GEMV_MAX_M)
-                    : (force == 1) ? false
-                                   : (M >= 1 && M <= KQ_GEMV_MAX_M);
+  const bool fits = M <= KQ_GEMV_MAX_M && K <= kGemvMaxK;
+  const bool gemv = (force == 2) ? fits : (force == 1) ? false : (M >= 1 && fits);
   if (gemv) {
     r.kind = KQ_ROUTE_GEMV;
     r.tile_m = KQ_GEMV_MAX_M;

@@ -49,8 +49,11 @@ struct WorkspaceLayout {
 };
 WorkspaceLayout workspace_layout(int64_t M, int64_t K, kq_wformat fmt);
 
-// GEMV route geometry.
-constexpr int kGemvCols = 32;     // output columns per workgroup
-constexpr int kGemvThreads = 256;
+// GEMV route geometry: 16 output columns per workgroup of 8 wavefronts,
+// which split K; each wavefront holds its K slice of the activations in
+// registers, up to 32 groups of 64, so the GEMV takes K <= 16384.
+constexpr int kGemvCols = 16;
+constexpr int kGemvThreads = 512;
+constexpr int64_t kGemvMaxK = KQ_GEMV_MAX_K;
 
 }  // namespace kq
