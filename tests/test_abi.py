@@ -54,8 +54,9 @@ def test_workspace_layout():
     (17, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemm", None, None),
     (4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 192), 256),
     (16384, 12288, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 256), 3072),
-    (2048, 12288, 4096, kq.KQ_W4_AFFINE_G64, "gemm", (256, 128), 768),
-    (2048, 4096, 12288, kq.KQ_W4_AFFINE_G64, "gemm", (256, 128), 256),
+    (2048, 12288, 4096, kq.KQ_W4_AFFINE_G64, "gemm", (128, 256), 768),
+    (2048, 4096, 12288, kq.KQ_W4_AFFINE_G64, "gemm", (128, 256), 256),
+    (100, 640, 256, kq.KQ_W4_AFFINE_G64, "gemm", (64, 128), 10),
     (2048, 48, 5120, kq.KQ_W8_PER_CHANNEL, "gemm", (64, 64), 32),
 ])
 def test_route_decisions(M, N, K, fmt, kind, tile, grid, kq_env):
@@ -81,7 +82,13 @@ def test_route_levers(kq_env):
     assert (r["tile_m"], r["tile_n"], r["grid"]) == (128, 128, 32 * 24)
     kq_env(KQ_TILE="256x256")
     r = kq.kq_route(4096, 3072, 3072, kq.KQ_W4_AFFINE_G64)
-    assert (r["tile_m"], r["tile_n"]) == (256, 128)     # int4 caps at 256x128
+    assert (r["tile_m"], r["tile_n"]) == (128, 256)     # int4: nearest tile it has
+    kq_env(KQ_TILE="64x64")
+    r = kq.kq_route(4096, 3072, 3072, kq.KQ_W4_AFFINE_G64)
+    assert (r["tile_m"], r["tile_n"], r["threads"]) == (64, 128, 256)
+    kq_env(KQ_TILE="128x256")
+    r = kq.kq_route(4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL)
+    assert (r["tile_m"], r["tile_n"]) == (256, 128)     # int8: same area
 
 
 @pytest.mark.parametrize("K,msg", [

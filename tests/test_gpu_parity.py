@@ -123,8 +123,12 @@ def test_w8a8_outputs(M, K, N, tile, out, kq_env):
         check_bf16(host_bf16_bits(y), y64, T, f"w8a8 {M}x{K}x{N}")
 
 
-@pytest.mark.parametrize("tile", [None, "256x128", "128x128", "64x64"])
-@pytest.mark.parametrize("M,K,N", SHAPES)
+# K spanning several 16-group chunks of the int4 GEMM, whole and partial
+SHAPES_W4 = SHAPES + [(130, 2048, 200), (96, 2112, 272)]
+
+
+@pytest.mark.parametrize("tile", [None, "128x256", "64x128"])
+@pytest.mark.parametrize("M,K,N", SHAPES_W4)
 def test_w4a8_group_products_bit_exact(M, K, N, tile, kq_env):
     kq_env(KQ_TILE=tile, KQ_FORCE_ROUTE="gemm")
     xb, w, _ = _problem(M, K, N, seed=M + K * 5 + N)
@@ -136,8 +140,8 @@ def test_w4a8_group_products_bit_exact(M, K, N, tile, kq_env):
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-@pytest.mark.parametrize("tile", [None, "128x128", "64x64"])
-@pytest.mark.parametrize("M,K,N", SHAPES[:6])
+@pytest.mark.parametrize("tile", [None, "128x256", "64x128"])
+@pytest.mark.parametrize("M,K,N", SHAPES[:6] + SHAPES_W4[-2:])
 def test_w4a8_outputs(M, K, N, tile, out, kq_env):
     kq_env(KQ_TILE=tile, KQ_FORCE_ROUTE="gemm")
     xb, w, b = _problem(M, K, N, seed=2 * M + K + N, with_bias=(M % 2 == 1))

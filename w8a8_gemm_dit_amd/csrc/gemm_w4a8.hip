@@ -1,23 +1,36 @@
-// W4A8 GEMM of libkq:
-//   y[m,n] = sx[m] * sum_g (gs[n,g]*P[g,m,n] + gb[n,g]*A[m,g]) + bias[n],
-//   P[g,m,n] = sum_{k in group g} a[m,k]*q[n,k]   (exact int32),
-//   A[m,g]   = sum_{k in group g} a[m,k]          (from the quantize kernel).
-// This is x_hat . w_hat^T with w_hat = gs*q + gb per 64-group, regrouped so
-// the K loop stays on INT8 MFMA ("qlip-mlx" README, w4a8_linear bullet: the
-// same INT8 compute with packed int4 weights; MLX pull request 4722: stage
-// weights and activations as int8 instead of dequantizing to fp16).
+// W4A8 GEMM of libkq ("qlip-mlx" README, w4a8_linear bullet: int4 weights
+// with the INT8 matmul, affine group-64 dequantization):
+//   y[m,n] = sx[m] * sum_g (gs[n,g] * P[m,n,g] + gb[n,g] * A[m,g]) + bias[n]
+// with P the exact int32 product of one 64-wide group of activation codes
+// and unsigned 4-bit weight codes, and A the group sum of the activation
+// codes (MLX pull request 4722, "Kernel design": the bias term folds to
+// biases * sum(x_g)).
 //
-// gfx950 design: the W8A8 tile structure (2x2 wavefronts, 16x16x64 int8
-// MFMA, weights as the MFMA A operand, XOR-swizzled double-buffered LDS),
-// with three differences:
-//   - the weight tile arrives packed (32 bytes per row per 64-group) and is
-//     unpacked to int8 in registers (mask, shift, v_perm_b32) before the LDS
-//     store, so every wavefront reads plain int8 fragments;
-//   - one LDS stage is exactly one 64-group, so each stage's MFMA result is
-//     the group's P and is rescaled at once into fp32 accumulators:
-//     acc += gs*float(P) + gb*float(A), with the group's scales and offsets
-//     (and the tile rows' code sums) staged in LDS alongside the operands;
-//   - the epilogue is y = sx*acc + bias, rounded once to the output type.
+// gfx950 design:
+//   - a workgroup of 8 (or 4) wavefronts computes a BM x BN tile; each
+//     wavefront owns a WTM x WTN block of fp32 accumulators;
+//   - K advances one group (64 codes) per step.  Activation rows (64 bytes)
+//     and packed weight rows (32 bytes) move global -> LDS with direct
+//     buffer loads into a 4-slot ring, one array per slot, as in the W8A8
+//     GEMM (same swizzle for the activation rows);
+//   - per step and 16x16 block, v_mfma_i32_16x16x64_i8 gives P exactly
+//     (activation codes are the A operand, unpacked weights the B operand,
+//     so each lane holds 4 rows of one column and needs one scale), then
+//     two VALU ops per element apply the group scale: acc += gs * float(P);
+//   - the offset term sum_g gb*A runs on the matrix core: every 16 groups a
+//     table of the group sums split exactly into fp16 parts (A = 64*hi + lo,
+//     |hi| <= 128, 0 <= lo < 64) and of the fp16 offsets feeds one
+//     v_mfma_f32_16x16x32_f16 per block that accumulates straight into the
+//     fp32 accumulators (every product is exact in fp32);
+//   - the scale/offset/group-sum tables are double-buffered in LDS: loads
+//     for the next 16 groups go out at the first step of the current 16,
+//     LDS writes at the ninth, so no step waits for them;
+//   - the K loop is unrolled by 16 steps (4 ring turns) so every table event
+//     sits at a fixed place; uniform guards on each step (steps past K skip
+//     their compute) also keep the compiler from interleaving the steps'
+//     fragments, which would exhaust the registers.
+#include <type_traits>
+
 #include "kq_common.hpp"
 #include "kq_launch.hpp"
 #include "kq_route.hpp"
@@ -26,68 +39,139 @@ namespace kq {
 
 namespace {
 
-template <int BM, int BN>
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// Activation-row swizzle of the W8A8 ring: chunk index ^ ((r/2)%4 ^ (r/8)%2).
+__device__ __forceinline__ int swz4(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+
+constexpr int kSG = 16;  // groups per table chunk (one f16 MFMA: 16 groups x {hi, lo})
+
+template <int BM, int BN, int WTM, int WTN>
 struct Cfg4 {
-  static constexpr int kThreads = 256;
-  static constexpr int kWavesM = 2, kWavesN = 2;
-  static constexpr int kWTM = BM / kWavesM;
-  static constexpr int kWTN = BN / kWavesN;
-  static constexpr int kTM = kWTM / 16;
-  static constexpr int kTN = kWTN / 16;
-  static constexpr int kChA = BM * 4;        // int8 activation chunks per stage
-  static constexpr int kChB = BN * 4;        // unpacked int8 weight chunks per stage
-  static constexpr int kChP = BN * 2;        // packed weight chunks per stage
-  static constexpr int kLdA = (kChA + kThreads - 1) / kThreads;
-  static constexpr int kLdP = (kChP + kThreads - 1) / kThreads;
+  static constexpr int kWM = BM / WTM, kWN = BN / WTN;
+  static constexpr int kWaves = kWM * kWN;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kTM = WTM / 16, kTN = WTN / 16;
+  static constexpr int kABlk = BM / 16;   // 1 KB DMA blocks of activation rows per step
+  static constexpr int kWBlk = BN / 32;   // 1 KB DMA blocks of packed weight rows per step
+  static constexpr int kLPW = (kABlk + kWBlk) / kWaves;
+  static constexpr int kASlots = BM * 4;  // 16-byte granules of one slot's activation part
+  static constexpr int kSlots = kASlots + BN * 2;
+  // table staging per thread and chunk
+  static constexpr int kSBN = BN * kSG / kThreads;  // scale and offset entries
+  static constexpr int kSBM = BM * kSG / kThreads;  // group-sum entries
+  static_assert((kABlk + kWBlk) % kWaves == 0, "DMA blocks split evenly over the waves");
+  static_assert(BN * kSG % kThreads == 0 && BM * kSG % kThreads == 0, "table staging");
 };
 
-__device__ __forceinline__ int swz4(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 2) & 3)); }
+template <int OUT>
+__device__ __forceinline__ void store1(void* y, int64_t idx, float v) {
+  if (OUT == kOutF32) reinterpret_cast<float*>(y)[idx] = v;
+  else reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)f32_to_bf16_rne(v);
+}
 
-template <int BM, int BN, int OUT>
-__global__ __launch_bounds__(256) void gemm_w4a8_kernel(
+template <int BM, int BN, int WTM, int WTN, int OUT>
+__global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int32_t* __restrict__ gsum,
-    const uint8_t* __restrict__ W4, const __half* __restrict__ gs, const __half* __restrict__ gb,
+    const uint8_t* __restrict__ Q, const uint16_t* __restrict__ GS, const uint16_t* __restrict__ GB,
     const float* __restrict__ bias, void* __restrict__ y, int M, int N, int K) {
-  using C = Cfg4<BM, BN>;
-  __shared__ int4 lds_a[2][C::kChA];
-  __shared__ int4 lds_b[2][C::kChB];
-  __shared__ float lds_gs[2][BN];
-  __shared__ float lds_gb[2][BN];
-  __shared__ float lds_as[2][BM];
+  using C = Cfg4<BM, BN, WTM, WTN>;
+  constexpr bool kScaled = OUT != kOutI32;
+  __shared__ int4 lds0[C::kSlots], lds1[C::kSlots], lds2[C::kSlots], lds3[C::kSlots];
+  // tables, double-buffered: gs and gb as [column][16 groups] fp16, the group
+  // sums as [row][32] fp16 = {64*hi of groups 0..15, lo of groups 0..15}
+  __shared__ __attribute__((aligned(16))) uint16_t t_gs[kScaled ? 2 : 1][kScaled ? BN : 1][kSG];
+  __shared__ __attribute__((aligned(16))) uint16_t t_gb[kScaled ? 2 : 1][kScaled ? BN : 1][kSG];
+  __shared__ __attribute__((aligned(16))) uint16_t t_as[kScaled ? 2 : 1][kScaled ? BM : 1][2 * kSG];
 
-  const int G = K / 64;
   const int tiles_n = (N + BN - 1) / BN;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int m0 = (tile / tiles_n) * BM;
   const int n0 = (tile % tiles_n) * BN;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave % C::kWavesM;
-  const int wn = wave / C::kWavesM;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::kWN;
+  const int wn = wave % C::kWN;
+  const int G = K / 64;
+  const int KT = G;
+  const int QB = K / 2;  // packed bytes per weight row
 
-  int64_t off_a[C::kLdA];
-  int dst_a[C::kLdA];
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(A + (int64_t)m0 * K), 0, min(BM, M - m0) * K, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(Q + (int64_t)n0 * QB), 0, min(BN, N - n0) * QB, 0x00020000);
+
+  // DMA plan: block b = wave + kWaves*i.  Activation block b < kABlk holds
+  // rows 16b..16b+15 (lane l: row 16b + l/4, physical chunk l%4 holding
+  // logical chunk (l%4)^swz4(row)); weight block b' = b - kABlk holds rows
+  // 32b'..32b'+31 of 32 bytes (lane l: row 32b' + l/2, half l%2), stored
+  // after the activation part.
+  const int ar = lane >> 2;
+  const uint32_t voff_a = (uint32_t)(ar * K + (((lane & 3) ^ swz4(ar)) * 16));
+  const uint32_t voff_q = (uint32_t)((lane >> 1) * QB + (lane & 1) * 16);
+  auto issue = [&](int4* slot, int kt) {
+    const int k = min(kt, KT - 1);  // steps past the end re-load the last slice
 #pragma unroll
-  for (int i = 0; i < C::kLdA; ++i) {
-    const int q = tid + i * C::kThreads;
-    const int row = q >> 2, ch = q & 3;
-    off_a[i] = (int64_t)min(m0 + row, M - 1) * K + ch * 16;
-    dst_a[i] = (q < C::kChA) ? row : -1;
-  }
-  int64_t off_p[C::kLdP];
-  int dst_p[C::kLdP];
+    for (int i = 0; i < C::kLPW; ++i) {
+      const int b = wave + C::kWaves * i;
+      if (b < C::kABlk) {
+        lds_ptr_t dst = (lds_ptr_t)(slot + 64 * b);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, voff_a, 16 * b * K + k * 64, 0, 0);
+      } else {
+        const int bq = b - C::kABlk;
+        lds_ptr_t dst = (lds_ptr_t)(slot + C::kASlots + 64 * bq);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, dst, 16, voff_q, 32 * bq * QB + k * 32, 0, 0);
+      }
+    }
+  };
+
+  // ---- table staging (scales, offsets, group sums of 16 groups)
+  uint32_t st_s[C::kSBN], st_b[C::kSBN];
+  int32_t st_a[C::kSBM];
+  // Always issues the same number of loads (clamped addresses, values
+  // masked to zero past N, M or G): the ring's vmcnt waits count them.
+  auto stage_load = [&](int chunk) {
+    const int gbase = chunk * kSG;
 #pragma unroll
-  for (int i = 0; i < C::kLdP; ++i) {
-    const int q = tid + i * C::kThreads;
-    const int row = q >> 1, pc = q & 1;
-    off_p[i] = (int64_t)min(n0 + row, N - 1) * (K / 2) + pc * 16;
-    dst_p[i] = (q < C::kChP) ? row : -1;
-  }
-  // Per-group side data: thread t < BN stages the scale/offset of column
-  // n0+t; thread t < BM stages the code sum of row m0+t.
-  const int64_t side_n = (int64_t)min(n0 + tid, N - 1) * G;
-  const int64_t side_m = (int64_t)min(m0 + tid, M - 1) * G;
+    for (int u = 0; u < C::kSBN; ++u) {
+      const int e = tid + u * C::kThreads;
+      const int col = e / kSG, t = e % kSG;
+      const int n = n0 + col, g = gbase + t;
+      const bool ok = n < N && g < G;
+      const int64_t idx = (int64_t)min(n, N - 1) * G + min(g, G - 1);
+      const uint32_t s = GS[idx], b = GB[idx];
+      st_s[u] = ok ? s : 0u;
+      st_b[u] = ok ? b : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < C::kSBM; ++u) {
+      const int e = tid + u * C::kThreads;
+      const int row = e / kSG, t = e % kSG;
+      const int m = m0 + row, g = gbase + t;
+      const int32_t v = gsum[(int64_t)min(m, M - 1) * G + min(g, G - 1)];
+      st_a[u] = (m < M && g < G) ? v : 0;
+    }
+  };
+  auto stage_write = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < C::kSBN; ++u) {
+      const int e = tid + u * C::kThreads;
+      const int col = e / kSG, t = e % kSG;
+      t_gs[buf][col][t] = (uint16_t)st_s[u];
+      t_gb[buf][col][t] = (uint16_t)st_b[u];
+    }
+#pragma unroll
+    for (int u = 0; u < C::kSBM; ++u) {
+      const int e = tid + u * C::kThreads;
+      const int row = e / kSG, t = e % kSG;
+      const int v = st_a[u];
+      const int hi = v >> 6;        // floor(v / 64)
+      const int lo = v - hi * 64;   // 0..63
+      t_as[buf][row][t] = __half_as_ushort(__float2half_rn((float)(hi * 64)));
+      t_as[buf][row][kSG + t] = __half_as_ushort(__float2half_rn((float)lo));
+    }
+  };
 
   v4f acc[C::kTN][C::kTM];
 #pragma unroll
@@ -95,150 +179,173 @@ __global__ __launch_bounds__(256) void gemm_w4a8_kernel(
 #pragma unroll
     for (int j = 0; j < C::kTM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  int4 ra[C::kLdA];
-  uint4 rp[C::kLdP];
-  float r_gs = 0.f, r_gb = 0.f, r_as = 0.f;
-  auto gload = [&](int g) {
-#pragma unroll
-    for (int i = 0; i < C::kLdA; ++i)
-      if (dst_a[i] >= 0) ra[i] = *reinterpret_cast<const int4*>(A + off_a[i] + (int64_t)g * 64);
-#pragma unroll
-    for (int i = 0; i < C::kLdP; ++i)
-      if (dst_p[i] >= 0) rp[i] = *reinterpret_cast<const uint4*>(W4 + off_p[i] + (int64_t)g * 32);
-    if (tid < BN) {
-      r_gs = __half2float(gs[side_n + g]);
-      r_gb = __half2float(gb[side_n + g]);
-    }
-    if (tid < BM) r_as = (float)gsum[side_m + g];
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::kLdA; ++i)
-      if (dst_a[i] >= 0) {
-        const int q = tid + i * C::kThreads;
-        lds_a[buf][swz4(dst_a[i], q & 3)] = ra[i];
-      }
-#pragma unroll
-    for (int i = 0; i < C::kLdP; ++i)
-      if (dst_p[i] >= 0) {
-        const int pc = (tid + i * C::kThreads) & 1;
-        uint32_t u[8];
-        unpack8_u4(rp[i].x, u[0], u[1]);
-        unpack8_u4(rp[i].y, u[2], u[3]);
-        unpack8_u4(rp[i].z, u[4], u[5]);
-        unpack8_u4(rp[i].w, u[6], u[7]);
-        lds_b[buf][swz4(dst_p[i], 2 * pc)] = make_int4(u[0], u[1], u[2], u[3]);
-        lds_b[buf][swz4(dst_p[i], 2 * pc + 1)] = make_int4(u[4], u[5], u[6], u[7]);
-      }
-    if (tid < BN) {
-      lds_gs[buf][tid] = r_gs;
-      lds_gb[buf][tid] = r_gb;
-    }
-    if (tid < BM) lds_as[buf][tid] = r_as;
-  };
+  const int fr = lane & 15;  // A row / B column within a 16-block
+  const int fc = lane >> 4;  // k chunk (16 codes) / output row quad
+  const int a_row0 = wm * WTM + fr;
+  const int a_slot0 = a_row0 * 4 + (fc ^ swz4(a_row0));  // row block j: + 64*j (swz4 is 16-periodic)
+  const int q_col0 = wn * WTN + fr;
+  const int q_byte0 = C::kASlots * 16 + q_col0 * 32 + fc * 8;  // column block i: + 512*i
 
-  const int fr = lane & 15;
-  const int fc = lane >> 4;
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    if (g + 1 < G) gload(g + 1);
-    v4i fa[C::kTM], fw[C::kTN];
+  struct Frags {
+    v4i a[C::kTM];
+    uint2 q[C::kTN];
+    uint32_t s[C::kTN];
+  };
+  auto read_frags = [&](Frags& f, const int4* slot, int kt) {
 #pragma unroll
     for (int j = 0; j < C::kTM; ++j) {
-      const int4 t = lds_a[buf][swz4(wm * C::kWTM + j * 16 + fr, fc)];
-      fa[j] = v4i{t.x, t.y, t.z, t.w};
+      const int4 t = slot[a_slot0 + 64 * j];
+      f.a[j] = v4i{t.x, t.y, t.z, t.w};
     }
+    const char* sb = reinterpret_cast<const char*>(slot);
+#pragma unroll
+    for (int i = 0; i < C::kTN; ++i) f.q[i] = *reinterpret_cast<const uint2*>(sb + q_byte0 + 512 * i);
+    if (kScaled) {
+      const int g = min(kt, KT - 1);
+      const int buf = (g / kSG) & 1, t = g % kSG;
+#pragma unroll
+      for (int i = 0; i < C::kTN; ++i) f.s[i] = t_gs[buf][q_col0 + 16 * i][t];
+    }
+  };
+  auto compute = [&](const Frags& f, int kt) {
 #pragma unroll
     for (int i = 0; i < C::kTN; ++i) {
-      const int4 t = lds_b[buf][swz4(wn * C::kWTN + i * 16 + fr, fc)];
-      fw[i] = v4i{t.x, t.y, t.z, t.w};
-    }
-    float af[C::kTM];
-#pragma unroll
-    for (int j = 0; j < C::kTM; ++j) af[j] = lds_as[buf][wm * C::kWTM + j * 16 + fr];
-#pragma unroll
-    for (int i = 0; i < C::kTN; ++i) {
-      const int nb = wn * C::kWTN + i * 16 + fc * 4;
-      const float4 s4 = *reinterpret_cast<const float4*>(&lds_gs[buf][nb]);
-      const float4 b4 = *reinterpret_cast<const float4*>(&lds_gb[buf][nb]);
-      const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
-      const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+      uint32_t u0, u1, u2, u3;
+      unpack8_u4(f.q[i].x, u0, u1);
+      unpack8_u4(f.q[i].y, u2, u3);
+      const v4i fw = v4i{(int)u0, (int)u1, (int)u2, (int)u3};
+      const float s = kScaled ? __half2float(__ushort_as_half((unsigned short)f.s[i])) : 0.f;
 #pragma unroll
       for (int j = 0; j < C::kTM; ++j) {
-        const v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(fw[i], fa[j], v4i{0, 0, 0, 0}, 0, 0, 0);
-        if (OUT == kOutI32) {
-          const int m = m0 + wm * C::kWTM + j * 16 + fr;
-          const int n = n0 + nb;
-          if (m < M) {
-            int32_t* dst = reinterpret_cast<int32_t*>(y) + ((int64_t)g * M + m) * N;
+        const v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.a[j], fw, v4i{0, 0, 0, 0}, 0, 0, 0);
+        if (kScaled) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (n + r < N) dst[n + r] = p[r];
-          }
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(s, (float)p[r], acc[i][j][r]);
         } else {
+          // debug output: P of every group, [G, M, N]
+          const int n = n0 + q_col0 + 16 * i;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float t = fmaf(sv[r], (float)p[r], acc[i][j][r]);
-            acc[i][j][r] = fmaf(bv[r], af[j], t);
+            const int m = m0 + wm * WTM + 16 * j + 4 * fc + r;
+            if (m < M && n < N) reinterpret_cast<int32_t*>(y)[((int64_t)kt * M + m) * N + n] = p[r];
           }
         }
       }
     }
-    if (g + 1 < G) lstore(buf ^ 1);
-    __syncthreads();
-  }
-  if (OUT == kOutI32) return;
+  };
+  // Offset term of one table chunk: acc += sum_t (64*hi_t + lo_t) * gb_t.
+  auto offset_mfmas = [&](int buf) {
+    v8h fa[C::kTM], fb[C::kTN];
+#pragma unroll
+    for (int j = 0; j < C::kTM; ++j)
+      fa[j] = *reinterpret_cast<const v8h*>(&t_as[buf][wm * WTM + 16 * j + fr][8 * fc]);
+#pragma unroll
+    for (int i = 0; i < C::kTN; ++i)
+      fb[i] = *reinterpret_cast<const v8h*>(&t_gb[buf][q_col0 + 16 * i][8 * (fc & 1)]);
+#pragma unroll
+    for (int i = 0; i < C::kTN; ++i)
+#pragma unroll
+      for (int j = 0; j < C::kTM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[j], fb[i], acc[i][j], 0, 0, 0);
+  };
 
-  const bool vec_ok = (N % 4) == 0;
+  // One step of the ring (see the W8A8 GEMM): wait until step kt+1 landed,
+  // barrier, read step kt+1's fragments, refill step kt's slot with kt+4,
+  // compute step kt.  EXTRA = VMEM ops issued after step kt+1's loads
+  // besides the ring's own (the table loads, at two places per chunk).
+  auto step = [&](Frags& cur, Frags& nxt, int4* cur_slot, const int4* nxt_slot, int kt,
+                  auto extra_tag, auto s_tag) {
+    constexpr int EXTRA = decltype(extra_tag)::value;
+    constexpr int S = decltype(s_tag)::value;  // position in the 16-step chunk
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm_lgkm0<2 * C::kLPW + EXTRA>();
+    barrier_nofence();
+    read_frags(nxt, nxt_slot, kt + 1);
+    if (kScaled && S == 0) stage_load(kt / kSG + 1);
+    issue(cur_slot, kt + 4);
+    if (kt < KT) compute(cur, kt);
+    if (kScaled && S == 8) {
+      const int c = kt / kSG + 1;
+      if (c * kSG < G) stage_write(c & 1);
+    }
+    if (kScaled && S == kSG - 1) {
+      if (kt < KT) offset_mfmas((kt / kSG) & 1);
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  constexpr int kStageOps = kScaled ? 2 * C::kSBN + C::kSBM : 0;
+  using IX = std::integral_constant<int, kStageOps>;
+
+  // prologue: table chunk 0, ring steps 0..3
+  if (kScaled) {
+    stage_load(0);
+    stage_write(0);
+  }
+  issue(lds0, 0);
+  issue(lds1, 1);
+  issue(lds2, 2);
+  issue(lds3, 3);
+  wait_vm_lgkm0<3 * C::kLPW>();
+  barrier_nofence();
+  Frags f0, f1;
+  read_frags(f0, lds0, 0);
+
+  // With the table loads issued at position 0 before that step's ring
+  // loads, the waits at positions 1 and 2 allow them to stay in flight.
+  for (int kt = 0; kt < KT; kt += kSG) {
+#define KQ_STEP4(base, X1, X2)                                                   \
+    step(f0, f1, lds0, lds1, kt + base + 0, I0{}, std::integral_constant<int, base + 0>{}); \
+    step(f1, f0, lds1, lds2, kt + base + 1, X1{}, std::integral_constant<int, base + 1>{}); \
+    step(f0, f1, lds2, lds3, kt + base + 2, X2{}, std::integral_constant<int, base + 2>{}); \
+    step(f1, f0, lds3, lds0, kt + base + 3, I0{}, std::integral_constant<int, base + 3>{});
+    KQ_STEP4(0, IX, IX)
+    if (kt + 4 < KT) { KQ_STEP4(4, I0, I0) }
+    if (kt + 8 < KT) { KQ_STEP4(8, I0, I0) }
+    if (kt + 12 < KT) { KQ_STEP4(12, I0, I0) }
+#undef KQ_STEP4
+    if (kt + kSG > KT) {
+      // partial last chunk: its offset term was not applied at position 15
+      if (kScaled) {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm_lgkm0<63>();
+        barrier_nofence();
+        offset_mfmas((kt / kSG) & 1);
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm_lgkm0<0>();  // drain the dead loads before the workgroup exits
+
+  if (!kScaled) return;
+  // Epilogue: lane holds D[m = 4*fc + r][n = fr] of each 16x16 block.
 #pragma unroll
-  for (int j = 0; j < C::kTM; ++j) {
-    const int m = m0 + wm * C::kWTM + j * 16 + fr;
-    if (m >= M) continue;
-    const float s_m = sx[m];
+  for (int i = 0; i < C::kTN; ++i) {
+    const int n = n0 + q_col0 + 16 * i;
+    const float bv = (bias != nullptr && n < N) ? bias[n] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < C::kTN; ++i) {
-      const int n = n0 + wn * C::kWTN + i * 16 + fc * 4;
-      if (n >= N) continue;
-      const int valid = min(4, N - n);
-      float v[4];
+    for (int j = 0; j < C::kTM; ++j) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float b = bias ? bias[min(n + r, N - 1)] : 0.0f;
-        v[r] = fmaf(s_m, acc[i][j][r], b);
-      }
-      const int64_t idx = (int64_t)m * N + n;
-      if (OUT == kOutF32) {
-        float* p = reinterpret_cast<float*>(y) + idx;
-        if (vec_ok && valid == 4) *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-        else for (int r = 0; r < valid; ++r) p[r] = v[r];
-      } else {
-        uint16_t* p = reinterpret_cast<uint16_t*>(y) + idx;
-        if (vec_ok && valid == 4)
-          *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-        else for (int r = 0; r < valid; ++r) p[r] = (uint16_t)f32_to_bf16_rne(v[r]);
+        const int m = m0 + wm * WTM + 16 * j + 4 * fc + r;
+        if (m < M && n < N) store1<OUT>(y, (int64_t)m * N + n, fmaf(sx[m], acc[i][j][r], bv));
       }
     }
   }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WTM, int WTN>
 const char* launch_tile4(const int8_t* a, const float* sx, const int32_t* gsum, const uint8_t* q4,
-                         const void* gs, const void* gb, const float* bias, void* y, int out, int M,
-                         int N, int K, hipStream_t s, const char* name) {
+                         const uint16_t* gs, const uint16_t* gb, const float* bias, void* y,
+                         int out, int M, int N, int K, hipStream_t s, const char* name) {
+  using C = Cfg4<BM, BN, WTM, WTN>;
   const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const dim3 grid((unsigned)tiles), block(256);
-  const __half* hs = reinterpret_cast<const __half*>(gs);
-  const __half* hb = reinterpret_cast<const __half*>(gb);
+  const dim3 grid((unsigned)tiles), block(C::kThreads);
   if (out == kOutF32)
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, kOutF32>), grid, block, 0, s, a, sx, gsum, q4, hs, hb, bias, y, M, N, K);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutF32>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K);
   else if (out == kOutBF16)
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, kOutBF16>), grid, block, 0, s, a, sx, gsum, q4, hs, hb, bias, y, M, N, K);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutBF16>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K);
   else
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, kOutI32>), grid, block, 0, s, a, sx, gsum, q4, hs, hb, bias, y, M, N, K);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutI32>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K);
   return name;
 }
 
@@ -248,15 +355,13 @@ const char* launch_gemm_w4a8(int tile, const int8_t* a, const float* sx, const i
                              const uint8_t* q4, const void* gs, const void* gb,
                              const float* bias, void* y, int out, int M, int N, int K,
                              hipStream_t s) {
-  switch (tile) {
-    case kTile256x256:
-    case kTile256x128:
-      return launch_tile4<256, 128>(a, sx, gsum, q4, gs, gb, bias, y, out, M, N, K, s, "gemm_w4a8_256x128");
-    case kTile128x128:
-      return launch_tile4<128, 128>(a, sx, gsum, q4, gs, gb, bias, y, out, M, N, K, s, "gemm_w4a8_128x128");
-    default:
-      return launch_tile4<64, 64>(a, sx, gsum, q4, gs, gb, bias, y, out, M, N, K, s, "gemm_w4a8_64x64");
-  }
+  const uint16_t* hs = reinterpret_cast<const uint16_t*>(gs);
+  const uint16_t* hb = reinterpret_cast<const uint16_t*>(gb);
+  if (tile == kTile128x256)
+    return launch_tile4<128, 256, 64, 64>(a, sx, gsum, q4, hs, hb, bias, y, out, M, N, K, s,
+                                          "gemm_w4a8_128x256");
+  return launch_tile4<64, 128, 32, 64>(a, sx, gsum, q4, hs, hb, bias, y, out, M, N, K, s,
+                                       "gemm_w4a8_64x128");
 }
 
 }  // namespace kq

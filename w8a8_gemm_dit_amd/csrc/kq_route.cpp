@@ -8,6 +8,7 @@
 #include "kq_route.hpp"
 
 #include <cstdio>
+#include <cstdlib>
 
 namespace kq {
 
@@ -19,12 +20,14 @@ TileShape tile_shape(int32_t tile) {
     case kTile256x192: return {256, 192, 256};
     case kTile256x128: return {256, 128, 256};
     case kTile128x128: return {128, 128, 256};
+    case kTile128x256: return {128, 256, 512};
+    case kTile64x128: return {64, 128, 256};
     default: return {64, 64, 256};
   }
 }
 
 static const char* const kTileNames[kNumTiles] = {"256x256", "256x192", "256x128", "128x128",
-                                                  "64x64"};
+                                                  "64x64",   "128x256", "64x128"};
 
 const char* tile_name(int32_t tile) {
   return (tile >= 0 && tile < kNumTiles) ? kTileNames[tile] : "?";
@@ -90,19 +93,28 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
     r.grid = (N + kGemvCols - 1) / kGemvCols;
     return r;
   }
-  // Tiles each kernel offers; the int4 GEMM keeps fp32 accumulators and
-  // per-group int32 products, so its largest tile is 256x128.
+  // Tiles each kernel offers.  The int4 GEMM keeps fp32 accumulators that
+  // its VALU rescale updates every group, so it uses 64x64 (or 32x64)
+  // blocks per wavefront.
   static const int32_t kW8Tiles[] = {kTile256x256, kTile256x192, kTile256x128, kTile128x128,
                                      kTile64x64};
-  static const int32_t kW4Tiles[] = {kTile256x128, kTile128x128, kTile64x64};
+  static const int32_t kW4Tiles[] = {kTile128x256, kTile64x128};
   const bool w8 = fmt == KQ_W8_PER_CHANNEL;
   const int32_t* cand = w8 ? kW8Tiles : kW4Tiles;
-  const int ncand = w8 ? 5 : 3;
+  const int ncand = w8 ? 5 : 2;
   int32_t tile = -1;
   if (tile_override >= 0 && tile_override < kNumTiles) {
-    for (int i = 0; i < ncand; ++i)
-      if (cand[i] == tile_override) tile = tile_override;
-    if (tile < 0) tile = cand[0];  // a tile this kernel lacks: its largest
+    // a tile this kernel lacks: the one nearest in area (larger on a tie)
+    const TileShape want = tile_shape(tile_override);
+    int64_t best_d = -1;
+    for (int i = 0; i < ncand; ++i) {
+      const TileShape s = tile_shape(cand[i]);
+      const int64_t d = std::llabs((int64_t)s.bm * s.bn - (int64_t)want.bm * want.bn);
+      if (best_d < 0 || d < best_d) {
+        best_d = d;
+        tile = cand[i];
+      }
+    }
   } else {
     // Minimize (waves of 256 workgroups) x (tile area / relative tile
     // efficiency): larger tiles reuse operands better, but a partial last
@@ -112,7 +124,7 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
       const TileShape s = tile_shape(cand[i]);
       const int64_t tiles = ((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
       const int64_t waves = (tiles + 255) / 256;
-      static const double kEff[kNumTiles] = {1.0, 0.97, 0.9, 0.75, 0.45};
+      static const double kEff[kNumTiles] = {1.0, 0.97, 0.9, 0.75, 0.45, 1.0, 0.7};
       const double cost = (double)waves * s.bm * s.bn / kEff[cand[i]];
       if (tile < 0 || cost < best) {
         best = cost;
