@@ -232,6 +232,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="few eager steps of every workload, for profiler runs")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 3 plain device-to-device copies of MIB MiB, the known-size "
+                         "reference that scales HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this build runs on one GPU "
@@ -248,6 +251,16 @@ def main() -> int:
         print("bench.py: device 0 is not a gfx950 GPU", file=sys.stderr)
         return 1
     log(f"device {torch.cuda.get_device_name(0)}")
+
+    if args.copy_probe > 0:
+        n = args.copy_probe << 20
+        src = torch.full((n,), 7, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: 3 copies of {n} bytes")
+        return 0
 
     if args.profile:
         for name, wl in synth.WORKLOADS.items():

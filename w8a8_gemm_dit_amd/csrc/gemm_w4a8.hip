@@ -3,8 +3,9 @@
 //   y[m,n] = sx[m] * sum_g (gs[n,g] * P[m,n,g] + gb[n,g] * A[m,g]) + bias[n]
 // with P the exact int32 product of one 64-wide group of activation codes
 // and unsigned 4-bit weight codes, and A the group sum of the activation
-// codes (MLX pull request 4722, "Kernel design": the bias term folds to
-// biases * sum(x_g)).
+// codes.  This is the affine dequantization w = gs*q + gb (MLX pull request
+// 4722, serving test: affine 4-bit g64) multiplied out: the offset
+// contributes gb times the group's code sum.
 //
 // gfx950 design:
 //   - a workgroup of 8 (or 4) wavefronts computes a BM x BN tile; each
