@@ -53,7 +53,7 @@ def test_workspace_layout():
     (4, 512, 16448, kq.KQ_W8_PER_CHANNEL, "gemm", None, None),
     (17, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemm", None, None),
     (4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 192), 256),
-    (16384, 12288, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 256), 3072),
+    (16384, 12288, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 192), 4096),
     (2048, 12288, 4096, kq.KQ_W4_AFFINE_G64, "gemm", (128, 256), 768),
     (2048, 4096, 12288, kq.KQ_W4_AFFINE_G64, "gemm", (128, 256), 256),
     (100, 640, 256, kq.KQ_W4_AFFINE_G64, "gemm", (64, 128), 10),

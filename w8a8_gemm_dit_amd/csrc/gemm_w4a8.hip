@@ -85,10 +85,10 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
   __shared__ __attribute__((aligned(16))) uint16_t t_gb[kScaled ? 2 : 1][kScaled ? BN : 1][kSG];
   __shared__ __attribute__((aligned(16))) uint16_t t_as[kScaled ? 2 : 1][kScaled ? BM : 1][2 * kSG];
 
-  const int tiles_n = (N + BN - 1) / BN;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int m0 = (tile / tiles_n) * BM;
-  const int n0 = (tile % tiles_n) * BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

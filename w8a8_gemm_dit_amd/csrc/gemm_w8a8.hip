@@ -6,9 +6,11 @@
 // transposed weights).
 //
 // gfx950 design:
-//   - a workgroup of 4 wavefronts (2x2) computes a BM x BN output tile; each
-//     wavefront owns (BM/2) x (BN/2) int32 accumulators built from
-//     v_mfma_i32_16x16x64_i8 (16x16 outputs, K = 64 per instruction);
+//   - a workgroup of 4 (2x2) or 8 (4x2) wavefronts computes a BM x BN output
+//     tile; each wavefront owns its block of int32 accumulators built from
+//     v_mfma_i32_16x16x64_i8 (16x16 outputs, K = 64 per instruction).  With
+//     8 wavefronts (the 256x192 tile) each SIMD runs two, so the MFMA pipe
+//     keeps issuing while one of them waits on a full load queue;
 //   - K advances 64 bytes per step.  Operand tiles move global -> LDS with
 //     buffer_load_dwordx4 ... lds (no staging registers): 64 lanes write
 //     1 KB of LDS per instruction, each lane fetching the global 16-byte
@@ -30,7 +32,8 @@
 //   - the weights are the MFMA A operand and the activations the B operand,
 //     so each lane ends with 4 consecutive output columns of one row;
 //   - workgroup ids are remapped so each XCD (ids congruent mod 8) works on
-//     a contiguous block of tiles that share operand panels in its L2;
+//     a compact 2-D block of tiles (groups of 4 tile rows walked column by
+//     column) whose operand panels its L2 shares;
 //   - epilogue: fp32 acc * (sx[m]*sw[n]) + bias[n] with one fma, rounded
 //     once to fp32 or bf16 (round-to-nearest-even).
 #include "kq_common.hpp"
@@ -41,17 +44,24 @@ namespace kq {
 
 namespace {
 
-template <int BM, int BN>
+template <int BM, int BN, int WM, int WN>
 struct Cfg {
-  static constexpr int kThreads = 256;
-  static constexpr int kWTM = BM / 2;  // wave tile rows (m)
-  static constexpr int kWTN = BN / 2;  // wave tile columns (n)
+  static constexpr int kWaves = WM * WN;     // wavefront grid WM (rows) x WN (columns)
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kWTM = BM / WM;       // wave tile rows (m)
+  static constexpr int kWTN = BN / WN;       // wave tile columns (n)
   static constexpr int kTM = kWTM / 16;
   static constexpr int kTN = kWTN / 16;
-  static constexpr int kRows = BM + BN;            // LDS rows per step (A rows, then W rows)
-  static constexpr int kSlots = kRows * 4;         // 16-byte slots per step
-  static constexpr int kLPW = kRows / 64;          // 1 KB DMA blocks per wave per step
-  static_assert(kRows % 64 == 0 && BM % 64 == 0 && BN % 32 == 0, "tile shape");
+  static constexpr int kRows = BM + BN;      // LDS rows per step (A rows, then W rows)
+  static constexpr int kSlots = kRows * 4;   // 16-byte slots per step
+  static constexpr int kBlocks = kRows / 16; // 1 KB DMA blocks per step
+  // The first kDmaWaves waves move kLPW consecutive blocks each, the rest
+  // none (their vmcnt waits are then no-ops; the barrier covers them).
+  static constexpr int kLPW = (kBlocks + kWaves - 1) / kWaves;
+  static constexpr int kDmaWaves = kBlocks / kLPW;
+  static_assert(kBlocks % kLPW == 0, "DMA blocks split into whole per-wave runs");
+  static_assert(kRows % 64 == 0 && BM % 64 == 0 && BN % 32 == 0 && kTM >= 1 && kTN >= 1,
+                "tile shape");
 };
 
 // LDS row swizzle: the 16-byte chunk index of row r is XORed with
@@ -102,26 +112,36 @@ __device__ __forceinline__ void store4(void* y, int64_t idx, const float v[4], c
   }
 }
 
-// REM: K % 256 != 0, so up to 3 K steps follow the 4-step loop.  The
+// RING: LDS ring slots (4 or 5); the K loop is unrolled by RING steps (2*RING
+// when RING is odd, so the two fragment buffers line up again).  REM: K is
+// not a multiple of that unroll, so guarded tail steps follow the loop; the
 // conditional tail makes the register allocator copy accumulators at the
 // loop back-edge, so it is compiled only into the variant that needs it.
-template <int BM, int BN, int OUT, bool REM>
-__global__ __launch_bounds__(256) void gemm_w8a8_kernel(
+template <int RING>
+struct Unroll {
+  static constexpr int kSteps = (RING % 2 == 0) ? RING : 2 * RING;
+};
+
+template <int BM, int BN, int WM, int WN, int RING, int OUT, bool REM>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int8_t* __restrict__ W,
     const float* __restrict__ sw, const float* __restrict__ bias, void* __restrict__ y, int M,
     int N, int K) {
-  using C = Cfg<BM, BN>;
+  using C = Cfg<BM, BN, WM, WN>;
+  static_assert(RING == 4 || RING == 5, "ring depth");
+  constexpr int U = Unroll<RING>::kSteps;
   __shared__ int4 lds0[C::kSlots], lds1[C::kSlots], lds2[C::kSlots], lds3[C::kSlots];
+  __shared__ int4 lds4[RING > 4 ? C::kSlots : 1];
 
-  const int tiles_n = (N + BN - 1) / BN;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int m0 = (tile / tiles_n) * BM;
-  const int n0 = (tile % tiles_n) * BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA bases stay scalar
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
+  const int wm = wave % WM;
+  const int wn = wave / WM;
 
   // Buffer descriptors rebased on this tile's first row: rows past the
   // matrix edge fall outside num_records and read as zero.
@@ -130,23 +150,27 @@ __global__ __launch_bounds__(256) void gemm_w8a8_kernel(
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(W + (int64_t)n0 * K), 0, min(BN, N - n0) * K, 0x00020000);
 
-  // DMA plan: wave w moves 1 KB blocks b = w + 4*i (rows 16b..16b+15);
-  // lane l fills slot 64*b + l: row r = 16*b + l/4, physical chunk l%4,
-  // holding logical chunk (l%4) ^ swz(r).  swz(r) does not depend on i, so
-  // block i reads at the thread's base offset plus 64*i rows.  Blocks
-  // i < BM/64 are activation rows, the rest weight rows.
-  const int rb = 16 * wave + (lane >> 2);
+  // DMA plan: wave w < kDmaWaves moves 1 KB blocks b = w*kLPW + i (rows
+  // 16b..16b+15); lane l fills slot 64*b + l: row r = 16*b + l/4, physical
+  // chunk l%4, holding logical chunk (l%4) ^ swz(r).  swz(r) depends on r%16
+  // only, so every block uses the same per-lane offset (row l/4 of the block)
+  // and the block's first row goes into the scalar offset, which the buffer
+  // addressing needs non-negative.  Blocks b < BM/16 are activation rows,
+  // the rest weight rows.
+  const int rb = lane >> 2;
   const uint32_t voff = (uint32_t)(rb * K + (((lane & 3) ^ swz(rb)) * 16));
   const int KT = K / 64;
   auto issue = [&](int4* slot, int kt) {
+    if (wave >= C::kDmaWaves) return;
     const int ks = min(kt, KT - 1) * 64;  // steps past the end re-load the last slice
 #pragma unroll
     for (int i = 0; i < C::kLPW; ++i) {
-      lds_ptr_t dst = (lds_ptr_t)(slot + 64 * (wave + 4 * i));
-      if (i < BM / 64)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, voff, ks + 64 * i * K, 0, 0);
+      const int b = wave * C::kLPW + i;
+      lds_ptr_t dst = (lds_ptr_t)(slot + 64 * b);
+      if (b < BM / 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, voff, ks + 16 * b * K, 0, 0);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, voff, ks + (64 * i - BM) * K, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, voff, ks + (16 * b - BM) * K, 0, 0);
     }
   };
 
@@ -184,46 +208,107 @@ __global__ __launch_bounds__(256) void gemm_w8a8_kernel(
       for (int j = 0; j < C::kTM; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.w[i], f.a[j], acc[i][j], 0, 0, 0);
   };
-  // One step: (1) wait until step kt+1 has landed (at most 2 later steps of
-  // this wave's loads in flight) and this wave's reads of step kt's slot are
-  // done, then barrier; (2) issue the reads of step kt+1's fragments and
-  // refill step kt's slot with step kt+4, interleaved with (3) the MFMAs on
-  // step kt's fragments, so all three overlap.  The scheduling
+  // One step: (1) wait until step kt+1 has landed (at most RING-2 later
+  // steps of this wave's loads in flight) and this wave's reads of step kt's
+  // slot are done, then barrier; (2) issue the reads of step kt+1's fragments
+  // and refill step kt's slot with step kt+RING, interleaved with (3) the
+  // MFMAs on step kt's fragments, so all three overlap.  The scheduling
   // groups spread the reads and loads between the MFMAs.
   auto step = [&](Frags& cur, Frags& nxt, int4* cur_slot, const int4* nxt_slot, int kt) {
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm_lgkm0<2 * C::kLPW>();
+    wait_vm_lgkm0<(RING - 2) * C::kLPW>();
     barrier_nofence();
     read_frags(nxt, nxt_slot);
-    issue(cur_slot, kt + 4);
+    issue(cur_slot, kt + RING);
     mfmas(cur);
     interleave_step<C::kTM * C::kTN, C::kTM + C::kTN, C::kLPW>();
   };
+  // slot of step j (compile-time j): the ring arrays in turn
+#define KQ_SLOT(j)                                                                        \
+  ((j) % RING == 0 ? lds0 : (j) % RING == 1 ? lds1 : (j) % RING == 2 ? lds2             \
+   : (j) % RING == 3 ? lds3 : lds4)
+#define KQ_STEP(j) step((j) % 2 ? f1 : f0, (j) % 2 ? f0 : f1, KQ_SLOT(j), KQ_SLOT((j) + 1), kt + (j))
 
   Frags f0, f1;
   issue(lds0, 0);
   issue(lds1, 1);
   issue(lds2, 2);
   issue(lds3, 3);
-  wait_vm_lgkm0<3 * C::kLPW>();
+  if (RING > 4) issue(lds4, 4);
+  wait_vm_lgkm0<(RING - 1) * C::kLPW>();
   barrier_nofence();
   read_frags(f0, lds0);
   int kt = 0;
-  for (; kt + 4 <= KT; kt += 4) {
-    step(f0, f1, lds0, lds1, kt);
-    step(f1, f0, lds1, lds2, kt + 1);
-    step(f0, f1, lds2, lds3, kt + 2);
-    step(f1, f0, lds3, lds0, kt + 3);
+  for (; kt + U <= KT; kt += U) {
+    KQ_STEP(0); KQ_STEP(1); KQ_STEP(2); KQ_STEP(3);
+    if (U > 4) { KQ_STEP(4); KQ_STEP(5); KQ_STEP(6); KQ_STEP(7); KQ_STEP(8); KQ_STEP(9); }
   }
-  if (REM) {  // K steps beyond a multiple of 4
-    if (kt < KT) step(f0, f1, lds0, lds1, kt);
-    if (kt + 1 < KT) step(f1, f0, lds1, lds2, kt + 1);
-    if (kt + 2 < KT) step(f0, f1, lds2, lds3, kt + 2);
+  if (REM) {  // the K steps beyond a multiple of U
+    if (kt < KT) KQ_STEP(0);
+    if (kt + 1 < KT) KQ_STEP(1);
+    if (kt + 2 < KT) KQ_STEP(2);
+    if (U > 4) {
+      if (kt + 3 < KT) KQ_STEP(3);
+      if (kt + 4 < KT) KQ_STEP(4);
+      if (kt + 5 < KT) KQ_STEP(5);
+      if (kt + 6 < KT) KQ_STEP(6);
+      if (kt + 7 < KT) KQ_STEP(7);
+      if (kt + 8 < KT) KQ_STEP(8);
+    }
   }
+#undef KQ_STEP
+#undef KQ_SLOT
   __builtin_amdgcn_sched_barrier(0);
   wait_vm_lgkm0<0>();  // drain the dead loads before the workgroup exits
 
   // Epilogue: lane holds D[n = nb + 4*(lane/16) + r][m = mb + lane%16].
+  // bf16 output of a full tile goes through LDS: each wavefront writes its
+  // block, row-major, into a free ring slot and then stores whole 16-byte
+  // row chunks (non-temporal), instead of 8-byte pieces of 16 rows.
+  constexpr int kStage = C::kWTM * C::kWTN * 2;          // bytes of one wave's bf16 block
+  constexpr int kPerSlot = (C::kSlots * 16) / kStage;    // blocks per ring slot
+  constexpr int kRowChunks = C::kWTN / 8;                // 16-byte chunks per block row
+  if (OUT == kOutBF16 && kPerSlot * 4 >= C::kWaves && (N % 8) == 0 && m0 + BM <= M &&
+      n0 + BN <= N) {
+    __builtin_amdgcn_sched_barrier(0);
+    barrier_nofence();  // every wave is done with the ring (its loads drained above)
+    const int sidx = wave / kPerSlot;
+    char* stage = reinterpret_cast<char*>(sidx == 0 ? lds0 : sidx == 1 ? lds1 : sidx == 2 ? lds2 : lds3) +
+                  (wave % kPerSlot) * kStage;
+    float s_m[C::kTM];
+#pragma unroll
+    for (int j = 0; j < C::kTM; ++j) s_m[j] = sx[m0 + wm * C::kWTM + j * 16 + fr];
+#pragma unroll
+    for (int i = 0; i < C::kTN; ++i) {
+      const int n = n0 + wn * C::kWTN + i * 16 + fc * 4;
+      // sw and bias are only 4-byte aligned by contract: scalar loads
+      const float4 swv = make_float4(sw[n], sw[n + 1], sw[n + 2], sw[n + 3]);
+      const float4 bv = bias ? make_float4(bias[n], bias[n + 1], bias[n + 2], bias[n + 3])
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int c = 2 * i + (fc >> 1);  // 16-byte chunk of the block row
+#pragma unroll
+      for (int j = 0; j < C::kTM; ++j) {
+        const int r = 16 * j + fr;
+        const float sm = s_m[j];
+        const uint32_t lo = pack_bf16x2(fmaf(sm * swv.x, (float)acc[i][j][0], bv.x),
+                                        fmaf(sm * swv.y, (float)acc[i][j][1], bv.y));
+        const uint32_t hi = pack_bf16x2(fmaf(sm * swv.z, (float)acc[i][j][2], bv.z),
+                                        fmaf(sm * swv.w, (float)acc[i][j][3], bv.w));
+        *reinterpret_cast<uint2*>(stage + r * (C::kWTN * 2) + ((c ^ (r & 3)) * 16) + (fc & 1) * 8) =
+            make_uint2(lo, hi);
+      }
+    }
+    uint16_t* yb = reinterpret_cast<uint16_t*>(y) + (int64_t)(m0 + wm * C::kWTM) * N + n0 +
+                   wn * C::kWTN;
+#pragma unroll
+    for (int u = 0; u < C::kWTM * kRowChunks / 64; ++u) {
+      const int e = lane + 64 * u;
+      const int r = e / kRowChunks, c = e % kRowChunks;
+      const v4i v = *reinterpret_cast<const v4i*>(stage + r * (C::kWTN * 2) + ((c ^ (r & 3)) * 16));
+      __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(yb + (int64_t)r * N + 8 * c));
+    }
+    return;
+  }
   const bool vec_ok = (N % 4) == 0;
   float s_m[C::kTM];
 #pragma unroll
@@ -258,27 +343,27 @@ __global__ __launch_bounds__(256) void gemm_w8a8_kernel(
   }
 }
 
-template <int BM, int BN, bool REM>
+template <int BM, int BN, int WM, int WN, int RING, bool REM>
 void launch_rem(const int8_t* a, const float* sx, const int8_t* q, const float* sw,
                 const float* bias, void* y, int out, int M, int N, int K, hipStream_t s) {
   const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const dim3 grid((unsigned)tiles), block(256);
+  const dim3 grid((unsigned)tiles), block(64 * WM * WN);
   if (out == kOutF32)
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, kOutF32, REM>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, RING, kOutF32, REM>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
   else if (out == kOutBF16)
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, kOutBF16, REM>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, RING, kOutBF16, REM>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
   else
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, kOutI32, REM>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, RING, kOutI32, REM>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WM = 2, int WN = 2, int RING = 4>
 const char* launch_tile(const int8_t* a, const float* sx, const int8_t* q, const float* sw,
                         const float* bias, void* y, int out, int M, int N, int K,
                         hipStream_t s, const char* name) {
-  if (K % 256 == 0)
-    launch_rem<BM, BN, false>(a, sx, q, sw, bias, y, out, M, N, K, s);
+  if ((K / 64) % Unroll<RING>::kSteps == 0)
+    launch_rem<BM, BN, WM, WN, RING, false>(a, sx, q, sw, bias, y, out, M, N, K, s);
   else
-    launch_rem<BM, BN, true>(a, sx, q, sw, bias, y, out, M, N, K, s);
+    launch_rem<BM, BN, WM, WN, RING, true>(a, sx, q, sw, bias, y, out, M, N, K, s);
   return name;
 }
 
@@ -291,7 +376,7 @@ const char* launch_gemm_w8a8(int tile, const int8_t* a, const float* sx, const i
     case kTile256x256:
       return launch_tile<256, 256>(a, sx, q, sw, bias, y, out, M, N, K, s, "gemm_w8a8_256x256");
     case kTile256x192:
-      return launch_tile<256, 192>(a, sx, q, sw, bias, y, out, M, N, K, s, "gemm_w8a8_256x192");
+      return launch_tile<256, 192, 4, 2>(a, sx, q, sw, bias, y, out, M, N, K, s, "gemm_w8a8_256x192");
     case kTile256x128:
       return launch_tile<256, 128>(a, sx, q, sw, bias, y, out, M, N, K, s, "gemm_w8a8_256x128");
     case kTile128x128:

@@ -76,6 +76,23 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return (bid % kXcds) * per + bid / kXcds;
 }
 
+// Output tile of workgroup `bid` in a tiles_m x tiles_n grid: XCD-contiguous
+// index ranges (xcd_remap), walked in groups of kGroupRows tile rows,
+// column by column.  The tiles an XCD runs at the same time then form a
+// compact block (4 rows x 8 columns for 32 CUs), so its L2 fetches fewer
+// distinct activation and weight panels than with a row-major walk.
+__device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_m, int tiles_n,
+                                            int& tm, int& tn) {
+  constexpr int kGroupRows = 4;
+  const int t = xcd_remap(bid, nblocks);
+  const int group = t / (kGroupRows * tiles_n);
+  const int first = group * kGroupRows;
+  const int rows = min(tiles_m - first, kGroupRows);  // the last group may be shorter
+  const int r = t - group * kGroupRows * tiles_n;
+  tm = first + r % rows;
+  tn = r / rows;
+}
+
 // LDS pointer type taken by the direct global->LDS buffer loads.
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 

@@ -17,7 +17,7 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 TileShape tile_shape(int32_t tile) {
   switch (tile) {
     case kTile256x256: return {256, 256, 256};
-    case kTile256x192: return {256, 192, 256};
+    case kTile256x192: return {256, 192, 512};
     case kTile256x128: return {256, 128, 256};
     case kTile128x128: return {128, 128, 256};
     case kTile128x256: return {128, 256, 512};
@@ -124,7 +124,7 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
       const TileShape s = tile_shape(cand[i]);
       const int64_t tiles = ((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
       const int64_t waves = (tiles + 255) / 256;
-      static const double kEff[kNumTiles] = {1.0, 0.97, 0.9, 0.75, 0.45, 1.0, 0.7};
+      static const double kEff[kNumTiles] = {0.95, 1.0, 0.9, 0.75, 0.45, 1.0, 0.7};
       const double cost = (double)waves * s.bm * s.bn / kEff[cand[i]];
       if (tile < 0 || cost < best) {
         best = cost;

@@ -14,7 +14,7 @@ namespace kq {
 // Tile configurations of the W8A8 (ids 0-4) and W4A8 (ids 5-6) GEMM kernels.
 enum GemmTile : int32_t {
   kTile256x256 = 0,  // 256 rows x 256 columns, 4 waves of 128x128
-  kTile256x192 = 1,  // 256 x 192, 4 waves of 128x96
+  kTile256x192 = 1,  // 256 x 192, 8 waves of 64x96 (4x2)
   kTile256x128 = 2,  // 256 x 128, 4 waves of 128x64 (2x2)
   kTile128x128 = 3,  // 128 x 128, 4 waves of 64x64
   kTile64x64 = 4,    // 64 x 64, 4 waves of 32x32 (thin shapes)
