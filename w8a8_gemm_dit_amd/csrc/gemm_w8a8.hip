@@ -55,9 +55,15 @@ struct Cfg {
   static constexpr int kRows = BM + BN;      // LDS rows per step (A rows, then W rows)
   static constexpr int kSlots = kRows * 4;   // 16-byte slots per step
   static constexpr int kBlocks = kRows / 16; // 1 KB DMA blocks per step
-  // The first kDmaWaves waves move kLPW consecutive blocks each, the rest
-  // none (their vmcnt waits are then no-ops; the barrier covers them).
-  static constexpr int kLPW = (kBlocks + kWaves - 1) / kWaves;
+  // The first kDmaWaves waves move kLPW consecutive blocks each (the
+  // smallest divisor of kBlocks that covers them all), the rest none (their
+  // vmcnt waits are then no-ops; the barrier covers them).
+  static constexpr int lpw() {
+    int d = (kBlocks + kWaves - 1) / kWaves;
+    while (kBlocks % d != 0) ++d;
+    return d;
+  }
+  static constexpr int kLPW = lpw();
   static constexpr int kDmaWaves = kBlocks / kLPW;
   static_assert(kBlocks % kLPW == 0, "DMA blocks split into whole per-wave runs");
   static_assert(kRows % 64 == 0 && BM % 64 == 0 && BN % 32 == 0 && kTM >= 1 && kTN >= 1,
