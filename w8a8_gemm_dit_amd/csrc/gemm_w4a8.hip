@@ -319,6 +319,45 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
 
   if (!kScaled) return;
   // Epilogue: lane holds D[m = 4*fc + r][n = fr] of each 16x16 block.
+  // bf16 output of a full tile goes through LDS: each wavefront writes its
+  // block row-major into a free ring slot (16-byte chunk index XORed with
+  // row % 8) and stores whole 16-byte row chunks, instead of scattered
+  // 2-byte values.
+  constexpr int kStage = WTM * WTN * 2;                  // bytes of one wave's bf16 block
+  constexpr int kPerSlot = (C::kSlots * 16) / kStage;    // blocks per ring slot
+  constexpr int kRowChunks = WTN / 8;                    // 16-byte chunks per block row
+  if (OUT == kOutBF16 && kPerSlot * 4 >= C::kWaves && kRowChunks >= 8 && (N % 8) == 0 &&
+      m0 + BM <= M && n0 + BN <= N) {
+    __builtin_amdgcn_sched_barrier(0);
+    barrier_nofence();  // every wave is done with the ring (its loads drained above)
+    const int sidx = wave / kPerSlot;
+    char* stage = reinterpret_cast<char*>(sidx == 0 ? lds0 : sidx == 1 ? lds1 : sidx == 2 ? lds2 : lds3) +
+                  (wave % kPerSlot) * kStage;
+#pragma unroll
+    for (int i = 0; i < C::kTN; ++i) {
+      const int cl = 16 * i + fr;  // column within the block
+      const float bv = bias != nullptr ? bias[n0 + q_col0 + 16 * i] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < C::kTM; ++j) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rl = 16 * j + 4 * fc + r;  // row within the block
+          const float v = fmaf(sx[m0 + wm * WTM + rl], acc[i][j][r], bv);
+          *reinterpret_cast<uint16_t*>(stage + rl * (WTN * 2) + (((cl >> 3) ^ (rl & 7)) * 16) +
+                                       (cl & 7) * 2) = (uint16_t)f32_to_bf16_rne(v);
+        }
+      }
+    }
+    uint16_t* yb = reinterpret_cast<uint16_t*>(y) + (int64_t)(m0 + wm * WTM) * N + n0 + wn * WTN;
+#pragma unroll
+    for (int u = 0; u < WTM * kRowChunks / 64; ++u) {
+      const int e = lane + 64 * u;
+      const int rl = e / kRowChunks, c = e % kRowChunks;
+      const v4i v = *reinterpret_cast<const v4i*>(stage + rl * (WTN * 2) + ((c ^ (rl & 7)) * 16));
+      __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(yb + (int64_t)rl * N + 8 * c));
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < C::kTN; ++i) {
     const int n = n0 + q_col0 + 16 * i;
