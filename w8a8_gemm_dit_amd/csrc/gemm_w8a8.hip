@@ -14,21 +14,24 @@
 //   - K advances 64 bytes per step.  Operand tiles move global -> LDS with
 //     buffer_load_dwordx4 ... lds (no staging registers): 64 lanes write
 //     1 KB of LDS per instruction, each lane fetching the global 16-byte
-//     chunk that belongs at its LDS slot, so the tile lands with 64-byte
-//     rows whose 16-byte chunk index is XORed with (row/4)%4 and every
-//     16-lane phase of the fragment ds_read_b128 hits 16 distinct banks;
-//   - a 4-slot LDS ring keeps 3 steps of loads in flight, and fragments are
+//     chunk that belongs at its LDS slot.  One instruction covers 8 rows x
+//     128 bytes, i.e. two K steps of 8 whole cache lines: a CU's load path
+//     moves about 1.7x more bytes per clock that way than with 16 rows of
+//     64 bytes (half lines).  In LDS the rows are 64 bytes with the 16-byte
+//     chunk index XOR-swizzled per row, so every 16-lane phase of the
+//     fragment ds_read_b128 hits 16 distinct banks;
+//   - two pair buffers (4 K steps) form the ring, and fragments are
 //     software-pipelined: step k reads step k+1's fragments while its MFMAs
-//     run on step k's, then refills the slot step k was read from.  Each
-//     step costs one s_waitcnt of known depth and one barrier without a
-//     memory fence.  Each ring slot is its own LDS array (the compiler
-//     tracks the asynchronous LDS writes per array, so reads of one slot
-//     never wait for loads landing in another), the K loop is unrolled by
-//     4, and scheduling barriers between steps keep the accumulators in
-//     place in AGPRs;
+//     run on step k's; each odd step refills the pair it has finished with
+//     the pair two ahead.  Each step costs one s_waitcnt of known depth and
+//     one barrier without a memory fence.  Each pair buffer is its own LDS
+//     array (the compiler tracks the asynchronous LDS writes per array, so
+//     reads of one buffer never wait for loads landing in the other), the K
+//     loop is unrolled by 4, and scheduling barriers between steps keep the
+//     accumulators in place;
 //   - no data-dependent branches: buffer descriptors are rebased per
 //     workgroup so rows past M or N read as zero, and loads past the last
-//     K step re-load the final slice into slots that are never read;
+//     K step re-load the final pair into a buffer that is never read;
 //   - the weights are the MFMA A operand and the activations the B operand,
 //     so each lane ends with 4 consecutive output columns of one row;
 //   - workgroup ids are remapped so each XCD (ids congruent mod 8) works on
@@ -36,6 +39,8 @@
 //     column) whose operand panels its L2 shares;
 //   - epilogue: fp32 acc * (sx[m]*sw[n]) + bias[n] with one fma, rounded
 //     once to fp32 or bf16 (round-to-nearest-even).
+#include <type_traits>
+
 #include "kq_common.hpp"
 #include "kq_launch.hpp"
 #include "kq_route.hpp"
@@ -52,9 +57,9 @@ struct Cfg {
   static constexpr int kWTN = BN / WN;       // wave tile columns (n)
   static constexpr int kTM = kWTM / 16;
   static constexpr int kTN = kWTN / 16;
-  static constexpr int kRows = BM + BN;      // LDS rows per step (A rows, then W rows)
-  static constexpr int kSlots = kRows * 4;   // 16-byte slots per step
-  static constexpr int kBlocks = kRows / 16; // 1 KB DMA blocks per step
+  static constexpr int kRows = BM + BN;      // LDS rows (A rows, then W rows)
+  static constexpr int kBlocks = kRows / 8;  // 1 KB DMA blocks per pair of K steps
+  static constexpr int kPairSlots = kBlocks * 64;  // 16-byte slots of one pair buffer
   // The first kDmaWaves waves move kLPW consecutive blocks each (the
   // smallest divisor of kBlocks that covers them all), the rest none (their
   // vmcnt waits are then no-ops; the barrier covers them).
@@ -65,38 +70,56 @@ struct Cfg {
   }
   static constexpr int kLPW = lpw();
   static constexpr int kDmaWaves = kBlocks / kLPW;
-  static_assert(kBlocks % kLPW == 0, "DMA blocks split into whole per-wave runs");
-  static_assert(kRows % 64 == 0 && BM % 64 == 0 && BN % 32 == 0 && kTM >= 1 && kTN >= 1,
-                "tile shape");
+  static_assert(kBlocks % kLPW == 0 && kLPW < 64, "DMA blocks split into whole per-wave runs");
+  static_assert(BM % 64 == 0 && BN % 32 == 0 && kTM >= 1 && kTN >= 1, "tile shape");
 };
 
 // LDS row swizzle: the 16-byte chunk index of row r is XORed with
-// ((r/2)%4) ^ ((r/8)%2).  A fragment read (16 consecutive rows, one chunk)
-// then touches 16 distinct 16-byte bank groups per 16 lanes and 8 distinct
-// ones per 8 lanes, so it is conflict-free whether the LDS serves 8 or 16
-// lanes of a ds_read_b128 per clock.  The value depends on r % 16 only.
+// ((r/2)%4) ^ ((r/8)%2).  Rows r and r+8 sit a multiple of 256 bytes apart,
+// so a fragment read (16 consecutive rows, one chunk) touches 16 distinct
+// 16-byte bank groups per 16 lanes and 8 distinct ones per 8 lanes: it is
+// conflict-free whether the LDS serves 8 or 16 lanes of a ds_read_b128 per
+// clock.  The value depends on r % 16 only.
 __device__ __forceinline__ int swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
 
-__device__ __forceinline__ int slot_of(int row, int chunk) { return row * 4 + (chunk ^ swz(row)); }
+// A pair buffer holds two consecutive K steps (64 bytes of every row each)
+// as 1 KB blocks of 8 rows: [step 2p: 8 rows x 64 B][step 2p+1: 8 rows x
+// 64 B].  One DMA instruction fills one block, so each of its 8 rows is
+// read as one whole 128-byte line (16 rows of 64 bytes would touch twice as
+// many lines per instruction for the same bytes, which halves the load
+// throughput of a CU).  16-byte slot of (row, logical chunk) in half h:
+__device__ __forceinline__ int pair_slot(int row, int chunk, int h) {
+  return (row >> 3) * 64 + h * 32 + (row & 7) * 4 + (chunk ^ swz(row));
+}
 
-
-// Instruction interleave of one K step: NV groups of [MFMA x a, DS read x b,
-// MFMA x a, VMEM x 1], then the leftovers, so the MFMA pipe stays busy while
-// the fragment reads and the LDS DMA loads issue (sched_group_barrier mask
-// bits: 0x008 MFMA, 0x100 DS read, 0x020 VMEM read).
+// Instruction interleave of one K step.  Steps that refill a pair buffer:
+// NV groups of [MFMA x a, DS read x b, MFMA x a, VMEM x 1], then the
+// leftovers; the other steps: ND groups of [MFMA x a, DS read x 1].  The
+// MFMA pipe stays busy while the fragment reads and the LDS DMA loads issue
+// (sched_group_barrier mask bits: 0x008 MFMA, 0x100 DS read, 0x020 VMEM).
 template <int NM, int ND, int NV>
 __device__ __forceinline__ void interleave_step() {
-  constexpr int a = NM / (2 * NV);
-  constexpr int b = ND / NV;
+  if constexpr (NV == 0) {
+    constexpr int a = NM / ND;
 #pragma unroll
-  for (int g = 0; g < NV; ++g) {
-    __builtin_amdgcn_sched_group_barrier(0x008, a, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, b, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, a, 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    for (int g = 0; g < ND; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, a, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - a * ND, 0);
+  } else {
+    constexpr int a = NM / (2 * NV) > 0 ? NM / (2 * NV) : 1;
+    constexpr int b = ND / NV;
+#pragma unroll
+    for (int g = 0; g < NV; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, a, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, b, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, a, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, ND - b * NV, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - 2 * a * NV > 0 ? NM - 2 * a * NV : 0, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, ND - b * NV, 0);
-  __builtin_amdgcn_sched_group_barrier(0x008, NM - 2 * a * NV, 0);
 }
 
 template <int OUT>
@@ -118,26 +141,20 @@ __device__ __forceinline__ void store4(void* y, int64_t idx, const float v[4], c
   }
 }
 
-// RING: LDS ring slots (4 or 5); the K loop is unrolled by RING steps (2*RING
-// when RING is odd, so the two fragment buffers line up again).  REM: K is
-// not a multiple of that unroll, so guarded tail steps follow the loop; the
-// conditional tail makes the register allocator copy accumulators at the
-// loop back-edge, so it is compiled only into the variant that needs it.
-template <int RING>
-struct Unroll {
-  static constexpr int kSteps = (RING % 2 == 0) ? RING : 2 * RING;
-};
-
-template <int BM, int BN, int WM, int WN, int RING, int OUT, bool REM>
+// The K loop is unrolled by 4 steps (two pair buffers).  REM: K/64 is not a
+// multiple of 4, so guarded tail steps follow the loop; the conditional
+// tail makes the register allocator copy accumulators at the loop back-edge,
+// so it is compiled only into the variant that needs it.
+template <int BM, int BN, int WM, int WN, int OUT, bool REM>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int8_t* __restrict__ W,
     const float* __restrict__ sw, const float* __restrict__ bias, void* __restrict__ y, int M,
     int N, int K) {
   using C = Cfg<BM, BN, WM, WN>;
-  static_assert(RING == 4 || RING == 5, "ring depth");
-  constexpr int U = Unroll<RING>::kSteps;
-  __shared__ int4 lds0[C::kSlots], lds1[C::kSlots], lds2[C::kSlots], lds3[C::kSlots];
-  __shared__ int4 lds4[RING > 4 ? C::kSlots : 1];
+  // Two pair buffers (steps 4i, 4i+1 and 4i+2, 4i+3): each its own array,
+  // so the compiler's tracking of the asynchronous LDS writes never couples
+  // reads of one buffer to loads landing in the other.
+  __shared__ int4 lds0[C::kPairSlots], lds1[C::kPairSlots];
 
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
@@ -156,27 +173,37 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(W + (int64_t)n0 * K), 0, min(BN, N - n0) * K, 0x00020000);
 
-  // DMA plan: wave w < kDmaWaves moves 1 KB blocks b = w*kLPW + i (rows
-  // 16b..16b+15); lane l fills slot 64*b + l: row r = 16*b + l/4, physical
-  // chunk l%4, holding logical chunk (l%4) ^ swz(r).  swz(r) depends on r%16
-  // only, so every block uses the same per-lane offset (row l/4 of the block)
-  // and the block's first row goes into the scalar offset, which the buffer
-  // addressing needs non-negative.  Blocks b < BM/16 are activation rows,
+  // DMA plan: wave w < kDmaWaves moves blocks b = w*kLPW + i (rows 8b..8b+7
+  // of the pair); lane l fills slot 64*b + l: half h = l/32 (the pair's
+  // step), row r = 8*b + (l%32)/4, physical chunk l%4 holding logical chunk
+  // (l%4) ^ swz(r).  swz(r) depends on (l%32)/4 and the parity of b only,
+  // so two per-lane offsets serve every block; the block's first row and
+  // the pair's K offset go into the scalar offset, which the buffer
+  // addressing needs non-negative.  Blocks b < BM/8 are activation rows,
   // the rest weight rows.
-  const int rb = lane >> 2;
-  const uint32_t voff = (uint32_t)(rb * K + (((lane & 3) ^ swz(rb)) * 16));
+  const int rr = (lane & 31) >> 2;
+  const uint32_t vbase = (uint32_t)(rr * K + (lane >> 5) * 64);
+  const uint32_t voff0 = vbase + (uint32_t)(((lane & 3) ^ ((rr >> 1) & 3)) * 16);
+  const uint32_t voff1 = vbase + (uint32_t)(((lane & 3) ^ ((rr >> 1) & 3) ^ 1) * 16);
   const int KT = K / 64;
-  auto issue = [&](int4* slot, int kt) {
-    if (wave >= C::kDmaWaves) return;
-    const int ks = min(kt, KT - 1) * 64;  // steps past the end re-load the last slice
+  // Fill a pair buffer with K steps 2*pi and 2*pi+1.  Pairs past the end
+  // re-load the last one into a buffer that is never read again; with an
+  // odd step count the last pair's second half holds bytes past the row
+  // (the next row's, or zeros past the descriptor), which no step reads.
+  auto issue = [&](int4* buf, int pi) {
+    // (a branch here would split the step's basic block and keep the
+    // scheduler from interleaving the loads with the MFMAs)
+    if (C::kDmaWaves < C::kWaves && wave >= C::kDmaWaves) return;
+    const int ks = min(pi, (KT - 1) >> 1) * 128;
 #pragma unroll
     for (int i = 0; i < C::kLPW; ++i) {
       const int b = wave * C::kLPW + i;
-      lds_ptr_t dst = (lds_ptr_t)(slot + 64 * b);
-      if (b < BM / 16)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, voff, ks + 16 * b * K, 0, 0);
+      lds_ptr_t dst = (lds_ptr_t)(buf + 64 * b);
+      const uint32_t vo = (b & 1) ? voff1 : voff0;
+      if (b < BM / 8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, vo, ks + 8 * b * K, 0, 0);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, voff, ks + (16 * b - BM) * K, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, vo, ks + (8 * b - BM) * K, 0, 0);
     }
   };
 
@@ -188,9 +215,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
 
   const int fr = lane & 15;  // fragment row within a 16-row tile
   const int fc = lane >> 4;  // fragment 16-byte chunk
-  // Fragment slots: 16-row tile j sits 64 slots after tile j-1.
-  const int a_slot0 = slot_of(wm * C::kWTM + fr, fc);
-  const int w_slot0 = slot_of(BM + wn * C::kWTN + fr, fc);
+  // Fragment slots in the first half of a pair buffer: 16-row tile j sits
+  // 128 slots (two blocks) after tile j-1; the second half is 32 slots on.
+  const int a_slot0 = pair_slot(wm * C::kWTM + fr, fc, 0);
+  const int w_slot0 = pair_slot(BM + wn * C::kWTN + fr, fc, 0);
 
   struct Frags {
     v4i a[C::kTM], w[C::kTN];
@@ -198,12 +226,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
   auto read_frags = [&](Frags& f, const int4* slot) {
 #pragma unroll
     for (int j = 0; j < C::kTM; ++j) {
-      const int4 t = slot[a_slot0 + 64 * j];
+      const int4 t = slot[a_slot0 + 128 * j];
       f.a[j] = v4i{t.x, t.y, t.z, t.w};
     }
 #pragma unroll
     for (int i = 0; i < C::kTN; ++i) {
-      const int4 t = slot[w_slot0 + 64 * i];
+      const int4 t = slot[w_slot0 + 128 * i];
       f.w[i] = v4i{t.x, t.y, t.z, t.w};
     }
   };
@@ -214,56 +242,49 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
       for (int j = 0; j < C::kTM; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.w[i], f.a[j], acc[i][j], 0, 0, 0);
   };
-  // One step: (1) wait until step kt+1 has landed (at most RING-2 later
-  // steps of this wave's loads in flight) and this wave's reads of step kt's
-  // slot are done, then barrier; (2) issue the reads of step kt+1's fragments
-  // and refill step kt's slot with step kt+RING, interleaved with (3) the
-  // MFMAs on step kt's fragments, so all three overlap.  The scheduling
-  // groups spread the reads and loads between the MFMAs.
-  auto step = [&](Frags& cur, Frags& nxt, int4* cur_slot, const int4* nxt_slot, int kt) {
+  // One step kt: (1) wait until step kt+1 has landed and this wave's reads
+  // of step kt's fragments are done, then barrier; (2) issue the reads of
+  // step kt+1's fragments and, at odd kt, refill step kt's pair buffer
+  // (both of its steps are read by now) with steps kt+3 and kt+4,
+  // interleaved with (3) the MFMAs on step kt's fragments.  The refill of an
+  // odd step is the only one that can still be in flight at the next (even)
+  // step's wait; at an odd step the next step lies in the buffer refilled
+  // two steps earlier, so nothing may be outstanding.
+  auto step = [&](Frags& cur, Frags& nxt, int4* cur_buf, const int4* nxt_slot, int kt,
+                  auto odd_tag) {
+    constexpr bool kOdd = decltype(odd_tag)::value;
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm_lgkm0<(RING - 2) * C::kLPW>();
+    wait_vm_lgkm0<kOdd ? 0 : C::kLPW>();
     barrier_nofence();
     read_frags(nxt, nxt_slot);
-    issue(cur_slot, kt + RING);
+    if (kOdd) issue(cur_buf, (kt + 3) >> 1);
     mfmas(cur);
-    interleave_step<C::kTM * C::kTN, C::kTM + C::kTN, C::kLPW>();
+    interleave_step<C::kTM * C::kTN, C::kTM + C::kTN, kOdd ? C::kLPW : 0>();
   };
-  // slot of step j (compile-time j): the ring arrays in turn
-#define KQ_SLOT(j)                                                                        \
-  ((j) % RING == 0 ? lds0 : (j) % RING == 1 ? lds1 : (j) % RING == 2 ? lds2             \
-   : (j) % RING == 3 ? lds3 : lds4)
-#define KQ_STEP(j) step((j) % 2 ? f1 : f0, (j) % 2 ? f0 : f1, KQ_SLOT(j), KQ_SLOT((j) + 1), kt + (j))
+  using Even = std::integral_constant<bool, false>;
+  using Odd = std::integral_constant<bool, true>;
+  // step j of an unrolled group of 4: buffer, next step's slot, parity
+#define KQ_STEP(j)                                                                       \
+  step((j) % 2 ? f1 : f0, (j) % 2 ? f0 : f1, (j) < 2 ? lds0 : lds1,                     \
+       (j) == 0 ? lds0 + 32 : (j) == 1 ? lds1 : (j) == 2 ? lds1 + 32 : lds0, kt + (j),    \
+       std::conditional_t<(j) % 2 == 1, Odd, Even>{})
 
   Frags f0, f1;
   issue(lds0, 0);
   issue(lds1, 1);
-  issue(lds2, 2);
-  issue(lds3, 3);
-  if (RING > 4) issue(lds4, 4);
-  wait_vm_lgkm0<(RING - 1) * C::kLPW>();
+  wait_vm_lgkm0<C::kLPW>();
   barrier_nofence();
   read_frags(f0, lds0);
   int kt = 0;
-  for (; kt + U <= KT; kt += U) {
+  for (; kt + 4 <= KT; kt += 4) {
     KQ_STEP(0); KQ_STEP(1); KQ_STEP(2); KQ_STEP(3);
-    if (U > 4) { KQ_STEP(4); KQ_STEP(5); KQ_STEP(6); KQ_STEP(7); KQ_STEP(8); KQ_STEP(9); }
   }
-  if (REM) {  // the K steps beyond a multiple of U
+  if (REM) {  // the K steps beyond a multiple of 4
     if (kt < KT) KQ_STEP(0);
     if (kt + 1 < KT) KQ_STEP(1);
     if (kt + 2 < KT) KQ_STEP(2);
-    if (U > 4) {
-      if (kt + 3 < KT) KQ_STEP(3);
-      if (kt + 4 < KT) KQ_STEP(4);
-      if (kt + 5 < KT) KQ_STEP(5);
-      if (kt + 6 < KT) KQ_STEP(6);
-      if (kt + 7 < KT) KQ_STEP(7);
-      if (kt + 8 < KT) KQ_STEP(8);
-    }
   }
 #undef KQ_STEP
-#undef KQ_SLOT
   __builtin_amdgcn_sched_barrier(0);
   wait_vm_lgkm0<0>();  // drain the dead loads before the workgroup exits
 
@@ -272,14 +293,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
   // block, row-major, into a free ring slot and then stores whole 16-byte
   // row chunks (non-temporal), instead of 8-byte pieces of 16 rows.
   constexpr int kStage = C::kWTM * C::kWTN * 2;          // bytes of one wave's bf16 block
-  constexpr int kPerSlot = (C::kSlots * 16) / kStage;    // blocks per ring slot
+  constexpr int kPerSlot = (C::kPairSlots * 16) / kStage;  // blocks per pair buffer
   constexpr int kRowChunks = C::kWTN / 8;                // 16-byte chunks per block row
-  if (OUT == kOutBF16 && kPerSlot * 4 >= C::kWaves && (N % 8) == 0 && m0 + BM <= M &&
+  if (OUT == kOutBF16 && kPerSlot * 2 >= C::kWaves && (N % 8) == 0 && m0 + BM <= M &&
       n0 + BN <= N) {
     __builtin_amdgcn_sched_barrier(0);
     barrier_nofence();  // every wave is done with the ring (its loads drained above)
     const int sidx = wave / kPerSlot;
-    char* stage = reinterpret_cast<char*>(sidx == 0 ? lds0 : sidx == 1 ? lds1 : sidx == 2 ? lds2 : lds3) +
+    char* stage = reinterpret_cast<char*>(sidx == 0 ? lds0 : lds1) +
                   (wave % kPerSlot) * kStage;
     float s_m[C::kTM];
 #pragma unroll
@@ -349,27 +370,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
   }
 }
 
-template <int BM, int BN, int WM, int WN, int RING, bool REM>
+template <int BM, int BN, int WM, int WN, bool REM>
 void launch_rem(const int8_t* a, const float* sx, const int8_t* q, const float* sw,
                 const float* bias, void* y, int out, int M, int N, int K, hipStream_t s) {
   const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const dim3 grid((unsigned)tiles), block(64 * WM * WN);
   if (out == kOutF32)
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, RING, kOutF32, REM>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutF32, REM>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
   else if (out == kOutBF16)
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, RING, kOutBF16, REM>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutBF16, REM>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
   else
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, RING, kOutI32, REM>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutI32, REM>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
 }
 
-template <int BM, int BN, int WM = 2, int WN = 2, int RING = 4>
+template <int BM, int BN, int WM = 2, int WN = 2>
 const char* launch_tile(const int8_t* a, const float* sx, const int8_t* q, const float* sw,
                         const float* bias, void* y, int out, int M, int N, int K,
                         hipStream_t s, const char* name) {
-  if ((K / 64) % Unroll<RING>::kSteps == 0)
-    launch_rem<BM, BN, WM, WN, RING, false>(a, sx, q, sw, bias, y, out, M, N, K, s);
+  if ((K / 64) % 4 == 0)
+    launch_rem<BM, BN, WM, WN, false>(a, sx, q, sw, bias, y, out, M, N, K, s);
   else
-    launch_rem<BM, BN, WM, WN, RING, true>(a, sx, q, sw, bias, y, out, M, N, K, s);
+    launch_rem<BM, BN, WM, WN, true>(a, sx, q, sw, bias, y, out, M, N, K, s);
   return name;
 }
 
