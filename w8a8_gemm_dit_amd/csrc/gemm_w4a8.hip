@@ -61,7 +61,7 @@ struct Cfg4 {
   // table staging per thread and chunk
   static constexpr int kSBN = BN * kSG / kThreads;  // scale and offset entries
   static constexpr int kSBM = BM * kSG / kThreads;  // group-sum entries
-  static_assert((kABlk + kWBlk) % kWaves == 0, "DMA blocks split evenly over the waves");
+  static_assert(kABlk % kWaves == 0 && kWBlk % kWaves == 0, "DMA blocks split evenly over the waves");
   static_assert(BN * kSG % kThreads == 0 && BM * kSG % kThreads == 0, "table staging");
 };
 
@@ -116,7 +116,9 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
 #pragma unroll
     for (int i = 0; i < C::kLPW; ++i) {
       const int b = wave + C::kWaves * i;
-      if (b < C::kABlk) {
+      // compile-time split (kABlk is a multiple of kWaves): no branch, so
+      // the step stays one basic block
+      if (i < C::kABlk / C::kWaves) {
         lds_ptr_t dst = (lds_ptr_t)(slot + 64 * b);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, voff_a, 16 * b * K + k * 64, 0, 0);
       } else {
