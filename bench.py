@@ -122,9 +122,9 @@ class Prepared:
                             out_dtype=self.out_dtype, out=c["y"])
 
 
-def graph_time(fn, steps: int) -> float:
-    """Capture `steps` calls of fn(i) in one HIP graph, replay once untimed,
-    then time one replay; returns ms per call."""
+def graph_capture(fn, steps: int):
+    """Capture `steps` calls of fn(i) in one HIP graph and replay it once
+    untimed."""
     import torch
 
     s = torch.cuda.Stream()
@@ -139,6 +139,15 @@ def graph_time(fn, steps: int) -> float:
             fn(i)
     g.replay()
     torch.cuda.synchronize()
+    return g
+
+
+def graph_replay_time(g, steps: int) -> float:
+    """One timed replay of a captured graph of `steps` calls, bracketed by
+    synchronizations; returns ms per call."""
+    import torch
+
+    torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(st)
@@ -146,6 +155,31 @@ def graph_time(fn, steps: int) -> float:
     e1.record(st)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def graph_time(fn, steps: int) -> float:
+    """Capture `steps` calls of fn(i) in one HIP graph, replay once untimed,
+    then time one replay; returns ms per call."""
+    return graph_replay_time(graph_capture(fn, steps), steps)
+
+
+def median_ci95(xs):
+    """Median and a distribution-free 95% confidence interval for it from
+    order statistics: the smallest symmetric pair (x_(j), x_(n+1-j)) whose
+    binomial(n, 1/2) coverage is at least 95%."""
+    v = sorted(xs)
+    n = len(v)
+    med = statistics.median(v)
+    if n < 6:
+        return med, (v[0], v[-1]), 1.0
+    from math import comb
+    best = (v[0], v[-1], 1.0)
+    for j in range(1, n // 2 + 1):
+        cover = 1.0 - 2.0 * sum(comb(n, i) for i in range(j)) / 2.0 ** n
+        if cover < 0.95:
+            break
+        best = (v[j - 1], v[n - j], cover)
+    return med, (best[0], best[1]), best[2]
 
 
 def eager_time(fn, steps: int) -> float:
@@ -232,6 +266,13 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="few eager steps of every workload, for profiler runs")
+    ap.add_argument("--samples", type=int, default=9,
+                    help="extra timed replays of the headline graph (K steps each) for the median "
+                         "and its 95%% confidence interval")
+    ap.add_argument("--samples-out", default="", metavar="PATH",
+                    help="append the raw per-replay samples to this JSONL file")
+    ap.add_argument("--workload", default="", metavar="NAME",
+                    help="with --profile: only this workload")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device-to-device copies of MIB MiB, the known-size "
                          "reference that scales HBM byte counters")
@@ -264,6 +305,8 @@ def main() -> int:
 
     if args.profile:
         for name, wl in synth.WORKLOADS.items():
+            if args.workload and name != args.workload:
+                continue
             p = Prepared(wl)
             for i in range(max(args.steps, 1)):
                 p.step(i)
@@ -281,10 +324,18 @@ def main() -> int:
     for i in range(args.warmup):
         p.step(i)
     torch.cuda.synchronize()
-    ms = graph_time(p.step, args.steps)
+    g_step = graph_capture(p.step, args.steps)
+    ms = graph_replay_time(g_step, args.steps)
     ms_eager = eager_time(p.step, args.steps)
     ms_gemm = graph_time(p.gemm, args.steps)
     log(f"step {ms * 1e3:.2f} us (eager {ms_eager * 1e3:.2f} us), gemm {ms_gemm * 1e3:.2f} us")
+    samples = [graph_replay_time(g_step, args.steps) for _ in range(max(args.samples, 0))]
+    if args.samples_out and samples:
+        with open(args.samples_out, "a") as f:
+            for i, v in enumerate(samples):
+                f.write(json.dumps({"workload": wl.name, "sample": i, "steps": args.steps,
+                                    "ms_per_step": v}) + "\n")
+    del g_step
     route = kq.kq_route(wl.M, wl.N, wl.K, kq.KQ_W8_PER_CHANNEL)
     gemm_name = f"gemm_w8a8_{route['tile_m']}x{route['tile_n']}"
     tops = wl.ops / (ms * 1e-3) / 1e12
@@ -306,6 +357,7 @@ def main() -> int:
                    "weights": "int8 per output channel", "activations": "bf16 -> int8 per token",
                    "out": wl.out, "pct_of_int8_peak": round(100 * tops / PEAK_INT8_TOPS, 2),
                    "eager_ms_per_step": round(ms_eager, 6), "rotation_copies": p.R},
+        "samples": None,
         "roofline": {
             "kernel": gemm_name,
             "bound": "mfma",
@@ -317,6 +369,18 @@ def main() -> int:
             "avg_launch_us": round(ms_gemm * 1e3, 3),
         },
     }
+    if samples:
+        med, (lo, hi), cover = median_ci95(samples)
+        result["samples"] = {
+            "n": len(samples), "steps_each": args.steps,
+            "ms_per_step": [round(v, 6) for v in samples],
+            "median_ms_per_step": round(med, 6),
+            "ci95_ms_per_step": [round(lo, 6), round(hi, 6)],
+            "ci_coverage": round(cover, 4),
+            "median_tops": round(wl.ops / (med * 1e-3) / 1e12, 3),
+            "method": "extra replays of the timed graph; distribution-free order-statistic interval",
+        }
+        log(f"samples: median {med * 1e3:.2f} us/step, 95% CI [{lo * 1e3:.2f}, {hi * 1e3:.2f}] us")
     del p
     torch.cuda.empty_cache()
 
