@@ -300,3 +300,78 @@ def test_workload_full_size_sampled_rows(name):
         check_f32(host(ys), y64, T, name)
     else:
         check_bf16(host_bf16_bits(ys), y64, T, name)
+
+
+# ------------------------------------------------------- golden fixture
+def _golden_case():
+    import json
+
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "small_cases.json")
+    with open(path) as f:
+        d = json.load(f)
+
+    def arr(key, dtype, shape):
+        return np.array([int(h, 16) for h in d[key]], dtype=dtype).reshape(shape)
+
+    return d, arr
+
+
+@pytest.mark.parametrize("route", ["gemm", "gemv"])
+def test_golden_small_cases(route, kq_env):
+    """The stored fixture (oracle results, tests/golden/make_golden.py) on
+    the GPU: codes, scales, sums, weights, accumulators and group products
+    bit-exact; fp32 outputs within 1e-5 of the stored ones (relative to the
+    term magnitude) and bf16 outputs within 1 ulp."""
+    kq_env(KQ_FORCE_ROUTE=route)
+    d, arr = _golden_case()
+    M, K, N = d["shape"]["M"], d["shape"]["K"], d["shape"]["N"]
+    G = K // 64
+    print(f"[parity] golden small cases, route {route}", flush=True)
+    xb = arr("x_bf16_bits", np.uint16, (M, K))
+    w = arr("w_f32_bits", np.uint32, (N, K)).view(np.float32)
+    b = arr("bias_f32_bits", np.uint32, (N,)).view(np.float32)
+    x = dev_bf16(xb)
+    a, sx, gsum = kq.kq_quantize_act(x, group_sums=True)
+    q8, sw, _ = kq.kq_quantize_weights(dev(w), kq.KQ_W8_PER_CHANNEL)
+    p4, gs, gb = kq.kq_quantize_weights(dev(w), kq.KQ_W4_AFFINE_G64)
+    torch.cuda.synchronize()
+    assert host(a).astype(int).ravel().tolist() == d["act_codes"]
+    assert np.array_equal(host(sx).view(np.uint32), arr("act_scale_f32_bits", np.uint32, (M,)))
+    assert host(gsum).astype(int).ravel().tolist() == d["act_group_sums"]
+    assert host(q8).astype(int).ravel().tolist() == d["w8_codes"]
+    assert np.array_equal(host(sw).view(np.uint32), arr("w8_scale_f32_bits", np.uint32, (N,)))
+    assert host(p4).astype(int).ravel().tolist() == d["w4_packed"]
+    assert np.array_equal(host(gs).view(np.uint16), arr("w4_scale_f16_bits", np.uint16, (N, G)))
+    assert np.array_equal(host(gb).view(np.uint16), arr("w4_offset_f16_bits", np.uint16, (N, G)))
+
+    # magnitudes for the fp32 tolerance, from the stored quantized operands
+    q8h = np.array(d["w8_codes"], np.int8).reshape(N, K)
+    swh = arr("w8_scale_f32_bits", np.uint32, (N,)).view(np.float32)
+    q4h = oracle.unpack_w4(np.array(d["w4_packed"], np.uint8).reshape(N, K // 2))
+    gsh = arr("w4_scale_f16_bits", np.uint16, (N, G)).view(np.float16)
+    gbh = arr("w4_offset_f16_bits", np.uint16, (N, G)).view(np.float16)
+    T8 = oracle.w8a8_magnitude(xb, q8h, swh, b)
+    T4 = oracle.w4a8_magnitude(xb, q4h, gsh, gbh, b)
+
+    def check(y_f32, y_bf16, key32, key16, T):
+        r32 = arr(key32, np.uint32, (M, N)).view(np.float32).astype(np.float64)
+        err = np.abs(host(y_f32).astype(np.float64) - r32)
+        assert (err <= 1e-5 * np.maximum(np.abs(r32), T)).all(), key32
+        r16 = arr(key16, np.uint16, (M, N))
+        g = oracle.bf16_bits_to_f32(host_bf16_bits(y_bf16)).astype(np.float64)
+        r = oracle.bf16_bits_to_f32(r16).astype(np.float64)
+        assert (np.abs(g - r) <= oracle.bf16_ulp(r16)).all(), key16
+
+    bd = dev(b)
+    acc = kq.kq_w8a8_linear(x, q8, sw, out_dtype=torch.int32)
+    y32 = kq.kq_w8a8_linear(x, q8, sw, bd, out_dtype=torch.float32)
+    y16 = kq.kq_w8a8_linear(x, q8, sw, bd, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert host(acc).astype(np.int64).ravel().tolist() == d["w8a8_acc"]
+    check(y32, y16, "w8a8_y_f32_bits", "w8a8_y_bf16_bits", T8)
+    P = kq.kq_w4a8_linear(x, p4, gs, gb, out_dtype=torch.int32)
+    y32 = kq.kq_w4a8_linear(x, p4, gs, gb, bd, out_dtype=torch.float32)
+    y16 = kq.kq_w4a8_linear(x, p4, gs, gb, bd, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert host(P).astype(np.int64).ravel().tolist() == d["w4a8_group_products_gmn"]
+    check(y32, y16, "w4a8_y_f32_bits", "w4a8_y_bf16_bits", T4)

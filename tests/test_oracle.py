@@ -370,3 +370,69 @@ def test_bf16_ulp():
     bits = synth.to_bf16_bits(np.array([1.0, -1.0, 3.0, 1e-3], np.float32))
     np.testing.assert_array_equal(oracle.bf16_ulp(bits),
                                   [2 ** -7, 2 ** -7, 2 ** -6, 2.0 ** -17])
+
+
+# ------------------------------------------------------- golden fixture
+# tests/golden/small_cases.json is written by tests/golden/make_golden.py
+# from oracle/ and synth/ only.  The first test catches any drift of the
+# oracle's arithmetic; the second checks the fixture's hand-derivable rows
+# against their closed forms, independently of the oracle.
+def _golden():
+    import importlib.util
+    import json
+    import os
+
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    spec = importlib.util.spec_from_file_location("make_golden", os.path.join(here, "make_golden.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    with open(os.path.join(here, "small_cases.json")) as f:
+        return mod, json.load(f)
+
+
+def test_golden_fixture_is_reproduced_by_oracle(tmp_path, monkeypatch):
+    mod, stored = _golden()
+    monkeypatch.setattr(mod, "OUT", str(tmp_path / "again.json"))
+    mod.main()
+    import json
+
+    with open(tmp_path / "again.json") as f:
+        assert json.load(f) == stored
+
+
+def test_golden_fixture_closed_forms():
+    _, d = _golden()
+    M, K, N = d["shape"]["M"], d["shape"]["K"], d["shape"]["N"]
+    codes = np.array(d["act_codes"]).reshape(M, K)
+    scale_bits = [int(h, 16) for h in d["act_scale_f32_bits"]]
+    # row 3: amax = 127 gives inv = 127/127 = 1 and scale 127/127 = 1, so the
+    # codes are rint(x) with ties to even: 2.5 -> 2, -2.5 -> -2, 3.5 -> 4,
+    # +-0.5 -> 0, 1.5 -> 2
+    assert scale_bits[3] == 0x3F800000
+    assert codes[3, :7].tolist() == [127, 2, -2, 4, 0, 0, 2]
+    assert not codes[3, 7:].any()
+    # rows 1 (zeros) and 2 (bf16 subnormals: 127/amax > FLT_MAX): scale 0, codes 0
+    assert scale_bits[1] == 0 and scale_bits[2] == 0
+    assert not codes[1].any() and not codes[2].any()
+    # every other row reaches +-127 at its absmax element
+    for m in (0, 4, 5):
+        assert np.abs(codes[m]).max() == 127
+    # group sums are the sums of the codes
+    gs = np.array(d["act_group_sums"]).reshape(M, K // 64)
+    assert np.array_equal(gs, codes.reshape(M, K // 64, 64).sum(axis=2))
+    # int8 weights: the all-zero channel 1 gets scale 0 and zero codes
+    q8 = np.array(d["w8_codes"]).reshape(N, K)
+    sw_bits = [int(h, 16) for h in d["w8_scale_f32_bits"]]
+    assert sw_bits[1] == 0 and not q8[1].any()
+    # int4: channel 2, group 1 is constant 0.0123, so its scale is 0, its
+    # offset fp16(0.0123) and its codes 0
+    gs4 = [int(h, 16) for h in d["w4_scale_f16_bits"]]
+    gb4 = [int(h, 16) for h in d["w4_offset_f16_bits"]]
+    G = K // 64
+    assert gs4[2 * G + 1] == 0
+    assert gb4[2 * G + 1] == int(np.array(0.0123, np.float16).view(np.uint16))
+    packed = np.array(d["w4_packed"]).reshape(N, K // 2)
+    assert not packed[2, 32:].any()
+    # int32 accumulators are the exact integer products of the stored codes
+    acc = np.array(d["w8a8_acc"]).reshape(M, N)
+    assert np.array_equal(acc, codes.astype(np.int64) @ q8.astype(np.int64).T)
