@@ -195,10 +195,11 @@ def test_gemv_w8(M, K, N):
     check_bf16(host_bf16_bits(yb), y64, T, "gemv w8 bf16")
 
 
-def test_gemv_and_gemm_routes_agree_bitwise(kq_env):
+@pytest.mark.parametrize("M", [3, 8])
+def test_gemv_and_gemm_routes_agree_bitwise(M, kq_env):
     # The same per-group products whichever kernel runs (decode steps stay
     # bit-identical across routes, as MLX pull request 4722 checks).
-    M, K, N = 8, 1024, 200
+    K, N = 1024, 200
     xb, w, b = _problem(M, K, N, seed=99)
     p, gs, gb, q = oracle.quantize_w4(w)
     args = (dev_bf16(xb), dev(p), dev(gs), dev(gb))
@@ -375,3 +376,42 @@ def test_golden_small_cases(route, kq_env):
     torch.cuda.synchronize()
     assert host(P).astype(np.int64).ravel().tolist() == d["w4a8_group_products_gmn"]
     check(y32, y16, "w4a8_y_f32_bits", "w4a8_y_bf16_bits", T4)
+
+
+@pytest.mark.parametrize("fmt", ["w4", "w8"])
+def test_golden_rows_on_gemv(fmt):
+    """The fixture's first four rows (plain, all zero, subnormal, ties at
+    amax 127) through kq_gemv_small_m."""
+    d, arr = _golden_case()
+    M, K, N = 4, d["shape"]["K"], d["shape"]["N"]
+    Mf, G = d["shape"]["M"], K // 64
+    xb = arr("x_bf16_bits", np.uint16, (Mf, K))[:M]
+    b = arr("bias_f32_bits", np.uint32, (N,)).view(np.float32)
+    x = dev_bf16(xb)
+    if fmt == "w4":
+        p4 = np.array(d["w4_packed"], np.uint8).reshape(N, K // 2)
+        gs = arr("w4_scale_f16_bits", np.uint16, (N, G)).view(np.float16)
+        gb = arr("w4_offset_f16_bits", np.uint16, (N, G)).view(np.float16)
+        args = (kq.KQ_W4_AFFINE_G64, x, dev(p4), dev(gs), dev(gb))
+        ref_int = np.array(d["w4a8_group_products_gmn"], np.int64).reshape(G, Mf, N)[:, :M]
+        q4 = oracle.unpack_w4(p4)
+        T = oracle.w4a8_magnitude(xb, q4, gs, gb, b)
+        k32, k16 = "w4a8_y_f32_bits", "w4a8_y_bf16_bits"
+    else:
+        q8 = np.array(d["w8_codes"], np.int8).reshape(N, K)
+        sw = arr("w8_scale_f32_bits", np.uint32, (N,)).view(np.float32)
+        args = (kq.KQ_W8_PER_CHANNEL, x, dev(q8), dev(sw), None)
+        ref_int = np.array(d["w8a8_acc"], np.int64).reshape(Mf, N)[:M]
+        T = oracle.w8a8_magnitude(xb, q8, sw, b)
+        k32, k16 = "w8a8_y_f32_bits", "w8a8_y_bf16_bits"
+    P = kq.kq_gemv_small_m(*args, out_dtype=torch.int32)
+    yf = kq.kq_gemv_small_m(*args, bias=dev(b), out_dtype=torch.float32)
+    yb = kq.kq_gemv_small_m(*args, bias=dev(b), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(P).astype(np.int64), ref_int)
+    r32 = arr(k32, np.uint32, (Mf, N)).view(np.float32)[:M].astype(np.float64)
+    assert (np.abs(host(yf).astype(np.float64) - r32) <= 1e-5 * np.maximum(np.abs(r32), T)).all()
+    r16 = arr(k16, np.uint16, (Mf, N))[:M]
+    g = oracle.bf16_bits_to_f32(host_bf16_bits(yb)).astype(np.float64)
+    r = oracle.bf16_bits_to_f32(r16).astype(np.float64)
+    assert (np.abs(g - r) <= oracle.bf16_ulp(r16)).all()

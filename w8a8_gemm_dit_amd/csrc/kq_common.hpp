@@ -50,6 +50,16 @@ __device__ __forceinline__ int quant_code(float v, float inv) {
   return (int)t;
 }
 
+// Per-row scale rule of the symmetric int8 quantizer: inv = fp32(127/amax)
+// and scale = fp32(amax/127); a row whose 127/amax is not a finite fp32
+// (all zero, or too small) gets inv 0 (codes 0) and scale 0.
+__device__ __forceinline__ float row_inv(float amax, float& scale) {
+  const float inv = 127.0f / amax;
+  const bool ok = inv <= 3.402823466e38f;  // false for +inf
+  scale = ok ? amax / 127.0f : 0.0f;
+  return ok ? inv : 0.0f;
+}
+
 // Pack four int8 codes into one dword (byte i = code i).
 __device__ __forceinline__ uint32_t pack4_i8(int c0, int c1, int c2, int c3) {
   return (uint32_t)(c0 & 0xFF) | ((uint32_t)(c1 & 0xFF) << 8) |

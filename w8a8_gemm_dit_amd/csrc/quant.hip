@@ -26,13 +26,6 @@ namespace {
 
 constexpr int kRowsPerBlock = 4;  // one wavefront per row, 4 waves per block
 
-__device__ __forceinline__ float row_inv(float amax, float& scale) {
-  const float inv = 127.0f / amax;
-  const bool ok = inv <= FLT_MAX;  // false for +inf (amax 0 or tiny)
-  scale = ok ? amax / 127.0f : 0.0f;
-  return ok ? inv : 0.0f;
-}
-
 // Quantize 8 bf16 values held in a uint4; returns 8 codes as uint2 and their sum.
 __device__ __forceinline__ uint2 quant8(const uint4 v, float inv, int& sum) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
