@@ -122,9 +122,10 @@ class Prepared:
                             out_dtype=self.out_dtype, out=c["y"])
 
 
-def graph_capture(fn, steps: int):
-    """Capture `steps` calls of fn(i) in one HIP graph and replay it once
-    untimed."""
+def graph_capture(fn, steps: int, warm_replays: int = 3):
+    """Capture `steps` calls of fn(i) in one HIP graph and replay it
+    `warm_replays` times untimed (part of the warmup: the first replays run
+    measurably slower than the steady state)."""
     import torch
 
     s = torch.cuda.Stream()
@@ -137,7 +138,8 @@ def graph_capture(fn, steps: int):
     with torch.cuda.graph(g):
         for i in range(steps):
             fn(i)
-    g.replay()
+    for _ in range(max(warm_replays, 1)):
+        g.replay()
     torch.cuda.synchronize()
     return g
 
