@@ -81,7 +81,9 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
   __shared__ int4 lds0[C::kSlots], lds1[C::kSlots], lds2[C::kSlots], lds3[C::kSlots];
   // tables, double-buffered: gs and gb as [column][16 groups] fp16, the group
   // sums as [row][32] fp16 = {64*hi of groups 0..15, lo of groups 0..15}
-  __shared__ __attribute__((aligned(16))) uint16_t t_gs[kScaled ? 2 : 1][kScaled ? BN : 1][kSG];
+  // (t_gs rows padded to 18 halves: the per-step reads of 16 consecutive
+  // columns then hit 16 distinct banks instead of two columns per bank)
+  __shared__ __attribute__((aligned(16))) uint16_t t_gs[kScaled ? 2 : 1][kScaled ? BN : 1][kSG + 2];
   __shared__ __attribute__((aligned(16))) uint16_t t_gb[kScaled ? 2 : 1][kScaled ? BN : 1][kSG];
   __shared__ __attribute__((aligned(16))) uint16_t t_as[kScaled ? 2 : 1][kScaled ? BM : 1][2 * kSG];
 
@@ -106,11 +108,13 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
   // DMA plan: block b = wave + kWaves*i.  Activation block b < kABlk holds
   // rows 16b..16b+15 (lane l: row 16b + l/4, physical chunk l%4 holding
   // logical chunk (l%4)^swz4(row)); weight block b' = b - kABlk holds rows
-  // 32b'..32b'+31 of 32 bytes (lane l: row 32b' + l/2, half l%2), stored
-  // after the activation part.
+  // 32b'..32b'+31 of 32 bytes (lane l: row 32b' + l/2, physical half l%2
+  // holding logical half (l%2) ^ ((row/8)%2)), stored after the activation
+  // part.  The half swap makes the 8-byte fragment reads of rows r and r+8
+  // land in different banks.
   const int ar = lane >> 2;
   const uint32_t voff_a = (uint32_t)(ar * K + (((lane & 3) ^ swz4(ar)) * 16));
-  const uint32_t voff_q = (uint32_t)((lane >> 1) * QB + (lane & 1) * 16);
+  const uint32_t voff_q = (uint32_t)((lane >> 1) * QB + (((lane & 1) ^ ((lane >> 4) & 1)) * 16));
   auto issue = [&](int4* slot, int kt) {
     const int k = min(kt, KT - 1);  // steps past the end re-load the last slice
 #pragma unroll
@@ -187,7 +191,8 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
   const int a_row0 = wm * WTM + fr;
   const int a_slot0 = a_row0 * 4 + (fc ^ swz4(a_row0));  // row block j: + 64*j (swz4 is 16-periodic)
   const int q_col0 = wn * WTN + fr;
-  const int q_byte0 = C::kASlots * 16 + q_col0 * 32 + fc * 8;  // column block i: + 512*i
+  // column block i: + 512*i (16 rows, which keeps bit 3 of the row)
+  const int q_byte0 = C::kASlots * 16 + q_col0 * 32 + ((fc * 8) ^ (((q_col0 >> 3) & 1) << 4));
 
   struct Frags {
     v4i a[C::kTM];
