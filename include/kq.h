@@ -86,7 +86,8 @@ typedef enum kq_dtype {
 
 typedef enum kq_route_kind {
     KQ_ROUTE_GEMM = 0, /* LDS-tiled MFMA GEMM */
-    KQ_ROUTE_GEMV = 1  /* weight-streaming register-dequant kernel, M <= 16 */
+    KQ_ROUTE_GEMV = 1  /* weight-streaming register-dequant kernel: 16x16 output
+                          blocks over all of K (M <= 16, or thin N) */
 } kq_route_kind;
 
 /* Launch plan chosen for one linear call (see kq_route). */
@@ -122,10 +123,11 @@ const char* kq_last_error(void);
 size_t kq_workspace_bytes(int64_t M, int64_t K, kq_wformat fmt);
 
 /* Launch plan of a linear call; pure host function, no device access.
- * [kquant]: the route decision is one tested function.  Routing: M <= 16
- * with K <= KQ_GEMV_MAX_K takes the GEMV unless the environment variable
- * KQ_FORCE_ROUTE=gemm; KQ_FORCE_ROUTE=gemv forces the GEMV (and fails for
- * shapes it cannot take).
+ * [kquant]: the route decision is one tested function.  Routing: with
+ * K <= KQ_GEMV_MAX_K, M <= 16 or N <= 64 (thin N: the GEMM's tiles would
+ * leave most of the GPU idle) takes the GEMV unless the environment
+ * variable KQ_FORCE_ROUTE=gemm; KQ_FORCE_ROUTE=gemv forces the GEMV (and
+ * fails for shapes it cannot take: M > 16 or K > KQ_GEMV_MAX_K).
  * Returns KQ_ERR_INVALID_VALUE / KQ_ERR_UNSUPPORTED for shapes the linears
  * reject, with the same messages. */
 kq_status kq_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,

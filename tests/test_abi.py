@@ -57,7 +57,10 @@ def test_workspace_layout():
     (2048, 12288, 4096, kq.KQ_W4_AFFINE_G64, "gemm", (128, 256), 768),
     (2048, 4096, 12288, kq.KQ_W4_AFFINE_G64, "gemm", (128, 256), 256),
     (100, 640, 256, kq.KQ_W4_AFFINE_G64, "gemm", (64, 128), 10),
-    (2048, 48, 5120, kq.KQ_W8_PER_CHANNEL, "gemm", (64, 64), 32),
+    (2048, 48, 5120, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 3 * 128),   # thin N
+    (300, 64, 640, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 4 * 19),
+    (300, 65, 640, kq.KQ_W8_PER_CHANNEL, "gemm", (64, 64), 5 * 2),
+    (2048, 48, 16448, kq.KQ_W8_PER_CHANNEL, "gemm", (64, 64), 32),
 ])
 def test_route_decisions(M, N, K, fmt, kind, tile, grid, kq_env):
     kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None)

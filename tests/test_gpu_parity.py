@@ -195,6 +195,39 @@ def test_gemv_w8(M, K, N):
     check_bf16(host_bf16_bits(yb), y64, T, "gemv w8 bf16")
 
 
+@pytest.mark.parametrize("fmt", ["w8", "w4"])
+@pytest.mark.parametrize("M,K,N", [(300, 640, 48), (2048, 512, 64), (33, 128, 40), (17, 5120, 16)])
+def test_thin_n_linears_take_the_gemv(M, K, N, fmt, kq_env):
+    """Thin N at any M: 16-row blocks of the GEMV kernel (ragged last
+    block), against the oracle; int32 bit-exact, outputs within tolerance."""
+    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None)
+    assert kq.kq_route(M, N, K, kq.KQ_W8_PER_CHANNEL)["kind"] == "gemv"
+    xb, w, b = _problem(M, K, N, seed=3 * M + K + N)
+    a, _, _ = oracle.quantize_act(xb)
+    x = dev_bf16(xb)
+    if fmt == "w8":
+        q8, sw = oracle.quantize_w8(w)
+        acc = kq.kq_w8a8_linear(x, dev(q8), dev(sw), out_dtype=torch.int32)
+        yf = kq.kq_w8a8_linear(x, dev(q8), dev(sw), dev(b), out_dtype=torch.float32)
+        yb = kq.kq_w8a8_linear(x, dev(q8), dev(sw), dev(b), out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(acc), oracle.w8a8_acc(a, q8))
+        y64 = oracle.w8a8_linear_exact(xb, q8, sw, b)
+        T = oracle.w8a8_magnitude(xb, q8, sw, b)
+    else:
+        p, gs, gb, q = oracle.quantize_w4(w)
+        args = (x, dev(p), dev(gs), dev(gb))
+        P = kq.kq_w4a8_linear(*args, out_dtype=torch.int32)
+        yf = kq.kq_w4a8_linear(*args, bias=dev(b), out_dtype=torch.float32)
+        yb = kq.kq_w4a8_linear(*args, bias=dev(b), out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(P), oracle.w4a8_group_acc(a, q))
+        y64 = oracle.w4a8_linear_exact(xb, q, gs, gb, b)
+        T = oracle.w4a8_magnitude(xb, q, gs, gb, b)
+    check_f32(host(yf), y64, T, f"thin {fmt} f32")
+    check_bf16(host_bf16_bits(yb), y64, T, f"thin {fmt} bf16")
+
+
 @pytest.mark.parametrize("M", [3, 8])
 def test_gemv_and_gemm_routes_agree_bitwise(M, kq_env):
     # The same per-group products whichever kernel runs (decode steps stay
@@ -213,7 +246,7 @@ def test_gemv_and_gemm_routes_agree_bitwise(M, kq_env):
 # ------------------------------------------------------------- behaviour
 def test_route_log_names_kernels(kq_env, capfd):
     kq_env(KQ_LOG="1", KQ_FORCE_ROUTE=None, KQ_TILE=None)
-    xb, w, b = _problem(4, 256, 64, seed=5)
+    xb, w, b = _problem(4, 256, 96, seed=5)  # N > 64: M = 300 takes the GEMM
     p, gs, gb, _ = oracle.quantize_w4(w)
     kq.kq_w4a8_linear(dev_bf16(xb), dev(p), dev(gs), dev(gb))
     xb2 = synth.random_bf16((300, 256), seed=6)

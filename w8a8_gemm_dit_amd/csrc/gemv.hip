@@ -1,6 +1,10 @@
-// Small-M GEMV of libkq (1 <= M <= 16): "qlip-mlx" README, w4a8_linear
-// bullet -- a register-dequant GEMV path for small batches, so decode-style
-// calls run at weight-bandwidth speed.  Same math as the GEMM routes:
+// Small-M GEMV of libkq: "qlip-mlx" README, w4a8_linear bullet -- a
+// register-dequant GEMV path for small batches, so decode-style calls run at
+// weight-bandwidth speed.  One workgroup computes 16 activation rows x 16
+// output columns over all of K; the grid's second dimension walks 16-row
+// blocks, so the same kernel also serves thin-N shapes (few output
+// columns, many rows), which the tiled GEMM would spread over too few
+// workgroups.  Same math as the GEMM routes:
 //   int4: y = sx * sum_g (gs*P + gb*A) + bias,  int8: y = sx*sw*acc + bias,
 // with P the exact int32 dot product of one 64-wide group and A the group
 // sum of the activation codes.
@@ -39,7 +43,12 @@ template <bool W4, int OUT>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ sx,
     const void* __restrict__ Wq, const void* __restrict__ gsv, const void* __restrict__ gbv,
-    const float* __restrict__ bias, void* __restrict__ y, int M, int N, int K) {
+    const float* __restrict__ bias, void* __restrict__ y, int Mtot, int N, int K) {
+  // this workgroup's 16-row block of the activations
+  const int m0 = blockIdx.y * 16;
+  const int M = min(16, Mtot - m0);
+  A += (int64_t)m0 * K;
+  if (sx != nullptr) sx += m0;
   constexpr int UB = W4 ? 32 : 64;          // bytes of one weight row per group
   constexpr int LPR = UB / 16;              // DMA lanes per (row, group)
   constexpr int GPB = 128 / UB;             // groups per 128-byte line (one DMA block)
@@ -171,7 +180,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const int m = 4 * fc + r;
-                if (m < M) reinterpret_cast<int32_t*>(y)[((int64_t)g * M + m) * N + nn] = p[r];
+                if (m < M) reinterpret_cast<int32_t*>(y)[((int64_t)g * Mtot + m0 + m) * N + nn] = p[r];
               }
             }
           } else {
@@ -212,7 +221,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
   for (int r = 0; r < 4; ++r) {
     const int m = 4 * fc + r;
     if (m >= M) continue;
-    const int64_t idx = (int64_t)m * N + nn;
+    const int64_t idx = (int64_t)(m0 + m) * N + nn;
     if (OUT == kOutI32) {
       reinterpret_cast<int32_t*>(y)[idx] = iacc[r];
     } else {
@@ -227,7 +236,7 @@ template <bool W4>
 const char* launch_fmt(const int8_t* a, const float* sx, const void* q, const void* gs,
                        const void* gb, const float* bias, void* y, int out, int M, int N, int K,
                        hipStream_t s) {
-  const dim3 grid((unsigned)((N + 15) / 16)), block(kWaves * 64);
+  const dim3 grid((unsigned)((N + 15) / 16), (unsigned)((M + 15) / 16)), block(kWaves * 64);
   const size_t sb = (W4 && out != kOutI32) ? (size_t)16 * (K / 64) * sizeof(uint32_t) : 0;
   if (out == kOutF32)
     hipLaunchKernelGGL((gemv_kernel<W4, kOutF32>), grid, block, sb, s, a, sx, q, gs, gb, bias, y, M, N, K);

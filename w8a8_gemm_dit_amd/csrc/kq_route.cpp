@@ -84,13 +84,17 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
                            int force, int tile_override) {
   kq_route_info r{};
   const bool fits = M <= KQ_GEMV_MAX_M && K <= kGemvMaxK;
-  const bool gemv = (force == 2) ? fits : (force == 1) ? false : (M >= 1 && fits);
+  // Thin N: the GEMM's tiles would leave most CUs idle, while the GEMV
+  // kernel's 16x16 blocks over all of K give ceil(N/16)*ceil(M/16)
+  // workgroups.
+  const bool thin = N <= kGemvThinN && K <= kGemvMaxK;
+  const bool gemv = (force == 2) ? fits : (force == 1) ? false : (M >= 1 && (fits || thin));
   if (gemv) {
     r.kind = KQ_ROUTE_GEMV;
-    r.tile_m = KQ_GEMV_MAX_M;
+    r.tile_m = kGemvRows;
     r.tile_n = kGemvCols;
     r.threads = kGemvThreads;
-    r.grid = (N + kGemvCols - 1) / kGemvCols;
+    r.grid = ((N + kGemvCols - 1) / kGemvCols) * ((M + kGemvRows - 1) / kGemvRows);
     return r;
   }
   // Tiles each kernel offers.  The int4 GEMM keeps fp32 accumulators that

@@ -55,6 +55,8 @@ WorkspaceLayout workspace_layout(int64_t M, int64_t K, kq_wformat fmt);
 // which split K; each wavefront holds its K slice of the activations in
 // registers, up to 32 groups of 64, so the GEMV takes K <= 16384.
 constexpr int kGemvCols = 16;
+constexpr int kGemvRows = 16;   // activation rows per GEMV workgroup
+constexpr int kGemvThinN = 64;  // N up to this takes the GEMV at any M
 constexpr int kGemvThreads = 512;
 constexpr int64_t kGemvMaxK = KQ_GEMV_MAX_K;
 
