@@ -61,6 +61,8 @@ def test_workspace_layout():
     (300, 64, 640, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 4 * 19),
     (300, 65, 640, kq.KQ_W8_PER_CHANNEL, "gemm", (64, 64), 5 * 2),
     (2048, 48, 16448, kq.KQ_W8_PER_CHANNEL, "gemm", (64, 64), 32),
+    (16 * 65535, 48, 128, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 3 * 65535),
+    (16 * 65535 + 1, 48, 128, kq.KQ_W8_PER_CHANNEL, "gemm", None, None),  # grid y limit
 ])
 def test_route_decisions(M, N, K, fmt, kind, tile, grid, kq_env):
     kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None)

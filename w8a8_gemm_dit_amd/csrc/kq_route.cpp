@@ -87,7 +87,8 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
   // Thin N: the GEMM's tiles would leave most CUs idle, while the GEMV
   // kernel's 16x16 blocks over all of K give ceil(N/16)*ceil(M/16)
   // workgroups.
-  const bool thin = N <= kGemvThinN && K <= kGemvMaxK;
+  // (the row blocks are the grid's y dimension, at most 65535)
+  const bool thin = N <= kGemvThinN && K <= kGemvMaxK && (M + kGemvRows - 1) / kGemvRows <= 65535;
   const bool gemv = (force == 2) ? fits : (force == 1) ? false : (M >= 1 && (fits || thin));
   if (gemv) {
     r.kind = KQ_ROUTE_GEMV;
