@@ -25,6 +25,8 @@ from .kq_oracle import (  # noqa: F401
     linear_dequantized_fp64,
     w8a8_magnitude,
     w4a8_magnitude,
+    gated_residual_exact,
+    gated_magnitude,
     round_f32,
     round_bf16_bits,
     bf16_bits_to_f32,

@@ -258,6 +258,37 @@ def w4a8_magnitude(x_bf16_bits, q, gs, gb, bias=None) -> np.ndarray:
     return t
 
 
+# ------------------------------------------------- gated residual epilogue
+# mlx-kquant pull request 89 commit list: a quantized matmul with a gated
+# residual epilogue, its elements held within 2 ulp.  The pages give no
+# formula; the reading is the DiT block's gated residual add: the block
+# input plus a per-sample, per-channel gate times the linear's output, with
+# one gate row shared by `gate_rows` consecutive token rows.
+def gated_residual_exact(y64, residual_bf16_bits=None, gate=None, gate_rows=1) -> np.ndarray:
+    """out[m,n] = r[m,n] + g[m // gate_rows, n] * y[m,n] in float64, for the
+    linear's exact result y (float64 [M,N]); residual bf16 bits [M,N] or None
+    (zero), gate fp32 [ceil(M/gate_rows), N] or None (one)."""
+    y = np.asarray(y64, np.float64)
+    if gate is not None:
+        rows = np.arange(y.shape[0]) // int(gate_rows)
+        y = np.asarray(gate, np.float64)[rows, :] * y
+    if residual_bf16_bits is not None:
+        y = y + bf16_bits_to_f32(residual_bf16_bits).astype(np.float64)
+    return y
+
+
+def gated_magnitude(T, residual_bf16_bits=None, gate=None, gate_rows=1) -> np.ndarray:
+    """|r| + |g| * T for the linear's term magnitude T: the scale against
+    which an fp32 evaluation of the gated epilogue is accurate."""
+    t = np.asarray(T, np.float64)
+    if gate is not None:
+        rows = np.arange(t.shape[0]) // int(gate_rows)
+        t = np.abs(np.asarray(gate, np.float64)[rows, :]) * t
+    if residual_bf16_bits is not None:
+        t = t + np.abs(bf16_bits_to_f32(residual_bf16_bits).astype(np.float64))
+    return t
+
+
 # ------------------------------------------------------------ output rounding
 def round_f32(y64) -> np.ndarray:
     """Round float64 to fp32, nearest even."""

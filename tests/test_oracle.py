@@ -436,3 +436,43 @@ def test_golden_fixture_closed_forms():
     # int32 accumulators are the exact integer products of the stored codes
     acc = np.array(d["w8a8_acc"]).reshape(M, N)
     assert np.array_equal(acc, codes.astype(np.int64) @ q8.astype(np.int64).T)
+
+
+# ------------------------------------------------ gated residual epilogue
+def test_gated_residual_identities():
+    """No residual and no gate is the linear; gate 1 and residual 0 too;
+    gate 0 leaves the residual exactly."""
+    rng = np.random.default_rng(31)
+    y = rng.standard_normal((6, 5))
+    assert np.array_equal(oracle.gated_residual_exact(y), y)
+    ones = np.ones((6, 5), np.float32)
+    zeros_r = _bits(np.zeros((6, 5), np.float32))
+    assert np.array_equal(oracle.gated_residual_exact(y, zeros_r, ones, 1), y)
+    r = _bits(rng.standard_normal((6, 5)).astype(np.float32))
+    out = oracle.gated_residual_exact(y, r, np.zeros((3, 5), np.float32), 2)
+    assert np.array_equal(out, synth.bf16_bits_to_f32(r).astype(np.float64))
+
+
+def test_gated_residual_integer_grid_is_exact_arithmetic():
+    """Integer-grid linear (sx = sw = 1, so y is an exact integer GEMM plus
+    an integer bias), power-of-two gates shared by 3 rows each, and integer
+    residuals: the result is plain integer/dyadic arithmetic."""
+    rng = np.random.default_rng(32)
+    m, k, n, L = 9, 128, 7, 3
+    x = rng.integers(-127, 128, size=(m, k)).astype(np.float32)
+    x[:, 0] = 127.0
+    w = rng.integers(-127, 128, size=(n, k)).astype(np.float32)
+    w[:, 1] = 127.0
+    bias = rng.integers(-50, 50, size=n).astype(np.float32)
+    gate = (2.0 ** rng.integers(-3, 4, size=(m // L, n))).astype(np.float32)
+    gate[0, 0] = -0.5
+    r = rng.integers(-100, 100, size=(m, n)).astype(np.float32)
+    q8, sw = oracle.quantize_w8(w)
+    y = oracle.w8a8_linear_exact(_bits(x), q8, sw, bias)
+    out = oracle.gated_residual_exact(y, _bits(r), gate, L)
+    lin = x.astype(np.int64) @ w.astype(np.int64).T + bias.astype(np.int64)
+    g = np.repeat(gate.astype(np.float64), L, axis=0)
+    ref = r.astype(np.float64) + g * lin.astype(np.float64)   # exact: dyadic, < 2^53
+    assert np.array_equal(out, ref)
+    T = oracle.gated_magnitude(oracle.w8a8_magnitude(_bits(x), q8, sw, bias), _bits(r), gate, L)
+    assert np.all(T >= np.abs(out) - 1e-9)
