@@ -28,7 +28,8 @@
  *            sizes 32/64/128 (this library: 64).
  *   [kquant] mlx-kquant pull request 89 commit list: routes must not round
  *            beyond one weight and one output rounding; errors other than a
- *            declined route raise; the route decision is one tested function.
+ *            declined route raise; the route decision is one tested function;
+ *            a quantized matmul whose epilogue adds a gated residual.
  *
  * Conventions shared by every entry point:
  *   - All tensors are dense, row-major, non-batched (callers flatten [B,L,K]
@@ -229,6 +230,33 @@ kq_status kq_gemv_small_m(kq_wformat fmt, const void* x, int64_t M, int64_t K,
                           const void* gbias, const float* bias, void* y,
                           kq_dtype y_dtype, void* ws, size_t ws_bytes,
                           void* stream);
+
+/* Linear with the gated residual epilogue of a DiT block ([kquant]: a
+ * quantized matmul with a gated residual epilogue; the pages give no
+ * formula, and the reading taken is the DiT block's gated residual add):
+ *   y[m,n] = residual[m,n] + gate[m / gate_rows, n] * lin[m,n]
+ * where lin is what kq_w8a8_linear (fmt = KQ_W8_PER_CHANNEL) or
+ * kq_w4a8_linear (fmt = KQ_W4_AFFINE_G64) computes in fp32, bias included.
+ * The gate and residual terms are applied in the same kernel's epilogue as
+ * one fp32 fma, and y is rounded once to y_dtype.
+ *   wq, scale, gbias, bias   as the corresponding linear (gbias NULL for int8)
+ *   residual  device bf16 [M,N] (16-byte aligned), or NULL for zero.  It may
+ *             be y itself when y_dtype is BF16 (in place); any other
+ *             overlap with y is rejected.
+ *   gate      device fp32 [ceil(M/gate_rows), N] (4-byte aligned), or NULL
+ *             for one.  One gate row serves gate_rows consecutive token rows
+ *             (a DiT batch of B samples of L tokens each: gate_rows = L).
+ *   gate_rows >= 1
+ *   y_dtype   F32 or BF16 (I32 has no epilogue and is rejected)
+ * Routes, workspace and the other constraints as the plain linears; with
+ * residual and gate both NULL the result is the plain linear's, bit for
+ * bit. */
+kq_status kq_linear_gated(kq_wformat fmt, const void* x, int64_t M, int64_t K,
+                          int64_t N, const void* wq, const void* scale,
+                          const void* gbias, const float* bias,
+                          const void* residual, const float* gate,
+                          int64_t gate_rows, void* y, kq_dtype y_dtype,
+                          void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -24,7 +24,7 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     L = kq.lib()
     declared = _declared_functions()
-    assert len(declared) == 11, declared
+    assert len(declared) == 12, declared
     assert sorted(kq.exported_symbols) == declared
     for name in declared:
         assert hasattr(L, name), name
@@ -147,6 +147,43 @@ def test_linear_validation_without_device():
     st = L.kq_gemv_small_m(kq.KQ_W8_PER_CHANNEL, P(16), 4, 128, 64, P(32), P(48), P(64), None,
                            P(80), kq.KQ_DTYPE_BF16, P(96), 1 << 30, None)
     assert st == kq.KQ_ERR_INVALID_VALUE and "gbias must be NULL" in kq.kq_last_error()
+
+
+def _gated(fmt=kq.KQ_W8_PER_CHANNEL, M=64, K=128, N=64, gbias=None, residual=None, gate=None,
+           gate_rows=1, y=1 << 20, dtype=kq.KQ_DTYPE_BF16, wsb=1 << 30):
+    return kq.lib().kq_linear_gated(fmt, P(16), M, K, N, P(32), P(48), P(gbias) if gbias else None,
+                                    None, P(residual) if residual else None,
+                                    P(gate) if gate else None, gate_rows, P(y), dtype, P(1 << 24),
+                                    wsb, None)
+
+
+def test_gated_linear_validation_without_device():
+    assert _gated(dtype=kq.KQ_DTYPE_I32) == kq.KQ_ERR_UNSUPPORTED
+    assert "writes f32 or bf16, not i32" in kq.kq_last_error()
+    assert _gated(gate_rows=0, gate=64) == kq.KQ_ERR_INVALID_VALUE
+    assert "gate_rows=0" in kq.kq_last_error()
+    assert _gated(residual=(1 << 21) + 8) == kq.KQ_ERR_INVALID_VALUE
+    assert "residual must be 16-byte aligned" in kq.kq_last_error()
+    assert _gated(gate=(1 << 21) + 2) == kq.KQ_ERR_INVALID_VALUE
+    assert "gate must be 4-byte aligned" in kq.kq_last_error()
+    assert _gated(fmt=2) == kq.KQ_ERR_INVALID_VALUE
+    assert _gated(gbias=64) == kq.KQ_ERR_INVALID_VALUE and "gbias must be NULL" in kq.kq_last_error()
+    # a residual that overlaps y without being y (bf16 y of 64*64*2 bytes)
+    assert _gated(residual=(1 << 20) + 4096) == kq.KQ_ERR_INVALID_VALUE
+    assert "overlaps y" in kq.kq_last_error()
+    assert _gated(residual=(1 << 20) - 4096) == kq.KQ_ERR_INVALID_VALUE
+    # in place needs a bf16 output; a disjoint or in-place residual passes
+    # the overlap checks and stops at the (too small) workspace instead
+    assert _gated(residual=1 << 20, dtype=kq.KQ_DTYPE_F32) == kq.KQ_ERR_INVALID_VALUE
+    assert "in-place residual needs a bf16 output" in kq.kq_last_error()
+    for r in ((1 << 20) + 64 * 64 * 2, (1 << 20) - 64 * 64 * 2, 1 << 20):
+        assert _gated(residual=r, wsb=100) == kq.KQ_ERR_WORKSPACE, r
+    # the plain linears' checks still apply
+    assert _gated(K=100) == kq.KQ_ERR_UNSUPPORTED
+    assert _gated(fmt=kq.KQ_W4_AFFINE_G64) == kq.KQ_ERR_INVALID_VALUE
+    assert "group offsets" in kq.kq_last_error()
+    assert _gated(wsb=100) == kq.KQ_ERR_WORKSPACE
+    assert _gated(M=0) == kq.KQ_SUCCESS
 
 
 def test_quantizer_validation_without_device():

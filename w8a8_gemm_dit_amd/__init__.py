@@ -21,7 +21,7 @@ __all__ = [
     "KQ_DTYPE_I32", "KQ_MAX_K", "KQ_GEMV_MAX_M", "lib", "lib_path", "exported_symbols",
     "kq_is_available", "kq_last_error", "kq_workspace_bytes", "kq_route",
     "kq_quantize_weights", "kq_quantize_act", "kq_w8a8_linear", "kq_w4a8_linear",
-    "kq_gemv_small_m", "kq_w8a8_gemm", "kq_w4a8_gemm", "KqError",
+    "kq_gemv_small_m", "kq_w8a8_gemm", "kq_w4a8_gemm", "kq_linear_gated", "KqError",
 ]
 
 KQ_SUCCESS, KQ_ERR_INVALID_VALUE, KQ_ERR_UNSUPPORTED = 0, 1, 2
@@ -41,6 +41,7 @@ exported_symbols = (
     "kq_is_available", "kq_last_error", "kq_workspace_bytes", "kq_route",
     "kq_quantize_weights", "kq_quantize_act", "kq_w8a8_linear",
     "kq_w4a8_linear", "kq_gemv_small_m", "kq_w8a8_gemm", "kq_w4a8_gemm",
+    "kq_linear_gated",
 )
 
 
@@ -91,6 +92,9 @@ def lib() -> ctypes.CDLL:
     L.kq_w4a8_gemm.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp]
     L.kq_gemv_small_m.restype = i32
     L.kq_gemv_small_m.argtypes = [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    L.kq_linear_gated.restype = i32
+    L.kq_linear_gated.argtypes = [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, i64, vp, i32,
+                                  vp, sz, vp]
     _lib = L
     return L
 
@@ -267,6 +271,43 @@ def kq_gemv_small_m(fmt, x, wq, scale, gbias=None, bias=None, out_dtype=torch.bf
     ws, wsb = _prep_ws(workspace, M, K, fmt, x.device)
     _check(lib().kq_gemv_small_m(fmt, _ptr(x), M, K, N, _ptr(wq), _ptr(scale), _ptr(gbias),
                                  _ptr(bias), _ptr(y), _OUT[out_dtype], _ptr(ws), wsb, _stream()))
+    return y
+
+
+def kq_linear_gated(fmt, x, wq, scale, gbias=None, bias=None, residual=None, gate=None,
+                    gate_rows=1, out_dtype=torch.bfloat16, out=None, workspace=None):
+    """out = residual + gate[m // gate_rows] * linear(x), in the linear's
+    epilogue.  residual: bf16 [M,N] or None (may be `out` itself for a bf16
+    output); gate: fp32 [ceil(M/gate_rows), N] or None."""
+    _need(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    N = wq.shape[0]
+    if fmt == KQ_W4_AFFINE_G64:
+        _need(wq, "wq", torch.uint8, 2)
+        _need(scale, "scale", torch.float16, 2)
+        _need(gbias, "gbias", torch.float16, 2)
+    elif fmt == KQ_W8_PER_CHANNEL:
+        _need(wq, "wq", torch.int8, 2)
+        _need(scale, "scale", torch.float32, 1)
+    else:
+        raise ValueError(f"unknown weight format {fmt}")
+    if bias is not None:
+        _need(bias, "bias", torch.float32, 1)
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16, 2)
+        if tuple(residual.shape) != (M, N):
+            raise ValueError(f"[kq_linear_gated] residual must be [{M}, {N}]")
+    if gate is not None:
+        _need(gate, "gate", torch.float32, 2)
+        if gate_rows < 1 or tuple(gate.shape) != (-(-M // gate_rows), N):
+            raise ValueError("[kq_linear_gated] gate must be [ceil(M/gate_rows), N]")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("[kq_linear_gated] out_dtype must be float32 or bfloat16")
+    y = _prep_out(out, (M, N), out_dtype, x.device)
+    ws, wsb = _prep_ws(workspace, M, K, fmt, x.device)
+    _check(lib().kq_linear_gated(fmt, _ptr(x), M, K, N, _ptr(wq), _ptr(scale), _ptr(gbias),
+                                 _ptr(bias), _ptr(residual), _ptr(gate), gate_rows, _ptr(y),
+                                 _OUT[out_dtype], _ptr(ws), wsb, _stream()))
     return y
 
 

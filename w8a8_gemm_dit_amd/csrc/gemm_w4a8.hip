@@ -71,11 +71,12 @@ __device__ __forceinline__ void store1(void* y, int64_t idx, float v) {
   else reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)f32_to_bf16_rne(v);
 }
 
-template <int BM, int BN, int WTM, int WTN, int OUT>
+// GATED: the output goes through the gated residual epilogue (kq::Epilogue).
+template <int BM, int BN, int WTM, int WTN, int OUT, bool GATED>
 __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int32_t* __restrict__ gsum,
     const uint8_t* __restrict__ Q, const uint16_t* __restrict__ GS, const uint16_t* __restrict__ GB,
-    const float* __restrict__ bias, void* __restrict__ y, int M, int N, int K) {
+    const float* __restrict__ bias, void* y, int M, int N, int K, Epilogue ep) {
   using C = Cfg4<BM, BN, WTM, WTN>;
   constexpr bool kScaled = OUT != kOutI32;
   __shared__ int4 lds0[C::kSlots], lds1[C::kSlots], lds2[C::kSlots], lds3[C::kSlots];
@@ -349,7 +350,9 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int rl = 16 * j + 4 * fc + r;  // row within the block
-          const float v = fmaf(sx[m0 + wm * WTM + rl], acc[i][j][r], bv);
+          float v = fmaf(sx[m0 + wm * WTM + rl], acc[i][j][r], bv);
+          if (GATED)
+            v = gated1(v, ep.residual, ep.gate, ep.gate_rows, m0 + wm * WTM + rl, n0 + q_col0 + 16 * i, N);
           *reinterpret_cast<uint16_t*>(stage + rl * (WTN * 2) + (((cl >> 3) ^ (rl & 7)) * 16) +
                                        (cl & 7) * 2) = (uint16_t)f32_to_bf16_rne(v);
         }
@@ -374,7 +377,11 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + wm * WTM + 16 * j + 4 * fc + r;
-        if (m < M && n < N) store1<OUT>(y, (int64_t)m * N + n, fmaf(sx[m], acc[i][j][r], bv));
+        if (m < M && n < N) {
+          float v = fmaf(sx[m], acc[i][j][r], bv);
+          if (GATED) v = gated1(v, ep.residual, ep.gate, ep.gate_rows, m, n, N);
+          store1<OUT>(y, (int64_t)m * N + n, v);
+        }
       }
     }
   }
@@ -383,16 +390,21 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
 template <int BM, int BN, int WTM, int WTN>
 const char* launch_tile4(const int8_t* a, const float* sx, const int32_t* gsum, const uint8_t* q4,
                          const uint16_t* gs, const uint16_t* gb, const float* bias, void* y,
-                         int out, int M, int N, int K, hipStream_t s, const char* name) {
+                         int out, int M, int N, int K, hipStream_t s, const Epilogue& ep,
+                         const char* name) {
   using C = Cfg4<BM, BN, WTM, WTN>;
   const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const dim3 grid((unsigned)tiles), block(C::kThreads);
-  if (out == kOutF32)
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutF32>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K);
+  if (ep.active() && out == kOutF32)
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutF32, true>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep);
+  else if (ep.active() && out == kOutBF16)
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutBF16, true>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep);
+  else if (out == kOutF32)
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutF32, false>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep);
   else if (out == kOutBF16)
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutBF16>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutBF16, false>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep);
   else
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutI32>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutI32, false>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep);
   return name;
 }
 
@@ -401,13 +413,13 @@ const char* launch_tile4(const int8_t* a, const float* sx, const int32_t* gsum, 
 const char* launch_gemm_w4a8(int tile, const int8_t* a, const float* sx, const int32_t* gsum,
                              const uint8_t* q4, const void* gs, const void* gb,
                              const float* bias, void* y, int out, int M, int N, int K,
-                             hipStream_t s) {
+                             hipStream_t s, const Epilogue& ep) {
   const uint16_t* hs = reinterpret_cast<const uint16_t*>(gs);
   const uint16_t* hb = reinterpret_cast<const uint16_t*>(gb);
   if (tile == kTile128x256)
-    return launch_tile4<128, 256, 64, 64>(a, sx, gsum, q4, hs, hb, bias, y, out, M, N, K, s,
+    return launch_tile4<128, 256, 64, 64>(a, sx, gsum, q4, hs, hb, bias, y, out, M, N, K, s, ep,
                                           "gemm_w4a8_128x256");
-  return launch_tile4<64, 128, 32, 64>(a, sx, gsum, q4, hs, hb, bias, y, out, M, N, K, s,
+  return launch_tile4<64, 128, 32, 64>(a, sx, gsum, q4, hs, hb, bias, y, out, M, N, K, s, ep,
                                        "gemm_w4a8_64x128");
 }
 

@@ -145,11 +145,12 @@ __device__ __forceinline__ void store4(void* y, int64_t idx, const float v[4], c
 // multiple of 4, so guarded tail steps follow the loop; the conditional
 // tail makes the register allocator copy accumulators at the loop back-edge,
 // so it is compiled only into the variant that needs it.
-template <int BM, int BN, int WM, int WN, int OUT, bool REM>
+// GATED: the output goes through the gated residual epilogue (kq::Epilogue).
+template <int BM, int BN, int WM, int WN, int OUT, bool REM, bool GATED>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int8_t* __restrict__ W,
-    const float* __restrict__ sw, const float* __restrict__ bias, void* __restrict__ y, int M,
-    int N, int K) {
+    const float* __restrict__ sw, const float* __restrict__ bias, void* y, int M,
+    int N, int K, Epilogue ep) {
   using C = Cfg<BM, BN, WM, WN>;
   // Two pair buffers (steps 4i, 4i+1 and 4i+2, 4i+3): each its own array,
   // so the compiler's tracking of the asynchronous LDS writes never couples
@@ -317,10 +318,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
       for (int j = 0; j < C::kTM; ++j) {
         const int r = 16 * j + fr;
         const float sm = s_m[j];
-        const uint32_t lo = pack_bf16x2(fmaf(sm * swv.x, (float)acc[i][j][0], bv.x),
-                                        fmaf(sm * swv.y, (float)acc[i][j][1], bv.y));
-        const uint32_t hi = pack_bf16x2(fmaf(sm * swv.z, (float)acc[i][j][2], bv.z),
-                                        fmaf(sm * swv.w, (float)acc[i][j][3], bv.w));
+        float v[4] = {fmaf(sm * swv.x, (float)acc[i][j][0], bv.x),
+                      fmaf(sm * swv.y, (float)acc[i][j][1], bv.y),
+                      fmaf(sm * swv.z, (float)acc[i][j][2], bv.z),
+                      fmaf(sm * swv.w, (float)acc[i][j][3], bv.w)};
+        if (GATED) gated4(v, ep.residual, ep.gate, ep.gate_rows, m0 + wm * C::kWTM + r, n, N);
+        const uint32_t lo = pack_bf16x2(v[0], v[1]);
+        const uint32_t hi = pack_bf16x2(v[2], v[3]);
         *reinterpret_cast<uint2*>(stage + r * (C::kWTN * 2) + ((c ^ (r & 3)) * 16) + (fc & 1) * 8) =
             make_uint2(lo, hi);
       }
@@ -365,6 +369,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
         iv[r] = acc[i][j][r];
         v[r] = fmaf(s_m[j] * swv[r], (float)iv[r], bv[r]);
       }
+      if (GATED) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) v[r] = gated1(v[r], ep.residual, ep.gate, ep.gate_rows, m, n + r, N);
+      }
       store4<OUT>(y, (int64_t)m * N + n, v, iv, min(4, N - n), vec_ok);
     }
   }
@@ -372,25 +381,31 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
 
 template <int BM, int BN, int WM, int WN, bool REM>
 void launch_rem(const int8_t* a, const float* sx, const int8_t* q, const float* sw,
-                const float* bias, void* y, int out, int M, int N, int K, hipStream_t s) {
+                const float* bias, void* y, int out, int M, int N, int K, hipStream_t s,
+                const Epilogue& ep) {
   const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const dim3 grid((unsigned)tiles), block(64 * WM * WN);
-  if (out == kOutF32)
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutF32, REM>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
+  const bool g = ep.active();
+  if (out == kOutF32 && g)
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutF32, REM, true>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep);
+  else if (out == kOutF32)
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutF32, REM, false>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep);
+  else if (out == kOutBF16 && g)
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutBF16, REM, true>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep);
   else if (out == kOutBF16)
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutBF16, REM>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutBF16, REM, false>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep);
   else
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutI32, REM>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutI32, REM, false>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep);
 }
 
 template <int BM, int BN, int WM = 2, int WN = 2>
 const char* launch_tile(const int8_t* a, const float* sx, const int8_t* q, const float* sw,
                         const float* bias, void* y, int out, int M, int N, int K,
-                        hipStream_t s, const char* name) {
+                        hipStream_t s, const Epilogue& ep, const char* name) {
   if ((K / 64) % 4 == 0)
-    launch_rem<BM, BN, WM, WN, false>(a, sx, q, sw, bias, y, out, M, N, K, s);
+    launch_rem<BM, BN, WM, WN, false>(a, sx, q, sw, bias, y, out, M, N, K, s, ep);
   else
-    launch_rem<BM, BN, WM, WN, true>(a, sx, q, sw, bias, y, out, M, N, K, s);
+    launch_rem<BM, BN, WM, WN, true>(a, sx, q, sw, bias, y, out, M, N, K, s, ep);
   return name;
 }
 
@@ -398,18 +413,18 @@ const char* launch_tile(const int8_t* a, const float* sx, const int8_t* q, const
 
 const char* launch_gemm_w8a8(int tile, const int8_t* a, const float* sx, const int8_t* q,
                              const float* sw, const float* bias, void* y, int out, int M,
-                             int N, int K, hipStream_t s) {
+                             int N, int K, hipStream_t s, const Epilogue& ep) {
   switch (tile) {
     case kTile256x256:
-      return launch_tile<256, 256>(a, sx, q, sw, bias, y, out, M, N, K, s, "gemm_w8a8_256x256");
+      return launch_tile<256, 256>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_256x256");
     case kTile256x192:
-      return launch_tile<256, 192, 4, 2>(a, sx, q, sw, bias, y, out, M, N, K, s, "gemm_w8a8_256x192");
+      return launch_tile<256, 192, 4, 2>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_256x192");
     case kTile256x128:
-      return launch_tile<256, 128>(a, sx, q, sw, bias, y, out, M, N, K, s, "gemm_w8a8_256x128");
+      return launch_tile<256, 128>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_256x128");
     case kTile128x128:
-      return launch_tile<128, 128>(a, sx, q, sw, bias, y, out, M, N, K, s, "gemm_w8a8_128x128");
+      return launch_tile<128, 128>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_128x128");
     default:
-      return launch_tile<64, 64>(a, sx, q, sw, bias, y, out, M, N, K, s, "gemm_w8a8_64x64");
+      return launch_tile<64, 64>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_64x64");
   }
 }
 

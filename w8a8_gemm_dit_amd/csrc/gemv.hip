@@ -43,7 +43,7 @@ template <bool W4, int OUT>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ sx,
     const void* __restrict__ Wq, const void* __restrict__ gsv, const void* __restrict__ gbv,
-    const float* __restrict__ bias, void* __restrict__ y, int Mtot, int N, int K) {
+    const float* __restrict__ bias, void* y, int Mtot, int N, int K, Epilogue ep) {
   // this workgroup's 16-row block of the activations
   const int m0 = blockIdx.y * 16;
   const int M = min(16, Mtot - m0);
@@ -225,7 +225,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
     if (OUT == kOutI32) {
       reinterpret_cast<int32_t*>(y)[idx] = iacc[r];
     } else {
-      const float v = W4 ? fmaf(sxm[r], facc[r], bv) : fmaf(sxm[r] * swn, (float)iacc[r], bv);
+      float v = W4 ? fmaf(sxm[r], facc[r], bv) : fmaf(sxm[r] * swn, (float)iacc[r], bv);
+      if (ep.active()) v = gated1(v, ep.residual, ep.gate, ep.gate_rows, m0 + m, nn, N);
       if (OUT == kOutF32) reinterpret_cast<float*>(y)[idx] = v;
       else reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)f32_to_bf16_rne(v);
     }
@@ -235,15 +236,15 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
 template <bool W4>
 const char* launch_fmt(const int8_t* a, const float* sx, const void* q, const void* gs,
                        const void* gb, const float* bias, void* y, int out, int M, int N, int K,
-                       hipStream_t s) {
+                       hipStream_t s, const Epilogue& ep) {
   const dim3 grid((unsigned)((N + 15) / 16), (unsigned)((M + 15) / 16)), block(kWaves * 64);
   const size_t sb = (W4 && out != kOutI32) ? (size_t)16 * (K / 64) * sizeof(uint32_t) : 0;
   if (out == kOutF32)
-    hipLaunchKernelGGL((gemv_kernel<W4, kOutF32>), grid, block, sb, s, a, sx, q, gs, gb, bias, y, M, N, K);
+    hipLaunchKernelGGL((gemv_kernel<W4, kOutF32>), grid, block, sb, s, a, sx, q, gs, gb, bias, y, M, N, K, ep);
   else if (out == kOutBF16)
-    hipLaunchKernelGGL((gemv_kernel<W4, kOutBF16>), grid, block, sb, s, a, sx, q, gs, gb, bias, y, M, N, K);
+    hipLaunchKernelGGL((gemv_kernel<W4, kOutBF16>), grid, block, sb, s, a, sx, q, gs, gb, bias, y, M, N, K, ep);
   else
-    hipLaunchKernelGGL((gemv_kernel<W4, kOutI32>), grid, block, sb, s, a, sx, q, gs, gb, bias, y, M, N, K);
+    hipLaunchKernelGGL((gemv_kernel<W4, kOutI32>), grid, block, sb, s, a, sx, q, gs, gb, bias, y, M, N, K, ep);
   return W4 ? "gemv_w4a8" : "gemv_w8a8";
 }
 
@@ -251,9 +252,10 @@ const char* launch_fmt(const int8_t* a, const float* sx, const void* q, const vo
 
 const char* launch_gemv(bool w4, const int8_t* a, const float* sx, const int32_t* /*gsum*/,
                         const void* q, const void* gs, const void* gb, const float* bias,
-                        void* y, int out, int M, int N, int K, hipStream_t s) {
-  return w4 ? launch_fmt<true>(a, sx, q, gs, gb, bias, y, out, M, N, K, s)
-            : launch_fmt<false>(a, sx, q, gs, gb, bias, y, out, M, N, K, s);
+                        void* y, int out, int M, int N, int K, hipStream_t s,
+                        const Epilogue& ep) {
+  return w4 ? launch_fmt<true>(a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep)
+            : launch_fmt<false>(a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep);
 }
 
 }  // namespace kq

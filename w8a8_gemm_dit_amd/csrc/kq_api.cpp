@@ -90,13 +90,14 @@ const char* dtype_name(kq_dtype d) {
 kq_status launch_main(const char* op, int force, kq_wformat fmt, const int8_t* codes,
                       const float* sx, const int32_t* gsum, int64_t M, int64_t K, int64_t N,
                       const void* wq, const void* scale, const void* gbias, const float* bias,
-                      void* y, kq_dtype y_dtype, hipStream_t s, const char* kq_name) {
+                      void* y, kq_dtype y_dtype, hipStream_t s, const char* kq_name,
+                      const kq::Epilogue& ep = kq::Epilogue()) {
   const kq_route_info r = kq::choose_route(M, N, K, fmt, force, env_tile());
   const int out = out_kind(y_dtype);
   const char* k2;
   if (r.kind == KQ_ROUTE_GEMV) {
     k2 = kq::launch_gemv(fmt == KQ_W4_AFFINE_G64, codes, sx, gsum, wq, scale, gbias, bias, y, out,
-                         (int)M, (int)N, (int)K, s);
+                         (int)M, (int)N, (int)K, s, ep);
   } else {
     int tile = 0;
     for (int t = 0; t < kq::kNumTiles; ++t)
@@ -104,16 +105,17 @@ kq_status launch_main(const char* op, int force, kq_wformat fmt, const int8_t* c
     if (fmt == KQ_W8_PER_CHANNEL)
       k2 = kq::launch_gemm_w8a8(tile, codes, sx, reinterpret_cast<const int8_t*>(wq),
                                 reinterpret_cast<const float*>(scale), bias, y, out, (int)M,
-                                (int)N, (int)K, s);
+                                (int)N, (int)K, s, ep);
     else
       k2 = kq::launch_gemm_w4a8(tile, codes, sx, gsum, reinterpret_cast<const uint8_t*>(wq),
-                                scale, gbias, bias, y, out, (int)M, (int)N, (int)K, s);
+                                scale, gbias, bias, y, out, (int)M, (int)N, (int)K, s, ep);
   }
   const kq_status st = check_launch(op);
   if (st != KQ_SUCCESS) return st;
   if (env_log())
-    fprintf(stderr, "[kq] %s M=%lld N=%lld K=%lld out=%s route=%s kernels=%s%s%s tile=%dx%d grid=%lld\n",
+    fprintf(stderr, "[kq] %s M=%lld N=%lld K=%lld out=%s%s route=%s kernels=%s%s%s tile=%dx%d grid=%lld\n",
             op, (long long)M, (long long)N, (long long)K, dtype_name(y_dtype),
+            ep.active() ? " gated" : "",
             r.kind == KQ_ROUTE_GEMV ? "gemv" : "gemm", kq_name ? kq_name : "",
             kq_name ? "," : "", k2, r.tile_m, r.tile_n, (long long)r.grid);
   return KQ_SUCCESS;
@@ -145,7 +147,7 @@ kq_status check_linear_args(const char* op, int force, kq_wformat fmt, int64_t M
 kq_status run_linear(const char* op, int force, kq_wformat fmt, const void* x, int64_t M,
                      int64_t K, int64_t N, const void* wq, const void* scale, const void* gbias,
                      const float* bias, void* y, kq_dtype y_dtype, void* ws, size_t ws_bytes,
-                     void* stream) {
+                     void* stream, const kq::Epilogue& ep = kq::Epilogue()) {
   kq_status st = check_linear_args(op, force, fmt, M, K, N, y_dtype, x, wq, scale, gbias, y);
   if (st != KQ_SUCCESS || M == 0 || N == 0) return st;
   if (!aligned16(ws))
@@ -166,7 +168,7 @@ kq_status run_linear(const char* op, int force, kq_wformat fmt, const void* x, i
   st = check_launch(op);
   if (st != KQ_SUCCESS) return st;
   return launch_main(op, force, fmt, codes, sx, gsum, M, K, N, wq, scale, gbias, bias, y, y_dtype,
-                     s, kq_name);
+                     s, kq_name, ep);
 }
 
 // Shared body of the entry points on pre-quantized activations.
@@ -319,6 +321,44 @@ kq_status kq_gemv_small_m(kq_wformat fmt, const void* x, int64_t M, int64_t K, i
     return fail(KQ_ERR_INVALID_VALUE, "[%s] int8 weights take no group offsets (gbias must be NULL)", op);
   return run_linear(op, 2, fmt, x, M, K, N, wq, scale, gbias, bias, y, y_dtype, ws, ws_bytes,
                     stream);
+}
+
+kq_status kq_linear_gated(kq_wformat fmt, const void* x, int64_t M, int64_t K, int64_t N,
+                          const void* wq, const void* scale, const void* gbias, const float* bias,
+                          const void* residual, const float* gate, int64_t gate_rows, void* y,
+                          kq_dtype y_dtype, void* ws, size_t ws_bytes, void* stream) {
+  const char* op = "kq_linear_gated";
+  if (fmt != KQ_W8_PER_CHANNEL && fmt != KQ_W4_AFFINE_G64)
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] unknown weight format %d", op, (int)fmt);
+  if (fmt == KQ_W8_PER_CHANNEL && gbias)
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] int8 weights take no group offsets (gbias must be NULL)", op);
+  if (y_dtype != KQ_DTYPE_F32 && y_dtype != KQ_DTYPE_BF16)
+    return fail(KQ_ERR_UNSUPPORTED, "[%s] the gated epilogue writes f32 or bf16, not %s", op,
+                dtype_name(y_dtype));
+  if (gate_rows < 1 || gate_rows > INT32_MAX)
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] gate_rows=%lld must be in [1, 2^31)", op,
+                (long long)gate_rows);
+  if (residual && !aligned16(residual))
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] residual must be 16-byte aligned", op);
+  if (gate && ((uintptr_t)gate & 3))
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] gate must be 4-byte aligned", op);
+  if (residual && y && residual != y && M > 0 && N > 0) {
+    // Only an exact alias is race-free: each output element reads its own
+    // residual element before writing it, but overlapping shifted ranges
+    // would read elements another workgroup has already written.
+    const uintptr_t r0 = (uintptr_t)residual, r1 = r0 + (uintptr_t)(M * N * 2);
+    const uintptr_t y0 = (uintptr_t)y, y1 = y0 + (uintptr_t)(M * N * (y_dtype == KQ_DTYPE_F32 ? 4 : 2));
+    if (r0 < y1 && y0 < r1)
+      return fail(KQ_ERR_INVALID_VALUE, "[%s] residual overlaps y without being y itself", op);
+  }
+  if (residual && residual == y && y_dtype != KQ_DTYPE_BF16)
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] an in-place residual needs a bf16 output", op);
+  kq::Epilogue ep;
+  ep.residual = reinterpret_cast<const uint16_t*>(residual);
+  ep.gate = gate;
+  ep.gate_rows = (int)gate_rows;
+  return run_linear(op, env_force_route(), fmt, x, M, K, N, wq, scale, gbias, bias, y, y_dtype,
+                    ws, ws_bytes, stream, ep);
 }
 
 }  // extern "C"

@@ -12,6 +12,16 @@ namespace kq {
 
 enum OutKind : int { kOutF32 = 0, kOutBF16 = 1, kOutI32 = 2 };
 
+// Optional gated residual epilogue of the linears: out = residual +
+// gate[m / gate_rows] * y, one fma per element before the output rounding.
+// A null residual reads as 0 and a null gate as 1; plain launches pass {}.
+struct Epilogue {
+  const uint16_t* residual = nullptr;  // bf16 [M,N], may be the output itself
+  const float* gate = nullptr;         // fp32 [ceil(M/gate_rows), N]
+  int gate_rows = 1;                   // token rows per gate row (>= 1)
+  __host__ __device__ bool active() const { return residual != nullptr || gate != nullptr; }
+};
+
 const char* launch_quant_act(const uint16_t* x, int64_t M, int K, int8_t* a, float* sx,
                              int32_t* gsum, hipStream_t s);
 const char* launch_quant_w8(const float* w, int64_t N, int K, int8_t* q, float* sw,
@@ -22,17 +32,18 @@ const char* launch_quant_w4(const float* w, int64_t N, int K, uint8_t* q4, void*
 // W8A8 GEMM on quantized activations: y = sx*sw*(a . q^T) + bias.
 const char* launch_gemm_w8a8(int tile, const int8_t* a, const float* sx, const int8_t* q,
                              const float* sw, const float* bias, void* y, int out, int M,
-                             int N, int K, hipStream_t s);
+                             int N, int K, hipStream_t s, const Epilogue& ep = Epilogue());
 
 // W4A8 GEMM: y = sx * sum_g (gs*P + gb*A) + bias (or P per group for I32).
 const char* launch_gemm_w4a8(int tile, const int8_t* a, const float* sx, const int32_t* gsum,
                              const uint8_t* q4, const void* gs, const void* gb,
                              const float* bias, void* y, int out, int M, int N, int K,
-                             hipStream_t s);
+                             hipStream_t s, const Epilogue& ep = Epilogue());
 
 // GEMV for 1 <= M <= 16 (w4: q is packed int4 with gs/gb; w8: q int8, gs = fp32 [N]).
 const char* launch_gemv(bool w4, const int8_t* a, const float* sx, const int32_t* gsum,
                         const void* q, const void* gs, const void* gb, const float* bias,
-                        void* y, int out, int M, int N, int K, hipStream_t s);
+                        void* y, int out, int M, int N, int K, hipStream_t s,
+                        const Epilogue& ep = Epilogue());
 
 }  // namespace kq
