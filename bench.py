@@ -111,6 +111,23 @@ class Prepared:
             kq.kq_w4a8_linear(c["x"], c["wq"], c["sc"], c["gb"], c["b"], out_dtype=self.out_dtype,
                               out=c["y"], workspace=c["ws"])
 
+    def add_gate(self, gate_rows: int, seed: int = 0) -> None:
+        """fp32 gates [ceil(M/gate_rows), N] for the gated residual calls."""
+        import synth
+        from tests.parity import dev
+        self.gate_rows = gate_rows
+        g = dev(synth.random_f32((-(-self.wl.M // gate_rows), self.wl.N), seed=seed + 40,
+                                 scale=0.5))
+        for r, c in enumerate(self.copies):
+            c["gate"] = g if r == 0 else g.clone()
+
+    def gated(self, i: int) -> None:
+        """The DiT residual update in place: y += gate[m / L] * linear(x)."""
+        c = self.copies[i % self.R]
+        self.kq.kq_linear_gated(self.fmt, c["x"], c["wq"], c["sc"], c["gb"], c["b"],
+                                residual=c["y"], gate=c["gate"], gate_rows=self.gate_rows,
+                                out_dtype=self.out_dtype, out=c["y"], workspace=c["ws"])
+
     def gemm(self, i: int) -> None:
         c = self.copies[i % self.R]
         kq = self.kq
@@ -383,11 +400,29 @@ def main() -> int:
             "method": "extra replays of the timed graph; distribution-free order-statistic interval",
         }
         log(f"samples: median {med * 1e3:.2f} us/step, 95% CI [{lo * 1e3:.2f}, {hi * 1e3:.2f}] us")
+    gated = None
+    if not args.quick and wl.out == "bf16":
+        # the same linear with the gated residual epilogue, updating the
+        # residual stream in place (4 samples of 1024 tokens: one gate row each)
+        L = 1024
+        p.add_gate(L)
+        t = graph_time(p.gated, max(20, args.steps // 5))
+        extra_bytes = 2 * wl.M * wl.N + 4 * (-(-wl.M // L)) * wl.N  # residual read, gates
+        gated = {
+            "ms_per_call": round(t, 5), "gate_rows": L, "in_place": True,
+            "tops": round(wl.ops / (t * 1e-3) / 1e12, 2),
+            "overhead_vs_plain_pct": round(100 * (t - ms) / ms, 2),
+            "gbs": round((algorithmic_bytes(wl) + extra_bytes) / (t * 1e-3) / 1e9, 1),
+        }
+        log(f"gated residual (in place, L={L}): {t * 1e3:.2f} us/call "
+            f"({gated['overhead_vs_plain_pct']:+.1f}% vs plain)")
     del p
     torch.cuda.empty_cache()
 
     if not args.quick:
         extra = {}
+        if gated is not None:
+            extra[wl.name + "+gated_residual"] = gated
         steps_x = max(20, args.steps // 5)
         for name, w in synth.WORKLOADS.items():
             if name == synth.HEADLINE:

@@ -208,6 +208,30 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
     }
   };
 
+  // bf16 output of a full tile leaves through an LDS stage (epilogue below).
+  constexpr int kStage = C::kWTM * C::kWTN * 2;          // bytes of one wave's bf16 block
+  constexpr int kPerSlot = (C::kPairSlots * 16) / kStage;  // blocks per pair buffer
+  constexpr int kRowChunks = C::kWTN / 8;                // 16-byte chunks per block row
+  constexpr int kResLoads = C::kWTM * kRowChunks / 64;   // 16-byte residual loads per lane
+  const bool staged = OUT == kOutBF16 && kPerSlot * 2 >= C::kWaves && (N % 8) == 0 &&
+                      m0 + BM <= M && n0 + BN <= N;
+  // Gated, staged: the wave's residual block, read with whole 16-byte row
+  // chunks.  Where registers allow, the loads go out before the K loop and
+  // land while it runs (the vmcnt waits of the loop's first step then
+  // include them); otherwise they go out in the epilogue.
+  constexpr bool kResEarly = GATED && kResLoads <= 16;
+  const int64_t mrow0 = m0 + wm * C::kWTM;
+  v4i res[GATED ? kResLoads : 1];
+  auto load_residual = [&]() {
+    const uint16_t* rb = ep.residual + mrow0 * N + n0 + wn * C::kWTN;
+#pragma unroll
+    for (int u = 0; u < kResLoads; ++u) {
+      const int e = lane + 64 * u;
+      res[u] = *reinterpret_cast<const v4i*>(rb + (int64_t)(e / kRowChunks) * N + 8 * (e % kRowChunks));
+    }
+  };
+  if (kResEarly && staged && ep.residual != nullptr) load_residual();
+
   v4i acc[C::kTN][C::kTM];
 #pragma unroll
   for (int i = 0; i < C::kTN; ++i)
@@ -293,11 +317,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
   // bf16 output of a full tile goes through LDS: each wavefront writes its
   // block, row-major, into a free ring slot and then stores whole 16-byte
   // row chunks (non-temporal), instead of 8-byte pieces of 16 rows.
-  constexpr int kStage = C::kWTM * C::kWTN * 2;          // bytes of one wave's bf16 block
-  constexpr int kPerSlot = (C::kPairSlots * 16) / kStage;  // blocks per pair buffer
-  constexpr int kRowChunks = C::kWTN / 8;                // 16-byte chunks per block row
-  if (OUT == kOutBF16 && kPerSlot * 2 >= C::kWaves && (N % 8) == 0 && m0 + BM <= M &&
-      n0 + BN <= N) {
+  if (staged) {
     __builtin_amdgcn_sched_barrier(0);
     barrier_nofence();  // every wave is done with the ring (its loads drained above)
     const int sidx = wave / kPerSlot;
@@ -306,9 +326,31 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
     float s_m[C::kTM];
 #pragma unroll
     for (int j = 0; j < C::kTM; ++j) s_m[j] = sx[m0 + wm * C::kWTM + j * 16 + fr];
+    // Gated: the residual block goes into the stage at the places its
+    // outputs take (each lane then reads its 4 values where it writes the
+    // result); a tile whose rows share one gate row reads that row once per
+    // column group.
+    const bool one_gate = GATED && ep.gate != nullptr &&
+                          m0 / ep.gate_rows == (m0 + BM - 1) / ep.gate_rows;
+    if (GATED && ep.residual != nullptr) {
+      if (!kResEarly) load_residual();
+#pragma unroll
+      for (int u = 0; u < kResLoads; ++u) {
+        const int e = lane + 64 * u;
+        const int r = e / kRowChunks, c = e % kRowChunks;
+        *reinterpret_cast<v4i*>(stage + r * (C::kWTN * 2) + ((c ^ (r & 3)) * 16)) = res[u];
+      }
+      // lanes read what other lanes of the wave wrote: keep the order
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    }
 #pragma unroll
     for (int i = 0; i < C::kTN; ++i) {
       const int n = n0 + wn * C::kWTN + i * 16 + fc * 4;
+      float g4[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+      if (one_gate) {
+        const float* gr = ep.gate + (int64_t)(m0 / ep.gate_rows) * N + n;
+        g4[0] = gr[0]; g4[1] = gr[1]; g4[2] = gr[2]; g4[3] = gr[3];
+      }
       // sw and bias are only 4-byte aligned by contract: scalar loads
       const float4 swv = make_float4(sw[n], sw[n + 1], sw[n + 2], sw[n + 3]);
       const float4 bv = bias ? make_float4(bias[n], bias[n + 1], bias[n + 2], bias[n + 3])
@@ -322,13 +364,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
                       fmaf(sm * swv.y, (float)acc[i][j][1], bv.y),
                       fmaf(sm * swv.z, (float)acc[i][j][2], bv.z),
                       fmaf(sm * swv.w, (float)acc[i][j][3], bv.w)};
-        if (GATED) gated4(v, ep.residual, ep.gate, ep.gate_rows, m0 + wm * C::kWTM + r, n, N);
-        const uint32_t lo = pack_bf16x2(v[0], v[1]);
-        const uint32_t hi = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(stage + r * (C::kWTN * 2) + ((c ^ (r & 3)) * 16) + (fc & 1) * 8) =
-            make_uint2(lo, hi);
+        uint2* slot = reinterpret_cast<uint2*>(stage + r * (C::kWTN * 2) + ((c ^ (r & 3)) * 16) +
+                                               (fc & 1) * 8);
+        if (GATED) {
+          float g[4] = {g4[0], g4[1], g4[2], g4[3]};
+          if (ep.gate != nullptr && !one_gate) {
+            const float* gr = ep.gate + ((mrow0 + r) / ep.gate_rows) * N + n;
+            g[0] = gr[0]; g[1] = gr[1]; g[2] = gr[2]; g[3] = gr[3];
+          }
+          float rv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (ep.residual != nullptr) {
+            const uint2 u = *slot;
+            rv[0] = bf16_to_f32(u.x & 0xFFFFu); rv[1] = bf16_to_f32(u.x >> 16);
+            rv[2] = bf16_to_f32(u.y & 0xFFFFu); rv[3] = bf16_to_f32(u.y >> 16);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = fmaf(g[q], v[q], rv[q]);
+        }
+        *slot = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     uint16_t* yb = reinterpret_cast<uint16_t*>(y) + (int64_t)(m0 + wm * C::kWTM) * N + n0 +
                    wn * C::kWTN;
 #pragma unroll

@@ -70,25 +70,6 @@ __device__ __forceinline__ float gated1(float v, const uint16_t* residual, const
   return fmaf(g, v, r);
 }
 
-// The same for 4 consecutive columns n..n+3 (n % 4 == 0, N % 4 == 0, so
-// the 4 residual values are one aligned 8-byte load).
-__device__ __forceinline__ void gated4(float v[4], const uint16_t* residual, const float* gate,
-                                       int gate_rows, int64_t m, int n, int N) {
-  float g[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-  float r[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (gate) {
-    const float* gr = gate + (m / gate_rows) * (int64_t)N + n;
-    g[0] = gr[0]; g[1] = gr[1]; g[2] = gr[2]; g[3] = gr[3];
-  }
-  if (residual) {
-    const uint2 u = *reinterpret_cast<const uint2*>(residual + m * (int64_t)N + n);
-    r[0] = bf16_to_f32(u.x & 0xFFFFu); r[1] = bf16_to_f32(u.x >> 16);
-    r[2] = bf16_to_f32(u.y & 0xFFFFu); r[3] = bf16_to_f32(u.y >> 16);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = fmaf(g[i], v[i], r[i]);
-}
-
 // Pack four int8 codes into one dword (byte i = code i).
 __device__ __forceinline__ uint32_t pack4_i8(int c0, int c1, int c2, int c3) {
   return (uint32_t)(c0 & 0xFF) | ((uint32_t)(c1 & 0xFF) << 8) |
