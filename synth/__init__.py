@@ -67,6 +67,9 @@ WORKLOADS = {
                  x_dist="student_t4"),
         Workload("thin_n_w8a8_2048x5120x48", 2048, 5120, 48, "w8", "bf16",
                  x_dist="student_t4"),
+        # adaLN modulation of a DiT block: the conditioning vector of each
+        # sample (batch 2) to the six shift/scale/gate vectors, 6 x 3072.
+        Workload("dit_modulation_w8a8_2x3072x18432", 2, 3072, 18432, "w8", "bf16"),
         # Small-batch GEMV with int4 weights.
         Workload("gemv_w4a8_m1_5120x13824", 1, 5120, 13824, "w4", "bf16"),
         Workload("gemv_w4a8_m4_5120x13824", 4, 5120, 13824, "w4", "bf16"),
