@@ -1,13 +1,15 @@
-"""CPU oracle of the INT8 quantized linear -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle of the INT8 quantized linear and the INT8 attention -- TEST
+INFRASTRUCTURE ONLY.
 
 A plain, slow, obviously correct numpy implementation of what the GPU path
 computes.  Only the tests, the smoke check and the benchmark's CPU-baseline
 leg may import it; the product path (the HIP library and its Python
 binding) never does, and shares no code with it.
 
-Every function pinned by the CPU test suite (see kq_oracle.py's header for
-which pin covers which function).
+Every function pinned by the CPU test suite (see the headers of
+kq_oracle.py and sage_oracle.py for which pin covers which function).
 """
+from . import sage_oracle as sage  # noqa: F401
 from .kq_oracle import (  # noqa: F401
     F32_MAX,
     quantize_rows_absmax,

@@ -1,0 +1,243 @@
+"""CPU pins of the INT8 attention oracle (oracle/sage_oracle.py).
+
+Each check ties the oracle to something other than itself: exact rational
+arithmetic, an integer grid on which quantization is exact (so the method
+must reproduce unquantized attention, computed here by torch's own
+scaled_dot_product_attention in float64), invariances of the method
+(a per-channel shift of the keys, token order), closed forms (identical
+keys give the mean of V) and a pure-Python loop implementation on tiny
+inputs.  A dropped smoothing step, a transposed operand, a wrong scale
+or a wrong block split fails at least one of them."""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+S = oracle.sage
+
+
+def _f16(a):
+    return np.asarray(a, dtype=np.float64).astype(np.float16)
+
+
+# ------------------------------------------------------------- the K mean
+def test_k_mean_matches_exact_rational_mean():
+    rng = np.random.default_rng(1)
+    for L in (1, 2, 3, 7, 100, 1000):
+        k = _f16(rng.standard_normal((L, 16)) * rng.choice([1e-3, 1.0, 300.0], size=(1, 16)))
+        got = S.k_mean_exact(k)
+        for d in range(16):
+            exact = sum(Fraction(float(x)) for x in k[:, d]) / L
+            want = np.float32(float(exact))  # float(Fraction) rounds once to fp64
+            # fp64 -> fp32 can round twice; both sides of the library take
+            # the same steps, and here the result is within one fp32 ulp of
+            # the exact mean and equal to its correctly rounded value
+            assert abs(float(got[d]) - float(exact)) <= float(np.spacing(np.float32(abs(want)))), (L, d)
+            assert got[d] == want, (L, d)
+
+
+def test_k_mean_is_order_independent_and_exact_for_representable_means():
+    rng = np.random.default_rng(2)
+    k = _f16(rng.standard_normal((777, 128)) * 50)
+    perm = rng.permutation(777)
+    assert np.array_equal(S.k_mean_exact(k).view(np.uint32), S.k_mean_exact(k[perm]).view(np.uint32))
+    c = _f16(rng.standard_normal((1, 128)))
+    assert np.array_equal(S.k_mean_exact(np.repeat(c, 33, axis=0)), c[0].astype(np.float32))
+    # extremes: the largest fp16 and the smallest subnormal
+    big = np.full((5, 2), 65504.0, np.float16)
+    big[:, 1] = np.float16(2.0 ** -24)
+    assert S.k_mean_exact(big).tolist() == [65504.0, np.float32(2.0 ** -24)]
+
+
+def test_k_mean_is_per_channel_over_tokens():
+    k = np.zeros((4, 128), np.float16)
+    k[:, 3] = [1, 2, 3, 6]        # channel 3 mean 3
+    k[2, :] = 8                    # token 2 adds 2 to every channel's mean
+    k[2, 3] = 3
+    m = S.k_mean_exact(k)
+    assert m[3] == 3.0 and m[0] == 2.0 and m[127] == 2.0
+
+
+# ------------------------------------------------------------- block quantizer
+@pytest.mark.parametrize("block", [1, 16, 64, 128, 1000])
+def test_block_scales_are_shared_and_hit_127(block):
+    rng = np.random.default_rng(3)
+    L = 300
+    x = (rng.standard_normal((L, 128)) * np.linspace(0.1, 5, L)[:, None]).astype(np.float32)
+    codes, sc = S.quantize_token_blocks(x, block)
+    for t0 in range(0, L, block):
+        t1 = min(L, t0 + block)
+        assert np.all(sc[t0:t1] == sc[t0])
+        amax = np.abs(x[t0:t1]).max()
+        assert sc[t0] == np.float32(amax / np.float32(127))
+        assert np.abs(codes[t0:t1]).max() == 127
+        # the error bound of the rule, block-wide
+        err = np.abs(x[t0:t1].astype(np.float64) - sc[t0] * codes[t0:t1])
+        assert err.max() <= sc[t0] * (0.5 + 2.0 ** -16)
+    if block < L:
+        assert sc[0] != sc[-1]
+
+
+def test_block_quantizer_matches_exact_rationals():
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((5, 128)) * 3).astype(np.float32)
+    codes, sc = S.quantize_token_blocks(x, 2)
+    for t0 in (0, 2, 4):
+        blk = x[t0:t0 + 2]
+        amax = max(abs(float(v)) for v in blk.ravel())
+        inv = np.float32(Fraction(127) / Fraction(amax))          # one IEEE division
+        for t in range(t0, min(5, t0 + 2)):
+            for d in range(128):
+                prod = np.float32(Fraction(float(x[t, d])) * Fraction(float(inv)))
+                want = int(np.clip(np.rint(prod), -127, 127))
+                assert codes[t, d] == want
+
+
+# ------------------------------------------------------------- the whole method
+def _grid_operands(Lq, Lk, q_block, k_block, seed):
+    """Integer-valued q and k whose quantization is exact: every q block and
+    every smoothed-k block holds a +-127 and only integers in [-127, 127],
+    so inv = 1, codes = values and scales = 1.  The keys are k0 + c: k0
+    has zero column means (rows come in +- pairs inside one block), c a
+    per-channel offset that the smoothing must remove."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(-100, 101, size=(Lq, 128)).astype(np.float64)
+    for t0 in range(0, Lq, q_block):
+        q[t0, t0 % 128] = 127
+    half = rng.integers(-100, 101, size=(Lk // 2, 128)).astype(np.float64)
+    for t0 in range(0, Lk, k_block):
+        half[t0 // 2, (t0 // 2) % 128] = 127
+    k0 = np.empty((Lk, 128))
+    k0[0::2], k0[1::2] = half, -half
+    c = rng.integers(-64, 65, size=(1, 128)).astype(np.float64)
+    return _f16(q), k0, _f16(k0 + c), c
+
+
+def _sdpa_fp64(q, k, v, scale):
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(np.asarray(q, np.float64))[None, None],
+        torch.from_numpy(np.asarray(k, np.float64))[None, None],
+        torch.from_numpy(np.asarray(v, np.float64))[None, None], scale=scale)
+    return out[0, 0].numpy()
+
+
+@pytest.mark.parametrize("q_block,k_block", [(1, 2), (64, 64), (128, 32)])
+def test_integer_grid_reproduces_unquantized_attention(q_block, k_block):
+    Lq, Lk = 200, 256
+    q, k0, k, c = _grid_operands(Lq, Lk, q_block, k_block, seed=5)
+    v = _f16(np.random.default_rng(6).standard_normal((Lk, 128)))
+    scale = 2.0 ** -13           # scores of order 1: a sensitive softmax
+    qc, sq, kc, sk, mean = S.prepare(q, k, q_block, k_block)
+    assert np.array_equal(mean, c[0].astype(np.float32))
+    assert np.array_equal(qc, q.astype(np.int8)) and np.all(sq == 1)
+    assert np.array_equal(kc, k0.astype(np.int8)) and np.all(sk == 1)
+    O, T = S.sage_attention_head(q, k, v, scale, q_block, k_block)
+    ref = _sdpa_fp64(q, k0, v, scale)
+    assert np.allclose(O, ref, rtol=0, atol=1e-12)
+    # softmax does not see the per-channel offset either
+    assert np.allclose(_sdpa_fp64(q, k, v, scale), ref, rtol=0, atol=1e-9)
+    assert np.all(T >= np.abs(O) - 1e-15)
+
+
+def test_per_channel_key_shift_changes_nothing():
+    """Keys on a 1/8 grid, Lk a power of two: the mean of k + c is mean(k)
+    + c exactly, so smoothing gives identical codes and identical output."""
+    rng = np.random.default_rng(7)
+    q = _f16(rng.standard_normal((50, 128)))
+    k = _f16(rng.integers(-256, 257, size=(64, 128)) / 8.0)
+    c = rng.integers(-16, 17, size=(1, 128))
+    v = _f16(rng.standard_normal((64, 128)))
+    a = S.sage_attention_head(q, k, v, 128 ** -0.5, 16, 16)[0]
+    b = S.sage_attention_head(q, _f16(k.astype(np.float64) + c), v, 128 ** -0.5, 16, 16)[0]
+    assert np.array_equal(a, b)
+
+
+def test_identical_keys_give_the_mean_of_v():
+    rng = np.random.default_rng(8)
+    q = _f16(rng.standard_normal((9, 128)))
+    k = np.repeat(_f16(rng.standard_normal((1, 128)) * 10), 40, axis=0)
+    v = _f16(rng.standard_normal((40, 128)))
+    qc, sq, kc, sk, _ = S.prepare(q, k, 1, 8)
+    assert not kc.any() and not sk.any()          # smoothed keys are all zero
+    O, _ = S.attention_from_codes(qc, sq, kc, sk, v, 128 ** -0.5)
+    assert np.allclose(O, np.repeat(v.astype(np.float64).mean(axis=0, keepdims=True), 9, 0),
+                       rtol=0, atol=1e-15)
+
+
+def test_token_order_of_keys_and_values_does_not_matter():
+    rng = np.random.default_rng(9)
+    q = _f16(rng.standard_normal((20, 128)))
+    k = _f16(rng.standard_normal((48, 128)) + 3)
+    v = _f16(rng.standard_normal((48, 128)))
+    a = S.sage_attention_head(q, k, v, 0.1, 4, 1)[0]       # per-token k scales
+    p = rng.permutation(48)
+    b = S.sage_attention_head(q, k[p], v[p], 0.1, 4, 1)[0]
+    assert np.allclose(a, b, rtol=0, atol=1e-13)
+
+
+def test_pure_python_loops_on_a_tiny_head():
+    rng = np.random.default_rng(10)
+    Lq, Lk = 3, 5
+    q = _f16(rng.standard_normal((Lq, 128)))
+    k = _f16(rng.standard_normal((Lk, 128)) + 1)
+    v = _f16(rng.standard_normal((Lk, 128)))
+    scale = 0.2
+    qc, sq, kc, sk, _ = S.prepare(q, k, 2, 3)
+    O, _ = S.attention_from_codes(qc, sq, kc, sk, v, scale)
+    for i in range(Lq):
+        s = []
+        for j in range(Lk):
+            dot = sum(int(qc[i, d]) * int(kc[j, d]) for d in range(128))
+            s.append(scale * float(sq[i]) * float(sk[j]) * dot)
+        mx = max(s)
+        e = [math.exp(x - mx) for x in s]
+        tot = math.fsum(e)
+        for d in range(128):
+            want = math.fsum(e[j] * float(v[j, d]) for j in range(Lk)) / tot
+            assert abs(O[i, d] - want) <= 1e-13 * (1 + abs(want))
+
+
+def test_score_error_bound_against_unquantized_smoothed_scores():
+    rng = np.random.default_rng(11)
+    q = _f16(rng.standard_normal((64, 128)))
+    k = _f16(rng.standard_normal((96, 128)) * 2 + 5)
+    scale = 128 ** -0.5
+    qc, sq, kc, sk, _ = S.prepare(q, k, 32, 32)
+    ks = S.smooth_k(k).astype(np.float64)
+    q64 = q.astype(np.float64)
+    got = S.scores_exact(qc, sq, kc, sk, scale)
+    want = scale * q64 @ ks.T
+    eq = (sq[:, None] * (0.5 + 2.0 ** -16)).astype(np.float64)     # per-element code error
+    ek = (sk[:, None] * (0.5 + 2.0 ** -16)).astype(np.float64)
+    khat = sk[:, None].astype(np.float64) * kc
+    bound = scale * (np.abs(q64) @ np.broadcast_to(ek, ks.shape).T
+                     + eq * np.abs(khat).sum(axis=1)[None, :])
+    assert np.all(np.abs(got - want) <= bound * (1 + 1e-12))
+
+
+def test_quantization_error_on_dit_like_inputs_is_small():
+    """The pages quote about 1% total error against fp32 attention for
+    their models; on these synthetic heads (keys with a large per-channel
+    offset, which the smoothing removes) it is reported, and held under
+    3%."""
+    rng = np.random.default_rng(12)
+    q = _f16(rng.standard_normal((256, 128)))
+    k = _f16(rng.standard_normal((256, 128)) + rng.standard_normal((1, 128)) * 4)
+    v = _f16(rng.standard_normal((256, 128)))
+    O, _ = S.sage_attention_head(q, k, v, 128 ** -0.5, 128, 64)
+    ref = S.attention_fp64(q, k, v, 128 ** -0.5)
+    rel = np.linalg.norm(O - ref) / np.linalg.norm(ref)
+    print(f"relative Frobenius error {rel:.4f}")
+    assert rel < 0.03
+
+
+def test_f16_helpers():
+    assert S.f16_ulp(np.float16(1.0)) == 2.0 ** -10
+    assert S.f16_ulp(np.float16(65504)) == 32.0
+    assert S.f16_ulp(np.float16(0)) == 2.0 ** -24
+    x = np.array([1 + 2.0 ** -11, 1 + 2.0 ** -11 + 2.0 ** -40])
+    assert S.round_f16(x).astype(np.float64).tolist() == [1.0, 1 + 2.0 ** -10]
