@@ -38,6 +38,7 @@ if ROOT not in sys.path:
 
 PEAK_INT8_TOPS = 5000.0   # MI355X dense INT8 MFMA, tera-ops/s
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, GB/s
+PEAK_FP16_TFLOPS = 2500.0  # MI355X dense FP16 MFMA
 ROTATE_BYTES = 512 << 20  # working set rotated per timed pass
 METRIC = "W8A8/W4A8 GEMM INT8 TOPS + % of INT8 MFMA peak; GEMV GB/s at M≤16"
 
@@ -137,6 +138,41 @@ class Prepared:
         else:
             kq.kq_w4a8_gemm(c["a"], c["sx"], c["gs"], c["wq"], c["sc"], c["gb"], c["b"],
                             out_dtype=self.out_dtype, out=c["y"])
+
+
+class PreparedAttention:
+    """Device-resident q/k/v, output and workspace of one attention
+    workload (its working set is far above the Infinity Cache, so one
+    copy)."""
+
+    def __init__(self, wl, seed=0):
+        import torch
+        import synth
+        import w8a8_gemm_dit_amd as kq
+
+        self.wl, self.kq = wl, kq
+        q, k, v = synth.attention_inputs(wl.B, wl.H, wl.Lq, wl.Lk, seed=seed)
+        self.q, self.k, self.v = (torch.from_numpy(t).cuda() for t in (q, k, v))
+        del q, k, v
+        self.out = torch.empty_like(self.q)
+        self.ws = kq.kq_sage_prepare(self.q, self.k, self.v, wl.q_block, wl.k_block)
+        torch.cuda.synchronize()
+
+    def step(self, i: int) -> None:
+        """The whole call: preparation + attention."""
+        self.kq.kq_sage_attention(self.q, self.k, self.v, q_block=self.wl.q_block,
+                                  k_block=self.wl.k_block, out=self.out, workspace=self.ws)
+
+    def attend(self, i: int) -> None:
+        """The attention kernel alone, on the prepared workspace."""
+        w = self.wl
+        self.kq.kq_sage_attend(self.ws, w.B, w.H, w.Lq, w.Lk, out=self.out)
+
+
+def attention_peak_tops() -> float:
+    """Dense MFMA bound of the INT8 attention: half its operations run at
+    the INT8 rate (QK^T), half at the FP16 rate (P.V)."""
+    return 1.0 / (0.5 / PEAK_INT8_TOPS + 0.5 / PEAK_FP16_TFLOPS)
 
 
 def graph_capture(fn, steps: int, warm_replays: int = 3):
@@ -335,6 +371,16 @@ def main() -> int:
             log(f"profiled {name}")
             del p
             torch.cuda.empty_cache()
+        for name, wl in synth.ATTN_WORKLOADS.items():
+            if args.workload and name != args.workload:
+                continue
+            p = PreparedAttention(wl)
+            for i in range(max(args.steps, 1)):
+                p.step(i)
+            torch.cuda.synchronize()
+            log(f"profiled {name}")
+            del p
+            torch.cuda.empty_cache()
         return 0
 
     wl = synth.WORKLOADS[synth.HEADLINE]
@@ -444,6 +490,27 @@ def main() -> int:
             }
             log(f"{name}: {t * 1e3:.2f} us/call ({extra[name]['tops']} TOPS, {gbs:.0f} GB/s)")
             del pw
+            torch.cuda.empty_cache()
+        peak_att = attention_peak_tops()
+        for name, w in synth.ATTN_WORKLOADS.items():
+            pa = PreparedAttention(w)
+            pa.step(0)
+            steps_a = max(5, args.steps // 20)
+            t = graph_time(pa.step, steps_a)
+            ta = graph_time(pa.attend, steps_a)
+            extra[name] = {
+                "ms_per_call": round(t, 5), "kernel_ms": round(ta, 5),
+                "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk,
+                "q_block": w.q_block, "k_block": w.k_block,
+                "tops": round(w.ops / (t * 1e-3) / 1e12, 2),
+                "kernel_tops": round(w.ops / (ta * 1e-3) / 1e12, 2),
+                "mfma_peak_tops": round(peak_att, 1),
+                "pct_mfma_peak": round(100 * w.ops / (ta * 1e-3) / 1e12 / peak_att, 2),
+            }
+            log(f"{name}: {t * 1e3:.1f} us/call, attention kernel {ta * 1e3:.1f} us "
+                f"({extra[name]['kernel_tops']} TOPS, {extra[name]['pct_mfma_peak']}% of "
+                f"{peak_att:.0f})")
+            del pa
             torch.cuda.empty_cache()
         result["extra"] = extra
 

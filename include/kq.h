@@ -26,6 +26,15 @@
  *            "Selector rules": affine weights, 2-D transposed [N,K] weight
  *            layout, K % 64 == 0, K/64 <= 1024, non-batched operands, group
  *            sizes 32/64/128 (this library: 64).
+ *   [sage]   "qlip-mlx" README, sage_attention bullet, "Key features" and
+ *            "Quick start": INT8 QK^T inside a flash-attention structure
+ *            with exact online softmax; quantization touches only QK^T,
+ *            with per-token / per-block scales; softmax and P.V stay in
+ *            floating point; head dim 128, mask-free; q/k/v [B, heads, L,
+ *            128] or tokens-first; scale 128^-0.5; fp16 output in the same
+ *            layout.  The method is SageAttention's (published by Zhang et
+ *            al.): K is smoothed by its mean over the tokens before the
+ *            quantization.
  *   [kquant] mlx-kquant pull request 89 commit list: routes must not round
  *            beyond one weight and one output rounding; errors other than a
  *            declined route raise; the route decision is one tested function;
@@ -257,6 +266,77 @@ kq_status kq_linear_gated(kq_wformat fmt, const void* x, int64_t M, int64_t K,
                           const void* residual, const float* gate,
                           int64_t gate_rows, void* y, kq_dtype y_dtype,
                           void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * INT8 attention ([sage]).
+ *
+ * For each batch b and head h, with q [Lq,128], k and v [Lk,128] fp16:
+ *   kmean = the mean of k over its Lk tokens, per channel: the exact sum
+ *           (fp16 values as integers in units of 2^-24) converted to fp64,
+ *           scaled by 2^-24, divided by Lk in fp64, rounded to fp32;
+ *   ks    = fp32(k - kmean);
+ *   qc, sq / kc, sk = int8 codes and per-token fp32 scales of q / ks, one
+ *           absmax scale per block of q_block / k_block consecutive tokens
+ *           (the linears' rule: inv = fp32(127/amax), codes =
+ *           clamp(rint(fp32(v*inv)), +-127), scale = fp32(amax/127), 0 for
+ *           an all-zero block);
+ *   S     = scale * sq[i] * sk[j] * (qc[i] . kc[j])   (exact int32 dot);
+ *   out   = softmax_j(S) v, in fp32 with P rounded to fp16 for the P.v
+ *           product, rounded to fp16.
+ * Codes, scales and kmean are bit-exact; out is within the rounding of P
+ * and of the output (see the tests for the bound).
+ *
+ * Tensors: q, out [B,H,Lq,128] and k, v [B,H,Lk,128] fp16, dense, in the
+ * layout given (KQ_LAYOUT_BHLD: heads-first, KQ_LAYOUT_BLHD: tokens-first
+ * [B,L,H,128]), 16-byte aligned device memory.  Requirements: D = 128;
+ * 1 <= q_block, k_block <= 128, powers of two; scale > 0 and finite;
+ * B*H <= 65535; Lq, Lk <= 2^22; Lk >= 1 when Lq >= 1 (B, H or Lq = 0
+ * enqueues nothing).  Inputs must be finite.
+ * ------------------------------------------------------------------------ */
+typedef enum kq_layout {
+    KQ_LAYOUT_BHLD = 0,
+    KQ_LAYOUT_BLHD = 1
+} kq_layout;
+
+/* Workspace of the attention: byte offsets of its regions and the total.
+ * After kq_sage_prepare (or kq_sage_attention) it holds, with BH = B*H,
+ * lq_pad / lk_pad = Lq / Lk rounded up to 128:
+ *   qc    int8  [BH][lq_pad][128]  query codes (rows past Lq zero)
+ *   sq    fp32  [BH][lq_pad]       per-token query scales (0 past Lq)
+ *   kc    int8  [BH][lk_pad][128]  smoothed key codes
+ *   sk    fp32  [BH][lk_pad]       per-token key scales
+ *   vt    fp16  [BH][lk_pad/64][128][64]  v transposed per 64-key block,
+ *                keys permuted within each 32-key half (slot 8g+i holds
+ *                key 4g+i for i < 4, key 16+4g+(i-4) for i >= 4), zero
+ *                past Lk
+ *   kmean fp32  [BH][128]          the key means
+ *   colsum int64 [BH][chunks][128] partial key sums (units of 2^-24) */
+typedef struct kq_sage_workspace {
+    int64_t lq_pad, lk_pad, chunks;
+    size_t qc, sq, kc, sk, vt, kmean, colsum, total;
+} kq_sage_workspace;
+
+kq_status kq_sage_workspace_layout(int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                                   kq_sage_workspace* out /* host */);
+
+/* The preparation pass alone: key means, codes and scales, transposed v,
+ * written into the workspace. */
+kq_status kq_sage_prepare(const void* q, const void* k, const void* v, int64_t B,
+                          int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                          kq_layout layout, int64_t q_block, int64_t k_block,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* The attention alone, on a workspace kq_sage_prepare filled for the same
+ * B, H, Lq, Lk. */
+kq_status kq_sage_attend(const void* ws, size_t ws_bytes, void* out, int64_t B,
+                         int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                         kq_layout layout, float scale, void* stream);
+
+/* Both: out = INT8 attention of q, k, v. */
+kq_status kq_sage_attention(const void* q, const void* k, const void* v, void* out,
+                            int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                            kq_layout layout, float scale, int64_t q_block,
+                            int64_t k_block, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,4 +1,5 @@
-"""Seeded synthetic inputs for the INT8 quantized linear.
+"""Seeded synthetic inputs for the INT8 quantized linear and the INT8
+attention.
 
 Shared by the CPU oracle's tests, the GPU parity tests and the benchmark.  It
 holds no step of the method: it only draws activations, fp32 weights and
@@ -147,3 +148,60 @@ def random_bf16(shape, seed: int, scale: float = 1.0, dist: str = "normal") -> n
 def random_f32(shape, seed: int, scale: float = 1.0) -> np.ndarray:
     rng = np.random.default_rng(seed)
     return rng.standard_normal(shape, dtype=np.float32) * np.float32(scale)
+
+
+# ------------------------------------------------------------------ attention
+# "qlip-mlx" README, "Quick start": the bare-tensor attention check runs 40
+# heads x 14040 tokens at head dim 128 (q/k/v [B, heads, L, 128]); DiT
+# attention is bidirectional.  The draws stand in for a DiT's q/k/v after
+# its q/k normalization: q and v ~ N(0, 1); k ~ N(0, 1) plus a per-(head,
+# channel) offset ~ N(0, key_bias^2) shared by all tokens, the channel bias
+# of DiT keys that the SageAttention smoothing removes.  Recipe:
+# SeedSequence(seed).spawn(4) -> streams for (q, k, key offsets, v), drawn
+# in fp32 [B, H, L, 128] and cast to fp16 (nearest even); tokens-first
+# layouts are the same draws transposed.
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    name: str
+    B: int
+    H: int
+    Lq: int
+    Lk: int
+    q_block: int = 128
+    k_block: int = 64
+
+    @property
+    def ops(self) -> int:
+        """Operations of the two products (QK^T in int8, P.V in fp16), a
+        multiply-add counted as two."""
+        return 4 * self.B * self.H * self.Lq * self.Lk * 128
+
+
+ATTN_WORKLOADS = {
+    w.name: w
+    for w in [
+        # The README's bare-tensor attention check: 40 heads x 14040 tokens.
+        AttnWorkload("sage_attn_40x14040", 1, 40, 14040, 14040),
+        # A 1024px DiT block: 24 heads x 4096 image tokens, batch 2.
+        AttnWorkload("sage_attn_dit1024_2x24x4096", 2, 24, 4096, 4096),
+    ]
+}
+
+ATTN_HEADLINE = "sage_attn_40x14040"
+
+
+def attention_inputs(B: int, H: int, Lq: int, Lk: int, seed: int = 0, layout: str = "bhld",
+                     key_bias: float = 3.0):
+    """fp16 (q, k, v) numpy arrays, [B, H, L, 128] for layout "bhld" or
+    [B, L, H, 128] for "blhd" (the same values)."""
+    rq, rk, rb, rv = [np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(4)]
+    q = rq.standard_normal((B, H, Lq, 128), dtype=np.float32).astype(np.float16)
+    k = rk.standard_normal((B, H, Lk, 128), dtype=np.float32)
+    k += rb.standard_normal((B, H, 1, 128), dtype=np.float32) * np.float32(key_bias)
+    k = k.astype(np.float16)
+    v = rv.standard_normal((B, H, Lk, 128), dtype=np.float32).astype(np.float16)
+    if layout == "blhd":
+        q, k, v = (np.ascontiguousarray(t.transpose(0, 2, 1, 3)) for t in (q, k, v))
+    elif layout != "bhld":
+        raise ValueError(layout)
+    return q, k, v

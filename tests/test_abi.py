@@ -24,7 +24,7 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     L = kq.lib()
     declared = _declared_functions()
-    assert len(declared) == 12, declared
+    assert len(declared) == 16, declared
     assert sorted(kq.exported_symbols) == declared
     for name in declared:
         assert hasattr(L, name), name
@@ -184,6 +184,51 @@ def test_gated_linear_validation_without_device():
     assert "group offsets" in kq.kq_last_error()
     assert _gated(wsb=100) == kq.KQ_ERR_WORKSPACE
     assert _gated(M=0) == kq.KQ_SUCCESS
+
+
+def test_sage_workspace_layout():
+    lay = kq.kq_sage_workspace_layout(2, 3, 300, 777)
+    assert lay["lq_pad"] == 384 and lay["lk_pad"] == 896 and lay["chunks"] == 4
+    order = ["qc", "sq", "kc", "sk", "vt", "kmean", "colsum"]
+    sizes = {"qc": 6 * 384 * 128, "sq": 6 * 384 * 4, "kc": 6 * 896 * 128, "sk": 6 * 896 * 4,
+             "vt": 6 * 896 * 128 * 2, "kmean": 6 * 128 * 4, "colsum": 6 * 4 * 128 * 8}
+    for a, b in zip(order, order[1:] + ["total"]):
+        assert lay[a] % 256 == 0 and lay[b] - lay[a] >= sizes[a] and lay[b] - lay[a] < sizes[a] + 256
+    with pytest.raises(ValueError):
+        kq.kq_sage_workspace_layout(1, 70000, 10, 10)
+
+
+def _sage(B=1, H=2, Lq=64, Lk=64, D=128, layout=0, scale=0.1, qb=128, kb=64, q=16, k=32, v=48,
+          out=64, ws=1 << 20, wsb=1 << 40):
+    return kq.lib().kq_sage_attention(P(q), P(k), P(v), P(out), B, H, Lq, Lk, D, layout, scale, qb, kb,
+                                      P(ws), wsb, None)
+
+
+def test_sage_validation_without_device():
+    L = kq.lib()
+    assert _sage(D=64) == kq.KQ_ERR_UNSUPPORTED and "only 128" in kq.kq_last_error()
+    assert _sage(layout=2) == kq.KQ_ERR_INVALID_VALUE and "unknown layout" in kq.kq_last_error()
+    assert _sage(qb=3) == kq.KQ_ERR_UNSUPPORTED and "powers of two" in kq.kq_last_error()
+    assert _sage(kb=256) == kq.KQ_ERR_UNSUPPORTED
+    assert _sage(scale=0.0) == kq.KQ_ERR_INVALID_VALUE and "scale" in kq.kq_last_error()
+    assert _sage(scale=-1.0) == kq.KQ_ERR_INVALID_VALUE
+    assert _sage(scale=float("inf")) == kq.KQ_ERR_INVALID_VALUE
+    assert _sage(Lk=0) == kq.KQ_ERR_INVALID_VALUE and "no keys" in kq.kq_last_error()
+    assert _sage(B=0) == kq.KQ_SUCCESS and _sage(Lq=0) == kq.KQ_SUCCESS and _sage(H=0) == kq.KQ_SUCCESS
+    assert _sage(Lq=-1) == kq.KQ_ERR_INVALID_VALUE
+    assert _sage(B=300, H=300) == kq.KQ_ERR_UNSUPPORTED
+    assert _sage(Lk=(1 << 22) + 1) == kq.KQ_ERR_UNSUPPORTED
+    assert _sage(q=0) == kq.KQ_ERR_INVALID_VALUE and "null" in kq.kq_last_error()
+    assert _sage(v=40) == kq.KQ_ERR_INVALID_VALUE and "aligned" in kq.kq_last_error()
+    assert _sage(out=72) == kq.KQ_ERR_INVALID_VALUE and "aligned" in kq.kq_last_error()
+    assert _sage(wsb=100) == kq.KQ_ERR_WORKSPACE and "smaller than" in kq.kq_last_error()
+    assert _sage(ws=0) == kq.KQ_ERR_WORKSPACE
+    st = L.kq_sage_attend(P(16), 1 << 40, P(32), 1, 2, 64, 64, 128, 0, 0.0, None)
+    assert st == kq.KQ_ERR_INVALID_VALUE and "[kq_sage_attend] scale" in kq.kq_last_error()
+    st = L.kq_sage_prepare(P(16), P(32), P(48), 1, 2, 64, 64, 128, 0, 5, 64, P(64), 1 << 40, None)
+    assert st == kq.KQ_ERR_UNSUPPORTED and "[kq_sage_prepare]" in kq.kq_last_error()
+    st = L.kq_sage_prepare(P(16), P(32), P(48), 1, 2, 64, 64, 128, 0, 8, 64, P(64), 10, None)
+    assert st == kq.KQ_ERR_WORKSPACE
 
 
 def test_quantizer_validation_without_device():

@@ -1,0 +1,210 @@
+"""GPU parity of the INT8 attention (kq_sage_*) against the oracle
+(oracle/sage_oracle.py) on identical seeded inputs, through the C ABI.
+
+Bars:
+  - key means, query/key codes and scales (padding included) and the
+    transposed values: bit-exact;
+  - the fp16 output against the oracle's exact softmax(S) V for the same
+    codes: |out - O| <= ulp16(O) + (2^-10 + Lk 2^-24) (T + |O|)
+    + 2^-25 U, where T = P|V| (P the normalized probabilities) and
+    U = sum_j |V_j| / l (l the softmax normalizer relative to the row max).
+    The terms: the output rounding (1 ulp); P rounded to fp16 for the
+    P.V product (relative 2^-11, doubled for the normalizer built from the
+    unrounded P); fp32 accumulation over Lk keys; probabilities below the
+    fp16 normal range (absolute error 2^-25 relative to the row max).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import w8a8_gemm_dit_amd as kq
+
+S = oracle.sage
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    print(f"[sage] device: {torch.cuda.get_device_name(0)}", flush=True)
+    assert kq.kq_is_available(), "libkq reports no gfx950 device"
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _region(ws, off, count, dtype):
+    nbytes = count * torch.empty((), dtype=dtype).element_size()
+    return ws[off:off + nbytes].view(dtype).cpu().numpy()
+
+
+def _heads(t, layout):
+    """[B, H, L, 128] view of a numpy array in either layout."""
+    return t if layout == "bhld" else t.transpose(0, 2, 1, 3)
+
+
+def _vt_expected(v_head, lk_pad):
+    """The transposed, key-permuted V of one head: [lk_pad/64][128][64]."""
+    L = v_head.shape[0]
+    vp = np.zeros((lk_pad, 128), np.float16)
+    vp[:L] = v_head
+    out = np.empty((lk_pad // 64, 128, 64), np.float16)
+    for blk in range(lk_pad // 64):
+        for half in range(2):
+            for g in range(4):
+                for i in range(8):
+                    key = 32 * half + (4 * g + i if i < 4 else 16 + 4 * g + i - 4)
+                    out[blk, :, 32 * half + 8 * g + i] = vp[blk * 64 + key]
+    return out
+
+
+def _check_out(o_gpu, qc, sq, kc, sk, v_head, scale, what):
+    O, T = S.attention_from_codes(qc, sq, kc, sk, v_head, scale)
+    Sc = S.scores_exact(qc, sq, kc, sk, scale)
+    l = np.exp(Sc - Sc.max(axis=1, keepdims=True)).sum(axis=1)
+    U = np.abs(v_head.astype(np.float64)).sum(axis=0)[None, :] / l[:, None]
+    Lk = v_head.shape[0]
+    g = o_gpu.astype(np.float64)
+    tol = S.f16_ulp(S.round_f16(O)) + (2.0 ** -10 + Lk * 2.0 ** -24) * (T + np.abs(O)) + 2.0 ** -25 * U
+    err = np.abs(g - O)
+    bad = ~(err <= tol)
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; first {i}: "
+                             f"gpu {g[i]!r} oracle {O[i]!r} tol {tol[i]!r}")
+    return float(np.max(err / np.maximum(tol, 1e-30)))
+
+
+SHAPES = [  # B, H, Lq, Lk
+    (1, 2, 300, 200), (2, 4, 300, 777), (1, 1, 5, 1), (1, 1, 129, 65), (1, 3, 128, 64),
+    (2, 1, 1000, 300), (1, 8, 64, 1031),
+]
+BLOCKS = [(128, 64), (1, 1), (16, 128), (64, 32)]
+
+
+@pytest.mark.parametrize("layout", ["bhld", "blhd"])
+@pytest.mark.parametrize("q_block,k_block", BLOCKS)
+@pytest.mark.parametrize("B,H,Lq,Lk", SHAPES)
+def test_sage_prepare_bit_exact_and_outputs(B, H, Lq, Lk, q_block, k_block, layout):
+    q, k, v = synth.attention_inputs(B, H, Lq, Lk, seed=B * 1000 + H * 100 + Lq + Lk, layout=layout)
+    scale = 128 ** -0.5
+    ws = kq.kq_sage_prepare(_dev(q), _dev(k), _dev(v), q_block, k_block, layout)
+    out = kq.kq_sage_attend(ws, B, H, Lq, Lk, scale, layout)
+    torch.cuda.synchronize()
+    lay = kq.kq_sage_workspace_layout(B, H, Lq, Lk)
+    BH, lqp, lkp = B * H, lay["lq_pad"], lay["lk_pad"]
+    qc = _region(ws, lay["qc"], BH * lqp * 128, torch.int8).reshape(BH, lqp, 128)
+    sq = _region(ws, lay["sq"], BH * lqp, torch.float32).reshape(BH, lqp)
+    kc = _region(ws, lay["kc"], BH * lkp * 128, torch.int8).reshape(BH, lkp, 128)
+    sk = _region(ws, lay["sk"], BH * lkp, torch.float32).reshape(BH, lkp)
+    vt = _region(ws, lay["vt"], BH * lkp * 128, torch.float16).reshape(BH, lkp // 64, 128, 64)
+    km = _region(ws, lay["kmean"], BH * 128, torch.float32).reshape(BH, 128)
+    o = _heads(out.cpu().numpy(), layout)
+    qh, kh, vh = (_heads(t, layout) for t in (q, k, v))
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            i = b * H + h
+            rqc, rsq, rkc, rsk, rkm = S.prepare(qh[b, h], kh[b, h], q_block, k_block)
+            assert np.array_equal(km[i].view(np.uint32), rkm.view(np.uint32)), (b, h)
+            assert np.array_equal(qc[i, :Lq], rqc) and not qc[i, Lq:].any(), (b, h)
+            assert np.array_equal(sq[i, :Lq].view(np.uint32), rsq.view(np.uint32)) and not sq[i, Lq:].any()
+            assert np.array_equal(kc[i, :Lk], rkc) and not kc[i, Lk:].any(), (b, h)
+            assert np.array_equal(sk[i, :Lk].view(np.uint32), rsk.view(np.uint32)) and not sk[i, Lk:].any()
+            assert np.array_equal(vt[i].view(np.uint16), _vt_expected(vh[b, h], lkp).view(np.uint16))
+            worst = max(worst, _check_out(o[b, h], rqc, rsq, rkc, rsk, vh[b, h], scale,
+                                          f"{B}x{H}x{Lq}x{Lk} blocks {q_block}/{k_block} {layout} b{b} h{h}"))
+    print(f"[sage] {B}x{H}x{Lq}x{Lk} worst err/tol {worst:.3f}", flush=True)
+
+
+def test_entry_points_and_layouts_agree_bitwise():
+    B, H, Lq, Lk = 2, 3, 257, 190
+    q, k, v = synth.attention_inputs(B, H, Lq, Lk, seed=5)
+    a = kq.kq_sage_attention(_dev(q), _dev(k), _dev(v))
+    a2 = kq.kq_sage_attention(_dev(q), _dev(k), _dev(v))          # determinism
+    ws = kq.kq_sage_prepare(_dev(q), _dev(k), _dev(v))
+    b = kq.kq_sage_attend(ws, B, H, Lq, Lk)
+    qt, kt, vt = (np.ascontiguousarray(t.transpose(0, 2, 1, 3)) for t in (q, k, v))
+    c = kq.kq_sage_attention(_dev(qt), _dev(kt), _dev(vt), layout="blhd")
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16).cpu()
+    assert torch.equal(bits(a), bits(a2))
+    assert torch.equal(bits(a), bits(b))
+    assert torch.equal(bits(a), bits(c.transpose(1, 2).contiguous()))
+
+
+def test_single_key_returns_v_exactly():
+    q, k, v = synth.attention_inputs(1, 2, 77, 1, seed=6)
+    out = kq.kq_sage_attention(_dev(q), _dev(k), _dev(v)).cpu().numpy()
+    assert np.array_equal(out.view(np.uint16), np.broadcast_to(v, out.shape).view(np.uint16))
+
+
+def test_identical_keys_and_zero_queries_average_v():
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((1, 1, 130, 128)).astype(np.float16)
+    q[0, 0, :64] = 0                                       # an all-zero query block: scale 0
+    k = np.repeat(rng.standard_normal((1, 1, 1, 128)).astype(np.float16), 300, axis=2)
+    k[0, 0, :, :] = k[0, 0, 0]
+    v = rng.standard_normal((1, 1, 300, 128)).astype(np.float16)
+    out = kq.kq_sage_attention(_dev(q), _dev(k), _dev(v), q_block=64).cpu().numpy()[0, 0]
+    mean = v[0, 0].astype(np.float64).mean(axis=0)
+    T = np.abs(v[0, 0].astype(np.float64)).mean(axis=0)
+    tol = S.f16_ulp(S.round_f16(mean)) + (2.0 ** -10 + 300 * 2.0 ** -24) * (T + np.abs(mean))
+    assert np.all(np.abs(out.astype(np.float64) - mean[None, :]) <= tol[None, :])
+
+
+@pytest.mark.parametrize("scale", [1e-3, 128 ** -0.5, 0.5])
+def test_scales_from_flat_to_peaked(scale):
+    B, H, Lq, Lk = 1, 2, 200, 333
+    q, k, v = synth.attention_inputs(B, H, Lq, Lk, seed=8)
+    out = kq.kq_sage_attention(_dev(q), _dev(k), _dev(v), scale=scale, q_block=32, k_block=16)
+    o = out.cpu().numpy()
+    for h in range(H):
+        qc, sq, kc, sk, _ = S.prepare(q[0, h], k[0, h], 32, 16)
+        _check_out(o[0, h], qc, sq, kc, sk, v[0, h], scale, f"scale {scale} h{h}")
+
+
+def test_error_against_unquantized_attention_is_about_a_percent():
+    """The pages quote ~1% total error against fp32 attention on their
+    models; reported here on the synthetic heads and held under 3%."""
+    B, H, L = 1, 4, 1024
+    q, k, v = synth.attention_inputs(B, H, L, L, seed=9)
+    o = kq.kq_sage_attention(_dev(q), _dev(k), _dev(v)).cpu().numpy().astype(np.float64)
+    num = den = 0.0
+    for h in range(H):
+        ref = S.attention_fp64(q[0, h], k[0, h], v[0, h], 128 ** -0.5)
+        num += np.sum((o[0, h] - ref) ** 2)
+        den += np.sum(ref ** 2)
+    rel = (num / den) ** 0.5
+    print(f"[sage] relative Frobenius error vs fp64 attention: {rel:.4f}", flush=True)
+    assert rel < 0.03
+
+
+@pytest.mark.parametrize("name", list(synth.ATTN_WORKLOADS))
+def test_workload_full_size_sampled(name):
+    """The benchmark's launch at full size: codes and scales of sampled
+    heads bit-exact, outputs of sampled query rows (the oracle computes
+    them one row at a time against all keys) within tolerance."""
+    w = synth.ATTN_WORKLOADS[name]
+    print(f"[sage] workload {name}", flush=True)
+    q, k, v = synth.attention_inputs(w.B, w.H, w.Lq, w.Lk, seed=0)
+    ws = kq.kq_sage_prepare(_dev(q), _dev(k), _dev(v), w.q_block, w.k_block)
+    out = kq.kq_sage_attend(ws, w.B, w.H, w.Lq, w.Lk)
+    torch.cuda.synchronize()
+    lay = kq.kq_sage_workspace_layout(w.B, w.H, w.Lq, w.Lk)
+    lqp, lkp = lay["lq_pad"], lay["lk_pad"]
+    rng = np.random.default_rng(0)
+    heads = sorted(set(rng.choice(w.B * w.H, size=2, replace=False).tolist()) | {w.B * w.H - 1})
+    o = out.cpu().numpy()
+    for i in heads:
+        b, h = divmod(i, w.H)
+        qc = ws[lay["qc"] + i * lqp * 128: lay["qc"] + (i * lqp + w.Lq) * 128].view(torch.int8).cpu().numpy()
+        kc = ws[lay["kc"] + i * lkp * 128: lay["kc"] + (i * lkp + w.Lk) * 128].view(torch.int8).cpu().numpy()
+        sq = ws[lay["sq"] + 4 * i * lqp: lay["sq"] + 4 * (i * lqp + w.Lq)].view(torch.float32).cpu().numpy()
+        sk = ws[lay["sk"] + 4 * i * lkp: lay["sk"] + 4 * (i * lkp + w.Lk)].view(torch.float32).cpu().numpy()
+        rqc, rsq, rkc, rsk, _ = S.prepare(q[b, h], k[b, h], w.q_block, w.k_block)
+        assert np.array_equal(qc.reshape(w.Lq, 128), rqc) and np.array_equal(sq.view(np.uint32), rsq.view(np.uint32))
+        assert np.array_equal(kc.reshape(w.Lk, 128), rkc) and np.array_equal(sk.view(np.uint32), rsk.view(np.uint32))
+        rows = np.unique(np.concatenate([rng.choice(w.Lq, size=14, replace=False), [0, w.Lq - 1]]))
+        _check_out(o[b, h, rows], rqc[rows], rsq[rows], rkc, rsk, v[b, h], 128 ** -0.5, f"{name} head {i}")

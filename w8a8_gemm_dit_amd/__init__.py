@@ -1,5 +1,5 @@
 """w8a8_gemm_dit_amd -- Python binding of libkq, the MI355X INT8 quantized
-linear (W8A8 / W4A8 / small-M GEMV).
+linear (W8A8 / W4A8 / small-M GEMV) and INT8 attention.
 
 Argument marshalling only: every step of the computation runs in libkq's HIP
 kernels.  The functions carry the C entry points' names, take torch tensors
@@ -22,6 +22,8 @@ __all__ = [
     "kq_is_available", "kq_last_error", "kq_workspace_bytes", "kq_route",
     "kq_quantize_weights", "kq_quantize_act", "kq_w8a8_linear", "kq_w4a8_linear",
     "kq_gemv_small_m", "kq_w8a8_gemm", "kq_w4a8_gemm", "kq_linear_gated", "KqError",
+    "KQ_LAYOUT_BHLD", "KQ_LAYOUT_BLHD", "kq_sage_workspace_layout", "kq_sage_prepare",
+    "kq_sage_attend", "kq_sage_attention",
 ]
 
 KQ_SUCCESS, KQ_ERR_INVALID_VALUE, KQ_ERR_UNSUPPORTED = 0, 1, 2
@@ -32,6 +34,7 @@ KQ_ROUTE_GEMM, KQ_ROUTE_GEMV = 0, 1
 KQ_MAX_K = 65536
 KQ_GEMV_MAX_M = 16
 KQ_GEMV_MAX_K = 16384
+KQ_LAYOUT_BHLD, KQ_LAYOUT_BLHD = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkq.so")
@@ -41,7 +44,8 @@ exported_symbols = (
     "kq_is_available", "kq_last_error", "kq_workspace_bytes", "kq_route",
     "kq_quantize_weights", "kq_quantize_act", "kq_w8a8_linear",
     "kq_w4a8_linear", "kq_gemv_small_m", "kq_w8a8_gemm", "kq_w4a8_gemm",
-    "kq_linear_gated",
+    "kq_linear_gated", "kq_sage_workspace_layout", "kq_sage_prepare", "kq_sage_attend",
+    "kq_sage_attention",
 )
 
 
@@ -53,6 +57,13 @@ class RouteInfo(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("tile_m", ctypes.c_int32),
                 ("tile_n", ctypes.c_int32), ("threads", ctypes.c_int32),
                 ("grid", ctypes.c_int64)]
+
+
+class SageWorkspace(ctypes.Structure):
+    _fields_ = [("lq_pad", ctypes.c_int64), ("lk_pad", ctypes.c_int64), ("chunks", ctypes.c_int64),
+                ("qc", ctypes.c_size_t), ("sq", ctypes.c_size_t), ("kc", ctypes.c_size_t),
+                ("sk", ctypes.c_size_t), ("vt", ctypes.c_size_t), ("kmean", ctypes.c_size_t),
+                ("colsum", ctypes.c_size_t), ("total", ctypes.c_size_t)]
 
 
 def lib_path() -> str:
@@ -92,6 +103,15 @@ def lib() -> ctypes.CDLL:
     L.kq_w4a8_gemm.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp]
     L.kq_gemv_small_m.restype = i32
     L.kq_gemv_small_m.argtypes = [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+    L.kq_sage_workspace_layout.restype = i32
+    L.kq_sage_workspace_layout.argtypes = [i64, i64, i64, i64, ctypes.POINTER(SageWorkspace)]
+    L.kq_sage_prepare.restype = i32
+    L.kq_sage_prepare.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i32, i64, i64, vp, sz, vp]
+    L.kq_sage_attend.restype = i32
+    L.kq_sage_attend.argtypes = [vp, sz, vp, i64, i64, i64, i64, i64, i32, ctypes.c_float, vp]
+    L.kq_sage_attention.restype = i32
+    L.kq_sage_attention.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, ctypes.c_float,
+                                    i64, i64, vp, sz, vp]
     L.kq_linear_gated.restype = i32
     L.kq_linear_gated.argtypes = [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, i64, vp, i32,
                                   vp, sz, vp]
@@ -336,4 +356,77 @@ def kq_w4a8_gemm(a, sx, gsum, wq4, gscale, gbias, bias=None, out_dtype=torch.bfl
     y = _prep_out(out, _out_shape(M, N, K, out_dtype, True), out_dtype, a.device)
     _check(lib().kq_w4a8_gemm(_ptr(a), _ptr(sx), _ptr(gsum), M, K, N, _ptr(wq4), _ptr(gscale),
                               _ptr(gbias), _ptr(bias), _ptr(y), _OUT[out_dtype], _stream()))
+    return y
+
+
+# ---------------------------------------------------------------- attention
+_LAYOUTS = {"bhld": KQ_LAYOUT_BHLD, "blhd": KQ_LAYOUT_BLHD}
+
+
+def kq_sage_workspace_layout(B: int, H: int, Lq: int, Lk: int) -> dict:
+    """Byte offsets of the attention workspace's regions and its total size."""
+    out = SageWorkspace()
+    _check(lib().kq_sage_workspace_layout(B, H, Lq, Lk, ctypes.byref(out)))
+    return {name: getattr(out, name) for name, _ in SageWorkspace._fields_}
+
+
+def _sage_dims(q, k, v, layout):
+    if layout not in _LAYOUTS:
+        raise ValueError(f"layout must be 'bhld' or 'blhd', got {layout!r}")
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, torch.float16, 4)
+    if layout == "bhld":
+        B, H, Lq, D = q.shape
+        Lk = k.shape[2]
+        kshape = (B, H, Lk, D)
+    else:
+        B, Lq, H, D = q.shape
+        Lk = k.shape[1]
+        kshape = (B, Lk, H, D)
+    if tuple(k.shape) != kshape or tuple(v.shape) != kshape:
+        raise ValueError("[kq_sage_attention] q, k and v shapes disagree")
+    return B, H, Lq, Lk, D
+
+
+def _sage_ws(workspace, B, H, Lq, Lk, dev):
+    need = kq_sage_workspace_layout(B, H, Lq, Lk)["total"]
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def kq_sage_prepare(q, k, v, q_block=128, k_block=64, layout="bhld", workspace=None):
+    """The preparation pass: returns the workspace holding the key means,
+    the query/key codes and scales and the transposed values."""
+    B, H, Lq, Lk, D = _sage_dims(q, k, v, layout)
+    ws, wsb = _sage_ws(workspace, B, H, Lq, Lk, q.device)
+    _check(lib().kq_sage_prepare(_ptr(q), _ptr(k), _ptr(v), B, H, Lq, Lk, D, _LAYOUTS[layout],
+                                 q_block, k_block, _ptr(ws), wsb, _stream()))
+    return ws
+
+
+def kq_sage_attend(workspace, B, H, Lq, Lk, scale=None, layout="bhld", out=None, device=None):
+    """The attention on a prepared workspace; returns out (fp16)."""
+    if layout not in _LAYOUTS:
+        raise ValueError(f"layout must be 'bhld' or 'blhd', got {layout!r}")
+    shape = (B, H, Lq, 128) if layout == "bhld" else (B, Lq, H, 128)
+    y = _prep_out(out, shape, torch.float16, device or workspace.device)
+    scale = 128 ** -0.5 if scale is None else float(scale)
+    _check(lib().kq_sage_attend(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _ptr(y), B, H, Lq, Lk, 128, _LAYOUTS[layout], scale, _stream()))
+    return y
+
+
+def kq_sage_attention(q, k, v, scale=None, q_block=128, k_block=64, layout="bhld", out=None,
+                      workspace=None):
+    """INT8 attention: softmax(scale * dequant(Qc) dequant(Kc)^T) V with K
+    smoothed by its token mean, fp16 in and out.  layout 'bhld' takes
+    [B, H, L, 128] tensors, 'blhd' [B, L, H, 128]."""
+    B, H, Lq, Lk, D = _sage_dims(q, k, v, layout)
+    y = _prep_out(out, tuple(q.shape), torch.float16, q.device)
+    ws, wsb = _sage_ws(workspace, B, H, Lq, Lk, q.device)
+    scale = D ** -0.5 if scale is None else float(scale)
+    _check(lib().kq_sage_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(y), B, H, Lq, Lk, D,
+                                   _LAYOUTS[layout], scale, q_block, k_block, _ptr(ws), wsb,
+                                   _stream()))
     return y

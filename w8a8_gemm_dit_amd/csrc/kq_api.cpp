@@ -23,6 +23,7 @@
 #include "kq.h"
 #include "kq_launch.hpp"
 #include "kq_route.hpp"
+#include "sage.hpp"
 
 namespace {
 
@@ -185,6 +186,101 @@ kq_status run_gemm(const char* op, kq_wformat fmt, const int8_t* a, const float*
   if (st != KQ_SUCCESS) return st;
   return launch_main(op, force, fmt, a, sx, gsum, M, K, N, wq, scale, gbias, bias, y, y_dtype,
                      reinterpret_cast<hipStream_t>(stream), nullptr);
+}
+
+// ------------------------------------------------------------ attention
+kq::SageStrides sage_strides(kq_layout layout, int64_t H, int64_t L) {
+  if (layout == KQ_LAYOUT_BLHD) return kq::SageStrides{L * H * kq::kSageD, kq::kSageD, H * kq::kSageD};
+  return kq::SageStrides{H * L * kq::kSageD, L * kq::kSageD, kq::kSageD};
+}
+
+bool pow2_block(int64_t b) { return b >= 1 && b <= 128 && (b & (b - 1)) == 0; }
+
+// Shape checks shared by the attention entry points; *empty is set when
+// there is nothing to do.
+kq_status check_sage_shape(const char* op, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                           int64_t D, kq_layout layout, bool* empty) {
+  *empty = false;
+  if (B < 0 || H < 0 || Lq < 0 || Lk < 0) return fail(KQ_ERR_INVALID_VALUE, "[%s] negative size", op);
+  if (layout != KQ_LAYOUT_BHLD && layout != KQ_LAYOUT_BLHD)
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] unknown layout %d", op, (int)layout);
+  if (D != kq::kSageD)
+    return fail(KQ_ERR_UNSUPPORTED, "[%s] head dim %lld: only 128 is supported", op, (long long)D);
+  if (B * H > 65535)
+    return fail(KQ_ERR_UNSUPPORTED, "[%s] B*H=%lld exceeds 65535", op, (long long)(B * H));
+  if (Lq > (1 << 22) || Lk > (1 << 22))
+    return fail(KQ_ERR_UNSUPPORTED, "[%s] sequence lengths are limited to 2^22", op);
+  if (B == 0 || H == 0 || Lq == 0) {
+    *empty = true;
+    return KQ_SUCCESS;
+  }
+  if (Lk == 0) return fail(KQ_ERR_INVALID_VALUE, "[%s] no keys (Lk = 0) for %lld queries", op, (long long)Lq);
+  return KQ_SUCCESS;
+}
+
+kq_status check_sage_ws(const char* op, const void* ws, size_t ws_bytes, const kq::SageLayout& L) {
+  if (!ws || ws_bytes < L.total)
+    return fail(KQ_ERR_WORKSPACE, "[%s] workspace of %zu bytes is smaller than the %zu required", op,
+                ws_bytes, L.total);
+  if (!aligned16(ws)) return fail(KQ_ERR_INVALID_VALUE, "[%s] workspace must be 16-byte aligned", op);
+  return KQ_SUCCESS;
+}
+
+kq_status sage_prepare_impl(const char* op, const void* q, const void* k, const void* v, int64_t B,
+                            int64_t H, int64_t Lq, int64_t Lk, int64_t D, kq_layout layout,
+                            int64_t q_block, int64_t k_block, void* ws, size_t ws_bytes,
+                            void* stream, bool* empty) {
+  kq_status st = check_sage_shape(op, B, H, Lq, Lk, D, layout, empty);
+  if (st != KQ_SUCCESS || *empty) return st;
+  if (!pow2_block(q_block) || !pow2_block(k_block))
+    return fail(KQ_ERR_UNSUPPORTED, "[%s] q_block=%lld, k_block=%lld: blocks are powers of two in [1, 128]",
+                op, (long long)q_block, (long long)k_block);
+  if (!q || !k || !v) return fail(KQ_ERR_INVALID_VALUE, "[%s] null tensor pointer", op);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] q, k and v must be 16-byte aligned", op);
+  const kq::SageLayout L = kq::sage_layout(B, H, Lq, Lk);
+  st = check_sage_ws(op, ws, ws_bytes, L);
+  if (st != KQ_SUCCESS) return st;
+  st = check_device(op);
+  if (st != KQ_SUCCESS) return st;
+  const char* name = kq::launch_sage_prepare(
+      reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k),
+      reinterpret_cast<const uint16_t*>(v), sage_strides(layout, H, Lq), sage_strides(layout, H, Lk),
+      sage_strides(layout, H, Lk), B, H, Lq, Lk, (int)q_block, (int)k_block,
+      reinterpret_cast<char*>(ws), L, reinterpret_cast<hipStream_t>(stream));
+  st = check_launch(op);
+  if (st == KQ_SUCCESS && env_log())
+    fprintf(stderr, "[kq] %s B=%lld H=%lld Lq=%lld Lk=%lld q_block=%lld k_block=%lld kernels=%s\n", op,
+            (long long)B, (long long)H, (long long)Lq, (long long)Lk, (long long)q_block,
+            (long long)k_block, name);
+  return st;
+}
+
+kq_status sage_attend_impl(const char* op, const void* ws, size_t ws_bytes, void* out, int64_t B,
+                           int64_t H, int64_t Lq, int64_t Lk, int64_t D, kq_layout layout,
+                           float scale, void* stream) {
+  bool empty = false;
+  kq_status st = check_sage_shape(op, B, H, Lq, Lk, D, layout, &empty);
+  if (st != KQ_SUCCESS || empty) return st;
+  if (!(scale > 0.0f) || !(scale <= 3.402823466e38f))
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] scale must be positive and finite", op);
+  if (!out) return fail(KQ_ERR_INVALID_VALUE, "[%s] null output pointer", op);
+  if (!aligned16(out)) return fail(KQ_ERR_INVALID_VALUE, "[%s] out must be 16-byte aligned", op);
+  const kq::SageLayout L = kq::sage_layout(B, H, Lq, Lk);
+  st = check_sage_ws(op, ws, ws_bytes, L);
+  if (st != KQ_SUCCESS) return st;
+  st = check_device(op);
+  if (st != KQ_SUCCESS) return st;
+  const char* name = kq::launch_sage_attend(reinterpret_cast<const char*>(ws), L,
+                                            reinterpret_cast<uint16_t*>(out),
+                                            sage_strides(layout, H, Lq), B, H, Lq, Lk, scale,
+                                            reinterpret_cast<hipStream_t>(stream));
+  st = check_launch(op);
+  if (st == KQ_SUCCESS && env_log())
+    fprintf(stderr, "[kq] %s B=%lld H=%lld Lq=%lld Lk=%lld kernel=%s grid=%lld\n", op, (long long)B,
+            (long long)H, (long long)Lq, (long long)Lk, name,
+            (long long)(L.BH * (L.Lqp / kq::kSageQTile)));
+  return st;
 }
 
 }  // namespace
@@ -359,6 +455,62 @@ kq_status kq_linear_gated(kq_wformat fmt, const void* x, int64_t M, int64_t K, i
   ep.gate_rows = (int)gate_rows;
   return run_linear(op, env_force_route(), fmt, x, M, K, N, wq, scale, gbias, bias, y, y_dtype,
                     ws, ws_bytes, stream, ep);
+}
+
+kq_status kq_sage_workspace_layout(int64_t B, int64_t H, int64_t Lq, int64_t Lk,
+                                   kq_sage_workspace* out) {
+  const char* op = "kq_sage_workspace_layout";
+  if (!out) return fail(KQ_ERR_INVALID_VALUE, "[%s] null output", op);
+  if (B < 0 || H < 0 || Lq < 0 || Lk < 0) return fail(KQ_ERR_INVALID_VALUE, "[%s] negative size", op);
+  if (B * H > 65535 || Lq > (1 << 22) || Lk > (1 << 22))
+    return fail(KQ_ERR_UNSUPPORTED, "[%s] shape outside the supported envelope", op);
+  const kq::SageLayout L = kq::sage_layout(B, H, Lq, Lk);
+  out->lq_pad = L.Lqp;
+  out->lk_pad = L.Lkp;
+  out->chunks = L.nchunk;
+  out->qc = L.qc;
+  out->sq = L.sq;
+  out->kc = L.kc;
+  out->sk = L.sk;
+  out->vt = L.vt;
+  out->kmean = L.kmean;
+  out->colsum = L.colsum;
+  out->total = L.total;
+  return KQ_SUCCESS;
+}
+
+kq_status kq_sage_prepare(const void* q, const void* k, const void* v, int64_t B, int64_t H,
+                          int64_t Lq, int64_t Lk, int64_t D, kq_layout layout, int64_t q_block,
+                          int64_t k_block, void* ws, size_t ws_bytes, void* stream) {
+  bool empty = false;
+  return sage_prepare_impl("kq_sage_prepare", q, k, v, B, H, Lq, Lk, D, layout, q_block, k_block,
+                           ws, ws_bytes, stream, &empty);
+}
+
+kq_status kq_sage_attend(const void* ws, size_t ws_bytes, void* out, int64_t B, int64_t H,
+                         int64_t Lq, int64_t Lk, int64_t D, kq_layout layout, float scale,
+                         void* stream) {
+  return sage_attend_impl("kq_sage_attend", ws, ws_bytes, out, B, H, Lq, Lk, D, layout, scale,
+                          stream);
+}
+
+kq_status kq_sage_attention(const void* q, const void* k, const void* v, void* out, int64_t B,
+                            int64_t H, int64_t Lq, int64_t Lk, int64_t D, kq_layout layout,
+                            float scale, int64_t q_block, int64_t k_block, void* ws,
+                            size_t ws_bytes, void* stream) {
+  const char* op = "kq_sage_attention";
+  // validate everything before enqueueing anything
+  bool empty = false;
+  kq_status st = check_sage_shape(op, B, H, Lq, Lk, D, layout, &empty);
+  if (st != KQ_SUCCESS || empty) return st;
+  if (!(scale > 0.0f) || !(scale <= 3.402823466e38f))
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] scale must be positive and finite", op);
+  if (!out) return fail(KQ_ERR_INVALID_VALUE, "[%s] null output pointer", op);
+  if (!aligned16(out)) return fail(KQ_ERR_INVALID_VALUE, "[%s] out must be 16-byte aligned", op);
+  st = sage_prepare_impl(op, q, k, v, B, H, Lq, Lk, D, layout, q_block, k_block, ws, ws_bytes,
+                         stream, &empty);
+  if (st != KQ_SUCCESS) return st;
+  return sage_attend_impl(op, ws, ws_bytes, out, B, H, Lq, Lk, D, layout, scale, stream);
 }
 
 }  // extern "C"
