@@ -166,7 +166,7 @@ class PreparedAttention:
     def attend(self, i: int) -> None:
         """The attention kernel alone, on the prepared workspace."""
         w = self.wl
-        self.kq.kq_sage_attend(self.ws, w.B, w.H, w.Lq, w.Lk, out=self.out)
+        self.kq.kq_sage_attend(self.ws, w.B, w.H, w.Lq, w.Lk, out=self.out, k_block=w.k_block)
 
 
 def attention_peak_tops() -> float:

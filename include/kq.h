@@ -327,10 +327,13 @@ kq_status kq_sage_prepare(const void* q, const void* k, const void* v, int64_t B
                           void* ws, size_t ws_bytes, void* stream);
 
 /* The attention alone, on a workspace kq_sage_prepare filled for the same
- * B, H, Lq, Lk. */
+ * B, H, Lq, Lk and k_block (k_block >= 64 lets every 64-key step use one
+ * key scale; a k_block other than the one the workspace was prepared with
+ * gives wrong results). */
 kq_status kq_sage_attend(const void* ws, size_t ws_bytes, void* out, int64_t B,
                          int64_t H, int64_t Lq, int64_t Lk, int64_t D,
-                         kq_layout layout, float scale, void* stream);
+                         kq_layout layout, float scale, int64_t k_block,
+                         void* stream);
 
 /* Both: out = INT8 attention of q, k, v. */
 kq_status kq_sage_attention(const void* q, const void* k, const void* v, void* out,

@@ -223,8 +223,10 @@ def test_sage_validation_without_device():
     assert _sage(out=72) == kq.KQ_ERR_INVALID_VALUE and "aligned" in kq.kq_last_error()
     assert _sage(wsb=100) == kq.KQ_ERR_WORKSPACE and "smaller than" in kq.kq_last_error()
     assert _sage(ws=0) == kq.KQ_ERR_WORKSPACE
-    st = L.kq_sage_attend(P(16), 1 << 40, P(32), 1, 2, 64, 64, 128, 0, 0.0, None)
+    st = L.kq_sage_attend(P(16), 1 << 40, P(32), 1, 2, 64, 64, 128, 0, 0.0, 64, None)
     assert st == kq.KQ_ERR_INVALID_VALUE and "[kq_sage_attend] scale" in kq.kq_last_error()
+    st = L.kq_sage_attend(P(16), 1 << 40, P(32), 1, 2, 64, 64, 128, 0, 0.1, 96, None)
+    assert st == kq.KQ_ERR_UNSUPPORTED and "k_block=96" in kq.kq_last_error()
     st = L.kq_sage_prepare(P(16), P(32), P(48), 1, 2, 64, 64, 128, 0, 5, 64, P(64), 1 << 40, None)
     assert st == kq.KQ_ERR_UNSUPPORTED and "[kq_sage_prepare]" in kq.kq_last_error()
     st = L.kq_sage_prepare(P(16), P(32), P(48), 1, 2, 64, 64, 128, 0, 8, 64, P(64), 10, None)

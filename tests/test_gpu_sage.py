@@ -90,7 +90,7 @@ def test_sage_prepare_bit_exact_and_outputs(B, H, Lq, Lk, q_block, k_block, layo
     q, k, v = synth.attention_inputs(B, H, Lq, Lk, seed=B * 1000 + H * 100 + Lq + Lk, layout=layout)
     scale = 128 ** -0.5
     ws = kq.kq_sage_prepare(_dev(q), _dev(k), _dev(v), q_block, k_block, layout)
-    out = kq.kq_sage_attend(ws, B, H, Lq, Lk, scale, layout)
+    out = kq.kq_sage_attend(ws, B, H, Lq, Lk, scale, layout, k_block=k_block)
     torch.cuda.synchronize()
     lay = kq.kq_sage_workspace_layout(B, H, Lq, Lk)
     BH, lqp, lkp = B * H, lay["lq_pad"], lay["lk_pad"]
@@ -190,7 +190,7 @@ def test_workload_full_size_sampled(name):
     print(f"[sage] workload {name}", flush=True)
     q, k, v = synth.attention_inputs(w.B, w.H, w.Lq, w.Lk, seed=0)
     ws = kq.kq_sage_prepare(_dev(q), _dev(k), _dev(v), w.q_block, w.k_block)
-    out = kq.kq_sage_attend(ws, w.B, w.H, w.Lq, w.Lk)
+    out = kq.kq_sage_attend(ws, w.B, w.H, w.Lq, w.Lk, k_block=w.k_block)
     torch.cuda.synchronize()
     lay = kq.kq_sage_workspace_layout(w.B, w.H, w.Lq, w.Lk)
     lqp, lkp = lay["lq_pad"], lay["lk_pad"]

@@ -108,7 +108,8 @@ def lib() -> ctypes.CDLL:
     L.kq_sage_prepare.restype = i32
     L.kq_sage_prepare.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i32, i64, i64, vp, sz, vp]
     L.kq_sage_attend.restype = i32
-    L.kq_sage_attend.argtypes = [vp, sz, vp, i64, i64, i64, i64, i64, i32, ctypes.c_float, vp]
+    L.kq_sage_attend.argtypes = [vp, sz, vp, i64, i64, i64, i64, i64, i32, ctypes.c_float, i64,
+                                 vp]
     L.kq_sage_attention.restype = i32
     L.kq_sage_attention.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, ctypes.c_float,
                                     i64, i64, vp, sz, vp]
@@ -405,15 +406,18 @@ def kq_sage_prepare(q, k, v, q_block=128, k_block=64, layout="bhld", workspace=N
     return ws
 
 
-def kq_sage_attend(workspace, B, H, Lq, Lk, scale=None, layout="bhld", out=None, device=None):
-    """The attention on a prepared workspace; returns out (fp16)."""
+def kq_sage_attend(workspace, B, H, Lq, Lk, scale=None, layout="bhld", out=None, device=None,
+                   k_block=64):
+    """The attention on a workspace kq_sage_prepare filled (with the same
+    shape and k_block); returns out (fp16)."""
     if layout not in _LAYOUTS:
         raise ValueError(f"layout must be 'bhld' or 'blhd', got {layout!r}")
     shape = (B, H, Lq, 128) if layout == "bhld" else (B, Lq, H, 128)
     y = _prep_out(out, shape, torch.float16, device or workspace.device)
     scale = 128 ** -0.5 if scale is None else float(scale)
     _check(lib().kq_sage_attend(_ptr(workspace), workspace.numel() * workspace.element_size(),
-                                _ptr(y), B, H, Lq, Lk, 128, _LAYOUTS[layout], scale, _stream()))
+                                _ptr(y), B, H, Lq, Lk, 128, _LAYOUTS[layout], scale, k_block,
+                                _stream()))
     return y
 
 

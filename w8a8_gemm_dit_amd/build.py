@@ -34,6 +34,14 @@ DEVICE = [
 ]
 
 
+# Per-file device flags.  The attention kernel rescales its output
+# accumulators with VALU instructions, which cannot read AGPRs: its MFMA
+# results stay in VGPRs (otherwise every rescale copies them out and back).
+EXTRA = {
+    "sage_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith((".hip", ".cpp")))
@@ -42,7 +50,7 @@ def sources():
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     if src.endswith(".hip"):
-        cmd = [HIPCC, *COMMON, *DEVICE, "-c", src, "-o", obj]
+        cmd = [HIPCC, *COMMON, *DEVICE, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     else:  # host-only C++ (C ABI, routing)
         cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
     if verbose:

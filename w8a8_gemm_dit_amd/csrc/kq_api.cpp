@@ -258,15 +258,19 @@ kq_status sage_prepare_impl(const char* op, const void* q, const void* k, const 
 
 kq_status sage_attend_impl(const char* op, const void* ws, size_t ws_bytes, void* out, int64_t B,
                            int64_t H, int64_t Lq, int64_t Lk, int64_t D, kq_layout layout,
-                           float scale, void* stream) {
+                           float scale, int64_t k_block, void* stream) {
   bool empty = false;
   kq_status st = check_sage_shape(op, B, H, Lq, Lk, D, layout, &empty);
   if (st != KQ_SUCCESS || empty) return st;
   if (!(scale > 0.0f) || !(scale <= 3.402823466e38f))
     return fail(KQ_ERR_INVALID_VALUE, "[%s] scale must be positive and finite", op);
+  if (!pow2_block(k_block))
+    return fail(KQ_ERR_UNSUPPORTED, "[%s] k_block=%lld: blocks are powers of two in [1, 128]", op,
+                (long long)k_block);
   if (!out) return fail(KQ_ERR_INVALID_VALUE, "[%s] null output pointer", op);
   if (!aligned16(out)) return fail(KQ_ERR_INVALID_VALUE, "[%s] out must be 16-byte aligned", op);
   const kq::SageLayout L = kq::sage_layout(B, H, Lq, Lk);
+  const bool k_uniform = k_block >= kq::kSageKTile;
   st = check_sage_ws(op, ws, ws_bytes, L);
   if (st != KQ_SUCCESS) return st;
   st = check_device(op);
@@ -274,7 +278,7 @@ kq_status sage_attend_impl(const char* op, const void* ws, size_t ws_bytes, void
   const char* name = kq::launch_sage_attend(reinterpret_cast<const char*>(ws), L,
                                             reinterpret_cast<uint16_t*>(out),
                                             sage_strides(layout, H, Lq), B, H, Lq, Lk, scale,
-                                            reinterpret_cast<hipStream_t>(stream));
+                                            k_uniform, reinterpret_cast<hipStream_t>(stream));
   st = check_launch(op);
   if (st == KQ_SUCCESS && env_log())
     fprintf(stderr, "[kq] %s B=%lld H=%lld Lq=%lld Lk=%lld kernel=%s grid=%lld\n", op, (long long)B,
@@ -489,9 +493,9 @@ kq_status kq_sage_prepare(const void* q, const void* k, const void* v, int64_t B
 
 kq_status kq_sage_attend(const void* ws, size_t ws_bytes, void* out, int64_t B, int64_t H,
                          int64_t Lq, int64_t Lk, int64_t D, kq_layout layout, float scale,
-                         void* stream) {
+                         int64_t k_block, void* stream) {
   return sage_attend_impl("kq_sage_attend", ws, ws_bytes, out, B, H, Lq, Lk, D, layout, scale,
-                          stream);
+                          k_block, stream);
 }
 
 kq_status kq_sage_attention(const void* q, const void* k, const void* v, void* out, int64_t B,
@@ -510,7 +514,7 @@ kq_status kq_sage_attention(const void* q, const void* k, const void* v, void* o
   st = sage_prepare_impl(op, q, k, v, B, H, Lq, Lk, D, layout, q_block, k_block, ws, ws_bytes,
                          stream, &empty);
   if (st != KQ_SUCCESS) return st;
-  return sage_attend_impl(op, ws, ws_bytes, out, B, H, Lq, Lk, D, layout, scale, stream);
+  return sage_attend_impl(op, ws, ws_bytes, out, B, H, Lq, Lk, D, layout, scale, k_block, stream);
 }
 
 }  // extern "C"

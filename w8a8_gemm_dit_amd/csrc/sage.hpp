@@ -77,8 +77,9 @@ const char* launch_sage_prepare(const uint16_t* q, const uint16_t* k, const uint
                                 char* ws, const SageLayout& L, hipStream_t s);
 
 // Attention on a prepared workspace; out fp16 with strides so.
+// k_uniform: every 64-key step shares one key scale (k_block >= 64).
 const char* launch_sage_attend(const char* ws, const SageLayout& L, uint16_t* out,
                                SageStrides so, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
-                               float scale, hipStream_t s);
+                               float scale, bool k_uniform, hipStream_t s);
 
 }  // namespace kq

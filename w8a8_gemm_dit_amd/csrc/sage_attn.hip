@@ -40,11 +40,18 @@ static_assert(kWaves * 32 == kSageQTile, "4 wavefronts of 32 rows");
 // the XOR spreads the 8 even and the 8 odd rows over all 8 chunks).
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
+// KUNI: the key scale is uniform over each 64-key step (k_block >= 64), so
+// the exponent is one fma of the converted score and the step's max is an
+// integer max.
+template <bool KUNI>
 __global__ __launch_bounds__(kWaves * 64) void sage_attn_kernel(
     const int8_t* __restrict__ qc, const float* __restrict__ sqs, const int8_t* __restrict__ kc,
     const float* __restrict__ sks, const uint16_t* __restrict__ vt, uint16_t* __restrict__ out,
     SageStrides so, int H, int Lq, int Lk, int Lqp, int Lkp, float c_log2) {
-  __shared__ __attribute__((aligned(16))) char lds[2][kStage];
+  // Three stages: step j's keys are read at step j, its values at step
+  // j+1 (the P.V product runs one step behind the scores), and step j+1's
+  // loads land meanwhile.
+  __shared__ __attribute__((aligned(16))) char lds[3][kStage];
 
   const int ntq = Lqp / kSageQTile;
   const int t = xcd_remap(blockIdx.x, gridDim.x);
@@ -100,29 +107,22 @@ __global__ __launch_bounds__(kWaves * 64) void sage_attn_kernel(
                                                (uint32_t)(lane * 16), j * kSBytes, 0, 0);
   };
 
-  v4f o[8][kQB];
-  float m[kQB], l[kQB];
+  // O^T accumulators; block 8 multiplies P by a block of ones, so it holds
+  // the row sums of the rounded P (in every lane of the row), rescaled with
+  // the rest.
+  v4f o[9][kQB];
+  float m[kQB];  // exponent reference of the row, shared by its 4 lanes
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     m[qb] = -INFINITY;
-    l[qb] = 0.0f;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) o[db][qb] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < 9; ++db) o[db][qb] = v4f{0.f, 0.f, 0.f, 0.f};
   }
+  const v8h ones = v8h{1, 1, 1, 1, 1, 1, 1, 1};
 
-  const int nsteps = (Lk + kSageKTile - 1) / kSageKTile;
-  issue(0, 0);
-  for (int j = 0; j < nsteps; ++j) {
-    const int cur = j & 1;
-    wait_vm_lgkm0<0>();
-    barrier_nofence();  // step j has landed; every wave is done with step j-1
-    if (j + 1 < nsteps) issue(cur ^ 1, j + 1);
+  // S^T of one step: keys 16kb + (4g + r), query fr.
+  auto scores = [&](int cur, v4i (&st)[4][kQB]) {
     const char* ks = lds[cur];
-    const char* vs = lds[cur] + kKBytes;
-    const float* ss = reinterpret_cast<const float*>(lds[cur] + kKBytes + kVBytes);
-
-    // S^T blocks: keys 16kb + (4g + r), query fr
-    v4i st[4][kQB];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int row = 16 * kb + fr;
@@ -136,52 +136,12 @@ __global__ __launch_bounds__(kWaves * 64) void sage_attn_kernel(
           st[kb][qb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf, qf[qb][dh], st[kb][qb], 0, 0, 0);
       }
     }
-    float skv[4][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const float4 s4 = *reinterpret_cast<const float4*>(ss + 16 * kb + 4 * g);
-      skv[kb][0] = s4.x; skv[kb][1] = s4.y; skv[kb][2] = s4.z; skv[kb][3] = s4.w;
-    }
-    const int kvalid = Lk - j * kSageKTile;  // keys of this step below Lk (>= 1)
+  };
 
-    v8h pf[2][kQB];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      float x[4][4];
-      float xmax = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x[kb][r] = (float)st[kb][qb][r] * skv[kb][r];
-          if (16 * kb + 4 * g + r < kvalid) xmax = fmaxf(xmax, x[kb][r]);
-        }
-      xmax = fmaxf(xmax, __shfl_xor(xmax, 16, kWave));
-      xmax = fmaxf(xmax, __shfl_xor(xmax, 32, kWave));
-      const float mnew = fmaxf(m[qb], xmax * aq[qb]);
-      const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);
-      m[qb] = mnew;
-      float p[4][4];
-      float psum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(x[kb][r], aq[qb], -mnew));
-          p[kb][r] = (16 * kb + 4 * g + r < kvalid) ? e : 0.0f;
-          psum += p[kb][r];
-        }
-      l[qb] = fmaf(l[qb], alpha, psum);
-#pragma unroll
-      for (int db = 0; db < 8; ++db) o[db][qb] *= alpha;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        pf[h][qb] = v8h{(_Float16)p[2 * h][0], (_Float16)p[2 * h][1], (_Float16)p[2 * h][2],
-                        (_Float16)p[2 * h][3], (_Float16)p[2 * h + 1][0], (_Float16)p[2 * h + 1][1],
-                        (_Float16)p[2 * h + 1][2], (_Float16)p[2 * h + 1][3]};
-    }
-
-    // O^T[d][q] += V^T[d][slots] . P^T[slots][q]
+  // O^T[d][q] += V^T[d][slots] . P^T[slots][q] for the values of stage
+  // `cur`; block 8: the row sums.
+  auto pv = [&](int cur, const v8h (&pf)[2][kQB]) {
+    const char* vs = lds[cur] + kKBytes;
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const int row = 16 * db + fr;
@@ -193,16 +153,132 @@ __global__ __launch_bounds__(kWaves * 64) void sage_attn_kernel(
           o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[h][qb], o[db][qb], 0, 0, 0);
       }
     }
-  }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+        o[8][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[h][qb], o[8][qb], 0, 0, 0);
+  };
+
+  // Online softmax of one step's scores -> fp16 probabilities pf.  MASK:
+  // the last step, keys >= kvalid take no part.  The exponent reference m
+  // of a row only moves when the row's max exceeds it by more than kSlack
+  // (log2 units): the probabilities then stay below 2^kSlack (exact enough
+  // in fp16, far from overflow) and O, which already holds the products of
+  // every earlier step, is rescaled on a handful of steps only.
+  constexpr float kSlack = 8.0f;
+  auto softmax = [&](int cur, const v4i (&st)[4][kQB], int kvalid, auto mask_tag,
+                     v8h (&pf)[2][kQB]) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const float* ss = reinterpret_cast<const float*>(lds[cur] + kKBytes + kVBytes);
+    float skv[4][4];
+    if (KUNI) {
+      const float s0 = ss[0];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) skv[kb][r] = s0;
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const float4 s4 = *reinterpret_cast<const float4*>(ss + 16 * kb + 4 * g);
+        skv[kb][0] = s4.x; skv[kb][1] = s4.y; skv[kb][2] = s4.z; skv[kb][3] = s4.w;
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      // exponent of key (kb, r): x * mul - m (log2 units); x is the int32
+      // score converted (KUNI: mul = the step's key scale x aq) or times
+      // its key scale (mul = aq); both factors are >= 0, so the max of the
+      // exponents is the max of x times mul.
+      float x[4][4];
+      float xmax, mul;
+      if (KUNI && !MASK) {
+        mul = skv[0][0] * aq[qb];
+        int imax = st[0][qb][0];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            imax = max(imax, st[kb][qb][r]);
+            x[kb][r] = (float)st[kb][qb][r];
+          }
+        xmax = (float)imax;
+      } else {
+        mul = aq[qb];
+        xmax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            x[kb][r] = (float)st[kb][qb][r] * skv[kb][r];
+            if (!MASK || 16 * kb + 4 * g + r < kvalid) xmax = fmaxf(xmax, x[kb][r]);
+          }
+      }
+      const float tmax = xmax * mul;
+      if (__any(tmax > m[qb] + kSlack)) {  // wave-uniform: move the reference
+        float rm = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+        rm = fmaxf(rm, __shfl_xor(rm, 32, kWave));
+        const float mnew = fmaxf(m[qb], rm);
+        const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);
+        m[qb] = mnew;
+#pragma unroll
+        for (int db = 0; db < 9; ++db) o[db][qb] *= alpha;
+      }
+      float p[4][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(x[kb][r], mul, -m[qb]));
+          p[kb][r] = (!MASK || 16 * kb + 4 * g + r < kvalid) ? e : 0.0f;
+        }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        pf[h][qb] = v8h{(_Float16)p[2 * h][0], (_Float16)p[2 * h][1], (_Float16)p[2 * h][2],
+                        (_Float16)p[2 * h][3], (_Float16)p[2 * h + 1][0], (_Float16)p[2 * h + 1][1],
+                        (_Float16)p[2 * h + 1][2], (_Float16)p[2 * h + 1][3]};
+    }
+  };
+
+  using NoMask = std::integral_constant<bool, false>;
+  using Mask = std::integral_constant<bool, true>;
+  const int nsteps = (Lk + kSageKTile - 1) / kSageKTile;
+  const bool ragged = (Lk % kSageKTile) != 0;
+  const int nfull = ragged ? nsteps - 1 : nsteps;
+
+  // Step j: the scores of step j, the P.V product of step j-1 (its MFMAs
+  // do not depend on the scores, so the two run back to back), the softmax
+  // of step j.  Before the first step the probabilities are zero and their
+  // product (on step 0's finite values) adds nothing.  The ragged last
+  // step runs outside the loop.
+  v8h pf[2][kQB];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) pf[h][qb] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+  int prev = 0;
+  auto run = [&](int j, auto mask_tag) {
+    const int cur = j % 3;
+    wait_vm_lgkm0<0>();
+    barrier_nofence();  // step j has landed; every wave is done with step j-1
+    if (j + 1 < nsteps) issue((j + 1) % 3, j + 1);
+    v4i st[4][kQB];
+    scores(cur, st);
+    pv(prev, pf);
+    softmax(cur, st, Lk - j * kSageKTile, mask_tag, pf);
+    prev = cur;
+  };
+  issue(0, 0);
+  for (int j = 0; j < nfull; ++j) run(j, NoMask{});
+  if (ragged) run(nsteps - 1, Mask{});
+  pv(prev, pf);
   wait_vm_lgkm0<0>();
 
   const int b = bh / H, hh = bh % H;
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
-    float lt = l[qb];
-    lt += __shfl_xor(lt, 16, kWave);
-    lt += __shfl_xor(lt, 32, kWave);
-    const float inv = 1.0f / lt;
+    const float inv = 1.0f / o[8][qb][0];
     const int q = q0 + 16 * qb + fr;
     if (q >= Lq) continue;
     uint16_t* orow = out + (int64_t)b * so.b + (int64_t)hh * so.h + (int64_t)q * so.l + 4 * g;
@@ -221,16 +297,17 @@ __global__ __launch_bounds__(kWaves * 64) void sage_attn_kernel(
 
 const char* launch_sage_attend(const char* ws, const SageLayout& L, uint16_t* out,
                                SageStrides so, int64_t B, int64_t H, int64_t Lq, int64_t Lk,
-                               float scale, hipStream_t s) {
+                               float scale, bool k_uniform, hipStream_t s) {
   (void)B;
   const float c_log2 = (float)((double)scale * 1.4426950408889634);
   const int64_t tiles = L.BH * (L.Lqp / kSageQTile);
-  hipLaunchKernelGGL(sage_attn_kernel, dim3((unsigned)tiles), dim3(kWaves * 64), 0, s,
+  const auto kern = k_uniform ? sage_attn_kernel<true> : sage_attn_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kWaves * 64), 0, s,
                      reinterpret_cast<const int8_t*>(ws + L.qc), reinterpret_cast<const float*>(ws + L.sq),
                      reinterpret_cast<const int8_t*>(ws + L.kc), reinterpret_cast<const float*>(ws + L.sk),
                      reinterpret_cast<const uint16_t*>(ws + L.vt), out, so, (int)H, (int)Lq, (int)Lk,
                      (int)L.Lqp, (int)L.Lkp, c_log2);
-  return "sage_attn";
+  return k_uniform ? "sage_attn_kuni" : "sage_attn";
 }
 
 }  // namespace kq
