@@ -264,8 +264,13 @@ __global__ __launch_bounds__(kWaves * 64) void sage_attn_kernel(
     barrier_nofence();  // step j has landed; every wave is done with step j-1
     if (j + 1 < nsteps) issue((j + 1) % 3, j + 1);
     v4i st[4][kQB];
+    // The wave issuing MFMAs gets the higher priority, so that the other
+    // wave on the SIMD fills the matrix pipe's busy cycles with its softmax
+    // instead of competing for issue slots.
+    __builtin_amdgcn_s_setprio(1);
     scores(cur, st);
     pv(prev, pf);
+    __builtin_amdgcn_s_setprio(0);
     softmax(cur, st, Lk - j * kSageKTile, mask_tag, pf);
     prev = cur;
   };
