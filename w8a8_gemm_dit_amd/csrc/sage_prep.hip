@@ -20,33 +20,58 @@ __device__ __forceinline__ int64_t f16_units(uint32_t u) {
 }
 
 // Per (b*h, chunk of 256 tokens): the int64 column sums of the keys.
-// 256 threads: channel tid % 128, alternate tokens per half.
+// Thread t reads channels 8*(t%16)..+7 of rows t/16, t/16 + 16, ... with
+// 16-byte loads; the 16 row lanes of a channel group then add up in LDS.
 __global__ __launch_bounds__(256) void sage_k_colsum(const uint16_t* __restrict__ k,
                                                      SageStrides st, int H, int Lk,
                                                      int nchunk, int64_t* __restrict__ colsum) {
-  const int bh = blockIdx.y;
-  const int d = threadIdx.x & 127, half = threadIdx.x >> 7;
-  const uint16_t* kb = k + (int64_t)(bh / H) * st.b + (int64_t)(bh % H) * st.h + d;
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  const int cg = tid & 15, rl = tid >> 4;
+  const uint16_t* kb = k + (int64_t)(bh / H) * st.b + (int64_t)(bh % H) * st.h + 8 * cg;
   const int t0 = blockIdx.x * kSageChunk;
   const int t1 = min(Lk, t0 + kSageChunk);
-  int64_t s = 0;
-  for (int t = t0 + half; t < t1; t += 2) s += f16_units(kb[(int64_t)t * st.l]);
-  __shared__ int64_t part[128];
-  if (half) part[d] = s;
+  int64_t s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int t = t0 + rl; t < t1; t += 16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(kb + (int64_t)t * st.l);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s[2 * j] += f16_units(w[j] & 0xFFFFu);
+      s[2 * j + 1] += f16_units(w[j] >> 16);
+    }
+  }
+  __shared__ int64_t red[16][kSageD];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[rl][8 * cg + i] = s[i];
   __syncthreads();
-  if (!half) colsum[((int64_t)bh * nchunk + blockIdx.x) * kSageD + d] = s + part[d];
+  if (tid < kSageD) {
+    int64_t tot = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tot += red[r][tid];
+    colsum[((int64_t)bh * nchunk + blockIdx.x) * kSageD + tid] = tot;
+  }
+}
+
+// Per b*h: the key means from the column sums (int64 total -> fp64 ->
+// x 2^-24 -> / L in fp64 -> fp32, each step rounded to nearest even).
+__global__ __launch_bounds__(kSageD) void sage_k_mean(const int64_t* __restrict__ colsum,
+                                                      int nchunk, int Lk,
+                                                      float* __restrict__ kmean) {
+  const int bh = blockIdx.x, d = threadIdx.x;
+  const int64_t* cs = colsum + (int64_t)bh * nchunk * kSageD + d;
+  int64_t tot = 0;
+  for (int c = 0; c < nchunk; ++c) tot += cs[(int64_t)c * kSageD];
+  kmean[(int64_t)bh * kSageD + d] = (float)(((double)tot / 16777216.0) / (double)Lk);
 }
 
 // Quantizes 128 tokens of one (b, h): one absmax scale per `block` tokens
 // (a power of two <= 128, so blocks never straddle workgroups).  SMOOTH:
-// the keys, less their mean (computed here from the column sums: int64
-// total -> fp64 -> x 2^-24 -> / L in fp64 -> fp32, each step rounded to
-// nearest even).  Thread t holds token t/2, channels 64*(t%2)..+63.
+// the keys, less their mean (kmean).  Thread t holds token t/2, channels
+// 64*(t%2)..+63.
 template <bool SMOOTH>
 __global__ __launch_bounds__(256) void sage_quant(const uint16_t* __restrict__ x, SageStrides st,
                                                   int H, int L, int Lp, int block,
-                                                  const int64_t* __restrict__ colsum, int nchunk,
-                                                  float* __restrict__ kmean,
+                                                  const float* __restrict__ kmean,
                                                   int8_t* __restrict__ codes,
                                                   float* __restrict__ scales) {
   const int bh = blockIdx.y;
@@ -56,14 +81,7 @@ __global__ __launch_bounds__(256) void sage_quant(const uint16_t* __restrict__ x
   __shared__ float s_mean[kSageD];
   __shared__ float s_wmax[4];
   if (SMOOTH) {
-    if (tid < kSageD) {
-      int64_t tot = 0;
-      const int64_t* cs = colsum + (int64_t)bh * nchunk * kSageD + tid;
-      for (int c = 0; c < nchunk; ++c) tot += cs[(int64_t)c * kSageD];
-      const float mean = (float)(((double)tot / 16777216.0) / (double)L);
-      s_mean[tid] = mean;
-      if (blockIdx.x == 0) kmean[(int64_t)bh * kSageD + tid] = mean;
-    }
+    if (tid < kSageD) s_mean[tid] = kmean[(int64_t)bh * kSageD + tid];
     __syncthreads();
   }
   float v[64];
@@ -162,12 +180,14 @@ const char* launch_sage_prepare(const uint16_t* q, const uint16_t* k, const uint
   const dim3 blk(256);
   hipLaunchKernelGGL(sage_k_colsum, dim3((unsigned)L.nchunk, (unsigned)L.BH), blk, 0, s, k, sk,
                      (int)H, (int)Lk, (int)L.nchunk, colsum);
+  float* kmean = reinterpret_cast<float*>(ws + L.kmean);
+  hipLaunchKernelGGL(sage_k_mean, dim3((unsigned)L.BH), dim3(kSageD), 0, s, colsum, (int)L.nchunk,
+                     (int)Lk, kmean);
   hipLaunchKernelGGL(sage_quant<true>, dim3((unsigned)(L.Lkp / kSageRowTile), (unsigned)L.BH), blk,
-                     0, s, k, sk, (int)H, (int)Lk, (int)L.Lkp, k_block, colsum, (int)L.nchunk,
-                     reinterpret_cast<float*>(ws + L.kmean), reinterpret_cast<int8_t*>(ws + L.kc),
-                     reinterpret_cast<float*>(ws + L.sk));
+                     0, s, k, sk, (int)H, (int)Lk, (int)L.Lkp, k_block, kmean,
+                     reinterpret_cast<int8_t*>(ws + L.kc), reinterpret_cast<float*>(ws + L.sk));
   hipLaunchKernelGGL(sage_quant<false>, dim3((unsigned)(L.Lqp / kSageRowTile), (unsigned)L.BH), blk,
-                     0, s, q, sq, (int)H, (int)Lq, (int)L.Lqp, q_block, nullptr, 0, nullptr,
+                     0, s, q, sq, (int)H, (int)Lq, (int)L.Lqp, q_block, nullptr,
                      reinterpret_cast<int8_t*>(ws + L.qc), reinterpret_cast<float*>(ws + L.sq));
   const int nblk = (int)(L.Lkp / kSageKTile);
   hipLaunchKernelGGL(sage_v_transpose, dim3((unsigned)nblk, (unsigned)L.BH), blk, 0, s, v, sv,
