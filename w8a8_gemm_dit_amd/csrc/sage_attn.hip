@@ -21,18 +21,28 @@
 #include "kq_common.hpp"
 #include "sage.hpp"
 
+// 16-row query blocks per wavefront (a build-time choice): 2 gives 4
+// wavefronts of 32 rows, 2 wavefronts per SIMD; 1 gives 8 wavefronts of 16
+// rows and 4 per SIMD, but every wavefront then reads the whole key and
+// value tiles for half the rows, and the LDS traffic makes it 4% slower.
+#ifndef KQB
+#define KQB 2
+#endif
+
 namespace kq {
 namespace {
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
-constexpr int kQB = 2;        // 16-row query blocks per wavefront
-constexpr int kWaves = 4;
+constexpr int kQB = KQB;      // 16-row query blocks per wavefront
+constexpr int kWaves = kSageQTile / (16 * kQB);
 constexpr int kKBytes = kSageKTile * kSageD;       // key codes of one step
 constexpr int kVBytes = kSageD * kSageKTile * 2;   // V^T of one step
 constexpr int kSBytes = kSageKTile * 4;            // key scales of one step
 constexpr int kStage = kKBytes + kVBytes + kSBytes;
-static_assert(kWaves * 32 == kSageQTile, "4 wavefronts of 32 rows");
+static_assert(kWaves * 16 * kQB == kSageQTile && 8 % kWaves == 0, "query tile split");
+constexpr int kKPerWave = 8 / kWaves;    // 1 KB key-code loads per wavefront
+constexpr int kVPerWave = 16 / kWaves;   // 1 KB V^T loads per wavefront
 
 // 16-byte chunk swizzle of 128-byte LDS rows: chunk c of row r sits at
 // c ^ ((r >> 1) & 7).  16 consecutive rows read at one logical chunk then
@@ -59,7 +69,7 @@ __global__ __launch_bounds__(kWaves * 64) void sage_attn_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, g = lane >> 4;
-  const int q0 = qt * kSageQTile + wave * 32;
+  const int q0 = qt * kSageQTile + wave * 16 * kQB;
 
   // Query codes (B operand of S^T: row q = fr, 16 bytes at chunk g of each
   // 64-channel half) and the per-row exponent factor.
@@ -89,15 +99,15 @@ __global__ __launch_bounds__(kWaves * 64) void sage_attn_kernel(
   auto issue = [&](int stage, int j) {
     char* base = lds[stage];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {  // key codes: blocks 2w, 2w+1 of 8
-      const int b = 2 * wave + i;
+    for (int i = 0; i < kKPerWave; ++i) {  // key codes: 8 blocks
+      const int b = kKPerWave * wave + i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(base + 1024 * b), 16,
                                                (b & 1) ? voff1 : voff0,
                                                j * kKBytes + 1024 * b, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {  // V^T: blocks 4w..4w+3 of 16
-      const int b = 4 * wave + i;
+    for (int i = 0; i < kVPerWave; ++i) {  // V^T: 16 blocks
+      const int b = kVPerWave * wave + i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(base + kKBytes + 1024 * b), 16,
                                                (b & 1) ? voff1 : voff0,
                                                j * kVBytes + 1024 * b, 0, 0);
