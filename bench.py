@@ -81,7 +81,7 @@ class Prepared:
         self.fmt = fmt
         wq, sc, gb = kq.kq_quantize_weights(wd, fmt)
         del wd
-        ws_bytes = kq.kq_workspace_bytes(wl.M, wl.K, fmt)
+        ws_bytes = kq.kq_workspace_bytes(wl.M, wl.N, wl.K, fmt)
         ysz = wl.M * wl.N * (4 if wl.out == "f32" else 2)
         per_copy = (x0.numel() * 2 + wq.numel() + sc.numel() * sc.element_size()
                     + (0 if gb is None else gb.numel() * 2) + 4 * wl.N + ysz + ws_bytes)

@@ -107,6 +107,12 @@ typedef struct kq_route_info {
     int32_t tile_n;   /* output columns per workgroup */
     int32_t threads;  /* threads per workgroup */
     int64_t grid;     /* workgroups in the main kernel */
+    int32_t splits;   /* K slices of the GEMM (1: none).  With more, each
+                         slice writes exact int32 partial sums [splits,M,N]
+                         to the workspace and a fold kernel adds them and
+                         applies the epilogue, so the result is the same,
+                         bit for bit, as the unsplit product's. */
+    int32_t reserved;
 } kq_route_info;
 
 /* Largest K the linears accept: 65536 * 127 * 127 < 2^31, so the int32
@@ -126,11 +132,13 @@ int kq_is_available(void);
  * is owned by the library and valid until the next call on this thread. */
 const char* kq_last_error(void);
 
-/* Bytes of device workspace a linear call with this M, K and weight format
- * needs: int8 activation codes (M*K), fp32 token scales (4*M), and for the
- * int4 format the per-group code sums (4*M*K/64), each region 256-byte
- * aligned.  Returns 0 for M == 0.  Pure host function. */
-size_t kq_workspace_bytes(int64_t M, int64_t K, kq_wformat fmt);
+/* Bytes of device workspace a linear call with this shape and weight format
+ * needs: int8 activation codes (M*K), fp32 token scales (4*M), for the int4
+ * format the per-group code sums (4*M*K/64), and when the route splits K
+ * (kq_route_info.splits > 1) the int32 partial sums (4*splits*M*N), each
+ * region 256-byte aligned.  Returns 0 for M == 0 or N == 0.  Pure host
+ * function; it reads the same environment levers as the route. */
+size_t kq_workspace_bytes(int64_t M, int64_t N, int64_t K, kq_wformat fmt);
 
 /* Launch plan of a linear call; pure host function, no device access.
  * [kquant]: the route decision is one tested function.  Routing: with
@@ -138,6 +146,12 @@ size_t kq_workspace_bytes(int64_t M, int64_t K, kq_wformat fmt);
  * leave most of the GPU idle) takes the GEMV unless the environment
  * variable KQ_FORCE_ROUTE=gemm; KQ_FORCE_ROUTE=gemv forces the GEMV (and
  * fails for shapes it cannot take: M > 16 or K > KQ_GEMV_MAX_K).
+ * An int8-weight GEMM whose tiles would leave more than half of the 256
+ * CUs idle splits K into slices of at least 512 (at most 16 slices)
+ * ([kquant] split-K: partials folded so the result rounds once); the
+ * environment variable KQ_SPLIT=n forces n slices (1: never split).  The
+ * kq_w8a8_gemm / kq_w4a8_gemm entry points, which take no workspace, never
+ * split.
  * Returns KQ_ERR_INVALID_VALUE / KQ_ERR_UNSUPPORTED for shapes the linears
  * reject, with the same messages. */
 kq_status kq_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
@@ -185,7 +199,7 @@ kq_status kq_quantize_act(const void* x, int64_t M, int64_t K, int8_t* a,
  *           F32/BF16: y = sx[m]*sw[n]*acc[m,n] + bias[n], acc = sum_k a*q,
  *           computed in fp32 and rounded to y_dtype;
  *           I32: acc itself.
- *   ws    device workspace of at least kq_workspace_bytes(M,K,KQ_W8_...)
+ *   ws    device workspace of at least kq_workspace_bytes(M,N,K,KQ_W8_...)
  * Requires 64 <= K <= KQ_MAX_K and K % 64 == 0.  M <= 16 routes to the GEMV
  * kernel (see kq_route). */
 kq_status kq_w8a8_linear(const void* x, int64_t M, int64_t K, int64_t N,

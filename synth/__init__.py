@@ -68,6 +68,10 @@ WORKLOADS = {
                  x_dist="student_t4"),
         Workload("thin_n_w8a8_2048x5120x48", 2048, 5120, 48, "w8", "bf16",
                  x_dist="student_t4"),
+        # A short sequence through a long-K projection (128 tokens, e.g. a
+        # text-conditioning stream, through an MLP down-projection): 24
+        # output tiles of 128x128, so the GEMM splits K.
+        Workload("short_seq_w8a8_128x12288x3072", 128, 12288, 3072, "w8", "bf16"),
         # adaLN modulation of a DiT block: the conditioning vector of each
         # sample (batch 2) to the six shift/scale/gate vectors, 6 x 3072.
         Workload("dit_modulation_w8a8_2x3072x18432", 2, 3072, 18432, "w8", "bf16"),

@@ -40,10 +40,17 @@ def test_is_available_false_without_gpu():
 def test_workspace_layout():
     al = lambda v: (v + 255) // 256 * 256
     M, K = 4096, 3072
-    assert kq.kq_workspace_bytes(M, K, kq.KQ_W8_PER_CHANNEL) == al(M * K) + al(4 * M)
-    assert kq.kq_workspace_bytes(M, K, kq.KQ_W4_AFFINE_G64) == al(M * K) + al(4 * M) + al(4 * M * K // 64)
-    assert kq.kq_workspace_bytes(0, K, kq.KQ_W8_PER_CHANNEL) == 0
-    assert kq.kq_workspace_bytes(3, 64, kq.KQ_W8_PER_CHANNEL) == 256 + 256
+    N = 3072
+    assert kq.kq_workspace_bytes(M, N, K, kq.KQ_W8_PER_CHANNEL) == al(M * K) + al(4 * M)
+    assert kq.kq_workspace_bytes(M, N, K, kq.KQ_W4_AFFINE_G64) == al(M * K) + al(4 * M) + al(4 * M * K // 64)
+    assert kq.kq_workspace_bytes(0, N, K, kq.KQ_W8_PER_CHANNEL) == 0
+    assert kq.kq_workspace_bytes(M, 0, K, kq.KQ_W8_PER_CHANNEL) == 0
+    assert kq.kq_workspace_bytes(3, N, 64, kq.KQ_W8_PER_CHANNEL) == 256 + 256
+    # a split GEMM adds its int32 partial sums
+    r = kq.kq_route(128, 3072, 12288, kq.KQ_W8_PER_CHANNEL)
+    assert r["splits"] > 1
+    assert kq.kq_workspace_bytes(128, 3072, 12288, kq.KQ_W8_PER_CHANNEL) == \
+        al(128 * 12288) + al(4 * 128) + al(4 * r["splits"] * 128 * 3072)
 
 
 @pytest.mark.parametrize("M,N,K,fmt,kind,tile,grid", [
@@ -60,7 +67,7 @@ def test_workspace_layout():
     (2048, 48, 5120, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 3 * 128),   # thin N
     (300, 64, 640, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 4 * 19),
     (300, 65, 640, kq.KQ_W8_PER_CHANNEL, "gemm", (64, 64), 5 * 2),
-    (2048, 48, 16448, kq.KQ_W8_PER_CHANNEL, "gemm", (64, 64), 32),
+    (2048, 48, 16448, kq.KQ_W8_PER_CHANNEL, "gemm", (64, 64), 32 * 8),  # 8 K slices
     (16 * 65535, 48, 128, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 3 * 65535),
     (16 * 65535 + 1, 48, 128, kq.KQ_W8_PER_CHANNEL, "gemm", None, None),  # grid y limit
 ])
@@ -71,6 +78,36 @@ def test_route_decisions(M, N, K, fmt, kind, tile, grid, kq_env):
     if tile is not None:
         assert (r["tile_m"], r["tile_n"]) == tile
         assert r["grid"] == grid
+
+
+@pytest.mark.parametrize("M,N,K,tile,splits", [
+    (128, 3072, 12288, (128, 128), 8),      # small-M prefill, long K
+    (200, 1000, 65536, (128, 128), 16),
+    (4, 512, 16448, (64, 64), 13),          # past the GEMV's K limit
+    (4096, 3072, 3072, (256, 192), 1),      # a full grid never splits
+    (16384, 12288, 3072, (256, 192), 1),
+    (512, 3072, 3072, (64, 64), 1),         # short K: the partials would cost more
+])
+def test_split_k_decisions(M, N, K, tile, splits, kq_env):
+    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_SPLIT=None)
+    r = kq.kq_route(M, N, K, kq.KQ_W8_PER_CHANNEL)
+    assert (r["tile_m"], r["tile_n"]) == tile and r["splits"] == splits
+    assert r["grid"] == ((M + tile[0] - 1) // tile[0]) * ((N + tile[1] - 1) // tile[1]) * splits
+    # int4 weights never split (their fp32 partials would round differently)
+    assert kq.kq_route(M, N, K, kq.KQ_W4_AFFINE_G64)["splits"] == 1
+
+
+def test_split_k_lever(kq_env):
+    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_SPLIT="1")
+    assert kq.kq_route(128, 3072, 12288, kq.KQ_W8_PER_CHANNEL)["splits"] == 1
+    kq_env(KQ_SPLIT="4")
+    r = kq.kq_route(4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL)
+    assert r["splits"] == 4 and r["grid"] == 256 * 4
+    kq_env(KQ_SPLIT="16")
+    assert kq.kq_route(64, 256, 320, kq.KQ_W8_PER_CHANNEL)["splits"] == 2  # 5 steps: slices of 4
+    kq_env(KQ_SPLIT="7")
+    # 48 steps in slices of ceil(48/7) = 7 -> 8 steps: 6 slices
+    assert kq.kq_route(4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL)["splits"] == 6
 
 
 def test_route_levers(kq_env):

@@ -56,7 +56,7 @@ class KqError(RuntimeError):
 class RouteInfo(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("tile_m", ctypes.c_int32),
                 ("tile_n", ctypes.c_int32), ("threads", ctypes.c_int32),
-                ("grid", ctypes.c_int64)]
+                ("grid", ctypes.c_int64), ("splits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class SageWorkspace(ctypes.Structure):
@@ -86,7 +86,7 @@ def lib() -> ctypes.CDLL:
     L.kq_last_error.restype = ctypes.c_char_p
     L.kq_last_error.argtypes = []
     L.kq_workspace_bytes.restype = sz
-    L.kq_workspace_bytes.argtypes = [i64, i64, i32]
+    L.kq_workspace_bytes.argtypes = [i64, i64, i64, i32]
     L.kq_route.restype = i32
     L.kq_route.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(RouteInfo)]
     L.kq_quantize_weights.restype = i32
@@ -162,15 +162,16 @@ def kq_last_error() -> str:
     return lib().kq_last_error().decode()
 
 
-def kq_workspace_bytes(M: int, K: int, fmt: int) -> int:
-    return int(lib().kq_workspace_bytes(M, K, fmt))
+def kq_workspace_bytes(M: int, N: int, K: int, fmt: int) -> int:
+    return int(lib().kq_workspace_bytes(M, N, K, fmt))
 
 
 def kq_route(M: int, N: int, K: int, fmt: int, out_dtype: int = KQ_DTYPE_BF16) -> dict:
     info = RouteInfo()
     _check(lib().kq_route(M, N, K, fmt, out_dtype, ctypes.byref(info)))
     return {"kind": "gemv" if info.kind == KQ_ROUTE_GEMV else "gemm", "tile_m": info.tile_m,
-            "tile_n": info.tile_n, "threads": info.threads, "grid": info.grid}
+            "tile_n": info.tile_n, "threads": info.threads, "grid": info.grid,
+            "splits": info.splits}
 
 
 # ------------------------------------------------------------- quantizers
@@ -218,8 +219,8 @@ def _prep_out(out, shape, out_dtype, dev):
     return out
 
 
-def _prep_ws(workspace, M, K, fmt, dev):
-    need = kq_workspace_bytes(M, K, fmt)
+def _prep_ws(workspace, M, N, K, fmt, dev):
+    need = kq_workspace_bytes(M, N, K, fmt)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     return workspace, workspace.numel() * workspace.element_size()
@@ -243,7 +244,7 @@ def kq_w8a8_linear(x, wq, sw, bias=None, out_dtype=torch.bfloat16, out=None, wor
     if wq.shape[1] != K or sw.shape[0] != N or (bias is not None and bias.shape[0] != N):
         raise ValueError("[kq_w8a8_linear] operand shapes disagree")
     y = _prep_out(out, _out_shape(M, N, K, out_dtype, False), out_dtype, x.device)
-    ws, wsb = _prep_ws(workspace, M, K, KQ_W8_PER_CHANNEL, x.device)
+    ws, wsb = _prep_ws(workspace, M, N, K, KQ_W8_PER_CHANNEL, x.device)
     _check(lib().kq_w8a8_linear(_ptr(x), M, K, N, _ptr(wq), _ptr(sw), _ptr(bias), _ptr(y),
                                 _OUT[out_dtype], _ptr(ws), wsb, _stream()))
     return y
@@ -265,7 +266,7 @@ def kq_w4a8_linear(x, wq4, gscale, gbias, bias=None, out_dtype=torch.bfloat16, o
             or tuple(gbias.shape) != (N, K // 64) or (bias is not None and bias.shape[0] != N)):
         raise ValueError("[kq_w4a8_linear] operand shapes disagree")
     y = _prep_out(out, _out_shape(M, N, K, out_dtype, True), out_dtype, x.device)
-    ws, wsb = _prep_ws(workspace, M, K, KQ_W4_AFFINE_G64, x.device)
+    ws, wsb = _prep_ws(workspace, M, N, K, KQ_W4_AFFINE_G64, x.device)
     _check(lib().kq_w4a8_linear(_ptr(x), M, K, N, _ptr(wq4), _ptr(gscale), _ptr(gbias), _ptr(bias),
                                 _ptr(y), _OUT[out_dtype], _ptr(ws), wsb, _stream()))
     return y
@@ -289,7 +290,7 @@ def kq_gemv_small_m(fmt, x, wq, scale, gbias=None, bias=None, out_dtype=torch.bf
     if bias is not None:
         _need(bias, "bias", torch.float32, 1)
     y = _prep_out(out, _out_shape(M, N, K, out_dtype, fmt == KQ_W4_AFFINE_G64), out_dtype, x.device)
-    ws, wsb = _prep_ws(workspace, M, K, fmt, x.device)
+    ws, wsb = _prep_ws(workspace, M, N, K, fmt, x.device)
     _check(lib().kq_gemv_small_m(fmt, _ptr(x), M, K, N, _ptr(wq), _ptr(scale), _ptr(gbias),
                                  _ptr(bias), _ptr(y), _OUT[out_dtype], _ptr(ws), wsb, _stream()))
     return y
@@ -325,7 +326,7 @@ def kq_linear_gated(fmt, x, wq, scale, gbias=None, bias=None, residual=None, gat
     if out_dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("[kq_linear_gated] out_dtype must be float32 or bfloat16")
     y = _prep_out(out, (M, N), out_dtype, x.device)
-    ws, wsb = _prep_ws(workspace, M, K, fmt, x.device)
+    ws, wsb = _prep_ws(workspace, M, N, K, fmt, x.device)
     _check(lib().kq_linear_gated(fmt, _ptr(x), M, K, N, _ptr(wq), _ptr(scale), _ptr(gbias),
                                  _ptr(bias), _ptr(residual), _ptr(gate), gate_rows, _ptr(y),
                                  _OUT[out_dtype], _ptr(ws), wsb, _stream()))

@@ -146,11 +146,15 @@ __device__ __forceinline__ void store4(void* y, int64_t idx, const float v[4], c
 // tail makes the register allocator copy accumulators at the loop back-edge,
 // so it is compiled only into the variant that needs it.
 // GATED: the output goes through the gated residual epilogue (kq::Epilogue).
+// Split K: workgroup row blockIdx.y takes codes [y*kchunk, min(K, (y+1)*
+// kchunk)) of every row (K stays the row stride) and, with OUT == I32,
+// writes its int32 sums to slice y of y[splits][M][N]; kchunk = K and one
+// grid row otherwise.
 template <int BM, int BN, int WM, int WN, int OUT, bool REM, bool GATED>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int8_t* __restrict__ W,
     const float* __restrict__ sw, const float* __restrict__ bias, void* y, int M,
-    int N, int K, Epilogue ep) {
+    int N, int K, Epilogue ep, int kchunk) {
   using C = Cfg<BM, BN, WM, WN>;
   // Two pair buffers (steps 4i, 4i+1 and 4i+2, 4i+3): each its own array,
   // so the compiler's tracking of the asynchronous LDS writes never couples
@@ -166,6 +170,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA bases stay scalar
   const int wm = wave % WM;
   const int wn = wave / WM;
+  const int k0 = blockIdx.y * kchunk;
+  A += k0;
+  W += k0;
+  if (OUT == kOutI32) y = reinterpret_cast<int32_t*>(y) + (int64_t)blockIdx.y * M * N;
 
   // Buffer descriptors rebased on this tile's first row: rows past the
   // matrix edge fall outside num_records and read as zero.
@@ -186,7 +194,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
   const uint32_t vbase = (uint32_t)(rr * K + (lane >> 5) * 64);
   const uint32_t voff0 = vbase + (uint32_t)(((lane & 3) ^ ((rr >> 1) & 3)) * 16);
   const uint32_t voff1 = vbase + (uint32_t)(((lane & 3) ^ ((rr >> 1) & 3) ^ 1) * 16);
-  const int KT = K / 64;
+  const int KT = min(kchunk, K - k0) / 64;
   // Fill a pair buffer with K steps 2*pi and 2*pi+1.  Pairs past the end
   // re-load the last one into a buffer that is never read again; with an
   // odd step count the last pair's second half holds bytes past the row
@@ -438,49 +446,114 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
 template <int BM, int BN, int WM, int WN, bool REM>
 void launch_rem(const int8_t* a, const float* sx, const int8_t* q, const float* sw,
                 const float* bias, void* y, int out, int M, int N, int K, hipStream_t s,
-                const Epilogue& ep) {
+                const Epilogue& ep, int splits, int kchunk) {
   const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const dim3 grid((unsigned)tiles), block(64 * WM * WN);
+  const dim3 grid((unsigned)tiles, (unsigned)splits), block(64 * WM * WN);
   const bool g = ep.active();
   if (out == kOutF32 && g)
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutF32, REM, true>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutF32, REM, true>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep, kchunk);
   else if (out == kOutF32)
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutF32, REM, false>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutF32, REM, false>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep, kchunk);
   else if (out == kOutBF16 && g)
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutBF16, REM, true>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutBF16, REM, true>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep, kchunk);
   else if (out == kOutBF16)
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutBF16, REM, false>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutBF16, REM, false>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep, kchunk);
   else
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutI32, REM, false>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutI32, REM, false>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep, kchunk);
 }
 
 template <int BM, int BN, int WM = 2, int WN = 2>
 const char* launch_tile(const int8_t* a, const float* sx, const int8_t* q, const float* sw,
                         const float* bias, void* y, int out, int M, int N, int K,
-                        hipStream_t s, const Epilogue& ep, const char* name) {
-  if ((K / 64) % 4 == 0)
-    launch_rem<BM, BN, WM, WN, false>(a, sx, q, sw, bias, y, out, M, N, K, s, ep);
+                        hipStream_t s, const Epilogue& ep, const char* name, int splits,
+                        int kchunk) {
+  const int klast = K - (splits - 1) * kchunk;  // the last slice's codes
+  if ((kchunk / 64) % 4 == 0 && (klast / 64) % 4 == 0)
+    launch_rem<BM, BN, WM, WN, false>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, splits, kchunk);
   else
-    launch_rem<BM, BN, WM, WN, true>(a, sx, q, sw, bias, y, out, M, N, K, s, ep);
+    launch_rem<BM, BN, WM, WN, true>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, splits, kchunk);
   return name;
+}
+
+// Fold of a split GEMM: the exact int32 sum of the slices, then the same
+// epilogue expression as the unsplit kernel (one rounding), so the output
+// matches it bit for bit.  One thread per output element.
+template <int OUT, bool GATED>
+__global__ __launch_bounds__(256) void splitk_fold(const int32_t* __restrict__ P, int S,
+                                                   const float* __restrict__ sx,
+                                                   const float* __restrict__ sw,
+                                                   const float* __restrict__ bias, void* y,
+                                                   int M, int N, Epilogue ep) {
+  const int64_t MN = (int64_t)M * N;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= MN) return;
+  int32_t acc = 0;
+  for (int s = 0; s < S; ++s) acc += P[s * MN + e];
+  if (OUT == kOutI32) {
+    reinterpret_cast<int32_t*>(y)[e] = acc;
+    return;
+  }
+  const int m = (int)(e / N), n = (int)(e % N);
+  float v = fmaf(sx[m] * sw[n], (float)acc, bias != nullptr ? bias[n] : 0.0f);
+  if (GATED) v = gated1(v, ep.residual, ep.gate, ep.gate_rows, m, n, N);
+  if (OUT == kOutF32) reinterpret_cast<float*>(y)[e] = v;
+  else reinterpret_cast<uint16_t*>(y)[e] = (uint16_t)f32_to_bf16_rne(v);
+}
+
+void launch_fold(const int32_t* P, int S, const float* sx, const float* sw, const float* bias,
+                 void* y, int out, int M, int N, hipStream_t s, const Epilogue& ep) {
+  const dim3 grid((unsigned)(((int64_t)M * N + 255) / 256)), block(256);
+  const bool g = ep.active();
+  if (out == kOutF32 && g)
+    hipLaunchKernelGGL((splitk_fold<kOutF32, true>), grid, block, 0, s, P, S, sx, sw, bias, y, M, N, ep);
+  else if (out == kOutF32)
+    hipLaunchKernelGGL((splitk_fold<kOutF32, false>), grid, block, 0, s, P, S, sx, sw, bias, y, M, N, ep);
+  else if (out == kOutBF16 && g)
+    hipLaunchKernelGGL((splitk_fold<kOutBF16, true>), grid, block, 0, s, P, S, sx, sw, bias, y, M, N, ep);
+  else if (out == kOutBF16)
+    hipLaunchKernelGGL((splitk_fold<kOutBF16, false>), grid, block, 0, s, P, S, sx, sw, bias, y, M, N, ep);
+  else
+    hipLaunchKernelGGL((splitk_fold<kOutI32, false>), grid, block, 0, s, P, S, sx, sw, bias, y, M, N, ep);
 }
 
 }  // namespace
 
+// One launch of the tile kernel over `splits` K slices of kchunk codes.
+const char* launch_gemm_slices(int tile, const int8_t* a, const float* sx, const int8_t* q,
+                               const float* sw, const float* bias, void* y, int out, int M,
+                               int N, int K, hipStream_t s, const Epilogue& ep, int splits,
+                               int kchunk);
+
 const char* launch_gemm_w8a8(int tile, const int8_t* a, const float* sx, const int8_t* q,
                              const float* sw, const float* bias, void* y, int out, int M,
-                             int N, int K, hipStream_t s, const Epilogue& ep) {
+                             int N, int K, hipStream_t s, const Epilogue& ep, int splits,
+                             int32_t* partials) {
+  if (splits > 1) {
+    int64_t chunk = K;
+    const int sp = split_chunk(K, splits, chunk);
+    const char* name = launch_gemm_slices(tile, a, sx, q, sw, bias, partials, kOutI32, M, N, K,
+                                          s, Epilogue(), sp, (int)chunk);
+    launch_fold(partials, sp, sx, sw, bias, y, out, M, N, s, ep);
+    return name;
+  }
+  return launch_gemm_slices(tile, a, sx, q, sw, bias, y, out, M, N, K, s, ep, 1, K);
+}
+
+const char* launch_gemm_slices(int tile, const int8_t* a, const float* sx, const int8_t* q,
+                               const float* sw, const float* bias, void* y, int out, int M,
+                               int N, int K, hipStream_t s, const Epilogue& ep, int splits,
+                               int kchunk) {
   switch (tile) {
     case kTile256x256:
-      return launch_tile<256, 256>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_256x256");
+      return launch_tile<256, 256>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_256x256", splits, kchunk);
     case kTile256x192:
-      return launch_tile<256, 192, 4, 2>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_256x192");
+      return launch_tile<256, 192, 4, 2>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_256x192", splits, kchunk);
     case kTile256x128:
-      return launch_tile<256, 128>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_256x128");
+      return launch_tile<256, 128>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_256x128", splits, kchunk);
     case kTile128x128:
-      return launch_tile<128, 128>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_128x128");
+      return launch_tile<128, 128>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_128x128", splits, kchunk);
     default:
-      return launch_tile<64, 64>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_64x64");
+      return launch_tile<64, 64>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_64x64", splits, kchunk);
   }
 }
 

@@ -49,6 +49,14 @@ int env_force_route() {
 
 int env_tile() { return kq::tile_from_name(getenv("KQ_TILE")); }
 
+// KQ_SPLIT=n: n K slices for int8-weight GEMMs (1: never); unset: automatic.
+int env_split() {
+  const char* v = getenv("KQ_SPLIT");
+  if (!v || !v[0]) return -1;
+  const int n = atoi(v);
+  return n >= 1 ? n : -1;
+}
+
 bool env_log() {
   const char* v = getenv("KQ_LOG");
   return v && v[0] && strcmp(v, "0");
@@ -88,12 +96,14 @@ const char* dtype_name(kq_dtype d) {
 
 // Launches the GEMM/GEMV stage of a validated linear on quantized
 // activations (codes, scales and, for int4 weights, group sums).
+// partials: int32 workspace of a split GEMM, or NULL (then K is never split).
 kq_status launch_main(const char* op, int force, kq_wformat fmt, const int8_t* codes,
                       const float* sx, const int32_t* gsum, int64_t M, int64_t K, int64_t N,
                       const void* wq, const void* scale, const void* gbias, const float* bias,
                       void* y, kq_dtype y_dtype, hipStream_t s, const char* kq_name,
-                      const kq::Epilogue& ep = kq::Epilogue()) {
-  const kq_route_info r = kq::choose_route(M, N, K, fmt, force, env_tile());
+                      const kq::Epilogue& ep = kq::Epilogue(), int32_t* partials = nullptr) {
+  const kq_route_info r =
+      kq::choose_route(M, N, K, fmt, force, env_tile(), partials ? env_split() : 0);
   const int out = out_kind(y_dtype);
   const char* k2;
   if (r.kind == KQ_ROUTE_GEMV) {
@@ -106,7 +116,7 @@ kq_status launch_main(const char* op, int force, kq_wformat fmt, const int8_t* c
     if (fmt == KQ_W8_PER_CHANNEL)
       k2 = kq::launch_gemm_w8a8(tile, codes, sx, reinterpret_cast<const int8_t*>(wq),
                                 reinterpret_cast<const float*>(scale), bias, y, out, (int)M,
-                                (int)N, (int)K, s, ep);
+                                (int)N, (int)K, s, ep, r.splits, partials);
     else
       k2 = kq::launch_gemm_w4a8(tile, codes, sx, gsum, reinterpret_cast<const uint8_t*>(wq),
                                 scale, gbias, bias, y, out, (int)M, (int)N, (int)K, s, ep);
@@ -114,11 +124,12 @@ kq_status launch_main(const char* op, int force, kq_wformat fmt, const int8_t* c
   const kq_status st = check_launch(op);
   if (st != KQ_SUCCESS) return st;
   if (env_log())
-    fprintf(stderr, "[kq] %s M=%lld N=%lld K=%lld out=%s%s route=%s kernels=%s%s%s tile=%dx%d grid=%lld\n",
+    fprintf(stderr, "[kq] %s M=%lld N=%lld K=%lld out=%s%s route=%s kernels=%s%s%s%s tile=%dx%d splits=%d grid=%lld\n",
             op, (long long)M, (long long)N, (long long)K, dtype_name(y_dtype),
             ep.active() ? " gated" : "",
             r.kind == KQ_ROUTE_GEMV ? "gemv" : "gemm", kq_name ? kq_name : "",
-            kq_name ? "," : "", k2, r.tile_m, r.tile_n, (long long)r.grid);
+            kq_name ? "," : "", k2, r.splits > 1 ? ",splitk_fold" : "", r.tile_m, r.tile_n,
+            r.splits, (long long)r.grid);
   return KQ_SUCCESS;
 }
 
@@ -153,7 +164,8 @@ kq_status run_linear(const char* op, int force, kq_wformat fmt, const void* x, i
   if (st != KQ_SUCCESS || M == 0 || N == 0) return st;
   if (!aligned16(ws))
     return fail(KQ_ERR_INVALID_VALUE, "[%s] x, weights, y and workspace must be 16-byte aligned", op);
-  const kq::WorkspaceLayout wl = kq::workspace_layout(M, K, fmt);
+  const int splits = kq::choose_route(M, N, K, fmt, force, env_tile(), env_split()).splits;
+  const kq::WorkspaceLayout wl = kq::workspace_layout(M, N, K, fmt, splits);
   if (!ws || ws_bytes < wl.total)
     return fail(KQ_ERR_WORKSPACE, "[%s] workspace of %zu bytes is smaller than the %zu required", op,
                 ws_bytes, wl.total);
@@ -168,8 +180,9 @@ kq_status run_linear(const char* op, int force, kq_wformat fmt, const void* x, i
                                              sx, gsum, s);
   st = check_launch(op);
   if (st != KQ_SUCCESS) return st;
+  int32_t* partials = splits > 1 ? reinterpret_cast<int32_t*>(wsb + wl.part_off) : nullptr;
   return launch_main(op, force, fmt, codes, sx, gsum, M, K, N, wq, scale, gbias, bias, y, y_dtype,
-                     s, kq_name, ep);
+                     s, kq_name, ep, partials);
 }
 
 // Shared body of the entry points on pre-quantized activations.
@@ -306,8 +319,10 @@ int kq_is_available(void) {
 
 const char* kq_last_error(void) { return g_last_error.c_str(); }
 
-size_t kq_workspace_bytes(int64_t M, int64_t K, kq_wformat fmt) {
-  return kq::workspace_layout(M, K, fmt).total;
+size_t kq_workspace_bytes(int64_t M, int64_t N, int64_t K, kq_wformat fmt) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  const int splits = kq::choose_route(M, N, K, fmt, env_force_route(), env_tile(), env_split()).splits;
+  return kq::workspace_layout(M, N, K, fmt, splits).total;
 }
 
 kq_status kq_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt, kq_dtype y_dtype,
@@ -323,7 +338,7 @@ kq_status kq_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt, kq_dtype y_d
   if (force == 2 && K > kq::kGemvMaxK)
     return fail(KQ_ERR_UNSUPPORTED, "[kq_route] K=%lld exceeds the GEMV limit %lld", (long long)K,
                 (long long)kq::kGemvMaxK);
-  *out = kq::choose_route(M, N, K, fmt, force, env_tile());
+  *out = kq::choose_route(M, N, K, fmt, force, env_tile(), env_split());
   return KQ_SUCCESS;
 }
 

@@ -30,9 +30,12 @@ const char* launch_quant_w4(const float* w, int64_t N, int K, uint8_t* q4, void*
                             hipStream_t s);
 
 // W8A8 GEMM on quantized activations: y = sx*sw*(a . q^T) + bias.
+// splits > 1: K in that many slices (kq::split_chunk), int32 partial sums
+// into `partials` [splits][M][N], then a fold kernel writes y.
 const char* launch_gemm_w8a8(int tile, const int8_t* a, const float* sx, const int8_t* q,
                              const float* sw, const float* bias, void* y, int out, int M,
-                             int N, int K, hipStream_t s, const Epilogue& ep = Epilogue());
+                             int N, int K, hipStream_t s, const Epilogue& ep = Epilogue(),
+                             int splits = 1, int32_t* partials = nullptr);
 
 // W4A8 GEMM: y = sx * sum_g (gs*P + gb*A) + bias (or P per group for I32).
 const char* launch_gemm_w4a8(int tile, const int8_t* a, const float* sx, const int32_t* gsum,

@@ -8,6 +8,7 @@
 #include "kq_route.hpp"
 
 #include <cstdio>
+#include <algorithm>
 #include <cstdlib>
 
 namespace kq {
@@ -80,9 +81,22 @@ kq_status validate_linear(const char* op, int64_t M, int64_t K, int64_t N,
   return KQ_SUCCESS;
 }
 
+int split_chunk(int64_t K, int want, int64_t& chunk) {
+  const int64_t steps = K / 64;
+  if (want < 2 || steps < 2) {
+    chunk = K;
+    return 1;
+  }
+  int64_t cs = (steps + want - 1) / want;  // 64-code steps per slice
+  cs = (cs + 3) / 4 * 4;
+  chunk = cs * 64;
+  return (int)((steps + cs - 1) / cs);
+}
+
 kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
-                           int force, int tile_override) {
+                           int force, int tile_override, int split_override) {
   kq_route_info r{};
+  r.splits = 1;
   const bool fits = M <= KQ_GEMV_MAX_M && K <= kGemvMaxK;
   // Thin N: the GEMM's tiles would leave most CUs idle, while the GEMV
   // kernel's 16x16 blocks over all of K give ceil(N/16)*ceil(M/16)
@@ -120,17 +134,49 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
         tile = cand[i];
       }
     }
-  } else {
-    // Minimize (waves of 256 workgroups) x (tile area / relative tile
-    // efficiency): larger tiles reuse operands better, but a partial last
-    // wave leaves CUs idle.
+  }
+  // Modelled time of a tile grid with `sp` K slices (seconds): waves of 256
+  // workgroups, each tile at about 45% of a CU's share of the INT8 peak
+  // times the tile's relative efficiency; a split adds its int32 partials'
+  // HBM round trip (written, then read by the fold, at ~4 TB/s) and the
+  // fold's launch.
+  static const double kEff[kNumTiles] = {0.95, 1.0, 0.9, 0.75, 0.45, 1.0, 0.7};
+  auto model = [&](int32_t t, int sp, int64_t chunk) {
+    const TileShape sh = tile_shape(t);
+    const int64_t tiles = ((M + sh.bm - 1) / sh.bm) * ((N + sh.bn - 1) / sh.bn);
+    const int64_t waves = (tiles * sp + kSplitCUs - 1) / kSplitCUs;
+    const double tile_s = 2.0 * sh.bm * sh.bn * (double)chunk / (8.8e12 * kEff[t]);
+    double cost = (double)waves * tile_s;
+    if (sp > 1) cost += 8.0 * sp * (double)M * (double)N / 4.0e12 + 3e-6;
+    return cost;
+  };
+  // Slices for a tile (int8 weights only: exact int32 partials): the best
+  // modelled count up to kSplitMax with slices of at least kSplitMinK, or
+  // the forced count.
+  auto best_split = [&](int32_t t, int64_t& chunk) -> int {
+    chunk = K;
+    if (!w8 || split_override == 0 || split_override == 1) return 1;
+    if (split_override > 1) return split_chunk(K, std::min(split_override, kSplitMax), chunk);
+    int best_sp = 1;
+    double best_cost = model(t, 1, K);
+    for (int want = 2; want <= kSplitMax && K / want >= kSplitMinK; ++want) {
+      int64_t c;
+      const int sp = split_chunk(K, want, c);
+      const double cost = model(t, sp, c);
+      if (cost < best_cost) {
+        best_cost = cost;
+        best_sp = sp;
+        chunk = c;
+      }
+    }
+    return best_sp;
+  };
+  if (tile < 0) {
     double best = 0;
     for (int i = 0; i < ncand; ++i) {
-      const TileShape s = tile_shape(cand[i]);
-      const int64_t tiles = ((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
-      const int64_t waves = (tiles + 255) / 256;
-      static const double kEff[kNumTiles] = {0.95, 1.0, 0.9, 0.75, 0.45, 1.0, 0.7};
-      const double cost = (double)waves * s.bm * s.bn / kEff[cand[i]];
+      int64_t chunk;
+      const int sp = best_split(cand[i], chunk);
+      const double cost = model(cand[i], sp, chunk);
       if (tile < 0 || cost < best) {
         best = cost;
         tile = cand[i];
@@ -142,13 +188,16 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
   r.tile_m = s.bm;
   r.tile_n = s.bn;
   r.threads = s.threads;
-  r.grid = ((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
+  const int64_t tiles = ((M + s.bm - 1) / s.bm) * ((N + s.bn - 1) / s.bn);
+  int64_t chunk;
+  r.splits = best_split(tile, chunk);
+  r.grid = tiles * r.splits;
   return r;
 }
 
-WorkspaceLayout workspace_layout(int64_t M, int64_t K, kq_wformat fmt) {
+WorkspaceLayout workspace_layout(int64_t M, int64_t N, int64_t K, kq_wformat fmt, int splits) {
   WorkspaceLayout w{};
-  if (M <= 0 || K <= 0) return w;
+  if (M <= 0 || K <= 0 || N <= 0) return w;
   size_t off = 0;
   w.codes_off = off;
   w.codes_bytes = (size_t)M * (size_t)K;
@@ -160,6 +209,11 @@ WorkspaceLayout workspace_layout(int64_t M, int64_t K, kq_wformat fmt) {
     w.gsum_off = off;
     w.gsum_bytes = 4 * (size_t)M * (size_t)(K / 64);
     off = align256(off + w.gsum_bytes);
+  }
+  if (splits > 1) {
+    w.part_off = off;
+    w.part_bytes = 4 * (size_t)splits * (size_t)M * (size_t)N;
+    off = align256(off + w.part_bytes);
   }
   w.total = off;
   return w;

@@ -38,18 +38,34 @@ kq_status validate_linear(const char* op, int64_t M, int64_t K, int64_t N,
                           kq_wformat fmt, kq_dtype y_dtype, std::string& err);
 
 // Route of a validated linear call.  force: 0 = automatic, 1 = GEMM, 2 = GEMV.
-// tile_override: -1 = automatic, else a GemmTile.
+// tile_override: -1 = automatic, else a GemmTile.  split_override: -1 =
+// automatic (int8 weights only), 0 or 1 = never split K, n > 1 = n slices
+// (int8 weights only; fewer if K is short).
 kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
-                           int force, int tile_override);
+                           int force, int tile_override, int split_override = 0);
+
+// K slicing of a split GEMM: slices of `chunk` codes (a multiple of 256, so
+// that only the last slice can end between the kernel's 4-step unrolls);
+// returns the number of slices, at most `want`.
+int split_chunk(int64_t K, int want, int64_t& chunk);
 
 // Workspace layout of one linear call.
 struct WorkspaceLayout {
   size_t codes_off, codes_bytes;   // int8 [M,K]
   size_t scale_off, scale_bytes;   // fp32 [M]
   size_t gsum_off, gsum_bytes;     // int32 [M,K/64] (int4 format only)
+  size_t part_off, part_bytes;     // int32 [splits,M,N] (split GEMM only)
   size_t total;
 };
-WorkspaceLayout workspace_layout(int64_t M, int64_t K, kq_wformat fmt);
+WorkspaceLayout workspace_layout(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
+                                 int splits = 1);
+
+// Split-K policy: the slice count (at most kSplitMax, slices of at least
+// kSplitMinK codes) that minimizes a simple time model of the grid (waves
+// of kSplitCUs workgroups) plus the partial sums' round trip.
+constexpr int kSplitCUs = 256;
+constexpr int kSplitMax = 16;
+constexpr int64_t kSplitMinK = 512;
 
 // GEMV route geometry: 16 output columns per workgroup of 8 wavefronts,
 // which split K; each wavefront holds its K slice of the activations in
