@@ -208,3 +208,53 @@ def test_workload_full_size_sampled(name):
         assert np.array_equal(kc.reshape(w.Lk, 128), rkc) and np.array_equal(sk.view(np.uint32), rsk.view(np.uint32))
         rows = np.unique(np.concatenate([rng.choice(w.Lq, size=14, replace=False), [0, w.Lq - 1]]))
         _check_out(o[b, h, rows], rqc[rows], rsq[rows], rkc, rsk, v[b, h], 128 ** -0.5, f"{name} head {i}")
+
+
+@pytest.mark.parametrize("q_block,k_block", [(128, 64), (1, 1)])
+@pytest.mark.parametrize("B,H,Lq,Lk", [(2, 3, 513, 77), (1, 2, 4096, 64), (1, 1, 7, 300)])
+def test_cross_attention_shapes(B, H, Lq, Lk, q_block, k_block):
+    """Queries and keys of different lengths (a DiT's text cross-attention:
+    thousands of image tokens against tens of text tokens)."""
+    q, k, v = synth.attention_inputs(B, H, Lq, Lk, seed=Lq + 7 * Lk)
+    out = kq.kq_sage_attention(_dev(q), _dev(k), _dev(v), q_block=q_block, k_block=k_block)
+    o = out.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            qc, sq, kc, sk, _ = S.prepare(q[b, h], k[b, h], q_block, k_block)
+            _check_out(o[b, h], qc, sq, kc, sk, v[b, h], 128 ** -0.5, f"cross {B}x{H}x{Lq}x{Lk} b{b}h{h}")
+
+
+@pytest.mark.parametrize("k_block", [64, 1])
+def test_rising_scores_rescale_every_step(k_block):
+    """Scores that grow along the keys, so that each 64-key step raises the
+    row max by more than the 8 (log2) slack: the output rescale runs on
+    every step (uniform and per-token key scales)."""
+    rng = np.random.default_rng(31)
+    Lq, Lk = 130, 640
+    q = (rng.standard_normal((1, 1, Lq, 128)) * 0.5).astype(np.float32)
+    q[..., :8] = 3.0                                   # a shared direction
+    k = (rng.standard_normal((1, 1, Lk, 128)) * 0.5).astype(np.float32)
+    k[..., :8] = np.linspace(-8, 8, Lk, dtype=np.float32)[None, None, :, None]
+    q, k = q.astype(np.float16), k.astype(np.float16)
+    v = rng.standard_normal((1, 1, Lk, 128)).astype(np.float16)
+    scale = 0.35
+    out = kq.kq_sage_attention(_dev(q), _dev(k), _dev(v), scale=scale, q_block=64,
+                               k_block=k_block).cpu().numpy()
+    qc, sq, kc, sk, _ = S.prepare(q[0, 0], k[0, 0], 64, k_block)
+    Sc = S.scores_exact(qc, sq, kc, sk, scale) * np.log2(np.e)
+    step_max = Sc.reshape(Lq, Lk // 64, 64).max(axis=2)
+    assert (np.diff(step_max, axis=1) > 8).mean() > 0.5   # most steps raise the max by > 8
+    _check_out(out[0, 0], qc, sq, kc, sk, v[0, 0], scale, f"rising k_block {k_block}")
+
+
+def test_large_scores_are_one_hot():
+    """|S| in the thousands: softmax is one-hot, exp underflows to zero for
+    every other key, and the output is the argmax key's value row."""
+    rng = np.random.default_rng(32)
+    q = (rng.standard_normal((1, 2, 200, 128)) * 30).astype(np.float16)
+    k = (rng.standard_normal((1, 2, 333, 128)) * 30).astype(np.float16)
+    v = rng.standard_normal((1, 2, 333, 128)).astype(np.float16)
+    out = kq.kq_sage_attention(_dev(q), _dev(k), _dev(v)).cpu().numpy()
+    for h in range(2):
+        qc, sq, kc, sk, _ = S.prepare(q[0, h], k[0, h], 128, 64)
+        _check_out(out[0, h], qc, sq, kc, sk, v[0, h], 128 ** -0.5, f"one-hot h{h}")
