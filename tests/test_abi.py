@@ -93,8 +93,18 @@ def test_split_k_decisions(M, N, K, tile, splits, kq_env):
     r = kq.kq_route(M, N, K, kq.KQ_W8_PER_CHANNEL)
     assert (r["tile_m"], r["tile_n"]) == tile and r["splits"] == splits
     assert r["grid"] == ((M + tile[0] - 1) // tile[0]) * ((N + tile[1] - 1) // tile[1]) * splits
-    # int4 weights never split (their fp32 partials would round differently)
-    assert kq.kq_route(M, N, K, kq.KQ_W4_AFFINE_G64)["splits"] == 1
+
+
+@pytest.mark.parametrize("M,N,K,tile,splits", [
+    (128, 3072, 12288, (64, 128), 4),       # int4 slices are whole 16-group chunks
+    (64, 4096, 4096, (64, 128), 4),
+    (300, 640, 2112, (64, 128), 3),         # a one-group last slice
+    (2048, 4096, 12288, (128, 256), 1),
+])
+def test_split_k_decisions_int4(M, N, K, tile, splits, kq_env):
+    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_SPLIT=None)
+    r = kq.kq_route(M, N, K, kq.KQ_W4_AFFINE_G64)
+    assert (r["tile_m"], r["tile_n"]) == tile and r["splits"] == splits
 
 
 def test_split_k_lever(kq_env):
@@ -105,6 +115,7 @@ def test_split_k_lever(kq_env):
     assert r["splits"] == 4 and r["grid"] == 256 * 4
     kq_env(KQ_SPLIT="16")
     assert kq.kq_route(64, 256, 320, kq.KQ_W8_PER_CHANNEL)["splits"] == 2  # 5 steps: slices of 4
+    assert kq.kq_route(64, 256, 3200, kq.KQ_W4_AFFINE_G64)["splits"] == 4  # 50 groups: 16, 16, 16, 2
     kq_env(KQ_SPLIT="7")
     # 48 steps in slices of ceil(48/7) = 7 -> 8 steps: 6 slices
     assert kq.kq_route(4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL)["splits"] == 6

@@ -110,3 +110,69 @@ def test_workspace_too_small_for_the_partials_is_an_error(kq_env):
     small = torch.empty((need - 256,), dtype=torch.uint8, device="cuda")
     with pytest.raises(ValueError, match="workspace"):
         kq.kq_w8a8_linear(dev_bf16(xb), dev(q8), dev(sw), dev(b), workspace=small)
+
+
+# ---------------------------------------------------------------- int4
+def _problem4(M, K, N, seed):
+    xb = synth.random_bf16((M, K), seed=seed)
+    w = synth.random_f32((N, K), seed=seed + 1, scale=0.02)
+    b = synth.random_f32((N,), seed=seed + 2, scale=0.1)
+    p, gs, gb, q = oracle.quantize_w4(w)
+    return xb, p, gs, gb, q, b
+
+
+def _check4(xb, q, gs, gb, b, yf, yb, P, what):
+    a, _, _ = oracle.quantize_act(xb)
+    assert np.array_equal(host(P), oracle.w4a8_group_acc(a, q)), what
+    y64 = oracle.w4a8_linear_exact(xb, q, gs, gb, b)
+    T = oracle.w4a8_magnitude(xb, q, gs, gb, b)
+    check_f32(host(yf), y64, T, what + " f32")
+    check_bf16(host_bf16_bits(yb), y64, T, what + " bf16")
+
+
+@pytest.mark.parametrize("M,K,N", [(128, 12288, 3072), (64, 4096, 4096), (300, 2112, 640)])
+def test_int4_automatic_split(M, K, N, kq_env):
+    """fp32 slice sums folded in slice order: within the oracle's bars (not
+    bitwise the unsplit order), per-group products bit-exact."""
+    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_SPLIT=None)
+    assert kq.kq_route(M, N, K, kq.KQ_W4_AFFINE_G64)["splits"] > 1
+    xb, p, gs, gb, q, b = _problem4(M, K, N, seed=M + K)
+    args = (dev_bf16(xb), dev(p), dev(gs), dev(gb))
+    yf = kq.kq_w4a8_linear(*args, bias=dev(b), out_dtype=torch.float32)
+    yb = kq.kq_w4a8_linear(*args, bias=dev(b), out_dtype=torch.bfloat16)
+    P = kq.kq_w4a8_linear(*args, out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    _check4(xb, q, gs, gb, b, yf, yb, P, f"int4 split {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("tile", ["128x256", "64x128"])
+@pytest.mark.parametrize("split", ["2", "3", "7"])
+@pytest.mark.parametrize("M,K,N", [(257, 3200, 200), (100, 2112, 129)])
+def test_int4_forced_splits_every_tile(M, K, N, tile, split, kq_env):
+    """Ragged M and N; 50 and 33 groups, so the last slice holds a partial
+    16-group chunk (or a single group)."""
+    kq_env(KQ_FORCE_ROUTE="gemm", KQ_TILE=tile, KQ_SPLIT=split)
+    assert kq.kq_route(M, N, K, kq.KQ_W4_AFFINE_G64)["splits"] > 1
+    xb, p, gs, gb, q, b = _problem4(M, K, N, seed=2 * M + N + int(split))
+    args = (dev_bf16(xb), dev(p), dev(gs), dev(gb))
+    yf = kq.kq_w4a8_linear(*args, bias=dev(b), out_dtype=torch.float32)
+    yb = kq.kq_w4a8_linear(*args, bias=dev(b), out_dtype=torch.bfloat16)
+    P = kq.kq_w4a8_linear(*args, out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    _check4(xb, q, gs, gb, b, yf, yb, P, f"int4 {tile} split {split}")
+
+
+def test_int4_split_with_gated_epilogue(kq_env):
+    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_SPLIT=None)
+    M, K, N = 128, 12288, 3072
+    assert kq.kq_route(M, N, K, kq.KQ_W4_AFFINE_G64)["splits"] > 1
+    xb, p, gs, gb, q, b = _problem4(M, K, N, seed=41)
+    r = synth.random_bf16((M, N), seed=42)
+    g = synth.random_f32((1, N), seed=43, scale=0.5)
+    y = kq.kq_linear_gated(kq.KQ_W4_AFFINE_G64, dev_bf16(xb), dev(p), dev(gs), dev(gb),
+                           bias=dev(b), residual=dev_bf16(r), gate=dev(g), gate_rows=M,
+                           out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = oracle.gated_residual_exact(oracle.w4a8_linear_exact(xb, q, gs, gb, b), r, g, M)
+    T = oracle.gated_magnitude(oracle.w4a8_magnitude(xb, q, gs, gb, b), r, g, M)
+    check_bf16(host_bf16_bits(y), ref, T, "int4 split gated")

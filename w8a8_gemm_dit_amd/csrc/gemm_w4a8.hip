@@ -67,16 +67,19 @@ struct Cfg4 {
 
 template <int OUT>
 __device__ __forceinline__ void store1(void* y, int64_t idx, float v) {
-  if (OUT == kOutF32) reinterpret_cast<float*>(y)[idx] = v;
+  if (OUT == kOutF32 || OUT == kOutPart) reinterpret_cast<float*>(y)[idx] = v;
   else reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)f32_to_bf16_rne(v);
 }
 
 // GATED: the output goes through the gated residual epilogue (kq::Epilogue).
+// Split K: workgroup row blockIdx.y takes groups [y*gchunk, min(G, (y+1)*
+// gchunk)) (gchunk a multiple of the 16-group table chunk); with OUT ==
+// kOutPart it writes its raw fp32 sums to slice y of y[splits][M][N].
 template <int BM, int BN, int WTM, int WTN, int OUT, bool GATED>
 __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int32_t* __restrict__ gsum,
     const uint8_t* __restrict__ Q, const uint16_t* __restrict__ GS, const uint16_t* __restrict__ GB,
-    const float* __restrict__ bias, void* y, int M, int N, int K, Epilogue ep) {
+    const float* __restrict__ bias, void* y, int M, int N, int K, Epilogue ep, int gchunk) {
   using C = Cfg4<BM, BN, WTM, WTN>;
   constexpr bool kScaled = OUT != kOutI32;
   __shared__ int4 lds0[C::kSlots], lds1[C::kSlots], lds2[C::kSlots], lds3[C::kSlots];
@@ -97,9 +100,17 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::kWN;
   const int wn = wave % C::kWN;
-  const int G = K / 64;
+  const int Gall = K / 64;  // groups per row (the tables' row stride)
+  const int g0 = blockIdx.y * gchunk;
+  const int G = min(gchunk, Gall - g0);  // groups of this K slice
   const int KT = G;
   const int QB = K / 2;  // packed bytes per weight row
+  A += (int64_t)g0 * 64;
+  Q += (int64_t)g0 * 32;
+  GS += g0;
+  GB += g0;
+  if (kScaled && gsum != nullptr) gsum += g0;
+  if (OUT == kOutPart) y = reinterpret_cast<float*>(y) + (int64_t)blockIdx.y * M * N;
 
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(A + (int64_t)m0 * K), 0, min(BM, M - m0) * K, 0x00020000);
@@ -147,7 +158,7 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
       const int col = e / kSG, t = e % kSG;
       const int n = n0 + col, g = gbase + t;
       const bool ok = n < N && g < G;
-      const int64_t idx = (int64_t)min(n, N - 1) * G + min(g, G - 1);
+      const int64_t idx = (int64_t)min(n, N - 1) * Gall + min(g, G - 1);
       const uint32_t s = GS[idx], b = GB[idx];
       st_s[u] = ok ? s : 0u;
       st_b[u] = ok ? b : 0u;
@@ -157,7 +168,7 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
       const int e = tid + u * C::kThreads;
       const int row = e / kSG, t = e % kSG;
       const int m = m0 + row, g = gbase + t;
-      const int32_t v = gsum[(int64_t)min(m, M - 1) * G + min(g, G - 1)];
+      const int32_t v = gsum[(int64_t)min(m, M - 1) * Gall + min(g, G - 1)];
       st_a[u] = (m < M && g < G) ? v : 0;
     }
   };
@@ -236,7 +247,7 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int m = m0 + wm * WTM + 16 * j + 4 * fc + r;
-            if (m < M && n < N) reinterpret_cast<int32_t*>(y)[((int64_t)kt * M + m) * N + n] = p[r];
+            if (m < M && n < N) reinterpret_cast<int32_t*>(y)[((int64_t)(g0 + kt) * M + m) * N + n] = p[r];
           }
         }
       }
@@ -378,9 +389,13 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + wm * WTM + 16 * j + 4 * fc + r;
         if (m < M && n < N) {
-          float v = fmaf(sx[m], acc[i][j][r], bv);
-          if (GATED) v = gated1(v, ep.residual, ep.gate, ep.gate_rows, m, n, N);
-          store1<OUT>(y, (int64_t)m * N + n, v);
+          if (OUT == kOutPart) {
+            store1<OUT>(y, (int64_t)m * N + n, acc[i][j][r]);
+          } else {
+            float v = fmaf(sx[m], acc[i][j][r], bv);
+            if (GATED) v = gated1(v, ep.residual, ep.gate, ep.gate_rows, m, n, N);
+            store1<OUT>(y, (int64_t)m * N + n, v);
+          }
         }
       }
     }
@@ -391,21 +406,59 @@ template <int BM, int BN, int WTM, int WTN>
 const char* launch_tile4(const int8_t* a, const float* sx, const int32_t* gsum, const uint8_t* q4,
                          const uint16_t* gs, const uint16_t* gb, const float* bias, void* y,
                          int out, int M, int N, int K, hipStream_t s, const Epilogue& ep,
-                         const char* name) {
+                         const char* name, int splits, int gchunk) {
   using C = Cfg4<BM, BN, WTM, WTN>;
   const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const dim3 grid((unsigned)tiles), block(C::kThreads);
+  const dim3 grid((unsigned)tiles, (unsigned)splits), block(C::kThreads);
+  if (out == kOutPart) {
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutPart, false>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
+    return name;
+  }
   if (ep.active() && out == kOutF32)
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutF32, true>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutF32, true>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
   else if (ep.active() && out == kOutBF16)
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutBF16, true>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutBF16, true>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
   else if (out == kOutF32)
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutF32, false>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutF32, false>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
   else if (out == kOutBF16)
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutBF16, false>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutBF16, false>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
   else
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutI32, false>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutI32, false>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
   return name;
+}
+
+// Fold of a split int4 GEMM: the fp32 slice sums added in slice order,
+// then the unsplit epilogue expression (token scale, bias, gated residual),
+// rounded once to the output type.
+template <int OUT, bool GATED>
+__global__ __launch_bounds__(256) void splitk_fold4(const float* __restrict__ P, int S,
+                                                    const float* __restrict__ sx,
+                                                    const float* __restrict__ bias, void* y,
+                                                    int M, int N, Epilogue ep) {
+  const int64_t MN = (int64_t)M * N;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= MN) return;
+  float acc = P[e];
+  for (int s = 1; s < S; ++s) acc += P[s * MN + e];
+  const int m = (int)(e / N), n = (int)(e % N);
+  float v = fmaf(sx[m], acc, bias != nullptr ? bias[n] : 0.0f);
+  if (GATED) v = gated1(v, ep.residual, ep.gate, ep.gate_rows, m, n, N);
+  if (OUT == kOutF32) reinterpret_cast<float*>(y)[e] = v;
+  else reinterpret_cast<uint16_t*>(y)[e] = (uint16_t)f32_to_bf16_rne(v);
+}
+
+void launch_fold4(const float* P, int S, const float* sx, const float* bias, void* y, int out,
+                  int M, int N, hipStream_t s, const Epilogue& ep) {
+  const dim3 grid((unsigned)(((int64_t)M * N + 255) / 256)), block(256);
+  const bool g = ep.active();
+  if (out == kOutF32 && g)
+    hipLaunchKernelGGL((splitk_fold4<kOutF32, true>), grid, block, 0, s, P, S, sx, bias, y, M, N, ep);
+  else if (out == kOutF32)
+    hipLaunchKernelGGL((splitk_fold4<kOutF32, false>), grid, block, 0, s, P, S, sx, bias, y, M, N, ep);
+  else if (g)
+    hipLaunchKernelGGL((splitk_fold4<kOutBF16, true>), grid, block, 0, s, P, S, sx, bias, y, M, N, ep);
+  else
+    hipLaunchKernelGGL((splitk_fold4<kOutBF16, false>), grid, block, 0, s, P, S, sx, bias, y, M, N, ep);
 }
 
 }  // namespace
@@ -413,14 +466,29 @@ const char* launch_tile4(const int8_t* a, const float* sx, const int32_t* gsum, 
 const char* launch_gemm_w4a8(int tile, const int8_t* a, const float* sx, const int32_t* gsum,
                              const uint8_t* q4, const void* gs, const void* gb,
                              const float* bias, void* y, int out, int M, int N, int K,
-                             hipStream_t s, const Epilogue& ep) {
+                             hipStream_t s, const Epilogue& ep, int splits, float* partials) {
   const uint16_t* hs = reinterpret_cast<const uint16_t*>(gs);
   const uint16_t* hb = reinterpret_cast<const uint16_t*>(gb);
-  if (tile == kTile128x256)
-    return launch_tile4<128, 256, 64, 64>(a, sx, gsum, q4, hs, hb, bias, y, out, M, N, K, s, ep,
-                                          "gemm_w4a8_128x256");
-  return launch_tile4<64, 128, 32, 64>(a, sx, gsum, q4, hs, hb, bias, y, out, M, N, K, s, ep,
-                                       "gemm_w4a8_64x128");
+  int sp = 1, gchunk = K / 64;
+  if (splits > 1) {
+    int64_t chunk = K;
+    sp = split_chunk(K, splits, chunk, kSplitUnitW4);
+    gchunk = (int)(chunk / 64);
+  }
+  // the slices' output: the caller's y for one slice or for the int32
+  // per-group products (each slice writes its own groups), else partials
+  const bool fold = sp > 1 && out != kOutI32;
+  void* dst = fold ? static_cast<void*>(partials) : y;
+  const int dout = fold ? kOutPart : out;
+  const Epilogue dep = fold ? Epilogue() : ep;
+  const char* name =
+      tile == kTile128x256
+          ? launch_tile4<128, 256, 64, 64>(a, sx, gsum, q4, hs, hb, bias, dst, dout, M, N, K, s,
+                                           dep, "gemm_w4a8_128x256", sp, gchunk)
+          : launch_tile4<64, 128, 32, 64>(a, sx, gsum, q4, hs, hb, bias, dst, dout, M, N, K, s,
+                                          dep, "gemm_w4a8_64x128", sp, gchunk);
+  if (fold) launch_fold4(partials, sp, sx, bias, y, out, M, N, s, ep);
+  return name;
 }
 
 }  // namespace kq

@@ -119,7 +119,8 @@ kq_status launch_main(const char* op, int force, kq_wformat fmt, const int8_t* c
                                 (int)N, (int)K, s, ep, r.splits, partials);
     else
       k2 = kq::launch_gemm_w4a8(tile, codes, sx, gsum, reinterpret_cast<const uint8_t*>(wq),
-                                scale, gbias, bias, y, out, (int)M, (int)N, (int)K, s, ep);
+                                scale, gbias, bias, y, out, (int)M, (int)N, (int)K, s, ep,
+                                r.splits, reinterpret_cast<float*>(partials));
   }
   const kq_status st = check_launch(op);
   if (st != KQ_SUCCESS) return st;

@@ -10,7 +10,9 @@
 
 namespace kq {
 
-enum OutKind : int { kOutF32 = 0, kOutBF16 = 1, kOutI32 = 2 };
+// kOutPart (internal): the raw fp32 sums of one K slice of a split int4
+// GEMM, before the token scale and the bias.
+enum OutKind : int { kOutF32 = 0, kOutBF16 = 1, kOutI32 = 2, kOutPart = 3 };
 
 // Optional gated residual epilogue of the linears: out = residual +
 // gate[m / gate_rows] * y, one fma per element before the output rounding.
@@ -38,10 +40,14 @@ const char* launch_gemm_w8a8(int tile, const int8_t* a, const float* sx, const i
                              int splits = 1, int32_t* partials = nullptr);
 
 // W4A8 GEMM: y = sx * sum_g (gs*P + gb*A) + bias (or P per group for I32).
+// splits > 1: K in that many slices of whole 16-group chunks; fp32 slice
+// sums into `partials` [splits][M][N], then a fold kernel applies the token
+// scale and the bias (I32 output: each slice writes its own groups).
 const char* launch_gemm_w4a8(int tile, const int8_t* a, const float* sx, const int32_t* gsum,
                              const uint8_t* q4, const void* gs, const void* gb,
                              const float* bias, void* y, int out, int M, int N, int K,
-                             hipStream_t s, const Epilogue& ep = Epilogue());
+                             hipStream_t s, const Epilogue& ep = Epilogue(),
+                             int splits = 1, float* partials = nullptr);
 
 // GEMV for 1 <= M <= 16 (w4: q is packed int4 with gs/gb; w8: q int8, gs = fp32 [N]).
 const char* launch_gemv(bool w4, const int8_t* a, const float* sx, const int32_t* gsum,

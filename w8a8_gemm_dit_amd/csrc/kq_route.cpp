@@ -81,16 +81,15 @@ kq_status validate_linear(const char* op, int64_t M, int64_t K, int64_t N,
   return KQ_SUCCESS;
 }
 
-int split_chunk(int64_t K, int want, int64_t& chunk) {
-  const int64_t steps = K / 64;
-  if (want < 2 || steps < 2) {
+int split_chunk(int64_t K, int want, int64_t& chunk, int64_t unit) {
+  const int64_t units = (K + unit - 1) / unit;
+  if (want < 2 || units < 2) {
     chunk = K;
     return 1;
   }
-  int64_t cs = (steps + want - 1) / want;  // 64-code steps per slice
-  cs = (cs + 3) / 4 * 4;
-  chunk = cs * 64;
-  return (int)((steps + cs - 1) / cs);
+  const int64_t per = (units + want - 1) / want;  // units per slice
+  chunk = per * unit;
+  return (int)((K + chunk - 1) / chunk);
 }
 
 kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
@@ -141,27 +140,32 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
   // HBM round trip (written, then read by the fold, at ~4 TB/s) and the
   // fold's launch.
   static const double kEff[kNumTiles] = {0.95, 1.0, 0.9, 0.75, 0.45, 1.0, 0.7};
+  // int4 tiles run at about 18% of the INT8 peak (their rescale is
+  // VALU-bound), the int8 ones at about 45%
+  const double cu_rate = (w8 ? 0.45 : 0.18) * 5.0e15 / kSplitCUs;
+  const int64_t unit = w8 ? kSplitUnitW8 : kSplitUnitW4;
   auto model = [&](int32_t t, int sp, int64_t chunk) {
     const TileShape sh = tile_shape(t);
     const int64_t tiles = ((M + sh.bm - 1) / sh.bm) * ((N + sh.bn - 1) / sh.bn);
     const int64_t waves = (tiles * sp + kSplitCUs - 1) / kSplitCUs;
-    const double tile_s = 2.0 * sh.bm * sh.bn * (double)chunk / (8.8e12 * kEff[t]);
+    const double tile_s = 2.0 * sh.bm * sh.bn * (double)chunk / (cu_rate * kEff[t]);
     double cost = (double)waves * tile_s;
     if (sp > 1) cost += 8.0 * sp * (double)M * (double)N / 4.0e12 + 3e-6;
     return cost;
   };
-  // Slices for a tile (int8 weights only: exact int32 partials): the best
-  // modelled count up to kSplitMax with slices of at least kSplitMinK, or
-  // the forced count.
+  // Slices for a tile: the best modelled count up to kSplitMax with
+  // slices of at least kSplitMinK codes, or the forced count.  int8
+  // weights fold exact int32 partials; int4 weights fp32 ones.
   auto best_split = [&](int32_t t, int64_t& chunk) -> int {
     chunk = K;
-    if (!w8 || split_override == 0 || split_override == 1) return 1;
-    if (split_override > 1) return split_chunk(K, std::min(split_override, kSplitMax), chunk);
+    if (split_override == 0 || split_override == 1) return 1;
+    if (split_override > 1)
+      return split_chunk(K, std::min(split_override, kSplitMax), chunk, unit);
     int best_sp = 1;
     double best_cost = model(t, 1, K);
     for (int want = 2; want <= kSplitMax && K / want >= kSplitMinK; ++want) {
       int64_t c;
-      const int sp = split_chunk(K, want, c);
+      const int sp = split_chunk(K, want, c, unit);
       const double cost = model(t, sp, c);
       if (cost < best_cost) {
         best_cost = cost;

@@ -39,15 +39,17 @@ kq_status validate_linear(const char* op, int64_t M, int64_t K, int64_t N,
 
 // Route of a validated linear call.  force: 0 = automatic, 1 = GEMM, 2 = GEMV.
 // tile_override: -1 = automatic, else a GemmTile.  split_override: -1 =
-// automatic (int8 weights only), 0 or 1 = never split K, n > 1 = n slices
-// (int8 weights only; fewer if K is short).
+// automatic, 0 or 1 = never split K, n > 1 = n slices (fewer if K is short).
 kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
                            int force, int tile_override, int split_override = 0);
 
-// K slicing of a split GEMM: slices of `chunk` codes (a multiple of 256, so
-// that only the last slice can end between the kernel's 4-step unrolls);
-// returns the number of slices, at most `want`.
-int split_chunk(int64_t K, int want, int64_t& chunk);
+// K slicing of a split GEMM: slices of `chunk` codes, a multiple of `unit`
+// (int8 weights: 256, so that only the last slice can end between the
+// kernel's 4-step unrolls; int4 weights: 1024, whole 16-group table
+// chunks); returns the number of slices, at most `want`.
+constexpr int64_t kSplitUnitW8 = 256;
+constexpr int64_t kSplitUnitW4 = 1024;
+int split_chunk(int64_t K, int want, int64_t& chunk, int64_t unit = kSplitUnitW8);
 
 // Workspace layout of one linear call.
 struct WorkspaceLayout {
