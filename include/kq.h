@@ -143,7 +143,9 @@ size_t kq_workspace_bytes(int64_t M, int64_t N, int64_t K, kq_wformat fmt);
 /* Launch plan of a linear call; pure host function, no device access.
  * [kquant]: the route decision is one tested function.  Routing: with
  * K <= KQ_GEMV_MAX_K, M <= 16 or N <= 64 (thin N: the GEMM's tiles would
- * leave most of the GPU idle) takes the GEMV unless the environment
+ * leave most of the GPU idle) takes the GEMV, and so does M <= 32 (two
+ * 16-row blocks, measured faster than the GEMM at 5120 x 13824), unless
+ * the environment
  * variable KQ_FORCE_ROUTE=gemm; KQ_FORCE_ROUTE=gemv forces the GEMV (and
  * fails for shapes it cannot take: M > 16 or K > KQ_GEMV_MAX_K).
  * An int8-weight GEMM whose tiles would leave more than half of the 256

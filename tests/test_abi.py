@@ -58,7 +58,9 @@ def test_workspace_layout():
     (16, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 864),
     (4, 512, 16384, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 32),
     (4, 512, 16448, kq.KQ_W8_PER_CHANNEL, "gemm", None, None),
-    (17, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemm", None, None),
+    (17, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 864 * 2),  # two row blocks
+    (32, 13824, 5120, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 864 * 2),
+    (33, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemm", None, None),
     (4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 192), 256),
     (16384, 12288, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 192), 4096),
     (2048, 12288, 4096, kq.KQ_W4_AFFINE_G64, "gemm", (128, 256), 768),

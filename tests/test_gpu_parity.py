@@ -228,6 +228,34 @@ def test_thin_n_linears_take_the_gemv(M, K, N, fmt, kq_env):
     check_bf16(host_bf16_bits(yb), y64, T, f"thin {fmt} bf16")
 
 
+@pytest.mark.parametrize("fmt", ["w8", "w4"])
+@pytest.mark.parametrize("M", [17, 24, 32])
+def test_gemv_route_up_to_32_rows(M, fmt, kq_env):
+    """17..32 rows still take the GEMV kernel (two 16-row blocks, the
+    second ragged), against the oracle."""
+    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_SPLIT=None)
+    K, N = 1024, 1000
+    assert kq.kq_route(M, N, K, kq.KQ_W8_PER_CHANNEL)["kind"] == "gemv"
+    xb, w, b = _problem(M, K, N, seed=M + 17)
+    a, _, _ = oracle.quantize_act(xb)
+    x = dev_bf16(xb)
+    if fmt == "w8":
+        q8, sw = oracle.quantize_w8(w)
+        acc = kq.kq_w8a8_linear(x, dev(q8), dev(sw), out_dtype=torch.int32)
+        yb = kq.kq_w8a8_linear(x, dev(q8), dev(sw), dev(b), out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(acc), oracle.w8a8_acc(a, q8))
+        y64, T = oracle.w8a8_linear_exact(xb, q8, sw, b), oracle.w8a8_magnitude(xb, q8, sw, b)
+    else:
+        p, gs, gb, q = oracle.quantize_w4(w)
+        P = kq.kq_w4a8_linear(x, dev(p), dev(gs), dev(gb), out_dtype=torch.int32)
+        yb = kq.kq_w4a8_linear(x, dev(p), dev(gs), dev(gb), bias=dev(b), out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(P), oracle.w4a8_group_acc(a, q))
+        y64, T = oracle.w4a8_linear_exact(xb, q, gs, gb, b), oracle.w4a8_magnitude(xb, q, gs, gb, b)
+    check_bf16(host_bf16_bits(yb), y64, T, f"gemv {M} rows {fmt}")
+
+
 @pytest.mark.parametrize("M", [3, 8])
 def test_gemv_and_gemm_routes_agree_bitwise(M, kq_env):
     # The same per-group products whichever kernel runs (decode steps stay

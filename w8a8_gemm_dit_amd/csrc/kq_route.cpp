@@ -97,12 +97,15 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
   kq_route_info r{};
   r.splits = 1;
   const bool fits = M <= KQ_GEMV_MAX_M && K <= kGemvMaxK;
+  // Up to kGemvAutoRows rows the GEMV kernel (one weight pass per 16-row
+  // block, the later ones mostly from the caches) still beats the GEMM.
+  const bool small = M <= kGemvAutoRows && K <= kGemvMaxK;
   // Thin N: the GEMM's tiles would leave most CUs idle, while the GEMV
   // kernel's 16x16 blocks over all of K give ceil(N/16)*ceil(M/16)
   // workgroups.
   // (the row blocks are the grid's y dimension, at most 65535)
   const bool thin = N <= kGemvThinN && K <= kGemvMaxK && (M + kGemvRows - 1) / kGemvRows <= 65535;
-  const bool gemv = (force == 2) ? fits : (force == 1) ? false : (M >= 1 && (fits || thin));
+  const bool gemv = (force == 2) ? fits : (force == 1) ? false : (M >= 1 && (small || thin));
   if (gemv) {
     r.kind = KQ_ROUTE_GEMV;
     r.tile_m = kGemvRows;

@@ -75,6 +75,7 @@ constexpr int64_t kSplitMinK = 512;
 constexpr int kGemvCols = 16;
 constexpr int kGemvRows = 16;   // activation rows per GEMV workgroup
 constexpr int kGemvThinN = 64;  // N up to this takes the GEMV at any M
+constexpr int kGemvAutoRows = 32;  // the automatic route's GEMV takes M up to this
 constexpr int kGemvThreads = 512;
 constexpr int64_t kGemvMaxK = KQ_GEMV_MAX_K;
 
