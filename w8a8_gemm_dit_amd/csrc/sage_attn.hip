@@ -40,6 +40,11 @@ constexpr int kKBytes = kSageKTile * kSageD;       // key codes of one step
 constexpr int kVBytes = kSageD * kSageKTile * 2;   // V^T of one step
 constexpr int kSBytes = kSageKTile * 4;            // key scales of one step
 constexpr int kStage = kKBytes + kVBytes + kSBytes;
+// The score accumulators start at the bit pattern of 1.5 * 2^23: an int32
+// result then reads as the float 1.5 * 2^23 + S (exact, |S| <= 128 * 127^2
+// < 2^22), and one exact subtraction replaces the int -> float conversion.
+constexpr int kMagic = 0x4B400000;
+constexpr float kMagicF = 12582912.0f;
 static_assert(kWaves * 16 * kQB == kSageQTile && 8 % kWaves == 0, "query tile split");
 constexpr int kKPerWave = 8 / kWaves;    // 1 KB key-code loads per wavefront
 constexpr int kVPerWave = 16 / kWaves;   // 1 KB V^T loads per wavefront
@@ -137,7 +142,7 @@ __global__ __launch_bounds__(kWaves * 64) void sage_attn_kernel(
     for (int kb = 0; kb < 4; ++kb) {
       const int row = 16 * kb + fr;
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) st[kb][qb] = v4i{0, 0, 0, 0};
+      for (int qb = 0; qb < kQB; ++qb) st[kb][qb] = v4i{kMagic, kMagic, kMagic, kMagic};
 #pragma unroll
       for (int dh = 0; dh < 2; ++dh) {
         const v4i kf = *reinterpret_cast<const v4i*>(ks + row * 128 + (((4 * dh + g) ^ swz(row)) * 16));
@@ -211,9 +216,9 @@ __global__ __launch_bounds__(kWaves * 64) void sage_attn_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             imax = max(imax, st[kb][qb][r]);
-            x[kb][r] = (float)st[kb][qb][r];
+            x[kb][r] = __int_as_float(st[kb][qb][r]) - kMagicF;
           }
-        xmax = (float)imax;
+        xmax = __int_as_float(imax) - kMagicF;
       } else {
         mul = aq[qb];
         xmax = -INFINITY;
@@ -221,7 +226,7 @@ __global__ __launch_bounds__(kWaves * 64) void sage_attn_kernel(
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            x[kb][r] = (float)st[kb][qb][r] * skv[kb][r];
+            x[kb][r] = (__int_as_float(st[kb][qb][r]) - kMagicF) * skv[kb][r];
             if (!MASK || 16 * kb + 4 * g + r < kvalid) xmax = fmaxf(xmax, x[kb][r]);
           }
       }
