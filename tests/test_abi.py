@@ -46,6 +46,9 @@ def test_workspace_layout():
     assert kq.kq_workspace_bytes(0, N, K, kq.KQ_W8_PER_CHANNEL) == 0
     assert kq.kq_workspace_bytes(M, 0, K, kq.KQ_W8_PER_CHANNEL) == 0
     assert kq.kq_workspace_bytes(3, N, 64, kq.KQ_W8_PER_CHANNEL) == 256 + 256
+    # the fused thin-N route stores only the token scales
+    assert kq.kq_workspace_bytes(2048, 48, 5120, kq.KQ_W8_PER_CHANNEL) == al(4 * 2048)
+    assert kq.kq_workspace_bytes(2048, 48, 5120, kq.KQ_W4_AFFINE_G64) == al(4 * 2048)
     # a split GEMM adds its int32 partial sums
     r = kq.kq_route(128, 3072, 12288, kq.KQ_W8_PER_CHANNEL)
     assert r["splits"] > 1
@@ -66,15 +69,20 @@ def test_workspace_layout():
     (2048, 12288, 4096, kq.KQ_W4_AFFINE_G64, "gemm", (128, 256), 768),
     (2048, 4096, 12288, kq.KQ_W4_AFFINE_G64, "gemm", (128, 256), 256),
     (100, 640, 256, kq.KQ_W4_AFFINE_G64, "gemm", (64, 128), 10),
-    (2048, 48, 5120, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 3 * 128),   # thin N
-    (300, 64, 640, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 4 * 19),
+    (2048, 48, 5120, kq.KQ_W8_PER_CHANNEL, "fused", (16, 48), 128),   # thin N: one kernel
+    (300, 64, 640, kq.KQ_W4_AFFINE_G64, "fused", (16, 64), 19),
+    (17, 48, 5120, kq.KQ_W4_AFFINE_G64, "fused", (16, 48), 2),
+    (16, 48, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 3),         # one row block: GEMV
+    (2048, 33, 6144, kq.KQ_W8_PER_CHANNEL, "fused", (16, 48), 128),
+    (2048, 48, 6208, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 3 * 128),  # past the fused K limit
     (300, 65, 640, kq.KQ_W8_PER_CHANNEL, "gemm", (64, 64), 5 * 2),
     (2048, 48, 16448, kq.KQ_W8_PER_CHANNEL, "gemm", (64, 64), 32 * 8),  # 8 K slices
-    (16 * 65535, 48, 128, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 3 * 65535),
-    (16 * 65535 + 1, 48, 128, kq.KQ_W8_PER_CHANNEL, "gemm", None, None),  # grid y limit
+    (16 * 65535, 48, 6208, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 3 * 65535),
+    (16 * 65535 + 1, 48, 6208, kq.KQ_W8_PER_CHANNEL, "gemm", None, None),  # grid y limit
+    (16 * 65535 + 1, 48, 128, kq.KQ_W8_PER_CHANNEL, "fused", (16, 48), 65536),
 ])
 def test_route_decisions(M, N, K, fmt, kind, tile, grid, kq_env):
-    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None)
+    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_FUSE=None)
     r = kq.kq_route(M, N, K, fmt)
     assert r["kind"] == kind
     if tile is not None:
@@ -121,6 +129,14 @@ def test_split_k_lever(kq_env):
     kq_env(KQ_SPLIT="7")
     # 48 steps in slices of ceil(48/7) = 7 -> 8 steps: 6 slices
     assert kq.kq_route(4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL)["splits"] == 6
+
+
+def test_fused_route_lever(kq_env):
+    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_FUSE="0")
+    r = kq.kq_route(2048, 48, 5120, kq.KQ_W8_PER_CHANNEL)
+    assert (r["kind"], r["grid"]) == ("gemv", 3 * 128)
+    kq_env(KQ_FUSE=None, KQ_FORCE_ROUTE="gemm")
+    assert kq.kq_route(2048, 48, 5120, kq.KQ_W8_PER_CHANNEL)["kind"] == "gemm"
 
 
 def test_route_levers(kq_env):

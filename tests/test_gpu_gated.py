@@ -1,6 +1,6 @@
 """GPU parity of the gated residual epilogue (kq_linear_gated):
 out = residual + gate[m // gate_rows] * linear(x), against the oracle's
-fp64 gated_residual_exact, on every route (GEMM tiles, GEMV, thin-N GEMV).
+fp64 gated_residual_exact, on every route (GEMM tiles, GEMV, fused thin N).
 
 Tolerance: the plain linears' bars with the term magnitude widened to
 |residual| + |gate| * T (oracle.gated_magnitude), the scale of an fp32
@@ -57,9 +57,9 @@ def _check(y, out, y64, T, r, g, L, what):
         check_bf16(host_bf16_bits(y), ref, Tg, what)
 
 
-# (M, K, N, route): GEMM with whole and ragged tiles, GEMV, thin-N GEMV
+# (M, K, N, route): GEMM with whole and ragged tiles, GEMV, fused thin N
 SHAPES = [(300, 640, 200, "gemm"), (513, 320, 260, "gemm"), (256, 512, 256, "gemm"),
-          (5, 1024, 200, "gemv"), (16, 256, 130, "gemv"), (300, 512, 48, "gemv"),
+          (5, 1024, 200, "gemv"), (16, 256, 130, "gemv"), (300, 512, 48, "fused"),
           (96, 2112, 272, "gemm")]
 # (residual?, gate_rows or 0 for no gate)
 VARIANTS = [(True, 1), (True, 128), (False, 1), (True, 0), (True, 7)]
@@ -113,7 +113,7 @@ def test_gated_w4_every_tile(M, K, N, tile, out, kq_env):
 
 @pytest.mark.parametrize("fmt", ["w8", "w4"])
 @pytest.mark.parametrize("M,K,N,route", [(512, 512, 512, "gemm"), (300, 320, 260, "gemm"),
-                                          (7, 512, 200, "gemv"), (300, 256, 64, "gemv")])
+                                          (7, 512, 200, "gemv"), (300, 256, 64, "fused")])
 def test_gated_in_place(M, K, N, route, fmt, kq_env):
     """The residual stream updated in place (out is the residual tensor),
     a DiT block's x = x + gate * linear(...)."""

@@ -198,9 +198,10 @@ def test_gemv_w8(M, K, N):
 @pytest.mark.parametrize("fmt", ["w8", "w4"])
 @pytest.mark.parametrize("M,K,N", [(300, 640, 48), (2048, 512, 64), (33, 128, 40), (17, 5120, 16)])
 def test_thin_n_linears_take_the_gemv(M, K, N, fmt, kq_env):
-    """Thin N at any M: 16-row blocks of the GEMV kernel (ragged last
-    block), against the oracle; int32 bit-exact, outputs within tolerance."""
-    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None)
+    """Thin N at any M with the fused route off (KQ_FUSE=0): 16-row blocks
+    of the GEMV kernel (ragged last block) after the quantize kernel,
+    against the oracle; int32 bit-exact, outputs within tolerance."""
+    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_FUSE="0")
     assert kq.kq_route(M, N, K, kq.KQ_W8_PER_CHANNEL)["kind"] == "gemv"
     xb, w, b = _problem(M, K, N, seed=3 * M + K + N)
     a, _, _ = oracle.quantize_act(xb)

@@ -30,7 +30,8 @@ KQ_SUCCESS, KQ_ERR_INVALID_VALUE, KQ_ERR_UNSUPPORTED = 0, 1, 2
 KQ_ERR_NO_DEVICE, KQ_ERR_WORKSPACE, KQ_ERR_LAUNCH = 3, 4, 5
 KQ_W8_PER_CHANNEL, KQ_W4_AFFINE_G64 = 0, 1
 KQ_DTYPE_F32, KQ_DTYPE_BF16, KQ_DTYPE_I32 = 0, 1, 2
-KQ_ROUTE_GEMM, KQ_ROUTE_GEMV = 0, 1
+KQ_ROUTE_GEMM, KQ_ROUTE_GEMV, KQ_ROUTE_FUSED = 0, 1, 2
+_ROUTE_NAMES = {KQ_ROUTE_GEMM: "gemm", KQ_ROUTE_GEMV: "gemv", KQ_ROUTE_FUSED: "fused"}
 KQ_MAX_K = 65536
 KQ_GEMV_MAX_M = 16
 KQ_GEMV_MAX_K = 16384
@@ -169,7 +170,7 @@ def kq_workspace_bytes(M: int, N: int, K: int, fmt: int) -> int:
 def kq_route(M: int, N: int, K: int, fmt: int, out_dtype: int = KQ_DTYPE_BF16) -> dict:
     info = RouteInfo()
     _check(lib().kq_route(M, N, K, fmt, out_dtype, ctypes.byref(info)))
-    return {"kind": "gemv" if info.kind == KQ_ROUTE_GEMV else "gemm", "tile_m": info.tile_m,
+    return {"kind": _ROUTE_NAMES.get(info.kind, "?"), "tile_m": info.tile_m,
             "tile_n": info.tile_n, "threads": info.threads, "grid": info.grid,
             "splits": info.splits}
 

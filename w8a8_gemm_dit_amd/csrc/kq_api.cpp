@@ -12,6 +12,8 @@
 //   KQ_LOG=1            one stderr line per call: op, route, kernels, grid
 //   KQ_FORCE_ROUTE=gemm|gemv   override the M <= 16 GEMV routing
 //   KQ_TILE=256x256|256x192|256x128|128x128|64x64   pin the GEMM tile (A/B runs)
+//   KQ_SPLIT=n          K slices of a GEMM (1: never split)
+//   KQ_FUSE=0           no fused thin-N route (quantize kernel + GEMV instead)
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -55,6 +57,12 @@ int env_split() {
   if (!v || !v[0]) return -1;
   const int n = atoi(v);
   return n >= 1 ? n : -1;
+}
+
+// KQ_FUSE=0 turns the fused thin-N route off.
+bool env_fuse() {
+  const char* v = getenv("KQ_FUSE");
+  return !(v && !strcmp(v, "0"));
 }
 
 bool env_log() {
@@ -165,8 +173,10 @@ kq_status run_linear(const char* op, int force, kq_wformat fmt, const void* x, i
   if (st != KQ_SUCCESS || M == 0 || N == 0) return st;
   if (!aligned16(ws))
     return fail(KQ_ERR_INVALID_VALUE, "[%s] x, weights, y and workspace must be 16-byte aligned", op);
-  const int splits = kq::choose_route(M, N, K, fmt, force, env_tile(), env_split()).splits;
-  const kq::WorkspaceLayout wl = kq::workspace_layout(M, N, K, fmt, splits);
+  const kq_route_info r = kq::choose_route(M, N, K, fmt, force, env_tile(), env_split(), env_fuse());
+  const int splits = r.splits;
+  const bool fused = r.kind == KQ_ROUTE_FUSED;
+  const kq::WorkspaceLayout wl = kq::workspace_layout(M, N, K, fmt, splits, fused);
   if (!ws || ws_bytes < wl.total)
     return fail(KQ_ERR_WORKSPACE, "[%s] workspace of %zu bytes is smaller than the %zu required", op,
                 ws_bytes, wl.total);
@@ -174,6 +184,19 @@ kq_status run_linear(const char* op, int force, kq_wformat fmt, const void* x, i
   if (st != KQ_SUCCESS) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* wsb = reinterpret_cast<char*>(ws);
+  if (fused) {
+    const char* k = kq::launch_thin_fused(fmt == KQ_W4_AFFINE_G64, reinterpret_cast<const uint16_t*>(x),
+                                          reinterpret_cast<float*>(wsb + wl.scale_off), wq, scale,
+                                          gbias, bias, y, out_kind(y_dtype), (int)M, (int)N, (int)K,
+                                          s, ep);
+    st = check_launch(op);
+    if (st != KQ_SUCCESS) return st;
+    if (env_log())
+      fprintf(stderr, "[kq] %s M=%lld N=%lld K=%lld out=%s%s route=fused kernels=%s grid=%lld\n", op,
+              (long long)M, (long long)N, (long long)K, dtype_name(y_dtype),
+              ep.active() ? " gated" : "", k, (long long)r.grid);
+    return KQ_SUCCESS;
+  }
   int8_t* codes = reinterpret_cast<int8_t*>(wsb + wl.codes_off);
   float* sx = reinterpret_cast<float*>(wsb + wl.scale_off);
   int32_t* gsum = fmt == KQ_W4_AFFINE_G64 ? reinterpret_cast<int32_t*>(wsb + wl.gsum_off) : nullptr;
@@ -322,8 +345,9 @@ const char* kq_last_error(void) { return g_last_error.c_str(); }
 
 size_t kq_workspace_bytes(int64_t M, int64_t N, int64_t K, kq_wformat fmt) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  const int splits = kq::choose_route(M, N, K, fmt, env_force_route(), env_tile(), env_split()).splits;
-  return kq::workspace_layout(M, N, K, fmt, splits).total;
+  const kq_route_info r =
+      kq::choose_route(M, N, K, fmt, env_force_route(), env_tile(), env_split(), env_fuse());
+  return kq::workspace_layout(M, N, K, fmt, r.splits, r.kind == KQ_ROUTE_FUSED).total;
 }
 
 kq_status kq_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt, kq_dtype y_dtype,
@@ -339,7 +363,7 @@ kq_status kq_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt, kq_dtype y_d
   if (force == 2 && K > kq::kGemvMaxK)
     return fail(KQ_ERR_UNSUPPORTED, "[kq_route] K=%lld exceeds the GEMV limit %lld", (long long)K,
                 (long long)kq::kGemvMaxK);
-  *out = kq::choose_route(M, N, K, fmt, force, env_tile(), env_split());
+  *out = kq::choose_route(M, N, K, fmt, force, env_tile(), env_split(), env_fuse());
   return KQ_SUCCESS;
 }
 

@@ -55,4 +55,11 @@ const char* launch_gemv(bool w4, const int8_t* a, const float* sx, const int32_t
                         void* y, int out, int M, int N, int K, hipStream_t s,
                         const Epilogue& ep = Epilogue());
 
+// Thin-N linear with the activation quantization inside (N <= 64, K <=
+// kFusedMaxK): reads bf16 x, writes the token scales to sx (if not NULL)
+// and y; same weight arguments as launch_gemv.
+const char* launch_thin_fused(bool w4, const uint16_t* x, float* sx, const void* q, const void* gs,
+                              const void* gb, const float* bias, void* y, int out, int M, int N,
+                              int K, hipStream_t s, const Epilogue& ep = Epilogue());
+
 }  // namespace kq

@@ -9,6 +9,7 @@
 
 #include <cstdio>
 #include <algorithm>
+#include <cstdint>
 #include <cstdlib>
 
 namespace kq {
@@ -93,9 +94,20 @@ int split_chunk(int64_t K, int want, int64_t& chunk, int64_t unit) {
 }
 
 kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
-                           int force, int tile_override, int split_override) {
+                           int force, int tile_override, int split_override, bool fuse) {
   kq_route_info r{};
   r.splits = 1;
+  // Thin N with more than one 16-row block: one kernel quantizes its rows
+  // and covers every column, so x is read once and no codes are stored.
+  if (fuse && force == 0 && N <= kGemvThinN && M > KQ_GEMV_MAX_M && K <= kFusedMaxK &&
+      (M + kFusedRows - 1) / kFusedRows <= INT32_MAX) {
+    r.kind = KQ_ROUTE_FUSED;
+    r.tile_m = kFusedRows;
+    r.tile_n = (int32_t)((N + 15) / 16 * 16);
+    r.threads = kFusedThreads;
+    r.grid = (M + kFusedRows - 1) / kFusedRows;
+    return r;
+  }
   const bool fits = M <= KQ_GEMV_MAX_M && K <= kGemvMaxK;
   // Up to kGemvAutoRows rows the GEMV kernel (one weight pass per 16-row
   // block, the later ones mostly from the caches) still beats the GEMM.
@@ -202,10 +214,16 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
   return r;
 }
 
-WorkspaceLayout workspace_layout(int64_t M, int64_t N, int64_t K, kq_wformat fmt, int splits) {
+WorkspaceLayout workspace_layout(int64_t M, int64_t N, int64_t K, kq_wformat fmt, int splits,
+                                 bool fused) {
   WorkspaceLayout w{};
   if (M <= 0 || K <= 0 || N <= 0) return w;
   size_t off = 0;
+  if (fused) {
+    w.scale_bytes = 4 * (size_t)M;
+    w.total = align256(w.scale_bytes);
+    return w;
+  }
   w.codes_off = off;
   w.codes_bytes = (size_t)M * (size_t)K;
   off = align256(off + w.codes_bytes);

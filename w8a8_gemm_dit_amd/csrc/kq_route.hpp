@@ -40,8 +40,10 @@ kq_status validate_linear(const char* op, int64_t M, int64_t K, int64_t N,
 // Route of a validated linear call.  force: 0 = automatic, 1 = GEMM, 2 = GEMV.
 // tile_override: -1 = automatic, else a GemmTile.  split_override: -1 =
 // automatic, 0 or 1 = never split K, n > 1 = n slices (fewer if K is short).
+// fuse: the call quantizes x itself and may take the fused thin-N kernel.
 kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
-                           int force, int tile_override, int split_override = 0);
+                           int force, int tile_override, int split_override = 0,
+                           bool fuse = false);
 
 // K slicing of a split GEMM: slices of `chunk` codes, a multiple of `unit`
 // (int8 weights: 256, so that only the last slice can end between the
@@ -51,7 +53,8 @@ constexpr int64_t kSplitUnitW8 = 256;
 constexpr int64_t kSplitUnitW4 = 1024;
 int split_chunk(int64_t K, int want, int64_t& chunk, int64_t unit = kSplitUnitW8);
 
-// Workspace layout of one linear call.
+// Workspace layout of one linear call (the fused route keeps only the
+// token scales).
 struct WorkspaceLayout {
   size_t codes_off, codes_bytes;   // int8 [M,K]
   size_t scale_off, scale_bytes;   // fp32 [M]
@@ -60,7 +63,7 @@ struct WorkspaceLayout {
   size_t total;
 };
 WorkspaceLayout workspace_layout(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
-                                 int splits = 1);
+                                 int splits = 1, bool fused = false);
 
 // Split-K policy: the slice count (at most kSplitMax, slices of at least
 // kSplitMinK codes) that minimizes a simple time model of the grid (waves
@@ -78,5 +81,12 @@ constexpr int kGemvThinN = 64;  // N up to this takes the GEMV at any M
 constexpr int kGemvAutoRows = 32;  // the automatic route's GEMV takes M up to this
 constexpr int kGemvThreads = 512;
 constexpr int64_t kGemvMaxK = KQ_GEMV_MAX_K;
+
+// Fused thin-N route (N <= kGemvThinN, M > 16): 16 rows and all columns
+// per workgroup of 16 wavefronts, each holding its K slice of bf16 x in
+// registers, at most 6 groups of 64, so K <= 6144.
+constexpr int kFusedRows = 16;
+constexpr int kFusedThreads = 1024;
+constexpr int64_t kFusedMaxK = 6144;
 
 }  // namespace kq
