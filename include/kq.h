@@ -98,8 +98,9 @@ typedef enum kq_route_kind {
     KQ_ROUTE_GEMM = 0, /* LDS-tiled MFMA GEMM */
     KQ_ROUTE_GEMV = 1, /* weight-streaming register-dequant kernel: 16x16 output
                           blocks over all of K (M <= 16, or thin N) */
-    KQ_ROUTE_FUSED = 2 /* thin N (N <= 64) with M > 16 and K <= 6144 in the
-                          linears: one kernel quantizes 16 rows of x in
+    KQ_ROUTE_FUSED = 2 /* thin N (N <= 64) with M > 16, K <= 6144 and
+                          M*N <= 2^19 (any M for N <= 32) in the
+                          linears: one kernel quantizes 8 rows of x in
                           registers and computes all N columns of them, so x
                           is read once and no codes are stored ([qlip] W8A8
                           bullet: activation quantization inside the kernel) */
@@ -149,9 +150,9 @@ size_t kq_workspace_bytes(int64_t M, int64_t N, int64_t K, kq_wformat fmt);
 
 /* Launch plan of a linear call; pure host function, no device access.
  * [kquant]: the route decision is one tested function.  Routing: N <= 64
- * with M > 16 and K <= 6144 takes the fused thin-N kernel (the activation
- * quantization inside it, one launch; the environment variable KQ_FUSE=0
- * turns this off).  Otherwise, with
+ * with M > 16, K <= 6144 and M*N <= 2^19 (any M for N <= 32) takes the
+ * fused thin-N kernel (the activation quantization inside it, one launch;
+ * the environment variable KQ_FUSE=0 turns this off).  Otherwise, with
  * K <= KQ_GEMV_MAX_K, M <= 16 or N <= 64 (thin N: the GEMM's tiles would
  * leave most of the GPU idle) takes the GEMV, and so does M <= 32 (two
  * 16-row blocks, measured faster than the GEMM at 5120 x 13824), unless

@@ -69,17 +69,19 @@ def test_workspace_layout():
     (2048, 12288, 4096, kq.KQ_W4_AFFINE_G64, "gemm", (128, 256), 768),
     (2048, 4096, 12288, kq.KQ_W4_AFFINE_G64, "gemm", (128, 256), 256),
     (100, 640, 256, kq.KQ_W4_AFFINE_G64, "gemm", (64, 128), 10),
-    (2048, 48, 5120, kq.KQ_W8_PER_CHANNEL, "fused", (16, 48), 128),   # thin N: one kernel
-    (300, 64, 640, kq.KQ_W4_AFFINE_G64, "fused", (16, 64), 19),
-    (17, 48, 5120, kq.KQ_W4_AFFINE_G64, "fused", (16, 48), 2),
+    (2048, 48, 5120, kq.KQ_W8_PER_CHANNEL, "fused", (8, 48), 256),   # thin N: one kernel
+    (300, 64, 640, kq.KQ_W4_AFFINE_G64, "fused", (8, 64), 38),
+    (17, 48, 5120, kq.KQ_W4_AFFINE_G64, "fused", (8, 48), 3),
     (16, 48, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 3),         # one row block: GEMV
-    (2048, 33, 6144, kq.KQ_W8_PER_CHANNEL, "fused", (16, 48), 128),
+    (2048, 33, 6144, kq.KQ_W8_PER_CHANNEL, "fused", (8, 48), 256),
     (2048, 48, 6208, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 3 * 128),  # past the fused K limit
     (300, 65, 640, kq.KQ_W8_PER_CHANNEL, "gemm", (64, 64), 5 * 2),
     (2048, 48, 16448, kq.KQ_W8_PER_CHANNEL, "gemm", (64, 64), 32 * 8),  # 8 K slices
     (16 * 65535, 48, 6208, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 3 * 65535),
     (16 * 65535 + 1, 48, 6208, kq.KQ_W8_PER_CHANNEL, "gemm", None, None),  # grid y limit
-    (16 * 65535 + 1, 48, 128, kq.KQ_W8_PER_CHANNEL, "fused", (16, 48), 65536),
+    (16 * 65535 + 1, 32, 128, kq.KQ_W8_PER_CHANNEL, "fused", (8, 32), 131071),  # N <= 32: any M
+    (8192, 64, 3072, kq.KQ_W8_PER_CHANNEL, "fused", (8, 64), 1024),   # M*N = 2^19
+    (8193, 64, 3072, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 4 * 513),  # past it: two kernels
 ])
 def test_route_decisions(M, N, K, fmt, kind, tile, grid, kq_env):
     kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_FUSE=None)

@@ -1,5 +1,5 @@
 """GPU parity of the fused thin-N route (route kind "fused": the linear's
-kernel quantizes its 16 rows of x itself and covers all N <= 64 columns;
+kernel quantizes its 8 rows of x itself and covers all N <= 64 columns;
 M > 16, K <= 6144) against the oracle, and against the two-kernel route
 (quantize kernel + GEMV, KQ_FUSE=0).
 
@@ -24,7 +24,7 @@ def setup_module(module):
     assert kq.kq_is_available(), "libkq reports no gfx950 device"
 
 
-# (M, K, N): ragged row blocks, 1-4 column blocks (ragged), K from one group
+# (M, K, N): ragged 8-row blocks, 1-4 column blocks (ragged), K from one group
 # (15 idle slices) through uneven slices (17 groups) to the 6144 limit
 SHAPES = [(17, 64, 1), (33, 128, 16), (300, 640, 48), (2048, 512, 64), (100, 1088, 33),
           (65, 5120, 48), (40, 6144, 64), (257, 960, 17), (18, 1024, 40), (31, 192, 5)]
@@ -86,7 +86,7 @@ def _check_all(fmt, xb, w, b, what):
 def test_fused_matches_oracle(M, K, N, fmt, kq_env):
     kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_FUSE=None)
     r = kq.kq_route(M, N, K, _fmt_code(fmt))
-    assert (r["kind"], r["grid"]) == ("fused", -(-M // 16))
+    assert (r["kind"], r["grid"]) == ("fused", -(-M // 8))
     seed = 5 * M + K + 3 * N
     dist = "student_t4" if (M + N) % 2 else "normal"
     xb = synth.random_bf16((M, K), seed=seed, dist=dist)

@@ -100,6 +100,7 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
   // Thin N with more than one 16-row block: one kernel quantizes its rows
   // and covers every column, so x is read once and no codes are stored.
   if (fuse && force == 0 && N <= kGemvThinN && M > KQ_GEMV_MAX_M && K <= kFusedMaxK &&
+      (N <= kFusedAnyM_N || M * N <= kFusedMaxMN) &&
       (M + kFusedRows - 1) / kFusedRows <= INT32_MAX) {
     r.kind = KQ_ROUTE_FUSED;
     r.tile_m = kFusedRows;

@@ -82,11 +82,16 @@ constexpr int kGemvAutoRows = 32;  // the automatic route's GEMV takes M up to t
 constexpr int kGemvThreads = 512;
 constexpr int64_t kGemvMaxK = KQ_GEMV_MAX_K;
 
-// Fused thin-N route (N <= kGemvThinN, M > 16): 16 rows and all columns
+// Fused thin-N route (N <= kGemvThinN, M > 16): 8 rows and all columns
 // per workgroup of 16 wavefronts, each holding its K slice of bf16 x in
-// registers, at most 6 groups of 64, so K <= 6144.
-constexpr int kFusedRows = 16;
+// registers, at most 8 groups of 64, so K <= 6144.  Every workgroup reads
+// all N*K weight bytes, N/16 times the bytes of its x: past M*N = 2^19 the
+// two-kernel route (quantize + GEMV) measured as fast or faster, unless N
+// <= 32.
+constexpr int kFusedRows = 8;
 constexpr int kFusedThreads = 1024;
 constexpr int64_t kFusedMaxK = 6144;
+constexpr int64_t kFusedMaxMN = (int64_t)1 << 19;
+constexpr int kFusedAnyM_N = 32;
 
 }  // namespace kq

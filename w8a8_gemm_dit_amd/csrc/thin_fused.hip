@@ -17,30 +17,35 @@
 //          dot product of one 64-wide group, A the group sum of the codes.
 //
 // gfx950 design (HBM-bound on x):
-//   - a workgroup of 16 wavefronts owns 16 activation rows and all N
-//     columns (up to 4 blocks of 16); the wavefronts split the K groups into
-//     16 contiguous slices of at most 6 groups (K <= 6144);
-//   - each lane loads the 32 bytes of bf16 x that form its MFMA fragment
-//     (row lane%16, k = 16*(lane/16)..+15 of each group of its slice), so
-//     the quantized values are already in operand order.  The two 16-byte
-//     loads of a fragment touch the same lines, so the second hits the L1:
-//     ordinary loads measured 13% faster than non-temporal ones here;
-//   - the codes: the absmax on the bf16 bit patterns (packed 16-bit max),
-//     rint through the 1.5*2^23 shift, bytes packed with v_perm_b32; about
-//     5 VALU operations per element, the kernel's largest cost after the
-//     loads;
-//   - the row absmax: in-lane max, two cross-lane steps over the 4 lanes of
-//     a row, then the 16 slice maxima through LDS;
-//   - the weights (N*K bytes, shared by every workgroup and therefore served
-//     by the L2) are loaded into registers in chunks; the first chunk is in
-//     flight while x arrives;
+//   - a workgroup of 16 wavefronts owns 8 activation rows and all N columns
+//     (up to 4 blocks of 16); the wavefronts split the K groups into 16
+//     contiguous slices, each a whole number of 128-byte weight lines (2
+//     groups of int8 weights, 4 of int4), at most 8 groups (K <= 6144).
+//     Eight rows per workgroup give 256 workgroups at M = 2048;
+//   - x is read with whole lines: lane l loads 16 bytes (8 values) of row
+//     l/8, so one load instruction covers 8 rows x 128 bytes;
+//   - the row absmax: a packed 16-bit max over the bf16 bit patterns (for
+//     finite values the magnitude bits order as |x|), 3 cross-lane steps
+//     over the 8 lanes of a row, then the 16 slice maxima through LDS;
+//   - the codes: rint(x*inv) through the 1.5*2^23 shift (about 5 VALU
+//     operations per element with the max), packed with v_perm_b32, then
+//     moved into MFMA operand order with 4 ds_bpermute per group (lane
+//     m + 16*c takes codes 16c..16c+15 of row m % 8 from the two lanes that
+//     hold them); the MFMA's rows 8-15 repeat rows 0-7 and are discarded;
+//   - the weights (N*K bytes, read by every workgroup, so served by the L2)
+//     stream through a wavefront-private LDS chunk with direct global->LDS
+//     loads: one instruction moves 8 rows x one whole 128-byte line into
+//     the MFMA fragment order.  Loading them into registers instead (16
+//     rows x 64 bytes per instruction, the fragment layout) measured 1.6x
+//     slower for the whole kernel.  The first chunk is issued with x;
 //   - v_mfma_i32_16x16x64_i8 with the codes as the A operand; for int4
 //     weights a second MFMA against an all-ones operand gives the group sums
 //     A exactly;
-//   - the 16 slice partials are reduced through LDS in slice order (exact
-//     int32 for int8 weights), one output element per thread.
-#include <type_traits>
-
+//   - the slices are rotated by the workgroup index, so that the workgroups
+//     do not all ask the same L2 channels for the same weight lines at once;
+//   - the 16 slice partials go to the wavefronts' LDS chunks and are summed
+//     in slice order (exact int32 for int8 weights), one output element per
+//     thread.
 #include "kq_common.hpp"
 #include "kq_launch.hpp"
 #include "kq_route.hpp"
@@ -52,9 +57,12 @@ namespace {
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = kFusedThreads / 64;               // K slices per workgroup
+constexpr int kRows = kFusedRows;                        // activation rows per workgroup
 constexpr int kMaxG = (int)(kFusedMaxK / 64);            // groups per row at most
-constexpr int kMaxGPW = (kMaxG + kWaves - 1) / kWaves;   // groups per slice at most
-static_assert(kFusedRows == 16, "one MFMA row block per workgroup");
+constexpr int kMaxGPW = 8;                               // groups per slice at most
+static_assert(kRows == 8, "lane l of the x loads takes row l/8");
+static_assert((kWaves & (kWaves - 1)) == 0, "slice rotation by masking");
+static_assert(((kMaxG + kWaves - 1) / kWaves + 3) / 4 * 4 <= kMaxGPW, "slices of whole lines");
 
 // W4: int4 weights (gsv/gbv fp16 [N, K/64]); else int8 (gsv fp32 [N]).
 // NB: 16-column blocks (N <= 16*NB).
@@ -63,30 +71,38 @@ __global__ __launch_bounds__(kFusedThreads) void thin_fused_kernel(
     const uint16_t* __restrict__ x, float* __restrict__ sx_out, const void* __restrict__ Wq,
     const void* __restrict__ gsv, const void* __restrict__ gbv, const float* __restrict__ bias,
     void* y, int M, int N, int K, Epilogue ep) {
-  // Weight fragments per chunk: at most 24 registers, two chunks in flight
-  // (VGPR budget of 128 with 16 wavefronts per workgroup; x takes 48).
-  constexpr int kWRegs = W4 ? 2 : 4;  // registers per (group, column block)
-  constexpr int kChCap = 24 / (kWRegs * NB);
-  constexpr int kCh = kChCap < 1 ? 1 : (kChCap > kMaxGPW ? kMaxGPW : kChCap);
+  constexpr int UB = W4 ? 32 : 64;     // bytes of one weight row per group
+  constexpr int LPR = UB / 16;         // DMA lanes per (row, group)
+  constexpr int GPB = 128 / UB;        // groups per 128-byte line = groups per chunk
   constexpr bool kScales = W4 && OUT != kOutI32;
   constexpr int kSL = kScales ? (kMaxG * 16 * NB + kFusedThreads - 1) / kFusedThreads : 1;
-  __shared__ float s_amax[kWaves][16];
-  __shared__ float s_scale[16];
-  __shared__ float s_red[kWaves][NB * 4][64];
+  __shared__ float s_amax[kWaves][kRows];
+  __shared__ float s_scale[kRows];
+  // per wavefront: one chunk of weight lines, [cb][r8][1 KB DMA block]; at
+  // the end its partial sums
+  __shared__ int4 s_w[kWaves][NB * 2 * 64];
   __shared__ uint32_t s_sb[kScales ? kMaxG * 16 * NB : 1];  // [g][n]: scale | offset << 16
+  static_assert(NB * 2 * 1024 >= NB * 4 * 64 * 4, "partial sums fit the chunk");
 
-  const int m0 = blockIdx.x * kFusedRows;
+  const int m0 = blockIdx.x * kRows;
   const int G = K / 64;
+  const int RB = W4 ? K / 2 : K;    // bytes per weight row
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  // wave-uniform (readfirstlane): the slice guards are scalar branches
+  // wave-uniform (readfirstlane): the slice guards are scalar branches and
+  // the LDS DMA bases stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int fr = lane & 15;  // MFMA A row / B column of this lane
-  const int fc = lane >> 4;  // 16-wide k chunk of a group / output row block
-  const int per = (G + kWaves - 1) / kWaves;
-  const int g0 = min(wave * per, G);
+  const int per = ((G + kWaves - 1) / kWaves + GPB - 1) / GPB * GPB;
+  // Slice of this wavefront, rotated by the workgroup index: every
+  // workgroup reads all of the weights.
+  const int slice = (wave + (int)blockIdx.x) & (kWaves - 1);
+  const int g0 = min(slice * per, G);
   const int gn = min(per, G - g0);  // 0 for trailing slices of short K
-  const int m = m0 + fr;            // this lane's activation row
+  const int xr = lane >> 3;         // x loads: row m0 + xr, values 8*xc..8*xc+7 of a group
+  const int xc = lane & 7;
+  const int mx = m0 + xr;
+  const int fr = lane & 15;         // MFMA A row (codes of row fr % 8) / B column
+  const int fc = lane >> 4;         // 16-wide k chunk of a group / output row block
 
   // 1. Scale/offset staging loads (int4): rows 0..N-1 of the [N, G] arrays
   //    are one contiguous run of N*G halves.
@@ -104,69 +120,52 @@ __global__ __launch_bounds__(kFusedThreads) void thin_fused_kernel(
     }
   }
 
-  // 2. x fragments: 16 bf16 of row m per group, k = 16*fc..16*fc+15.
-  v4i xv[kMaxGPW][2];
+  // 2. x: one whole-line load per group (8 rows x 128 bytes per instruction).
+  v4i xv[kMaxGPW];
   {
-    const v4i* xr = reinterpret_cast<const v4i*>(x + (int64_t)min(m, M - 1) * K + 16 * fc);
+    const v4i* xrow = reinterpret_cast<const v4i*>(x + (int64_t)min(mx, M - 1) * K + 8 * xc);
 #pragma unroll
     for (int i = 0; i < kMaxGPW; ++i) {
-      xv[i][0] = v4i{0, 0, 0, 0};
-      xv[i][1] = v4i{0, 0, 0, 0};
-      if (i < gn && m < M) {
-        xv[i][0] = xr[(g0 + i) * 8];
-        xv[i][1] = xr[(g0 + i) * 8 + 1];
-      }
+      xv[i] = v4i{0, 0, 0, 0};
+      if (i < gn && mx < M) xv[i] = xrow[(g0 + i) * 8];
     }
   }
 
-  // 3. Weight fragments of one chunk: column n = 16*cb + fr, the 16 k of
-  //    chunk fc (int8: 16 bytes; int4: 8 bytes, unpacked before use).
-  typedef typename std::conditional<W4, uint2, int4>::type WFrag;
-  WFrag wf[2][kCh][NB];  // chunk c0/kCh goes to wf[(c0/kCh) % 2]
-  auto load_chunk = [&](int c0) {
-    WFrag (&dst)[kCh][NB] = wf[(c0 / kCh) & 1];
+  // 3. Weight DMA of one chunk (the GPB groups from g0 + c): the descriptor
+  //    covers rows 0..N-1, so rows past N read as zero; lane l moves the 16
+  //    bytes of (group l/(8*LPR), row (l/LPR)%8, piece l%LPR) of its block
+  //    to LDS byte 16*l of the block, which puts (row r, group i, chunk fc)
+  //    at block (cb, r/8), byte i*8*UB + (r%8)*UB + fc*UB/4: the fragment
+  //    order.  Bytes past the slice or past K (the next row's, or zeros past
+  //    the last) land in groups that are never read.
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(Wq), 0, N * RB, 0x00020000);
+  const int voff = ((lane / LPR) & 7) * RB + (lane / (8 * LPR)) * UB + (lane % LPR) * 16;
+  auto issue = [&](int c) {
 #pragma unroll
-    for (int i = 0; i < kCh; ++i) {
+    for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
-      for (int cb = 0; cb < NB; ++cb) {
-        const int n = 16 * cb + fr;
-        const int g = g0 + c0 + i;
-        if constexpr (W4) {
-          uint2 v = make_uint2(0, 0);
-          if (c0 + i < gn && n < N)
-            v = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(Wq) +
-                                                (int64_t)n * (K / 2) + g * 32 + 8 * fc);
-          dst[i][cb] = v;
-        } else {
-          int4 v = make_int4(0, 0, 0, 0);
-          if (c0 + i < gn && n < N)
-            v = *reinterpret_cast<const int4*>(reinterpret_cast<const int8_t*>(Wq) +
-                                               (int64_t)n * K + g * 64 + 16 * fc);
-          dst[i][cb] = v;
-        }
+      for (int r8 = 0; r8 < 2; ++r8) {
+        lds_ptr_t dst = (lds_ptr_t)(&s_w[wave][(cb * 2 + r8) * 64]);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, voff,
+                                                 (16 * cb + 8 * r8) * RB + (g0 + c) * UB, 0, 0);
       }
-    }
   };
-  load_chunk(0);
+  if (gn > 0) issue(0);
 
-  // 4. Row absmax over the whole row: in-lane, then the 4 lanes of the row,
-  //    then the 16 slices.
-  //    For finite values |x| orders as its magnitude bits, so the max runs
-  //    on the bf16 bit patterns, two at a time (exact, and no fp32 copy of x
-  //    stays live).
-  u16x2 mx = u16x2{0, 0};
+  // 4. Row absmax over the whole row: in-lane (two values at a time, on the
+  //    bit patterns), then the 8 lanes of the row, then the 16 slices.
+  u16x2 mxb = u16x2{0, 0};
 #pragma unroll
   for (int i = 0; i < kMaxGPW; ++i)
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, (uint32_t)xv[i][h][j] & 0x7FFF7FFFu));
-  const uint32_t mbits = max((uint32_t)mx.x, (uint32_t)mx.y);
-  float amax = bf16_to_f32(mbits);
-  amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
-  amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-  if (fc == 0) s_amax[wave][fr] = amax;
+    for (int j = 0; j < 4; ++j)
+      mxb = __builtin_elementwise_max(mxb, __builtin_bit_cast(u16x2, (uint32_t)xv[i][j] & 0x7FFF7FFFu));
+  float amax = bf16_to_f32(max((uint32_t)mxb.x, (uint32_t)mxb.y));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
+  if (xc == 0) s_amax[wave][xr] = amax;
   if (kScales) {
 #pragma unroll
     for (int j = 0; j < kSL; ++j) {
@@ -177,48 +176,52 @@ __global__ __launch_bounds__(kFusedThreads) void thin_fused_kernel(
       }
     }
   }
-  wait_vm_lgkm0<63>();  // LDS writes done; weight loads may still fly
+  wait_vm_lgkm0<63>();  // LDS writes done; the weight DMA may still fly
   barrier_nofence();
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) amax = fmaxf(amax, s_amax[w][fr]);
+  for (int w = 0; w < kWaves; ++w) amax = fmaxf(amax, s_amax[w][xr]);
   float scale;
   const float inv = row_inv(amax, scale);
-  if (wave == 0 && fc == 0) {
-    s_scale[fr] = scale;
-    if (sx_out != nullptr && m < M) sx_out[m] = scale;
+  if (wave == 0 && xc == 0) {
+    s_scale[xr] = scale;
+    if (sx_out != nullptr && mx < M) sx_out[mx] = scale;
   }
 
-  // 5. Codes in MFMA operand order.  rint(x*inv) through the 1.5*2^23
-  //    shift: the product rounds once, and adding 1.5*2^23 (exact spacing 1
-  //    at that magnitude) rounds it to the nearest integer, ties to even,
-  //    leaving the code in the low byte of the sum's bits.  No clamp: with
-  //    inv = fp32(127/amax), |x*inv| <= 127*(1 + 2^-24)^2 < 127.5.
+  // 5. Codes.  rint(x*inv) through the 1.5*2^23 shift: the product rounds
+  //    once, and adding 1.5*2^23 (exact spacing 1 at that magnitude) rounds
+  //    it to the nearest integer, ties to even, leaving the code in the low
+  //    byte of the sum's bits.  No clamp: with inv = fp32(127/amax),
+  //    |x*inv| <= 127*(1 + 2^-24)^2 < 127.5.  Then operand order: lane
+  //    fr + 16*fc takes its 16 codes from lanes 8*(fr%8) + 2*fc and + 1.
+  const int src0 = 4 * (8 * (fr & 7) + 2 * fc);  // ds_bpermute byte address
+  const int src1 = src0 + 4;
   v4i fa[kMaxGPW];
 #pragma unroll
   for (int i = 0; i < kMaxGPW; ++i) {
 #pragma clang fp contract(off)  // two roundings, as the rule has them: no fma
-    uint32_t t[16];
+    uint32_t t[8];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = (uint32_t)xv[i][j];
+      const float p0 = bf16_to_f32(w & 0xFFFFu) * inv;
+      const float p1 = bf16_to_f32(w >> 16) * inv;
+      t[2 * j] = __float_as_uint(p0 + 12582912.0f);
+      t[2 * j + 1] = __float_as_uint(p1 + 12582912.0f);
+    }
+    int d[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = (uint32_t)xv[i][h][j];
-        const float p0 = bf16_to_f32(w & 0xFFFFu) * inv;
-        const float p1 = bf16_to_f32(w >> 16) * inv;
-        t[8 * h + 2 * j] = __float_as_uint(p0 + 12582912.0f);
-        t[8 * h + 2 * j + 1] = __float_as_uint(p1 + 12582912.0f);
-      }
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
+    for (int q = 0; q < 2; ++q) {
       // v_perm_b32 selectors: bytes 0-3 come from the second operand, 4-7
       // from the first, 0x0c gives zero
-      const uint32_t lo = __builtin_amdgcn_perm(t[4 * d + 1], t[4 * d], 0x0c0c0400u);
-      const uint32_t hi = __builtin_amdgcn_perm(t[4 * d + 3], t[4 * d + 2], 0x0c0c0400u);
-      fa[i][d] = (int)__builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      const uint32_t lo = __builtin_amdgcn_perm(t[4 * q + 1], t[4 * q], 0x0c0c0400u);
+      const uint32_t hi = __builtin_amdgcn_perm(t[4 * q + 3], t[4 * q + 2], 0x0c0c0400u);
+      d[q] = (int)__builtin_amdgcn_perm(hi, lo, 0x05040100u);
     }
+    fa[i] = v4i{__builtin_amdgcn_ds_bpermute(src0, d[0]), __builtin_amdgcn_ds_bpermute(src0, d[1]),
+                __builtin_amdgcn_ds_bpermute(src1, d[0]), __builtin_amdgcn_ds_bpermute(src1, d[1])};
   }
 
-  // 6. Products over the slice, one weight chunk at a time.
+  // 6. Products over the slice, one chunk of weight lines at a time.
   v4i iacc[NB];
   v4f facc[NB];
 #pragma unroll
@@ -227,33 +230,38 @@ __global__ __launch_bounds__(kFusedThreads) void thin_fused_kernel(
     facc[cb] = v4f{0.f, 0.f, 0.f, 0.f};
   }
   const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
-  // the later chunks' loads stay below this point (hoisted, they would
-  // hold registers next to x)
-  __builtin_amdgcn_sched_barrier(0);
+  const char* wl = reinterpret_cast<const char*>(&s_w[wave][0]) + (fr >> 3) * 1024 +
+                   (fr & 7) * UB + fc * (UB / 4);
 #pragma unroll
-  for (int c0 = 0; c0 < kMaxGPW; c0 += kCh) {
-    if (c0 + kCh < kMaxGPW) load_chunk(c0 + kCh);
-    const WFrag (&cur)[kCh][NB] = wf[(c0 / kCh) & 1];
+  for (int c = 0; c < kMaxGPW; c += GPB) {
+    if (c >= gn) break;
+    if (c > 0) {
+      wait_vm_lgkm0<63>();  // fragment reads of the last chunk done before the DMA reuses it
+      issue(c);
+    }
+    wait_vm_lgkm0<0>();     // this chunk has landed
 #pragma unroll
-    for (int i = 0; i < kCh; ++i) {
-      const int gi = c0 + i;
-      if (gi >= kMaxGPW || gi >= gn) continue;
+    for (int i = 0; i < GPB; ++i) {
+      const int gi = c + i;
+      if (gi >= gn) continue;
       const int g = g0 + gi;
+      const v4i fa_g = fa[gi];
       if constexpr (W4) {
         v4i as = v4i{0, 0, 0, 0};
-        if (OUT != kOutI32) as = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[gi], ones, as, 0, 0, 0);
+        if (OUT != kOutI32) as = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa_g, ones, as, 0, 0, 0);
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) {
-          const uint2 wv = cur[i][cb];
+          const uint2 wv = *reinterpret_cast<const uint2*>(wl + cb * 2048 + i * 8 * UB);
           uint32_t u0, u1, u2, u3;
           unpack8_u4(wv.x, u0, u1);
           unpack8_u4(wv.y, u2, u3);
           const v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-              fa[gi], v4i{(int)u0, (int)u1, (int)u2, (int)u3}, v4i{0, 0, 0, 0}, 0, 0, 0);
+              fa_g, v4i{(int)u0, (int)u1, (int)u2, (int)u3}, v4i{0, 0, 0, 0}, 0, 0, 0);
           const int n = 16 * cb + fr;
           if (OUT == kOutI32) {
             // debug output: P of every group, [G, M, N]; p[r] = P[g, m0 + 4*fc + r, n]
-            if (n < N) {
+            // (lanes with fc >= 2 hold the repeated rows)
+            if (n < N && fc < 2) {
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const int mr = m0 + 4 * fc + r;
@@ -272,8 +280,8 @@ __global__ __launch_bounds__(kFusedThreads) void thin_fused_kernel(
       } else {
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) {
-          const int4 wv = cur[i][cb];
-          iacc[cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[gi], v4i{wv.x, wv.y, wv.z, wv.w},
+          const int4 wv = *reinterpret_cast<const int4*>(wl + cb * 2048 + i * 8 * UB);
+          iacc[cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa_g, v4i{wv.x, wv.y, wv.z, wv.w},
                                                            iacc[cb], 0, 0, 0);
         }
       }
@@ -281,17 +289,22 @@ __global__ __launch_bounds__(kFusedThreads) void thin_fused_kernel(
   }
   if (W4 && OUT == kOutI32) return;
 
-  // 7. Slice partials -> LDS; thread t then sums element t over the slices
-  //    in order and applies the epilogue.  Element e = (cb*4 + r)*64 + l is
-  //    output row m0 + 4*(l/16) + r, column 16*cb + l%16.
+  // 7. Slice partials -> the wavefront's chunk buffer (its reads are done);
+  //    thread t then sums element t over the slices in order and applies
+  //    the epilogue.  Element e = (cb*4 + r)*64 + l is output row
+  //    m0 + 4*(l/16) + r (l < 32; the rest repeat rows), column 16*cb + l%16.
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  float* part = reinterpret_cast<float*>(&s_w[wave][0]);
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      s_red[wave][cb * 4 + r][lane] = W4 ? facc[cb][r] : __int_as_float(iacc[cb][r]);
+      part[(cb * 4 + r) * 64 + lane] = W4 ? facc[cb][r] : __int_as_float(iacc[cb][r]);
   __syncthreads();
   if (tid >= NB * 256) return;
   const int j = tid >> 6, l = tid & 63;
+  if (l >= 32) return;
   const int cb = j >> 2, r = j & 3;
   const int mo = m0 + 4 * (l >> 4) + r;
   const int n = 16 * cb + (l & 15);
@@ -299,9 +312,11 @@ __global__ __launch_bounds__(kFusedThreads) void thin_fused_kernel(
   float fs = 0.0f;
   int32_t is = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    if (W4) fs += s_red[w][j][l];
-    else is += __float_as_int(s_red[w][j][l]);
+  for (int sl = 0; sl < kWaves; ++sl) {  // in slice order
+    const int w = (sl - (int)blockIdx.x) & (kWaves - 1);
+    const float v = reinterpret_cast<const float*>(&s_w[w][0])[j * 64 + l];
+    if (W4) fs += v;
+    else is += __float_as_int(v);
   }
   const int64_t idx = (int64_t)mo * N + n;
   if (OUT == kOutI32) {
