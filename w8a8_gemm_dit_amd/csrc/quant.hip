@@ -14,7 +14,10 @@
 // The activation kernel is HBM-bound (2 bytes in, 1 byte out per element):
 // one wavefront per row, 16-byte coalesced non-temporal loads kept in
 // registers, a wavefront max-reduction, then 8-byte code stores from the
-// same registers.
+// same registers.  The per-element VALU work is kept small because it runs
+// after the row has arrived: the absmax on the bf16 bit patterns, rint by
+// the 1.5*2^23 shift, codes packed with v_perm_b32, group sums with
+// v_dot4_i32_i8.
 #include <float.h>
 
 #include "kq_common.hpp"
@@ -26,28 +29,52 @@ namespace {
 
 constexpr int kRowsPerBlock = 4;  // one wavefront per row, 4 waves per block
 
-// Quantize 8 bf16 values held in a uint4; returns 8 codes as uint2 and their sum.
+// Quantize 8 bf16 values held in a uint4; returns 8 codes as uint2 and their
+// sum.  rint(x*inv) through the 1.5*2^23 shift: the product rounds once, and
+// adding 1.5*2^23 (exact spacing 1 at that magnitude) rounds it to the
+// nearest integer, ties to even, leaving the code in the low byte of the
+// sum's bits.  The clamp to +-127 never binds: inv = fp32(127/amax) gives
+// |x*inv| <= 127*(1 + 2^-24)^2 < 127.5 (and inv = 0 gives 0).
 __device__ __forceinline__ uint2 quant8(const uint4 v, float inv, int& sum) {
+#pragma clang fp contract(off)  // two roundings, as the rule has them: no fma
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  int c[8];
+  uint32_t t[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    c[2 * i] = quant_code(bf16_to_f32(w[i] & 0xFFFFu), inv);
-    c[2 * i + 1] = quant_code(bf16_to_f32(w[i] >> 16), inv);
+    const float p0 = bf16_to_f32(w[i] & 0xFFFFu) * inv;
+    const float p1 = bf16_to_f32(w[i] >> 16) * inv;
+    t[2 * i] = __float_as_uint(p0 + 12582912.0f);
+    t[2 * i + 1] = __float_as_uint(p1 + 12582912.0f);
   }
-  sum = c[0] + c[1] + c[2] + c[3] + c[4] + c[5] + c[6] + c[7];
-  return make_uint2(pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7]));
+  // v_perm_b32 selectors: bytes 0-3 come from the second operand, 4-7 from
+  // the first, 0x0c gives zero
+  uint32_t d[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t lo = __builtin_amdgcn_perm(t[4 * q + 1], t[4 * q], 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(t[4 * q + 3], t[4 * q + 2], 0x0c0c0400u);
+    d[q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+  }
+  // the codes' sum: two signed 4-way byte dot products against ones
+  sum = __builtin_amdgcn_sdot4((int)d[1], 0x01010101, __builtin_amdgcn_sdot4((int)d[0], 0x01010101, 0, false),
+                               false);
+  return make_uint2(d[0], d[1]);
 }
 
-__device__ __forceinline__ float absmax8(const uint4 v) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m = fmaxf(m, fabsf(bf16_to_f32(w[i] & 0xFFFFu)));
-    m = fmaxf(m, fabsf(bf16_to_f32(w[i] >> 16)));
-  }
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Running max of |x| over 8 bf16 values, two at a time on the bit patterns:
+// for finite values the magnitude bits order as |x|.
+__device__ __forceinline__ u16x2 absmax8_bits(u16x2 m, const uint4 v) {
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu));
   return m;
+}
+
+__device__ __forceinline__ float bits_to_amax(u16x2 m) {
+  return bf16_to_f32(max((uint32_t)m.x, (uint32_t)m.y));
 }
 
 // Sum over the 8 aligned lanes of a group (lanes 8q..8q+7).
@@ -72,16 +99,16 @@ __global__ __launch_bounds__(256) void quant_act_regs(
   // than ordinary ones for this read-2-bytes/write-1-byte stream.
   const v4i* xr = reinterpret_cast<const v4i*>(x + row * (int64_t)K);
   uint4 v[CH];
-  float amax = 0.0f;
+  u16x2 mb = u16x2{0, 0};
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
     const int c = lane + 64 * j;
     v4i t = v4i{0, 0, 0, 0};
     if (c < nch) t = __builtin_nontemporal_load(xr + c);
     v[j] = make_uint4((uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w);
-    amax = fmaxf(amax, absmax8(v[j]));
+    mb = absmax8_bits(mb, v[j]);
   }
-  amax = wave_max(amax);
+  const float amax = wave_max(bits_to_amax(mb));
   float scale;
   const float inv = row_inv(amax, scale);
   if (lane == 0) sx[row] = scale;
@@ -109,9 +136,9 @@ __global__ __launch_bounds__(256) void quant_act_stream(
   if (row >= M) return;
   const int nch = K >> 3;
   const uint4* xr = reinterpret_cast<const uint4*>(x + row * (int64_t)K);
-  float amax = 0.0f;
-  for (int c = lane; c < nch; c += 64) amax = fmaxf(amax, absmax8(xr[c]));
-  amax = wave_max(amax);
+  u16x2 mb = u16x2{0, 0};
+  for (int c = lane; c < nch; c += 64) mb = absmax8_bits(mb, xr[c]);
+  const float amax = wave_max(bits_to_amax(mb));
   float scale;
   const float inv = row_inv(amax, scale);
   if (lane == 0) sx[row] = scale;
