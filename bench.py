@@ -23,6 +23,7 @@ build targets one GPU.
 from __future__ import annotations
 
 import argparse
+import contextlib
 import hashlib
 import json
 import math
@@ -62,6 +63,20 @@ def algorithmic_bytes(wl, M=None) -> int:
     return x + w + 4 * wl.N + y
 
 
+@contextlib.contextmanager
+def fuse_off():
+    """KQ_FUSE=0 for the duration: the linears take the two-kernel routes."""
+    prev = os.environ.get("KQ_FUSE")
+    os.environ["KQ_FUSE"] = "0"
+    try:
+        yield
+    finally:
+        if prev is None:
+            del os.environ["KQ_FUSE"]
+        else:
+            os.environ["KQ_FUSE"] = prev
+
+
 class Prepared:
     """Device-resident inputs of one workload, in R rotation copies."""
 
@@ -81,7 +96,11 @@ class Prepared:
         self.fmt = fmt
         wq, sc, gb = kq.kq_quantize_weights(wd, fmt)
         del wd
-        ws_bytes = kq.kq_workspace_bytes(wl.M, wl.N, wl.K, fmt)
+        # room for either route: the fused thin-N route keeps only the token
+        # scales, the two-kernel route (timed beside it) the codes as well
+        with fuse_off():
+            ws_two = kq.kq_workspace_bytes(wl.M, wl.N, wl.K, fmt)
+        ws_bytes = max(ws_two, kq.kq_workspace_bytes(wl.M, wl.N, wl.K, fmt))
         ysz = wl.M * wl.N * (4 if wl.out == "f32" else 2)
         per_copy = (x0.numel() * 2 + wq.numel() + sc.numel() * sc.element_size()
                     + (0 if gb is None else gb.numel() * 2) + 4 * wl.N + ysz + ws_bytes)
@@ -477,9 +496,17 @@ def main() -> int:
             for i in range(3):
                 pw.step(i)
             t = graph_time(pw.step, steps_x)
-            tg = graph_time(pw.gemm, steps_x)
-            gbs = algorithmic_bytes(w) / (t * 1e-3) / 1e9
             r = kq.kq_route(w.M, w.N, w.K, pw.fmt)
+            unfused = None
+            if r["kind"] == "fused":
+                # one kernel per call: the call is the kernel; the two-kernel
+                # route (quantize + GEMV) is timed beside it
+                tg = t
+                with fuse_off():
+                    unfused = graph_time(pw.step, steps_x)
+            else:
+                tg = graph_time(pw.gemm, steps_x)
+            gbs = algorithmic_bytes(w) / (t * 1e-3) / 1e9
             extra[name] = {
                 "ms_per_call": round(t, 5), "kernel_ms": round(tg, 5),
                 "route": r["kind"], "tile": f"{r['tile_m']}x{r['tile_n']}",
@@ -488,6 +515,8 @@ def main() -> int:
                 "kernel_tops": round(w.ops / (tg * 1e-3) / 1e12, 2),
                 "gbs": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
             }
+            if unfused is not None:
+                extra[name]["two_kernel_ms_per_call"] = round(unfused, 5)
             log(f"{name}: {t * 1e3:.2f} us/call ({extra[name]['tops']} TOPS, {gbs:.0f} GB/s)")
             del pw
             torch.cuda.empty_cache()
