@@ -96,11 +96,7 @@ class Prepared:
         self.fmt = fmt
         wq, sc, gb = kq.kq_quantize_weights(wd, fmt)
         del wd
-        # room for either route: the fused thin-N route keeps only the token
-        # scales, the two-kernel route (timed beside it) the codes as well
-        with fuse_off():
-            ws_two = kq.kq_workspace_bytes(wl.M, wl.N, wl.K, fmt)
-        ws_bytes = max(ws_two, kq.kq_workspace_bytes(wl.M, wl.N, wl.K, fmt))
+        ws_bytes = kq.kq_workspace_bytes(wl.M, wl.N, wl.K, fmt)  # any route of the shape
         ysz = wl.M * wl.N * (4 if wl.out == "f32" else 2)
         per_copy = (x0.numel() * 2 + wq.numel() + sc.numel() * sc.element_size()
                     + (0 if gb is None else gb.numel() * 2) + 4 * wl.N + ysz + ws_bytes)

@@ -98,12 +98,14 @@ typedef enum kq_route_kind {
     KQ_ROUTE_GEMM = 0, /* LDS-tiled MFMA GEMM */
     KQ_ROUTE_GEMV = 1, /* weight-streaming register-dequant kernel: 16x16 output
                           blocks over all of K (M <= 16, or thin N) */
-    KQ_ROUTE_FUSED = 2 /* thin N (N <= 64) with M > 16, K <= 6144 and
-                          M*N <= 2^19 (any M for N <= 32) in the
-                          linears: one kernel quantizes 8 rows of x in
-                          registers and computes all N columns of them, so x
-                          is read once and no codes are stored ([qlip] W8A8
-                          bullet: activation quantization inside the kernel) */
+    KQ_ROUTE_FUSED = 2 /* the linears' activation quantization inside the
+                          product kernel, one launch and no codes stored
+                          ([qlip] W8A8 bullet: quantization inside the
+                          kernel), K <= 6144: M <= 4 on the GEMV kernel
+                          (which quantizes its rows in its prologue), and
+                          thin N (N <= 64) with M > 16 and M*N <= 2^19 (any M
+                          for N <= 32), where one kernel quantizes 8 rows of
+                          x in registers and computes all N columns of them */
 } kq_route_kind;
 
 /* Launch plan chosen for one linear call (see kq_route). */
@@ -142,17 +144,20 @@ const char* kq_last_error(void);
  * needs: int8 activation codes (M*K), fp32 token scales (4*M), for the int4
  * format the per-group code sums (4*M*K/64), and when the route splits K
  * (kq_route_info.splits > 1) the int32 partial sums (4*splits*M*N), each
- * region 256-byte aligned.  The fused thin-N route (KQ_ROUTE_FUSED) stores
- * no codes: its workspace is the token scales alone, at offset 0.  Returns
- * 0 for M == 0 or N == 0.  Pure host function; it reads the same
- * environment levers as the route. */
+ * region 256-byte aligned.  The fused routes (KQ_ROUTE_FUSED) store no
+ * codes and use only 4*M bytes of token scales at offset 0; the size
+ * returned still covers the two-kernel route of the same shape, so one
+ * workspace serves every linear entry point (kq_gemv_small_m included) and
+ * KQ_FUSE setting.  Returns 0 for M == 0 or N == 0.  Pure host function; it
+ * reads the same environment levers as the route. */
 size_t kq_workspace_bytes(int64_t M, int64_t N, int64_t K, kq_wformat fmt);
 
 /* Launch plan of a linear call; pure host function, no device access.
- * [kquant]: the route decision is one tested function.  Routing: N <= 64
- * with M > 16, K <= 6144 and M*N <= 2^19 (any M for N <= 32) takes the
- * fused thin-N kernel (the activation quantization inside it, one launch;
- * the environment variable KQ_FUSE=0 turns this off).  Otherwise, with
+ * [kquant]: the route decision is one tested function.  Routing: with
+ * K <= 6144, M <= 4 takes the GEMV with the activation quantization in its
+ * prologue, and N <= 64 with M > 16 and M*N <= 2^19 (any M for N <= 32)
+ * the fused thin-N kernel (one launch each; the environment variable
+ * KQ_FUSE=0 turns both off).  Otherwise, with
  * K <= KQ_GEMV_MAX_K, M <= 16 or N <= 64 (thin N: the GEMM's tiles would
  * leave most of the GPU idle) takes the GEMV, and so does M <= 32 (two
  * 16-row blocks, measured faster than the GEMM at 5120 x 13824), unless

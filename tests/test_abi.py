@@ -46,9 +46,12 @@ def test_workspace_layout():
     assert kq.kq_workspace_bytes(0, N, K, kq.KQ_W8_PER_CHANNEL) == 0
     assert kq.kq_workspace_bytes(M, 0, K, kq.KQ_W8_PER_CHANNEL) == 0
     assert kq.kq_workspace_bytes(3, N, 64, kq.KQ_W8_PER_CHANNEL) == 256 + 256
-    # the fused thin-N route stores only the token scales
-    assert kq.kq_workspace_bytes(2048, 48, 5120, kq.KQ_W8_PER_CHANNEL) == al(4 * 2048)
-    assert kq.kq_workspace_bytes(2048, 48, 5120, kq.KQ_W4_AFFINE_G64) == al(4 * 2048)
+    # the fused routes use only the scales, but the size covers the
+    # two-kernel route of the same shape
+    assert kq.kq_route(2048, 48, 5120, kq.KQ_W8_PER_CHANNEL)["kind"] == "fused"
+    assert kq.kq_workspace_bytes(2048, 48, 5120, kq.KQ_W8_PER_CHANNEL) == al(2048 * 5120) + al(4 * 2048)
+    assert kq.kq_workspace_bytes(2048, 48, 5120, kq.KQ_W4_AFFINE_G64) == \
+        al(2048 * 5120) + al(4 * 2048) + al(4 * 2048 * 80)
     # a split GEMM adds its int32 partial sums
     r = kq.kq_route(128, 3072, 12288, kq.KQ_W8_PER_CHANNEL)
     assert r["splits"] > 1
@@ -57,7 +60,10 @@ def test_workspace_layout():
 
 
 @pytest.mark.parametrize("M,N,K,fmt,kind,tile,grid", [
-    (1, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 864),
+    (1, 13824, 5120, kq.KQ_W4_AFFINE_G64, "fused", (4, 16), 864),   # GEMV quantizing x itself
+    (4, 18432, 3072, kq.KQ_W8_PER_CHANNEL, "fused", (4, 16), 1152),
+    (4, 512, 6208, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 32),      # past its K limit
+    (5, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 864),
     (16, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 864),
     (4, 512, 16384, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 32),
     (4, 512, 16448, kq.KQ_W8_PER_CHANNEL, "gemm", None, None),
@@ -137,6 +143,8 @@ def test_fused_route_lever(kq_env):
     kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_FUSE="0")
     r = kq.kq_route(2048, 48, 5120, kq.KQ_W8_PER_CHANNEL)
     assert (r["kind"], r["grid"]) == ("gemv", 3 * 128)
+    assert kq.kq_route(1, 13824, 5120, kq.KQ_W4_AFFINE_G64)["kind"] == "gemv"
+    assert kq.kq_workspace_bytes(3, 3072, 64, kq.KQ_W8_PER_CHANNEL) == 256 + 256
     kq_env(KQ_FUSE=None, KQ_FORCE_ROUTE="gemm")
     assert kq.kq_route(2048, 48, 5120, kq.KQ_W8_PER_CHANNEL)["kind"] == "gemm"
 

@@ -1,7 +1,8 @@
-"""GPU parity of the fused thin-N route (route kind "fused": the linear's
-kernel quantizes its 8 rows of x itself and covers all N <= 64 columns;
-M > 16, K <= 6144) against the oracle, and against the two-kernel route
-(quantize kernel + GEMV, KQ_FUSE=0).
+"""GPU parity of the fused routes (route kind "fused"), where the linear's
+product kernel quantizes x itself: the thin-N kernel (8 rows of x per
+workgroup, all N <= 64 columns; M > 16, K <= 6144) and the GEMV with the
+quantization in its prologue (M <= 4, K <= 6144), against the oracle and
+against the two-kernel routes (quantize kernel + GEMV, KQ_FUSE=0).
 
 Bars as in the other parity tests: int32 accumulators and per-group
 products bit-exact (they pin the codes the kernel forms in registers), the
@@ -167,3 +168,69 @@ def test_fused_route_log(kq_env, capfd):
     err = capfd.readouterr().err
     assert "kq_w8a8_linear M=100 N=48 K=256" in err and "route=fused" in err
     assert "thin_fused_w8a8" in err and "thin_fused_w4a8" in err
+
+
+# ---------------------------------------------------- GEMV quantizing x itself
+# (M, K, N): 1-4 rows, one group to the 6144 limit, ragged column blocks
+GEMV_XQ = [(1, 64, 16), (2, 320, 200), (3, 1088, 33), (4, 5120, 256), (1, 6144, 100),
+           (4, 192, 17), (2, 3072, 1000)]
+
+
+@pytest.mark.parametrize("fmt", ["w8", "w4"])
+@pytest.mark.parametrize("M,K,N", GEMV_XQ)
+def test_gemv_xq_matches_oracle(M, K, N, fmt, kq_env):
+    """M <= 4: the GEMV quantizes its rows in its prologue (route "fused",
+    4-row tile); codes (through the int32 outputs) and scales bit-exact."""
+    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_FUSE=None)
+    r = kq.kq_route(M, N, K, _fmt_code(fmt))
+    assert (r["kind"], r["tile_m"], r["grid"]) == ("fused", 4, -(-N // 16))
+    seed = 7 * M + K + N
+    dist = "student_t4" if (M + K) % 2 else "normal"
+    xb = synth.random_bf16((M, K), seed=seed, dist=dist)
+    w = synth.random_f32((N, K), seed=seed + 1, scale=0.02)
+    b = synth.random_f32((N,), seed=seed + 2, scale=0.1)
+    print(f"[fused] gemv xq {fmt} {M}x{K}x{N} {dist}", flush=True)
+    _check_all(fmt, xb, w, b, f"gemv xq {fmt} {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("fmt", ["w8", "w4"])
+def test_gemv_xq_special_rows(fmt, kq_env):
+    """A zero row, a row whose 127/amax overflows, a subnormal row and a huge
+    outlier, quantized inside the GEMV."""
+    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_FUSE=None)
+    M, K, N = 4, 3072, 48
+    x = synth.bf16_bits_to_f32(synth.random_bf16((M, K), seed=23)).copy()
+    x[0] = 0.0
+    x[1] = 0.0
+    x[1, 17] = 1e-38
+    x[2] = 0.0
+    x[2, ::7] = np.float32(2.0 ** -130)
+    x[3, 5] = np.float32(3.0e38)
+    xb = synth.to_bf16_bits(x)
+    w = synth.random_f32((N, K), seed=24, scale=0.02)
+    b = synth.random_f32((N,), seed=25, scale=0.1)
+    assert kq.kq_route(M, N, K, _fmt_code(fmt))["kind"] == "fused"
+    _check_all(fmt, xb, w, b, f"gemv xq special rows {fmt}")
+
+
+@pytest.mark.parametrize("fmt", ["w8", "w4"])
+@pytest.mark.parametrize("M,K,N", [(1, 5120, 512), (4, 1088, 200), (2, 3072, 1000)])
+def test_gemv_xq_and_two_kernel_gemv_agree_bitwise(M, K, N, fmt, kq_env):
+    """The same GEMV kernel, slices and sum order whether it quantizes x
+    itself or reads the quantize kernel's codes: every output bit agrees,
+    for int4 weights too."""
+    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None)
+    seed = M + 3 * K + N
+    xb = synth.random_bf16((M, K), seed=seed, dist="student_t4")
+    w = synth.random_f32((N, K), seed=seed + 1, scale=0.02)
+    b = synth.random_f32((N,), seed=seed + 2, scale=0.1)
+    outs = {}
+    for fuse in (None, "0"):
+        kq_env(KQ_FUSE=fuse)
+        kind = kq.kq_route(M, N, K, _fmt_code(fmt))["kind"]
+        assert kind == ("fused" if fuse is None else "gemv")
+        outs[kind] = [host(_run(fmt, xb, w, b, dt)) for dt in (torch.float32, torch.int32)]
+        outs[kind].append(host_bf16_bits(_run(fmt, xb, w, b, torch.bfloat16)))
+    torch.cuda.synchronize()
+    for u, v in zip(outs["fused"], outs["gemv"]):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8))

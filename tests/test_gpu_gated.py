@@ -60,6 +60,7 @@ def _check(y, out, y64, T, r, g, L, what):
 # (M, K, N, route): GEMM with whole and ragged tiles, GEMV, fused thin N
 SHAPES = [(300, 640, 200, "gemm"), (513, 320, 260, "gemm"), (256, 512, 256, "gemm"),
           (5, 1024, 200, "gemv"), (16, 256, 130, "gemv"), (300, 512, 48, "fused"),
+          (3, 1024, 200, "fused"),
           (96, 2112, 272, "gemm")]
 # (residual?, gate_rows or 0 for no gate)
 VARIANTS = [(True, 1), (True, 128), (False, 1), (True, 0), (True, 7)]

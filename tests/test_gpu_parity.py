@@ -274,16 +274,22 @@ def test_gemv_and_gemm_routes_agree_bitwise(M, kq_env):
 
 # ------------------------------------------------------------- behaviour
 def test_route_log_names_kernels(kq_env, capfd):
-    kq_env(KQ_LOG="1", KQ_FORCE_ROUTE=None, KQ_TILE=None)
-    xb, w, b = _problem(4, 256, 96, seed=5)  # N > 64: M = 300 takes the GEMM
+    kq_env(KQ_LOG="1", KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_FUSE=None)
+    xb, w, b = _problem(5, 256, 96, seed=5)  # N > 64: M = 300 takes the GEMM
     p, gs, gb, _ = oracle.quantize_w4(w)
     kq.kq_w4a8_linear(dev_bf16(xb), dev(p), dev(gs), dev(gb))
     xb2 = synth.random_bf16((300, 256), seed=6)
     kq.kq_w4a8_linear(dev_bf16(xb2), dev(p), dev(gs), dev(gb))
+    xb3 = synth.random_bf16((4, 256), seed=7)
+    kq.kq_w4a8_linear(dev_bf16(xb3), dev(p), dev(gs), dev(gb))
     torch.cuda.synchronize()
-    err = capfd.readouterr().err
-    assert "kq_w4a8_linear M=4" in err and "route=gemv" in err and "gemv_w4a8" in err
-    assert "kq_w4a8_linear M=300" in err and "route=gemm" in err and "gemm_w4a8_" in err
+    lines = capfd.readouterr().err.splitlines()
+    m5 = [l for l in lines if "kq_w4a8_linear M=5 " in l]
+    m300 = [l for l in lines if "kq_w4a8_linear M=300 " in l]
+    m4 = [l for l in lines if "kq_w4a8_linear M=4 " in l]
+    assert m5 and "route=gemv" in m5[0] and "quant_act" in m5[0] and "gemv_w4a8" in m5[0]
+    assert m300 and "route=gemm" in m300[0] and "gemm_w4a8_" in m300[0]
+    assert m4 and "route=fused" in m4[0] and "gemv_xq_w4a8" in m4[0]
 
 
 def test_empty_and_error_paths():

@@ -24,9 +24,11 @@ def setup_module(module):
     assert kq.kq_is_available(), "libkq reports no gfx950 device"
 
 
-# (M, K, N, route the linear takes): GEMV rows, thin N (fused for the
-# linear), GEMM with ragged tiles, a shape the linear would split
-SHAPES = [(3, 512, 200, "gemv"), (300, 640, 48, "fused"), (257, 320, 129, "gemm"),
+# (M, K, N, route the linear takes): a few rows (the linear's GEMV quantizes
+# x itself; these entry points take the plain GEMV), 16 rows, thin N (fused
+# for the linear), GEMM with ragged tiles, a shape the linear would split
+SHAPES = [(3, 512, 200, "fused"), (16, 512, 200, "gemv"), (300, 640, 48, "fused"),
+          (257, 320, 129, "gemm"),
           (64, 1024, 1000, "gemm"), (128, 12288, 256, "gemm")]
 
 

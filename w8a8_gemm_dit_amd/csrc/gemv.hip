@@ -38,12 +38,25 @@ namespace {
 constexpr int kWaves = 8;         // K slices per workgroup
 constexpr int kChunk = 4;         // groups per LDS chunk of one wavefront
 constexpr int kMaxG = kGemvMaxK / 64;
+// In-kernel quantization (XQ): at most kGemvXqRows rows and slices of at
+// most kXqMaxGPW groups (K <= kFusedMaxK).
+constexpr int kXqMaxGPW = 12;
+constexpr int kXT = kXqMaxGPW / 2;  // 16-byte x loads per lane
+static_assert(((int)(kFusedMaxK / 64) + kWaves - 1) / kWaves <= kXqMaxGPW &&
+              kXqMaxGPW % kChunk == 0, "XQ slices");
+static_assert(kGemvXqRows * 16 == 64, "XQ x loads: 16 lanes per row");
 
-template <bool W4, int OUT>
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// XQ: A is unused and the kernel quantizes bf16 rows X itself (Mtot <=
+// kGemvXqRows, one row block): the same absmax rule and rounding as the
+// quantize kernel; the token scales go to sx_out (if not NULL).
+template <bool W4, int OUT, bool XQ>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ sx,
     const void* __restrict__ Wq, const void* __restrict__ gsv, const void* __restrict__ gbv,
-    const float* __restrict__ bias, void* y, int Mtot, int N, int K, Epilogue ep) {
+    const float* __restrict__ bias, void* y, int Mtot, int N, int K, Epilogue ep,
+    const uint16_t* __restrict__ X, float* __restrict__ sx_out) {
   // this workgroup's 16-row block of the activations
   const int m0 = blockIdx.y * 16;
   const int M = min(16, Mtot - m0);
@@ -57,6 +70,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
   static_assert(kChunk % GPB == 0, "a chunk is whole DMA blocks");
   __shared__ __attribute__((aligned(16))) int8_t lds_w[kWaves][WLDS];
   __shared__ float lds_red[kWaves - 1][4][64];
+  __shared__ float s_xamax[XQ ? kWaves : 1][kGemvXqRows];
+  __shared__ float s_xscale[kGemvXqRows];
   extern __shared__ uint32_t lds_sb[];      // [G][16]: scale | offset << 16 (int4 only)
 
   const int G = K / 64;
@@ -128,7 +143,34 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
     }
   };
   issue(g0, min(gn, kChunk));
-  load_a(g0, min(gn, kChunk));
+  if (!XQ) load_a(g0, min(gn, kChunk));
+
+  // XQ: x with whole-line loads.  Lane l takes row l/16 and, for t < kXT,
+  // the 16 bytes of values 8*(l%8)..+7 of slice group 2t + (l%16)/8, so
+  // the 16 lanes of a row read 256 contiguous bytes per instruction.
+  const int xr = lane >> 4, xj = lane & 15;
+  v4i xq[XQ ? kXT : 1];
+  if constexpr (XQ) {
+    const v4i* xrow = reinterpret_cast<const v4i*>(X + (int64_t)min(xr, Mtot - 1) * K + 8 * (xj & 7));
+#pragma unroll
+    for (int t = 0; t < kXT; ++t) {
+      const int gi = 2 * t + (xj >> 3);
+      xq[t] = v4i{0, 0, 0, 0};
+      if (gi < gn && xr < Mtot) xq[t] = xrow[(g0 + gi) * 8];
+    }
+    // Row absmax on the bf16 bit patterns (for finite values the magnitude
+    // bits order as |x|), over the row's 16 lanes, then the 8 slices.
+    u16x2 mb = u16x2{0, 0};
+#pragma unroll
+    for (int t = 0; t < kXT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        mb = __builtin_elementwise_max(mb, __builtin_bit_cast(u16x2, (uint32_t)xq[t][j] & 0x7FFF7FFFu));
+    float am = bf16_to_f32(max((uint32_t)mb.x, (uint32_t)mb.y));
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) am = fmaxf(am, __shfl_xor(am, off, kWave));
+    if (xj == 0) s_xamax[wave][xr] = am;
+  }
 
   // Epilogue operands, loaded while the weights stream.
   const int nn = n0 + fr;
@@ -137,7 +179,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
   const float swn = (!W4 && OUT != kOutI32) ? reinterpret_cast<const float*>(gsv)[nc] : 0.0f;
   float sxm[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) sxm[r] = (OUT != kOutI32) ? sx[min(4 * fc + r, M - 1)] : 0.0f;
+  for (int r = 0; r < 4; ++r) sxm[r] = (OUT != kOutI32 && !XQ) ? sx[min(4 * fc + r, M - 1)] : 0.0f;
 
   if (kScales) {
 #pragma unroll
@@ -148,55 +190,124 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
         lds_sb[g * 16 + r] = sreg[j];
       }
     }
-    wait_vm_lgkm0<63>();
+  }
+  if (kScales || XQ) {
+    wait_vm_lgkm0<63>();  // LDS writes done; the weight DMA may still fly
     barrier_nofence();
+  }
+  // XQ: the codes.  rint(x*inv) through the 1.5*2^23 shift (the product
+  // rounds once; adding 1.5*2^23, exact at spacing 1, rounds it to the
+  // nearest integer, ties to even, leaving the code in the low byte); no
+  // clamp: inv = fp32(127/amax) gives |x*inv| <= 127*(1 + 2^-24)^2 < 127.5.
+  // xc[t] holds the 8 codes of the lane's loads, 4 per dword.
+  int xc[XQ ? kXT : 1][2];
+  if constexpr (XQ) {
+    float am = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) am = fmaxf(am, s_xamax[w][xr]);
+    float scale;
+    const float inv = row_inv(am, scale);
+    if (wave == 0 && xj == 0) {
+      s_xscale[xr] = scale;
+      if (sx_out != nullptr && xr < Mtot) sx_out[xr] = scale;
+    }
+#pragma unroll
+    for (int t = 0; t < kXT; ++t) {
+#pragma clang fp contract(off)  // two roundings, as the rule has them: no fma
+      uint32_t tt[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = (uint32_t)xq[t][j];
+        const float p0 = bf16_to_f32(w & 0xFFFFu) * inv;
+        const float p1 = bf16_to_f32(w >> 16) * inv;
+        tt[2 * j] = __float_as_uint(p0 + 12582912.0f);
+        tt[2 * j + 1] = __float_as_uint(p1 + 12582912.0f);
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        // v_perm_b32 selectors: bytes 0-3 come from the second operand, 4-7
+        // from the first, 0x0c gives zero
+        const uint32_t lo = __builtin_amdgcn_perm(tt[4 * q + 1], tt[4 * q], 0x0c0c0400u);
+        const uint32_t hi = __builtin_amdgcn_perm(tt[4 * q + 3], tt[4 * q + 2], 0x0c0c0400u);
+        xc[t][q] = (int)__builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      }
+    }
   }
 
   v4f facc = v4f{0.f, 0.f, 0.f, 0.f};
   v4i iacc = v4i{0, 0, 0, 0};
   const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
   const int8_t* wl = &lds_w[wave][(fr >> 3) * (kChunk * 8 * UB) + (fr & 7) * UB + fc * (UB / 4)];
-  for (int c0 = 0; c0 < gn; c0 += kChunk) {
-    const int gc = min(kChunk, gn - c0);
-    if (c0 > 0) {
-      wait_vm_lgkm0<63>();  // fragment reads of the last chunk done before the DMA reuses it
-      issue(g0 + c0, gc);
-      load_a(g0 + c0, gc);
-    }
+  // One group's products: weight fragment i of the chunk in LDS, codes fa_g.
+  auto group_product = [&](int i, int g, const v4i& fa_g) {
+    if (W4) {
+      const uint2 wv = *reinterpret_cast<const uint2*>(wl + i * 8 * UB);
+      uint32_t u0, u1, u2, u3;
+      unpack8_u4(wv.x, u0, u1);
+      unpack8_u4(wv.y, u2, u3);
+      const v4i fw = v4i{(int)u0, (int)u1, (int)u2, (int)u3};
+      const v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa_g, fw, v4i{0, 0, 0, 0}, 0, 0, 0);
+      if (OUT == kOutI32) {
+        // debug output: P of every group, [G, M, N]; p[r] = P[g, 4*fc + r, n]
+        if (nn < N) {
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-      if (i < gc) {
-        const int g = g0 + c0 + i;
-        if (W4) {
-          const uint2 wv = *reinterpret_cast<const uint2*>(wl + i * 8 * UB);
-          uint32_t u0, u1, u2, u3;
-          unpack8_u4(wv.x, u0, u1);
-          unpack8_u4(wv.y, u2, u3);
-          const v4i fw = v4i{(int)u0, (int)u1, (int)u2, (int)u3};
-          const v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fw, v4i{0, 0, 0, 0}, 0, 0, 0);
-          if (OUT == kOutI32) {
-            // debug output: P of every group, [G, M, N]; p[r] = P[g, 4*fc + r, n]
-            if (nn < N) {
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int m = 4 * fc + r;
-                if (m < M) reinterpret_cast<int32_t*>(y)[((int64_t)g * Mtot + m0 + m) * N + nn] = p[r];
-              }
-            }
-          } else {
-            const v4i as = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], ones, v4i{0, 0, 0, 0}, 0, 0, 0);
-            const uint32_t sb = lds_sb[g * 16 + fr];
-            const float s = __half2float(__ushort_as_half((unsigned short)(sb & 0xffff)));
-            const float b = __half2float(__ushort_as_half((unsigned short)(sb >> 16)));
-#pragma unroll
-            for (int r = 0; r < 4; ++r) facc[r] = fmaf(b, (float)as[r], fmaf(s, (float)p[r], facc[r]));
+          for (int r = 0; r < 4; ++r) {
+            const int m = 4 * fc + r;
+            if (m < M) reinterpret_cast<int32_t*>(y)[((int64_t)g * Mtot + m0 + m) * N + nn] = p[r];
           }
-        } else {
-          const int4 wv = *reinterpret_cast<const int4*>(wl + i * 8 * UB);
-          iacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], v4i{wv.x, wv.y, wv.z, wv.w}, iacc,
-                                                       0, 0, 0);
+        }
+      } else {
+        const v4i as = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa_g, ones, v4i{0, 0, 0, 0}, 0, 0, 0);
+        const uint32_t sb = lds_sb[g * 16 + fr];
+        const float s = __half2float(__ushort_as_half((unsigned short)(sb & 0xffff)));
+        const float b = __half2float(__ushort_as_half((unsigned short)(sb >> 16)));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) facc[r] = fmaf(b, (float)as[r], fmaf(s, (float)p[r], facc[r]));
+      }
+    } else {
+      const int4 wv = *reinterpret_cast<const int4*>(wl + i * 8 * UB);
+      iacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa_g, v4i{wv.x, wv.y, wv.z, wv.w}, iacc, 0, 0, 0);
+    }
+  };
+  if constexpr (XQ) {
+    // Operand of slice group gi: lane fr + 16*fc (rows fr < 4) takes the
+    // codes of values 16*fc..16*fc+15 from lanes 16*fr + 8*(gi%2) + 2*fc and
+    // + 1 (their loads t = gi/2); rows 4-15 are zero.  Fully unrolled, so
+    // the register of each load is known.
+    const int src0 = 4 * (16 * (fr & 3) + 2 * fc);  // ds_bpermute byte address, gi even
+#pragma unroll
+    for (int c0 = 0; c0 < kXqMaxGPW; c0 += kChunk) {
+      if (c0 >= gn) break;
+      const int gc = min(kChunk, gn - c0);
+      if (c0 > 0) {
+        wait_vm_lgkm0<63>();  // fragment reads of the last chunk done before the DMA reuses it
+        issue(g0 + c0, gc);
+      }
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) {
+        if (i < gc) {
+          const int gi = c0 + i;
+          const int sa = src0 + 32 * (gi & 1);
+          v4i f = v4i{__builtin_amdgcn_ds_bpermute(sa, xc[gi >> 1][0]),
+                      __builtin_amdgcn_ds_bpermute(sa, xc[gi >> 1][1]),
+                      __builtin_amdgcn_ds_bpermute(sa + 4, xc[gi >> 1][0]),
+                      __builtin_amdgcn_ds_bpermute(sa + 4, xc[gi >> 1][1])};
+          if (fr >= kGemvXqRows) f = v4i{0, 0, 0, 0};
+          group_product(i, g0 + gi, f);
         }
       }
+    }
+  } else {
+    for (int c0 = 0; c0 < gn; c0 += kChunk) {
+      const int gc = min(kChunk, gn - c0);
+      if (c0 > 0) {
+        wait_vm_lgkm0<63>();  // fragment reads of the last chunk done before the DMA reuses it
+        issue(g0 + c0, gc);
+        load_a(g0 + c0, gc);
+      }
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i)
+        if (i < gc) group_product(i, g0 + c0 + i, fa[i]);
     }
   }
   if (W4 && OUT == kOutI32) return;
@@ -209,6 +320,10 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
   }
   __syncthreads();
   if (wave != 0) return;
+  if (XQ && OUT != kOutI32) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sxm[r] = s_xscale[min(4 * fc + r, M - 1)];
+  }
 #pragma unroll
   for (int w = 0; w < kWaves - 1; ++w)
 #pragma unroll
@@ -233,18 +348,19 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
   }
 }
 
-template <bool W4>
+template <bool W4, bool XQ>
 const char* launch_fmt(const int8_t* a, const float* sx, const void* q, const void* gs,
                        const void* gb, const float* bias, void* y, int out, int M, int N, int K,
-                       hipStream_t s, const Epilogue& ep) {
+                       hipStream_t s, const Epilogue& ep, const uint16_t* x, float* sx_out) {
   const dim3 grid((unsigned)((N + 15) / 16), (unsigned)((M + 15) / 16)), block(kWaves * 64);
   const size_t sb = (W4 && out != kOutI32) ? (size_t)16 * (K / 64) * sizeof(uint32_t) : 0;
   if (out == kOutF32)
-    hipLaunchKernelGGL((gemv_kernel<W4, kOutF32>), grid, block, sb, s, a, sx, q, gs, gb, bias, y, M, N, K, ep);
+    hipLaunchKernelGGL((gemv_kernel<W4, kOutF32, XQ>), grid, block, sb, s, a, sx, q, gs, gb, bias, y, M, N, K, ep, x, sx_out);
   else if (out == kOutBF16)
-    hipLaunchKernelGGL((gemv_kernel<W4, kOutBF16>), grid, block, sb, s, a, sx, q, gs, gb, bias, y, M, N, K, ep);
+    hipLaunchKernelGGL((gemv_kernel<W4, kOutBF16, XQ>), grid, block, sb, s, a, sx, q, gs, gb, bias, y, M, N, K, ep, x, sx_out);
   else
-    hipLaunchKernelGGL((gemv_kernel<W4, kOutI32>), grid, block, sb, s, a, sx, q, gs, gb, bias, y, M, N, K, ep);
+    hipLaunchKernelGGL((gemv_kernel<W4, kOutI32, XQ>), grid, block, sb, s, a, sx, q, gs, gb, bias, y, M, N, K, ep, x, sx_out);
+  if (XQ) return W4 ? "gemv_xq_w4a8" : "gemv_xq_w8a8";
   return W4 ? "gemv_w4a8" : "gemv_w8a8";
 }
 
@@ -253,9 +369,12 @@ const char* launch_fmt(const int8_t* a, const float* sx, const void* q, const vo
 const char* launch_gemv(bool w4, const int8_t* a, const float* sx, const int32_t* /*gsum*/,
                         const void* q, const void* gs, const void* gb, const float* bias,
                         void* y, int out, int M, int N, int K, hipStream_t s,
-                        const Epilogue& ep) {
-  return w4 ? launch_fmt<true>(a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep)
-            : launch_fmt<false>(a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep);
+                        const Epilogue& ep, const uint16_t* x, float* sx_out) {
+  if (x != nullptr)
+    return w4 ? launch_fmt<true, true>(nullptr, nullptr, q, gs, gb, bias, y, out, M, N, K, s, ep, x, sx_out)
+              : launch_fmt<false, true>(nullptr, nullptr, q, gs, gb, bias, y, out, M, N, K, s, ep, x, sx_out);
+  return w4 ? launch_fmt<true, false>(a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, nullptr, nullptr)
+            : launch_fmt<false, false>(a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, nullptr, nullptr);
 }
 
 }  // namespace kq

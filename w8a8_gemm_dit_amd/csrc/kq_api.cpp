@@ -185,10 +185,15 @@ kq_status run_linear(const char* op, int force, kq_wformat fmt, const void* x, i
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* wsb = reinterpret_cast<char*>(ws);
   if (fused) {
-    const char* k = kq::launch_thin_fused(fmt == KQ_W4_AFFINE_G64, reinterpret_cast<const uint16_t*>(x),
-                                          reinterpret_cast<float*>(wsb + wl.scale_off), wq, scale,
-                                          gbias, bias, y, out_kind(y_dtype), (int)M, (int)N, (int)K,
-                                          s, ep);
+    const bool w4 = fmt == KQ_W4_AFFINE_G64;
+    const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+    float* sxo = reinterpret_cast<float*>(wsb + wl.scale_off);
+    const char* k =
+        M <= kq::kGemvXqRows
+            ? kq::launch_gemv(w4, nullptr, nullptr, nullptr, wq, scale, gbias, bias, y,
+                              out_kind(y_dtype), (int)M, (int)N, (int)K, s, ep, xb, sxo)
+            : kq::launch_thin_fused(w4, xb, sxo, wq, scale, gbias, bias, y, out_kind(y_dtype),
+                                    (int)M, (int)N, (int)K, s, ep);
     st = check_launch(op);
     if (st != KQ_SUCCESS) return st;
     if (env_log())
@@ -345,9 +350,13 @@ const char* kq_last_error(void) { return g_last_error.c_str(); }
 
 size_t kq_workspace_bytes(int64_t M, int64_t N, int64_t K, kq_wformat fmt) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
+  // Sized for the two-kernel layout even where the route is fused (which
+  // needs only the scales): the same workspace then serves every entry
+  // point and lever for this shape (KQ_FUSE=0, kq_gemv_small_m), whose
+  // routes never split K where the fused ones apply (K <= 6144).
   const kq_route_info r =
       kq::choose_route(M, N, K, fmt, env_force_route(), env_tile(), env_split(), env_fuse());
-  return kq::workspace_layout(M, N, K, fmt, r.splits, r.kind == KQ_ROUTE_FUSED).total;
+  return kq::workspace_layout(M, N, K, fmt, r.splits, false).total;
 }
 
 kq_status kq_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt, kq_dtype y_dtype,

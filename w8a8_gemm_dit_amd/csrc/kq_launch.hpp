@@ -50,10 +50,13 @@ const char* launch_gemm_w4a8(int tile, const int8_t* a, const float* sx, const i
                              int splits = 1, float* partials = nullptr);
 
 // GEMV for 1 <= M <= 16 (w4: q is packed int4 with gs/gb; w8: q int8, gs = fp32 [N]).
+// x != NULL: the kernel quantizes the bf16 rows x itself (a, sx unused;
+// M <= kGemvXqRows, K <= kFusedMaxK) and writes the token scales to sx_out.
 const char* launch_gemv(bool w4, const int8_t* a, const float* sx, const int32_t* gsum,
                         const void* q, const void* gs, const void* gb, const float* bias,
                         void* y, int out, int M, int N, int K, hipStream_t s,
-                        const Epilogue& ep = Epilogue());
+                        const Epilogue& ep = Epilogue(), const uint16_t* x = nullptr,
+                        float* sx_out = nullptr);
 
 // Thin-N linear with the activation quantization inside (N <= 64, K <=
 // kFusedMaxK): reads bf16 x, writes the token scales to sx (if not NULL)

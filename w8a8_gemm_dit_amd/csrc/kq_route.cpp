@@ -97,6 +97,16 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
                            int force, int tile_override, int split_override, bool fuse) {
   kq_route_info r{};
   r.splits = 1;
+  // Up to 4 rows the GEMV quantizes x in its prologue (the separate
+  // quantize kernel would cost a launch and a round trip for a few rows).
+  if (fuse && force == 0 && M >= 1 && M <= kGemvXqRows && K <= kFusedMaxK) {
+    r.kind = KQ_ROUTE_FUSED;
+    r.tile_m = kGemvXqRows;
+    r.tile_n = kGemvCols;
+    r.threads = kGemvThreads;
+    r.grid = (N + kGemvCols - 1) / kGemvCols;
+    return r;
+  }
   // Thin N with more than one 16-row block: one kernel quantizes its rows
   // and covers every column, so x is read once and no codes are stored.
   if (fuse && force == 0 && N <= kGemvThinN && M > KQ_GEMV_MAX_M && K <= kFusedMaxK &&

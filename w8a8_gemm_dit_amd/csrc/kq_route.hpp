@@ -80,6 +80,7 @@ constexpr int kGemvRows = 16;   // activation rows per GEMV workgroup
 constexpr int kGemvThinN = 64;  // N up to this takes the GEMV at any M
 constexpr int kGemvAutoRows = 32;  // the automatic route's GEMV takes M up to this
 constexpr int kGemvThreads = 512;
+constexpr int kGemvXqRows = 4;  // the GEMV quantizes x itself up to this many rows
 constexpr int64_t kGemvMaxK = KQ_GEMV_MAX_K;
 
 // Fused thin-N route (N <= kGemvThinN, M > 16): 8 rows and all columns
