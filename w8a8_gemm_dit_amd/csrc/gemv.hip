@@ -46,8 +46,6 @@ static_assert(((int)(kFusedMaxK / 64) + kWaves - 1) / kWaves <= kXqMaxGPW &&
               kXqMaxGPW % kChunk == 0, "XQ slices");
 static_assert(kGemvXqRows * 16 == 64, "XQ x loads: 16 lanes per row");
 
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
 // XQ: A is unused and the kernel quantizes bf16 rows X itself (Mtot <=
 // kGemvXqRows, one row block): the same absmax rule and rounding as the
 // quantize kernel; the token scales go to sx_out (if not NULL).
@@ -164,9 +162,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
 #pragma unroll
     for (int t = 0; t < kXT; ++t)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        mb = __builtin_elementwise_max(mb, __builtin_bit_cast(u16x2, (uint32_t)xq[t][j] & 0x7FFF7FFFu));
-    float am = bf16_to_f32(max((uint32_t)mb.x, (uint32_t)mb.y));
+      for (int j = 0; j < 4; ++j) mb = absmax_bits2(mb, (uint32_t)xq[t][j]);
+    float am = absmax_bits_value(mb);
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) am = fmaxf(am, __shfl_xor(am, off, kWave));
     if (xj == 0) s_xamax[wave][xr] = am;
@@ -195,11 +192,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
     wait_vm_lgkm0<63>();  // LDS writes done; the weight DMA may still fly
     barrier_nofence();
   }
-  // XQ: the codes.  rint(x*inv) through the 1.5*2^23 shift (the product
-  // rounds once; adding 1.5*2^23, exact at spacing 1, rounds it to the
-  // nearest integer, ties to even, leaving the code in the low byte); no
-  // clamp: inv = fp32(127/amax) gives |x*inv| <= 127*(1 + 2^-24)^2 < 127.5.
-  // xc[t] holds the 8 codes of the lane's loads, 4 per dword.
+  // XQ: the codes (codes8_shift: the quantize kernel's rule); xc[t] holds
+  // the 8 codes of the lane's load t, 4 per dword.
   int xc[XQ ? kXT : 1][2];
   if constexpr (XQ) {
     float am = 0.0f;
@@ -213,24 +207,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
     }
 #pragma unroll
     for (int t = 0; t < kXT; ++t) {
-#pragma clang fp contract(off)  // two roundings, as the rule has them: no fma
-      uint32_t tt[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = (uint32_t)xq[t][j];
-        const float p0 = bf16_to_f32(w & 0xFFFFu) * inv;
-        const float p1 = bf16_to_f32(w >> 16) * inv;
-        tt[2 * j] = __float_as_uint(p0 + 12582912.0f);
-        tt[2 * j + 1] = __float_as_uint(p1 + 12582912.0f);
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        // v_perm_b32 selectors: bytes 0-3 come from the second operand, 4-7
-        // from the first, 0x0c gives zero
-        const uint32_t lo = __builtin_amdgcn_perm(tt[4 * q + 1], tt[4 * q], 0x0c0c0400u);
-        const uint32_t hi = __builtin_amdgcn_perm(tt[4 * q + 3], tt[4 * q + 2], 0x0c0c0400u);
-        xc[t][q] = (int)__builtin_amdgcn_perm(hi, lo, 0x05040100u);
-      }
+      const uint32_t w[4] = {(uint32_t)xq[t][0], (uint32_t)xq[t][1], (uint32_t)xq[t][2],
+                             (uint32_t)xq[t][3]};
+      const uint2 c = codes8_shift(w, inv);
+      xc[t][0] = (int)c.x;
+      xc[t][1] = (int)c.y;
     }
   }
 

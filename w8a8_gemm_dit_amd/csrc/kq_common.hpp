@@ -50,6 +50,48 @@ __device__ __forceinline__ int quant_code(float v, float inv) {
   return (int)t;
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Running max of |x| over the two bf16 values of a dword, on their bit
+// patterns: for finite values the magnitude bits order as |x| (exact).
+__device__ __forceinline__ u16x2 absmax_bits2(u16x2 m, uint32_t w) {
+  return __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu));
+}
+
+// |x| max as a float from absmax_bits2's running value.
+__device__ __forceinline__ float absmax_bits_value(u16x2 m) {
+  return bf16_to_f32(max((uint32_t)m.x, (uint32_t)m.y));
+}
+
+// int8 codes of the 8 bf16 values of w[0..3] (low half first), 4 per dword
+// in value order, with inv from row_inv: the same result as quant_code.
+// rint(x*inv) goes through the 1.5*2^23 shift: the product rounds once, and
+// adding 1.5*2^23 (exact spacing 1 at that magnitude) rounds it to the
+// nearest integer, ties to even, leaving the code in the low byte of the
+// sum's bits.  No clamp: inv = fp32(127/amax) gives |x*inv| <= 127*(1 +
+// 2^-24)^2 < 127.5 (and inv = 0 gives 0).
+__device__ __forceinline__ uint2 codes8_shift(const uint32_t w[4], float inv) {
+#pragma clang fp contract(off)  // two roundings, as the rule has them: no fma
+  uint32_t t[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p0 = bf16_to_f32(w[i] & 0xFFFFu) * inv;
+    const float p1 = bf16_to_f32(w[i] >> 16) * inv;
+    t[2 * i] = __float_as_uint(p0 + 12582912.0f);
+    t[2 * i + 1] = __float_as_uint(p1 + 12582912.0f);
+  }
+  // v_perm_b32 selectors: bytes 0-3 come from the second operand, 4-7 from
+  // the first, 0x0c gives zero
+  uint32_t d[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t lo = __builtin_amdgcn_perm(t[4 * q + 1], t[4 * q], 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(t[4 * q + 3], t[4 * q + 2], 0x0c0c0400u);
+    d[q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+  }
+  return make_uint2(d[0], d[1]);
+}
+
 // Per-row scale rule of the symmetric int8 quantizer: inv = fp32(127/amax)
 // and scale = fp32(amax/127); a row whose 127/amax is not a finite fp32
 // (all zero, or too small) gets inv 0 (codes 0) and scale 0.

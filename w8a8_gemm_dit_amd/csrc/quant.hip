@@ -30,51 +30,21 @@ namespace {
 constexpr int kRowsPerBlock = 4;  // one wavefront per row, 4 waves per block
 
 // Quantize 8 bf16 values held in a uint4; returns 8 codes as uint2 and their
-// sum.  rint(x*inv) through the 1.5*2^23 shift: the product rounds once, and
-// adding 1.5*2^23 (exact spacing 1 at that magnitude) rounds it to the
-// nearest integer, ties to even, leaving the code in the low byte of the
-// sum's bits.  The clamp to +-127 never binds: inv = fp32(127/amax) gives
-// |x*inv| <= 127*(1 + 2^-24)^2 < 127.5 (and inv = 0 gives 0).
+// sum (two signed 4-way byte dot products against ones).
 __device__ __forceinline__ uint2 quant8(const uint4 v, float inv, int& sum) {
-#pragma clang fp contract(off)  // two roundings, as the rule has them: no fma
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t t[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float p0 = bf16_to_f32(w[i] & 0xFFFFu) * inv;
-    const float p1 = bf16_to_f32(w[i] >> 16) * inv;
-    t[2 * i] = __float_as_uint(p0 + 12582912.0f);
-    t[2 * i + 1] = __float_as_uint(p1 + 12582912.0f);
-  }
-  // v_perm_b32 selectors: bytes 0-3 come from the second operand, 4-7 from
-  // the first, 0x0c gives zero
-  uint32_t d[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const uint32_t lo = __builtin_amdgcn_perm(t[4 * q + 1], t[4 * q], 0x0c0c0400u);
-    const uint32_t hi = __builtin_amdgcn_perm(t[4 * q + 3], t[4 * q + 2], 0x0c0c0400u);
-    d[q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-  }
-  // the codes' sum: two signed 4-way byte dot products against ones
-  sum = __builtin_amdgcn_sdot4((int)d[1], 0x01010101, __builtin_amdgcn_sdot4((int)d[0], 0x01010101, 0, false),
+  const uint2 c = codes8_shift(w, inv);
+  sum = __builtin_amdgcn_sdot4((int)c.y, 0x01010101, __builtin_amdgcn_sdot4((int)c.x, 0x01010101, 0, false),
                                false);
-  return make_uint2(d[0], d[1]);
+  return c;
 }
 
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-// Running max of |x| over 8 bf16 values, two at a time on the bit patterns:
-// for finite values the magnitude bits order as |x|.
+// Running max of |x| over 8 bf16 values held in a uint4.
 __device__ __forceinline__ u16x2 absmax8_bits(u16x2 m, const uint4 v) {
-  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu));
-  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu));
-  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu));
-  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu));
-  return m;
-}
-
-__device__ __forceinline__ float bits_to_amax(u16x2 m) {
-  return bf16_to_f32(max((uint32_t)m.x, (uint32_t)m.y));
+  m = absmax_bits2(m, v.x);
+  m = absmax_bits2(m, v.y);
+  m = absmax_bits2(m, v.z);
+  return absmax_bits2(m, v.w);
 }
 
 // Sum over the 8 aligned lanes of a group (lanes 8q..8q+7).
@@ -108,7 +78,7 @@ __global__ __launch_bounds__(256) void quant_act_regs(
     v[j] = make_uint4((uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w);
     mb = absmax8_bits(mb, v[j]);
   }
-  const float amax = wave_max(bits_to_amax(mb));
+  const float amax = wave_max(absmax_bits_value(mb));
   float scale;
   const float inv = row_inv(amax, scale);
   if (lane == 0) sx[row] = scale;
@@ -138,7 +108,7 @@ __global__ __launch_bounds__(256) void quant_act_stream(
   const uint4* xr = reinterpret_cast<const uint4*>(x + row * (int64_t)K);
   u16x2 mb = u16x2{0, 0};
   for (int c = lane; c < nch; c += 64) mb = absmax8_bits(mb, xr[c]);
-  const float amax = wave_max(bits_to_amax(mb));
+  const float amax = wave_max(absmax_bits_value(mb));
   float scale;
   const float inv = row_inv(amax, scale);
   if (lane == 0) sx[row] = scale;

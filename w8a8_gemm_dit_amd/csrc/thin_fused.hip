@@ -11,7 +11,8 @@
 // Same rules and math as the two-kernel route:
 //   codes: amax = max |x| over the row, inv = fp32(127/amax), code =
 //          clamp(rint(x*inv), -127, 127), sx = fp32(amax/127) (the quantize
-//          kernel's helpers, so codes and scales are identical bit for bit);
+//          kernel's helpers row_inv and codes8_shift, so codes and scales
+//          are identical bit for bit);
 //   int8 weights: y = (sx*sw) * acc + bias, acc the exact int32 dot product;
 //   int4 weights: y = sx * sum_g (gs*P + gb*A) + bias, P the exact int32
 //          dot product of one 64-wide group, A the group sum of the codes.
@@ -27,9 +28,9 @@
 //   - the row absmax: a packed 16-bit max over the bf16 bit patterns (for
 //     finite values the magnitude bits order as |x|), 3 cross-lane steps
 //     over the 8 lanes of a row, then the 16 slice maxima through LDS;
-//   - the codes: rint(x*inv) through the 1.5*2^23 shift (about 5 VALU
-//     operations per element with the max), packed with v_perm_b32, then
-//     moved into MFMA operand order with 4 ds_bpermute per group (lane
+//   - the codes: rint(x*inv) through the 1.5*2^23 shift (codes8_shift;
+//     about 5 VALU operations per element with the max), then moved into
+//     MFMA operand order with 4 ds_bpermute per group (lane
 //     m + 16*c takes codes 16c..16c+15 of row m % 8 from the two lanes that
 //     hold them); the MFMA's rows 8-15 repeat rows 0-7 and are discarded;
 //   - the weights (N*K bytes, read by every workgroup, so served by the L2)
@@ -53,8 +54,6 @@
 namespace kq {
 
 namespace {
-
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = kFusedThreads / 64;               // K slices per workgroup
 constexpr int kRows = kFusedRows;                        // activation rows per workgroup
@@ -159,9 +158,8 @@ __global__ __launch_bounds__(kFusedThreads) void thin_fused_kernel(
 #pragma unroll
   for (int i = 0; i < kMaxGPW; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      mxb = __builtin_elementwise_max(mxb, __builtin_bit_cast(u16x2, (uint32_t)xv[i][j] & 0x7FFF7FFFu));
-  float amax = bf16_to_f32(max((uint32_t)mxb.x, (uint32_t)mxb.y));
+    for (int j = 0; j < 4; ++j) mxb = absmax_bits2(mxb, (uint32_t)xv[i][j]);
+  float amax = absmax_bits_value(mxb);
   amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
   amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
   amax = fmaxf(amax, __shfl_xor(amax, 4, kWave));
@@ -187,38 +185,18 @@ __global__ __launch_bounds__(kFusedThreads) void thin_fused_kernel(
     if (sx_out != nullptr && mx < M) sx_out[mx] = scale;
   }
 
-  // 5. Codes.  rint(x*inv) through the 1.5*2^23 shift: the product rounds
-  //    once, and adding 1.5*2^23 (exact spacing 1 at that magnitude) rounds
-  //    it to the nearest integer, ties to even, leaving the code in the low
-  //    byte of the sum's bits.  No clamp: with inv = fp32(127/amax),
-  //    |x*inv| <= 127*(1 + 2^-24)^2 < 127.5.  Then operand order: lane
-  //    fr + 16*fc takes its 16 codes from lanes 8*(fr%8) + 2*fc and + 1.
+  // 5. Codes (codes8_shift: the quantize kernel's rule), then operand order:
+  //    lane fr + 16*fc takes its 16 codes from lanes 8*(fr%8) + 2*fc and + 1.
   const int src0 = 4 * (8 * (fr & 7) + 2 * fc);  // ds_bpermute byte address
   const int src1 = src0 + 4;
   v4i fa[kMaxGPW];
 #pragma unroll
   for (int i = 0; i < kMaxGPW; ++i) {
-#pragma clang fp contract(off)  // two roundings, as the rule has them: no fma
-    uint32_t t[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t w = (uint32_t)xv[i][j];
-      const float p0 = bf16_to_f32(w & 0xFFFFu) * inv;
-      const float p1 = bf16_to_f32(w >> 16) * inv;
-      t[2 * j] = __float_as_uint(p0 + 12582912.0f);
-      t[2 * j + 1] = __float_as_uint(p1 + 12582912.0f);
-    }
-    int d[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      // v_perm_b32 selectors: bytes 0-3 come from the second operand, 4-7
-      // from the first, 0x0c gives zero
-      const uint32_t lo = __builtin_amdgcn_perm(t[4 * q + 1], t[4 * q], 0x0c0c0400u);
-      const uint32_t hi = __builtin_amdgcn_perm(t[4 * q + 3], t[4 * q + 2], 0x0c0c0400u);
-      d[q] = (int)__builtin_amdgcn_perm(hi, lo, 0x05040100u);
-    }
-    fa[i] = v4i{__builtin_amdgcn_ds_bpermute(src0, d[0]), __builtin_amdgcn_ds_bpermute(src0, d[1]),
-                __builtin_amdgcn_ds_bpermute(src1, d[0]), __builtin_amdgcn_ds_bpermute(src1, d[1])};
+    const uint32_t w[4] = {(uint32_t)xv[i][0], (uint32_t)xv[i][1], (uint32_t)xv[i][2],
+                           (uint32_t)xv[i][3]};
+    const uint2 c = codes8_shift(w, inv);
+    fa[i] = v4i{__builtin_amdgcn_ds_bpermute(src0, (int)c.x), __builtin_amdgcn_ds_bpermute(src0, (int)c.y),
+                __builtin_amdgcn_ds_bpermute(src1, (int)c.x), __builtin_amdgcn_ds_bpermute(src1, (int)c.y)};
   }
 
   // 6. Products over the slice, one chunk of weight lines at a time.
