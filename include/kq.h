@@ -265,7 +265,9 @@ kq_status kq_w4a8_gemm(const int8_t* a, const float* sx, const int32_t* gsum,
  * there) or kq_w8a8_linear (fmt = KQ_W8_PER_CHANNEL: wq int8, scale fp32 [N],
  * gbias NULL), always on the GEMV kernel.  Requires 1 <= M <= 16 and
  * K <= KQ_GEMV_MAX_K (each wavefront keeps its K slice of the activations in
- * registers); the linears route larger K to the GEMM. */
+ * registers); the linears route larger K to the GEMM.  For M <= 4 and
+ * K <= 6144 the GEMV quantizes x in its prologue (one launch, the same
+ * results bit for bit), unless KQ_FUSE=0 or KQ_FORCE_ROUTE=gemv. */
 kq_status kq_gemv_small_m(kq_wformat fmt, const void* x, int64_t M, int64_t K,
                           int64_t N, const void* wq, const void* scale,
                           const void* gbias, const float* bias, void* y,

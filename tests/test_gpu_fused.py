@@ -234,3 +234,35 @@ def test_gemv_xq_and_two_kernel_gemv_agree_bitwise(M, K, N, fmt, kq_env):
     torch.cuda.synchronize()
     for u, v in zip(outs["fused"], outs["gemv"]):
         assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+
+
+@pytest.mark.parametrize("fmt", ["w8", "w4"])
+def test_gemv_small_m_entry_quantizes_in_kernel(fmt, kq_env, capfd):
+    """kq_gemv_small_m at M <= 4 runs the GEMV with the quantization in its
+    prologue; KQ_FORCE_ROUTE=gemv gives the plain GEMV after the quantize
+    kernel; every output bit agrees."""
+    M, K, N = 3, 1024, 300
+    xb = synth.random_bf16((M, K), seed=51, dist="student_t4")
+    w = synth.random_f32((N, K), seed=52, scale=0.02)
+    b = synth.random_f32((N,), seed=53, scale=0.1)
+    x = dev_bf16(xb)
+    if fmt == "w8":
+        q8, sw = oracle.quantize_w8(w)
+        args = (kq.KQ_W8_PER_CHANNEL, x, dev(q8), dev(sw), None)
+    else:
+        p, gs, gb, _ = oracle.quantize_w4(w)
+        args = (kq.KQ_W4_AFFINE_G64, x, dev(p), dev(gs), dev(gb))
+    outs = []
+    for force in (None, "gemv"):
+        kq_env(KQ_LOG="1", KQ_FORCE_ROUTE=force, KQ_TILE=None, KQ_FUSE=None)
+        outs.append([host(kq.kq_gemv_small_m(*args, bias=dev(b), out_dtype=torch.float32)),
+                     host(kq.kq_gemv_small_m(*args, out_dtype=torch.int32))])
+    torch.cuda.synchronize()
+    lines = [l for l in capfd.readouterr().err.splitlines() if "kq_gemv_small_m" in l]
+    assert len(lines) == 4
+    assert all("route=fused" in l and "gemv_xq_" in l for l in lines[:2])
+    assert all("route=gemv" in l and "quant_act" in l for l in lines[2:])
+    for u, v in zip(*outs):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+    y64, T = _exact(fmt, xb, w, b)
+    check_f32(outs[0][0], y64, T, f"kq_gemv_small_m {fmt}")

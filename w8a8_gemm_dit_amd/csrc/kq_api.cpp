@@ -155,10 +155,10 @@ kq_status check_linear_args(const char* op, int force, kq_wformat fmt, int64_t M
     return fail(KQ_ERR_INVALID_VALUE, "[%s] int4 weights need the group offsets", op);
   if (!aligned16(x) || !aligned16(wq) || !aligned16(y))
     return fail(KQ_ERR_INVALID_VALUE, "[%s] x, weights, y and workspace must be 16-byte aligned", op);
-  if (force == 2 && M > KQ_GEMV_MAX_M)
+  if (force >= 2 && M > KQ_GEMV_MAX_M)
     return fail(KQ_ERR_UNSUPPORTED, "[%s] M=%lld exceeds the GEMV limit %d", op, (long long)M,
                 KQ_GEMV_MAX_M);
-  if (force == 2 && K > kq::kGemvMaxK)
+  if (force >= 2 && K > kq::kGemvMaxK)
     return fail(KQ_ERR_UNSUPPORTED, "[%s] K=%lld exceeds the GEMV limit %lld", op, (long long)K,
                 (long long)kq::kGemvMaxK);
   return KQ_SUCCESS;
@@ -468,7 +468,9 @@ kq_status kq_gemv_small_m(kq_wformat fmt, const void* x, int64_t M, int64_t K, i
                 KQ_GEMV_MAX_M);
   if (fmt == KQ_W8_PER_CHANNEL && gbias)
     return fail(KQ_ERR_INVALID_VALUE, "[%s] int8 weights take no group offsets (gbias must be NULL)", op);
-  return run_linear(op, 2, fmt, x, M, K, N, wq, scale, gbias, bias, y, y_dtype, ws, ws_bytes,
+  // the GEMV kernel, quantizing x in its prologue where it can (force 3),
+  // unless KQ_FORCE_ROUTE=gemv asks for the plain two-kernel GEMV (force 2)
+  return run_linear(op, env_force_route() == 2 ? 2 : 3, fmt, x, M, K, N, wq, scale, gbias, bias, y, y_dtype, ws, ws_bytes,
                     stream);
 }
 

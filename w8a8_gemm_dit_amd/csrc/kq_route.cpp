@@ -99,7 +99,7 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
   r.splits = 1;
   // Up to 4 rows the GEMV quantizes x in its prologue (the separate
   // quantize kernel would cost a launch and a round trip for a few rows).
-  if (fuse && force == 0 && M >= 1 && M <= kGemvXqRows && K <= kFusedMaxK) {
+  if (fuse && (force == 0 || force == 3) && M >= 1 && M <= kGemvXqRows && K <= kFusedMaxK) {
     r.kind = KQ_ROUTE_FUSED;
     r.tile_m = kGemvXqRows;
     r.tile_n = kGemvCols;
@@ -128,7 +128,7 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
   // workgroups.
   // (the row blocks are the grid's y dimension, at most 65535)
   const bool thin = N <= kGemvThinN && K <= kGemvMaxK && (M + kGemvRows - 1) / kGemvRows <= 65535;
-  const bool gemv = (force == 2) ? fits : (force == 1) ? false : (M >= 1 && (small || thin));
+  const bool gemv = (force >= 2) ? fits : (force == 1) ? false : (M >= 1 && (small || thin));
   if (gemv) {
     r.kind = KQ_ROUTE_GEMV;
     r.tile_m = kGemvRows;

@@ -37,7 +37,9 @@ TileShape tile_shape(int32_t tile);
 kq_status validate_linear(const char* op, int64_t M, int64_t K, int64_t N,
                           kq_wformat fmt, kq_dtype y_dtype, std::string& err);
 
-// Route of a validated linear call.  force: 0 = automatic, 1 = GEMM, 2 = GEMV.
+// Route of a validated linear call.  force: 0 = automatic, 1 = GEMM, 2 = GEMV
+// after the quantize kernel, 3 = GEMV, quantizing x in its prologue where it
+// can (M <= kGemvXqRows, K <= kFusedMaxK, fuse).
 // tile_override: -1 = automatic, else a GemmTile.  split_override: -1 =
 // automatic, 0 or 1 = never split K, n > 1 = n slices (fewer if K is short).
 // fuse: the call quantizes x itself and may take the fused thin-N kernel.
