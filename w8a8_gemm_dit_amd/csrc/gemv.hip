@@ -96,13 +96,19 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
     const uint16_t* hs = reinterpret_cast<const uint16_t*>(gsv) + (int64_t)n0 * G;
     const uint16_t* hb = reinterpret_cast<const uint16_t*>(gbv) + (int64_t)n0 * G;
     const int lim = rows * G;
+    // Unconditional loads at a clamped index (lim >= 1): all of them issue
+    // back to back (loads under a per-lane guard were each waited for
+    // before the next one issued).
+    uint16_t sl[kSL], bl[kSL];
 #pragma unroll
     for (int j = 0; j < kSL; ++j) {
-      const int e = tid + j * kWaves * 64;
-      uint32_t v = 0;
-      if (e < lim) v = (uint32_t)hs[e] | ((uint32_t)hb[e] << 16);
-      sreg[j] = v;
+      const int e = min(tid + j * kWaves * 64, lim - 1);
+      sl[j] = hs[e];
+      bl[j] = hb[e];
     }
+#pragma unroll
+    for (int j = 0; j < kSL; ++j)
+      sreg[j] = tid + j * kWaves * 64 < lim ? (uint32_t)sl[j] | ((uint32_t)bl[j] << 16) : 0u;
   }
 
   // 2. Weight DMA.  The descriptor is rebased on row n0 with num_records =
@@ -140,12 +146,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
       fa[i] = v4i{t.x, t.y, t.z, t.w};
     }
   };
-  issue(g0, min(gn, kChunk));
-  if (!XQ) load_a(g0, min(gn, kChunk));
-
-  // XQ: x with whole-line loads.  Lane l takes row l/16 and, for t < kXT,
-  // the 16 bytes of values 8*(l%8)..+7 of slice group 2t + (l%16)/8, so
-  // the 16 lanes of a row read 256 contiguous bytes per instruction.
+  // XQ: x with whole-line loads, issued before the weight DMA (load
+  // counters retire in order, so the absmax below then waits for x alone).
+  // Lane l takes row l/16 and, for t < kXT, the 16 bytes of values
+  // 8*(l%8)..+7 of slice group 2t + (l%16)/8, so the 16 lanes of a row read
+  // 256 contiguous bytes per instruction.
   const int xr = lane >> 4, xj = lane & 15;
   v4i xq[XQ ? kXT : 1];
   if constexpr (XQ) {
@@ -156,6 +161,10 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
       xq[t] = v4i{0, 0, 0, 0};
       if (gi < gn && xr < Mtot) xq[t] = xrow[(g0 + gi) * 8];
     }
+  }
+  issue(g0, min(gn, kChunk));
+  if (!XQ) load_a(g0, min(gn, kChunk));
+  if constexpr (XQ) {
     // Row absmax on the bf16 bit patterns (for finite values the magnitude
     // bits order as |x|), over the row's 16 lanes, then the 8 slices.
     u16x2 mb = u16x2{0, 0};

@@ -110,13 +110,19 @@ __global__ __launch_bounds__(kFusedThreads) void thin_fused_kernel(
     const uint16_t* hs = reinterpret_cast<const uint16_t*>(gsv);
     const uint16_t* hb = reinterpret_cast<const uint16_t*>(gbv);
     const int lim = N * G;
+    // Unconditional loads at a clamped index (lim >= 1): all of them issue
+    // back to back (loads under a per-lane guard were each waited for
+    // before the next one issued).
+    uint16_t sl[kSL], bl[kSL];
 #pragma unroll
     for (int j = 0; j < kSL; ++j) {
-      const int e = tid + j * kFusedThreads;
-      uint32_t v = 0;
-      if (e < lim) v = (uint32_t)hs[e] | ((uint32_t)hb[e] << 16);
-      sreg[j] = v;
+      const int e = min(tid + j * kFusedThreads, lim - 1);
+      sl[j] = hs[e];
+      bl[j] = hb[e];
     }
+#pragma unroll
+    for (int j = 0; j < kSL; ++j)
+      sreg[j] = tid + j * kFusedThreads < lim ? (uint32_t)sl[j] | ((uint32_t)bl[j] << 16) : 0u;
   }
 
   // 2. x: one whole-line load per group (8 rows x 128 bytes per instruction).
