@@ -148,8 +148,11 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
   // ---- table staging (scales, offsets, group sums of 16 groups)
   uint32_t st_s[C::kSBN], st_b[C::kSBN];
   int32_t st_a[C::kSBM];
-  // Always issues the same number of loads (clamped addresses, values
-  // masked to zero past N, M or G): the ring's vmcnt waits count them.
+  // Always issues the same number of loads (clamped addresses): the ring's
+  // vmcnt waits count them.  The values past N, M or G are zeroed where
+  // they are written, not here: a select at the load lets the compiler sink
+  // the load under a branch and wait for it (and for every ring load in
+  // flight) on the spot.
   auto stage_load = [&](int chunk) {
     const int gbase = chunk * kSG;
 #pragma unroll
@@ -157,34 +160,33 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
       const int e = tid + u * C::kThreads;
       const int col = e / kSG, t = e % kSG;
       const int n = n0 + col, g = gbase + t;
-      const bool ok = n < N && g < G;
       const int64_t idx = (int64_t)min(n, N - 1) * Gall + min(g, G - 1);
-      const uint32_t s = GS[idx], b = GB[idx];
-      st_s[u] = ok ? s : 0u;
-      st_b[u] = ok ? b : 0u;
+      st_s[u] = GS[idx];
+      st_b[u] = GB[idx];
     }
 #pragma unroll
     for (int u = 0; u < C::kSBM; ++u) {
       const int e = tid + u * C::kThreads;
       const int row = e / kSG, t = e % kSG;
       const int m = m0 + row, g = gbase + t;
-      const int32_t v = gsum[(int64_t)min(m, M - 1) * Gall + min(g, G - 1)];
-      st_a[u] = (m < M && g < G) ? v : 0;
+      st_a[u] = gsum[(int64_t)min(m, M - 1) * Gall + min(g, G - 1)];
     }
   };
-  auto stage_write = [&](int buf) {
+  auto stage_write = [&](int buf, int chunk) {
+    const int gbase = chunk * kSG;
 #pragma unroll
     for (int u = 0; u < C::kSBN; ++u) {
       const int e = tid + u * C::kThreads;
       const int col = e / kSG, t = e % kSG;
-      t_gs[buf][col][t] = (uint16_t)st_s[u];
-      t_gb[buf][col][t] = (uint16_t)st_b[u];
+      const bool ok = n0 + col < N && gbase + t < G;
+      t_gs[buf][col][t] = ok ? (uint16_t)st_s[u] : (uint16_t)0;
+      t_gb[buf][col][t] = ok ? (uint16_t)st_b[u] : (uint16_t)0;
     }
 #pragma unroll
     for (int u = 0; u < C::kSBM; ++u) {
       const int e = tid + u * C::kThreads;
       const int row = e / kSG, t = e % kSG;
-      const int v = st_a[u];
+      const int v = (m0 + row < M && gbase + t < G) ? st_a[u] : 0;
       const int hi = v >> 6;        // floor(v / 64)
       const int lo = v - hi * 64;   // 0..63
       t_as[buf][row][t] = __half_as_ushort(__float2half_rn((float)(hi * 64)));
@@ -286,7 +288,7 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
     if (kt < KT) compute(cur, kt);
     if (kScaled && S == 8) {
       const int c = kt / kSG + 1;
-      if (c * kSG < G) stage_write(c & 1);
+      if (c * kSG < G) stage_write(c & 1, c);
     }
     if (kScaled && S == kSG - 1) {
       if (kt < KT) offset_mfmas((kt / kSG) & 1);
@@ -299,7 +301,7 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
   // prologue: table chunk 0, ring steps 0..3
   if (kScaled) {
     stage_load(0);
-    stage_write(0);
+    stage_write(0, 0);
   }
   issue(lds0, 0);
   issue(lds1, 1);
@@ -352,16 +354,25 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
     const int sidx = wave / kPerSlot;
     char* stage = reinterpret_cast<char*>(sidx == 0 ? lds0 : sidx == 1 ? lds1 : sidx == 2 ? lds2 : lds3) +
                   (wave % kPerSlot) * kStage;
+    // The lane's token scales and biases, loaded together up front (loaded
+    // at their uses, each waited for before the next one issued).
+    float s_m[C::kTM][4], b_n[C::kTN];
+#pragma unroll
+    for (int j = 0; j < C::kTM; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_m[j][r] = sx[m0 + wm * WTM + 16 * j + 4 * fc + r];
+#pragma unroll
+    for (int i = 0; i < C::kTN; ++i) b_n[i] = bias != nullptr ? bias[n0 + q_col0 + 16 * i] : 0.0f;
 #pragma unroll
     for (int i = 0; i < C::kTN; ++i) {
       const int cl = 16 * i + fr;  // column within the block
-      const float bv = bias != nullptr ? bias[n0 + q_col0 + 16 * i] : 0.0f;
+      const float bv = b_n[i];
 #pragma unroll
       for (int j = 0; j < C::kTM; ++j) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int rl = 16 * j + 4 * fc + r;  // row within the block
-          float v = fmaf(sx[m0 + wm * WTM + rl], acc[i][j][r], bv);
+          float v = fmaf(s_m[j][r], acc[i][j][r], bv);
           if (GATED)
             v = gated1(v, ep.residual, ep.gate, ep.gate_rows, m0 + wm * WTM + rl, n0 + q_col0 + 16 * i, N);
           *reinterpret_cast<uint16_t*>(stage + rl * (WTN * 2) + (((cl >> 3) ^ (rl & 7)) * 16) +
