@@ -334,6 +334,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
     float s_m[C::kTM];
 #pragma unroll
     for (int j = 0; j < C::kTM; ++j) s_m[j] = sx[m0 + wm * C::kWTM + j * 16 + fr];
+    // Channel scales and biases of every column group, loaded together up
+    // front (loaded per group, each group was waited for before the next
+    // one issued).  sw and bias are only 4-byte aligned by contract: scalar
+    // loads.
+    float4 swq[C::kTN], bq[C::kTN];
+#pragma unroll
+    for (int i = 0; i < C::kTN; ++i) {
+      const int n = n0 + wn * C::kWTN + i * 16 + fc * 4;
+      swq[i] = make_float4(sw[n], sw[n + 1], sw[n + 2], sw[n + 3]);
+      bq[i] = bias ? make_float4(bias[n], bias[n + 1], bias[n + 2], bias[n + 3])
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    asm volatile("" ::: "memory");  // (the compiler would sink them back to their uses)
     // Gated: the residual block goes into the stage at the places its
     // outputs take (each lane then reads its 4 values where it writes the
     // result); a tile whose rows share one gate row reads that row once per
@@ -359,10 +372,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
         const float* gr = ep.gate + (int64_t)(m0 / ep.gate_rows) * N + n;
         g4[0] = gr[0]; g4[1] = gr[1]; g4[2] = gr[2]; g4[3] = gr[3];
       }
-      // sw and bias are only 4-byte aligned by contract: scalar loads
-      const float4 swv = make_float4(sw[n], sw[n + 1], sw[n + 2], sw[n + 3]);
-      const float4 bv = bias ? make_float4(bias[n], bias[n + 1], bias[n + 2], bias[n + 3])
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 swv = swq[i];
+      const float4 bv = bq[i];
       const int c = 2 * i + (fc >> 1);  // 16-byte chunk of the block row
 #pragma unroll
       for (int j = 0; j < C::kTM; ++j) {
