@@ -141,14 +141,22 @@ __global__ __launch_bounds__(256) void sage_v_transpose(const uint16_t* __restri
   const int bh = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
   __shared__ uint16_t sv[kSageKTile][kSageD + 8];
   const uint16_t* vb = v + (int64_t)(bh / H) * st.b + (int64_t)(bh % H) * st.h;
+  // loads at clamped rows, all issued before any is used (guarded loads
+  // were each waited for before the next one issued); keys past Lk -> 0
+  uint4 u[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 256 * i;
+    const int t = blk * kSageKTile + (e >> 4);
+    u[i] = *reinterpret_cast<const uint4*>(vb + (int64_t)min(t, Lk - 1) * st.l + 8 * (e & 15));
+  }
+  asm volatile("" ::: "memory");
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = tid + 256 * i;
     const int key = e >> 4, c = e & 15;
     const int t = blk * kSageKTile + key;
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (t < Lk) u = *reinterpret_cast<const uint4*>(vb + (int64_t)t * st.l + 8 * c);
-    *reinterpret_cast<uint4*>(&sv[key][8 * c]) = u;
+    *reinterpret_cast<uint4*>(&sv[key][8 * c]) = t < Lk ? u[i] : make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
   uint16_t* out = vt + ((int64_t)bh * nblk + blk) * kSageD * kSageKTile;
