@@ -449,8 +449,19 @@ __global__ __launch_bounds__(256) void splitk_fold4(const float* __restrict__ P,
   const int64_t MN = (int64_t)M * N;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= MN) return;
-  float acc = P[e];
-  for (int s = 1; s < S; ++s) acc += P[s * MN + e];
+  // Four slices' loads at a time, all issued before they are added, in
+  // slice order (a load-add loop waited for each load before issuing the
+  // next); indices past the last slice are clamped and not added.
+  float acc = 0.0f;
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = P[(int64_t)min(s0 + j, S - 1) * MN + e];
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (s0 + j < S) acc = (s0 + j == 0) ? v[j] : acc + v[j];
+  }
   const int m = (int)(e / N), n = (int)(e % N);
   float v = fmaf(sx[m], acc, bias != nullptr ? bias[n] : 0.0f);
   if (GATED) v = gated1(v, ep.residual, ep.gate, ep.gate_rows, m, n, N);

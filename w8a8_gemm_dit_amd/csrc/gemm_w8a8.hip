@@ -498,8 +498,19 @@ __global__ __launch_bounds__(256) void splitk_fold(const int32_t* __restrict__ P
   const int64_t MN = (int64_t)M * N;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= MN) return;
+  // Four slices' loads at a time, all issued before they are added (a
+  // load-add loop waited for each load before issuing the next); indices
+  // past the last slice are clamped and their values not added.
   int32_t acc = 0;
-  for (int s = 0; s < S; ++s) acc += P[s * MN + e];
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    int32_t v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = P[(int64_t)min(s0 + j, S - 1) * MN + e];
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (s0 + j < S) acc += v[j];
+  }
   if (OUT == kOutI32) {
     reinterpret_cast<int32_t*>(y)[e] = acc;
     return;
