@@ -10,16 +10,9 @@
 namespace kq {
 namespace {
 
-// An fp16 bit pattern as a whole number of 2^-24 units (exact for finite
-// values: the smallest subnormal is 2^-24, the largest value < 2^16).
-__device__ __forceinline__ int64_t f16_units(uint32_t u) {
-  const int e = (u >> 10) & 31;
-  const int64_t m = u & 1023;
-  const int64_t mag = e ? ((1024 + m) << (e - 1)) : m;
-  return (u & 0x8000u) ? -mag : mag;
-}
-
-// Per (b*h, chunk of 256 tokens): the int64 column sums of the keys.
+// Per (b*h, chunk of 256 tokens): the column sums of the keys as int64
+// counts of 2^-24 (every fp16 value is a whole number of them, so the sums
+// are exact).
 // Thread t reads channels 8*(t%16)..+7 of rows t/16, t/16 + 16, ... with
 // 16-byte loads; the 16 row lanes of a channel group then add up in LDS.
 __global__ __launch_bounds__(256) void sage_k_colsum(const uint16_t* __restrict__ k,
@@ -30,19 +23,37 @@ __global__ __launch_bounds__(256) void sage_k_colsum(const uint16_t* __restrict_
   const uint16_t* kb = k + (int64_t)(bh / H) * st.b + (int64_t)(bh % H) * st.h + 8 * cg;
   const int t0 = blockIdx.x * kSageChunk;
   const int t1 = min(Lk, t0 + kSageChunk);
-  int64_t s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int t = t0 + rl; t < t1; t += 16) {
-    const uint4 u = *reinterpret_cast<const uint4*>(kb + (int64_t)t * st.l);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  // The lane's 16 rows are summed in fp64, exactly: every fp16 value is a
+  // multiple of 2^-24 below 2^16, so the partial sums need at most 45 of
+  // fp64's 53 significant bits.  One conversion to units per channel
+  // follows (3 VALU operations per value instead of the ~12 of an integer
+  // conversion each).
+  // Rows go in batches of 8 loads (clamped to the last token, masked
+  // after), all issued before any is added: a load-add loop waited for each
+  // load before issuing the next.
+  double s[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  constexpr int kBatch = 8;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      s[2 * j] += f16_units(w[j] & 0xFFFFu);
-      s[2 * j + 1] += f16_units(w[j] >> 16);
+  for (int b = 0; b < kSageChunk / 16; b += kBatch) {
+    uint4 u[kBatch];
+#pragma unroll
+    for (int it = 0; it < kBatch; ++it)
+      u[it] = *reinterpret_cast<const uint4*>(kb + (int64_t)min(t0 + rl + 16 * (b + it), Lk - 1) * st.l);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int it = 0; it < kBatch; ++it) {
+      if (t0 + rl + 16 * (b + it) >= t1) continue;
+      const uint32_t w[4] = {u[it].x, u[it].y, u[it].z, u[it].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s[2 * j] += (double)__half2float(__ushort_as_half((uint16_t)(w[j] & 0xFFFFu)));
+        s[2 * j + 1] += (double)__half2float(__ushort_as_half((uint16_t)(w[j] >> 16)));
+      }
     }
   }
   __shared__ int64_t red[16][kSageD];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) red[rl][8 * cg + i] = s[i];
+  for (int i = 0; i < 8; ++i) red[rl][8 * cg + i] = (int64_t)(s[i] * 16777216.0);  // exact
   __syncthreads();
   if (tid < kSageD) {
     int64_t tot = 0;
