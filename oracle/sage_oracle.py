@@ -126,6 +126,22 @@ def attention_from_codes(qc, sq, kc, sk, v_f16, scale: float):
     return P @ v, P @ np.abs(v)
 
 
+def attention_terms(qc, sq, kc, sk, v_f16, scale: float):
+    """(T fp64 [Lq, D], U fp64 [Lq, D]): the two magnitudes against which an
+    evaluation with fp16-rounded probabilities and fp32 accumulation is
+    accurate.  T = softmax(S) |V|; U = sum_j |V_j| / l with l = sum_j
+    exp(S_j - max_j S), the softmax normalizer relative to the row max
+    (probabilities in the fp16 subnormal range lose absolute precision
+    2^-25 each, relative to that normalizer)."""
+    S = scores_exact(qc, sq, kc, sk, scale)
+    e = np.exp(S - S.max(axis=1, keepdims=True))
+    l = e.sum(axis=1)
+    av = np.abs(np.asarray(v_f16).astype(np.float64))
+    T = (e / l[:, None]) @ av
+    U = av.sum(axis=0)[None, :] / l[:, None]
+    return T, U
+
+
 def sage_attention_head(q_f16, k_f16, v_f16, scale: float, q_block: int, k_block: int):
     """The whole method for one (batch, head): (O fp64 [Lq, D], T fp64
     [Lq, D]) as attention_from_codes."""

@@ -60,10 +60,8 @@ def _vt_expected(v_head, lk_pad):
 
 
 def _check_out(o_gpu, qc, sq, kc, sk, v_head, scale, what):
-    O, T = S.attention_from_codes(qc, sq, kc, sk, v_head, scale)
-    Sc = S.scores_exact(qc, sq, kc, sk, scale)
-    l = np.exp(Sc - Sc.max(axis=1, keepdims=True)).sum(axis=1)
-    U = np.abs(v_head.astype(np.float64)).sum(axis=0)[None, :] / l[:, None]
+    O, _ = S.attention_from_codes(qc, sq, kc, sk, v_head, scale)
+    T, U = S.attention_terms(qc, sq, kc, sk, v_head, scale)
     Lk = v_head.shape[0]
     g = o_gpu.astype(np.float64)
     tol = S.f16_ulp(S.round_f16(O)) + (2.0 ** -10 + Lk * 2.0 ** -24) * (T + np.abs(O)) + 2.0 ** -25 * U

@@ -476,3 +476,152 @@ def test_gated_residual_integer_grid_is_exact_arithmetic():
     assert np.array_equal(out, ref)
     T = oracle.gated_magnitude(oracle.w8a8_magnitude(_bits(x), q8, sw, bias), _bits(r), gate, L)
     assert np.all(T >= np.abs(out) - 1e-9)
+
+
+# ------------------------------------- tolerance scales, pinned on both sides
+# The term magnitudes T set every fp32 bar (1e-5 * max(|y|, T)) and the bf16
+# cancellation fallback of the GPU parity tests, so an inflated T would
+# loosen every bar.  Each is pinned from above as well as from below: exact
+# equality with Python-integer / rational sums on integer grids, an identity
+# with the oracle's independently pinned result, and elementwise
+# triangle-inequality bounds on random inputs small enough (tiny token
+# scales) that a missing scale factor cannot hide under them.
+def _grid_w4(rng, n, k):
+    """int4 weights that are exactly gs*q + gb (gs a power of two, gb fp16)."""
+    q = rng.integers(0, 16, size=(n, k)).astype(np.uint8)
+    q[:, 0::64] = 0
+    q[:, 1::64] = 15
+    g = np.arange(k) // 64
+    s = (2.0 ** -rng.integers(6, 10, size=(n, k // 64))).astype(np.float32)
+    b = np.float16(rng.standard_normal((n, k // 64)) * 0.05).astype(np.float32)
+    return s[:, g] * q + b[:, g], q, s, b
+
+
+def test_w8a8_magnitude_equals_integer_terms_on_grid():
+    # sx = sw = 1 on the integer grid: T = |acc| + |bias| in Python integers
+    rng = np.random.default_rng(33)
+    m, k, n = 5, 192, 7
+    x = rng.integers(-127, 128, size=(m, k)).astype(np.float32)
+    x[:, 2] = -127.0
+    w = rng.integers(-127, 128, size=(n, k)).astype(np.float32)
+    w[:, 7] = 127.0
+    bias = rng.integers(-5000, 5000, size=n).astype(np.float32)
+    q8, sw = oracle.quantize_w8(w)
+    T = oracle.w8a8_magnitude(_bits(x), q8, sw, bias)
+    for i in range(m):
+        for j in range(n):
+            acc = sum(int(x[i, kk]) * int(w[j, kk]) for kk in range(k))
+            assert T[i, j] == abs(acc) + abs(int(bias[j]))
+
+
+def test_w4a8_magnitude_equals_rational_terms_on_grid():
+    # x on the integer grid (sx = 1) and w = gs*q + gb exactly: T is the
+    # rational sum over groups of |gs*P| + |gb*A| plus |bias|, every term a
+    # dyadic number, so the fp64 value must be exact
+    rng = np.random.default_rng(34)
+    m, k, n = 4, 256, 5
+    w, q, s, b = _grid_w4(rng, n, k)
+    x = rng.integers(-127, 128, size=(m, k)).astype(np.float32)
+    x[:, 0] = 127.0
+    bias = np.float32(rng.standard_normal(n) * 0.1)
+    _, gs, gb, q2 = oracle.quantize_w4(w)
+    assert np.array_equal(q2, q)
+    T = oracle.w4a8_magnitude(_bits(x), q2, gs, gb, bias)
+    for i in range(m):
+        for j in range(n):
+            want = abs(Fraction(float(bias[j])))
+            for g in range(k // 64):
+                ks = range(64 * g, 64 * g + 64)
+                P = sum(int(x[i, kk]) * int(q[j, kk]) for kk in ks)
+                A = sum(int(x[i, kk]) for kk in ks)
+                want += abs(Fraction(float(s[j, g])) * P) + abs(Fraction(float(b[j, g])) * A)
+            assert Fraction(float(T[i, j])) == want
+
+
+def test_w8a8_magnitude_is_the_terms_of_the_result():
+    # y = sx*sw*acc + bias, so T = |sx*sw*acc| + |bias| = |y - bias| + |bias|
+    # (y pinned independently above), to fp64 rounding
+    m, k, n = 12, 320, 20
+    xb = synth.random_bf16((m, k), 35, scale=0.01, dist="student_t4")
+    w = synth.random_f32((n, k), 36, scale=0.02)
+    bias = synth.random_f32((n,), 37, scale=0.1)
+    q8, sw = oracle.quantize_w8(w)
+    y = oracle.w8a8_linear_exact(xb, q8, sw, bias)
+    T = oracle.w8a8_magnitude(xb, q8, sw, bias)
+    want = np.abs(y - bias.astype(np.float64)) + np.abs(bias.astype(np.float64))
+    assert np.all(np.abs(T - want) <= 4 * 2.0 ** -52 * want)
+
+
+@pytest.mark.parametrize("fmt", ["w8", "w4"])
+def test_magnitudes_between_result_and_elementwise_sums(fmt):
+    # From below: T >= |y - bias| + |bias|.  From above, by the triangle
+    # inequality on the dequantized operands: |sx*sw*acc| <= sum_k
+    # |x_hat||w_hat|; |gs*P| + |gb*A| <= sum_{k in g} |a|(|gs*q| + |gb|).
+    # The activations are small (sx ~ 3e-4), so a magnitude that lost its
+    # token scale, or was scaled up, lands above the bound.
+    m, k, n = 10, 384, 24
+    xb = synth.random_bf16((m, k), 38, scale=0.01)
+    w = synth.random_f32((n, k), 39, scale=0.02)
+    bias = synth.random_f32((n,), 40, scale=0.1)
+    a, sx, _ = oracle.quantize_act(xb)
+    b64 = np.abs(bias.astype(np.float64))
+    if fmt == "w8":
+        q8, sw = oracle.quantize_w8(w)
+        y = oracle.w8a8_linear_exact(xb, q8, sw, bias)
+        T = oracle.w8a8_magnitude(xb, q8, sw, bias)
+        xh = sx.astype(np.float64)[:, None] * a.astype(np.float64)
+        upper = np.abs(xh) @ np.abs(oracle.dequant_w8(q8, sw)).T + b64
+    else:
+        _, gs, gb, q = oracle.quantize_w4(w)
+        y = oracle.w4a8_linear_exact(xb, q, gs, gb, bias)
+        T = oracle.w4a8_magnitude(xb, q, gs, gb, bias)
+        g = np.arange(k) // 64
+        wabs = (np.abs(gs.astype(np.float64)[:, g] * q) + np.abs(gb.astype(np.float64))[:, g])
+        upper = sx.astype(np.float64)[:, None] * (np.abs(a.astype(np.float64)) @ wabs.T) + b64
+    lower = np.abs(y - bias.astype(np.float64)) + b64
+    assert np.all(T >= lower * (1 - 1e-12))
+    assert np.all(T <= upper * (1 + 1e-12))
+    assert np.max(upper / T) < 200       # the upper bound is not vacuous
+
+
+def test_gated_magnitude_equals_integer_terms_on_grid():
+    # integer grid, integer residuals, power-of-two gates shared by 2 rows:
+    # T_gated = |r| + |g| * (|acc| + |bias|) in Python integers and dyadics
+    rng = np.random.default_rng(41)
+    m, k, n, L = 6, 128, 5, 2
+    x = rng.integers(-127, 128, size=(m, k)).astype(np.float32)
+    x[:, 1] = 127.0
+    w = rng.integers(-127, 128, size=(n, k)).astype(np.float32)
+    w[:, 4] = -127.0
+    bias = rng.integers(-300, 300, size=n).astype(np.float32)
+    gate = (2.0 ** rng.integers(-3, 4, size=(m // L, n))).astype(np.float32)
+    gate[1, 2] = -4.0
+    r = rng.integers(-200, 200, size=(m, n)).astype(np.float32)
+    q8, sw = oracle.quantize_w8(w)
+    T = oracle.gated_magnitude(oracle.w8a8_magnitude(_bits(x), q8, sw, bias), _bits(r), gate, L)
+    for i in range(m):
+        for j in range(n):
+            acc = sum(int(x[i, kk]) * int(w[j, kk]) for kk in range(k))
+            want = abs(int(r[i, j])) + abs(Fraction(float(gate[i // L, j]))) * (abs(acc) + abs(int(bias[j])))
+            assert Fraction(float(T[i, j])) == want
+
+
+def test_gated_magnitude_between_result_and_elementwise_sums():
+    m, k, n, L = 8, 256, 12, 3
+    xb = synth.random_bf16((m, k), 42, scale=0.01)
+    w = synth.random_f32((n, k), 43, scale=0.02)
+    bias = synth.random_f32((n,), 44, scale=0.1)
+    gate = synth.random_f32((-(-m // L), n), 45, scale=0.5)
+    r = synth.random_bf16((m, n), 46)
+    q8, sw = oracle.quantize_w8(w)
+    y = oracle.w8a8_linear_exact(xb, q8, sw, bias)
+    out = oracle.gated_residual_exact(y, r, gate, L)
+    T = oracle.gated_magnitude(oracle.w8a8_magnitude(xb, q8, sw, bias), r, gate, L)
+    a, sx, _ = oracle.quantize_act(xb)
+    xh = sx.astype(np.float64)[:, None] * a.astype(np.float64)
+    lin_upper = np.abs(xh) @ np.abs(oracle.dequant_w8(q8, sw)).T + np.abs(bias.astype(np.float64))
+    rows = np.arange(m) // L
+    upper = (np.abs(oracle.bf16_bits_to_f32(r).astype(np.float64))
+             + np.abs(gate.astype(np.float64))[rows] * lin_upper)
+    assert np.all(T >= np.abs(out) * (1 - 1e-12))
+    assert np.all(T <= upper * (1 + 1e-12))

@@ -187,7 +187,11 @@ def test_pure_python_loops_on_a_tiny_head():
     v = _f16(rng.standard_normal((Lk, 128)))
     scale = 0.2
     qc, sq, kc, sk, _ = S.prepare(q, k, 2, 3)
-    O, _ = S.attention_from_codes(qc, sq, kc, sk, v, scale)
+    O, T0 = S.attention_from_codes(qc, sq, kc, sk, v, scale)
+    T, U = S.attention_terms(qc, sq, kc, sk, v, scale)
+    # the tolerance magnitudes, pinned on both sides: T = P|V| and
+    # U = sum_j |V_j| / l (l = sum_j exp(S_j - max))
+    assert np.array_equal(T, T0)
     for i in range(Lq):
         s = []
         for j in range(Lk):
@@ -199,6 +203,9 @@ def test_pure_python_loops_on_a_tiny_head():
         for d in range(128):
             want = math.fsum(e[j] * float(v[j, d]) for j in range(Lk)) / tot
             assert abs(O[i, d] - want) <= 1e-13 * (1 + abs(want))
+            t = math.fsum(e[j] * abs(float(v[j, d])) for j in range(Lk)) / tot
+            u = math.fsum(abs(float(v[j, d])) for j in range(Lk)) / tot
+            assert abs(T[i, d] - t) <= 1e-13 * t and abs(U[i, d] - u) <= 1e-13 * u
 
 
 def test_score_error_bound_against_unquantized_smoothed_scores():
