@@ -344,10 +344,11 @@ typedef enum kq_layout {
  *                key 4g+i for i < 4, key 16+4g+(i-4) for i >= 4), zero
  *                past Lk
  *   kmean fp32  [BH][128]          the key means
- *   colsum int64 [BH][chunks][128] partial key sums (units of 2^-24) */
+ *   colsum int64 [BH][chunks][128] partial key sums (units of 2^-24)
+ *   meta  int32 [4]                {k_block, q_block} of the preparation */
 typedef struct kq_sage_workspace {
     int64_t lq_pad, lk_pad, chunks;
-    size_t qc, sq, kc, sk, vt, kmean, colsum, total;
+    size_t qc, sq, kc, sk, vt, kmean, colsum, meta, total;
 } kq_sage_workspace;
 
 kq_status kq_sage_workspace_layout(int64_t B, int64_t H, int64_t Lq, int64_t Lk,
@@ -361,9 +362,14 @@ kq_status kq_sage_prepare(const void* q, const void* k, const void* v, int64_t B
                           void* ws, size_t ws_bytes, void* stream);
 
 /* The attention alone, on a workspace kq_sage_prepare filled for the same
- * B, H, Lq, Lk and k_block (k_block >= 64 lets every 64-key step use one
- * key scale; a k_block other than the one the workspace was prepared with
- * gives wrong results). */
+ * B, H, Lq and Lk.  k_block >= 64 asserts that every 64-key step shares one
+ * key scale and takes the faster kernel for it; the kernel checks that
+ * assertion against the key block the preparation recorded in the
+ * workspace (meta) and, on a workspace prepared with a smaller k_block,
+ * writes NaN to every output element instead of wrong values (the host
+ * cannot read the workspace without synchronizing, so the mismatch cannot
+ * be returned as a status).  A k_block below 64 is correct on any prepared
+ * workspace. */
 kq_status kq_sage_attend(const void* ws, size_t ws_bytes, void* out, int64_t B,
                          int64_t H, int64_t Lq, int64_t Lk, int64_t D,
                          kq_layout layout, float scale, int64_t k_block,
@@ -374,6 +380,30 @@ kq_status kq_sage_attention(const void* q, const void* k, const void* v, void* o
                             int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
                             kq_layout layout, float scale, int64_t q_block,
                             int64_t k_block, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement probes: the machine's own floors beside its published peaks,
+ * for roofline figures (mlx-kquant pull request 89 commit list: a DiT-shape
+ * harness with a three-floor roofline).  They compute nothing of the
+ * method.
+ * ------------------------------------------------------------------------ */
+
+/* Streaming read of `bytes` at src (device, 16-byte aligned, bytes a
+ * multiple of 16), split into `grid` equal contiguous ranges, one per
+ * workgroup of `threads` (64..1024, a multiple of 64) threads, with 16-byte
+ * non-temporal loads.  sink: device uint32 [grid]; it is written only if a
+ * data-dependent test that practically never holds succeeds, so the probe
+ * moves the buffer's bytes and writes (almost surely) nothing.  Timing it
+ * gives the HBM read rate a kernel with that grid can reach. */
+kq_status kq_probe_read(const void* src, int64_t bytes, int64_t grid,
+                        int32_t threads, uint32_t* sink, void* stream);
+
+/* iters x 8 v_mfma_i32_16x16x64_i8 per wavefront on register operands, 8
+ * wavefronts per workgroup, `grid` workgroups: 2^18 * iters * grid integer
+ * operations (a multiply-add counted as two) with no memory traffic.
+ * sink: device int32 [grid], written as for kq_probe_read. */
+kq_status kq_probe_mfma_i8(int64_t iters, int64_t grid, int32_t* sink,
+                           void* stream);
 
 #ifdef __cplusplus
 }

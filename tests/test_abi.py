@@ -24,7 +24,7 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     L = kq.lib()
     declared = _declared_functions()
-    assert len(declared) == 16, declared
+    assert len(declared) == 18, declared
     assert sorted(kq.exported_symbols) == declared
     for name in declared:
         assert hasattr(L, name), name
@@ -265,9 +265,10 @@ def test_gated_linear_validation_without_device():
 def test_sage_workspace_layout():
     lay = kq.kq_sage_workspace_layout(2, 3, 300, 777)
     assert lay["lq_pad"] == 384 and lay["lk_pad"] == 896 and lay["chunks"] == 4
-    order = ["qc", "sq", "kc", "sk", "vt", "kmean", "colsum"]
+    order = ["qc", "sq", "kc", "sk", "vt", "kmean", "colsum", "meta"]
     sizes = {"qc": 6 * 384 * 128, "sq": 6 * 384 * 4, "kc": 6 * 896 * 128, "sk": 6 * 896 * 4,
-             "vt": 6 * 896 * 128 * 2, "kmean": 6 * 128 * 4, "colsum": 6 * 4 * 128 * 8}
+             "vt": 6 * 896 * 128 * 2, "kmean": 6 * 128 * 4, "colsum": 6 * 4 * 128 * 8,
+             "meta": 16}
     for a, b in zip(order, order[1:] + ["total"]):
         assert lay[a] % 256 == 0 and lay[b] - lay[a] >= sizes[a] and lay[b] - lay[a] < sizes[a] + 256
     with pytest.raises(ValueError):

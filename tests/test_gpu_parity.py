@@ -324,51 +324,98 @@ def test_deterministic_bits():
 
 
 # ------------------------------------------------------ full-size workloads
-def _sample_rows(M, rng):
-    rows = {0, 1, M // 2, M - 2, M - 1}
-    rows.update(int(r) for r in rng.integers(0, M, size=4))
-    return np.array(sorted(r for r in rows if 0 <= r < M))
+def _workers():
+    n = len(os.sched_getaffinity(0))
+    return max(1, min(8, n // 2))
 
 
 @pytest.mark.parametrize("name", [n for n in synth.WORKLOADS])
-def test_workload_full_size_sampled_rows(name):
-    """Full-size launch (as the benchmark runs it); the weights are checked
-    bit-exact in full and the outputs on sampled rows, which the oracle can
-    compute on their own because quantization is per row."""
+def test_workload_full_size_every_row(name):
+    """Full-size launch, as the benchmark runs it: the weights bit-exact in
+    full and EVERY output element against the oracle (computed by blocks of
+    rows, which the per-row quantization makes independent).  The MLP down
+    projection takes the oracle's up projection output as its input."""
+    from tests import fullsize
+
     wl = synth.WORKLOADS[name]
-    print(f"[parity] workload {name}", flush=True)
-    xb = synth.activations(wl)
+    print(f"[parity] workload {name} (every row)", flush=True)
     w = synth.weights(wl)
     b = synth.bias(wl)
-    rows = _sample_rows(wl.M, np.random.default_rng(0))
-    wd = dev(w)
     out_dt = torch.float32 if wl.out == "f32" else torch.bfloat16
-    x = dev_bf16(xb)
+    wd = dev(w)
     if wl.fmt == "w8":
         q8, sw, _ = kq.kq_quantize_weights(wd, kq.KQ_W8_PER_CHANNEL)
-        del wd
-        y = kq.kq_w8a8_linear(x, q8, sw, dev(b), out_dtype=out_dt)
-        q8_ref, sw_ref = oracle.quantize_w8(w)
+        q8_ref, sw_ref = fullsize.quantized_weights(name)
         assert np.array_equal(host(q8), q8_ref)
         assert np.array_equal(host(sw).view(np.uint32), sw_ref.view(np.uint32))
-        y64 = oracle.w8a8_linear_exact(xb[rows], q8_ref, sw_ref, b)
-        T = oracle.w8a8_magnitude(xb[rows], q8_ref, sw_ref, b)
+        run = lambda x: kq.kq_w8a8_linear(x, q8, sw, dev(b), out_dtype=out_dt)  # noqa: E731
     else:
         p, gs, gb = kq.kq_quantize_weights(wd, kq.KQ_W4_AFFINE_G64)
-        del wd
-        y = kq.kq_w4a8_linear(x, p, gs, gb, dev(b), out_dtype=out_dt)
-        p_ref, gs_ref, gb_ref, q_ref = oracle.quantize_w4(w)
+        p_ref, gs_ref, gb_ref, _ = fullsize.quantized_weights(name)
         assert np.array_equal(host(p), p_ref)
         assert np.array_equal(host(gs).view(np.uint16), gs_ref.view(np.uint16))
         assert np.array_equal(host(gb).view(np.uint16), gb_ref.view(np.uint16))
-        y64 = oracle.w4a8_linear_exact(xb[rows], q_ref, gs_ref, gb_ref, b)
-        T = oracle.w4a8_magnitude(xb[rows], q_ref, gs_ref, gb_ref, b)
-    ys = y[torch.from_numpy(rows).cuda()]
+        run = lambda x: kq.kq_w4a8_linear(x, p, gs, gb, dev(b), out_dtype=out_dt)  # noqa: E731
+    del wd
+    got = list(fullsize.blocks(name, wl.M, 2048 if wl.fmt == "w8" else 256, _workers()))
+    xb = np.concatenate([g[2] for g in got])      # the input rows, in order
+    assert xb.shape == (wl.M, wl.K)
+    y = run(dev_bf16(xb))
     torch.cuda.synchronize()
-    if wl.out == "f32":
-        check_f32(host(ys), y64, T, name)
-    else:
-        check_bf16(host_bf16_bits(ys), y64, T, name)
+    y_host = host(y) if wl.out == "f32" else host_bf16_bits(y)
+    for r0, r1, _, y64, T in got:
+        if wl.out == "f32":
+            check_f32(y_host[r0:r1], y64, T, f"{name} rows {r0}:{r1}")
+        else:
+            check_bf16(y_host[r0:r1], y64, T, f"{name} rows {r0}:{r1}")
+
+
+@pytest.mark.parametrize("name,split", [
+    ("dit_proj_w8a8_4096x3072x3072", None),
+    ("dit_4k_w8a8_16384x3072x12288", None),
+    ("short_seq_w8a8_128x12288x3072", None),
+    ("short_seq_w8a8_128x12288x3072", "1"),
+])
+def test_workload_full_size_w8a8_accumulators(name, split, kq_env):
+    """The int32 accumulators of a full-size int8 workload, every element
+    bit-exact: the big tiles' XCD-remapped tile walk at the DiT shapes, and
+    a K = 12288 product both split (the automatic route) and unsplit."""
+    from tests import fullsize
+
+    kq_env(KQ_SPLIT=split)
+    wl = synth.WORKLOADS[name]
+    print(f"[parity] workload {name} int32 accumulators (KQ_SPLIT={split})", flush=True)
+    xb = synth.activations(wl)
+    q8_ref, sw_ref = fullsize.quantized_weights(name)
+    acc = kq.kq_w8a8_linear(dev_bf16(xb), dev(q8_ref), dev(sw_ref), out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    acc = host(acc)
+    for r0 in range(0, wl.M, 2048):
+        r1 = min(wl.M, r0 + 2048)
+        a, _, _ = oracle.quantize_act(xb[r0:r1], with_group_sums=False)
+        assert np.array_equal(acc[r0:r1], oracle.w8a8_acc(a, q8_ref)), (name, r0)
+
+
+@pytest.mark.parametrize("name", ["dit_mlp_up_w4a8_2048x4096x12288",
+                                  "dit_mlp_down_w4a8_2048x12288x4096"])
+def test_workload_full_size_w4a8_group_products(name):
+    """The per-group int32 products P [K/64, M, N] of a full-size int4
+    workload, every element bit-exact (compared one group at a time)."""
+    from tests import fullsize
+
+    wl = synth.WORKLOADS[name]
+    print(f"[parity] workload {name} per-group products", flush=True)
+    xb = synth.activations(wl)          # int products: any input of the shape
+    p_ref, gs_ref, gb_ref, q_ref = fullsize.quantized_weights(name)
+    P = kq.kq_w4a8_linear(dev_bf16(xb), dev(p_ref), dev(gs_ref), dev(gb_ref),
+                          out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    a, _, _ = oracle.quantize_act(xb, with_group_sums=False)
+    for g in range(wl.K // 64):
+        sl = slice(64 * g, 64 * g + 64)
+        want = oracle.w4a8_group_acc(a[:, sl], q_ref[:, sl])[0]
+        assert np.array_equal(host(P[g]), want), (name, g)
+    del P
 
 
 # ------------------------------------------------------- golden fixture

@@ -1,0 +1,106 @@
+"""CPU model of the GEMM kernels' buffer-descriptor reads.
+
+The tiled GEMMs move operand rows global -> LDS through buffer descriptors
+rebased on the tile's first row and the K slice's first code; a read at an
+offset at or past the descriptor's num_records returns zero instead of
+touching memory.  This models the descriptor arithmetic of gemm_w8a8.hip
+and gemm_w4a8.hip for every tile and forced slice count, and checks that
+(1) every byte fetched from memory lies inside the operand buffer, and
+(2) every byte the products use lies below num_records (nothing needed is
+zeroed).  Pure host arithmetic, no GPU.
+"""
+import pytest
+
+# (BM, BN) of the int8 tiles and of the int4 tiles
+W8_TILES = [(256, 256), (256, 192), (256, 128), (128, 128), (64, 64)]
+W4_TILES = [(128, 256), (64, 128)]
+
+
+def split_chunk(K, want, unit):
+    """Slices of `chunk` codes, a multiple of `unit` (kq_route.cpp)."""
+    units = -(-K // unit)
+    if want < 2 or units < 2:
+        return 1, K
+    per = -(-units // want)
+    chunk = per * unit
+    return -(-K // chunk), chunk
+
+
+def _check(rows_total, stride, row0, rows_valid, base_shift, num_records, reads, used):
+    """reads / used: iterables of (row, byte offset within the slice's row)."""
+    size = rows_total * stride
+    base = row0 * stride + base_shift
+    for r, off in reads:
+        rel = r * stride + off
+        if rel < num_records:               # fetched from memory
+            a = base + rel
+            assert 0 <= a < size, (r, off, a, size)
+    for r, off in used:
+        assert r < rows_valid
+        assert r * stride + off < num_records, (r, off, num_records)
+
+
+def _w8_case(M, N, K, BM, BN, splits):
+    sp, kchunk = split_chunk(K, splits, 256)
+    for y in range(sp):
+        k0 = y * kchunk
+        KT = min(kchunk, K - k0) // 64
+        last = max(0, (KT - 1) >> 1) * 128   # pairs past the end re-load the last pair
+        for rows_total, B, t in ((M, BM, "a"), (N, BN, "w")):
+            for t0 in range(0, rows_total, B):
+                rows = min(B, rows_total - t0)
+                nrec = rows * K - k0
+                # every pair buffer load reads 128 bytes of each of the tile's
+                # rows at ks = 0, 128, ..., last (the odd tail's second half
+                # included); rows past the edge lie past num_records
+                ends = [(r, last + 127) for r in range(B)] + [(r, last) for r in range(B)]
+                used = [(r, KT * 64 - 1) for r in range(rows)] + [(r, 0) for r in range(rows)]
+                _check(rows_total, K, t0, rows, k0, nrec, ends, used)
+
+
+def _w4_case(M, N, K, BM, BN, splits):
+    sp, chunk = split_chunk(K, splits, 1024)
+    gchunk = chunk // 64
+    G_all = K // 64
+    for y in range(sp):
+        g0 = y * gchunk
+        G = min(gchunk, G_all - g0)
+        for rows_total, B, stride, per_group in ((M, BM, K, 64), (N, BN, K // 2, 32)):
+            for t0 in range(0, rows_total, B):
+                rows = min(B, rows_total - t0)
+                nrec = rows * stride - g0 * per_group
+                # steps past the slice re-load its last group
+                ends = [(r, G * per_group - 1) for r in range(B)]
+                used = [(r, G * per_group - 1) for r in range(rows)] + [(r, 0) for r in range(rows)]
+                _check(rows_total, stride, t0, rows, g0 * per_group, nrec, ends, used)
+
+
+SHAPES = [(1, 64, 64), (70, 130, 1088), (300, 200, 1344), (256, 192, 4096), (129, 257, 12288),
+          (64, 48, 5120), (17, 1000, 2112)]
+
+
+@pytest.mark.parametrize("tile", W8_TILES)
+@pytest.mark.parametrize("splits", [1, 2, 3, 4, 7, 16])
+def test_w8a8_reads_stay_in_the_operands(tile, splits):
+    for M, N, K in SHAPES:
+        _w8_case(M, N, K, *tile, splits)
+
+
+@pytest.mark.parametrize("tile", W4_TILES)
+@pytest.mark.parametrize("splits", [1, 2, 3, 5, 12])
+def test_w4a8_reads_stay_in_the_operands(tile, splits):
+    for M, N, K in SHAPES:
+        _w4_case(M, N, K, *tile, splits)
+
+
+def test_unfixed_descriptor_is_caught():
+    # the descriptor before the fix (num_records = rows*K with the base moved
+    # by k0) lets the dead half of an odd last slice fetch past the buffer
+    M, N, K, BM, BN = 64, 64, 1088, 64, 64
+    sp, kchunk = split_chunk(K, 2, 256)
+    k0 = (sp - 1) * kchunk
+    KT = (K - k0) // 64
+    assert KT % 2 == 1
+    last = ((KT - 1) >> 1) * 128
+    with pytest.raises(AssertionError):
+        _check(N, K, 0, N, k0, N * K, [(N - 1, last + 127)], [])

@@ -23,7 +23,7 @@ __all__ = [
     "kq_quantize_weights", "kq_quantize_act", "kq_w8a8_linear", "kq_w4a8_linear",
     "kq_gemv_small_m", "kq_w8a8_gemm", "kq_w4a8_gemm", "kq_linear_gated", "KqError",
     "KQ_LAYOUT_BHLD", "KQ_LAYOUT_BLHD", "kq_sage_workspace_layout", "kq_sage_prepare",
-    "kq_sage_attend", "kq_sage_attention",
+    "kq_sage_attend", "kq_sage_attention", "kq_probe_read", "kq_probe_mfma_i8",
 ]
 
 KQ_SUCCESS, KQ_ERR_INVALID_VALUE, KQ_ERR_UNSUPPORTED = 0, 1, 2
@@ -46,7 +46,7 @@ exported_symbols = (
     "kq_quantize_weights", "kq_quantize_act", "kq_w8a8_linear",
     "kq_w4a8_linear", "kq_gemv_small_m", "kq_w8a8_gemm", "kq_w4a8_gemm",
     "kq_linear_gated", "kq_sage_workspace_layout", "kq_sage_prepare", "kq_sage_attend",
-    "kq_sage_attention",
+    "kq_sage_attention", "kq_probe_read", "kq_probe_mfma_i8",
 )
 
 
@@ -64,7 +64,8 @@ class SageWorkspace(ctypes.Structure):
     _fields_ = [("lq_pad", ctypes.c_int64), ("lk_pad", ctypes.c_int64), ("chunks", ctypes.c_int64),
                 ("qc", ctypes.c_size_t), ("sq", ctypes.c_size_t), ("kc", ctypes.c_size_t),
                 ("sk", ctypes.c_size_t), ("vt", ctypes.c_size_t), ("kmean", ctypes.c_size_t),
-                ("colsum", ctypes.c_size_t), ("total", ctypes.c_size_t)]
+                ("colsum", ctypes.c_size_t), ("meta", ctypes.c_size_t),
+                ("total", ctypes.c_size_t)]
 
 
 def lib_path() -> str:
@@ -117,6 +118,10 @@ def lib() -> ctypes.CDLL:
     L.kq_linear_gated.restype = i32
     L.kq_linear_gated.argtypes = [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, i64, vp, i32,
                                   vp, sz, vp]
+    L.kq_probe_read.restype = i32
+    L.kq_probe_read.argtypes = [vp, i64, i64, ctypes.c_int32, vp, vp]
+    L.kq_probe_mfma_i8.restype = i32
+    L.kq_probe_mfma_i8.argtypes = [i64, i64, vp, vp]
     _lib = L
     return L
 
@@ -199,14 +204,28 @@ def kq_quantize_weights(w: torch.Tensor, fmt: int):
     return wq, sc, gb
 
 
-def kq_quantize_act(x: torch.Tensor, group_sums: bool = False):
+def kq_quantize_act(x: torch.Tensor, group_sums: bool = False, out=None):
     """bf16 [M,K] -> (codes int8 [M,K], scales fp32 [M], group sums int32
-    [M,K/64] or None)."""
+    [M,K/64] or None).  out: optional (codes, scales, group sums or None)
+    tensors to write into."""
     _need(x, "x", torch.bfloat16, 2)
     M, K = x.shape
-    a = torch.empty((M, K), dtype=torch.int8, device=x.device)
-    sx = torch.empty((M,), dtype=torch.float32, device=x.device)
-    gs = torch.empty((M, K // 64), dtype=torch.int32, device=x.device) if group_sums else None
+    if out is None:
+        a = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        sx = torch.empty((M,), dtype=torch.float32, device=x.device)
+        gs = torch.empty((M, K // 64), dtype=torch.int32, device=x.device) if group_sums else None
+    else:
+        a, sx, gs = out
+        _need(a, "codes", torch.int8, 2)
+        _need(sx, "scales", torch.float32, 1)
+        if tuple(a.shape) != (M, K) or tuple(sx.shape) != (M,):
+            raise ValueError("out codes / scales have the wrong shape")
+        if group_sums:
+            _need(gs, "group sums", torch.int32, 2)
+            if tuple(gs.shape) != (M, K // 64):
+                raise ValueError("out group sums have the wrong shape")
+        else:
+            gs = None
     _check(lib().kq_quantize_act(_ptr(x), M, K, _ptr(a), _ptr(sx), _ptr(gs), _stream()))
     return a, sx, gs
 
@@ -436,3 +455,26 @@ def kq_sage_attention(q, k, v, scale=None, q_block=128, k_block=64, layout="bhld
                                    _LAYOUTS[layout], scale, q_block, k_block, _ptr(ws), wsb,
                                    _stream()))
     return y
+
+
+# --------------------------------------------------------- measurement probes
+def kq_probe_read(src: torch.Tensor, grid: int, threads: int = 512,
+                  sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Streaming read of all of `src` (any dtype, contiguous, a multiple of
+    16 bytes) over `grid` workgroups; returns the (untouched) sink."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    if sink is None:
+        sink = torch.zeros((grid,), dtype=torch.int32, device=src.device)
+    _check(lib().kq_probe_read(_ptr(src), src.numel() * src.element_size(), grid, threads,
+                               _ptr(sink), _stream()))
+    return sink
+
+
+def kq_probe_mfma_i8(iters: int, grid: int, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """iters x 8 int8 MFMAs per wavefront, 8 wavefronts x `grid` workgroups
+    (2^18 * iters * grid integer operations)."""
+    if sink is None:
+        sink = torch.zeros((grid,), dtype=torch.int32, device="cuda")
+    _check(lib().kq_probe_mfma_i8(iters, grid, _ptr(sink), _stream()))
+    return sink

@@ -112,10 +112,12 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
   if (kScaled && gsum != nullptr) gsum += g0;
   if (OUT == kOutPart) y = reinterpret_cast<float*>(y) + (int64_t)blockIdx.y * M * N;
 
+  // (num_records ends at the last row's end, which lies g0*64 or g0*32
+  // bytes before base + rows*stride once the base moved to the slice)
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(A + (int64_t)m0 * K), 0, min(BM, M - m0) * K, 0x00020000);
+      const_cast<int8_t*>(A + (int64_t)m0 * K), 0, min(BM, M - m0) * K - g0 * 64, 0x00020000);
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(Q + (int64_t)n0 * QB), 0, min(BN, N - n0) * QB, 0x00020000);
+      const_cast<uint8_t*>(Q + (int64_t)n0 * QB), 0, min(BN, N - n0) * QB - g0 * 32, 0x00020000);
 
   // DMA plan: block b = wave + kWaves*i.  Activation block b < kABlk holds
   // rows 16b..16b+15 (lane l: row 16b + l/4, physical chunk l%4 holding

@@ -175,12 +175,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
   W += k0;
   if (OUT == kOutI32) y = reinterpret_cast<int32_t*>(y) + (int64_t)blockIdx.y * M * N;
 
-  // Buffer descriptors rebased on this tile's first row: rows past the
-  // matrix edge fall outside num_records and read as zero.
+  // Buffer descriptors rebased on this tile's first row (and the slice's
+  // first code): rows past the matrix edge fall outside num_records and
+  // read as zero.  num_records ends at the last row's end, K - k0 bytes
+  // into it, so the dead second half of an odd slice's last pair (bytes
+  // past the row end) reads zeros there instead of memory past the buffer.
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(A + (int64_t)m0 * K), 0, min(BM, M - m0) * K, 0x00020000);
+      const_cast<int8_t*>(A + (int64_t)m0 * K), 0, min(BM, M - m0) * K - k0, 0x00020000);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(W + (int64_t)n0 * K), 0, min(BN, N - n0) * K, 0x00020000);
+      const_cast<int8_t*>(W + (int64_t)n0 * K), 0, min(BN, N - n0) * K - k0, 0x00020000);
 
   // DMA plan: wave w < kDmaWaves moves blocks b = w*kLPW + i (rows 8b..8b+7
   // of the pair); lane l fills slot 64*b + l: half h = l/32 (the pair's

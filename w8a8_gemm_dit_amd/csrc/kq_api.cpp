@@ -16,6 +16,7 @@
 //   KQ_FUSE=0           no fused thin-N route (quantize kernel + GEMV instead)
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -530,6 +531,7 @@ kq_status kq_sage_workspace_layout(int64_t B, int64_t H, int64_t Lq, int64_t Lk,
   out->vt = L.vt;
   out->kmean = L.kmean;
   out->colsum = L.colsum;
+  out->meta = L.meta;
   out->total = L.total;
   return KQ_SUCCESS;
 }
@@ -566,6 +568,37 @@ kq_status kq_sage_attention(const void* q, const void* k, const void* v, void* o
                          stream, &empty);
   if (st != KQ_SUCCESS) return st;
   return sage_attend_impl(op, ws, ws_bytes, out, B, H, Lq, Lk, D, layout, scale, k_block, stream);
+}
+
+// ------------------------------------------------------------ probes
+kq_status kq_probe_read(const void* src, int64_t bytes, int64_t grid, int32_t threads,
+                        uint32_t* sink, void* stream) {
+  const char* op = "kq_probe_read";
+  if (bytes < 0 || bytes % 16 != 0)
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] bytes=%lld must be a non-negative multiple of 16", op,
+                (long long)bytes);
+  if (grid < 1 || grid > INT32_MAX || threads < 64 || threads > 1024 || threads % 64 != 0)
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] grid=%lld, threads=%d out of range", op,
+                (long long)grid, (int)threads);
+  if (bytes == 0) return KQ_SUCCESS;
+  if (!src || !sink) return fail(KQ_ERR_INVALID_VALUE, "[%s] null pointer", op);
+  if (!aligned16(src)) return fail(KQ_ERR_INVALID_VALUE, "[%s] src must be 16-byte aligned", op);
+  kq_status st = check_device(op);
+  if (st != KQ_SUCCESS) return st;
+  kq::launch_probe_read(src, bytes, grid, threads, sink, reinterpret_cast<hipStream_t>(stream));
+  return check_launch(op);
+}
+
+kq_status kq_probe_mfma_i8(int64_t iters, int64_t grid, int32_t* sink, void* stream) {
+  const char* op = "kq_probe_mfma_i8";
+  if (iters < 1 || iters > INT32_MAX || grid < 1 || grid > INT32_MAX)
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] iters=%lld, grid=%lld out of range", op,
+                (long long)iters, (long long)grid);
+  if (!sink) return fail(KQ_ERR_INVALID_VALUE, "[%s] null sink", op);
+  kq_status st = check_device(op);
+  if (st != KQ_SUCCESS) return st;
+  kq::launch_probe_mfma((int)iters, grid, sink, reinterpret_cast<hipStream_t>(stream));
+  return check_launch(op);
 }
 
 }  // extern "C"

@@ -65,4 +65,13 @@ const char* launch_thin_fused(bool w4, const uint16_t* x, float* sx, const void*
                               const void* gb, const float* bias, void* y, int out, int M, int N,
                               int K, hipStream_t s, const Epilogue& ep = Epilogue());
 
+// Measurement probes (probe.hip): a streaming read of `bytes` (a multiple
+// of 16) in equal contiguous ranges over `grid` workgroups of `threads`,
+// and `iters` x 8 int8 MFMAs per wavefront over `grid` workgroups of 8
+// wavefronts.  sink: device, at least grid entries, written only if a
+// data-dependent test that practically never holds succeeds.
+const char* launch_probe_read(const void* src, int64_t bytes, int64_t grid, int threads,
+                              uint32_t* sink, hipStream_t s);
+const char* launch_probe_mfma(int iters, int64_t grid, int32_t* sink, hipStream_t s);
+
 }  // namespace kq

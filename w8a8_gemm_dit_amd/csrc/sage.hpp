@@ -38,9 +38,11 @@ struct SageStrides {
 //                product consumes them in
 //   kmean  fp32  [BH][128]        the key means
 //   colsum int64 [BH][nchunk][128] per-chunk key column sums (units 2^-24)
+//   meta   int32 [4]              {k_block, q_block} the preparation used
+//                (the attention checks that the key blocks it assumes match)
 struct SageLayout {
   int64_t BH, Lqp, Lkp, nchunk;
-  size_t qc, sq, kc, sk, vt, kmean, colsum, total;
+  size_t qc, sq, kc, sk, vt, kmean, colsum, meta, total;
 };
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
@@ -64,6 +66,7 @@ inline SageLayout sage_layout(int64_t B, int64_t H, int64_t Lq, int64_t Lk) {
   s.vt = take((size_t)(s.BH * s.Lkp * kSageD * 2));
   s.kmean = take((size_t)(s.BH * kSageD * 4));
   s.colsum = take((size_t)(s.BH * s.nchunk * kSageD * 8));
+  s.meta = take(16);
   s.total = off;
   return s;
 }

@@ -57,12 +57,16 @@ __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 // KUNI: the key scale is uniform over each 64-key step (k_block >= 64), so
 // the exponent is one fma of the converted score and the step's max is an
-// integer max.
+// integer max.  It reads the key block the preparation recorded in the
+// workspace (meta[0]); if that block is shorter than a step, the scales are
+// not uniform and the workgroup writes NaN to its output rows instead of
+// wrong values (the host cannot read the workspace without a sync).
 template <bool KUNI>
 __global__ __launch_bounds__(kWaves * 64) void sage_attn_kernel(
     const int8_t* __restrict__ qc, const float* __restrict__ sqs, const int8_t* __restrict__ kc,
     const float* __restrict__ sks, const uint16_t* __restrict__ vt, uint16_t* __restrict__ out,
-    SageStrides so, int H, int Lq, int Lk, int Lqp, int Lkp, float c_log2) {
+    SageStrides so, int H, int Lq, int Lk, int Lqp, int Lkp, float c_log2,
+    const int32_t* __restrict__ meta) {
   // Three stages: step j's keys are read at step j, its values at step
   // j+1 (the P.V product runs one step behind the scores), and step j+1's
   // loads land meanwhile.
@@ -75,6 +79,19 @@ __global__ __launch_bounds__(kWaves * 64) void sage_attn_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, g = lane >> 4;
   const int q0 = qt * kSageQTile + wave * 16 * kQB;
+  if (KUNI && __builtin_amdgcn_readfirstlane(meta[0]) < kSageKTile) {
+    const int b = bh / H, hh = bh % H;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int q = q0 + 16 * qb + fr;
+      if (q >= Lq) continue;
+      uint16_t* orow = out + (int64_t)b * so.b + (int64_t)hh * so.h + (int64_t)q * so.l + 4 * g;
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        *reinterpret_cast<uint2*>(orow + 16 * db) = make_uint2(0x7E007E00u, 0x7E007E00u);
+    }
+    return;
+  }
 
   // Query codes (B operand of S^T: row q = fr, 16 bytes at chunk g of each
   // 64-channel half) and the per-row exponent factor.
@@ -326,7 +343,7 @@ const char* launch_sage_attend(const char* ws, const SageLayout& L, uint16_t* ou
                      reinterpret_cast<const int8_t*>(ws + L.qc), reinterpret_cast<const float*>(ws + L.sq),
                      reinterpret_cast<const int8_t*>(ws + L.kc), reinterpret_cast<const float*>(ws + L.sk),
                      reinterpret_cast<const uint16_t*>(ws + L.vt), out, so, (int)H, (int)Lq, (int)Lk,
-                     (int)L.Lqp, (int)L.Lkp, c_log2);
+                     (int)L.Lqp, (int)L.Lkp, c_log2, reinterpret_cast<const int32_t*>(ws + L.meta));
   return k_uniform ? "sage_attn_kuni" : "sage_attn";
 }
 

@@ -65,10 +65,13 @@ __global__ __launch_bounds__(256) void sage_k_colsum(const uint16_t* __restrict_
 
 // Per b*h: the key means from the column sums (int64 total -> fp64 ->
 // x 2^-24 -> / L in fp64 -> fp32, each step rounded to nearest even).
+// Workgroup 0 also records the block sizes in the workspace's meta region.
 __global__ __launch_bounds__(kSageD) void sage_k_mean(const int64_t* __restrict__ colsum,
                                                       int nchunk, int Lk,
-                                                      float* __restrict__ kmean) {
+                                                      float* __restrict__ kmean, int k_block,
+                                                      int q_block, int32_t* __restrict__ meta) {
   const int bh = blockIdx.x, d = threadIdx.x;
+  if (bh == 0 && d < 4) meta[d] = d == 0 ? k_block : d == 1 ? q_block : 0;
   const int64_t* cs = colsum + (int64_t)bh * nchunk * kSageD + d;
   int64_t tot = 0;
   for (int c = 0; c < nchunk; ++c) tot += cs[(int64_t)c * kSageD];
@@ -201,7 +204,7 @@ const char* launch_sage_prepare(const uint16_t* q, const uint16_t* k, const uint
                      (int)H, (int)Lk, (int)L.nchunk, colsum);
   float* kmean = reinterpret_cast<float*>(ws + L.kmean);
   hipLaunchKernelGGL(sage_k_mean, dim3((unsigned)L.BH), dim3(kSageD), 0, s, colsum, (int)L.nchunk,
-                     (int)Lk, kmean);
+                     (int)Lk, kmean, k_block, q_block, reinterpret_cast<int32_t*>(ws + L.meta));
   hipLaunchKernelGGL(sage_quant<true>, dim3((unsigned)(L.Lkp / kSageRowTile), (unsigned)L.BH), blk,
                      0, s, k, sk, (int)H, (int)Lk, (int)L.Lkp, k_block, kmean,
                      reinterpret_cast<int8_t*>(ws + L.kc), reinterpret_cast<float*>(ws + L.sk));
