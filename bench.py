@@ -409,7 +409,7 @@ def mfma_floor(sink: SampleSink) -> dict:
     import w8a8_gemm_dit_amd as kq
 
     iters, grid = 4000, 512
-    ops = (1 << 18) * iters * grid
+    ops = (1 << 21) * iters * grid       # 8 waves x 8 MFMAs x 2^15 ops per iteration
     m = measure(lambda i: kq.kq_probe_mfma_i8(iters, grid), 4, 9, 0.2, sink, "probe_mfma_i8",
                 "kernel")
     tops = ops / (m["ms"] * 1e-3) / 1e12

@@ -399,8 +399,9 @@ kq_status kq_probe_read(const void* src, int64_t bytes, int64_t grid,
                         int32_t threads, uint32_t* sink, void* stream);
 
 /* iters x 8 v_mfma_i32_16x16x64_i8 per wavefront on register operands, 8
- * wavefronts per workgroup, `grid` workgroups: 2^18 * iters * grid integer
- * operations (a multiply-add counted as two) with no memory traffic.
+ * wavefronts per workgroup, `grid` workgroups: 2^21 * iters * grid integer
+ * operations (2^15 per instruction, a multiply-add counted as two) with no
+ * memory traffic.
  * sink: device int32 [grid], written as for kq_probe_read. */
 kq_status kq_probe_mfma_i8(int64_t iters, int64_t grid, int32_t* sink,
                            void* stream);

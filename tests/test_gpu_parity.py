@@ -530,3 +530,57 @@ def test_golden_rows_on_gemv(fmt):
     g = oracle.bf16_bits_to_f32(host_bf16_bits(yb)).astype(np.float64)
     r = oracle.bf16_bits_to_f32(r16).astype(np.float64)
     assert (np.abs(g - r) <= oracle.bf16_ulp(r16)).all()
+
+
+# -------------------------------------------- persistent tile loop (int8)
+# More whole 256x192 tiles than CUs with K % 256 == 0 takes the persistent
+# kernel (one workgroup per CU looping over tiles, the next tile's first
+# operands fetched during the current tile's last steps) under KQ_PERSIST=1;
+# KQ_PERSIST=0 gives the one-tile-per-workgroup kernel.  Shapes: whole tiles (persistent:
+# 320, 288 and 270 tiles, K from 512 to 3072), then ragged M and N and N not
+# a multiple of 4 (which keep the one-tile kernel).
+PERSIST_SHAPES = [(2560, 512, 6144), (4096, 3072, 3456), (2304, 1024, 5760), (4100, 1024, 3000),
+                  (4100, 256, 2998)]
+
+
+@pytest.mark.parametrize("M,K,N", PERSIST_SHAPES)
+def test_persistent_gemm_matches_oracle_and_one_tile_kernel(M, K, N, kq_env):
+    print(f"[parity] persistent {M}x{K}x{N}", flush=True)
+    kq_env(KQ_TILE="256x192", KQ_PERSIST="1")
+    xb, w, b = _problem(M, K, N, seed=M + N)
+    q8, sw = oracle.quantize_w8(w)
+    x, wq, swd, bd = dev_bf16(xb), dev(q8), dev(sw), dev(b)
+    acc = kq.kq_w8a8_linear(x, wq, swd, out_dtype=torch.int32)
+    y16 = kq.kq_w8a8_linear(x, wq, swd, bd, out_dtype=torch.bfloat16)
+    y32 = kq.kq_w8a8_linear(x, wq, swd, bd, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    a, _, _ = oracle.quantize_act(xb, with_group_sums=False)
+    assert np.array_equal(host(acc), oracle.w8a8_acc(a, q8))
+    y64 = oracle.w8a8_linear_exact(xb, q8, sw, b)
+    T = oracle.w8a8_magnitude(xb, q8, sw, b)
+    check_bf16(host_bf16_bits(y16), y64, T, f"persistent bf16 {M}x{K}x{N}")
+    check_f32(host(y32), y64, T, f"persistent f32 {M}x{K}x{N}")
+    kq_env(KQ_PERSIST="0")
+    r16 = kq.kq_w8a8_linear(x, wq, swd, bd, out_dtype=torch.bfloat16)
+    r32 = kq.kq_w8a8_linear(x, wq, swd, bd, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y16.view(torch.int16), r16.view(torch.int16))
+    assert torch.equal(y32.view(torch.int32), r32.view(torch.int32))
+
+
+def test_persistent_gemm_gated_in_place(kq_env):
+    M, K, N, L = 4100, 1024, 3000, 100
+    print(f"[parity] persistent gated {M}x{K}x{N} L={L}", flush=True)
+    kq_env(KQ_TILE="256x192")
+    xb, w, b = _problem(M, K, N, seed=5)
+    q8, sw = oracle.quantize_w8(w)
+    r = synth.random_bf16((M, N), seed=6)
+    gate = synth.random_f32((-(-M // L), N), seed=7, scale=0.5)
+    x, wq, swd, bd = dev_bf16(xb), dev(q8), dev(sw), dev(b)
+    y = dev_bf16(r)
+    kq.kq_linear_gated(kq.KQ_W8_PER_CHANNEL, x, wq, swd, None, bd, residual=y, gate=dev(gate),
+                       gate_rows=L, out_dtype=torch.bfloat16, out=y)
+    torch.cuda.synchronize()
+    y64 = oracle.gated_residual_exact(oracle.w8a8_linear_exact(xb, q8, sw, b), r, gate, L)
+    T = oracle.gated_magnitude(oracle.w8a8_magnitude(xb, q8, sw, b), r, gate, L)
+    check_bf16(host_bf16_bits(y), y64, T, "persistent gated in place")

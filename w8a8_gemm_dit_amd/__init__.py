@@ -473,7 +473,7 @@ def kq_probe_read(src: torch.Tensor, grid: int, threads: int = 512,
 
 def kq_probe_mfma_i8(iters: int, grid: int, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
     """iters x 8 int8 MFMAs per wavefront, 8 wavefronts x `grid` workgroups
-    (2^18 * iters * grid integer operations)."""
+    (2^21 * iters * grid integer operations)."""
     if sink is None:
         sink = torch.zeros((grid,), dtype=torch.int32, device="cuda")
     _check(lib().kq_probe_mfma_i8(iters, grid, _ptr(sink), _stream()))

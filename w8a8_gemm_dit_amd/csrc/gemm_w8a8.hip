@@ -39,6 +39,8 @@
 //     column) whose operand panels its L2 shares;
 //   - epilogue: fp32 acc * (sx[m]*sw[n]) + bias[n] with one fma, rounded
 //     once to fp32 or bf16 (round-to-nearest-even).
+#include <climits>
+#include <cstdlib>
 #include <type_traits>
 
 #include "kq_common.hpp"
@@ -457,6 +459,286 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
   }
 }
 
+// Persistent form, for unsplit products whose K steps are a multiple of 4
+// (K % 256 == 0) and that have more tiles than the GPU has CUs: a grid of
+// one workgroup per CU (a multiple of 8), each looping over tiles t =
+// blockIdx.x, blockIdx.x + gridDim.x, ... in the one-tile kernel's
+// XCD-aware order (t keeps running on XCD t % 8).  Per tile, the same K
+// loop as the one-tile kernel, except that the last two refills, which the
+// one-tile kernel spends on dead re-loads of the final pair, fetch the next
+// tile's first two pairs, and the last step reads the next tile's first
+// fragments: the next tile's MFMAs start without a load round trip.  The
+// epilogue stores straight from the accumulators (the LDS ring already
+// holds the next tile's operands); its token scales, channel scales and
+// biases were moved into LDS by DMA during the tile's first steps (double
+// buffered by tile parity), so no epilogue load waits behind the next
+// tile's operand loads.  The arithmetic and the output expression are the
+// one-tile kernel's, so the results are identical bit for bit.
+//
+// Whole tiles only (M % BM == 0, N % BN == 0) and no gated epilogue: the
+// epilogue is straight-line code.  Wait accounting at a tile's first steps
+// (vmcnt retires in issue order): the epilogue issues exactly kStores
+// vector stores after the next tile's pair-1 loads, so "at most kStores
+// outstanding" at step 1 means pair 1 has landed, and steps 0 and 2 need
+// nothing new; the first tile's prologue waits for both pairs.
+template <int BM, int BN, int WM, int WN, int OUT>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_persist(
+    const int8_t* __restrict__ A, const float* __restrict__ sx, const int8_t* __restrict__ W,
+    const float* __restrict__ sw, const float* __restrict__ bias, void* y, int M, int N, int K) {
+  using C = Cfg<BM, BN, WM, WN>;
+  __shared__ int4 lds0[C::kPairSlots], lds1[C::kPairSlots];
+  // Epilogue operands per tile parity: token scales of the BM rows, then
+  // channel scales and biases of the BN columns (64-float DMA units).
+  constexpr int kEU = (BM + 2 * BN) / 64;
+  static_assert((BM + 2 * BN) % 64 == 0 && BM % 64 == 0 && BN % 64 == 0 && kEU <= 2 * C::kWaves,
+                "epilogue operand units: two per wave at most");
+  __shared__ __attribute__((aligned(16))) float eops[2][BM + 2 * BN];
+  constexpr int kStores = C::kTN * C::kTM;  // vector stores of a full tile's epilogue
+  constexpr int kExtra = 2;                 // epilogue-operand DMAs per wave and tile
+  static_assert(C::kLPW + kStores + kExtra < 64, "vmcnt range");
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int ntiles = tiles_m * tiles_n;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % WM;
+  const int wn = wave / WM;
+  const int KT = K / 64;  // a multiple of 4
+  const int NP = KT / 2;  // K-step pairs per tile
+
+  const int rr = (lane & 31) >> 2;
+  const uint32_t vbase = (uint32_t)(rr * K + (lane >> 5) * 64);
+  const uint32_t voff0 = vbase + (uint32_t)(((lane & 3) ^ ((rr >> 1) & 3)) * 16);
+  const uint32_t voff1 = vbase + (uint32_t)(((lane & 3) ^ ((rr >> 1) & 3) ^ 1) * 16);
+
+  // This tile (m0, n0) and the next one (m1, n1); has_next false at the last.
+  int t = blockIdx.x;
+  int m0, n0, m1, n1;
+  {
+    int tm, tn;
+    tile_coords(t, ntiles, tiles_m, tiles_n, tm, tn);
+    m0 = tm * BM;
+    n0 = tn * BN;
+  }
+  bool has_next = t + (int)gridDim.x < ntiles;
+  auto next_coords = [&]() {
+    int tm, tn;
+    tile_coords(has_next ? t + (int)gridDim.x : t, ntiles, tiles_m, tiles_n, tm, tn);
+    m1 = tm * BM;
+    n1 = tn * BN;
+  };
+  next_coords();
+
+  // Fill a pair buffer with pair pi of this tile; pi >= NP: pair pi - NP
+  // of the next tile (or, at the last tile, a dead re-load of this tile's
+  // final pair).  Uniform selects, no branch: the step stays one block.
+  auto issue = [&](int4* buf, int pi) {
+    if (C::kDmaWaves < C::kWaves && wave >= C::kDmaWaves) return;
+    const bool nx = pi >= NP && has_next;
+    const int mb = nx ? m1 : m0, nb = nx ? n1 : n0;
+    const int ks = (pi < NP ? pi : has_next ? pi - NP : NP - 1) * 128;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t*>(A + (int64_t)mb * K), 0, min(BM, M - mb) * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t*>(W + (int64_t)nb * K), 0, min(BN, N - nb) * K, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < C::kLPW; ++i) {
+      const int b = wave * C::kLPW + i;
+      lds_ptr_t dst = (lds_ptr_t)(buf + 64 * b);
+      const uint32_t vo = (b & 1) ? voff1 : voff0;
+      if (b < BM / 8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, vo, ks + 8 * b * K, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, vo, ks + (8 * b - BM) * K, 0, 0);
+    }
+  };
+  // The epilogue operands of the tile at (mb, nb) into eops[buf]: every
+  // wave moves units wave and wave + kWaves (a unit past kEU repeats the
+  // last one, writing the same values again); rows or columns past the
+  // matrix edge, and a missing bias, read as zero.
+  auto issue_eops = [&](int buf, int mb, int nb) {
+    if (OUT == kOutI32) return;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int u = min(wave + h * C::kWaves, kEU - 1);
+      const bool is_sx = u < BM / 64, is_sw = !is_sx && u < (BM + BN) / 64;
+      const float* base = is_sx ? sx + mb : is_sw ? sw + nb : (bias ? bias + nb : sw);
+      const int valid = is_sx ? M - mb : bias || is_sw ? N - nb : 0;
+      const int first = 64 * (is_sx ? u : is_sw ? u - BM / 64 : u - (BM + BN) / 64);
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(base), 0, valid * 4, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)&eops[buf][64 * u], 4, lane * 4,
+                                               first * 4, 0, 0);
+    }
+  };
+
+  v4i acc[C::kTN][C::kTM];
+  const int fr = lane & 15;
+  const int fc = lane >> 4;
+  const int a_slot0 = pair_slot(wm * C::kWTM + fr, fc, 0);
+  const int w_slot0 = pair_slot(BM + wn * C::kWTN + fr, fc, 0);
+  struct Frags {
+    v4i a[C::kTM], w[C::kTN];
+  };
+  auto read_frags = [&](Frags& f, const int4* slot) {
+#pragma unroll
+    for (int j = 0; j < C::kTM; ++j) {
+      const int4 v = slot[a_slot0 + 128 * j];
+      f.a[j] = v4i{v.x, v.y, v.z, v.w};
+    }
+#pragma unroll
+    for (int i = 0; i < C::kTN; ++i) {
+      const int4 v = slot[w_slot0 + 128 * i];
+      f.w[i] = v4i{v.x, v.y, v.z, v.w};
+    }
+  };
+  auto mfmas = [&](const Frags& f) {
+#pragma unroll
+    for (int i = 0; i < C::kTN; ++i)
+#pragma unroll
+      for (int j = 0; j < C::kTM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.w[i], f.a[j], acc[i][j], 0, 0, 0);
+  };
+  int par = 0;  // tile parity: eops[par] holds this tile's epilogue operands
+  // One step (the one-tile kernel's): VM is the vmcnt this wave waits for
+  // before the barrier; EO: also move the next tile's epilogue operands
+  // (after the barrier, so every wave is past the previous epilogue).
+  auto step = [&](Frags& cur, Frags& nxt, int4* cur_buf, const int4* nxt_slot, int kt,
+                  auto odd_tag, auto vm_tag, auto eo_tag) {
+    constexpr bool kOdd = decltype(odd_tag)::value;
+    constexpr int VM = decltype(vm_tag)::value;
+    constexpr bool EO = decltype(eo_tag)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm_lgkm0<VM>();
+    barrier_nofence();
+    read_frags(nxt, nxt_slot);
+    if (kOdd) issue(cur_buf, (kt + 3) >> 1);
+    if (EO) issue_eops(par ^ 1, m1, n1);
+    mfmas(cur);
+    interleave_step<C::kTM * C::kTN, C::kTM + C::kTN, kOdd ? C::kLPW : 0>();
+  };
+  using Even = std::integral_constant<bool, false>;
+  using Odd = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+  using Yes = std::integral_constant<bool, true>;
+  using VmEven = std::integral_constant<int, C::kLPW>;
+  using VmOdd = std::integral_constant<int, 0>;
+  using VmFirst = std::integral_constant<int, C::kLPW + kStores + kExtra>;  // steps 0 and 2
+  using VmSecond = std::integral_constant<int, kStores>;                   // step 1
+#define KQ_PSTEP(j, VMT, EOT)                                                            \
+  step((j) % 2 ? f1 : f0, (j) % 2 ? f0 : f1, (j) < 2 ? lds0 : lds1,                     \
+       (j) == 0 ? lds0 + 32 : (j) == 1 ? lds1 : (j) == 2 ? lds1 + 32 : lds0, kt + (j),    \
+       std::conditional_t<(j) % 2 == 1, Odd, Even>{}, VMT{}, EOT{})
+
+  Frags f0, f1;
+  issue_eops(0, m0, n0);
+  issue(lds0, 0);
+  issue(lds1, 1);
+  wait_vm_lgkm0<0>();  // both pairs: a tile's relaxed first waits then hold for the first tile
+  barrier_nofence();
+  read_frags(f0, lds0);
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < C::kTN; ++i)
+#pragma unroll
+      for (int j = 0; j < C::kTM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+    int kt = 0;
+    KQ_PSTEP(0, VmFirst, No); KQ_PSTEP(1, VmSecond, Yes);
+    KQ_PSTEP(2, VmFirst, No); KQ_PSTEP(3, VmOdd, No);
+    for (kt = 4; kt + 4 <= KT; kt += 4) {
+      KQ_PSTEP(0, VmEven, No); KQ_PSTEP(1, VmOdd, No);
+      KQ_PSTEP(2, VmEven, No); KQ_PSTEP(3, VmOdd, No);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Epilogue: lane holds D[n = nb + 4*(lane/16) + r][m = mb + lane%16];
+    // whole tiles only (checked at launch): exactly kStores vector stores,
+    // straight-line code.
+    const float* ebuf = eops[par];
+    float s_m[C::kTM];
+#pragma unroll
+    for (int j = 0; j < C::kTM; ++j) s_m[j] = ebuf[wm * C::kWTM + j * 16 + fr];
+#pragma unroll
+    for (int i = 0; i < C::kTN; ++i) {
+      const int c = wn * C::kWTN + i * 16 + fc * 4;
+      const int n = n0 + c;
+      const float4 swv = *reinterpret_cast<const float4*>(ebuf + BM + c);
+      const float4 bv = *reinterpret_cast<const float4*>(ebuf + BM + BN + c);
+#pragma unroll
+      for (int j = 0; j < C::kTM; ++j) {
+        const int64_t idx = (int64_t)(m0 + wm * C::kWTM + j * 16 + fr) * N + n;
+        const float sm = s_m[j];
+        if (OUT == kOutI32) {
+          *reinterpret_cast<int4*>(reinterpret_cast<int32_t*>(y) + idx) =
+              make_int4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        } else {
+          const float v0 = fmaf(sm * swv.x, (float)acc[i][j][0], bv.x);
+          const float v1 = fmaf(sm * swv.y, (float)acc[i][j][1], bv.y);
+          const float v2 = fmaf(sm * swv.z, (float)acc[i][j][2], bv.z);
+          const float v3 = fmaf(sm * swv.w, (float)acc[i][j][3], bv.w);
+          if (OUT == kOutF32)
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + idx) = make_float4(v0, v1, v2, v3);
+          else
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + idx) =
+                make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+        }
+      }
+    }
+    if (!has_next) break;
+    t += gridDim.x;
+    m0 = m1;
+    n0 = n1;
+    par ^= 1;
+    has_next = t + (int)gridDim.x < ntiles;
+    next_coords();
+  }
+#undef KQ_PSTEP
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm_lgkm0<0>();  // drain the dead loads before the workgroup exits
+}
+
+// CUs of the current device (cached per device), for the persistent grid.
+int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// KQ_PERSIST=1 takes the persistent form where it applies (off by
+// default: measured slower at the 4K shape, the next tile's refills wait
+// behind the previous tile's output stores).
+bool persist_enabled() {
+  const char* v = getenv("KQ_PERSIST");
+  return v && v[0] == '1';
+}
+
+template <int BM, int BN, int WM, int WN>
+bool launch_persist(const int8_t* a, const float* sx, const int8_t* q, const float* sw,
+                    const float* bias, void* y, int out, int M, int N, int K, hipStream_t s,
+                    const Epilogue& ep) {
+  const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int cus = device_cus() / 8 * 8;
+  if (!persist_enabled() || ep.active() || (K / 64) % 4 != 0 || M % BM != 0 || N % BN != 0 ||
+      cus < 8 || tiles <= cus || tiles > INT32_MAX)
+    return false;
+  const dim3 grid((unsigned)cus), block(64 * WM * WN);
+  if (out == kOutF32)
+    hipLaunchKernelGGL((gemm_w8a8_persist<BM, BN, WM, WN, kOutF32>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
+  else if (out == kOutBF16)
+    hipLaunchKernelGGL((gemm_w8a8_persist<BM, BN, WM, WN, kOutBF16>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
+  else
+    hipLaunchKernelGGL((gemm_w8a8_persist<BM, BN, WM, WN, kOutI32>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K);
+  return true;
+}
+
 template <int BM, int BN, int WM, int WN, bool REM>
 void launch_rem(const int8_t* a, const float* sx, const int8_t* q, const float* sw,
                 const float* bias, void* y, int out, int M, int N, int K, hipStream_t s,
@@ -482,6 +764,10 @@ const char* launch_tile(const int8_t* a, const float* sx, const int8_t* q, const
                         hipStream_t s, const Epilogue& ep, const char* name, int splits,
                         int kchunk) {
   const int klast = K - (splits - 1) * kchunk;  // the last slice's codes
+  if constexpr (WM * WN == 8 && BN == 192) {  // (the 8-wave 256x256 tile would spill)
+    if (splits == 1 && launch_persist<BM, BN, WM, WN>(a, sx, q, sw, bias, y, out, M, N, K, s, ep))
+      return name;
+  }
   if ((kchunk / 64) % 4 == 0 && (klast / 64) % 4 == 0)
     launch_rem<BM, BN, WM, WN, false>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, splits, kchunk);
   else
@@ -571,6 +857,8 @@ const char* launch_gemm_slices(int tile, const int8_t* a, const float* sx, const
   switch (tile) {
     case kTile256x256:
       return launch_tile<256, 256>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_256x256", splits, kchunk);
+    case kTile256x256w8:
+      return launch_tile<256, 256, 4, 2>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_256x256w8", splits, kchunk);
     case kTile256x192:
       return launch_tile<256, 192, 4, 2>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_256x192", splits, kchunk);
     case kTile256x128:

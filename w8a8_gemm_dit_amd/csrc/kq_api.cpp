@@ -121,7 +121,9 @@ kq_status launch_main(const char* op, int force, kq_wformat fmt, const int8_t* c
   } else {
     int tile = 0;
     for (int t = 0; t < kq::kNumTiles; ++t)
-      if (kq::tile_shape(t).bm == r.tile_m && kq::tile_shape(t).bn == r.tile_n) tile = t;
+      if (kq::tile_shape(t).bm == r.tile_m && kq::tile_shape(t).bn == r.tile_n &&
+          kq::tile_shape(t).threads == r.threads)
+        tile = t;
     if (fmt == KQ_W8_PER_CHANNEL)
       k2 = kq::launch_gemm_w8a8(tile, codes, sx, reinterpret_cast<const int8_t*>(wq),
                                 reinterpret_cast<const float*>(scale), bias, y, out, (int)M,

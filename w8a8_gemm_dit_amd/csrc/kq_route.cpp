@@ -24,12 +24,13 @@ TileShape tile_shape(int32_t tile) {
     case kTile128x128: return {128, 128, 256};
     case kTile128x256: return {128, 256, 512};
     case kTile64x128: return {64, 128, 256};
+    case kTile256x256w8: return {256, 256, 512};
     default: return {64, 64, 256};
   }
 }
 
 static const char* const kTileNames[kNumTiles] = {"256x256", "256x192", "256x128", "128x128",
-                                                  "64x64",   "128x256", "64x128"};
+                                                  "64x64",   "128x256", "64x128",  "256x256w8"};
 
 const char* tile_name(int32_t tile) {
   return (tile >= 0 && tile < kNumTiles) ? kTileNames[tile] : "?";
@@ -165,7 +166,7 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
   // times the tile's relative efficiency; a split adds its int32 partials'
   // HBM round trip (written, then read by the fold, at ~4 TB/s) and the
   // fold's launch.
-  static const double kEff[kNumTiles] = {0.95, 1.0, 0.9, 0.75, 0.45, 1.0, 0.7};
+  static const double kEff[kNumTiles] = {0.95, 1.0, 0.9, 0.75, 0.45, 1.0, 0.7, 1.0};
   // int4 tiles run at about 18% of the INT8 peak (their rescale is
   // VALU-bound), the int8 ones at about 45%
   const double cu_rate = (w8 ? 0.45 : 0.18) * 5.0e15 / kSplitCUs;

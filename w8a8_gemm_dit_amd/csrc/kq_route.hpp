@@ -20,7 +20,8 @@ enum GemmTile : int32_t {
   kTile64x64 = 4,    // 64 x 64, 4 waves of 32x32 (thin shapes)
   kTile128x256 = 5,  // int4 GEMM: 128 x 256, 8 waves of 64x64 (2x4)
   kTile64x128 = 6,   // int4 GEMM: 64 x 128, 4 waves of 32x64 (2x2)
-  kNumTiles = 7,
+  kTile256x256w8 = 7,  // 256 x 256, 8 waves of 64x128 (4x2)
+  kNumTiles = 8,
 };
 
 const char* tile_name(int32_t tile);
