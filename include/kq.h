@@ -381,6 +381,29 @@ kq_status kq_sage_attention(const void* q, const void* k, const void* v, void* o
                             kq_layout layout, float scale, int64_t q_block,
                             int64_t k_block, void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of the library's own device scratch on each GPU (64 MiB). */
+#define KQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* kq_w8a8_linear without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments (minus ws, ws_bytes),
+ * routes, kernels and results, bit for bit, as kq_w8a8_linear; the
+ * workspace is a fixed array of KQ_NOALLOC_SCRATCH_BYTES in the library's
+ * device memory, one per GPU, held until the process ends.  The call
+ * allocates nothing.
+ *   Limit: kq_workspace_bytes(M, N, K, KQ_W8_PER_CHANNEL) must not exceed
+ *   KQ_NOALLOC_SCRATCH_BYTES (e.g. M*K <= 64 MiB less the token scales);
+ *   larger shapes return KQ_ERR_UNSUPPORTED and enqueue nothing.
+ *   Concurrency: every call on one GPU shares that GPU's array, and it keeps
+ *   the last call's contents (no kernel reads what it did not write in the
+ *   same call, so nothing needs clearing).  Calls that may overlap on one
+ *   GPU (several streams, several threads) race on it and must be
+ *   serialized by the caller. */
+kq_status kq_w8a8_linear_noalloc(const void* x, int64_t M, int64_t K, int64_t N,
+                                 const int8_t* wq, const float* sw,
+                                 const float* bias, void* y, kq_dtype y_dtype,
+                                 void* stream);
+
 /* ------------------------------------------------------------------------
  * Measurement probes: the machine's own floors beside its published peaks,
  * for roofline figures (mlx-kquant pull request 89 commit list: a DiT-shape

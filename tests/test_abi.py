@@ -24,7 +24,7 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     L = kq.lib()
     declared = _declared_functions()
-    assert len(declared) == 18, declared
+    assert len(declared) == 19, declared
     assert sorted(kq.exported_symbols) == declared
     for name in declared:
         assert hasattr(L, name), name

@@ -24,6 +24,7 @@ __all__ = [
     "kq_gemv_small_m", "kq_w8a8_gemm", "kq_w4a8_gemm", "kq_linear_gated", "KqError",
     "KQ_LAYOUT_BHLD", "KQ_LAYOUT_BLHD", "kq_sage_workspace_layout", "kq_sage_prepare",
     "kq_sage_attend", "kq_sage_attention", "kq_probe_read", "kq_probe_mfma_i8",
+    "kq_w8a8_linear_noalloc", "KQ_NOALLOC_SCRATCH_BYTES",
 ]
 
 KQ_SUCCESS, KQ_ERR_INVALID_VALUE, KQ_ERR_UNSUPPORTED = 0, 1, 2
@@ -36,6 +37,7 @@ KQ_MAX_K = 65536
 KQ_GEMV_MAX_M = 16
 KQ_GEMV_MAX_K = 16384
 KQ_LAYOUT_BHLD, KQ_LAYOUT_BLHD = 0, 1
+KQ_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkq.so")
@@ -46,7 +48,7 @@ exported_symbols = (
     "kq_quantize_weights", "kq_quantize_act", "kq_w8a8_linear",
     "kq_w4a8_linear", "kq_gemv_small_m", "kq_w8a8_gemm", "kq_w4a8_gemm",
     "kq_linear_gated", "kq_sage_workspace_layout", "kq_sage_prepare", "kq_sage_attend",
-    "kq_sage_attention", "kq_probe_read", "kq_probe_mfma_i8",
+    "kq_sage_attention", "kq_probe_read", "kq_probe_mfma_i8", "kq_w8a8_linear_noalloc",
 )
 
 
@@ -118,6 +120,8 @@ def lib() -> ctypes.CDLL:
     L.kq_linear_gated.restype = i32
     L.kq_linear_gated.argtypes = [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, i64, vp, i32,
                                   vp, sz, vp]
+    L.kq_w8a8_linear_noalloc.restype = i32
+    L.kq_w8a8_linear_noalloc.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, i32, vp]
     L.kq_probe_read.restype = i32
     L.kq_probe_read.argtypes = [vp, i64, i64, ctypes.c_int32, vp, vp]
     L.kq_probe_mfma_i8.restype = i32
@@ -454,6 +458,30 @@ def kq_sage_attention(q, k, v, scale=None, q_block=128, k_block=64, layout="bhld
     _check(lib().kq_sage_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(y), B, H, Lq, Lk, D,
                                    _LAYOUTS[layout], scale, q_block, k_block, _ptr(ws), wsb,
                                    _stream()))
+    return y
+
+
+def kq_w8a8_linear_noalloc(x: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor,
+                           bias: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """kq_w8a8_linear on the library's own device scratch (no workspace;
+    the C call allocates nothing).  Shapes whose workspace would exceed
+    KQ_NOALLOC_SCRATCH_BYTES raise ValueError; calls that may overlap on
+    one GPU race on the shared scratch."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(wq, "wq", torch.int8, 2)
+    _need(sw, "sw", torch.float32, 1)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, 1)
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or sw.shape[0] != N or (bias is not None and bias.shape[0] != N):
+        raise ValueError("[kq_w8a8_linear_noalloc] operand shapes disagree")
+    if out_dtype not in _OUT:
+        raise ValueError(f"unsupported out_dtype {out_dtype}")
+    y = _prep_out(out, (M, N), out_dtype, x.device)
+    _check(lib().kq_w8a8_linear_noalloc(_ptr(x), M, K, N, _ptr(wq), _ptr(sw), _ptr(bias), _ptr(y),
+                                        _OUT[out_dtype], _stream()))
     return y
 
 

@@ -572,6 +572,30 @@ kq_status kq_sage_attention(const void* q, const void* k, const void* v, void* o
   return sage_attend_impl(op, ws, ws_bytes, out, B, H, Lq, Lk, D, layout, scale, k_block, stream);
 }
 
+kq_status kq_w8a8_linear_noalloc(const void* x, int64_t M, int64_t K, int64_t N,
+                                 const int8_t* wq, const float* sw, const float* bias, void* y,
+                                 kq_dtype y_dtype, void* stream) {
+  const char* op = "kq_w8a8_linear_noalloc";
+  const int force = env_force_route();
+  kq_status st = check_linear_args(op, force, KQ_W8_PER_CHANNEL, M, K, N, y_dtype, x, wq, sw,
+                                   nullptr, y);
+  if (st != KQ_SUCCESS || M == 0 || N == 0) return st;
+  const size_t need = kq_workspace_bytes(M, N, K, KQ_W8_PER_CHANNEL);
+  if (need > kq::kScratchBytes)
+    return fail(KQ_ERR_UNSUPPORTED,
+                "[%s] M=%lld, N=%lld, K=%lld needs %zu bytes of scratch; the library holds %zu",
+                op, (long long)M, (long long)N, (long long)K, need, kq::kScratchBytes);
+  st = check_device(op);
+  if (st != KQ_SUCCESS) return st;
+  hipError_t e = hipSuccess;
+  void* ws = kq::scratch_address(&e);
+  if (ws == nullptr)
+    return fail(KQ_ERR_NO_DEVICE, "[%s] no device address for the scratch: %s", op,
+                hipGetErrorString(e));
+  return run_linear(op, force, KQ_W8_PER_CHANNEL, x, M, K, N, wq, sw, nullptr, bias, y, y_dtype,
+                    ws, kq::kScratchBytes, stream);
+}
+
 // ------------------------------------------------------------ probes
 kq_status kq_probe_read(const void* src, int64_t bytes, int64_t grid, int32_t threads,
                         uint32_t* sink, void* stream) {

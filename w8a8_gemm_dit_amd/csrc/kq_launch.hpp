@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kq.h"
+
 namespace kq {
 
 // kOutPart (internal): the raw fp32 sums of one K slice of a split int4
@@ -64,6 +66,14 @@ const char* launch_gemv(bool w4, const int8_t* a, const float* sx, const int32_t
 const char* launch_thin_fused(bool w4, const uint16_t* x, float* sx, const void* q, const void* gs,
                               const void* gb, const float* bias, void* y, int out, int M, int N,
                               int K, hipStream_t s, const Epilogue& ep = Epilogue());
+
+// The library's device scratch (noalloc.hip): kScratchBytes per GPU, for
+// the entry point that allocates nothing.  scratch_address returns its
+// device address on the current device (fetched once per device), or NULL
+// with *err set.
+constexpr size_t kScratchBytes = (size_t)KQ_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+void* scratch_address(hipError_t* err);
 
 // Measurement probes (probe.hip): a streaming read of `bytes` (a multiple
 // of 16) in equal contiguous ranges over `grid` workgroups of `threads`,
