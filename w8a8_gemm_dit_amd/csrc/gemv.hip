@@ -7,7 +7,9 @@
 // workgroups.  Same math as the GEMM routes:
 //   int4: y = sx * sum_g (gs*P + gb*A) + bias,  int8: y = sx*sw*acc + bias,
 // with P the exact int32 dot product of one 64-wide group and A the group
-// sum of the activation codes.
+// sum of the activation codes.  int4 weights with M <= 2 and K <= 6144 take
+// the lane-per-column kernel further down instead (fewer instructions per
+// weight byte where the 16-row MFMA tile would be mostly empty).
 //
 // gfx950 design (HBM-bound: every weight byte is read once):
 //   - a workgroup owns 16 output columns and its 8 wavefronts split the K
@@ -27,6 +29,8 @@
 //     read;
 //   - the 8 partial sums are reduced through LDS (fp32 for int4 weights,
 //     exact int32 for int8) and one wavefront applies the epilogue.
+#include <cstdlib>
+
 #include "kq_common.hpp"
 #include "kq_launch.hpp"
 #include "kq_route.hpp"
@@ -338,6 +342,381 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Lane-per-column GEMV for 1 <= M <= kLaneRows rows with int4 weights (K <=
+// kFusedMaxK).  The weight bytes are the whole cost (each read once, 0.5625
+// B per weight), so every byte a workgroup needs is in flight before it
+// computes anything, and the arithmetic per byte is kept small enough to
+// finish while the loads of the other wavefronts are still arriving:
+//   - a workgroup of 8 wavefronts owns 32 output columns: wavefront w takes
+//     columns 8*(w%4) .. +8 and K slice w/4 (one half) of each row's
+//     128-byte lines (four slices, 16 wavefronts, measured slower); lane
+//     (c, p) = (l/8, l%8) takes the 16-byte piece p of each of those lines
+//     of column c, i.e. half p%2 of group 4i + p/2 of line i.  The 8 lanes
+//     of a column read whole lines, every load instruction moves 8 columns x
+//     128 bytes, and the loads go straight to registers (up to 12 lines a
+//     lane), all issued at once behind the activation and scale loads, so
+//     the waits for those never wait for weights;
+//   - the 32 weights of a half group are 4 dwords of nibbles; nibble 2b of a
+//     dword (low half of byte b) is an even k and nibble 2b+1 an odd k, so
+//     the low nibbles (w & 0x0f0f0f0f) and the high ones ((w >> 4) &
+//     0x0f0f0f0f) are 4 int8 values each, without reordering.  The
+//     activation codes sit in LDS split the same way (the even and the odd
+//     codes of each run of 8), and v_dot4_i32_i8 takes 4 products a step: 8
+//     steps (two chains) give the exact int32 dot product P of the half
+//     group for one row (unsigned nibbles are non-negative int8);
+//   - each lane rescales its own half groups: acc += gs*P + gb*A, with A the
+//     half group's code sum and gs, gb as floats, both staged in LDS by the
+//     prologue (gs = gb = 0 past the last group), so no lane exchange
+//     happens per group; the 8 lanes of a column add their sums (xor 1, 2,
+//     4), the second K half's sums go through LDS, and lane 0 of the first
+//     half applies the epilogue.
+// XQ (x given): the workgroup quantizes the rows itself with the quantize
+// kernel's rule and rounding (bit-pattern absmax over the whole row, the
+// 1.5*2^23 shift); the token scales go to sx_out.  Codes given (XQ false):
+// the quantize kernel's codes and scales.
+constexpr int kLSlices = 2;               // K slices of a column set
+constexpr int kLWaves = 4 * kLSlices;
+constexpr int kLCols = 32;       // output columns per workgroup (4 sets of 8)
+constexpr int kLaneRows = 2;     // rows the lane kernel takes
+constexpr int kLMaxLines = (int)(kFusedMaxK / 256);
+static_assert(kFusedMaxK % (256 * kLSlices) == 0, "whole lines in each K slice");
+
+// int8 codes of the 8 bf16 values of w[0..3], as codes8_shift computes them,
+// split by parity: .x = codes 0, 2, 4, 6 and .y = codes 1, 3, 5, 7.
+__device__ __forceinline__ uint2 codes8_shift_eo(const uint32_t w[4], float inv) {
+#pragma clang fp contract(off)  // two roundings, as the rule has them: no fma
+  uint32_t t[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p0 = bf16_to_f32(w[i] & 0xFFFFu) * inv;
+    const float p1 = bf16_to_f32(w[i] >> 16) * inv;
+    t[2 * i] = __float_as_uint(p0 + 12582912.0f);
+    t[2 * i + 1] = __float_as_uint(p1 + 12582912.0f);
+  }
+  // v_perm_b32: bytes 0-3 select from the second operand, 4-7 from the
+  // first, 0x0c gives zero
+  uint32_t d[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t lo = __builtin_amdgcn_perm(t[2 + q], t[q], 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(t[6 + q], t[4 + q], 0x0c0c0400u);
+    d[q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+  }
+  return make_uint2(d[0], d[1]);
+}
+
+// The same split of 8 codes given in value order (c0..c3 in d0, c4..c7 in d1).
+__device__ __forceinline__ uint2 codes8_eo(uint32_t d0, uint32_t d1) {
+  return make_uint2(__builtin_amdgcn_perm(d1, d0, 0x06040200u), __builtin_amdgcn_perm(d1, d0, 0x07050301u));
+}
+
+// NL: lines per wavefront (each takes one K slice of a row's lines), so K
+// <= 256*kLSlices*NL.
+template <int OUT, bool XQ, int MR, int NL>
+__global__ __launch_bounds__(kLWaves * 64) void gemv_lane_kernel(
+    const uint16_t* __restrict__ X, const int8_t* __restrict__ Acodes, const float* __restrict__ sx,
+    const uint8_t* __restrict__ Wq, const uint16_t* __restrict__ GS, const uint16_t* __restrict__ GB,
+    const float* __restrict__ bias, void* y, int M, int N, int K, Epilogue ep,
+    float* __restrict__ sx_out) {
+  static_assert(kLSlices * NL <= kLMaxLines && MR >= 1 && MR <= kLaneRows, "lane GEMV shape");
+  constexpr int kT = kLWaves * 64;
+  constexpr int kMaxK = NL * 256 * kLSlices;                // K that the slices' lines cover
+  constexpr int kHPT = (MR * kMaxK / 32 + kT - 1) / kT;     // half groups per thread
+  constexpr bool kScales = OUT != kOutI32;
+  constexpr int kG4 = kMaxK / 64;                           // groups of kLSlices*NL lines
+  constexpr int kSPT = kScales ? (kLCols * kG4 + kT - 1) / kT : 1;  // scale entries per thread
+  __shared__ __attribute__((aligned(16))) uint32_t s_code[MR * kMaxK / 4];  // [row][K] split codes
+  __shared__ float s_hsum[MR * kMaxK / 32];                                 // [row][half group] code sums
+  __shared__ float2 s_sb[kScales ? kLCols * kG4 : 1];                       // [column][group] (gs, gb)
+  __shared__ float s_amax[XQ ? kLWaves : 1][MR];
+  __shared__ float s_part[kScales ? kLSlices - 1 : 1][4][MR][64];           // later K slices' sums
+
+  const int G = K / 64, H = K / 32;
+  const int nl = (G + 3) / 4;          // lines per weight row
+  const int nlh = (nl + kLSlices - 1) / kLSlices;  // lines of a K slice (<= NL)
+  const int G4 = 4 * nl;               // groups with padding to whole lines
+  const int n0 = blockIdx.x * kLCols;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cw = wave & 3, kh = wave >> 2;
+  const int c8 = lane >> 3, p = lane & 7;
+  const int nw = n0 + 8 * cw;        // first column of this wavefront
+  const int n = nw + c8;             // this lane's column (>= N: computed, not stored)
+  const int l0 = kh * nlh;                  // first line of this wavefront
+  const int nlw = max(0, min(nlh, nl - l0)); // its lines (later slices may have fewer)
+
+  // 1. activations: half groups h = tid + kT*j of rows < M (clamped index;
+  //    the ones past the rows are loaded and not used)
+  const int HM = M * H;
+  v4i xv[XQ ? kHPT : 1][4];
+  uint4 cv[XQ ? 1 : kHPT][2];
+#pragma unroll
+  for (int j = 0; j < kHPT; ++j) {
+    const int h = min(tid + kT * j, HM - 1);
+    const int r = h / H, hg = h - r * H;
+    if constexpr (XQ) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        xv[j][q] = *reinterpret_cast<const v4i*>(X + (int64_t)r * K + hg * 32 + 8 * q);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        cv[j][q] = *reinterpret_cast<const uint4*>(Acodes + (int64_t)r * K + hg * 32 + 16 * q);
+    }
+  }
+  // 2. scales and offsets: entry e = c*G4 + g for the workgroup's column c
+  //    (clamped to the last column) and group g (clamped to the last group;
+  //    entries g >= G are stored as zero)
+  uint16_t sh[kSPT], bh[kSPT];
+  if constexpr (kScales) {
+#pragma unroll
+    for (int j = 0; j < kSPT; ++j) {
+      const int e = min(tid + kT * j, kLCols * G4 - 1);
+      const int c = e / G4, g = e - c * G4;
+      const int64_t src = (int64_t)min(n0 + c, N - 1) * G + min(g, G - 1);
+      sh[j] = GS[src];
+      bh[j] = GB[src];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // 3. weights: line l0 + i of column n at byte n*(K/2) + 128*(l0 + i),
+  //    piece p.  The descriptor covers this wavefront's columns < N: columns
+  //    past N read as zero; lines past the wavefront's share (i >= nlw) get
+  //    an offset past the descriptor, so they read zero without touching
+  //    memory.  (readfirstlane: a descriptor the compiler cannot prove
+  //    uniform is taken apart lane by lane in a loop around every load.)
+  const int nrec = __builtin_amdgcn_readfirstlane(max(0, min(8, N - nw)) * (K / 2));
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(Wq + (int64_t)min(nw, N - 1) * (K / 2)), 0, nrec, 0x00020000);
+  const int voff = c8 * (K / 2) + 128 * l0 + 16 * p;
+  v4i wv[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+    wv[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, i < nlw ? voff + 128 * i : 0x40000000, 0, 0));
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 4. row scales, codes and half-group sums into LDS
+  const int ones = 0x01010101;
+  float sxm[MR];
+  if constexpr (XQ) {
+    float amj[kHPT];
+#pragma unroll
+    for (int j = 0; j < kHPT; ++j) {
+      u16x2 mb = u16x2{0, 0};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) mb = absmax_bits2(mb, (uint32_t)xv[j][q][d]);
+      amj[j] = tid + kT * j < HM ? absmax_bits_value(mb) : 0.0f;
+    }
+#pragma unroll
+    for (int rr = 0; rr < MR; ++rr) {
+      float a = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kHPT; ++j) a = fmaxf(a, min(tid + kT * j, HM - 1) / H == rr ? amj[j] : 0.0f);
+      a = wave_max(a);
+      if (lane == 0) s_amax[wave][rr] = a;
+    }
+    wait_vm_lgkm0<63>();  // the LDS writes (the weight loads stay in flight)
+    barrier_nofence();
+    float inv[MR];
+#pragma unroll
+    for (int rr = 0; rr < MR; ++rr) {
+      float am = s_amax[0][rr];
+#pragma unroll
+      for (int w = 1; w < kLWaves; ++w) am = fmaxf(am, s_amax[w][rr]);
+      inv[rr] = row_inv(am, sxm[rr]);
+      if (blockIdx.x == 0 && tid == rr && rr < M && sx_out != nullptr) sx_out[rr] = sxm[rr];
+    }
+#pragma unroll
+    for (int j = 0; j < kHPT; ++j) {
+      const int h = tid + kT * j;
+      if (h >= HM) continue;
+      const int r = h / H, hg = h - r * H;
+      float iv = inv[0];
+#pragma unroll
+      for (int rr = 1; rr < MR; ++rr) iv = r == rr ? inv[rr] : iv;
+      uint32_t c[8];
+      int s = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w4[4] = {(uint32_t)xv[j][q][0], (uint32_t)xv[j][q][1], (uint32_t)xv[j][q][2],
+                                (uint32_t)xv[j][q][3]};
+        const uint2 eo = codes8_shift_eo(w4, iv);
+        c[2 * q] = eo.x;
+        c[2 * q + 1] = eo.y;
+        s = __builtin_amdgcn_sdot4((int)eo.x, ones, s, false);
+        s = __builtin_amdgcn_sdot4((int)eo.y, ones, s, false);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(s_code + r * (K / 4) + hg * 8);
+      dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
+      dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
+      s_hsum[r * H + hg] = (float)s;
+    }
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < MR; ++rr) sxm[rr] = kScales ? sx[min(rr, M - 1)] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < kHPT; ++j) {
+      const int h = tid + kT * j;
+      if (h >= HM) continue;
+      const int r = h / H, hg = h - r * H;
+      uint32_t c[8];
+      int s = 0;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint2 e0 = codes8_eo(cv[j][q].x, cv[j][q].y);
+        const uint2 e1 = codes8_eo(cv[j][q].z, cv[j][q].w);
+        c[4 * q] = e0.x;
+        c[4 * q + 1] = e0.y;
+        c[4 * q + 2] = e1.x;
+        c[4 * q + 3] = e1.y;
+      }
+#pragma unroll
+      for (int d = 0; d < 8; ++d) s = __builtin_amdgcn_sdot4((int)c[d], ones, s, false);
+      uint4* dst = reinterpret_cast<uint4*>(s_code + r * (K / 4) + hg * 8);
+      dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
+      dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
+      s_hsum[r * H + hg] = (float)s;
+    }
+  }
+  if constexpr (kScales) {
+#pragma unroll
+    for (int j = 0; j < kSPT; ++j) {
+      const int e = tid + kT * j;
+      if (e >= kLCols * G4) continue;
+      const bool ok = e - (e / G4) * G4 < G;
+      s_sb[e] = ok ? make_float2(__half2float(__ushort_as_half(sh[j])), __half2float(__ushort_as_half(bh[j])))
+                   : make_float2(0.0f, 0.0f);
+    }
+  }
+  wait_vm_lgkm0<63>();
+  barrier_nofence();
+
+  // 5. the half groups, line by line as they arrive
+  float facc[MR];
+#pragma unroll
+  for (int rr = 0; rr < MR; ++rr) facc[rr] = 0.0f;
+  const int hh = p & 1;
+  const float2* sbp = s_sb + (8 * cw + c8) * G4 + 4 * l0 + (p >> 1);
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    if (i >= nlw) continue;  // uniform
+    const int g = 4 * (l0 + i) + (p >> 1);  // < G4
+    float2 so = make_float2(0.0f, 0.0f);
+    if constexpr (kScales) so = sbp[4 * i];
+#pragma unroll
+    for (int rr = 0; rr < MR; ++rr) {
+      // codes of half group 2g + hh of row rr (inside s_code for every g <
+      // G4; unused past G: the scale and offset are zero there)
+      const uint4* ap = reinterpret_cast<const uint4*>(s_code + rr * (K / 4) + 16 * g + 8 * hh);
+      const uint4 a0 = ap[0], a1 = ap[1];
+      const uint32_t a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      int acc0 = 0, acc1 = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w = (uint32_t)wv[i][q];
+        acc0 = __builtin_amdgcn_sdot4((int)(w & 0x0F0F0F0Fu), (int)a[2 * q], acc0, false);
+        acc1 = __builtin_amdgcn_sdot4((int)((w >> 4) & 0x0F0F0F0Fu), (int)a[2 * q + 1], acc1, false);
+      }
+      const int acc = acc0 + acc1;
+      if constexpr (OUT == kOutI32) {
+        // debug output: P of every group, [G, M, N]
+        const int pg = acc + __builtin_amdgcn_mov_dpp(acc, 0xB1, 0xF, 0xF, false);  // + lane ^ 1
+        if (hh == 0 && g < G && n < N && rr < M)
+          reinterpret_cast<int32_t*>(y)[((int64_t)g * M + rr) * N + n] = pg;
+      } else {
+        const float hs = s_hsum[rr * H + min(2 * g + hh, H - 1)];
+        facc[rr] = fmaf(so.y, hs, fmaf(so.x, (float)acc, facc[rr]));
+      }
+    }
+  }
+  if constexpr (OUT == kOutI32) return;
+
+  // 6. the column's 8 lanes, the later K slices through LDS, then the
+  //    epilogue in lane p = 0 of the first slice, adding the slices in order
+#pragma unroll
+  for (int rr = 0; rr < MR; ++rr) {
+    float v = facc[rr];
+    v += __shfl_xor(v, 1, kWave);
+    v += __shfl_xor(v, 2, kWave);
+    v += __shfl_xor(v, 4, kWave);
+    facc[rr] = v;
+  }
+  if (kh > 0) {
+#pragma unroll
+    for (int rr = 0; rr < MR; ++rr) s_part[kh - 1][cw][rr][lane] = facc[rr];
+  }
+  __syncthreads();
+  if (kh > 0 || p != 0 || n >= N) return;
+#pragma unroll
+  for (int rr = 0; rr < MR; ++rr)
+#pragma unroll
+    for (int k = 0; k < kLSlices - 1; ++k) facc[rr] += s_part[k][cw][rr][lane];
+  const float bv = bias ? bias[n] : 0.0f;
+#pragma unroll
+  for (int rr = 0; rr < MR; ++rr) {
+    if (rr >= M) continue;
+    const int64_t idx = (int64_t)rr * N + n;
+    float v = fmaf(sxm[rr], facc[rr], bv);
+    if (ep.active()) v = gated1(v, ep.residual, ep.gate, ep.gate_rows, rr, n, N);
+    if (OUT == kOutF32) reinterpret_cast<float*>(y)[idx] = v;
+    else reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)f32_to_bf16_rne(v);
+  }
+}
+
+template <bool XQ, int MR, int NL>
+void launch_lane_out(const uint16_t* x, const int8_t* a, const float* sx, const void* q,
+                     const void* gs, const void* gb, const float* bias, void* y, int out, int M,
+                     int N, int K, hipStream_t s, const Epilogue& ep, float* sx_out) {
+  const dim3 grid((unsigned)((N + kLCols - 1) / kLCols)), block(kLWaves * 64);
+  const uint8_t* qw = reinterpret_cast<const uint8_t*>(q);
+  const uint16_t* hs = reinterpret_cast<const uint16_t*>(gs);
+  const uint16_t* hb = reinterpret_cast<const uint16_t*>(gb);
+  if (out == kOutF32)
+    hipLaunchKernelGGL((gemv_lane_kernel<kOutF32, XQ, MR, NL>), grid, block, 0, s, x, a, sx, qw, hs, hb, bias, y, M, N, K, ep, sx_out);
+  else if (out == kOutBF16)
+    hipLaunchKernelGGL((gemv_lane_kernel<kOutBF16, XQ, MR, NL>), grid, block, 0, s, x, a, sx, qw, hs, hb, bias, y, M, N, K, ep, sx_out);
+  else
+    hipLaunchKernelGGL((gemv_lane_kernel<kOutI32, XQ, MR, NL>), grid, block, 0, s, x, a, sx, qw, hs, hb, bias, y, M, N, K, ep, sx_out);
+}
+
+template <bool XQ, int MR>
+void launch_lane_mr(int nlh, const uint16_t* x, const int8_t* a, const float* sx, const void* q,
+                    const void* gs, const void* gb, const float* bias, void* y, int out, int M,
+                    int N, int K, hipStream_t s, const Epilogue& ep, float* sx_out) {
+  static_assert(kLSlices * 12 == kLMaxLines, "NL = 12 covers K = kFusedMaxK");
+  if (nlh <= 2)
+    launch_lane_out<XQ, MR, 2>(x, a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, sx_out);
+  else if (nlh <= 4)
+    launch_lane_out<XQ, MR, 4>(x, a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, sx_out);
+  else if (nlh <= 6)
+    launch_lane_out<XQ, MR, 6>(x, a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, sx_out);
+  else if (nlh <= 8)
+    launch_lane_out<XQ, MR, 8>(x, a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, sx_out);
+  else if (nlh <= 10)
+    launch_lane_out<XQ, MR, 10>(x, a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, sx_out);
+  else
+    launch_lane_out<XQ, MR, 12>(x, a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, sx_out);
+}
+
+// The lane-per-column GEMV (int4 weights, M <= kLaneRows, K <=
+// kFusedMaxK); x != NULL: it quantizes x itself.
+const char* launch_lane(const uint16_t* x, const int8_t* a, const float* sx, const void* q,
+                        const void* gs, const void* gb, const float* bias, void* y, int out,
+                        int M, int N, int K, hipStream_t s, const Epilogue& ep, float* sx_out) {
+  const int nlh = ((K / 64 + 3) / 4 + kLSlices - 1) / kLSlices;
+  if (x != nullptr) {
+    if (M == 1) launch_lane_mr<true, 1>(nlh, x, a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, sx_out);
+    else launch_lane_mr<true, 2>(nlh, x, a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, sx_out);
+    return "gemv_xq_w4a8_lane";
+  }
+  if (M == 1) launch_lane_mr<false, 1>(nlh, x, a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, sx_out);
+  else launch_lane_mr<false, 2>(nlh, x, a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, sx_out);
+  return "gemv_w4a8_lane";
+}
+
 template <bool W4, bool XQ>
 const char* launch_fmt(const int8_t* a, const float* sx, const void* q, const void* gs,
                        const void* gb, const float* bias, void* y, int out, int M, int N, int K,
@@ -360,6 +739,9 @@ const char* launch_gemv(bool w4, const int8_t* a, const float* sx, const int32_t
                         const void* q, const void* gs, const void* gb, const float* bias,
                         void* y, int out, int M, int N, int K, hipStream_t s,
                         const Epilogue& ep, const uint16_t* x, float* sx_out) {
+  const char* st = getenv("KQ_GEMV_LANE");
+  if (w4 && M <= kLaneRows && K <= kFusedMaxK && !(st && st[0] == '0'))
+    return launch_lane(x, a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, sx_out);
   if (x != nullptr)
     return w4 ? launch_fmt<true, true>(nullptr, nullptr, q, gs, gb, bias, y, out, M, N, K, s, ep, x, sx_out)
               : launch_fmt<false, true>(nullptr, nullptr, q, gs, gb, bias, y, out, M, N, K, s, ep, x, sx_out);
