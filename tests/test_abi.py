@@ -60,7 +60,10 @@ def test_workspace_layout():
 
 
 @pytest.mark.parametrize("M,N,K,fmt,kind,tile,grid", [
-    (1, 13824, 5120, kq.KQ_W4_AFFINE_G64, "fused", (4, 16), 864),   # GEMV quantizing x itself
+    (1, 13824, 5120, kq.KQ_W4_AFFINE_G64, "fused", (2, 32), 432),   # lane GEMV quantizing x itself
+    (2, 13824, 5120, kq.KQ_W4_AFFINE_G64, "fused", (2, 32), 432),
+    (3, 13824, 5120, kq.KQ_W4_AFFINE_G64, "fused", (4, 16), 864),   # MFMA GEMV quantizing x itself
+    (1, 13824, 6208, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 864),   # past the lane kernel's K limit
     (4, 18432, 3072, kq.KQ_W8_PER_CHANNEL, "fused", (4, 16), 1152),
     (4, 512, 6208, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 32),      # past its K limit
     (5, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 864),
@@ -72,8 +75,8 @@ def test_workspace_layout():
     (33, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemm", None, None),
     (4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 192), 256),
     (16384, 12288, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 192), 4096),
-    (2048, 12288, 4096, kq.KQ_W4_AFFINE_G64, "gemm", (128, 256), 768),
-    (2048, 4096, 12288, kq.KQ_W4_AFFINE_G64, "gemm", (128, 256), 256),
+    (2048, 12288, 4096, kq.KQ_W4_AFFINE_G64, "gemm", (128, 128), 1536),
+    (2048, 4096, 12288, kq.KQ_W4_AFFINE_G64, "gemm", (128, 128), 512),
     (100, 640, 256, kq.KQ_W4_AFFINE_G64, "gemm", (64, 128), 10),
     (2048, 48, 5120, kq.KQ_W8_PER_CHANNEL, "fused", (8, 48), 256),   # thin N: one kernel
     (300, 64, 640, kq.KQ_W4_AFFINE_G64, "fused", (8, 64), 38),
@@ -114,10 +117,10 @@ def test_split_k_decisions(M, N, K, tile, splits, kq_env):
 
 
 @pytest.mark.parametrize("M,N,K,tile,splits", [
-    (128, 3072, 12288, (64, 128), 4),       # int4 slices are whole 16-group chunks
+    (128, 3072, 12288, (128, 128), 6),      # int4 slices are whole 16-group chunks
     (64, 4096, 4096, (64, 128), 4),
     (300, 640, 2112, (64, 128), 3),         # a one-group last slice
-    (2048, 4096, 12288, (128, 256), 1),
+    (2048, 4096, 12288, (128, 128), 1),
 ])
 def test_split_k_decisions_int4(M, N, K, tile, splits, kq_env):
     kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_SPLIT=None)
@@ -137,6 +140,18 @@ def test_split_k_lever(kq_env):
     kq_env(KQ_SPLIT="7")
     # 48 steps in slices of ceil(48/7) = 7 -> 8 steps: 6 slices
     assert kq.kq_route(4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL)["splits"] == 6
+
+
+def test_gemv_lane_lever(kq_env):
+    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_FUSE=None, KQ_GEMV_LANE="0")
+    r = kq.kq_route(1, 13824, 5120, kq.KQ_W4_AFFINE_G64)
+    assert (r["kind"], r["tile_m"], r["tile_n"], r["grid"]) == ("fused", 4, 16, 864)
+    kq_env(KQ_GEMV_LANE=None, KQ_FORCE_ROUTE="gemv")
+    r = kq.kq_route(2, 13824, 5120, kq.KQ_W4_AFFINE_G64)
+    assert (r["kind"], r["tile_m"], r["tile_n"], r["grid"]) == ("gemv", 2, 32, 432)
+    # int8 weights never take it
+    r = kq.kq_route(1, 13824, 5120, kq.KQ_W8_PER_CHANNEL)
+    assert (r["kind"], r["tile_m"], r["tile_n"]) == ("gemv", 16, 16)
 
 
 def test_fused_route_lever(kq_env):

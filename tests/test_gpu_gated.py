@@ -98,7 +98,7 @@ def test_gated_w8_every_tile(M, K, N, tile, out, kq_env):
     _check(y, out, y64, T, r, g, 64, f"gated w8 tile {tile} {M}x{K}x{N}")
 
 
-@pytest.mark.parametrize("tile", ["128x256", "64x128"])
+@pytest.mark.parametrize("tile", ["128x256", "128x128", "64x128"])
 @pytest.mark.parametrize("M,K,N", [(300, 448, 200), (257, 128, 129), (256, 1024, 512)])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_gated_w4_every_tile(M, K, N, tile, out, kq_env):

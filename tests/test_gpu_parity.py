@@ -127,7 +127,7 @@ def test_w8a8_outputs(M, K, N, tile, out, kq_env):
 SHAPES_W4 = SHAPES + [(130, 2048, 200), (96, 2112, 272)]
 
 
-@pytest.mark.parametrize("tile", [None, "128x256", "64x128"])
+@pytest.mark.parametrize("tile", [None, "128x256", "128x128", "64x128"])
 @pytest.mark.parametrize("M,K,N", SHAPES_W4)
 def test_w4a8_group_products_bit_exact(M, K, N, tile, kq_env):
     kq_env(KQ_TILE=tile, KQ_FORCE_ROUTE="gemm")
@@ -140,7 +140,7 @@ def test_w4a8_group_products_bit_exact(M, K, N, tile, kq_env):
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-@pytest.mark.parametrize("tile", [None, "128x256", "64x128"])
+@pytest.mark.parametrize("tile", [None, "128x256", "128x128", "64x128"])
 @pytest.mark.parametrize("M,K,N", SHAPES[:6] + SHAPES_W4[-2:])
 def test_w4a8_outputs(M, K, N, tile, out, kq_env):
     kq_env(KQ_TILE=tile, KQ_FORCE_ROUTE="gemm")

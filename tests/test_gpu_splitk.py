@@ -145,7 +145,7 @@ def test_int4_automatic_split(M, K, N, kq_env):
     _check4(xb, q, gs, gb, b, yf, yb, P, f"int4 split {M}x{K}x{N}")
 
 
-@pytest.mark.parametrize("tile", ["128x256", "64x128"])
+@pytest.mark.parametrize("tile", ["128x256", "128x128", "64x128"])
 @pytest.mark.parametrize("split", ["2", "3", "7"])
 @pytest.mark.parametrize("M,K,N", [(257, 3200, 200), (100, 2112, 129)])
 def test_int4_forced_splits_every_tile(M, K, N, tile, split, kq_env):

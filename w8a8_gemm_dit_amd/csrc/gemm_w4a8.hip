@@ -76,7 +76,8 @@ __device__ __forceinline__ void store1(void* y, int64_t idx, float v) {
 // gchunk)) (gchunk a multiple of the 16-group table chunk); with OUT ==
 // kOutPart it writes its raw fp32 sums to slice y of y[splits][M][N].
 template <int BM, int BN, int WTM, int WTN, int OUT, bool GATED>
-__global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel(
+// (128x128: two workgroups per CU, so at most 256 registers per lane)
+__global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, (BM == 128 && BN == 128) ? 2 : 1) void gemm_w4a8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int32_t* __restrict__ gsum,
     const uint8_t* __restrict__ Q, const uint16_t* __restrict__ GS, const uint16_t* __restrict__ GB,
     const float* __restrict__ bias, void* y, int M, int N, int K, Epilogue ep, int gchunk) {
@@ -87,7 +88,9 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64) void gemm_w4a8_kernel
   // sums as [row][32] fp16 = {64*hi of groups 0..15, lo of groups 0..15}
   // (t_gs rows padded to 18 halves: the per-step reads of 16 consecutive
   // columns then hit 16 distinct banks instead of two columns per bank)
-  __shared__ __attribute__((aligned(16))) uint16_t t_gs[kScaled ? 2 : 1][kScaled ? BN : 1][kSG + 2];
+  // (128x128: unpadded, so that two workgroups fit in a CU's 160 KB of LDS)
+  constexpr int kGsPad = (BM == 128 && BN == 128) ? 0 : 2;
+  __shared__ __attribute__((aligned(16))) uint16_t t_gs[kScaled ? 2 : 1][kScaled ? BN : 1][kSG + kGsPad];
   __shared__ __attribute__((aligned(16))) uint16_t t_gb[kScaled ? 2 : 1][kScaled ? BN : 1][kSG];
   __shared__ __attribute__((aligned(16))) uint16_t t_as[kScaled ? 2 : 1][kScaled ? BM : 1][2 * kSG];
 
@@ -509,6 +512,9 @@ const char* launch_gemm_w4a8(int tile, const int8_t* a, const float* sx, const i
       tile == kTile128x256
           ? launch_tile4<128, 256, 64, 64>(a, sx, gsum, q4, hs, hb, bias, dst, dout, M, N, K, s,
                                            dep, "gemm_w4a8_128x256", sp, gchunk)
+      : tile == kTile128x128
+          ? launch_tile4<128, 128, 64, 64>(a, sx, gsum, q4, hs, hb, bias, dst, dout, M, N, K, s,
+                                           dep, "gemm_w4a8_128x128", sp, gchunk)
           : launch_tile4<64, 128, 32, 64>(a, sx, gsum, q4, hs, hb, bias, dst, dout, M, N, K, s,
                                           dep, "gemm_w4a8_64x128", sp, gchunk);
   if (fold) launch_fold4(partials, sp, sx, bias, y, out, M, N, s, ep);

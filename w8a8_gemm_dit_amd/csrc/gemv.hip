@@ -29,8 +29,6 @@
 //     read;
 //   - the 8 partial sums are reduced through LDS (fp32 for int4 weights,
 //     exact int32 for int8) and one wavefront applies the epilogue.
-#include <cstdlib>
-
 #include "kq_common.hpp"
 #include "kq_launch.hpp"
 #include "kq_route.hpp"
@@ -343,7 +341,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Lane-per-column GEMV for 1 <= M <= kLaneRows rows with int4 weights (K <=
+// Lane-per-column GEMV for 1 <= M <= kGemvLaneRows rows with int4 weights (K <=
 // kFusedMaxK).  The weight bytes are the whole cost (each read once, 0.5625
 // B per weight), so every byte a workgroup needs is in flight before it
 // computes anything, and the arithmetic per byte is kept small enough to
@@ -377,8 +375,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
 // the quantize kernel's codes and scales.
 constexpr int kLSlices = 2;               // K slices of a column set
 constexpr int kLWaves = 4 * kLSlices;
-constexpr int kLCols = 32;       // output columns per workgroup (4 sets of 8)
-constexpr int kLaneRows = 2;     // rows the lane kernel takes
+constexpr int kLCols = kGemvLaneCols;  // output columns per workgroup (4 sets of 8)
+static_assert(kLCols == 32 && kLWaves * 64 == kGemvLaneThreads, "lane GEMV geometry");
 constexpr int kLMaxLines = (int)(kFusedMaxK / 256);
 static_assert(kFusedMaxK % (256 * kLSlices) == 0, "whole lines in each K slice");
 
@@ -419,7 +417,7 @@ __global__ __launch_bounds__(kLWaves * 64) void gemv_lane_kernel(
     const uint8_t* __restrict__ Wq, const uint16_t* __restrict__ GS, const uint16_t* __restrict__ GB,
     const float* __restrict__ bias, void* y, int M, int N, int K, Epilogue ep,
     float* __restrict__ sx_out) {
-  static_assert(kLSlices * NL <= kLMaxLines && MR >= 1 && MR <= kLaneRows, "lane GEMV shape");
+  static_assert(kLSlices * NL <= kLMaxLines && MR >= 1 && MR <= kGemvLaneRows, "lane GEMV shape");
   constexpr int kT = kLWaves * 64;
   constexpr int kMaxK = NL * 256 * kLSlices;                // K that the slices' lines cover
   constexpr int kHPT = (MR * kMaxK / 32 + kT - 1) / kT;     // half groups per thread
@@ -701,7 +699,7 @@ void launch_lane_mr(int nlh, const uint16_t* x, const int8_t* a, const float* sx
     launch_lane_out<XQ, MR, 12>(x, a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, sx_out);
 }
 
-// The lane-per-column GEMV (int4 weights, M <= kLaneRows, K <=
+// The lane-per-column GEMV (int4 weights, M <= kGemvLaneRows, K <=
 // kFusedMaxK); x != NULL: it quantizes x itself.
 const char* launch_lane(const uint16_t* x, const int8_t* a, const float* sx, const void* q,
                         const void* gs, const void* gb, const float* bias, void* y, int out,
@@ -738,9 +736,8 @@ const char* launch_fmt(const int8_t* a, const float* sx, const void* q, const vo
 const char* launch_gemv(bool w4, const int8_t* a, const float* sx, const int32_t* /*gsum*/,
                         const void* q, const void* gs, const void* gb, const float* bias,
                         void* y, int out, int M, int N, int K, hipStream_t s,
-                        const Epilogue& ep, const uint16_t* x, float* sx_out) {
-  const char* st = getenv("KQ_GEMV_LANE");
-  if (w4 && M <= kLaneRows && K <= kFusedMaxK && !(st && st[0] == '0'))
+                        const Epilogue& ep, const uint16_t* x, float* sx_out, bool lane) {
+  if (lane && w4 && M <= kGemvLaneRows && K <= kFusedMaxK)
     return launch_lane(x, a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, sx_out);
   if (x != nullptr)
     return w4 ? launch_fmt<true, true>(nullptr, nullptr, q, gs, gb, bias, y, out, M, N, K, s, ep, x, sx_out)

@@ -14,6 +14,8 @@
 //   KQ_TILE=256x256|256x192|256x128|128x128|64x64   pin the GEMM tile (A/B runs)
 //   KQ_SPLIT=n          K slices of a GEMM (1: never split)
 //   KQ_FUSE=0           no fused thin-N route (quantize kernel + GEMV instead)
+//   KQ_GEMV_LANE=0      int4 GEMVs at M <= 2 on the MFMA GEMV kernel instead
+//                       of the lane-per-column one
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -66,6 +68,12 @@ bool env_fuse() {
   return !(v && !strcmp(v, "0"));
 }
 
+// KQ_GEMV_LANE=0 turns the lane-per-column int4 GEMV off.
+bool env_gemv_lane() {
+  const char* v = getenv("KQ_GEMV_LANE");
+  return !(v && !strcmp(v, "0"));
+}
+
 bool env_log() {
   const char* v = getenv("KQ_LOG");
   return v && v[0] && strcmp(v, "0");
@@ -112,12 +120,13 @@ kq_status launch_main(const char* op, int force, kq_wformat fmt, const int8_t* c
                       void* y, kq_dtype y_dtype, hipStream_t s, const char* kq_name,
                       const kq::Epilogue& ep = kq::Epilogue(), int32_t* partials = nullptr) {
   const kq_route_info r =
-      kq::choose_route(M, N, K, fmt, force, env_tile(), partials ? env_split() : 0);
+      kq::choose_route(M, N, K, fmt, force, env_tile(), partials ? env_split() : 0, false,
+                       env_gemv_lane());
   const int out = out_kind(y_dtype);
   const char* k2;
   if (r.kind == KQ_ROUTE_GEMV) {
     k2 = kq::launch_gemv(fmt == KQ_W4_AFFINE_G64, codes, sx, gsum, wq, scale, gbias, bias, y, out,
-                         (int)M, (int)N, (int)K, s, ep);
+                         (int)M, (int)N, (int)K, s, ep, nullptr, nullptr, env_gemv_lane());
   } else {
     int tile = 0;
     for (int t = 0; t < kq::kNumTiles; ++t)
@@ -176,7 +185,8 @@ kq_status run_linear(const char* op, int force, kq_wformat fmt, const void* x, i
   if (st != KQ_SUCCESS || M == 0 || N == 0) return st;
   if (!aligned16(ws))
     return fail(KQ_ERR_INVALID_VALUE, "[%s] x, weights, y and workspace must be 16-byte aligned", op);
-  const kq_route_info r = kq::choose_route(M, N, K, fmt, force, env_tile(), env_split(), env_fuse());
+  const kq_route_info r = kq::choose_route(M, N, K, fmt, force, env_tile(), env_split(), env_fuse(),
+                                           env_gemv_lane());
   const int splits = r.splits;
   const bool fused = r.kind == KQ_ROUTE_FUSED;
   const kq::WorkspaceLayout wl = kq::workspace_layout(M, N, K, fmt, splits, fused);
@@ -194,7 +204,8 @@ kq_status run_linear(const char* op, int force, kq_wformat fmt, const void* x, i
     const char* k =
         M <= kq::kGemvXqRows
             ? kq::launch_gemv(w4, nullptr, nullptr, nullptr, wq, scale, gbias, bias, y,
-                              out_kind(y_dtype), (int)M, (int)N, (int)K, s, ep, xb, sxo)
+                              out_kind(y_dtype), (int)M, (int)N, (int)K, s, ep, xb, sxo,
+                              env_gemv_lane())
             : kq::launch_thin_fused(w4, xb, sxo, wq, scale, gbias, bias, y, out_kind(y_dtype),
                                     (int)M, (int)N, (int)K, s, ep);
     st = check_launch(op);
@@ -358,7 +369,8 @@ size_t kq_workspace_bytes(int64_t M, int64_t N, int64_t K, kq_wformat fmt) {
   // point and lever for this shape (KQ_FUSE=0, kq_gemv_small_m), whose
   // routes never split K where the fused ones apply (K <= 6144).
   const kq_route_info r =
-      kq::choose_route(M, N, K, fmt, env_force_route(), env_tile(), env_split(), env_fuse());
+      kq::choose_route(M, N, K, fmt, env_force_route(), env_tile(), env_split(), env_fuse(),
+                       env_gemv_lane());
   return kq::workspace_layout(M, N, K, fmt, r.splits, false).total;
 }
 
@@ -375,7 +387,8 @@ kq_status kq_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt, kq_dtype y_d
   if (force == 2 && K > kq::kGemvMaxK)
     return fail(KQ_ERR_UNSUPPORTED, "[kq_route] K=%lld exceeds the GEMV limit %lld", (long long)K,
                 (long long)kq::kGemvMaxK);
-  *out = kq::choose_route(M, N, K, fmt, force, env_tile(), env_split(), env_fuse());
+  *out = kq::choose_route(M, N, K, fmt, force, env_tile(), env_split(), env_fuse(),
+                                           env_gemv_lane());
   return KQ_SUCCESS;
 }
 

@@ -95,9 +95,18 @@ int split_chunk(int64_t K, int want, int64_t& chunk, int64_t unit) {
 }
 
 kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
-                           int force, int tile_override, int split_override, bool fuse) {
+                           int force, int tile_override, int split_override, bool fuse,
+                           bool lane) {
   kq_route_info r{};
   r.splits = 1;
+  const bool lane_gemv = lane && fmt == KQ_W4_AFFINE_G64 && M >= 1 && M <= kGemvLaneRows &&
+                         K <= kFusedMaxK;
+  auto lane_geometry = [&]() {
+    r.tile_m = kGemvLaneRows;
+    r.tile_n = kGemvLaneCols;
+    r.threads = kGemvLaneThreads;
+    r.grid = (N + kGemvLaneCols - 1) / kGemvLaneCols;
+  };
   // Up to 4 rows the GEMV quantizes x in its prologue (the separate
   // quantize kernel would cost a launch and a round trip for a few rows).
   if (fuse && (force == 0 || force == 3) && M >= 1 && M <= kGemvXqRows && K <= kFusedMaxK) {
@@ -106,6 +115,7 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
     r.tile_n = kGemvCols;
     r.threads = kGemvThreads;
     r.grid = (N + kGemvCols - 1) / kGemvCols;
+    if (lane_gemv) lane_geometry();
     return r;
   }
   // Thin N with more than one 16-row block: one kernel quantizes its rows
@@ -136,6 +146,7 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
     r.tile_n = kGemvCols;
     r.threads = kGemvThreads;
     r.grid = ((N + kGemvCols - 1) / kGemvCols) * ((M + kGemvRows - 1) / kGemvRows);
+    if (lane_gemv) lane_geometry();
     return r;
   }
   // Tiles each kernel offers.  The int4 GEMM keeps fp32 accumulators that
@@ -143,10 +154,10 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
   // blocks per wavefront.
   static const int32_t kW8Tiles[] = {kTile256x256, kTile256x192, kTile256x128, kTile128x128,
                                      kTile64x64};
-  static const int32_t kW4Tiles[] = {kTile128x256, kTile64x128};
+  static const int32_t kW4Tiles[] = {kTile128x256, kTile128x128, kTile64x128};
   const bool w8 = fmt == KQ_W8_PER_CHANNEL;
   const int32_t* cand = w8 ? kW8Tiles : kW4Tiles;
-  const int ncand = w8 ? 5 : 2;
+  const int ncand = w8 ? 5 : 3;
   int32_t tile = -1;
   if (tile_override >= 0 && tile_override < kNumTiles) {
     // a tile this kernel lacks: the one nearest in area (larger on a tie)
@@ -167,6 +178,9 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
   // HBM round trip (written, then read by the fold, at ~4 TB/s) and the
   // fold's launch.
   static const double kEff[kNumTiles] = {0.95, 1.0, 0.9, 0.75, 0.45, 1.0, 0.7, 1.0};
+  // the int4 GEMM's 128x128 tile runs two workgroups per CU: measured 7%
+  // faster than 128x256 on 2048 x 4096 -> 12288 and equal on 12288 -> 4096
+  constexpr double kEffW4_128x128 = 1.05;
   // int4 tiles run at about 18% of the INT8 peak (their rescale is
   // VALU-bound), the int8 ones at about 45%
   const double cu_rate = (w8 ? 0.45 : 0.18) * 5.0e15 / kSplitCUs;
@@ -175,7 +189,8 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
     const TileShape sh = tile_shape(t);
     const int64_t tiles = ((M + sh.bm - 1) / sh.bm) * ((N + sh.bn - 1) / sh.bn);
     const int64_t waves = (tiles * sp + kSplitCUs - 1) / kSplitCUs;
-    const double tile_s = 2.0 * sh.bm * sh.bn * (double)chunk / (cu_rate * kEff[t]);
+    const double eff = (!w8 && t == kTile128x128) ? kEffW4_128x128 : kEff[t];
+    const double tile_s = 2.0 * sh.bm * sh.bn * (double)chunk / (cu_rate * eff);
     double cost = (double)waves * tile_s;
     if (sp > 1) cost += 8.0 * sp * (double)M * (double)N / 4.0e12 + 3e-6;
     return cost;

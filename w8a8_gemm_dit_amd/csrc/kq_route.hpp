@@ -44,9 +44,11 @@ kq_status validate_linear(const char* op, int64_t M, int64_t K, int64_t N,
 // tile_override: -1 = automatic, else a GemmTile.  split_override: -1 =
 // automatic, 0 or 1 = never split K, n > 1 = n slices (fewer if K is short).
 // fuse: the call quantizes x itself and may take the fused thin-N kernel.
+// lane: int4 weights with M <= kGemvLaneRows and K <= kFusedMaxK take the
+// lane-per-column GEMV kernel (on both GEMV routes).
 kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
                            int force, int tile_override, int split_override = 0,
-                           bool fuse = false);
+                           bool fuse = false, bool lane = true);
 
 // K slicing of a split GEMM: slices of `chunk` codes, a multiple of `unit`
 // (int8 weights: 256, so that only the last slice can end between the
@@ -84,6 +86,11 @@ constexpr int kGemvThinN = 64;  // N up to this takes the GEMV at any M
 constexpr int kGemvAutoRows = 32;  // the automatic route's GEMV takes M up to this
 constexpr int kGemvThreads = 512;
 constexpr int kGemvXqRows = 4;  // the GEMV quantizes x itself up to this many rows
+// Lane-per-column GEMV (int4 weights, M <= kGemvLaneRows, K <= kFusedMaxK):
+// 32 output columns per workgroup of 8 wavefronts, 8 lanes per column.
+constexpr int kGemvLaneRows = 2;
+constexpr int kGemvLaneCols = 32;
+constexpr int kGemvLaneThreads = 512;
 constexpr int64_t kGemvMaxK = KQ_GEMV_MAX_K;
 
 // Fused thin-N route (N <= kGemvThinN, M > 16): 8 rows and all columns
