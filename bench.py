@@ -563,6 +563,100 @@ def summarize_trace(path: str) -> int:
     return 0
 
 
+# ------------------------------------------------------------ counter summaries
+def short_kernel_name(name: str) -> str:
+    """The launch name of a libkq kernel (the route's name for it, as KQ_LOG
+    prints it) from its full template name; the full name if unknown."""
+    import re
+
+    m = re.search(r"gemm_w8a8_kernel<(\d+), (\d+), (\d+), (\d+)", name)
+    if m:
+        bm, bn, wm, wn = (int(v) for v in m.groups())
+        return f"gemm_w8a8_{bm}x{bn}" + ("w8" if bm == bn == 256 and wm * wn == 8 else "")
+    m = re.search(r"gemm_w4a8_kernel<(\d+), (\d+),", name)
+    if m:
+        return f"gemm_w4a8_{m.group(1)}x{m.group(2)}"
+    if "gemv_lane_kernel" in name:
+        return "gemv_w4a8_lane"
+    m = re.search(r"gemv_kernel<(true|false)", name)
+    if m:
+        return "gemv_w4a8" if m.group(1) == "true" else "gemv_w8a8"
+    if "quant_act" in name:
+        return "quant_act"
+    if "thin_fused" in name:
+        return "thin_fused"
+    return name
+
+
+def _counter_values(path: str, counter: str) -> dict:
+    """(kernel, grid threads) -> per-dispatch values (KiB) of one counter
+    from rocprofv3 --pmc CSV output under path."""
+    import csv
+    import glob
+
+    out = {}
+    for fn in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                key = (r["Kernel_Name"], int(r["Grid_Size"]))
+                out.setdefault(key, {})[r["Dispatch_Id"]] = (
+                    out.get(key, {}).get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"]))
+    return {k: list(v.values()) for k, v in out.items()}
+
+
+def summarize_counters(dirs: str, copy_mib: int, workload: str, traffic_out: str) -> int:
+    """Markdown table of FETCH_SIZE / WRITE_SIZE per kernel from four
+    rocprofv3 --pmc passes (dirs = FETCH,WRITE,COPY_FETCH,COPY_WRITE), each
+    counter scaled by what it reads for a plain device copy of copy_mib MiB.
+    With a workload name and traffic_out, the libkq kernels' bytes per
+    launch go into that JSON file under "kernel@workload", with the hash of
+    their sources."""
+    fd, wd, cfd, cwd = dirs.split(",")
+    fetch, write = _counter_values(fd, "FETCH_SIZE"), _counter_values(wd, "WRITE_SIZE")
+    cfetch, cwrite = _counter_values(cfd, "FETCH_SIZE"), _counter_values(cwd, "WRITE_SIZE")
+
+    def copy_avg(vals):
+        xs = [v for (n, _), d in vals.items() if "copy" in n.lower() for v in d]
+        return sum(xs) / len(xs) if xs else float("nan")
+
+    nkib = copy_mib * 1024
+    sf, sw = nkib / copy_avg(cfetch), nkib / copy_avg(cwrite)
+    print(f"Scale: a {copy_mib} MiB device copy ({nkib} KiB read and written) reads "
+          f"{nkib / sf:.0f} KiB of FETCH_SIZE and {nkib / sw:.0f} KiB of WRITE_SIZE, so "
+          f"FETCH_SIZE is multiplied by {sf:.4f} and WRITE_SIZE by {sw:.4f}.\n")
+    print("| kernel | grid threads | dispatches | FETCH_SIZE KiB (avg) | WRITE_SIZE KiB (avg) "
+          "| scaled MB read | scaled MB written |")
+    print("|---|---:|---:|---:|---:|---:|---:|")
+    rec = {}
+    for key in sorted(fetch, key=lambda k: -sum(fetch[k]) / len(fetch[k])):
+        name, grid = key
+        f = sum(fetch[key]) / len(fetch[key])
+        w = sum(write.get(key, [0.0])) / max(1, len(write.get(key, [])))
+        short = short_kernel_name(name)
+        shown = short if short != name else (name if len(name) < 60 else name[:57] + "...")
+        print(f"| `{shown}` | {grid} | {len(fetch[key])} | {f:.0f} | {w:.0f} | "
+              f"{f * sf * 1024 / 1e6:.1f} | {w * sw * 1024 / 1e6:.1f} |")
+        if short != name and kernel_source_hash(short):
+            fb, wb = f * sf * 1024, w * sw * 1024
+            prev = rec.get(short)
+            if prev is None or prev["dispatches"] < len(fetch[key]):
+                rec[short] = {"bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb),
+                              "write_bytes": round(wb), "dispatches": len(fetch[key]),
+                              "grid_threads": grid, "source_hash": kernel_source_hash(short)}
+    if workload and traffic_out:
+        data = json.load(open(traffic_out)) if os.path.exists(traffic_out) else {}
+        data = {k: v for k, v in data.items() if "@" in k}  # entries keyed by workload only
+        for short, r in rec.items():
+            data[f"{short}@{workload}"] = r
+        with open(traffic_out, "w") as fh:
+            json.dump(data, fh, indent=1, sort_keys=True)
+            fh.write("\n")
+        print(f"\n{len(rec)} kernel(s) of {workload} written to {traffic_out}", file=sys.stderr)
+    return 0
+
+
 # ------------------------------------------------------------ hashes
 def output_hashes(workloads=None) -> dict:
     import torch
@@ -611,6 +705,14 @@ def main() -> int:
                          "any difference")
     ap.add_argument("--summarize-trace", default="", metavar="PATH",
                     help="per-kernel averages from a rocprofv3 kernel-trace CSV (no GPU)")
+    ap.add_argument("--summarize-counters", default="", metavar="F,W,CF,CW",
+                    help="FETCH_SIZE/WRITE_SIZE table from four rocprofv3 --pmc output "
+                         "directories (the run, then the copy probe; no GPU)")
+    ap.add_argument("--copy-mib", type=int, default=256,
+                    help="size of the copy probe the counters are scaled by")
+    ap.add_argument("--traffic-out", default="", metavar="JSON",
+                    help="with --summarize-counters and --workload: record the libkq "
+                         "kernels' bytes per launch in this file")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device-to-device copies of MIB MiB, the known-size "
                          "reference that scales HBM byte counters")
@@ -619,6 +721,9 @@ def main() -> int:
         return reaggregate(args.reaggregate)
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace)
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters, args.copy_mib, args.workload,
+                                  args.traffic_out)
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this build runs on one GPU "
               "(the linear would shard by output rows or columns with no collective).",
@@ -821,8 +926,8 @@ def main() -> int:
             })
             if w.M <= 16:
                 # the same bytes as a plain streaming read with the GEMV's grid
-                g = -(-w.N // 16)
-                fl = read_floor(weight_bytes(w), g, 512, sink, f"probe_read_{name}")
+                fl = read_floor(weight_bytes(w), r["grid"], r["threads"], sink,
+                                f"probe_read_{name}")
                 e["read_floor_same_grid"] = fl
                 e["vs_read_floor"] = round(tg * 1e3 / fl["us"], 3)
             if name == "dit_proj_w8a8_4096x3072x3072" and w.out == "bf16":

@@ -13,7 +13,7 @@ import pytest
 
 # (BM, BN) of the int8 tiles and of the int4 tiles
 W8_TILES = [(256, 256), (256, 192), (256, 128), (128, 128), (64, 64)]
-W4_TILES = [(128, 256), (64, 128)]
+W4_TILES = [(128, 256), (128, 128), (64, 128)]
 
 
 def split_chunk(K, want, unit):
@@ -104,3 +104,43 @@ def test_unfixed_descriptor_is_caught():
     last = ((KT - 1) >> 1) * 128
     with pytest.raises(AssertionError):
         _check(N, K, 0, N, k0, N * K, [(N - 1, last + 127)], [])
+
+
+# Lane-per-column GEMV (gemv.hip, int4 weights, M <= 2): wavefront w of a
+# workgroup takes the 8 columns nw = 32*block + 8*(w % 4) .. +8 and K slice
+# w / 4 of each row's 128-byte lines.  Its descriptor starts at row
+# min(nw, N-1) with num_records = max(0, min(8, N - nw)) * K/2; lane (c, p)
+# reads 16 bytes at c*K/2 + 128*(l0 + i) + 16p for i < its line count, and
+# lines past its share get an offset past num_records.
+def _lane_gemv_case(N, K, slices=2):
+    G = K // 64
+    QB = K // 2
+    nl = -(-G // 4)
+    nlh = -(-nl // slices)
+    for blk in range(-(-N // 32)):
+        for w in range(4 * slices):
+            cw, kh = w % 4, w // 4
+            nw = 32 * blk + 8 * cw
+            row0 = min(nw, N - 1)
+            nrec = max(0, min(8, N - nw)) * QB
+            l0 = kh * nlh
+            nlw = max(0, min(nlh, nl - l0))
+            reads, used = [], []
+            for c in range(8):
+                for p in range(8):
+                    for i in range(nlw):
+                        off = c * QB + 128 * (l0 + i) + 16 * p
+                        reads += [(0, off), (0, off + 15)]
+                        g = 4 * (l0 + i) + p // 2
+                        if nw + c < N and g < G:
+                            used.append((c, 128 * (l0 + i) + 16 * p + 15))
+            _check(N, QB, row0, 8, 0, nrec, reads, [])
+            for c, off in used:  # every byte a used group needs lies below num_records
+                assert c * QB + off < nrec, (N, K, blk, w, c, off)
+                assert (row0 + c) * QB + off < N * QB
+
+
+@pytest.mark.parametrize("N,K", [(1, 64), (16, 128), (33, 320), (200, 1088), (100, 6144),
+                                 (13824, 5120), (40, 4160), (8, 2112)])
+def test_lane_gemv_reads_stay_in_the_weights(N, K):
+    _lane_gemv_case(N, K)
