@@ -657,6 +657,65 @@ def summarize_counters(dirs: str, copy_mib: int, workload: str, traffic_out: str
     return 0
 
 
+def summarize_pmc(path: str) -> int:
+    """Per (kernel, grid) averages over dispatches of every counter in a
+    rocprofv3 --pmc CSV output directory, as a markdown table."""
+    import csv
+    import glob
+
+    vals, counters, dur = {}, [], {}
+    for fn in glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True):
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                dur[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    for fn in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                c = r["Counter_Name"]
+                if c not in counters:
+                    counters.append(c)
+                key = (short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size"]))
+                d = vals.setdefault(key, {}).setdefault(c, {})
+                d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not vals:
+        print(f"no counter_collection.csv under {path}", file=sys.stderr)
+        return 1
+    # With the dispatches' durations (--kernel-trace in the same run):
+    # GRBM_GUI_ACTIVE summed over the 8 XCDs / duration = the shader clock,
+    # and the MFMA / VALU busy shares of those cycles over 1024 SIMDs
+    # (SQ_ACTIVE_INST_VALU counts quad-cycles).
+    derived = ["avg us"] if dur else []
+    if dur and "GRBM_GUI_ACTIVE" in counters:
+        derived.append("clock GHz")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in counters:
+            derived.append("MFMA busy %")
+        if "SQ_ACTIVE_INST_VALU" in counters:
+            derived.append("VALU busy %")
+    print("| kernel | grid threads | dispatches | " + " | ".join(counters + derived) + " |")
+    print("|---|---:|---:|" + "---:|" * (len(counters) + len(derived)))
+    for (name, grid), cs in sorted(vals.items(), key=lambda kv: kv[0]):
+        ids = sorted(set().union(*(v.keys() for v in cs.values())))
+        cells = [f"{sum(cs[c].values()) / len(cs[c]):.4g}" if c in cs else "" for c in counters]
+        ds = [dur[i] for i in ids if i in dur]
+        if derived and ds:
+            us = sum(ds) / len(ds)
+            cells.append(f"{us:.2f}")
+            if "clock GHz" in derived:
+                gui = sum(cs["GRBM_GUI_ACTIVE"].values()) / len(cs["GRBM_GUI_ACTIVE"]) / 8
+                cells.append(f"{gui / us / 1e3:.2f}")
+                if "MFMA busy %" in derived:
+                    m = sum(cs["SQ_VALU_MFMA_BUSY_CYCLES"].values()) / len(cs["SQ_VALU_MFMA_BUSY_CYCLES"])
+                    cells.append(f"{100 * m / 1024 / gui:.1f}")
+                if "VALU busy %" in derived:
+                    v = sum(cs["SQ_ACTIVE_INST_VALU"].values()) / len(cs["SQ_ACTIVE_INST_VALU"])
+                    cells.append(f"{100 * 4 * v / 1024 / gui:.1f}")
+        elif derived:
+            cells += [""] * len(derived)
+        shown = name if len(name) < 60 else name[:57] + "..."
+        print(f"| `{shown}` | {grid} | {len(ids)} | " + " | ".join(cells) + " |")
+    return 0
+
+
 # ------------------------------------------------------------ hashes
 def output_hashes(workloads=None) -> dict:
     import torch
@@ -708,6 +767,9 @@ def main() -> int:
     ap.add_argument("--summarize-counters", default="", metavar="F,W,CF,CW",
                     help="FETCH_SIZE/WRITE_SIZE table from four rocprofv3 --pmc output "
                          "directories (the run, then the copy probe; no GPU)")
+    ap.add_argument("--summarize-pmc", default="", metavar="DIR",
+                    help="per-kernel averages of every counter in a rocprofv3 --pmc output "
+                         "directory (no GPU)")
     ap.add_argument("--copy-mib", type=int, default=256,
                     help="size of the copy probe the counters are scaled by")
     ap.add_argument("--traffic-out", default="", metavar="JSON",
@@ -721,6 +783,8 @@ def main() -> int:
         return reaggregate(args.reaggregate)
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace)
+    if args.summarize_pmc:
+        return summarize_pmc(args.summarize_pmc)
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters, args.copy_mib, args.workload,
                                   args.traffic_out)
