@@ -878,7 +878,8 @@ def main() -> int:
         f"gemm {ms_gemm * 1e3:.2f} us, quantize {quant['ms'] * 1e3:.2f} us, eager "
         f"{ms_eager * 1e3:.2f} us")
     route = kq.kq_route(wl.M, wl.N, wl.K, kq.KQ_W8_PER_CHANNEL)
-    gemm_name = f"gemm_w8a8_{route['tile_m']}x{route['tile_n']}"
+    gemm_name = f"gemm_w8a8_{route['tile_m']}x{route['tile_n']}" + (
+        "w8" if route["tile_m"] == route["tile_n"] == 256 and route["threads"] == 512 else "")
     head_copies = p.R
     del p
     torch.cuda.empty_cache()

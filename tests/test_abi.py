@@ -74,7 +74,7 @@ def test_workspace_layout():
     (32, 13824, 5120, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 864 * 2),
     (33, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemm", None, None),
     (4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 192), 256),
-    (16384, 12288, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 192), 4096),
+    (16384, 12288, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 256), 3072),  # 8-wave 256x256
     (2048, 12288, 4096, kq.KQ_W4_AFFINE_G64, "gemm", (128, 128), 1536),
     (2048, 4096, 12288, kq.KQ_W4_AFFINE_G64, "gemm", (128, 128), 512),
     (100, 640, 256, kq.KQ_W4_AFFINE_G64, "gemm", (64, 128), 10),
@@ -106,7 +106,7 @@ def test_route_decisions(M, N, K, fmt, kind, tile, grid, kq_env):
     (200, 1000, 65536, (128, 128), 16),
     (4, 512, 16448, (64, 64), 13),          # past the GEMV's K limit
     (4096, 3072, 3072, (256, 192), 1),      # a full grid never splits
-    (16384, 12288, 3072, (256, 192), 1),
+    (16384, 12288, 3072, (256, 256), 1),
     (512, 3072, 3072, (64, 64), 1),         # short K: the partials would cost more
 ])
 def test_split_k_decisions(M, N, K, tile, splits, kq_env):
@@ -133,7 +133,8 @@ def test_split_k_lever(kq_env):
     assert kq.kq_route(128, 3072, 12288, kq.KQ_W8_PER_CHANNEL)["splits"] == 1
     kq_env(KQ_SPLIT="4")
     r = kq.kq_route(4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL)
-    assert r["splits"] == 4 and r["grid"] == 256 * 4
+    tiles = (4096 // r["tile_m"]) * (3072 // r["tile_n"])
+    assert r["splits"] == 4 and r["grid"] == tiles * 4
     kq_env(KQ_SPLIT="16")
     assert kq.kq_route(64, 256, 320, kq.KQ_W8_PER_CHANNEL)["splits"] == 2  # 5 steps: slices of 4
     assert kq.kq_route(64, 256, 3200, kq.KQ_W4_AFFINE_G64)["splits"] == 4  # 50 groups: 16, 16, 16, 2

@@ -82,7 +82,7 @@ def test_gated_matches_oracle(M, K, N, route, fmt, out, res, L, kq_env):
     _check(y, out, y64, T, r, g, max(L, 1), f"gated {fmt} {out} {M}x{K}x{N} res={res} L={L}")
 
 
-@pytest.mark.parametrize("tile", ["256x256", "256x192", "256x128", "128x128", "64x64"])
+@pytest.mark.parametrize("tile", ["256x256", "256x256w8", "256x192", "256x128", "128x128", "64x64"])
 @pytest.mark.parametrize("M,K,N", [(300, 448, 200), (257, 128, 129), (512, 256, 512)])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_gated_w8_every_tile(M, K, N, tile, out, kq_env):

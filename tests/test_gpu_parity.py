@@ -90,7 +90,7 @@ def _problem(M, K, N, seed, dist="normal", with_bias=True):
 SHAPES = [(64, 512, 512), (1, 64, 16), (17, 64, 33), (100, 192, 200), (257, 128, 129),
           (300, 256, 48), (64, 1024, 1000), (513, 320, 260), (300, 448, 200), (130, 576, 72),
           (70, 640, 70)]
-TILES = [None, "256x256", "256x192", "256x128", "128x128", "64x64"]
+TILES = [None, "256x256", "256x256w8", "256x192", "256x128", "128x128", "64x64"]
 
 
 @pytest.mark.parametrize("tile", TILES)
@@ -106,7 +106,7 @@ def test_w8a8_accumulators_bit_exact(M, K, N, tile, kq_env):
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-@pytest.mark.parametrize("tile", [None, "256x256", "256x192", "64x64"])
+@pytest.mark.parametrize("tile", [None, "256x256", "256x256w8", "256x192", "64x64"])
 @pytest.mark.parametrize("M,K,N", SHAPES[:6])
 def test_w8a8_outputs(M, K, N, tile, out, kq_env):
     kq_env(KQ_TILE=tile, KQ_FORCE_ROUTE="gemm")

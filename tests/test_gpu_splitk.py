@@ -54,7 +54,7 @@ def test_automatic_split_matches_unsplit_bitwise(M, K, N, kq_env):
     check_bf16(host_bf16_bits(outs[None][1]), y64, T, f"split {M}x{K}x{N} bf16")
 
 
-@pytest.mark.parametrize("tile", ["256x256", "256x192", "256x128", "128x128", "64x64"])
+@pytest.mark.parametrize("tile", ["256x256", "256x256w8", "256x192", "256x128", "128x128", "64x64"])
 @pytest.mark.parametrize("split", ["2", "3", "7", "16"])
 @pytest.mark.parametrize("M,K,N", [(257, 1088, 200), (100, 2304, 129)])
 def test_forced_splits_every_tile(M, K, N, tile, split, kq_env):

@@ -858,6 +858,10 @@ const char* launch_gemm_slices(int tile, const int8_t* a, const float* sx, const
     case kTile256x256:
       return launch_tile<256, 256>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_256x256", splits, kchunk);
     case kTile256x256w8:
+      // its gated bf16 instance spills (128 accumulators plus the
+      // residual block in the epilogue): gated calls take 256x192
+      if (ep.active())
+        return launch_tile<256, 192, 4, 2>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_256x192", splits, kchunk);
       return launch_tile<256, 256, 4, 2>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_256x256w8", splits, kchunk);
     case kTile256x192:
       return launch_tile<256, 192, 4, 2>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, "gemm_w8a8_256x192", splits, kchunk);

@@ -153,11 +153,11 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
   // its VALU rescale updates every group, so it uses 64x64 (or 32x64)
   // blocks per wavefront.
   static const int32_t kW8Tiles[] = {kTile256x256, kTile256x192, kTile256x128, kTile128x128,
-                                     kTile64x64};
+                                     kTile64x64, kTile256x256w8};
   static const int32_t kW4Tiles[] = {kTile128x256, kTile128x128, kTile64x128};
   const bool w8 = fmt == KQ_W8_PER_CHANNEL;
   const int32_t* cand = w8 ? kW8Tiles : kW4Tiles;
-  const int ncand = w8 ? 5 : 3;
+  const int ncand = w8 ? 6 : 3;
   int32_t tile = -1;
   if (tile_override >= 0 && tile_override < kNumTiles) {
     // a tile this kernel lacks: the one nearest in area (larger on a tie)
@@ -177,7 +177,10 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
   // times the tile's relative efficiency; a split adds its int32 partials'
   // HBM round trip (written, then read by the fold, at ~4 TB/s) and the
   // fold's launch.
-  static const double kEff[kNumTiles] = {0.95, 1.0, 0.9, 0.75, 0.45, 1.0, 0.7, 1.0};
+  // (256x256w8: measured 5% faster than 256x192 at 16384 x 3072 -> 12288,
+  // 12 rounds of tiles against 16; slower on single-round grids, which the
+  // model leaves to 256x192 since its tiles there cost more)
+  static const double kEff[kNumTiles] = {0.95, 1.0, 0.9, 0.75, 0.45, 1.0, 0.7, 1.04};
   // the int4 GEMM's 128x128 tile runs two workgroups per CU: measured 7%
   // faster than 128x256 on 2048 x 4096 -> 12288 and equal on 12288 -> 4096
   constexpr double kEffW4_128x128 = 1.05;
