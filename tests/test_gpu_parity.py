@@ -25,7 +25,7 @@ K_SWEEP = [1, 7, 8, 31, 33, 63, 64, 65, 127, 128, 511, 512, 520, 3072, 4096, 512
 
 
 @pytest.mark.parametrize("K", K_SWEEP)
-@pytest.mark.parametrize("M", [1, 5])
+@pytest.mark.parametrize("M", [1, 5, 256, 257])
 def test_quantize_act_k_sweep(M, K):
     xb = synth.random_bf16((M, K), seed=1000 + K + M, scale=2.0, dist="student_t4")
     a_ref, sx_ref, g_ref = oracle.quantize_act(xb)

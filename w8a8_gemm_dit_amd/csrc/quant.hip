@@ -28,6 +28,7 @@ namespace kq {
 namespace {
 
 constexpr int kRowsPerBlock = 4;  // one wavefront per row, 4 waves per block
+constexpr int64_t kWideMaxRows = 256;  // up to this many rows: a workgroup per row
 
 // Quantize 8 bf16 values held in a uint4; returns 8 codes as uint2 and their
 // sum (two signed 4-way byte dot products against ones).
@@ -87,6 +88,57 @@ __global__ __launch_bounds__(256) void quant_act_regs(
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
     const int c = lane + 64 * j;
+    int s;
+    const uint2 codes = quant8(v[j], inv, s);
+    if (c < nch) ar[c] = codes;
+    if (gsum != nullptr) {
+      s = group8_sum(s);
+      if ((lane & 7) == 0 && c < nch) gsum[row * G + (c >> 3)] = s;
+    }
+  }
+}
+
+// Few rows (a GEMV's, a short sequence's): one workgroup of 8 wavefronts
+// per row, so a row's loads are spread over 512 lanes and the kernel's
+// latency is one load round trip, not one wavefront walking the row.  K %
+// 8 == 0 and K <= 4096*CH; chunk c = tid + 512*j covers elements 8c..8c+7
+// (the 8 chunks of a 64-group sit in 8 adjacent lanes).  The same
+// per-element operations as quant_act_regs: identical codes and scales.
+constexpr int kWideThreads = 512;
+
+template <int CH>
+__global__ __launch_bounds__(kWideThreads) void quant_act_wide(
+    const uint16_t* __restrict__ x, int64_t M, int K, int8_t* __restrict__ a,
+    float* __restrict__ sx, int32_t* __restrict__ gsum) {
+  __shared__ float s_am[kWideThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const int nch = K >> 3;
+  const v4i* xr = reinterpret_cast<const v4i*>(x + row * (int64_t)K);
+  uint4 v[CH];
+  u16x2 mb = u16x2{0, 0};
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int c = tid + kWideThreads * j;
+    v4i t = v4i{0, 0, 0, 0};
+    if (c < nch) t = __builtin_nontemporal_load(xr + c);
+    v[j] = make_uint4((uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w);
+    mb = absmax8_bits(mb, v[j]);
+  }
+  float amax = wave_max(absmax_bits_value(mb));
+  if (lane == 0) s_am[wave] = amax;
+  __syncthreads();
+  amax = s_am[0];
+#pragma unroll
+  for (int w = 1; w < kWideThreads / 64; ++w) amax = fmaxf(amax, s_am[w]);
+  float scale;
+  const float inv = row_inv(amax, scale);
+  if (tid == 0) sx[row] = scale;
+  uint2* ar = reinterpret_cast<uint2*>(a + row * (int64_t)K);
+  const int G = K >> 6;
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int c = tid + kWideThreads * j;
     int s;
     const uint2 codes = quant8(v[j], inv, s);
     if (c < nch) ar[c] = codes;
@@ -221,6 +273,16 @@ const char* launch_quant_act(const uint16_t* x, int64_t M, int K, int8_t* a, flo
   if (K % 8 != 0) {
     hipLaunchKernelGGL(quant_act_scalar, grid, dim3(256), 0, s, x, M, K, a, sx);
     return "quant_act_scalar";
+  }
+  // Few rows: a workgroup per row (measured: 16 rows of 5120, one
+  // wavefront per row took 4.7 us, latency-bound).
+  const int wide = (K / 8 + kWideThreads - 1) / kWideThreads;  // chunks per lane
+  if (M <= kWideMaxRows && K >= 1024 && wide <= 4) {
+    const dim3 g1((unsigned)M);
+    if (wide <= 1) { hipLaunchKernelGGL(quant_act_wide<1>, g1, dim3(kWideThreads), 0, s, x, M, K, a, sx, gsum); return "quant_act_wide1"; }
+    if (wide <= 2) { hipLaunchKernelGGL(quant_act_wide<2>, g1, dim3(kWideThreads), 0, s, x, M, K, a, sx, gsum); return "quant_act_wide2"; }
+    hipLaunchKernelGGL(quant_act_wide<4>, g1, dim3(kWideThreads), 0, s, x, M, K, a, sx, gsum);
+    return "quant_act_wide4";
   }
   const int need = (K / 8 + 63) / 64;  // chunks per lane
   if (need <= 1) { launch_regs<1>(x, M, K, a, sx, gsum, s, grid); return "quant_act_regs1"; }
