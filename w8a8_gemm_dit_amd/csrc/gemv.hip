@@ -589,26 +589,33 @@ __global__ __launch_bounds__(kLWaves * 64) void gemv_lane_kernel(
                    : make_float2(0.0f, 0.0f);
     }
   }
+  // The half-group sums past the rows' (the main loop reads them for the
+  // padding groups past G, with a zero offset): zero, not stale LDS.
+  for (int e = HM + tid; e < MR * kMaxK / 32; e += kT) s_hsum[e] = 0.0f;
   wait_vm_lgkm0<63>();
   barrier_nofence();
 
-  // 5. the half groups, line by line as they arrive
+  // 5. the half groups, line by line as they arrive (every LDS address is a
+  //    per-lane base plus a constant offset per line)
   float facc[MR];
 #pragma unroll
   for (int rr = 0; rr < MR; ++rr) facc[rr] = 0.0f;
   const int hh = p & 1;
-  const float2* sbp = s_sb + (8 * cw + c8) * G4 + 4 * l0 + (p >> 1);
+  const int g0l = 4 * l0 + (p >> 1);  // the lane's group in its first line
+  const float2* sbp = s_sb + (8 * cw + c8) * G4 + g0l;
+  const uint32_t* cbase = s_code + 16 * g0l + 8 * hh;
+  const float* hbase = s_hsum + 2 * g0l + hh;
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     if (i >= nlw) continue;  // uniform
-    const int g = 4 * (l0 + i) + (p >> 1);  // < G4
+    const int g = g0l + 4 * i;  // < G4
     float2 so = make_float2(0.0f, 0.0f);
     if constexpr (kScales) so = sbp[4 * i];
 #pragma unroll
     for (int rr = 0; rr < MR; ++rr) {
       // codes of half group 2g + hh of row rr (inside s_code for every g <
       // G4; unused past G: the scale and offset are zero there)
-      const uint4* ap = reinterpret_cast<const uint4*>(s_code + rr * (K / 4) + 16 * g + 8 * hh);
+      const uint4* ap = reinterpret_cast<const uint4*>(cbase + rr * (K / 4) + 64 * i);
       const uint4 a0 = ap[0], a1 = ap[1];
       const uint32_t a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
       int acc0 = 0, acc1 = 0;
@@ -625,7 +632,9 @@ __global__ __launch_bounds__(kLWaves * 64) void gemv_lane_kernel(
         if (hh == 0 && g < G && n < N && rr < M)
           reinterpret_cast<int32_t*>(y)[((int64_t)g * M + rr) * N + n] = pg;
       } else {
-        const float hs = s_hsum[rr * H + min(2 * g + hh, H - 1)];
+        // (past the row's H entries: the next row's sums or the zeroed
+        // tail, finite either way, times a zero offset)
+        const float hs = hbase[rr * H + 8 * i];
         facc[rr] = fmaf(so.y, hs, fmaf(so.x, (float)acc, facc[rr]));
       }
     }
