@@ -995,6 +995,13 @@ def main() -> int:
                                 f"probe_read_{name}")
                 e["read_floor_same_grid"] = fl
                 e["vs_read_floor"] = round(tg * 1e3 / fl["us"], 3)
+            if name == "dit_proj_w8a8_4096x3072x3072":
+                # NEXT-1 on the tiled GEMM: any in-GEMM quantization needs the
+                # rows' absmax first, i.e. a pass over x; this is the fastest
+                # such pass (a plain streaming read of the 2*M*K bytes of x)
+                fx = read_floor(2 * w.M * w.K, 2048, 512, sink, f"probe_read_x_{name}")
+                e["x_read_floor"] = fx
+                e["call_minus_kernel_us"] = round((t - tg) * 1e3, 3)
             if name == "dit_proj_w8a8_4096x3072x3072" and w.out == "bf16":
                 # the gated residual epilogue, updating the residual stream in
                 # place (4 samples of 1024 tokens: one gate row each)
