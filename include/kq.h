@@ -140,12 +140,18 @@ typedef struct kq_route_info {
  * hardware is missing (is_available() -> False).  Never fails. */
 int kq_is_available(void);
 
-/* Message of the last failed call on this thread ("" if none).  The string
- * is owned by the library and valid until the next call on this thread. */
+/* Message of the last failed call on this thread ("" if none), in the
+ * "[op] reason" form of the argument checks MLX pull request 3026 reviews
+ * for its quantized SDPA (invalid arguments name the op and the bad value).
+ * The string is owned by the library and valid until the next call on this
+ * thread. */
 const char* kq_last_error(void);
 
 /* Bytes of device workspace a linear call with this shape and weight format
- * needs: int8 activation codes (M*K), fp32 token scales (4*M), for the int4
+ * needs (MLX pull request 4722 stages a quantized matmul through int8
+ * activations, "quantize_x", before the integer product; here that stage's
+ * output lives in this caller-owned workspace): int8 activation codes
+ * (M*K), fp32 token scales (4*M), for the int4
  * format the per-group code sums (4*M*K/64), and when the route splits K
  * (kq_route_info.splits > 1) the int32 partial sums (4*splits*M*N), each
  * region 256-byte aligned.  The fused routes (KQ_ROUTE_FUSED) store no
