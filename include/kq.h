@@ -97,10 +97,10 @@ typedef enum kq_dtype {
 typedef enum kq_route_kind {
     KQ_ROUTE_GEMM = 0, /* LDS-tiled MFMA GEMM */
     KQ_ROUTE_GEMV = 1, /* weight-streaming register-dequant kernels: 16x16 output
-                          blocks over all of K (M <= 16, or thin N); int4
-                          weights with M <= 2 and K <= 6144 take a kernel
-                          with 8 lanes per output column (32 columns per
-                          workgroup, v_dot4 products), unless the
+                          blocks over all of K (M <= 16, or thin N); M <= 2
+                          with K <= 6144 takes kernels with 8 lanes per
+                          output column (32 columns per workgroup, v_dot4
+                          products; int4 and int8 weights), unless the
                           environment variable KQ_GEMV_LANE=0 */
     KQ_ROUTE_FUSED = 2 /* the linears' activation quantization inside the
                           product kernel, one launch and no codes stored

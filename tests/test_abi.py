@@ -150,8 +150,10 @@ def test_gemv_lane_lever(kq_env):
     kq_env(KQ_GEMV_LANE=None, KQ_FORCE_ROUTE="gemv")
     r = kq.kq_route(2, 13824, 5120, kq.KQ_W4_AFFINE_G64)
     assert (r["kind"], r["tile_m"], r["tile_n"], r["grid"]) == ("gemv", 2, 32, 432)
-    # int8 weights never take it
+    # int8 weights take it too (the int8 lane kernel)
     r = kq.kq_route(1, 13824, 5120, kq.KQ_W8_PER_CHANNEL)
+    assert (r["kind"], r["tile_m"], r["tile_n"]) == ("gemv", 2, 32)
+    r = kq.kq_route(3, 13824, 5120, kq.KQ_W8_PER_CHANNEL)
     assert (r["kind"], r["tile_m"], r["tile_n"]) == ("gemv", 16, 16)
 
 

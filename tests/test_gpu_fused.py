@@ -181,14 +181,14 @@ GEMV_XQ = [(1, 64, 16), (2, 320, 200), (3, 1088, 33), (4, 5120, 256), (1, 6144, 
 @pytest.mark.parametrize("M,K,N", GEMV_XQ)
 def test_gemv_xq_matches_oracle(M, K, N, fmt, lane, kq_env):
     """M <= 4: the GEMV quantizes its rows in its prologue (route "fused");
-    int4 weights at M <= 2 on the lane-per-column kernel (2-row, 32-column
-    tile) unless KQ_GEMV_LANE=0, else the MFMA GEMV (4-row, 16-column
-    tile); codes (through the int32 outputs) and scales bit-exact."""
-    if lane == "0" and not (fmt == "w4" and M <= 2):
-        pytest.skip("the lever changes only int4 GEMVs at M <= 2")
+    M <= 2 on the lane-per-column kernels (2-row, 32-column tile) unless
+    KQ_GEMV_LANE=0, else the MFMA GEMV (4-row, 16-column tile); codes
+    (through the int32 outputs) and scales bit-exact."""
+    if lane == "0" and not M <= 2:
+        pytest.skip("the lever changes only GEMVs at M <= 2")
     kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_FUSE=None, KQ_GEMV_LANE=lane)
     r = kq.kq_route(M, N, K, _fmt_code(fmt))
-    if fmt == "w4" and M <= 2 and lane is None:
+    if M <= 2 and lane is None:
         assert (r["kind"], r["tile_m"], r["grid"]) == ("fused", 2, -(-N // 32))
     else:
         assert (r["kind"], r["tile_m"], r["grid"]) == ("fused", 4, -(-N // 16))

@@ -106,16 +106,16 @@ def test_unfixed_descriptor_is_caught():
         _check(N, K, 0, N, k0, N * K, [(N - 1, last + 127)], [])
 
 
-# Lane-per-column GEMV (gemv.hip, int4 weights, M <= 2): wavefront w of a
+# Lane-per-column GEMVs (gemv.hip, M <= 2, int4 or int8 weights): wavefront w of a
 # workgroup takes the 8 columns nw = 32*block + 8*(w % 4) .. +8 and K slice
 # w / 4 of each row's 128-byte lines.  Its descriptor starts at row
-# min(nw, N-1) with num_records = max(0, min(8, N - nw)) * K/2; lane (c, p)
-# reads 16 bytes at c*K/2 + 128*(l0 + i) + 16p for i < its line count, and
+# min(nw, N-1) with num_records = max(0, min(8, N - nw)) * row bytes (K/2 or
+# K); lane (c, p) reads 16 bytes at c*rowbytes + 128*(l0 + i) + 16p for i < its line count, and
 # lines past its share get an offset past num_records.
-def _lane_gemv_case(N, K, slices=2):
+def _lane_gemv_case(N, K, slices=2, w8=False):
     G = K // 64
-    QB = K // 2
-    nl = -(-G // 4)
+    QB = K if w8 else K // 2   # bytes per weight row
+    nl = -(-QB // 128)
     nlh = -(-nl // slices)
     for blk in range(-(-N // 32)):
         for w in range(4 * slices):
@@ -131,9 +131,9 @@ def _lane_gemv_case(N, K, slices=2):
                     for i in range(nlw):
                         off = c * QB + 128 * (l0 + i) + 16 * p
                         reads += [(0, off), (0, off + 15)]
-                        g = 4 * (l0 + i) + p // 2
-                        if nw + c < N and g < G:
-                            used.append((c, 128 * (l0 + i) + 16 * p + 15))
+                        byte = 128 * (l0 + i) + 16 * p  # first byte of the piece in the row
+                        if nw + c < N and byte < QB:
+                            used.append((c, byte + 15))
             _check(N, QB, row0, 8, 0, nrec, reads, [])
             for c, off in used:  # every byte a used group needs lies below num_records
                 assert c * QB + off < nrec, (N, K, blk, w, c, off)
@@ -142,5 +142,6 @@ def _lane_gemv_case(N, K, slices=2):
 
 @pytest.mark.parametrize("N,K", [(1, 64), (16, 128), (33, 320), (200, 1088), (100, 6144),
                                  (13824, 5120), (40, 4160), (8, 2112)])
-def test_lane_gemv_reads_stay_in_the_weights(N, K):
-    _lane_gemv_case(N, K)
+@pytest.mark.parametrize("w8", [False, True])
+def test_lane_gemv_reads_stay_in_the_weights(N, K, w8):
+    _lane_gemv_case(N, K, w8=w8)

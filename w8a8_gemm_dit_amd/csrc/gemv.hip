@@ -7,8 +7,8 @@
 // workgroups.  Same math as the GEMM routes:
 //   int4: y = sx * sum_g (gs*P + gb*A) + bias,  int8: y = sx*sw*acc + bias,
 // with P the exact int32 dot product of one 64-wide group and A the group
-// sum of the activation codes.  int4 weights with M <= 2 and K <= 6144 take
-// the lane-per-column kernel further down instead (fewer instructions per
+// sum of the activation codes.  M <= 2 with K <= 6144 takes the
+// lane-per-column kernels further down instead (fewer instructions per
 // weight byte where the 16-row MFMA tile would be mostly empty).
 //
 // gfx950 design (HBM-bound: every weight byte is read once):
@@ -724,6 +724,253 @@ const char* launch_lane(const uint16_t* x, const int8_t* a, const float* sx, con
   return "gemv_w4a8_lane";
 }
 
+// ---------------------------------------------------------------------------
+// The lane-per-column GEMV for int8 weights (M <= kGemvLaneRows, K <=
+// kFusedMaxK): the same workgroup and lane geometry as the int4 kernel
+// above, with 128 weights per 128-byte line.  Per line and row a lane takes
+// 16 weights and the 16 matching activation codes (natural order in LDS)
+// in four v_dot4_i32_i8 steps; the int32 sum runs over the whole row (the
+// scale is per output channel), the 8 lanes of a column and the two K
+// slices add exactly, and the epilogue is the MFMA GEMV's expression,
+// fma(sx*sw, acc, bias), so the outputs equal the other routes' bit for
+// bit.  Codes past K (a half line at the end) are zero in LDS.
+template <int OUT, bool XQ, int MR, int NL>
+__global__ __launch_bounds__(kLWaves * 64) void gemv_lane8_kernel(
+    const uint16_t* __restrict__ X, const int8_t* __restrict__ Acodes, const float* __restrict__ sx,
+    const int8_t* __restrict__ Wq, const float* __restrict__ SW, const float* __restrict__ bias,
+    void* y, int M, int N, int K, Epilogue ep, float* __restrict__ sx_out) {
+  static_assert(kLSlices * NL <= 2 * kLMaxLines && MR >= 1 && MR <= kGemvLaneRows, "lane GEMV shape");
+  constexpr int kT = kLWaves * 64;
+  constexpr int kMaxK = NL * 128 * kLSlices;                // K that the slices' lines cover
+  constexpr int kHPT = (MR * kMaxK / 32 + kT - 1) / kT;     // 32-value units per thread
+  __shared__ __attribute__((aligned(16))) uint32_t s_code[MR * kMaxK / 4];  // [row][kMaxK] codes
+  __shared__ float s_amax[XQ ? kLWaves : 1][MR];
+  __shared__ int s_part[kLSlices - 1][4][MR][64];          // later K slices' sums
+
+  const int H = K / 32;
+  const int nl = (K + 127) / 128;                  // lines per weight row
+  const int nlh = (nl + kLSlices - 1) / kLSlices;  // lines of a K slice (<= NL)
+  const int n0 = blockIdx.x * kLCols;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cw = wave & 3, kh = wave >> 2;
+  const int c8 = lane >> 3, p = lane & 7;
+  const int nw = n0 + 8 * cw;
+  const int n = nw + c8;
+  const int l0 = kh * nlh;
+  const int nlw = max(0, min(nlh, nl - l0));
+
+  // 1. activations: 32-value units h = tid + kT*j of rows < M
+  const int HM = M * H;
+  v4i xv[XQ ? kHPT : 1][4];
+  uint4 cv[XQ ? 1 : kHPT][2];
+#pragma unroll
+  for (int j = 0; j < kHPT; ++j) {
+    const int h = min(tid + kT * j, HM - 1);
+    const int r = h / H, hg = h - r * H;
+    if constexpr (XQ) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        xv[j][q] = *reinterpret_cast<const v4i*>(X + (int64_t)r * K + hg * 32 + 8 * q);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        cv[j][q] = *reinterpret_cast<const uint4*>(Acodes + (int64_t)r * K + hg * 32 + 16 * q);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // 2. weights: line l0 + i of column n at byte n*K + 128*(l0 + i), piece p
+  //    (descriptor as in the int4 kernel: columns past N and lines past the
+  //    wavefront's share read zero)
+  const int nrec = __builtin_amdgcn_readfirstlane(max(0, min(8, N - nw)) * K);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(Wq + (int64_t)min(nw, N - 1) * K), 0, nrec, 0x00020000);
+  const int voff = c8 * K + 128 * l0 + 16 * p;
+  v4i wv[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+    wv[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, i < nlw ? voff + 128 * i : 0x40000000, 0, 0));
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. row scales and codes into LDS (rows at a kMaxK-byte stride)
+  float sxm[MR];
+  if constexpr (XQ) {
+    float amj[kHPT];
+#pragma unroll
+    for (int j = 0; j < kHPT; ++j) {
+      u16x2 mb = u16x2{0, 0};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) mb = absmax_bits2(mb, (uint32_t)xv[j][q][d]);
+      amj[j] = tid + kT * j < HM ? absmax_bits_value(mb) : 0.0f;
+    }
+#pragma unroll
+    for (int rr = 0; rr < MR; ++rr) {
+      float a = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kHPT; ++j) a = fmaxf(a, min(tid + kT * j, HM - 1) / H == rr ? amj[j] : 0.0f);
+      a = wave_max(a);
+      if (lane == 0) s_amax[wave][rr] = a;
+    }
+    wait_vm_lgkm0<63>();  // the LDS writes (the weight loads stay in flight)
+    barrier_nofence();
+    float inv[MR];
+#pragma unroll
+    for (int rr = 0; rr < MR; ++rr) {
+      float am = s_amax[0][rr];
+#pragma unroll
+      for (int w = 1; w < kLWaves; ++w) am = fmaxf(am, s_amax[w][rr]);
+      inv[rr] = row_inv(am, sxm[rr]);
+      if (blockIdx.x == 0 && tid == rr && rr < M && sx_out != nullptr) sx_out[rr] = sxm[rr];
+    }
+#pragma unroll
+    for (int j = 0; j < kHPT; ++j) {
+      const int h = tid + kT * j;
+      if (h >= HM) continue;
+      const int r = h / H, hg = h - r * H;
+      float iv = inv[0];
+#pragma unroll
+      for (int rr = 1; rr < MR; ++rr) iv = r == rr ? inv[rr] : iv;
+      uint32_t c[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w4[4] = {(uint32_t)xv[j][q][0], (uint32_t)xv[j][q][1], (uint32_t)xv[j][q][2],
+                                (uint32_t)xv[j][q][3]};
+        const uint2 cc = codes8_shift(w4, iv);
+        c[2 * q] = cc.x;
+        c[2 * q + 1] = cc.y;
+      }
+      uint4* dst = reinterpret_cast<uint4*>(s_code + r * (kMaxK / 4) + hg * 8);
+      dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
+      dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
+    }
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < MR; ++rr) sxm[rr] = OUT != kOutI32 ? sx[min(rr, M - 1)] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < kHPT; ++j) {
+      const int h = tid + kT * j;
+      if (h >= HM) continue;
+      const int r = h / H, hg = h - r * H;
+      uint4* dst = reinterpret_cast<uint4*>(s_code + r * (kMaxK / 4) + hg * 8);
+      dst[0] = cv[j][0];
+      dst[1] = cv[j][1];
+    }
+  }
+  // the codes past K in each row (a half line at the end): zero
+  for (int e = tid; e < MR * (kMaxK - K) / 4; e += kT) {
+    const int r = e / ((kMaxK - K) / 4), d = e - r * ((kMaxK - K) / 4);
+    s_code[r * (kMaxK / 4) + K / 4 + d] = 0u;
+  }
+  wait_vm_lgkm0<63>();
+  barrier_nofence();
+
+  // 4. the lines as they arrive: 4 dot steps per line and row
+  int acc[MR];
+#pragma unroll
+  for (int rr = 0; rr < MR; ++rr) acc[rr] = 0;
+  const uint32_t* cbase = s_code + 32 * l0 + 4 * p;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    if (i >= nlw) continue;  // uniform
+#pragma unroll
+    for (int rr = 0; rr < MR; ++rr) {
+      const uint4 a = *reinterpret_cast<const uint4*>(cbase + rr * (kMaxK / 4) + 32 * i);
+      acc[rr] = __builtin_amdgcn_sdot4(wv[i][0], (int)a.x, acc[rr], false);
+      acc[rr] = __builtin_amdgcn_sdot4(wv[i][1], (int)a.y, acc[rr], false);
+      acc[rr] = __builtin_amdgcn_sdot4(wv[i][2], (int)a.z, acc[rr], false);
+      acc[rr] = __builtin_amdgcn_sdot4(wv[i][3], (int)a.w, acc[rr], false);
+    }
+  }
+
+  // 5. exact int32 sums over the column's 8 lanes and the K slices, then
+  //    the epilogue in lane p = 0 of the first slice
+#pragma unroll
+  for (int rr = 0; rr < MR; ++rr) {
+    int v = acc[rr];
+    v += __shfl_xor(v, 1, kWave);
+    v += __shfl_xor(v, 2, kWave);
+    v += __shfl_xor(v, 4, kWave);
+    acc[rr] = v;
+  }
+  if (kh > 0) {
+#pragma unroll
+    for (int rr = 0; rr < MR; ++rr) s_part[kh - 1][cw][rr][lane] = acc[rr];
+  }
+  __syncthreads();
+  if (kh > 0 || p != 0 || n >= N) return;
+#pragma unroll
+  for (int rr = 0; rr < MR; ++rr)
+#pragma unroll
+    for (int k = 0; k < kLSlices - 1; ++k) acc[rr] += s_part[k][cw][rr][lane];
+  const float swn = OUT != kOutI32 ? SW[n] : 0.0f;
+  const float bv = (OUT != kOutI32 && bias) ? bias[n] : 0.0f;
+#pragma unroll
+  for (int rr = 0; rr < MR; ++rr) {
+    if (rr >= M) continue;
+    const int64_t idx = (int64_t)rr * N + n;
+    if (OUT == kOutI32) {
+      reinterpret_cast<int32_t*>(y)[idx] = acc[rr];
+    } else {
+      float v = fmaf(sxm[rr] * swn, (float)acc[rr], bv);
+      if (ep.active()) v = gated1(v, ep.residual, ep.gate, ep.gate_rows, rr, n, N);
+      if (OUT == kOutF32) reinterpret_cast<float*>(y)[idx] = v;
+      else reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)f32_to_bf16_rne(v);
+    }
+  }
+}
+
+template <bool XQ, int MR, int NL>
+void launch_lane8_out(const uint16_t* x, const int8_t* a, const float* sx, const void* q,
+                      const void* sw, const float* bias, void* y, int out, int M, int N, int K,
+                      hipStream_t s, const Epilogue& ep, float* sx_out) {
+  const dim3 grid((unsigned)((N + kLCols - 1) / kLCols)), block(kLWaves * 64);
+  const int8_t* qw = reinterpret_cast<const int8_t*>(q);
+  const float* swf = reinterpret_cast<const float*>(sw);
+  if (out == kOutF32)
+    hipLaunchKernelGGL((gemv_lane8_kernel<kOutF32, XQ, MR, NL>), grid, block, 0, s, x, a, sx, qw, swf, bias, y, M, N, K, ep, sx_out);
+  else if (out == kOutBF16)
+    hipLaunchKernelGGL((gemv_lane8_kernel<kOutBF16, XQ, MR, NL>), grid, block, 0, s, x, a, sx, qw, swf, bias, y, M, N, K, ep, sx_out);
+  else
+    hipLaunchKernelGGL((gemv_lane8_kernel<kOutI32, XQ, MR, NL>), grid, block, 0, s, x, a, sx, qw, swf, bias, y, M, N, K, ep, sx_out);
+}
+
+template <bool XQ, int MR>
+void launch_lane8_mr(int nlh, const uint16_t* x, const int8_t* a, const float* sx, const void* q,
+                     const void* sw, const float* bias, void* y, int out, int M, int N, int K,
+                     hipStream_t s, const Epilogue& ep, float* sx_out) {
+  static_assert(kLSlices * 24 == 2 * kLMaxLines, "NL = 24 covers K = kFusedMaxK");
+  if (nlh <= 4)
+    launch_lane8_out<XQ, MR, 4>(x, a, sx, q, sw, bias, y, out, M, N, K, s, ep, sx_out);
+  else if (nlh <= 8)
+    launch_lane8_out<XQ, MR, 8>(x, a, sx, q, sw, bias, y, out, M, N, K, s, ep, sx_out);
+  else if (nlh <= 12)
+    launch_lane8_out<XQ, MR, 12>(x, a, sx, q, sw, bias, y, out, M, N, K, s, ep, sx_out);
+  else if (nlh <= 16)
+    launch_lane8_out<XQ, MR, 16>(x, a, sx, q, sw, bias, y, out, M, N, K, s, ep, sx_out);
+  else if (nlh <= 20)
+    launch_lane8_out<XQ, MR, 20>(x, a, sx, q, sw, bias, y, out, M, N, K, s, ep, sx_out);
+  else
+    launch_lane8_out<XQ, MR, 24>(x, a, sx, q, sw, bias, y, out, M, N, K, s, ep, sx_out);
+}
+
+// The lane-per-column GEMV for int8 weights (M <= kGemvLaneRows, K <=
+// kFusedMaxK); x != NULL: it quantizes x itself.
+const char* launch_lane8(const uint16_t* x, const int8_t* a, const float* sx, const void* q,
+                         const void* sw, const float* bias, void* y, int out, int M, int N, int K,
+                         hipStream_t s, const Epilogue& ep, float* sx_out) {
+  const int nlh = ((K + 127) / 128 + kLSlices - 1) / kLSlices;
+  if (x != nullptr) {
+    if (M == 1) launch_lane8_mr<true, 1>(nlh, x, a, sx, q, sw, bias, y, out, M, N, K, s, ep, sx_out);
+    else launch_lane8_mr<true, 2>(nlh, x, a, sx, q, sw, bias, y, out, M, N, K, s, ep, sx_out);
+    return "gemv_xq_w8a8_lane";
+  }
+  if (M == 1) launch_lane8_mr<false, 1>(nlh, x, a, sx, q, sw, bias, y, out, M, N, K, s, ep, sx_out);
+  else launch_lane8_mr<false, 2>(nlh, x, a, sx, q, sw, bias, y, out, M, N, K, s, ep, sx_out);
+  return "gemv_w8a8_lane";
+}
+
 template <bool W4, bool XQ>
 const char* launch_fmt(const int8_t* a, const float* sx, const void* q, const void* gs,
                        const void* gb, const float* bias, void* y, int out, int M, int N, int K,
@@ -746,8 +993,9 @@ const char* launch_gemv(bool w4, const int8_t* a, const float* sx, const int32_t
                         const void* q, const void* gs, const void* gb, const float* bias,
                         void* y, int out, int M, int N, int K, hipStream_t s,
                         const Epilogue& ep, const uint16_t* x, float* sx_out, bool lane) {
-  if (lane && w4 && M <= kGemvLaneRows && K <= kFusedMaxK)
-    return launch_lane(x, a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, sx_out);
+  if (lane && M <= kGemvLaneRows && K <= kFusedMaxK)
+    return w4 ? launch_lane(x, a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, sx_out)
+              : launch_lane8(x, a, sx, q, gs, bias, y, out, M, N, K, s, ep, sx_out);
   if (x != nullptr)
     return w4 ? launch_fmt<true, true>(nullptr, nullptr, q, gs, gb, bias, y, out, M, N, K, s, ep, x, sx_out)
               : launch_fmt<false, true>(nullptr, nullptr, q, gs, gb, bias, y, out, M, N, K, s, ep, x, sx_out);

@@ -14,8 +14,8 @@
 //   KQ_TILE=256x256|256x192|256x128|128x128|64x64   pin the GEMM tile (A/B runs)
 //   KQ_SPLIT=n          K slices of a GEMM (1: never split)
 //   KQ_FUSE=0           no fused thin-N route (quantize kernel + GEMV instead)
-//   KQ_GEMV_LANE=0      int4 GEMVs at M <= 2 on the MFMA GEMV kernel instead
-//                       of the lane-per-column one
+//   KQ_GEMV_LANE=0      GEMVs at M <= 2 on the MFMA GEMV kernel instead of
+//                       the lane-per-column ones
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -68,7 +68,7 @@ bool env_fuse() {
   return !(v && !strcmp(v, "0"));
 }
 
-// KQ_GEMV_LANE=0 turns the lane-per-column int4 GEMV off.
+// KQ_GEMV_LANE=0 turns the lane-per-column GEMVs off.
 bool env_gemv_lane() {
   const char* v = getenv("KQ_GEMV_LANE");
   return !(v && !strcmp(v, "0"));

@@ -99,8 +99,7 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
                            bool lane) {
   kq_route_info r{};
   r.splits = 1;
-  const bool lane_gemv = lane && fmt == KQ_W4_AFFINE_G64 && M >= 1 && M <= kGemvLaneRows &&
-                         K <= kFusedMaxK;
+  const bool lane_gemv = lane && M >= 1 && M <= kGemvLaneRows && K <= kFusedMaxK;
   auto lane_geometry = [&]() {
     r.tile_m = kGemvLaneRows;
     r.tile_n = kGemvLaneCols;

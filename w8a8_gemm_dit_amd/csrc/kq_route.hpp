@@ -44,8 +44,8 @@ kq_status validate_linear(const char* op, int64_t M, int64_t K, int64_t N,
 // tile_override: -1 = automatic, else a GemmTile.  split_override: -1 =
 // automatic, 0 or 1 = never split K, n > 1 = n slices (fewer if K is short).
 // fuse: the call quantizes x itself and may take the fused thin-N kernel.
-// lane: int4 weights with M <= kGemvLaneRows and K <= kFusedMaxK take the
-// lane-per-column GEMV kernel (on both GEMV routes).
+// lane: M <= kGemvLaneRows and K <= kFusedMaxK take the lane-per-column
+// GEMV kernels (int4 and int8 weights, on both GEMV routes).
 kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
                            int force, int tile_override, int split_override = 0,
                            bool fuse = false, bool lane = true);
@@ -86,8 +86,9 @@ constexpr int kGemvThinN = 64;  // N up to this takes the GEMV at any M
 constexpr int kGemvAutoRows = 32;  // the automatic route's GEMV takes M up to this
 constexpr int kGemvThreads = 512;
 constexpr int kGemvXqRows = 4;  // the GEMV quantizes x itself up to this many rows
-// Lane-per-column GEMV (int4 weights, M <= kGemvLaneRows, K <= kFusedMaxK):
-// 32 output columns per workgroup of 8 wavefronts, 8 lanes per column.
+// Lane-per-column GEMVs (M <= kGemvLaneRows, K <= kFusedMaxK, either weight
+// format): 32 output columns per workgroup of 8 wavefronts, 8 lanes per
+// column.
 constexpr int kGemvLaneRows = 2;
 constexpr int kGemvLaneCols = 32;
 constexpr int kGemvLaneThreads = 512;
