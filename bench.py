@@ -370,13 +370,25 @@ def graph_replay_time(g, steps: int) -> float:
     return e0.elapsed_time(e1) / steps
 
 
+MIN_SAMPLE_MS = 1.0  # a timed sample (one replay) lasts at least this long
+MAX_CALLS_PER_SAMPLE = 4000
+
+
 def measure(fn, steps: int, n_samples: int, warm_s: float, sink: SampleSink, workload: str,
             leg: str) -> dict:
     """Capture, warm for warm_s, then n_samples timed replays of `steps`
     calls; raw samples go to the sink first.  Returns the summary with the
-    median in "ms"."""
+    median in "ms".  A replay shorter than MIN_SAMPLE_MS is re-captured with
+    proportionally more calls (fast shapes get more calls per sample, so
+    every sample spans at least a millisecond of GPU time)."""
     g = graph_capture(fn, steps)
     nw = warm_replays(g, warm_s)
+    t = graph_replay_time(g, steps) * steps
+    if t < MIN_SAMPLE_MS and steps < MAX_CALLS_PER_SAMPLE:
+        steps = min(MAX_CALLS_PER_SAMPLE, math.ceil(steps * MIN_SAMPLE_MS / max(t, 1e-4)))
+        del g
+        g = graph_capture(fn, steps)
+        nw += warm_replays(g, min(warm_s, 0.1))
     xs = []
     for i in range(n_samples):
         v = graph_replay_time(g, steps)
@@ -385,6 +397,7 @@ def measure(fn, steps: int, n_samples: int, warm_s: float, sink: SampleSink, wor
     del g
     s = summarize(xs, steps)
     s["warm_replays"] = nw
+    s["calls_per_sample"] = steps
     s["ms"] = s["median_ms_per_step"]
     return s
 
@@ -578,6 +591,8 @@ def short_kernel_name(name: str) -> str:
         return f"gemm_w4a8_{m.group(1)}x{m.group(2)}"
     if "gemv_lane_kernel" in name:
         return "gemv_w4a8_lane"
+    if "gemv_lane8_kernel" in name:
+        return "gemv_w8a8_lane"
     m = re.search(r"gemv_kernel<(true|false)", name)
     if m:
         return "gemv_w4a8" if m.group(1) == "true" else "gemv_w8a8"
@@ -657,9 +672,12 @@ def summarize_counters(dirs: str, copy_mib: int, workload: str, traffic_out: str
     return 0
 
 
-def summarize_pmc(path: str) -> int:
+def summarize_pmc(path: str, workload: str = "", clock_out: str = "") -> int:
     """Per (kernel, grid) averages over dispatches of every counter in a
-    rocprofv3 --pmc CSV output directory, as a markdown table."""
+    rocprofv3 --pmc CSV output directory, as a markdown table.  With a
+    workload name and clock_out, the libkq kernels' sustained clock and MFMA /
+    VALU busy shares are recorded in clock_out (keyed kernel@workload, with
+    the kernel's source hash)."""
     import csv
     import glob
 
@@ -691,6 +709,7 @@ def summarize_pmc(path: str) -> int:
             derived.append("MFMA busy %")
         if "SQ_ACTIVE_INST_VALU" in counters:
             derived.append("VALU busy %")
+    rec = {}
     print("| kernel | grid threads | dispatches | " + " | ".join(counters + derived) + " |")
     print("|---|---:|---:|" + "---:|" * (len(counters) + len(derived)))
     for (name, grid), cs in sorted(vals.items(), key=lambda kv: kv[0]):
@@ -702,18 +721,49 @@ def summarize_pmc(path: str) -> int:
             cells.append(f"{us:.2f}")
             if "clock GHz" in derived:
                 gui = sum(cs["GRBM_GUI_ACTIVE"].values()) / len(cs["GRBM_GUI_ACTIVE"]) / 8
+                r = {"clock_ghz": round(gui / us / 1e3, 3), "avg_us": round(us, 3),
+                     "cycles": round(gui), "dispatches": len(ds)}
                 cells.append(f"{gui / us / 1e3:.2f}")
                 if "MFMA busy %" in derived:
                     m = sum(cs["SQ_VALU_MFMA_BUSY_CYCLES"].values()) / len(cs["SQ_VALU_MFMA_BUSY_CYCLES"])
                     cells.append(f"{100 * m / 1024 / gui:.1f}")
+                    r["mfma_busy_pct"] = round(100 * m / 1024 / gui, 2)
                 if "VALU busy %" in derived:
                     v = sum(cs["SQ_ACTIVE_INST_VALU"].values()) / len(cs["SQ_ACTIVE_INST_VALU"])
                     cells.append(f"{100 * 4 * v / 1024 / gui:.1f}")
+                    r["valu_busy_pct"] = round(100 * 4 * v / 1024 / gui, 2)
+                if kernel_source_hash(name):
+                    r["source_hash"] = kernel_source_hash(name)
+                    prev = rec.get(name)
+                    if prev is None or prev["dispatches"] < r["dispatches"]:
+                        rec[name] = r
         elif derived:
             cells += [""] * len(derived)
         shown = name if len(name) < 60 else name[:57] + "..."
         print(f"| `{shown}` | {grid} | {len(ids)} | " + " | ".join(cells) + " |")
+    if workload and clock_out:
+        data = json.load(open(clock_out)) if os.path.exists(clock_out) else {}
+        for k, r in rec.items():
+            data[f"{k}@{workload}"] = r
+        with open(clock_out, "w") as fh:
+            json.dump(data, fh, indent=1, sort_keys=True)
+        print(f"\n{len(rec)} kernel(s) of {workload} written to {clock_out}", file=sys.stderr)
     return 0
+
+
+def recorded_clock(kernel: str, workload: str):
+    """The sustained clock record of `kernel` at `workload` from the committed
+    counter summary, or None if absent or taken on a different source."""
+    p = os.path.join(ROOT, "profiles", "sustained_clock.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(f"{kernel}@{workload}")
+    except Exception:
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash(kernel):
+        return None
+    return rec
 
 
 # ------------------------------------------------------------ hashes
@@ -770,6 +820,9 @@ def main() -> int:
     ap.add_argument("--summarize-pmc", default="", metavar="DIR",
                     help="per-kernel averages of every counter in a rocprofv3 --pmc output "
                          "directory (no GPU)")
+    ap.add_argument("--clock-out", default="", metavar="JSON",
+                    help="with --summarize-pmc and --workload: record the libkq kernels' "
+                         "sustained clock and MFMA / VALU busy shares in this file")
     ap.add_argument("--copy-mib", type=int, default=256,
                     help="size of the copy probe the counters are scaled by")
     ap.add_argument("--traffic-out", default="", metavar="JSON",
@@ -784,7 +837,7 @@ def main() -> int:
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace)
     if args.summarize_pmc:
-        return summarize_pmc(args.summarize_pmc)
+        return summarize_pmc(args.summarize_pmc, args.workload, args.clock_out)
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters, args.copy_mib, args.workload,
                                   args.traffic_out)
@@ -935,6 +988,24 @@ def main() -> int:
                        "gemm_kernel_us": round(ms_gemm * 1e3, 3),
                        "call_us": round(ms * 1e3, 3)},
     }
+    clk = recorded_clock(gemm_name, wl.name)
+    if clk:
+        # the peak scaled to the clock the kernel sustains under load (the
+        # published peak assumes 2.4 GHz; the package power limit lowers it)
+        # A counter run serializes dispatches; the kernel's cycle count from
+        # it over the launch time measured here gives the clock it holds
+        # in the timed region (its cycles barely move with the clock when
+        # it is compute bound); the higher of the two readings is used
+        ghz = clk["clock_ghz"]
+        if clk.get("cycles"):
+            ghz = max(ghz, clk["cycles"] / (ms_gemm * 1e6))
+        peak_clk = PEAK_INT8_TOPS * min(ghz, 2.4) / 2.4
+        result["roofline"]["sustained_clock_ghz"] = round(ghz, 3)
+        result["roofline"]["counter_run_clock_ghz"] = clk["clock_ghz"]
+        result["roofline"]["peak_at_sustained_clock"] = round(peak_clk, 1)
+        result["roofline"]["frac_at_sustained_clock"] = round(gemm_tops / peak_clk, 4)
+        if "mfma_busy_pct" in clk:
+            result["roofline"]["mfma_busy_pct"] = clk["mfma_busy_pct"]
     if "mfma_i8" in floors:
         result["roofline"]["measured_mfma_only_tops"] = floors["mfma_i8"]["tops"]
         result["roofline"]["frac_of_measured"] = round(gemm_tops / floors["mfma_i8"]["tops"], 4)

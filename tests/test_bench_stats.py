@@ -80,3 +80,48 @@ def test_summarize_trace(tmp_path):
                           str(tmp_path)], capture_output=True, text=True, check=True).stdout
     line = next(l for l in out.splitlines() if "gemm_a" in l)
     assert "| 2 | 3.00 | 3.00 |" in line
+
+
+def test_summarize_pmc_records_the_sustained_clock(tmp_path):
+    # one dispatch of 1000 us whose GRBM_GUI_ACTIVE sums to 8 x 1.8e6 cycles
+    # over the 8 XCDs: 1.8 GHz; MFMA busy 1024 SIMDs x 0.9e6 cycles: 50 %
+    name = "void kq::gemm_w8a8_kernel<256, 256, 2, 4, 64, __hip_bfloat16, false>(...)"
+    (tmp_path / "s_kernel_trace.csv").write_text(
+        "Dispatch_Id,Kernel_Name,Start_Timestamp,End_Timestamp\n"
+        f"7,\"{name}\",0,1000000\n")
+    (tmp_path / "s_counter_collection.csv").write_text(
+        "Dispatch_Id,Kernel_Name,Grid_Size,Counter_Name,Counter_Value\n"
+        f"7,\"{name}\",1572864,GRBM_GUI_ACTIVE,{8 * 1.8e6}\n"
+        f"7,\"{name}\",1572864,SQ_VALU_MFMA_BUSY_CYCLES,{1024 * 0.9e6}\n")
+    out = tmp_path / "clock.json"
+    subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--summarize-pmc", str(tmp_path),
+                    "--workload", "wl", "--clock-out", str(out)], capture_output=True, text=True,
+                   check=True)
+    rec = json.load(open(out))["gemm_w8a8_256x256w8@wl"]
+    assert rec["clock_ghz"] == pytest.approx(1.8)
+    assert rec["mfma_busy_pct"] == pytest.approx(50.0)
+    assert rec["cycles"] == pytest.approx(1.8e6)
+    assert rec["source_hash"] == bench.kernel_source_hash("gemm_w8a8_256x256w8")
+
+
+class _FakeGraph:
+    def __init__(self, per_call_ms):
+        self.per_call_ms = per_call_ms
+
+
+def test_fast_shapes_get_more_calls_per_sample(monkeypatch):
+    per_call = 0.01   # ms per call: 20 calls take 0.2 ms, below the 1 ms floor
+    monkeypatch.setattr(bench, "graph_capture", lambda fn, steps: _FakeGraph(per_call))
+    monkeypatch.setattr(bench, "warm_replays", lambda g, s: 1)
+    monkeypatch.setattr(bench, "graph_replay_time", lambda g, steps: g.per_call_ms)
+    got = []
+
+    class Sink:
+        def add(self, wl, leg, i, steps, v):
+            got.append(steps)
+
+    s = bench.measure(None, 20, 5, 0.1, Sink(), "wl", "call")
+    assert s["calls_per_sample"] * per_call >= bench.MIN_SAMPLE_MS
+    assert set(got) == {s["calls_per_sample"]}
+    s = bench.measure(None, 500, 5, 0.1, Sink(), "wl", "call")   # 5 ms: unchanged
+    assert s["calls_per_sample"] == 500
