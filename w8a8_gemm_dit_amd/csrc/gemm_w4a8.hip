@@ -42,8 +42,11 @@ namespace {
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
-// Activation-row swizzle of the W8A8 ring: chunk index ^ ((r/2)%4 ^ (r/8)%2).
-__device__ __forceinline__ int swz4(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+// Activation-row swizzle of the W8A8 ring: chunk index ^ ((r/2)%4 ^ 3*((r/8)%2)),
+// so that the 32 lanes gfx950 serves per clock of a ds_read_b128 fragment
+// read (16 rows x 2 chunks, rows r and r+8 512 bytes apart) hit distinct
+// bank groups.
+__device__ __forceinline__ int swz4(int row) { return ((row >> 1) & 3) ^ (((row >> 3) & 1) * 3); }
 
 constexpr int kSG = 16;  // groups per table chunk (one f16 MFMA: 16 groups x {hi, lo})
 

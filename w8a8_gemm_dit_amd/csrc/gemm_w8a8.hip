@@ -77,12 +77,14 @@ struct Cfg {
 };
 
 // LDS row swizzle: the 16-byte chunk index of row r is XORed with
-// ((r/2)%4) ^ ((r/8)%2).  Rows r and r+8 sit a multiple of 256 bytes apart,
-// so a fragment read (16 consecutive rows, one chunk) touches 16 distinct
-// 16-byte bank groups per 16 lanes and 8 distinct ones per 8 lanes: it is
-// conflict-free whether the LDS serves 8 or 16 lanes of a ds_read_b128 per
-// clock.  The value depends on r % 16 only.
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+// ((r/2)%4) ^ 3*((r/8)%2).  gfx950 serves 32 lanes of a ds_read_b128 per
+// clock from a 512-byte bank period; a fragment read (16 consecutive rows,
+// chunk c for lanes 0-15 and c^1 for lanes 16-31) then needs rows r and
+// r+8, which sit a multiple of 512 bytes apart, to differ in bit 1 of the XOR (with
+// ^1 instead of ^3 they collide pairwise: 2-way conflicts, measured).
+// Every 8, 16 and 32 consecutive lanes hit distinct 16-byte bank groups.
+// The value depends on r % 16 only.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) & 3) ^ (((row >> 3) & 1) * 3); }
 
 // A pair buffer holds two consecutive K steps (64 bytes of every row each)
 // as 1 KB blocks of 8 rows: [step 2p: 8 rows x 64 B][step 2p+1: 8 rows x
@@ -198,7 +200,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
   const int rr = (lane & 31) >> 2;
   const uint32_t vbase = (uint32_t)(rr * K + (lane >> 5) * 64);
   const uint32_t voff0 = vbase + (uint32_t)(((lane & 3) ^ ((rr >> 1) & 3)) * 16);
-  const uint32_t voff1 = vbase + (uint32_t)(((lane & 3) ^ ((rr >> 1) & 3) ^ 1) * 16);
+  const uint32_t voff1 = vbase + (uint32_t)(((lane & 3) ^ ((rr >> 1) & 3) ^ 3) * 16);
   const int KT = min(kchunk, K - k0) / 64;
   // Fill a pair buffer with K steps 2*pi and 2*pi+1.  Pairs past the end
   // re-load the last one into a buffer that is never read again; with an
@@ -509,7 +511,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_persist(
   const int rr = (lane & 31) >> 2;
   const uint32_t vbase = (uint32_t)(rr * K + (lane >> 5) * 64);
   const uint32_t voff0 = vbase + (uint32_t)(((lane & 3) ^ ((rr >> 1) & 3)) * 16);
-  const uint32_t voff1 = vbase + (uint32_t)(((lane & 3) ^ ((rr >> 1) & 3) ^ 1) * 16);
+  const uint32_t voff1 = vbase + (uint32_t)(((lane & 3) ^ ((rr >> 1) & 3) ^ 3) * 16);
 
   // This tile (m0, n0) and the next one (m1, n1); has_next false at the last.
   int t = blockIdx.x;
