@@ -45,7 +45,9 @@ def test_workspace_layout():
     assert kq.kq_workspace_bytes(M, N, K, kq.KQ_W4_AFFINE_G64) == al(M * K) + al(4 * M) + al(4 * M * K // 64)
     assert kq.kq_workspace_bytes(0, N, K, kq.KQ_W8_PER_CHANNEL) == 0
     assert kq.kq_workspace_bytes(M, 0, K, kq.KQ_W8_PER_CHANNEL) == 0
-    assert kq.kq_workspace_bytes(3, N, 64, kq.KQ_W8_PER_CHANNEL) == 256 + 256
+    # codes for rows rounded up to 16 (the GEMV's fragment order covers
+    # whole 16-row blocks)
+    assert kq.kq_workspace_bytes(3, N, 64, kq.KQ_W8_PER_CHANNEL) == 1024 + 256
     # the fused routes use only the scales, but the size covers the
     # two-kernel route of the same shape
     assert kq.kq_route(2048, 48, 5120, kq.KQ_W8_PER_CHANNEL)["kind"] == "fused"
@@ -62,15 +64,15 @@ def test_workspace_layout():
 @pytest.mark.parametrize("M,N,K,fmt,kind,tile,grid", [
     (1, 13824, 5120, kq.KQ_W4_AFFINE_G64, "fused", (2, 32), 432),   # lane GEMV quantizing x itself
     (2, 13824, 5120, kq.KQ_W4_AFFINE_G64, "fused", (2, 32), 432),
-    (3, 13824, 5120, kq.KQ_W4_AFFINE_G64, "fused", (4, 16), 864),   # MFMA GEMV quantizing x itself
-    (1, 13824, 6208, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 864),   # past the lane kernel's K limit
-    (4, 18432, 3072, kq.KQ_W8_PER_CHANNEL, "fused", (4, 16), 1152),
+    (3, 13824, 5120, kq.KQ_W4_AFFINE_G64, "fused", (4, 32), 432),   # MFMA GEMV quantizing x itself
+    (1, 13824, 6208, kq.KQ_W4_AFFINE_G64, "gemv", (16, 32), 432),   # past the lane kernel's K limit
+    (4, 18432, 3072, kq.KQ_W8_PER_CHANNEL, "fused", (4, 16), 1152),  # int8: 16 columns
     (4, 512, 6208, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 32),      # past its K limit
-    (5, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 864),
-    (16, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 864),
+    (5, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 32), 432),
+    (16, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 32), 432),
     (4, 512, 16384, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 32),
     (4, 512, 16448, kq.KQ_W8_PER_CHANNEL, "gemm", None, None),
-    (17, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 864 * 2),  # two row blocks
+    (17, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 32), 432 * 2),  # two row blocks
     (32, 13824, 5120, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 864 * 2),
     (33, 13824, 5120, kq.KQ_W4_AFFINE_G64, "gemm", None, None),
     (4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL, "gemm", (256, 192), 256),
@@ -81,7 +83,7 @@ def test_workspace_layout():
     (2048, 48, 5120, kq.KQ_W8_PER_CHANNEL, "fused", (8, 48), 256),   # thin N: one kernel
     (300, 64, 640, kq.KQ_W4_AFFINE_G64, "fused", (8, 64), 38),
     (17, 48, 5120, kq.KQ_W4_AFFINE_G64, "fused", (8, 48), 3),
-    (16, 48, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 16), 3),         # one row block: GEMV
+    (16, 48, 5120, kq.KQ_W4_AFFINE_G64, "gemv", (16, 32), 2),         # one row block: GEMV
     (2048, 33, 6144, kq.KQ_W8_PER_CHANNEL, "fused", (8, 48), 256),
     (2048, 48, 6208, kq.KQ_W8_PER_CHANNEL, "gemv", (16, 16), 3 * 128),  # past the fused K limit
     (300, 65, 640, kq.KQ_W8_PER_CHANNEL, "gemm", (64, 64), 5 * 2),
@@ -146,7 +148,7 @@ def test_split_k_lever(kq_env):
 def test_gemv_lane_lever(kq_env):
     kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_FUSE=None, KQ_GEMV_LANE="0")
     r = kq.kq_route(1, 13824, 5120, kq.KQ_W4_AFFINE_G64)
-    assert (r["kind"], r["tile_m"], r["tile_n"], r["grid"]) == ("fused", 4, 16, 864)
+    assert (r["kind"], r["tile_m"], r["tile_n"], r["grid"]) == ("fused", 4, 32, 432)
     kq_env(KQ_GEMV_LANE=None, KQ_FORCE_ROUTE="gemv")
     r = kq.kq_route(2, 13824, 5120, kq.KQ_W4_AFFINE_G64)
     assert (r["kind"], r["tile_m"], r["tile_n"], r["grid"]) == ("gemv", 2, 32, 432)
@@ -155,6 +157,8 @@ def test_gemv_lane_lever(kq_env):
     assert (r["kind"], r["tile_m"], r["tile_n"]) == ("gemv", 2, 32)
     r = kq.kq_route(3, 13824, 5120, kq.KQ_W8_PER_CHANNEL)
     assert (r["kind"], r["tile_m"], r["tile_n"]) == ("gemv", 16, 16)
+    r = kq.kq_route(3, 13824, 5120, kq.KQ_W4_AFFINE_G64)
+    assert (r["kind"], r["tile_m"], r["tile_n"]) == ("gemv", 16, 32)
 
 
 def test_fused_route_lever(kq_env):
@@ -162,7 +166,7 @@ def test_fused_route_lever(kq_env):
     r = kq.kq_route(2048, 48, 5120, kq.KQ_W8_PER_CHANNEL)
     assert (r["kind"], r["grid"]) == ("gemv", 3 * 128)
     assert kq.kq_route(1, 13824, 5120, kq.KQ_W4_AFFINE_G64)["kind"] == "gemv"
-    assert kq.kq_workspace_bytes(3, 3072, 64, kq.KQ_W8_PER_CHANNEL) == 256 + 256
+    assert kq.kq_workspace_bytes(3, 3072, 64, kq.KQ_W8_PER_CHANNEL) == 1024 + 256
     kq_env(KQ_FUSE=None, KQ_FORCE_ROUTE="gemm")
     assert kq.kq_route(2048, 48, 5120, kq.KQ_W8_PER_CHANNEL)["kind"] == "gemm"
 

@@ -182,7 +182,8 @@ GEMV_XQ = [(1, 64, 16), (2, 320, 200), (3, 1088, 33), (4, 5120, 256), (1, 6144, 
 def test_gemv_xq_matches_oracle(M, K, N, fmt, lane, kq_env):
     """M <= 4: the GEMV quantizes its rows in its prologue (route "fused");
     M <= 2 on the lane-per-column kernels (2-row, 32-column tile) unless
-    KQ_GEMV_LANE=0, else the MFMA GEMV (4-row, 16-column tile); codes
+    KQ_GEMV_LANE=0, else the MFMA GEMV (4-row tile of 32 columns for int4
+    weights, 16 for int8); codes
     (through the int32 outputs) and scales bit-exact."""
     if lane == "0" and not M <= 2:
         pytest.skip("the lever changes only GEMVs at M <= 2")
@@ -191,7 +192,8 @@ def test_gemv_xq_matches_oracle(M, K, N, fmt, lane, kq_env):
     if M <= 2 and lane is None:
         assert (r["kind"], r["tile_m"], r["grid"]) == ("fused", 2, -(-N // 32))
     else:
-        assert (r["kind"], r["tile_m"], r["grid"]) == ("fused", 4, -(-N // 16))
+        cols = 32 if fmt == "w4" else 16
+        assert (r["kind"], r["tile_m"], r["grid"]) == ("fused", 4, -(-N // cols))
     seed = 7 * M + K + N
     dist = "student_t4" if (M + K) % 2 else "normal"
     xb = synth.random_bf16((M, K), seed=seed, dist=dist)

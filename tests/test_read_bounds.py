@@ -145,3 +145,51 @@ def _lane_gemv_case(N, K, slices=2, w8=False):
 @pytest.mark.parametrize("w8", [False, True])
 def test_lane_gemv_reads_stay_in_the_weights(N, K, w8):
     _lane_gemv_case(N, K, w8=w8)
+
+
+# int4 MFMA GEMV (gemv.hip, M >= 3 or K > 6144): a workgroup owns 32 columns
+# (two blocks of 16) and 8 wavefronts split the K groups into slices of
+# `per` groups (rounded to the 2-group load unit for int4).  Weights: the
+# descriptor starts at column n0 with num_records = cols * RB; lane (q, c)
+# of unit u reads 16 bytes at c*RB + UB*g0 + 16q + 16*b*RB + UB*GU*u for
+# column block b, units past the wavefront's share at an offset past
+# num_records.  Activation codes in fragment order: the descriptor starts at
+# the 16-row block (G KB each) with num_records = G*1024; lane l of group g
+# reads 16 bytes at 1024*g + 16*l.
+def _reg_gemv_case(M, N, K, w4):
+    G = K // 64
+    RB = K // 2 if w4 else K
+    UB, GU = (32, 2) if w4 else (64, 1)
+    per = (-(-G // 8) + GU - 1) // GU * GU
+    for blk in range(-(-N // 32)):
+        n0 = 32 * blk
+        cols = min(32, N - n0)
+        nrec = cols * RB
+        for w in range(8):
+            g0 = min(w * per, G)
+            gn = min(per, G - g0)
+            nu = -(-gn // GU)
+            for u in range(nu):
+                for lane in range(64):
+                    q, c = lane >> 4, lane & 15
+                    for b in range(2):
+                        off = c * RB + UB * g0 + 16 * q + 16 * b * RB + UB * GU * u
+                        if off < nrec:  # fetched: inside the weight buffer
+                            assert 0 <= n0 * RB + off and n0 * RB + off + 15 < N * RB
+                        col = 16 * b + c
+                        byte = UB * (g0 + GU * u) + 16 * q  # first byte in the column's row
+                        g = (g0 + GU * u) + (16 * q) // UB   # the group those bytes hold
+                        if col < cols and g < G and g - g0 < gn:  # used: the right column's row
+                            assert byte + 15 < RB and col * RB + byte + 15 < nrec
+        for mb in range(-(-M // 16)):
+            for g in range(G):
+                for lane in range(64):
+                    off = 1024 * g + 16 * lane
+                    assert off + 15 < G * 1024
+                    assert mb * G * 1024 + off + 15 < (-(-M // 16) * 16) * K
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 13824, 5120), (16, 48, 5120), (17, 40, 6208), (5, 33, 64),
+                                   (32, 100, 16384), (4, 64, 1088)])
+def test_mfma_gemv_reads_stay_in_the_operands(M, N, K):
+    _reg_gemv_case(M, N, K, True)

@@ -1,6 +1,6 @@
 // Small-M GEMV of libkq: "qlip-mlx" README, w4a8_linear bullet -- a
 // register-dequant GEMV path for small batches, so decode-style calls run at
-// weight-bandwidth speed.  One workgroup computes 16 activation rows x 16
+// weight-bandwidth speed.  One workgroup computes 16 activation rows x 32
 // output columns over all of K; the grid's second dimension walks 16-row
 // blocks, so the same kernel also serves thin-N shapes (few output
 // columns, many rows), which the tiled GEMM would spread over too few
@@ -12,23 +12,37 @@
 // weight byte where the 16-row MFMA tile would be mostly empty).
 //
 // gfx950 design (HBM-bound: every weight byte is read once):
-//   - a workgroup owns 16 output columns and its 8 wavefronts split the K
-//     groups into 8 contiguous slices (rounded to whole 128-byte lines);
-//   - each wavefront streams its slice through a private LDS chunk with
-//     direct global->LDS buffer loads: one load instruction moves 8 rows x
-//     one full 128-byte line, and the LDS layout is the MFMA fragment order,
-//     so the fragment reads are contiguous and conflict-free.  A small chunk
-//     (4 groups) keeps the LDS per workgroup low, so several workgroups per
-//     CU keep loads in flight;
-//   - the 16 columns' fp16 group scales and offsets are one contiguous run
+//   - a workgroup owns 32 output columns (two MFMA column blocks) and its 8
+//     wavefronts split the K groups into 8 contiguous slices; each
+//     wavefront computes both column blocks of its slice, so one activation
+//     operand serves two weight operands;
+//   - the weights go straight to registers, already in MFMA operand order:
+//     a load unit is 16 bytes a lane, lane (q, c) = (l/16, l%16) taking
+//     bytes 16q..16q+15 of a 64-byte run of column c, so one instruction
+//     moves 64 bytes of each of 16 columns (two int4 groups or one int8
+//     group).  The units of a slice are issued D ahead of the arithmetic,
+//     so the weight stream stays in flight while it runs;
+//   - int4: lanes q = 0, 1 hold the first group of a unit and q = 2, 3 the
+//     second; v_permlane32_swap exchanges the upper half of the first
+//     operand with the lower half of the second, which leaves MFMA k chunk
+//     q of one group with bytes {0, 16, 8, 24}[q] .. +8 of it (16 codes in
+//     order), and the activation codes are read at the matching k offsets;
+//   - the activation codes come either row-major (the entry points on
+//     caller-given codes: 16 rows x 64 bytes per load) or in the fragment
+//     order the linears' quantize kernel writes for this kernel (one
+//     contiguous 1 KB per 16-row block and group: the load of a group's
+//     operand reads 8 whole lines);
+//   - buffer descriptors: rows past M, columns past N, groups past K and
+//     units past a wavefront's share read as zero without touching memory;
+//   - the 32 columns' fp16 group scales and offsets are one contiguous run
 //     per array; the workgroup stages them in LDS with coalesced loads
 //     issued before the weight loads;
-//   - v_mfma_i32_16x16x64_i8 with the activation codes as the A operand
-//     (rows >= M zero) and the weights as B; a second MFMA against an
-//     all-ones B gives the group sums A exactly, so no group-sum input is
-//     read;
-//   - the 8 partial sums are reduced through LDS (fp32 for int4 weights,
-//     exact int32 for int8) and one wavefront applies the epilogue.
+//   - v_mfma_i32_16x16x64_i8 with the activation codes as the A operand and
+//     the weights as B; a second MFMA against an all-ones B gives the group
+//     sums A exactly, so no group-sum input is read;
+//   - the 8 partial sums of each column block are reduced through LDS (fp32
+//     for int4 weights, exact int32 for int8) and wavefronts 0 and 1 apply
+//     the epilogue of one column block each.
 #include "kq_common.hpp"
 #include "kq_launch.hpp"
 #include "kq_route.hpp"
@@ -38,66 +52,67 @@ namespace kq {
 namespace {
 
 constexpr int kWaves = 8;         // K slices per workgroup
-constexpr int kChunk = 4;         // groups per LDS chunk of one wavefront
-constexpr int kMaxG = kGemvMaxK / 64;
+constexpr int kCB = 2;            // 16-column MFMA blocks per workgroup
+static_assert(16 * kCB == kGemvCols, "GEMV columns per workgroup");
 // In-kernel quantization (XQ): at most kGemvXqRows rows and slices of at
 // most kXqMaxGPW groups (K <= kFusedMaxK).
 constexpr int kXqMaxGPW = 12;
 constexpr int kXT = kXqMaxGPW / 2;  // 16-byte x loads per lane
-static_assert(((int)(kFusedMaxK / 64) + kWaves - 1) / kWaves <= kXqMaxGPW &&
-              kXqMaxGPW % kChunk == 0, "XQ slices");
+static_assert(((int)(kFusedMaxK / 64) + kWaves - 1) / kWaves <= kXqMaxGPW, "XQ slices");
 static_assert(kGemvXqRows * 16 == 64, "XQ x loads: 16 lanes per row");
 
 // XQ: A is unused and the kernel quantizes bf16 rows X itself (Mtot <=
 // kGemvXqRows, one row block): the same absmax rule and rounding as the
 // quantize kernel; the token scales go to sx_out (if not NULL).
-template <bool W4, int OUT, bool XQ>
-__global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
+// AF: A in the fragment order (gemv_frag_offset), else row-major.
+// NU: load units a wavefront issues (its slice, rounded up; the units past
+// its share read zero), D: units in flight ahead of the arithmetic.
+template <int OUT, bool XQ, bool AF, int NU, int D>
+__global__ __launch_bounds__(kWaves * 64) void gemv_w4_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ sx,
-    const void* __restrict__ Wq, const void* __restrict__ gsv, const void* __restrict__ gbv,
-    const float* __restrict__ bias, void* y, int Mtot, int N, int K, Epilogue ep,
-    const uint16_t* __restrict__ X, float* __restrict__ sx_out) {
+    const uint8_t* __restrict__ Wq, const uint16_t* __restrict__ gsv,
+    const uint16_t* __restrict__ gbv, const float* __restrict__ bias, void* y, int Mtot, int N,
+    int K, Epilogue ep, const uint16_t* __restrict__ X, float* __restrict__ sx_out) {
+  static_assert(D >= 1 && D <= NU, "pipeline depth");
+  constexpr int GU = 2;                     // groups per load unit
+  constexpr int UB = 32;                    // bytes of one weight column per group
+  constexpr bool kScales = OUT != kOutI32;
+  constexpr int kC = 16 * kCB;              // columns per workgroup
+  static_assert(!XQ || NU * GU <= kXqMaxGPW, "XQ slices");
   // this workgroup's 16-row block of the activations
   const int m0 = blockIdx.y * 16;
   const int M = min(16, Mtot - m0);
-  A += (int64_t)m0 * K;
   if (sx != nullptr) sx += m0;
-  constexpr int UB = W4 ? 32 : 64;          // bytes of one weight row per group
-  constexpr int LPR = UB / 16;              // DMA lanes per (row, group)
-  constexpr int GPB = 128 / UB;             // groups per 128-byte line (one DMA block)
-  constexpr int WLDS = kChunk * 16 * UB;    // LDS bytes of one wavefront's chunk
-  constexpr bool kScales = W4 && OUT != kOutI32;
-  static_assert(kChunk % GPB == 0, "a chunk is whole DMA blocks");
-  __shared__ __attribute__((aligned(16))) int8_t lds_w[kWaves][WLDS];
-  __shared__ float lds_red[kWaves - 1][4][64];
+  __shared__ float lds_red[kWaves][kCB][4][64];
   __shared__ float s_xamax[XQ ? kWaves : 1][kGemvXqRows];
   __shared__ float s_xscale[kGemvXqRows];
-  extern __shared__ uint32_t lds_sb[];      // [G][16]: scale | offset << 16 (int4 only)
+  extern __shared__ uint32_t lds_sb[];      // [G][kC]: scale | offset << 16 (int4 only)
 
   const int G = K / 64;
-  const int RB = W4 ? K / 2 : K;            // bytes per weight row
-  const int n0 = blockIdx.x * 16;
-  const int rows = min(16, N - n0);
+  const int RB = K / 2;                     // bytes per weight row
+  const int n0 = blockIdx.x * kC;
+  const int cols = min(kC, N - n0);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  // Wave-uniform (readfirstlane): slice guards are scalar branches, the
-  // LDS DMA bases stay scalar and every MFMA runs with the full EXEC mask.
+  // Wave-uniform (readfirstlane): slice guards are scalar branches and
+  // every MFMA runs with the full EXEC mask.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15;  // MFMA A row m / B column of this lane
   const int fc = lane >> 4;  // MFMA 16-wide k chunk / output row block
-  const int per = ((G + kWaves - 1) / kWaves + GPB - 1) / GPB * GPB;
+  const int per = ((G + kWaves - 1) / kWaves + GU - 1) / GU * GU;
   const int g0 = min(wave * per, G);
   const int gn = min(per, G - g0);  // 0 for trailing wavefronts of short K
+  const int nu = (gn + GU - 1) / GU;
 
-  // 1. Scale/offset staging loads: rows n0..n0+rows-1 of the [N, G] arrays
-  //    are one contiguous run of rows*G halves; issued first so that the LDS
-  //    writes below wait for these loads only.
-  constexpr int kSL = kScales ? kMaxG * 16 / (kWaves * 64) : 1;
+  // 1. Scale/offset staging loads: columns n0..n0+cols-1 of the [N, G]
+  //    arrays are one contiguous run of cols*G halves; issued first so that
+  //    the LDS writes below wait for these loads only.
+  constexpr int kSL = kScales ? (NU * GU * kWaves * kC + kWaves * 64 - 1) / (kWaves * 64) : 1;
   uint32_t sreg[kSL];
   if (kScales) {
-    const uint16_t* hs = reinterpret_cast<const uint16_t*>(gsv) + (int64_t)n0 * G;
-    const uint16_t* hb = reinterpret_cast<const uint16_t*>(gbv) + (int64_t)n0 * G;
-    const int lim = rows * G;
+    const uint16_t* hs = gsv + (int64_t)n0 * G;
+    const uint16_t* hb = gbv + (int64_t)n0 * G;
+    const int lim = cols * G;
     // Unconditional loads at a clamped index (lim >= 1): all of them issue
     // back to back (loads under a per-lane guard were each waited for
     // before the next one issued).
@@ -112,39 +127,327 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
     for (int j = 0; j < kSL; ++j)
       sreg[j] = tid + j * kWaves * 64 < lim ? (uint32_t)sl[j] | ((uint32_t)bl[j] << 16) : 0u;
   }
+  // XQ: x with whole-line loads, issued before the weights (load counters
+  // retire in order, so the absmax below then waits for x alone).  Lane l
+  // takes row l/16 and, for t < kXT, the 16 bytes of values 8*(l%8)..+7 of
+  // slice group 2t + (l%16)/8, so the 16 lanes of a row read 256
+  // contiguous bytes per instruction.
+  const int xr = lane >> 4, xj = lane & 15;
+  v4i xq[XQ ? kXT : 1];
+  if constexpr (XQ) {
+    const v4i* xrow = reinterpret_cast<const v4i*>(X + (int64_t)min(xr, Mtot - 1) * K + 8 * (xj & 7));
+#pragma unroll
+    for (int t = 0; t < kXT; ++t) {
+      const int gi = 2 * t + (xj >> 3);
+      xq[t] = v4i{0, 0, 0, 0};
+      if (gi < gn && xr < Mtot) xq[t] = xrow[(g0 + gi) * 8];
+    }
+  }
+  // Epilogue operands of column block wave (< kCB), loaded ahead of the
+  // weights.
+  const int eb = min(wave, kCB - 1);
+  const int nn = n0 + 16 * eb + fr;
+  const int nc = min(nn, N - 1);
+  const float bv = bias ? bias[nc] : 0.0f;
+  float sxm[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) sxm[r] = (OUT != kOutI32 && !XQ) ? sx[min(4 * fc + r, M - 1)] : 0.0f;
+  __builtin_amdgcn_sched_barrier(0);
 
-  // 2. Weight DMA.  The descriptor is rebased on row n0 with num_records =
-  //    rows*RB: rows past N and groups past the matrix end read as zero.
-  //    Block (r8, blk) = rows 8*r8..8*r8+7 x groups blk*GPB.. of the chunk;
-  //    lane l moves 16 bytes: group l/(8*LPR), row (l/LPR)%8, piece l%LPR,
-  //    into LDS byte 16*l of the block, which puts (row r, chunk group i) at
-  //    (r/8)*kChunk*8*UB + i*8*UB + (r%8)*UB -- the fragment order.
+  // 2. Weight and activation loads of unit u (groups g0 + GU*u ..).
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(reinterpret_cast<const int8_t*>(Wq) + (int64_t)n0 * RB), 0,
-      rows * RB, 0x00020000);
+      const_cast<uint8_t*>(Wq + (int64_t)n0 * RB), 0,
+      __builtin_amdgcn_readfirstlane(cols * RB), 0x00020000);
+  const int8_t* abase = XQ ? reinterpret_cast<const int8_t*>(X)
+                      : AF ? A + (int64_t)blockIdx.y * G * 1024 : A + (int64_t)m0 * K;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(abase), 0,
+      __builtin_amdgcn_readfirstlane(XQ ? 0 : AF ? G * 1024 : M * K), 0x00020000);
+  const int woff = fr * RB + UB * g0 + 16 * fc;
+  const int kc0 = ((fc & 1) << 5) | ((fc & 2) << 3);  // k of chunk fc: 0, 32, 16, 48
+  const int aoff = AF ? 1024 * g0 + 16 * lane : fr * K + 64 * g0 + kc0;
+  constexpr int AG = AF ? 1024 : 64;        // A bytes from one group to the next
+  v4i wr[D][kCB];
+  v4i ar[XQ ? 1 : D][GU];
+  auto issue = [&](int u, int s) {
+    const bool ok = u < nu;  // wave-uniform
+    if constexpr (!XQ) {
+#pragma unroll
+      for (int j = 0; j < GU; ++j) {
+        const int gi = GU * u + j;
+        ar[s][j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+            ra, ok && gi < gn ? aoff + AG * gi : 0x40000000, 0, 0));
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kCB; ++b)
+      wr[s][b] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+          rw, ok ? woff + 16 * b * RB + UB * GU * u : 0x40000000, 0, 0));
+  };
+#pragma unroll
+  for (int u = 0; u < D; ++u) issue(u, u);
+  __builtin_amdgcn_sched_barrier(0);
+
+  if constexpr (XQ) {
+    // Row absmax on the bf16 bit patterns (for finite values the magnitude
+    // bits order as |x|), over the row's 16 lanes, then the 8 slices.
+    u16x2 mb = u16x2{0, 0};
+#pragma unroll
+    for (int t = 0; t < kXT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mb = absmax_bits2(mb, (uint32_t)xq[t][j]);
+    float am = absmax_bits_value(mb);
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) am = fmaxf(am, __shfl_xor(am, off, kWave));
+    if (xj == 0) s_xamax[wave][xr] = am;
+  }
+  if (kScales) {
+#pragma unroll
+    for (int j = 0; j < kSL; ++j) {
+      const int e = tid + j * kWaves * 64;
+      if (e < kC * G) {
+        const int r = e / G, g = e - r * G;
+        lds_sb[g * kC + r] = sreg[j];
+      }
+    }
+  }
+  if (kScales || XQ) {
+    wait_vm_lgkm0<63>();  // LDS writes done; the weights may still fly
+    barrier_nofence();
+  }
+  // XQ: the codes (codes8_shift: the quantize kernel's rule); xc[t] holds
+  // the 8 codes of the lane's load t, 4 per dword.
+  int xc[XQ ? kXT : 1][2];
+  if constexpr (XQ) {
+    float am = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) am = fmaxf(am, s_xamax[w][xr]);
+    float scale;
+    const float inv = row_inv(am, scale);
+    if (wave == 0 && xj == 0) {
+      s_xscale[xr] = scale;
+      if (sx_out != nullptr && xr < Mtot) sx_out[xr] = scale;
+    }
+#pragma unroll
+    for (int t = 0; t < kXT; ++t) {
+      const uint32_t w[4] = {(uint32_t)xq[t][0], (uint32_t)xq[t][1], (uint32_t)xq[t][2],
+                             (uint32_t)xq[t][3]};
+      const uint2 c = codes8_shift(w, inv);
+      xc[t][0] = (int)c.x;
+      xc[t][1] = (int)c.y;
+    }
+  }
+  // XQ operand of slice group gi: lane fr + 16*fc (rows fr < 4) takes the
+  // codes of values kc0..kc0+15 of the group from lanes 16*fr + 8*(gi%2) +
+  // kc0/8 and + 1 (their loads t = gi/2); rows 4-15 are zero.
+  const int xsrc = 4 * (16 * (fr & 3) + kc0 / 8);  // ds_bpermute byte address, gi even
+  auto xq_operand = [&](int gi) {
+    const int sa = xsrc + 32 * (gi & 1);
+    v4i f = v4i{__builtin_amdgcn_ds_bpermute(sa, xc[gi >> 1][0]),
+                __builtin_amdgcn_ds_bpermute(sa, xc[gi >> 1][1]),
+                __builtin_amdgcn_ds_bpermute(sa + 4, xc[gi >> 1][0]),
+                __builtin_amdgcn_ds_bpermute(sa + 4, xc[gi >> 1][1])};
+    if (fr >= kGemvXqRows) f = v4i{0, 0, 0, 0};
+    return f;
+  };
+
+  v4f facc[kCB];
+#pragma unroll
+  for (int b = 0; b < kCB; ++b) facc[b] = v4f{0.f, 0.f, 0.f, 0.f};
+  const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
+  // One int4 group's products for both column blocks: the weight operands
+  // (two dwords of nibbles each) and the codes.
+  auto group_w4 = [&](int gi, const uint32_t (&d)[kCB][2], const v4i& fa_g) {
+    const int g = g0 + gi;
+    v4i p[kCB];
+#pragma unroll
+    for (int b = 0; b < kCB; ++b) {
+      uint32_t u0, u1, u2, u3;
+      unpack8_u4(d[b][0], u0, u1);
+      unpack8_u4(d[b][1], u2, u3);
+      p[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa_g, v4i{(int)u0, (int)u1, (int)u2, (int)u3},
+                                                   v4i{0, 0, 0, 0}, 0, 0, 0);
+    }
+    if (OUT == kOutI32) {
+      // debug output: P of every group, [G, M, N]; p[b][r] = P[g, 4*fc + r, n]
+#pragma unroll
+      for (int b = 0; b < kCB; ++b) {
+        const int n = n0 + 16 * b + fr;
+        if (n < N && gi < gn) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = 4 * fc + r;
+            if (m < M) reinterpret_cast<int32_t*>(y)[((int64_t)g * Mtot + m0 + m) * N + n] = p[b][r];
+          }
+        }
+      }
+    } else {
+      const v4i as = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa_g, ones, v4i{0, 0, 0, 0}, 0, 0, 0);
+      float asf[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) asf[r] = (float)as[r];
+#pragma unroll
+      for (int b = 0; b < kCB; ++b) {
+        // groups past the slice (the second group of a unit past G): zero
+        // scale and offset, so their products add nothing
+        const uint32_t sb = gi < gn ? lds_sb[g * kC + 16 * b + fr] : 0u;
+        const float s = __half2float(__ushort_as_half((unsigned short)(sb & 0xffff)));
+        const float o = __half2float(__ushort_as_half((unsigned short)(sb >> 16)));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) facc[b][r] = fmaf(o, asf[r], fmaf(s, (float)p[b][r], facc[b][r]));
+      }
+    }
+  };
+
+  // 3. Units in order as they arrive; the unit D ahead reuses the registers
+  //    of the one just finished.
+  for (int u0 = 0; u0 < nu; u0 += D) {  // one pass when all units are in flight
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      const int u = u0 + s;
+      if (u >= nu) break;  // wave-uniform
+      {
+        uint32_t d0[kCB][2], d1[kCB][2];
+#pragma unroll
+        for (int b = 0; b < kCB; ++b) {
+          const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)wr[s][b][0], (uint32_t)wr[s][b][2], false, false);
+          const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)wr[s][b][1], (uint32_t)wr[s][b][3], false, false);
+          d0[b][0] = lo[0];
+          d0[b][1] = hi[0];
+          d1[b][0] = lo[1];
+          d1[b][1] = hi[1];
+        }
+        if constexpr (XQ) {
+          group_w4(2 * u, d0, xq_operand(2 * u));
+          group_w4(2 * u + 1, d1, xq_operand(2 * u + 1));
+        } else {
+          group_w4(2 * u, d0, ar[s][0]);
+          group_w4(2 * u + 1, d1, ar[s][1]);
+        }
+      }
+      if (u + D < NU) issue(u + D, s);
+    }
+  }
+  if (OUT == kOutI32) return;
+
+  // Reduce the 8 partials of each column block (fp32): wavefront b < kCB
+  // finishes column block b.
+#pragma unroll
+  for (int b = 0; b < kCB; ++b) {
+    if (wave == b) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lds_red[wave][b][r][lane] = facc[b][r];
+  }
+  __syncthreads();
+  if (wave >= kCB) return;
+  v4f fs = facc[0];
+#pragma unroll
+  for (int b = 1; b < kCB; ++b)
+    if (wave == b) fs = facc[b];
+  if (XQ) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sxm[r] = s_xscale[min(4 * fc + r, M - 1)];
+  }
+  // slices in order 0..7, the wavefront's own at its place
+  v4f ft = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ft[r] += w == wave ? fs[r] : lds_red[w][eb][r][lane];
+  if (nn >= N) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * fc + r;
+    if (m >= M) continue;
+    const int64_t idx = (int64_t)(m0 + m) * N + nn;
+    {
+      float v = fmaf(sxm[r], ft[r], bv);
+      if (ep.active()) v = gated1(v, ep.residual, ep.gate, ep.gate_rows, m0 + m, nn, N);
+      if (OUT == kOutF32) reinterpret_cast<float*>(y)[idx] = v;
+      else reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)f32_to_bf16_rne(v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA GEMV for int8 weights (M >= 3, or K > kFusedMaxK): 16 rows x 16
+// output columns per workgroup of 8 wavefronts, each owning a K slice.  An
+// int8 group is 64 bytes a column, so the register layout above would read
+// half lines (16 columns x 64 bytes per instruction) twice as often as for
+// int4; here the weights stream through a private LDS chunk per wavefront
+// with direct buffer loads of 8 rows x one full 128-byte line, in the MFMA
+// fragment order, four groups a chunk (measured faster for int8 than the
+// register layout: 17.1 against 19.3 us at 4 x 5120 -> 13824).
+constexpr int kChunk8 = 4;        // groups per LDS chunk of one wavefront
+static_assert(kXqMaxGPW % kChunk8 == 0, "XQ slices are whole chunks");
+
+template <int OUT, bool XQ, bool AF>
+__global__ __launch_bounds__(kWaves * 64) void gemv_lds8_kernel(
+    const int8_t* __restrict__ A, const float* __restrict__ sx,
+    const int8_t* __restrict__ Wq, const float* __restrict__ sw,
+    const float* __restrict__ bias, void* y, int Mtot, int N, int K, Epilogue ep,
+    const uint16_t* __restrict__ X, float* __restrict__ sx_out) {
+  // this workgroup's 16-row block of the activations
+  const int m0 = blockIdx.y * 16;
+  const int M = min(16, Mtot - m0);
+  if (sx != nullptr) sx += m0;
+  constexpr int UB = 64;                    // bytes of one weight row per group
+  constexpr int LPR = UB / 16;              // DMA lanes per (row, group)
+  constexpr int GPB = 128 / UB;             // groups per 128-byte line (one DMA block)
+  constexpr int WLDS = kChunk8 * 16 * UB;   // LDS bytes of one wavefront's chunk
+  static_assert(kChunk8 % GPB == 0, "a chunk is whole DMA blocks");
+  __shared__ __attribute__((aligned(16))) int8_t lds_w[kWaves][WLDS];
+  __shared__ float lds_red[kWaves - 1][4][64];
+  __shared__ float s_xamax[XQ ? kWaves : 1][kGemvXqRows];
+  __shared__ float s_xscale[kGemvXqRows];
+
+  const int G = K / 64;
+  const int n0 = blockIdx.x * 16;
+  const int rows = min(16, N - n0);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // Wave-uniform (readfirstlane): slice guards are scalar branches, the
+  // LDS DMA bases stay scalar and every MFMA runs with the full EXEC mask.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fr = lane & 15;  // MFMA A row m / B column of this lane
+  const int fc = lane >> 4;  // MFMA 16-wide k chunk / output row block
+  const int per = ((G + kWaves - 1) / kWaves + GPB - 1) / GPB * GPB;
+  const int g0 = min(wave * per, G);
+  const int gn = min(per, G - g0);  // 0 for trailing wavefronts of short K
+
+  // Weight DMA.  The descriptor is rebased on row n0 with num_records =
+  // rows*K: rows past N and groups past the matrix end read as zero.  Block
+  // (r8, blk) = rows 8*r8..8*r8+7 x groups blk*GPB.. of the chunk; lane l
+  // moves 16 bytes: group l/(8*LPR), row (l/LPR)%8, piece l%LPR, into LDS
+  // byte 16*l of the block, which puts (row r, chunk group i) at
+  // (r/8)*kChunk8*8*UB + i*8*UB + (r%8)*UB -- the fragment order.
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(Wq + (int64_t)n0 * K), 0, rows * K, 0x00020000);
   const int d_gg = lane / (8 * LPR), d_rr = (lane / LPR) & 7, d_pc = lane % LPR;
-  const int voff = d_rr * RB + d_gg * UB + d_pc * 16;
+  const int voff = d_rr * K + d_gg * UB + d_pc * 16;
   auto issue = [&](int gs, int gc) {
 #pragma unroll
-    for (int blk = 0; blk < kChunk / GPB; ++blk) {
+    for (int blk = 0; blk < kChunk8 / GPB; ++blk) {
       if (blk * GPB < gc) {
 #pragma unroll
         for (int r8 = 0; r8 < 2; ++r8) {
-          lds_ptr_t dst = (lds_ptr_t)(&lds_w[wave][r8 * (kChunk * 8 * UB) + blk * 1024]);
+          lds_ptr_t dst = (lds_ptr_t)(&lds_w[wave][r8 * (kChunk8 * 8 * UB) + blk * 1024]);
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, voff,
-                                                   r8 * 8 * RB + (gs + blk * GPB) * UB, 0, 0);
+                                                   r8 * 8 * K + (gs + blk * GPB) * UB, 0, 0);
         }
       }
     }
   };
-  // 3. Activation fragments of a chunk: A row fr (< M), k chunk fc.
-  v4i fa[kChunk];
-  const int8_t* arow = A + (int64_t)fr * K + fc * 16;
+  // Activation fragments of a chunk: A row fr (< M), k chunk fc; in the
+  // fragment order one contiguous 1 KB per group of the 16-row block.
+  v4i fa[kChunk8];
+  const int8_t* arow = AF ? A + (int64_t)blockIdx.y * G * 1024 + 16 * lane
+                          : A + (int64_t)(m0 + fr) * K + fc * 16;
   auto load_a = [&](int gs, int gc) {
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
+    for (int i = 0; i < kChunk8; ++i) {
       int4 t = make_int4(0, 0, 0, 0);
-      if (i < gc && fr < M) t = *reinterpret_cast<const int4*>(arow + (gs + i) * 64);
+      if (i < gc && (AF || fr < M)) t = *reinterpret_cast<const int4*>(arow + (gs + i) * (AF ? 1024 : 64));
       fa[i] = v4i{t.x, t.y, t.z, t.w};
     }
   };
@@ -164,8 +467,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
       if (gi < gn && xr < Mtot) xq[t] = xrow[(g0 + gi) * 8];
     }
   }
-  issue(g0, min(gn, kChunk));
-  if (!XQ) load_a(g0, min(gn, kChunk));
+  issue(g0, min(gn, kChunk8));
+  if (!XQ) load_a(g0, min(gn, kChunk8));
   if constexpr (XQ) {
     // Row absmax on the bf16 bit patterns (for finite values the magnitude
     // bits order as |x|), over the row's 16 lanes, then the 8 slices.
@@ -184,22 +487,12 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
   const int nn = n0 + fr;
   const int nc = min(nn, N - 1);
   const float bv = bias ? bias[nc] : 0.0f;
-  const float swn = (!W4 && OUT != kOutI32) ? reinterpret_cast<const float*>(gsv)[nc] : 0.0f;
+  const float swn = OUT != kOutI32 ? sw[nc] : 0.0f;
   float sxm[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) sxm[r] = (OUT != kOutI32 && !XQ) ? sx[min(4 * fc + r, M - 1)] : 0.0f;
 
-  if (kScales) {
-#pragma unroll
-    for (int j = 0; j < kSL; ++j) {
-      const int e = tid + j * kWaves * 64;
-      if (e < 16 * G) {
-        const int r = e / G, g = e - r * G;
-        lds_sb[g * 16 + r] = sreg[j];
-      }
-    }
-  }
-  if (kScales || XQ) {
+  if (XQ) {
     wait_vm_lgkm0<63>();  // LDS writes done; the weight DMA may still fly
     barrier_nofence();
   }
@@ -226,40 +519,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
     }
   }
 
-  v4f facc = v4f{0.f, 0.f, 0.f, 0.f};
   v4i iacc = v4i{0, 0, 0, 0};
-  const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
-  const int8_t* wl = &lds_w[wave][(fr >> 3) * (kChunk * 8 * UB) + (fr & 7) * UB + fc * (UB / 4)];
-  // One group's products: weight fragment i of the chunk in LDS, codes fa_g.
-  auto group_product = [&](int i, int g, const v4i& fa_g) {
-    if (W4) {
-      const uint2 wv = *reinterpret_cast<const uint2*>(wl + i * 8 * UB);
-      uint32_t u0, u1, u2, u3;
-      unpack8_u4(wv.x, u0, u1);
-      unpack8_u4(wv.y, u2, u3);
-      const v4i fw = v4i{(int)u0, (int)u1, (int)u2, (int)u3};
-      const v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa_g, fw, v4i{0, 0, 0, 0}, 0, 0, 0);
-      if (OUT == kOutI32) {
-        // debug output: P of every group, [G, M, N]; p[r] = P[g, 4*fc + r, n]
-        if (nn < N) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = 4 * fc + r;
-            if (m < M) reinterpret_cast<int32_t*>(y)[((int64_t)g * Mtot + m0 + m) * N + nn] = p[r];
-          }
-        }
-      } else {
-        const v4i as = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa_g, ones, v4i{0, 0, 0, 0}, 0, 0, 0);
-        const uint32_t sb = lds_sb[g * 16 + fr];
-        const float s = __half2float(__ushort_as_half((unsigned short)(sb & 0xffff)));
-        const float b = __half2float(__ushort_as_half((unsigned short)(sb >> 16)));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) facc[r] = fmaf(b, (float)as[r], fmaf(s, (float)p[r], facc[r]));
-      }
-    } else {
-      const int4 wv = *reinterpret_cast<const int4*>(wl + i * 8 * UB);
-      iacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa_g, v4i{wv.x, wv.y, wv.z, wv.w}, iacc, 0, 0, 0);
-    }
+  const int8_t* wl = &lds_w[wave][(fr >> 3) * (kChunk8 * 8 * UB) + (fr & 7) * UB + fc * (UB / 4)];
+  auto group_product = [&](int i, const v4i& fa_g) {
+    const int4 wv = *reinterpret_cast<const int4*>(wl + i * 8 * UB);
+    iacc = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa_g, v4i{wv.x, wv.y, wv.z, wv.w}, iacc, 0, 0, 0);
   };
   if constexpr (XQ) {
     // Operand of slice group gi: lane fr + 16*fc (rows fr < 4) takes the
@@ -268,15 +532,15 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
     // the register of each load is known.
     const int src0 = 4 * (16 * (fr & 3) + 2 * fc);  // ds_bpermute byte address, gi even
 #pragma unroll
-    for (int c0 = 0; c0 < kXqMaxGPW; c0 += kChunk) {
+    for (int c0 = 0; c0 < kXqMaxGPW; c0 += kChunk8) {
       if (c0 >= gn) break;
-      const int gc = min(kChunk, gn - c0);
+      const int gc = min(kChunk8, gn - c0);
       if (c0 > 0) {
         wait_vm_lgkm0<63>();  // fragment reads of the last chunk done before the DMA reuses it
         issue(g0 + c0, gc);
       }
 #pragma unroll
-      for (int i = 0; i < kChunk; ++i) {
+      for (int i = 0; i < kChunk8; ++i) {
         if (i < gc) {
           const int gi = c0 + i;
           const int sa = src0 + 32 * (gi & 1);
@@ -285,30 +549,28 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
                       __builtin_amdgcn_ds_bpermute(sa + 4, xc[gi >> 1][0]),
                       __builtin_amdgcn_ds_bpermute(sa + 4, xc[gi >> 1][1])};
           if (fr >= kGemvXqRows) f = v4i{0, 0, 0, 0};
-          group_product(i, g0 + gi, f);
+          group_product(i, f);
         }
       }
     }
   } else {
-    for (int c0 = 0; c0 < gn; c0 += kChunk) {
-      const int gc = min(kChunk, gn - c0);
+    for (int c0 = 0; c0 < gn; c0 += kChunk8) {
+      const int gc = min(kChunk8, gn - c0);
       if (c0 > 0) {
         wait_vm_lgkm0<63>();  // fragment reads of the last chunk done before the DMA reuses it
         issue(g0 + c0, gc);
         load_a(g0 + c0, gc);
       }
 #pragma unroll
-      for (int i = 0; i < kChunk; ++i)
-        if (i < gc) group_product(i, g0 + c0 + i, fa[i]);
+      for (int i = 0; i < kChunk8; ++i)
+        if (i < gc) group_product(i, fa[i]);
     }
   }
-  if (W4 && OUT == kOutI32) return;
 
-  // Reduce the 8 partials: fp32 for int4 weights, exact int32 for int8.
+  // Reduce the 8 partials (exact int32).
   if (wave > 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      lds_red[wave - 1][r][lane] = W4 ? facc[r] : __int_as_float(iacc[r]);
+    for (int r = 0; r < 4; ++r) lds_red[wave - 1][r][lane] = __int_as_float(iacc[r]);
   }
   __syncthreads();
   if (wave != 0) return;
@@ -319,10 +581,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
 #pragma unroll
   for (int w = 0; w < kWaves - 1; ++w)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (W4) facc[r] += lds_red[w][r][lane];
-      else iacc[r] += __float_as_int(lds_red[w][r][lane]);
-    }
+    for (int r = 0; r < 4; ++r) iacc[r] += __float_as_int(lds_red[w][r][lane]);
   if (nn >= N) return;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -332,7 +591,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(
     if (OUT == kOutI32) {
       reinterpret_cast<int32_t*>(y)[idx] = iacc[r];
     } else {
-      float v = W4 ? fmaf(sxm[r], facc[r], bv) : fmaf(sxm[r] * swn, (float)iacc[r], bv);
+      float v = fmaf(sxm[r] * swn, (float)iacc[r], bv);
       if (ep.active()) v = gated1(v, ep.residual, ep.gate, ep.gate_rows, m0 + m, nn, N);
       if (OUT == kOutF32) reinterpret_cast<float*>(y)[idx] = v;
       else reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)f32_to_bf16_rne(v);
@@ -971,20 +1230,73 @@ const char* launch_lane8(const uint16_t* x, const int8_t* a, const float* sx, co
   return "gemv_w8a8_lane";
 }
 
-template <bool W4, bool XQ>
-const char* launch_fmt(const int8_t* a, const float* sx, const void* q, const void* gs,
-                       const void* gb, const float* bias, void* y, int out, int M, int N, int K,
-                       hipStream_t s, const Epilogue& ep, const uint16_t* x, float* sx_out) {
-  const dim3 grid((unsigned)((N + 15) / 16), (unsigned)((M + 15) / 16)), block(kWaves * 64);
-  const size_t sb = (W4 && out != kOutI32) ? (size_t)16 * (K / 64) * sizeof(uint32_t) : 0;
+template <int OUT, bool XQ, bool AF, int NU>
+void launch_w4_out(dim3 grid, size_t sb, const int8_t* a, const float* sx, const void* q,
+                   const void* gs, const void* gb, const float* bias, void* y, int M, int N,
+                   int K, hipStream_t s, const Epilogue& ep, const uint16_t* x, float* sx_out) {
+  // Two units in flight ahead of the arithmetic (measured best of 2, 3, 4
+  // and all of them: deeper pipelines cost occupancy).
+  constexpr int D = NU < 2 ? NU : 2;
+  hipLaunchKernelGGL((gemv_w4_kernel<OUT, XQ, AF, NU, D>), grid, dim3(kWaves * 64), sb, s, a, sx,
+                     reinterpret_cast<const uint8_t*>(q), reinterpret_cast<const uint16_t*>(gs),
+                     reinterpret_cast<const uint16_t*>(gb), bias, y, M, N, K, ep, x, sx_out);
+}
+
+template <bool XQ, bool AF, int NU>
+void launch_w4_nu(dim3 grid, size_t sb, const int8_t* a, const float* sx, const void* q,
+                  const void* gs, const void* gb, const float* bias, void* y, int out, int M,
+                  int N, int K, hipStream_t s, const Epilogue& ep, const uint16_t* x,
+                  float* sx_out) {
   if (out == kOutF32)
-    hipLaunchKernelGGL((gemv_kernel<W4, kOutF32, XQ>), grid, block, sb, s, a, sx, q, gs, gb, bias, y, M, N, K, ep, x, sx_out);
+    launch_w4_out<kOutF32, XQ, AF, NU>(grid, sb, a, sx, q, gs, gb, bias, y, M, N, K, s, ep, x, sx_out);
   else if (out == kOutBF16)
-    hipLaunchKernelGGL((gemv_kernel<W4, kOutBF16, XQ>), grid, block, sb, s, a, sx, q, gs, gb, bias, y, M, N, K, ep, x, sx_out);
+    launch_w4_out<kOutBF16, XQ, AF, NU>(grid, sb, a, sx, q, gs, gb, bias, y, M, N, K, s, ep, x, sx_out);
   else
-    hipLaunchKernelGGL((gemv_kernel<W4, kOutI32, XQ>), grid, block, sb, s, a, sx, q, gs, gb, bias, y, M, N, K, ep, x, sx_out);
-  if (XQ) return W4 ? "gemv_xq_w4a8" : "gemv_xq_w8a8";
-  return W4 ? "gemv_w4a8" : "gemv_w8a8";
+    launch_w4_out<kOutI32, XQ, AF, NU>(grid, sb, a, sx, q, gs, gb, bias, y, M, N, K, s, ep, x, sx_out);
+}
+
+template <bool XQ, bool AF>
+const char* launch_w4(const int8_t* a, const float* sx, const void* q, const void* gs,
+                      const void* gb, const float* bias, void* y, int out, int M, int N, int K,
+                      hipStream_t s, const Epilogue& ep, const uint16_t* x, float* sx_out) {
+  const dim3 grid((unsigned)((N + kGemvCols - 1) / kGemvCols), (unsigned)((M + 15) / 16));
+  const size_t sb = out != kOutI32 ? (size_t)kGemvCols * (K / 64) * sizeof(uint32_t) : 0;
+  const int nu = ((K / 64 + kWaves - 1) / kWaves + 1) / 2;  // load units per wavefront
+#define KQ_GEMV_NU(n) \
+  launch_w4_nu<XQ, AF, n>(grid, sb, a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, x, sx_out)
+  if constexpr (XQ) {
+    // K <= kFusedMaxK: at most kXqMaxGPW groups a wavefront
+    static_assert(kXqMaxGPW == 12, "XQ unit counts");
+    if (nu <= 2) KQ_GEMV_NU(2);
+    else if (nu <= 4) KQ_GEMV_NU(4);
+    else KQ_GEMV_NU(6);
+  } else {
+    static_assert(kGemvMaxK / 64 / kWaves <= 32, "unit counts");
+    if (nu <= 2) KQ_GEMV_NU(2);
+    else if (nu <= 4) KQ_GEMV_NU(4);
+    else if (nu <= 6) KQ_GEMV_NU(6);
+    else if (nu <= 8) KQ_GEMV_NU(8);
+    else KQ_GEMV_NU(16);
+  }
+#undef KQ_GEMV_NU
+  return XQ ? "gemv_xq_w4a8" : "gemv_w4a8";
+}
+
+template <bool XQ, bool AF>
+const char* launch_w8(const int8_t* a, const float* sx, const void* q, const void* sw,
+                      const float* bias, void* y, int out, int M, int N, int K, hipStream_t s,
+                      const Epilogue& ep, const uint16_t* x, float* sx_out) {
+  const dim3 grid((unsigned)((N + kGemvCols8 - 1) / kGemvCols8), (unsigned)((M + 15) / 16)),
+      block(kWaves * 64);
+  const int8_t* qw = reinterpret_cast<const int8_t*>(q);
+  const float* swf = reinterpret_cast<const float*>(sw);
+  if (out == kOutF32)
+    hipLaunchKernelGGL((gemv_lds8_kernel<kOutF32, XQ, AF>), grid, block, 0, s, a, sx, qw, swf, bias, y, M, N, K, ep, x, sx_out);
+  else if (out == kOutBF16)
+    hipLaunchKernelGGL((gemv_lds8_kernel<kOutBF16, XQ, AF>), grid, block, 0, s, a, sx, qw, swf, bias, y, M, N, K, ep, x, sx_out);
+  else
+    hipLaunchKernelGGL((gemv_lds8_kernel<kOutI32, XQ, AF>), grid, block, 0, s, a, sx, qw, swf, bias, y, M, N, K, ep, x, sx_out);
+  return XQ ? "gemv_xq_w8a8" : "gemv_w8a8";
 }
 
 }  // namespace
@@ -992,15 +1304,19 @@ const char* launch_fmt(const int8_t* a, const float* sx, const void* q, const vo
 const char* launch_gemv(bool w4, const int8_t* a, const float* sx, const int32_t* /*gsum*/,
                         const void* q, const void* gs, const void* gb, const float* bias,
                         void* y, int out, int M, int N, int K, hipStream_t s,
-                        const Epilogue& ep, const uint16_t* x, float* sx_out, bool lane) {
+                        const Epilogue& ep, const uint16_t* x, float* sx_out, bool lane,
+                        bool frag) {
   if (lane && M <= kGemvLaneRows && K <= kFusedMaxK)
     return w4 ? launch_lane(x, a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, sx_out)
               : launch_lane8(x, a, sx, q, gs, bias, y, out, M, N, K, s, ep, sx_out);
   if (x != nullptr)
-    return w4 ? launch_fmt<true, true>(nullptr, nullptr, q, gs, gb, bias, y, out, M, N, K, s, ep, x, sx_out)
-              : launch_fmt<false, true>(nullptr, nullptr, q, gs, gb, bias, y, out, M, N, K, s, ep, x, sx_out);
-  return w4 ? launch_fmt<true, false>(a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, nullptr, nullptr)
-            : launch_fmt<false, false>(a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, nullptr, nullptr);
+    return w4 ? launch_w4<true, false>(nullptr, nullptr, q, gs, gb, bias, y, out, M, N, K, s, ep, x, sx_out)
+              : launch_w8<true, false>(nullptr, nullptr, q, gs, bias, y, out, M, N, K, s, ep, x, sx_out);
+  if (frag)
+    return w4 ? launch_w4<false, true>(a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, nullptr, nullptr)
+              : launch_w8<false, true>(a, sx, q, gs, bias, y, out, M, N, K, s, ep, nullptr, nullptr);
+  return w4 ? launch_w4<false, false>(a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, nullptr, nullptr)
+            : launch_w8<false, false>(a, sx, q, gs, bias, y, out, M, N, K, s, ep, nullptr, nullptr);
 }
 
 }  // namespace kq

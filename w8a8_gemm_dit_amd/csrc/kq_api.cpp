@@ -114,11 +114,14 @@ const char* dtype_name(kq_dtype d) {
 // Launches the GEMM/GEMV stage of a validated linear on quantized
 // activations (codes, scales and, for int4 weights, group sums).
 // partials: int32 workspace of a split GEMM, or NULL (then K is never split).
+// frag: the codes are in the MFMA GEMV's fragment order (the linears'
+// quantize kernel writes them so when the route takes that kernel).
 kq_status launch_main(const char* op, int force, kq_wformat fmt, const int8_t* codes,
                       const float* sx, const int32_t* gsum, int64_t M, int64_t K, int64_t N,
                       const void* wq, const void* scale, const void* gbias, const float* bias,
                       void* y, kq_dtype y_dtype, hipStream_t s, const char* kq_name,
-                      const kq::Epilogue& ep = kq::Epilogue(), int32_t* partials = nullptr) {
+                      const kq::Epilogue& ep = kq::Epilogue(), int32_t* partials = nullptr,
+                      bool frag = false) {
   const kq_route_info r =
       kq::choose_route(M, N, K, fmt, force, env_tile(), partials ? env_split() : 0, false,
                        env_gemv_lane());
@@ -126,7 +129,8 @@ kq_status launch_main(const char* op, int force, kq_wformat fmt, const int8_t* c
   const char* k2;
   if (r.kind == KQ_ROUTE_GEMV) {
     k2 = kq::launch_gemv(fmt == KQ_W4_AFFINE_G64, codes, sx, gsum, wq, scale, gbias, bias, y, out,
-                         (int)M, (int)N, (int)K, s, ep, nullptr, nullptr, env_gemv_lane());
+                         (int)M, (int)N, (int)K, s, ep, nullptr, nullptr, env_gemv_lane(),
+                         frag && kq::gemv_frag_codes(r));
   } else {
     int tile = 0;
     for (int t = 0; t < kq::kNumTiles; ++t)
@@ -219,13 +223,17 @@ kq_status run_linear(const char* op, int force, kq_wformat fmt, const void* x, i
   int8_t* codes = reinterpret_cast<int8_t*>(wsb + wl.codes_off);
   float* sx = reinterpret_cast<float*>(wsb + wl.scale_off);
   int32_t* gsum = fmt == KQ_W4_AFFINE_G64 ? reinterpret_cast<int32_t*>(wsb + wl.gsum_off) : nullptr;
+  // the MFMA GEMV reads the codes in its fragment order (whole 1 KB
+  // operands per load), every other route row-major
+  const bool frag = kq::gemv_frag_codes(r);
   const char* kq_name = kq::launch_quant_act(reinterpret_cast<const uint16_t*>(x), M, (int)K, codes,
-                                             sx, gsum, s);
+                                             sx, gsum, s,
+                                             frag ? (fmt == KQ_W4_AFFINE_G64 ? 2 : 1) : 0);
   st = check_launch(op);
   if (st != KQ_SUCCESS) return st;
   int32_t* partials = splits > 1 ? reinterpret_cast<int32_t*>(wsb + wl.part_off) : nullptr;
   return launch_main(op, force, fmt, codes, sx, gsum, M, K, N, wq, scale, gbias, bias, y, y_dtype,
-                     s, kq_name, ep, partials);
+                     s, kq_name, ep, partials, frag);
 }
 
 // Shared body of the entry points on pre-quantized activations.

@@ -26,8 +26,11 @@ struct Epilogue {
   __host__ __device__ bool active() const { return residual != nullptr || gate != nullptr; }
 };
 
+// frag: where the codes go: 0 row-major [M][K]; 1 / 2 the MFMA GEMV's
+// fragment order for int8 / int4 weights (kq::gemv_frag_offset, rows
+// rounded up to 16; the padding rows are not written).
 const char* launch_quant_act(const uint16_t* x, int64_t M, int K, int8_t* a, float* sx,
-                             int32_t* gsum, hipStream_t s);
+                             int32_t* gsum, hipStream_t s, int frag = 0);
 const char* launch_quant_w8(const float* w, int64_t N, int K, int8_t* q, float* sw,
                             hipStream_t s);
 const char* launch_quant_w4(const float* w, int64_t N, int K, uint8_t* q4, void* gs, void* gb,
@@ -55,12 +58,13 @@ const char* launch_gemm_w4a8(int tile, const int8_t* a, const float* sx, const i
 // x != NULL: the kernel quantizes the bf16 rows x itself (a, sx unused;
 // M <= kGemvXqRows, K <= kFusedMaxK) and writes the token scales to sx_out.
 // lane: M <= kGemvLaneRows and K <= kFusedMaxK take the lane-per-column
-// kernels (the route's lane flag).
+// kernels (the route's lane flag).  frag: the codes a are in the MFMA
+// GEMV's fragment order (launch_quant_act's frag 1 / 2), else row-major.
 const char* launch_gemv(bool w4, const int8_t* a, const float* sx, const int32_t* gsum,
                         const void* q, const void* gs, const void* gb, const float* bias,
                         void* y, int out, int M, int N, int K, hipStream_t s,
                         const Epilogue& ep = Epilogue(), const uint16_t* x = nullptr,
-                        float* sx_out = nullptr, bool lane = true);
+                        float* sx_out = nullptr, bool lane = true, bool frag = false);
 
 // Thin-N linear with the activation quantization inside (N <= 64, K <=
 // kFusedMaxK): reads bf16 x, writes the token scales to sx (if not NULL)

@@ -109,11 +109,12 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
   // Up to 4 rows the GEMV quantizes x in its prologue (the separate
   // quantize kernel would cost a launch and a round trip for a few rows).
   if (fuse && (force == 0 || force == 3) && M >= 1 && M <= kGemvXqRows && K <= kFusedMaxK) {
+    const int cols = fmt == KQ_W4_AFFINE_G64 ? kGemvCols : kGemvCols8;
     r.kind = KQ_ROUTE_FUSED;
     r.tile_m = kGemvXqRows;
-    r.tile_n = kGemvCols;
+    r.tile_n = cols;
     r.threads = kGemvThreads;
-    r.grid = (N + kGemvCols - 1) / kGemvCols;
+    r.grid = (N + cols - 1) / cols;
     if (lane_gemv) lane_geometry();
     return r;
   }
@@ -140,11 +141,12 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
   const bool thin = N <= kGemvThinN && K <= kGemvMaxK && (M + kGemvRows - 1) / kGemvRows <= 65535;
   const bool gemv = (force >= 2) ? fits : (force == 1) ? false : (M >= 1 && (small || thin));
   if (gemv) {
+    const int cols = fmt == KQ_W4_AFFINE_G64 ? kGemvCols : kGemvCols8;
     r.kind = KQ_ROUTE_GEMV;
     r.tile_m = kGemvRows;
-    r.tile_n = kGemvCols;
+    r.tile_n = cols;
     r.threads = kGemvThreads;
-    r.grid = ((N + kGemvCols - 1) / kGemvCols) * ((M + kGemvRows - 1) / kGemvRows);
+    r.grid = ((N + cols - 1) / cols) * ((M + kGemvRows - 1) / kGemvRows);
     if (lane_gemv) lane_geometry();
     return r;
   }
@@ -254,7 +256,10 @@ WorkspaceLayout workspace_layout(int64_t M, int64_t N, int64_t K, kq_wformat fmt
     return w;
   }
   w.codes_off = off;
-  w.codes_bytes = (size_t)M * (size_t)K;
+  // rows rounded up to the GEMV's 16-row blocks (its fragment order covers
+  // whole blocks; the padding rows are never written and only reach output
+  // rows past M, which are not stored)
+  w.codes_bytes = (size_t)((M + 15) / 16 * 16) * (size_t)K;
   off = align256(off + w.codes_bytes);
   w.scale_off = off;
   w.scale_bytes = 4 * (size_t)M;
@@ -271,6 +276,10 @@ WorkspaceLayout workspace_layout(int64_t M, int64_t N, int64_t K, kq_wformat fmt
   }
   w.total = off;
   return w;
+}
+
+bool gemv_frag_codes(const kq_route_info& r) {
+  return r.kind == KQ_ROUTE_GEMV && r.tile_m == kGemvRows;  // not the lane kernels
 }
 
 }  // namespace kq

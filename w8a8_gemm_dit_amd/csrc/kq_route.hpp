@@ -61,7 +61,7 @@ int split_chunk(int64_t K, int want, int64_t& chunk, int64_t unit = kSplitUnitW8
 // Workspace layout of one linear call (the fused route keeps only the
 // token scales).
 struct WorkspaceLayout {
-  size_t codes_off, codes_bytes;   // int8 [M,K]
+  size_t codes_off, codes_bytes;   // int8 [M rounded up to 16, K]
   size_t scale_off, scale_bytes;   // fp32 [M]
   size_t gsum_off, gsum_bytes;     // int32 [M,K/64] (int4 format only)
   size_t part_off, part_bytes;     // int32 [splits,M,N] (split GEMM only)
@@ -70,6 +70,21 @@ struct WorkspaceLayout {
 WorkspaceLayout workspace_layout(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
                                  int splits = 1, bool fused = false);
 
+// The MFMA GEMV of a linear reads the activation codes in its fragment
+// order (gemv_frag_offset: per 16-row block and group of 64, four k chunks
+// x 16 rows x 16 bytes), which the quantize kernel writes for it; the
+// other routes read them row-major.
+bool gemv_frag_codes(const kq_route_info& r);
+// Byte offset of code (row, k) in the fragment order for int8 (w4 false)
+// or int4 weights: k chunk h = (k%64)/16 of a group sits at slot h for
+// int8 and at the bit-swapped slot ((h&1)<<1 | h>>1) for int4, whose
+// operand pairs its k chunks that way.
+constexpr int64_t gemv_frag_offset(int64_t row, int64_t k, int64_t K, bool w4) {
+  const int64_t G = K / 64, g = k / 64, h = (k % 64) / 16;
+  const int64_t q = w4 ? (((h & 1) << 1) | (h >> 1)) : h;
+  return (((row / 16) * G + g) * 4 + q) * 256 + (row % 16) * 16 + k % 16;
+}
+
 // Split-K policy: the slice count (at most kSplitMax, slices of at least
 // kSplitMinK codes) that minimizes a simple time model of the grid (waves
 // of kSplitCUs workgroups) plus the partial sums' round trip.
@@ -77,10 +92,12 @@ constexpr int kSplitCUs = 256;
 constexpr int kSplitMax = 16;
 constexpr int64_t kSplitMinK = 512;
 
-// GEMV route geometry: 16 output columns per workgroup of 8 wavefronts,
-// which split K; each wavefront holds its K slice of the activations in
-// registers, up to 32 groups of 64, so the GEMV takes K <= 16384.
-constexpr int kGemvCols = 16;
+// GEMV route geometry: 32 output columns (two MFMA column blocks) per
+// workgroup of 8 wavefronts for int4 weights, 16 for int8; the wavefronts
+// split K into slices of up to 32 groups of 64, so the GEMV takes K <=
+// 16384.
+constexpr int kGemvCols = 32;
+constexpr int kGemvCols8 = 16;
 constexpr int kGemvRows = 16;   // activation rows per GEMV workgroup
 constexpr int kGemvThinN = 64;  // N up to this takes the GEMV at any M
 constexpr int kGemvAutoRows = 32;  // the automatic route's GEMV takes M up to this

@@ -22,6 +22,7 @@
 
 #include "kq_common.hpp"
 #include "kq_launch.hpp"
+#include "kq_route.hpp"
 
 namespace kq {
 
@@ -58,7 +59,15 @@ __device__ __forceinline__ int group8_sum(int v) {
 
 // K % 8 == 0 and K <= 512*CH: the row stays in registers (CH chunks of 8
 // values per lane; chunk c = lane + 64*j covers elements 8c..8c+7).
-template <int CH>
+// FR: where the codes go: 0 row-major [M][K]; 1 and 2 the MFMA GEMV's
+// fragment order for int8 and int4 weights (gemv_frag_offset).
+template <int FR>
+__device__ __forceinline__ uint2* code_slot(int8_t* a, int64_t row, int c, int K) {
+  const int64_t off = FR == 0 ? row * (int64_t)K + 8 * c : gemv_frag_offset(row, 8 * c, K, FR == 2);
+  return reinterpret_cast<uint2*>(a + off);
+}
+
+template <int CH, int FR>
 __global__ __launch_bounds__(256) void quant_act_regs(
     const uint16_t* __restrict__ x, int64_t M, int K, int8_t* __restrict__ a,
     float* __restrict__ sx, int32_t* __restrict__ gsum) {
@@ -83,14 +92,13 @@ __global__ __launch_bounds__(256) void quant_act_regs(
   float scale;
   const float inv = row_inv(amax, scale);
   if (lane == 0) sx[row] = scale;
-  uint2* ar = reinterpret_cast<uint2*>(a + row * (int64_t)K);
   const int G = K >> 6;
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
     const int c = lane + 64 * j;
     int s;
     const uint2 codes = quant8(v[j], inv, s);
-    if (c < nch) ar[c] = codes;
+    if (c < nch) *code_slot<FR>(a, row, c, K) = codes;
     if (gsum != nullptr) {
       s = group8_sum(s);
       if ((lane & 7) == 0 && c < nch) gsum[row * G + (c >> 3)] = s;
@@ -106,7 +114,7 @@ __global__ __launch_bounds__(256) void quant_act_regs(
 // per-element operations as quant_act_regs: identical codes and scales.
 constexpr int kWideThreads = 512;
 
-template <int CH>
+template <int CH, int FR>
 __global__ __launch_bounds__(kWideThreads) void quant_act_wide(
     const uint16_t* __restrict__ x, int64_t M, int K, int8_t* __restrict__ a,
     float* __restrict__ sx, int32_t* __restrict__ gsum) {
@@ -134,14 +142,13 @@ __global__ __launch_bounds__(kWideThreads) void quant_act_wide(
   float scale;
   const float inv = row_inv(amax, scale);
   if (tid == 0) sx[row] = scale;
-  uint2* ar = reinterpret_cast<uint2*>(a + row * (int64_t)K);
   const int G = K >> 6;
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
     const int c = tid + kWideThreads * j;
     int s;
     const uint2 codes = quant8(v[j], inv, s);
-    if (c < nch) ar[c] = codes;
+    if (c < nch) *code_slot<FR>(a, row, c, K) = codes;
     if (gsum != nullptr) {
       s = group8_sum(s);
       if ((lane & 7) == 0 && c < nch) gsum[row * G + (c >> 3)] = s;
@@ -150,6 +157,7 @@ __global__ __launch_bounds__(kWideThreads) void quant_act_wide(
 }
 
 // K % 8 == 0, any K: two passes over the row (the second hits the cache).
+template <int FR>
 __global__ __launch_bounds__(256) void quant_act_stream(
     const uint16_t* __restrict__ x, int64_t M, int K, int8_t* __restrict__ a,
     float* __restrict__ sx, int32_t* __restrict__ gsum) {
@@ -164,14 +172,13 @@ __global__ __launch_bounds__(256) void quant_act_stream(
   float scale;
   const float inv = row_inv(amax, scale);
   if (lane == 0) sx[row] = scale;
-  uint2* ar = reinterpret_cast<uint2*>(a + row * (int64_t)K);
   const int G = K >> 6;
   for (int c0 = 0; c0 < nch; c0 += 64) {
     const int c = c0 + lane;
     int s = 0;
     uint2 codes = make_uint2(0, 0);
     if (c < nch) codes = quant8(xr[c], inv, s);
-    if (c < nch) ar[c] = codes;
+    if (c < nch) *code_slot<FR>(a, row, c, K) = codes;
     if (gsum != nullptr) {
       s = group8_sum(s);
       if ((lane & 7) == 0 && c < nch) gsum[row * G + (c >> 3)] = s;
@@ -259,42 +266,45 @@ __global__ __launch_bounds__(256) void quant_w4_groups(const float* __restrict__
   dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
 }
 
-template <int CH>
-void launch_regs(const uint16_t* x, int64_t M, int K, int8_t* a, float* sx, int32_t* gsum,
-                 hipStream_t s, dim3 grid) {
-  hipLaunchKernelGGL(quant_act_regs<CH>, grid, dim3(256), 0, s, x, M, K, a, sx, gsum);
+template <int FR>
+const char* launch_act(const uint16_t* x, int64_t M, int K, int8_t* a, float* sx, int32_t* gsum,
+                       hipStream_t s) {
+  const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock));
+  // Few rows: a workgroup per row (measured: 16 rows of 5120, one
+  // wavefront per row took 4.7 us, latency-bound).
+  const int wide = (K / 8 + kWideThreads - 1) / kWideThreads;  // chunks per lane
+  if (M <= kWideMaxRows && K >= 1024 && wide <= 4) {
+    const dim3 g1((unsigned)M), b1(kWideThreads);
+    if (wide <= 1) { hipLaunchKernelGGL((quant_act_wide<1, FR>), g1, b1, 0, s, x, M, K, a, sx, gsum); return "quant_act_wide1"; }
+    if (wide <= 2) { hipLaunchKernelGGL((quant_act_wide<2, FR>), g1, b1, 0, s, x, M, K, a, sx, gsum); return "quant_act_wide2"; }
+    hipLaunchKernelGGL((quant_act_wide<4, FR>), g1, b1, 0, s, x, M, K, a, sx, gsum);
+    return "quant_act_wide4";
+  }
+  const int need = (K / 8 + 63) / 64;  // chunks per lane
+  const dim3 b(256);
+#define KQ_REGS(ch)                                                                   \
+  if (need <= ch) {                                                                   \
+    hipLaunchKernelGGL((quant_act_regs<ch, FR>), grid, b, 0, s, x, M, K, a, sx, gsum); \
+    return "quant_act_regs" #ch;                                                      \
+  }
+  KQ_REGS(1) KQ_REGS(2) KQ_REGS(4) KQ_REGS(6) KQ_REGS(8) KQ_REGS(12) KQ_REGS(16) KQ_REGS(24)
+#undef KQ_REGS
+  hipLaunchKernelGGL((quant_act_stream<FR>), grid, b, 0, s, x, M, K, a, sx, gsum);
+  return "quant_act_stream";
 }
 
 }  // namespace
 
 const char* launch_quant_act(const uint16_t* x, int64_t M, int K, int8_t* a, float* sx,
-                             int32_t* gsum, hipStream_t s) {
-  const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock));
+                             int32_t* gsum, hipStream_t s, int frag) {
   if (K % 8 != 0) {
+    const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock));
     hipLaunchKernelGGL(quant_act_scalar, grid, dim3(256), 0, s, x, M, K, a, sx);
     return "quant_act_scalar";
   }
-  // Few rows: a workgroup per row (measured: 16 rows of 5120, one
-  // wavefront per row took 4.7 us, latency-bound).
-  const int wide = (K / 8 + kWideThreads - 1) / kWideThreads;  // chunks per lane
-  if (M <= kWideMaxRows && K >= 1024 && wide <= 4) {
-    const dim3 g1((unsigned)M);
-    if (wide <= 1) { hipLaunchKernelGGL(quant_act_wide<1>, g1, dim3(kWideThreads), 0, s, x, M, K, a, sx, gsum); return "quant_act_wide1"; }
-    if (wide <= 2) { hipLaunchKernelGGL(quant_act_wide<2>, g1, dim3(kWideThreads), 0, s, x, M, K, a, sx, gsum); return "quant_act_wide2"; }
-    hipLaunchKernelGGL(quant_act_wide<4>, g1, dim3(kWideThreads), 0, s, x, M, K, a, sx, gsum);
-    return "quant_act_wide4";
-  }
-  const int need = (K / 8 + 63) / 64;  // chunks per lane
-  if (need <= 1) { launch_regs<1>(x, M, K, a, sx, gsum, s, grid); return "quant_act_regs1"; }
-  if (need <= 2) { launch_regs<2>(x, M, K, a, sx, gsum, s, grid); return "quant_act_regs2"; }
-  if (need <= 4) { launch_regs<4>(x, M, K, a, sx, gsum, s, grid); return "quant_act_regs4"; }
-  if (need <= 6) { launch_regs<6>(x, M, K, a, sx, gsum, s, grid); return "quant_act_regs6"; }
-  if (need <= 8) { launch_regs<8>(x, M, K, a, sx, gsum, s, grid); return "quant_act_regs8"; }
-  if (need <= 12) { launch_regs<12>(x, M, K, a, sx, gsum, s, grid); return "quant_act_regs12"; }
-  if (need <= 16) { launch_regs<16>(x, M, K, a, sx, gsum, s, grid); return "quant_act_regs16"; }
-  if (need <= 24) { launch_regs<24>(x, M, K, a, sx, gsum, s, grid); return "quant_act_regs24"; }
-  hipLaunchKernelGGL(quant_act_stream, grid, dim3(256), 0, s, x, M, K, a, sx, gsum);
-  return "quant_act_stream";
+  if (frag == 1) return launch_act<1>(x, M, K, a, sx, gsum, s);
+  if (frag == 2) return launch_act<2>(x, M, K, a, sx, gsum, s);
+  return launch_act<0>(x, M, K, a, sx, gsum, s);
 }
 
 const char* launch_quant_w8(const float* w, int64_t N, int K, int8_t* q, float* sw,
