@@ -151,7 +151,9 @@ const char* kq_last_error(void);
  * needs (MLX pull request 4722 stages a quantized matmul through int8
  * activations, "quantize_x", before the integer product; here that stage's
  * output lives in this caller-owned workspace): int8 activation codes
- * (M*K), fp32 token scales (4*M), for the int4
+ * (M rounded up to 16, times K: where the route takes the MFMA GEMV the
+ * codes are stored in its 16-row fragment order), fp32 token scales
+ * (4*M), for the int4
  * format the per-group code sums (4*M*K/64), and when the route splits K
  * (kq_route_info.splits > 1) the int32 partial sums (4*splits*M*N), each
  * region 256-byte aligned.  The fused routes (KQ_ROUTE_FUSED) store no
