@@ -103,7 +103,9 @@ __device__ __forceinline__ int pair_slot(int row, int chunk, int h) {
 // (sched_group_barrier mask bits: 0x008 MFMA, 0x100 DS read, 0x020 VMEM).
 template <int NM, int ND, int NV>
 __device__ __forceinline__ void interleave_step() {
-  if constexpr (NV == 0) {
+  if constexpr (ND == 0 && NV == 0) {
+    // MFMAs only: nothing to interleave
+  } else if constexpr (NV == 0) {
     constexpr int a = NM / ND;
 #pragma unroll
     for (int g = 0; g < ND; ++g) {
@@ -145,10 +147,12 @@ __device__ __forceinline__ void store4(void* y, int64_t idx, const float v[4], c
   }
 }
 
-// The K loop is unrolled by 4 steps (two pair buffers).  REM: K/64 is not a
-// multiple of 4, so guarded tail steps follow the loop; the conditional
-// tail makes the register allocator copy accumulators at the loop back-edge,
-// so it is compiled only into the variant that needs it.
+// The K loop is unrolled by 4 steps (two pair buffers); where K/64 is a
+// multiple of 4 the last group issues no refills (its pairs are all
+// loaded), so nothing is in flight when the epilogue starts.  REM: K/64 is
+// not a multiple of 4, so guarded tail steps follow the loop; the
+// conditional tail makes the register allocator copy accumulators at the
+// loop back-edge, so it is compiled only into the variant that needs it.
 // GATED: the output goes through the gated residual epilogue (kq::Epilogue).
 // Split K: workgroup row blockIdx.y takes codes [y*kchunk, min(K, (y+1)*
 // kchunk)) of every row (K stays the row stride) and, with OUT == I32,
@@ -164,6 +168,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
   // so the compiler's tracking of the asynchronous LDS writes never couples
   // reads of one buffer to loads landing in the other.
   __shared__ int4 lds0[C::kPairSlots], lds1[C::kPairSlots];
+  // bf16 output: the staged epilogue's operands (token scales of the BM
+  // rows, then channel scales and biases of the BN columns), moved into
+  // LDS by DMA ahead of the first pair, so the epilogue waits for no load.
+  constexpr bool kEops = OUT == kOutBF16;
+  constexpr int kEU = (BM + 2 * BN) / 64;           // 64-float DMA units
+  constexpr int kEH = (kEU + C::kWaves - 1) / C::kWaves;  // units per wave
+  static_assert(!kEops || (BM + 2 * BN) % 64 == 0, "whole epilogue operand units");
+  __shared__ __attribute__((aligned(16))) float eops[kEops ? BM + 2 * BN : 1];
 
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
@@ -290,43 +302,76 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
   // odd step is the only one that can still be in flight at the next (even)
   // step's wait; at an odd step the next step lies in the buffer refilled
   // two steps earlier, so nothing may be outstanding.
+  // LAST: a step of the last group (no refill; at the last step no reads).
   auto step = [&](Frags& cur, Frags& nxt, int4* cur_buf, const int4* nxt_slot, int kt,
-                  auto odd_tag) {
+                  auto odd_tag, auto last_tag, auto final_tag) {
     constexpr bool kOdd = decltype(odd_tag)::value;
+    constexpr bool kRefill = kOdd && !decltype(last_tag)::value;
+    constexpr bool kReads = !decltype(final_tag)::value;
     __builtin_amdgcn_sched_barrier(0);
     wait_vm_lgkm0<kOdd ? 0 : C::kLPW>();
     barrier_nofence();
-    read_frags(nxt, nxt_slot);
-    if (kOdd) issue(cur_buf, (kt + 3) >> 1);
+    if (kReads) read_frags(nxt, nxt_slot);
+    if (kRefill) issue(cur_buf, (kt + 3) >> 1);
     mfmas(cur);
-    interleave_step<C::kTM * C::kTN, C::kTM + C::kTN, kOdd ? C::kLPW : 0>();
+    interleave_step<C::kTM * C::kTN, kReads ? C::kTM + C::kTN : 0, kRefill ? C::kLPW : 0>();
   };
   using Even = std::integral_constant<bool, false>;
   using Odd = std::integral_constant<bool, true>;
   // step j of an unrolled group of 4: buffer, next step's slot, parity
-#define KQ_STEP(j)                                                                       \
+#define KQ_STEPX(j, LAST)                                                                \
   step((j) % 2 ? f1 : f0, (j) % 2 ? f0 : f1, (j) < 2 ? lds0 : lds1,                     \
        (j) == 0 ? lds0 + 32 : (j) == 1 ? lds1 : (j) == 2 ? lds1 + 32 : lds0, kt + (j),    \
-       std::conditional_t<(j) % 2 == 1, Odd, Even>{})
+       std::conditional_t<(j) % 2 == 1, Odd, Even>{}, std::integral_constant<bool, LAST>{}, \
+       std::integral_constant<bool, LAST && (j) == 3>{})
+#define KQ_STEP(j) KQ_STEPX(j, false)
+#define KQ_LAST(j) KQ_STEPX(j, true)
 
   Frags f0, f1;
+  if (kEops && staged) {
+    // every wave moves units wave + h*kWaves (a unit past kEU repeats the
+    // last one, writing the same values again); a missing bias reads as
+    // zero.  Issued first, so the waits for the first pairs cover them.
+#pragma unroll
+    for (int h = 0; h < kEH; ++h) {
+      const int u = min(wave + h * C::kWaves, kEU - 1);
+      const bool is_sx = u < BM / 64, is_sw = !is_sx && u < (BM + BN) / 64;
+      const float* base = is_sx ? sx + m0 : is_sw ? sw + n0 : (bias ? bias + n0 : sw);
+      const int valid = is_sx ? BM : bias || is_sw ? BN : 0;
+      const int first = 64 * (is_sx ? u : is_sw ? u - BM / 64 : u - (BM + BN) / 64);
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(base), 0, valid * 4, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)&eops[64 * u], 4, lane * 4,
+                                               first * 4, 0, 0);
+    }
+  }
   issue(lds0, 0);
   issue(lds1, 1);
   wait_vm_lgkm0<C::kLPW>();
   barrier_nofence();
   read_frags(f0, lds0);
   int kt = 0;
-  for (; kt + 4 <= KT; kt += 4) {
-    KQ_STEP(0); KQ_STEP(1); KQ_STEP(2); KQ_STEP(3);
-  }
-  if (REM) {  // the K steps beyond a multiple of 4
+  if constexpr (!REM) {
+    for (; kt + 4 < KT; kt += 4) {
+      KQ_STEP(0); KQ_STEP(1); KQ_STEP(2); KQ_STEP(3);
+    }
+    // the last group: its pairs are in the buffers, so no refills (and no
+    // reads for a step past the end)
+    KQ_LAST(0); KQ_LAST(1); KQ_LAST(2); KQ_LAST(3);
+  } else {
+    for (; kt + 4 <= KT; kt += 4) {
+      KQ_STEP(0); KQ_STEP(1); KQ_STEP(2); KQ_STEP(3);
+    }
+    // the K steps beyond a multiple of 4
     if (kt < KT) KQ_STEP(0);
     if (kt + 1 < KT) KQ_STEP(1);
     if (kt + 2 < KT) KQ_STEP(2);
   }
 #undef KQ_STEP
+#undef KQ_LAST
+#undef KQ_STEPX
   __builtin_amdgcn_sched_barrier(0);
-  wait_vm_lgkm0<0>();  // drain the dead loads before the workgroup exits
+  wait_vm_lgkm0<0>();  // drain the dead loads of a tail before the workgroup exits
 
   // Epilogue: lane holds D[n = nb + 4*(lane/16) + r][m = mb + lane%16].
   // bf16 output of a full tile goes through LDS: each wavefront writes its
@@ -338,22 +383,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
     const int sidx = wave / kPerSlot;
     char* stage = reinterpret_cast<char*>(sidx == 0 ? lds0 : lds1) +
                   (wave % kPerSlot) * kStage;
+    // token scales, channel scales and biases: in LDS since the first pair
     float s_m[C::kTM];
 #pragma unroll
-    for (int j = 0; j < C::kTM; ++j) s_m[j] = sx[m0 + wm * C::kWTM + j * 16 + fr];
-    // Channel scales and biases of every column group, loaded together up
-    // front (loaded per group, each group was waited for before the next
-    // one issued).  sw and bias are only 4-byte aligned by contract: scalar
-    // loads.
-    float4 swq[C::kTN], bq[C::kTN];
-#pragma unroll
-    for (int i = 0; i < C::kTN; ++i) {
-      const int n = n0 + wn * C::kWTN + i * 16 + fc * 4;
-      swq[i] = make_float4(sw[n], sw[n + 1], sw[n + 2], sw[n + 3]);
-      bq[i] = bias ? make_float4(bias[n], bias[n + 1], bias[n + 2], bias[n + 3])
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    asm volatile("" ::: "memory");  // (the compiler would sink them back to their uses)
+    for (int j = 0; j < C::kTM; ++j) s_m[j] = eops[wm * C::kWTM + j * 16 + fr];
+    // (channel scales and biases are read per column group below)
     // Gated: the residual block goes into the stage at the places its
     // outputs take (each lane then reads its 4 values where it writes the
     // result); a tile whose rows share one gate row reads that row once per
@@ -379,8 +413,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
         const float* gr = ep.gate + (int64_t)(m0 / ep.gate_rows) * N + n;
         g4[0] = gr[0]; g4[1] = gr[1]; g4[2] = gr[2]; g4[3] = gr[3];
       }
-      const float4 swv = swq[i];
-      const float4 bv = bq[i];
+      const int ce = wn * C::kWTN + i * 16 + fc * 4;
+      const float4 swv = *reinterpret_cast<const float4*>(eops + BM + ce);
+      const float4 bv = *reinterpret_cast<const float4*>(eops + BM + BN + ce);
       const int c = 2 * i + (fc >> 1);  // 16-byte chunk of the block row
 #pragma unroll
       for (int j = 0; j < C::kTM; ++j) {
