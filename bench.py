@@ -202,6 +202,11 @@ class Prepared:
         b0 = dev(synth.bias(wl, seed))
         fmt = kq.KQ_W8_PER_CHANNEL if wl.fmt == "w8" else kq.KQ_W4_AFFINE_G64
         self.fmt = fmt
+        # int4 weights on the tiled GEMM: the linear hands that kernel its
+        # codes in the split order, so the kernel-only leg does the same
+        self.order = (kq.KQ_CODES_SPLIT8 if fmt == kq.KQ_W4_AFFINE_G64
+                      and kq.kq_route(wl.M, wl.N, wl.K, fmt)["kind"] == "gemm"
+                      else kq.KQ_CODES_NATURAL)
         wq, sc, gb = kq.kq_quantize_weights(wd, fmt)
         del wd
         ws_bytes = kq.kq_workspace_bytes(wl.M, wl.N, wl.K, fmt)  # any route of the shape
@@ -220,7 +225,8 @@ class Prepared:
                 "y": torch.empty((wl.M, wl.N), dtype=self.out_dtype, device="cuda"),
                 "ws": torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device="cuda"),
             }
-            a, sx, gs = kq.kq_quantize_act(c["x"], group_sums=(fmt == kq.KQ_W4_AFFINE_G64))
+            a, sx, gs = kq.kq_quantize_act_ordered(c["x"], self.order,
+                                                   group_sums=(fmt == kq.KQ_W4_AFFINE_G64))
             c.update(a=a, sx=sx, gs=gs)
             self.copies.append(c)
         torch.cuda.synchronize()
@@ -238,8 +244,8 @@ class Prepared:
     def quant(self, i: int) -> None:
         """The activation quantize kernel alone (into the copy's codes)."""
         c = self.copies[i % self.R]
-        self.kq.kq_quantize_act(c["x"], out=(c["a"], c["sx"], c["gs"]),
-                                group_sums=c["gs"] is not None)
+        self.kq.kq_quantize_act_ordered(c["x"], self.order, out=(c["a"], c["sx"], c["gs"]),
+                                        group_sums=c["gs"] is not None)
 
     def add_gate(self, gate_rows: int, seed: int = 0) -> None:
         """fp32 gates [ceil(M/gate_rows), N] for the gated residual calls."""
@@ -264,8 +270,8 @@ class Prepared:
             kq.kq_w8a8_gemm(c["a"], c["sx"], c["wq"], c["sc"], c["b"], out_dtype=self.out_dtype,
                             out=c["y"])
         else:
-            kq.kq_w4a8_gemm(c["a"], c["sx"], c["gs"], c["wq"], c["sc"], c["gb"], c["b"],
-                            out_dtype=self.out_dtype, out=c["y"])
+            kq.kq_w4a8_gemm_ordered(c["a"], c["sx"], c["gs"], c["wq"], c["sc"], c["gb"],
+                                    self.order, c["b"], out_dtype=self.out_dtype, out=c["y"])
 
     def output_hash(self) -> str:
         """sha256 of copy 0's output after one call."""

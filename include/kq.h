@@ -85,6 +85,18 @@ typedef enum kq_wformat {
     KQ_W4_AFFINE_G64 = 1
 } kq_wformat;
 
+/* Order of the activation codes within a row, for the entry points that
+ * hand codes over (kq_quantize_act_ordered, kq_w4a8_gemm_ordered). */
+typedef enum kq_code_order {
+    KQ_CODES_NATURAL = 0, /* a[m,k] at byte m*K + k */
+    /* each run of 8 codes k = 8j..8j+7 of a row stored as its even codes,
+     * then its odd ones: bytes m*K + 8j + (0..7) hold k = 8j + {0, 2, 4, 6,
+     * 1, 3, 5, 7}.  The order in which the int4 GEMM unpacks a packed
+     * weight dword (low nibbles = even k, high nibbles = odd k), so its
+     * weights need no reordering; K % 8 == 0. */
+    KQ_CODES_SPLIT8 = 1
+} kq_code_order;
+
 typedef enum kq_dtype {
     KQ_DTYPE_F32 = 0,  /* fp32 output, rounded once from the exact result */
     KQ_DTYPE_BF16 = 1, /* bf16 output: the fp32 result rounded to nearest even */
@@ -270,6 +282,30 @@ kq_status kq_w4a8_gemm(const int8_t* a, const float* sx, const int32_t* gsum,
                        const void* gscale, const void* gbias,
                        const float* bias, void* y, kq_dtype y_dtype,
                        void* stream);
+
+/* The same per-token quantization and int4 linear with the codes in a
+ * chosen order ([qlip] w4a8_linear bullet: activations quantized once feed
+ * the in-register int4 unpack; kq_code_order).  kq_quantize_act_ordered
+ * with KQ_CODES_NATURAL is kq_quantize_act; with KQ_CODES_SPLIT8 it writes
+ * the same codes, scales and group sums, the codes of each run of 8 in the
+ * split order (K % 8 == 0, else KQ_ERR_UNSUPPORTED).
+ * kq_w4a8_gemm_ordered reads codes in `order`: KQ_CODES_NATURAL is
+ * kq_w4a8_gemm; KQ_CODES_SPLIT8 always takes the tiled int4 GEMM (the
+ * kernel kq_w4a8_linear uses there: its weights then need no reordering),
+ * for any M, with results identical to kq_w4a8_gemm on the natural codes
+ * (the int32 group products are the same sums); KQ_FORCE_ROUTE=gemv with
+ * split codes is KQ_ERR_UNSUPPORTED.  Other arguments as kq_quantize_act /
+ * kq_w4a8_gemm; an unknown order is KQ_ERR_INVALID_VALUE. */
+kq_status kq_quantize_act_ordered(const void* x, int64_t M, int64_t K,
+                                  int8_t* a, float* sx, int32_t* gsum,
+                                  kq_code_order order, void* stream);
+
+kq_status kq_w4a8_gemm_ordered(const int8_t* a, const float* sx,
+                               const int32_t* gsum, int64_t M, int64_t K,
+                               int64_t N, const uint8_t* wq4,
+                               const void* gscale, const void* gbias,
+                               const float* bias, void* y, kq_dtype y_dtype,
+                               kq_code_order order, void* stream);
 
 /* Small-M GEMV ([qlip] w4a8_linear bullet: a register-dequant GEMV path for
  * M <= 16 runs decode-style calls at weight-bandwidth speed).  Same math and

@@ -24,7 +24,7 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     L = kq.lib()
     declared = _declared_functions()
-    assert len(declared) == 19, declared
+    assert len(declared) == 21, declared
     assert sorted(kq.exported_symbols) == declared
     for name in declared:
         assert hasattr(L, name), name
@@ -245,6 +245,22 @@ def test_linear_validation_without_device():
     st = L.kq_gemv_small_m(kq.KQ_W8_PER_CHANNEL, P(16), 4, 128, 64, P(32), P(48), P(64), None,
                            P(80), kq.KQ_DTYPE_BF16, P(96), 1 << 30, None)
     assert st == kq.KQ_ERR_INVALID_VALUE and "gbias must be NULL" in kq.kq_last_error()
+
+
+def test_code_order_validation_without_device(monkeypatch):
+    L = kq.lib()
+    st = L.kq_quantize_act_ordered(P(16), 4, 128, P(32), P(48), None, 7, None)
+    assert st == kq.KQ_ERR_INVALID_VALUE and "unknown code order 7" in kq.kq_last_error()
+    st = L.kq_quantize_act_ordered(P(16), 4, 100, P(32), P(48), None, kq.KQ_CODES_SPLIT8, None)
+    assert st == kq.KQ_ERR_UNSUPPORTED and "needs K % 8 == 0" in kq.kq_last_error()
+    st = L.kq_quantize_act_ordered(P(16), 0, 104, P(32), P(48), None, kq.KQ_CODES_SPLIT8, None)
+    assert st == kq.KQ_SUCCESS  # empty: nothing enqueued
+    args = (P(16), P(32), P(48), 4, 128, 64, P(64), P(80), P(96), None, P(112), kq.KQ_DTYPE_BF16)
+    assert L.kq_w4a8_gemm_ordered(*args, 9, None) == kq.KQ_ERR_INVALID_VALUE
+    assert "unknown code order 9" in kq.kq_last_error()
+    monkeypatch.setenv("KQ_FORCE_ROUTE", "gemv")
+    assert L.kq_w4a8_gemm_ordered(*args, kq.KQ_CODES_SPLIT8, None) == kq.KQ_ERR_UNSUPPORTED
+    assert "natural-order codes" in kq.kq_last_error()
 
 
 def _gated(fmt=kq.KQ_W8_PER_CHANNEL, M=64, K=128, N=64, gbias=None, residual=None, gate=None,

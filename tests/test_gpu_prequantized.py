@@ -102,3 +102,83 @@ def test_prequantized_errors():
         kq.kq_w8a8_gemm(torch.zeros((4, 100), dtype=torch.int8, device="cuda"),
                         torch.ones((4,), dtype=torch.float32, device="cuda"),
                         torch.zeros((16, 100), dtype=torch.int8, device="cuda"), sw)
+
+
+# ------------------------------------------------------- split code order
+# KQ_CODES_SPLIT8: bytes 8j + i of a row hold the code of k = 8j + SPLIT8[i]
+SPLIT8 = np.array([0, 2, 4, 6, 1, 3, 5, 7])
+
+
+def _split8(a):
+    M, K = a.shape
+    return a.reshape(M, K // 8, 8)[:, :, SPLIT8].reshape(M, K)
+
+
+def test_split8_permutation_is_the_header_one():
+    # the natural codes 0..15 of one row come out as 0 2 4 6 1 3 5 7 8 10 ...
+    assert _split8(np.arange(16).reshape(1, 16)).tolist() == [
+        [0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15]]
+
+
+@pytest.mark.parametrize("M,K", [(1, 64), (7, 520), (16, 5120), (300, 4096), (64, 12288),
+                                 (3, 24)])
+def test_quantize_act_split_order(M, K):
+    """Split-order codes are the natural codes permuted within each run of 8;
+    scales and group sums are unchanged, bit for bit."""
+    print(f"[prequant] split quantize {M}x{K}", flush=True)
+    xb = synth.random_bf16((M, K), seed=M * 7 + K, dist="student_t4")
+    a_ref, s_ref, g_ref = oracle.quantize_act(xb)
+    sums = K % 64 == 0
+    a, sx, gs = kq.kq_quantize_act_ordered(dev_bf16(xb), kq.KQ_CODES_SPLIT8, group_sums=sums)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(a), _split8(a_ref))
+    assert np.array_equal(host(sx).view(np.uint32), s_ref.view(np.uint32))
+    if sums:
+        assert np.array_equal(host(gs), g_ref)
+
+
+@pytest.mark.parametrize("tile", [None, "128x256", "128x128", "64x128"])
+@pytest.mark.parametrize("M,K,N", [(1, 512, 200), (16, 512, 200), (257, 320, 129),
+                                   (130, 2048, 200), (96, 2112, 272), (128, 12288, 256)])
+def test_w4a8_gemm_split_order(M, K, N, tile, kq_env):
+    """The int4 GEMM on split-order codes: per-group products bit-exact
+    against the oracle, outputs bit-identical to the same tile on the
+    natural codes and within the oracle's bars."""
+    kq_env(KQ_FORCE_ROUTE="gemm", KQ_TILE=tile, KQ_SPLIT=None, KQ_FUSE=None)
+    print(f"[prequant] split w4 gemm {M}x{K}x{N} tile {tile}", flush=True)
+    xb, w, b = _operands(M, K, N, seed=3 * M + K + 5 * N)
+    p, gs, gb, q = oracle.quantize_w4(w)
+    x = dev_bf16(xb)
+    an, sx, gsum = kq.kq_quantize_act(x, group_sums=True)
+    asp, sx2, gsum2 = kq.kq_quantize_act_ordered(x, kq.KQ_CODES_SPLIT8, group_sums=True)
+    W = (dev(p), dev(gs), dev(gb))
+    S = kq.KQ_CODES_SPLIT8
+    P = kq.kq_w4a8_gemm_ordered(asp, sx2, gsum2, *W, S, out_dtype=torch.int32)
+    yf = kq.kq_w4a8_gemm_ordered(asp, sx2, gsum2, *W, S, dev(b), out_dtype=torch.float32)
+    yb = kq.kq_w4a8_gemm_ordered(asp, sx2, gsum2, *W, S, dev(b), out_dtype=torch.bfloat16)
+    nf = kq.kq_w4a8_gemm(an, sx, gsum, *W, dev(b), out_dtype=torch.float32)
+    nb = kq.kq_w4a8_gemm(an, sx, gsum, *W, dev(b), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    a_ref, _, _ = oracle.quantize_act(xb)
+    assert np.array_equal(host(P), oracle.w4a8_group_acc(a_ref, q))
+    assert np.array_equal(host(yf).view(np.uint32), host(nf).view(np.uint32))
+    assert np.array_equal(host_bf16_bits(yb), host_bf16_bits(nb))
+    y64 = oracle.w4a8_linear_exact(xb, q, gs, gb, b)
+    T = oracle.w4a8_magnitude(xb, q, gs, gb, b)
+    check_f32(host(yf), y64, T, f"split w4 gemm {M}x{K}x{N}")
+    check_bf16(host_bf16_bits(yb), y64, T, f"split w4 gemm {M}x{K}x{N}")
+
+
+def test_split_order_small_m_takes_the_gemm(kq_env):
+    """Without a forced route, split-order codes at M <= 16 (where natural
+    codes take the GEMV) still go through the tiled GEMM."""
+    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_SPLIT=None, KQ_FUSE=None)
+    M, K, N = 4, 1024, 96
+    xb, w, b = _operands(M, K, N, seed=77)
+    p, gs, gb, q = oracle.quantize_w4(w)
+    asp, sx, gsum = kq.kq_quantize_act_ordered(dev_bf16(xb), kq.KQ_CODES_SPLIT8, group_sums=True)
+    P = kq.kq_w4a8_gemm_ordered(asp, sx, gsum, dev(p), dev(gs), dev(gb), kq.KQ_CODES_SPLIT8,
+                                out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    a_ref, _, _ = oracle.quantize_act(xb)
+    assert np.array_equal(host(P), oracle.w4a8_group_acc(a_ref, q))

@@ -24,7 +24,8 @@ __all__ = [
     "kq_gemv_small_m", "kq_w8a8_gemm", "kq_w4a8_gemm", "kq_linear_gated", "KqError",
     "KQ_LAYOUT_BHLD", "KQ_LAYOUT_BLHD", "kq_sage_workspace_layout", "kq_sage_prepare",
     "kq_sage_attend", "kq_sage_attention", "kq_probe_read", "kq_probe_mfma_i8",
-    "kq_w8a8_linear_noalloc", "KQ_NOALLOC_SCRATCH_BYTES",
+    "kq_w8a8_linear_noalloc", "KQ_NOALLOC_SCRATCH_BYTES", "KQ_CODES_NATURAL",
+    "KQ_CODES_SPLIT8", "kq_quantize_act_ordered", "kq_w4a8_gemm_ordered",
 ]
 
 KQ_SUCCESS, KQ_ERR_INVALID_VALUE, KQ_ERR_UNSUPPORTED = 0, 1, 2
@@ -38,6 +39,7 @@ KQ_GEMV_MAX_M = 16
 KQ_GEMV_MAX_K = 16384
 KQ_LAYOUT_BHLD, KQ_LAYOUT_BLHD = 0, 1
 KQ_NOALLOC_SCRATCH_BYTES = 64 << 20
+KQ_CODES_NATURAL, KQ_CODES_SPLIT8 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkq.so")
@@ -49,6 +51,7 @@ exported_symbols = (
     "kq_w4a8_linear", "kq_gemv_small_m", "kq_w8a8_gemm", "kq_w4a8_gemm",
     "kq_linear_gated", "kq_sage_workspace_layout", "kq_sage_prepare", "kq_sage_attend",
     "kq_sage_attention", "kq_probe_read", "kq_probe_mfma_i8", "kq_w8a8_linear_noalloc",
+    "kq_quantize_act_ordered", "kq_w4a8_gemm_ordered",
 )
 
 
@@ -105,6 +108,10 @@ def lib() -> ctypes.CDLL:
     L.kq_w8a8_gemm.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, i32, vp]
     L.kq_w4a8_gemm.restype = i32
     L.kq_w4a8_gemm.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp]
+    L.kq_quantize_act_ordered.restype = i32
+    L.kq_quantize_act_ordered.argtypes = [vp, i64, i64, vp, vp, vp, i32, vp]
+    L.kq_w4a8_gemm_ordered.restype = i32
+    L.kq_w4a8_gemm_ordered.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, i32, i32, vp]
     L.kq_gemv_small_m.restype = i32
     L.kq_gemv_small_m.argtypes = [i32, vp, i64, i64, i64, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     L.kq_sage_workspace_layout.restype = i32
@@ -212,6 +219,16 @@ def kq_quantize_act(x: torch.Tensor, group_sums: bool = False, out=None):
     """bf16 [M,K] -> (codes int8 [M,K], scales fp32 [M], group sums int32
     [M,K/64] or None).  out: optional (codes, scales, group sums or None)
     tensors to write into."""
+    return _quantize_act(x, None, group_sums, out)
+
+
+def kq_quantize_act_ordered(x: torch.Tensor, order: int, group_sums: bool = False, out=None):
+    """kq_quantize_act with the codes of each row in `order` (KQ_CODES_*)."""
+    return _quantize_act(x, int(order), group_sums, out)
+
+
+def _quantize_act(x, order, group_sums, out):
+    # order None: kq_quantize_act, else kq_quantize_act_ordered
     _need(x, "x", torch.bfloat16, 2)
     M, K = x.shape
     if out is None:
@@ -230,7 +247,11 @@ def kq_quantize_act(x: torch.Tensor, group_sums: bool = False, out=None):
                 raise ValueError("out group sums have the wrong shape")
         else:
             gs = None
-    _check(lib().kq_quantize_act(_ptr(x), M, K, _ptr(a), _ptr(sx), _ptr(gs), _stream()))
+    if order is None:
+        _check(lib().kq_quantize_act(_ptr(x), M, K, _ptr(a), _ptr(sx), _ptr(gs), _stream()))
+    else:
+        _check(lib().kq_quantize_act_ordered(_ptr(x), M, K, _ptr(a), _ptr(sx), _ptr(gs), order,
+                                             _stream()))
     return a, sx, gs
 
 
@@ -373,6 +394,18 @@ def kq_w8a8_gemm(a, sx, wq, sw, bias=None, out_dtype=torch.bfloat16, out=None):
 
 def kq_w4a8_gemm(a, sx, gsum, wq4, gscale, gbias, bias=None, out_dtype=torch.bfloat16, out=None):
     """kq_w4a8_linear on codes/scales/group sums from kq_quantize_act."""
+    return _w4a8_gemm(a, sx, gsum, wq4, gscale, gbias, None, bias, out_dtype, out)
+
+
+def kq_w4a8_gemm_ordered(a, sx, gsum, wq4, gscale, gbias, order, bias=None,
+                         out_dtype=torch.bfloat16, out=None):
+    """kq_w4a8_gemm on codes in `order` (KQ_CODES_*), e.g. from
+    kq_quantize_act_ordered."""
+    return _w4a8_gemm(a, sx, gsum, wq4, gscale, gbias, int(order), bias, out_dtype, out)
+
+
+def _w4a8_gemm(a, sx, gsum, wq4, gscale, gbias, order, bias, out_dtype, out):
+    # order None: kq_w4a8_gemm, else kq_w4a8_gemm_ordered
     _need(a, "a", torch.int8, 2)
     _need(sx, "sx", torch.float32, 1)
     _need(gsum, "gsum", torch.int32, 2)
@@ -380,8 +413,12 @@ def kq_w4a8_gemm(a, sx, gsum, wq4, gscale, gbias, bias=None, out_dtype=torch.bfl
     M, K = a.shape
     N = wq4.shape[0]
     y = _prep_out(out, _out_shape(M, N, K, out_dtype, True), out_dtype, a.device)
-    _check(lib().kq_w4a8_gemm(_ptr(a), _ptr(sx), _ptr(gsum), M, K, N, _ptr(wq4), _ptr(gscale),
-                              _ptr(gbias), _ptr(bias), _ptr(y), _OUT[out_dtype], _stream()))
+    args = (_ptr(a), _ptr(sx), _ptr(gsum), M, K, N, _ptr(wq4), _ptr(gscale), _ptr(gbias),
+            _ptr(bias), _ptr(y), _OUT[out_dtype])
+    if order is None:
+        _check(lib().kq_w4a8_gemm(*args, _stream()))
+    else:
+        _check(lib().kq_w4a8_gemm_ordered(*args, order, _stream()))
     return y
 
 

@@ -78,7 +78,13 @@ __device__ __forceinline__ void store1(void* y, int64_t idx, float v) {
 // Split K: workgroup row blockIdx.y takes groups [y*gchunk, min(G, (y+1)*
 // gchunk)) (gchunk a multiple of the 16-group table chunk); with OUT ==
 // kOutPart it writes its raw fp32 sums to slice y of y[splits][M][N].
-template <int BM, int BN, int WTM, int WTN, int OUT, bool GATED>
+// EO: every run of 8 activation codes holds its even codes, then its odd
+// ones, the order in which a packed weight dword's low and high nibbles
+// come out (w & 0x0f0f0f0f, (w >> 4) & 0x0f0f0f0f): the weights need no
+// reordering.  Otherwise the codes are in natural order and the unpacked
+// nibbles are put back into it (two v_perm_b32 a dword).  The dot product
+// of a group is the same sum in another order, exact in int32.
+template <int BM, int BN, int WTM, int WTN, int OUT, bool GATED, bool EO>
 // (128x128: two workgroups per CU, so at most 256 registers per lane)
 __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, (BM == 128 && BN == 128) ? 2 : 1) void gemm_w4a8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int32_t* __restrict__ gsum,
@@ -241,8 +247,15 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, (BM == 128 && BN == 1
 #pragma unroll
     for (int i = 0; i < C::kTN; ++i) {
       uint32_t u0, u1, u2, u3;
-      unpack8_u4(f.q[i].x, u0, u1);
-      unpack8_u4(f.q[i].y, u2, u3);
+      if constexpr (EO) {
+        u0 = f.q[i].x & 0x0F0F0F0Fu;
+        u1 = (f.q[i].x >> 4) & 0x0F0F0F0Fu;
+        u2 = f.q[i].y & 0x0F0F0F0Fu;
+        u3 = (f.q[i].y >> 4) & 0x0F0F0F0Fu;
+      } else {
+        unpack8_u4(f.q[i].x, u0, u1);
+        unpack8_u4(f.q[i].y, u2, u3);
+      }
       const v4i fw = v4i{(int)u0, (int)u1, (int)u2, (int)u3};
       const float s = kScaled ? __half2float(__ushort_as_half((unsigned short)f.s[i])) : 0.f;
 #pragma unroll
@@ -421,7 +434,7 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, (BM == 128 && BN == 1
   }
 }
 
-template <int BM, int BN, int WTM, int WTN>
+template <int BM, int BN, int WTM, int WTN, bool EO>
 const char* launch_tile4(const int8_t* a, const float* sx, const int32_t* gsum, const uint8_t* q4,
                          const uint16_t* gs, const uint16_t* gb, const float* bias, void* y,
                          int out, int M, int N, int K, hipStream_t s, const Epilogue& ep,
@@ -430,19 +443,19 @@ const char* launch_tile4(const int8_t* a, const float* sx, const int32_t* gsum, 
   const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const dim3 grid((unsigned)tiles, (unsigned)splits), block(C::kThreads);
   if (out == kOutPart) {
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutPart, false>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutPart, false, EO>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
     return name;
   }
   if (ep.active() && out == kOutF32)
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutF32, true>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutF32, true, EO>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
   else if (ep.active() && out == kOutBF16)
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutBF16, true>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutBF16, true, EO>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
   else if (out == kOutF32)
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutF32, false>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutF32, false, EO>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
   else if (out == kOutBF16)
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutBF16, false>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutBF16, false, EO>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
   else
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutI32, false>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutI32, false, EO>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
   return name;
 }
 
@@ -496,7 +509,8 @@ void launch_fold4(const float* P, int S, const float* sx, const float* bias, voi
 const char* launch_gemm_w4a8(int tile, const int8_t* a, const float* sx, const int32_t* gsum,
                              const uint8_t* q4, const void* gs, const void* gb,
                              const float* bias, void* y, int out, int M, int N, int K,
-                             hipStream_t s, const Epilogue& ep, int splits, float* partials) {
+                             hipStream_t s, const Epilogue& ep, int splits, float* partials,
+                             bool eo) {
   const uint16_t* hs = reinterpret_cast<const uint16_t*>(gs);
   const uint16_t* hb = reinterpret_cast<const uint16_t*>(gb);
   int sp = 1, gchunk = K / 64;
@@ -511,15 +525,18 @@ const char* launch_gemm_w4a8(int tile, const int8_t* a, const float* sx, const i
   void* dst = fold ? static_cast<void*>(partials) : y;
   const int dout = fold ? kOutPart : out;
   const Epilogue dep = fold ? Epilogue() : ep;
-  const char* name =
-      tile == kTile128x256
-          ? launch_tile4<128, 256, 64, 64>(a, sx, gsum, q4, hs, hb, bias, dst, dout, M, N, K, s,
-                                           dep, "gemm_w4a8_128x256", sp, gchunk)
-      : tile == kTile128x128
-          ? launch_tile4<128, 128, 64, 64>(a, sx, gsum, q4, hs, hb, bias, dst, dout, M, N, K, s,
-                                           dep, "gemm_w4a8_128x128", sp, gchunk)
-          : launch_tile4<64, 128, 32, 64>(a, sx, gsum, q4, hs, hb, bias, dst, dout, M, N, K, s,
-                                          dep, "gemm_w4a8_64x128", sp, gchunk);
+  auto run = [&](auto eo_tag) {
+    constexpr bool E = decltype(eo_tag)::value;
+    return tile == kTile128x256
+               ? launch_tile4<128, 256, 64, 64, E>(a, sx, gsum, q4, hs, hb, bias, dst, dout, M, N,
+                                                   K, s, dep, "gemm_w4a8_128x256", sp, gchunk)
+           : tile == kTile128x128
+               ? launch_tile4<128, 128, 64, 64, E>(a, sx, gsum, q4, hs, hb, bias, dst, dout, M, N,
+                                                   K, s, dep, "gemm_w4a8_128x128", sp, gchunk)
+               : launch_tile4<64, 128, 32, 64, E>(a, sx, gsum, q4, hs, hb, bias, dst, dout, M, N,
+                                                  K, s, dep, "gemm_w4a8_64x128", sp, gchunk);
+  };
+  const char* name = eo ? run(std::true_type{}) : run(std::false_type{});
   if (fold) launch_fold4(partials, sp, sx, bias, y, out, M, N, s, ep);
   return name;
 }

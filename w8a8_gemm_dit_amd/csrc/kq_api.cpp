@@ -116,17 +116,21 @@ const char* dtype_name(kq_dtype d) {
 // partials: int32 workspace of a split GEMM, or NULL (then K is never split).
 // frag: the codes are in the MFMA GEMV's fragment order (the linears'
 // quantize kernel writes them so when the route takes that kernel).
+// eo: int4 weights on the tiled GEMM, codes in the quantize kernel's
+// frag-3 order (each run of 8 as its even codes, then its odd ones).
 kq_status launch_main(const char* op, int force, kq_wformat fmt, const int8_t* codes,
                       const float* sx, const int32_t* gsum, int64_t M, int64_t K, int64_t N,
                       const void* wq, const void* scale, const void* gbias, const float* bias,
                       void* y, kq_dtype y_dtype, hipStream_t s, const char* kq_name,
                       const kq::Epilogue& ep = kq::Epilogue(), int32_t* partials = nullptr,
-                      bool frag = false) {
+                      bool frag = false, bool eo = false) {
   const kq_route_info r =
       kq::choose_route(M, N, K, fmt, force, env_tile(), partials ? env_split() : 0, false,
                        env_gemv_lane());
   const int out = out_kind(y_dtype);
   const char* k2;
+  if (eo && (r.kind == KQ_ROUTE_GEMV || fmt != KQ_W4_AFFINE_G64))
+    return fail(KQ_ERR_UNSUPPORTED, "[%s] internal: split-order codes on a route that reads them in natural order", op);
   if (r.kind == KQ_ROUTE_GEMV) {
     k2 = kq::launch_gemv(fmt == KQ_W4_AFFINE_G64, codes, sx, gsum, wq, scale, gbias, bias, y, out,
                          (int)M, (int)N, (int)K, s, ep, nullptr, nullptr, env_gemv_lane(),
@@ -144,7 +148,7 @@ kq_status launch_main(const char* op, int force, kq_wformat fmt, const int8_t* c
     else
       k2 = kq::launch_gemm_w4a8(tile, codes, sx, gsum, reinterpret_cast<const uint8_t*>(wq),
                                 scale, gbias, bias, y, out, (int)M, (int)N, (int)K, s, ep,
-                                r.splits, reinterpret_cast<float*>(partials));
+                                r.splits, reinterpret_cast<float*>(partials), eo);
   }
   const kq_status st = check_launch(op);
   if (st != KQ_SUCCESS) return st;
@@ -224,24 +228,60 @@ kq_status run_linear(const char* op, int force, kq_wformat fmt, const void* x, i
   float* sx = reinterpret_cast<float*>(wsb + wl.scale_off);
   int32_t* gsum = fmt == KQ_W4_AFFINE_G64 ? reinterpret_cast<int32_t*>(wsb + wl.gsum_off) : nullptr;
   // the MFMA GEMV reads the codes in its fragment order (whole 1 KB
-  // operands per load), every other route row-major
+  // operands per load), the int4 GEMM row-major with each run of 8 split
+  // into its even and odd codes (its weights' unpack order), every other
+  // route row-major
   const bool frag = kq::gemv_frag_codes(r);
+  const bool eo = !frag && fmt == KQ_W4_AFFINE_G64 && r.kind != KQ_ROUTE_GEMV;
   const char* kq_name = kq::launch_quant_act(reinterpret_cast<const uint16_t*>(x), M, (int)K, codes,
                                              sx, gsum, s,
-                                             frag ? (fmt == KQ_W4_AFFINE_G64 ? 2 : 1) : 0);
+                                             frag ? (fmt == KQ_W4_AFFINE_G64 ? 2 : 1) : eo ? 3 : 0);
   st = check_launch(op);
   if (st != KQ_SUCCESS) return st;
   int32_t* partials = splits > 1 ? reinterpret_cast<int32_t*>(wsb + wl.part_off) : nullptr;
   return launch_main(op, force, fmt, codes, sx, gsum, M, K, N, wq, scale, gbias, bias, y, y_dtype,
-                     s, kq_name, ep, partials, frag);
+                     s, kq_name, ep, partials, frag, eo);
+}
+
+// Shared body of the activation-quantization entry points.
+kq_status quantize_act(const char* op, const void* x, int64_t M, int64_t K, int8_t* a, float* sx,
+                       int32_t* gsum, kq_code_order order, void* stream) {
+  if (order != KQ_CODES_NATURAL && order != KQ_CODES_SPLIT8)
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] unknown code order %d", op, (int)order);
+  if (M < 0 || K < 0) return fail(KQ_ERR_INVALID_VALUE, "[%s] negative size", op);
+  if (K == 0) return fail(KQ_ERR_UNSUPPORTED, "[%s] K must be positive", op);
+  if (K > INT32_MAX / 2) return fail(KQ_ERR_UNSUPPORTED, "[%s] K=%lld too large", op, (long long)K);
+  if (order == KQ_CODES_SPLIT8 && K % 8)
+    return fail(KQ_ERR_UNSUPPORTED, "[%s] split code order needs K %% 8 == 0 (K=%lld)", op, (long long)K);
+  if (gsum && K % 64)
+    return fail(KQ_ERR_UNSUPPORTED, "[%s] group sums need K %% 64 == 0 (K=%lld)", op, (long long)K);
+  if (M == 0) return KQ_SUCCESS;
+  if (!x || !a || !sx) return fail(KQ_ERR_INVALID_VALUE, "[%s] null tensor pointer", op);
+  if (K % 8 == 0 && (!aligned16(x) || ((uintptr_t)a & 7)))
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] x must be 16-byte and a 8-byte aligned", op);
+  kq_status st = check_device(op);
+  if (st != KQ_SUCCESS) return st;
+  const char* name = kq::launch_quant_act(reinterpret_cast<const uint16_t*>(x), M, (int)K, a, sx,
+                                          gsum, reinterpret_cast<hipStream_t>(stream),
+                                          order == KQ_CODES_SPLIT8 ? 3 : 0);
+  st = check_launch(op);
+  if (st == KQ_SUCCESS && env_log())
+    fprintf(stderr, "[kq] %s M=%lld K=%lld kernel=%s\n", op, (long long)M, (long long)K, name);
+  return st;
 }
 
 // Shared body of the entry points on pre-quantized activations.
 kq_status run_gemm(const char* op, kq_wformat fmt, const int8_t* a, const float* sx,
                    const int32_t* gsum, int64_t M, int64_t K, int64_t N, const void* wq,
                    const void* scale, const void* gbias, const float* bias, void* y,
-                   kq_dtype y_dtype, void* stream) {
-  const int force = env_force_route();
+                   kq_dtype y_dtype, void* stream, kq_code_order order = KQ_CODES_NATURAL) {
+  if (order != KQ_CODES_NATURAL && order != KQ_CODES_SPLIT8)
+    return fail(KQ_ERR_INVALID_VALUE, "[%s] unknown code order %d", op, (int)order);
+  const bool eo = order == KQ_CODES_SPLIT8;
+  int force = env_force_route();
+  if (eo && force == 2)
+    return fail(KQ_ERR_UNSUPPORTED, "[%s] the GEMV reads natural-order codes (KQ_FORCE_ROUTE=gemv)", op);
+  if (eo) force = 1;  // the tiled int4 GEMM reads split-order codes
   kq_status st = check_linear_args(op, force, fmt, M, K, N, y_dtype, a, wq, scale, gbias, y);
   if (st != KQ_SUCCESS || M == 0 || N == 0) return st;
   if (!sx || (fmt == KQ_W4_AFFINE_G64 && !gsum))
@@ -249,7 +289,8 @@ kq_status run_gemm(const char* op, kq_wformat fmt, const int8_t* a, const float*
   st = check_device(op);
   if (st != KQ_SUCCESS) return st;
   return launch_main(op, force, fmt, a, sx, gsum, M, K, N, wq, scale, gbias, bias, y, y_dtype,
-                     reinterpret_cast<hipStream_t>(stream), nullptr);
+                     reinterpret_cast<hipStream_t>(stream), nullptr, kq::Epilogue(), nullptr,
+                     false, eo);
 }
 
 // ------------------------------------------------------------ attention
@@ -435,24 +476,12 @@ kq_status kq_quantize_weights(const float* w, int64_t N, int64_t K, kq_wformat f
 
 kq_status kq_quantize_act(const void* x, int64_t M, int64_t K, int8_t* a, float* sx,
                           int32_t* gsum, void* stream) {
-  const char* op = "kq_quantize_act";
-  if (M < 0 || K < 0) return fail(KQ_ERR_INVALID_VALUE, "[%s] negative size", op);
-  if (K == 0) return fail(KQ_ERR_UNSUPPORTED, "[%s] K must be positive", op);
-  if (K > INT32_MAX / 2) return fail(KQ_ERR_UNSUPPORTED, "[%s] K=%lld too large", op, (long long)K);
-  if (gsum && K % 64)
-    return fail(KQ_ERR_UNSUPPORTED, "[%s] group sums need K %% 64 == 0 (K=%lld)", op, (long long)K);
-  if (M == 0) return KQ_SUCCESS;
-  if (!x || !a || !sx) return fail(KQ_ERR_INVALID_VALUE, "[%s] null tensor pointer", op);
-  if (K % 8 == 0 && (!aligned16(x) || ((uintptr_t)a & 7)))
-    return fail(KQ_ERR_INVALID_VALUE, "[%s] x must be 16-byte and a 8-byte aligned", op);
-  kq_status st = check_device(op);
-  if (st != KQ_SUCCESS) return st;
-  const char* name = kq::launch_quant_act(reinterpret_cast<const uint16_t*>(x), M, (int)K, a, sx,
-                                          gsum, reinterpret_cast<hipStream_t>(stream));
-  st = check_launch(op);
-  if (st == KQ_SUCCESS && env_log())
-    fprintf(stderr, "[kq] %s M=%lld K=%lld kernel=%s\n", op, (long long)M, (long long)K, name);
-  return st;
+  return quantize_act("kq_quantize_act", x, M, K, a, sx, gsum, KQ_CODES_NATURAL, stream);
+}
+
+kq_status kq_quantize_act_ordered(const void* x, int64_t M, int64_t K, int8_t* a, float* sx,
+                                  int32_t* gsum, kq_code_order order, void* stream) {
+  return quantize_act("kq_quantize_act_ordered", x, M, K, a, sx, gsum, order, stream);
 }
 
 kq_status kq_w8a8_linear(const void* x, int64_t M, int64_t K, int64_t N, const int8_t* wq,
@@ -481,6 +510,14 @@ kq_status kq_w4a8_gemm(const int8_t* a, const float* sx, const int32_t* gsum, in
                        const float* bias, void* y, kq_dtype y_dtype, void* stream) {
   return run_gemm("kq_w4a8_gemm", KQ_W4_AFFINE_G64, a, sx, gsum, M, K, N, wq4, gscale, gbias, bias,
                   y, y_dtype, stream);
+}
+
+kq_status kq_w4a8_gemm_ordered(const int8_t* a, const float* sx, const int32_t* gsum, int64_t M,
+                               int64_t K, int64_t N, const uint8_t* wq4, const void* gscale,
+                               const void* gbias, const float* bias, void* y, kq_dtype y_dtype,
+                               kq_code_order order, void* stream) {
+  return run_gemm("kq_w4a8_gemm_ordered", KQ_W4_AFFINE_G64, a, sx, gsum, M, K, N, wq4, gscale,
+                  gbias, bias, y, y_dtype, stream, order);
 }
 
 kq_status kq_gemv_small_m(kq_wformat fmt, const void* x, int64_t M, int64_t K, int64_t N,

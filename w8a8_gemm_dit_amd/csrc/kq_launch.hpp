@@ -28,7 +28,9 @@ struct Epilogue {
 
 // frag: where the codes go: 0 row-major [M][K]; 1 / 2 the MFMA GEMV's
 // fragment order for int8 / int4 weights (kq::gemv_frag_offset, rows
-// rounded up to 16; the padding rows are not written).
+// rounded up to 16; the padding rows are not written); 3 row-major with
+// each run of 8 codes as its even codes, then its odd ones (the int4
+// GEMM's unpack order, launch_gemm_w4a8's eo).
 const char* launch_quant_act(const uint16_t* x, int64_t M, int K, int8_t* a, float* sx,
                              int32_t* gsum, hipStream_t s, int frag = 0);
 const char* launch_quant_w8(const float* w, int64_t N, int K, int8_t* q, float* sw,
@@ -48,11 +50,12 @@ const char* launch_gemm_w8a8(int tile, const int8_t* a, const float* sx, const i
 // splits > 1: K in that many slices of whole 16-group chunks; fp32 slice
 // sums into `partials` [splits][M][N], then a fold kernel applies the token
 // scale and the bias (I32 output: each slice writes its own groups).
+// eo: the codes a are in launch_quant_act's frag-3 order, else natural.
 const char* launch_gemm_w4a8(int tile, const int8_t* a, const float* sx, const int32_t* gsum,
                              const uint8_t* q4, const void* gs, const void* gb,
                              const float* bias, void* y, int out, int M, int N, int K,
                              hipStream_t s, const Epilogue& ep = Epilogue(),
-                             int splits = 1, float* partials = nullptr);
+                             int splits = 1, float* partials = nullptr, bool eo = false);
 
 // GEMV for 1 <= M <= 16 (w4: q is packed int4 with gs/gb; w8: q int8, gs = fp32 [N]).
 // x != NULL: the kernel quantizes the bf16 rows x itself (a, sx unused;

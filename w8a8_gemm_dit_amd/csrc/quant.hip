@@ -60,11 +60,23 @@ __device__ __forceinline__ int group8_sum(int v) {
 // K % 8 == 0 and K <= 512*CH: the row stays in registers (CH chunks of 8
 // values per lane; chunk c = lane + 64*j covers elements 8c..8c+7).
 // FR: where the codes go: 0 row-major [M][K]; 1 and 2 the MFMA GEMV's
-// fragment order for int8 and int4 weights (gemv_frag_offset).
+// fragment order for int8 and int4 weights (gemv_frag_offset); 3 row-major
+// with every run of 8 codes stored as its even codes, then its odd ones
+// (the order in which the int4 GEMM unpacks a packed weight dword).
 template <int FR>
 __device__ __forceinline__ uint2* code_slot(int8_t* a, int64_t row, int c, int K) {
-  const int64_t off = FR == 0 ? row * (int64_t)K + 8 * c : gemv_frag_offset(row, 8 * c, K, FR == 2);
+  const int64_t off = FR == 0 || FR == 3 ? row * (int64_t)K + 8 * c
+                                         : gemv_frag_offset(row, 8 * c, K, FR == 2);
   return reinterpret_cast<uint2*>(a + off);
+}
+
+// The 8 codes of a chunk (c0..c3 in .x, c4..c7 in .y) in FR's order.
+template <int FR>
+__device__ __forceinline__ uint2 order_codes(uint2 v) {
+  if constexpr (FR != 3) return v;
+  // v_perm_b32: bytes 0-3 select from the second operand, 4-7 from the first
+  return make_uint2(__builtin_amdgcn_perm(v.y, v.x, 0x06040200u),   // c0 c2 c4 c6
+                    __builtin_amdgcn_perm(v.y, v.x, 0x07050301u));  // c1 c3 c5 c7
 }
 
 template <int CH, int FR>
@@ -98,7 +110,7 @@ __global__ __launch_bounds__(256) void quant_act_regs(
     const int c = lane + 64 * j;
     int s;
     const uint2 codes = quant8(v[j], inv, s);
-    if (c < nch) *code_slot<FR>(a, row, c, K) = codes;
+    if (c < nch) *code_slot<FR>(a, row, c, K) = order_codes<FR>(codes);
     if (gsum != nullptr) {
       s = group8_sum(s);
       if ((lane & 7) == 0 && c < nch) gsum[row * G + (c >> 3)] = s;
@@ -148,7 +160,7 @@ __global__ __launch_bounds__(kWideThreads) void quant_act_wide(
     const int c = tid + kWideThreads * j;
     int s;
     const uint2 codes = quant8(v[j], inv, s);
-    if (c < nch) *code_slot<FR>(a, row, c, K) = codes;
+    if (c < nch) *code_slot<FR>(a, row, c, K) = order_codes<FR>(codes);
     if (gsum != nullptr) {
       s = group8_sum(s);
       if ((lane & 7) == 0 && c < nch) gsum[row * G + (c >> 3)] = s;
@@ -178,7 +190,7 @@ __global__ __launch_bounds__(256) void quant_act_stream(
     int s = 0;
     uint2 codes = make_uint2(0, 0);
     if (c < nch) codes = quant8(xr[c], inv, s);
-    if (c < nch) *code_slot<FR>(a, row, c, K) = codes;
+    if (c < nch) *code_slot<FR>(a, row, c, K) = order_codes<FR>(codes);
     if (gsum != nullptr) {
       s = group8_sum(s);
       if ((lane & 7) == 0 && c < nch) gsum[row * G + (c >> 3)] = s;
@@ -304,6 +316,7 @@ const char* launch_quant_act(const uint16_t* x, int64_t M, int K, int8_t* a, flo
   }
   if (frag == 1) return launch_act<1>(x, M, K, a, sx, gsum, s);
   if (frag == 2) return launch_act<2>(x, M, K, a, sx, gsum, s);
+  if (frag == 3) return launch_act<3>(x, M, K, a, sx, gsum, s);
   return launch_act<0>(x, M, K, a, sx, gsum, s);
 }
 
