@@ -203,6 +203,28 @@ def test_gemv_xq_matches_oracle(M, K, N, fmt, lane, kq_env):
     _check_all(fmt, xb, w, b, f"gemv xq {fmt} {M}x{K}x{N}")
 
 
+# M <= 2 on grids of at least one workgroup per CU (N >= 8161): the lane
+# kernels keep a window of lines in flight per lane instead of issuing every
+# line at once; one line window, a ragged line count, the K limit
+GEMV_LANE_WIDE = [(1, 5120, 8192), (2, 1088, 8200), (1, 2112, 9000), (2, 6144, 8224)]
+
+
+@pytest.mark.parametrize("fmt", ["w8", "w4"])
+@pytest.mark.parametrize("M,K,N", GEMV_LANE_WIDE)
+def test_gemv_lane_windowed_matches_oracle(M, K, N, fmt, kq_env):
+    """The windowed lane kernels: int32 results and scales bit-exact,
+    outputs within the oracle's bars."""
+    kq_env(KQ_FORCE_ROUTE=None, KQ_TILE=None, KQ_FUSE=None, KQ_GEMV_LANE=None)
+    r = kq.kq_route(M, N, K, _fmt_code(fmt))
+    assert (r["kind"], r["tile_m"]) == ("fused", 2) and r["grid"] >= 256
+    seed = 11 * M + K + N
+    xb = synth.random_bf16((M, K), seed=seed, dist="student_t4")
+    w = synth.random_f32((N, K), seed=seed + 1, scale=0.02)
+    b = synth.random_f32((N,), seed=seed + 2, scale=0.1)
+    print(f"[fused] windowed lane {fmt} {M}x{K}x{N}", flush=True)
+    _check_all(fmt, xb, w, b, f"windowed lane {fmt} {M}x{K}x{N}")
+
+
 @pytest.mark.parametrize("fmt", ["w8", "w4"])
 def test_gemv_xq_special_rows(fmt, kq_env):
     """A zero row, a row whose 127/amax overflows, a subnormal row and a huge
@@ -224,7 +246,8 @@ def test_gemv_xq_special_rows(fmt, kq_env):
 
 
 @pytest.mark.parametrize("fmt", ["w8", "w4"])
-@pytest.mark.parametrize("M,K,N", [(1, 5120, 512), (4, 1088, 200), (2, 3072, 1000)])
+@pytest.mark.parametrize("M,K,N", [(1, 5120, 512), (4, 1088, 200), (2, 3072, 1000),
+                                   (1, 5120, 8192), (2, 3072, 8256)])
 def test_gemv_xq_and_two_kernel_gemv_agree_bitwise(M, K, N, fmt, kq_env):
     """The same GEMV kernel, slices and sum order whether it quantizes x
     itself or reads the quantize kernel's codes: every output bit agrees,

@@ -669,14 +669,22 @@ __device__ __forceinline__ uint2 codes8_eo(uint32_t d0, uint32_t d1) {
 }
 
 // NL: lines per wavefront (each takes one K slice of a row's lines), so K
-// <= 256*kLSlices*NL.
-template <int OUT, bool XQ, int MR, int NL>
+// <= 256*kLSlices*NL.  WIN: lines a lane keeps in flight.  WIN = NL issues
+// every line at once (one memory latency: grids too small to fill the
+// chip).  On a grid that fills it every byte in flight at once makes the
+// lines land in random order, and a wavefront consumes them in issue order
+// (vmcnt), so most of the arithmetic waited for the last line; with a
+// window of WIN lines, line i + WIN is issued when line i is consumed and
+// the arithmetic runs under the loads (5120 -> 13824, M = 1, per call:
+// 10.5 -> 9.3 us at WIN = 3; 9.6 at 2, 9.7 at 4, 10.0 at 5).
+template <int OUT, bool XQ, int MR, int NL, int WIN>
 __global__ __launch_bounds__(kLWaves * 64) void gemv_lane_kernel(
     const uint16_t* __restrict__ X, const int8_t* __restrict__ Acodes, const float* __restrict__ sx,
     const uint8_t* __restrict__ Wq, const uint16_t* __restrict__ GS, const uint16_t* __restrict__ GB,
     const float* __restrict__ bias, void* y, int M, int N, int K, Epilogue ep,
     float* __restrict__ sx_out) {
   static_assert(kLSlices * NL <= kLMaxLines && MR >= 1 && MR <= kGemvLaneRows, "lane GEMV shape");
+  static_assert(WIN >= 1 && WIN <= NL, "line window");
   constexpr int kT = kLWaves * 64;
   constexpr int kMaxK = NL * 256 * kLSlices;                // K that the slices' lines cover
   constexpr int kHPT = (MR * kMaxK / 32 + kT - 1) / kT;     // half groups per thread
@@ -747,10 +755,13 @@ __global__ __launch_bounds__(kLWaves * 64) void gemv_lane_kernel(
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(Wq + (int64_t)min(nw, N - 1) * (K / 2)), 0, nrec, 0x00020000);
   const int voff = c8 * (K / 2) + 128 * l0 + 16 * p;
+  auto load_line = [&](int i) {
+    return __builtin_bit_cast(
+        v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, i < nlw ? voff + 128 * i : 0x40000000, 0, 0));
+  };
   v4i wv[NL];
 #pragma unroll
-  for (int i = 0; i < NL; ++i)
-    wv[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, i < nlw ? voff + 128 * i : 0x40000000, 0, 0));
+  for (int i = 0; i < WIN; ++i) wv[i] = load_line(i);  // the rest as lines are consumed
   __builtin_amdgcn_sched_barrier(0);
 
   // 4. row scales, codes and half-group sums into LDS
@@ -866,6 +877,7 @@ __global__ __launch_bounds__(kLWaves * 64) void gemv_lane_kernel(
   const float* hbase = s_hsum + 2 * g0l + hh;
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
+    if (i + WIN < NL) wv[i + WIN] = load_line(i + WIN);  // keep WIN lines in flight
     if (i >= nlw) continue;  // uniform
     const int g = g0l + 4 * i;  // < G4
     float2 so = make_float2(0.0f, 0.0f);
@@ -932,8 +944,14 @@ __global__ __launch_bounds__(kLWaves * 64) void gemv_lane_kernel(
   }
 }
 
-template <bool XQ, int MR, int NL>
-void launch_lane_out(const uint16_t* x, const int8_t* a, const float* sx, const void* q,
+// Lines in flight per lane on grids that fill the chip (measured best).
+constexpr int kLaneWin4 = 3, kLaneWin8 = 4;
+
+// The windowed form on a grid of at least one workgroup per CU.
+inline bool lane_streams(int N) { return (N + kLCols - 1) / kLCols >= kSplitCUs; }
+
+template <bool XQ, int MR, int NL, int WIN>
+void launch_lane_win(const uint16_t* x, const int8_t* a, const float* sx, const void* q,
                      const void* gs, const void* gb, const float* bias, void* y, int out, int M,
                      int N, int K, hipStream_t s, const Epilogue& ep, float* sx_out) {
   const dim3 grid((unsigned)((N + kLCols - 1) / kLCols)), block(kLWaves * 64);
@@ -941,11 +959,24 @@ void launch_lane_out(const uint16_t* x, const int8_t* a, const float* sx, const 
   const uint16_t* hs = reinterpret_cast<const uint16_t*>(gs);
   const uint16_t* hb = reinterpret_cast<const uint16_t*>(gb);
   if (out == kOutF32)
-    hipLaunchKernelGGL((gemv_lane_kernel<kOutF32, XQ, MR, NL>), grid, block, 0, s, x, a, sx, qw, hs, hb, bias, y, M, N, K, ep, sx_out);
+    hipLaunchKernelGGL((gemv_lane_kernel<kOutF32, XQ, MR, NL, WIN>), grid, block, 0, s, x, a, sx, qw, hs, hb, bias, y, M, N, K, ep, sx_out);
   else if (out == kOutBF16)
-    hipLaunchKernelGGL((gemv_lane_kernel<kOutBF16, XQ, MR, NL>), grid, block, 0, s, x, a, sx, qw, hs, hb, bias, y, M, N, K, ep, sx_out);
+    hipLaunchKernelGGL((gemv_lane_kernel<kOutBF16, XQ, MR, NL, WIN>), grid, block, 0, s, x, a, sx, qw, hs, hb, bias, y, M, N, K, ep, sx_out);
   else
-    hipLaunchKernelGGL((gemv_lane_kernel<kOutI32, XQ, MR, NL>), grid, block, 0, s, x, a, sx, qw, hs, hb, bias, y, M, N, K, ep, sx_out);
+    hipLaunchKernelGGL((gemv_lane_kernel<kOutI32, XQ, MR, NL, WIN>), grid, block, 0, s, x, a, sx, qw, hs, hb, bias, y, M, N, K, ep, sx_out);
+}
+
+template <bool XQ, int MR, int NL>
+void launch_lane_out(const uint16_t* x, const int8_t* a, const float* sx, const void* q,
+                     const void* gs, const void* gb, const float* bias, void* y, int out, int M,
+                     int N, int K, hipStream_t s, const Epilogue& ep, float* sx_out) {
+  if constexpr (NL > kLaneWin4) {
+    if (lane_streams(N)) {
+      launch_lane_win<XQ, MR, NL, kLaneWin4>(x, a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, sx_out);
+      return;
+    }
+  }
+  launch_lane_win<XQ, MR, NL, NL>(x, a, sx, q, gs, gb, bias, y, out, M, N, K, s, ep, sx_out);
 }
 
 template <bool XQ, int MR>
@@ -993,12 +1024,15 @@ const char* launch_lane(const uint16_t* x, const int8_t* a, const float* sx, con
 // slices add exactly, and the epilogue is the MFMA GEMV's expression,
 // fma(sx*sw, acc, bias), so the outputs equal the other routes' bit for
 // bit.  Codes past K (a half line at the end) are zero in LDS.
-template <int OUT, bool XQ, int MR, int NL>
+// WIN: lines a lane keeps in flight, as in the int4 kernel (the modulation
+// linear 2x3072 -> 18432: 14.2 -> 13.95 us at WIN = 4).
+template <int OUT, bool XQ, int MR, int NL, int WIN>
 __global__ __launch_bounds__(kLWaves * 64) void gemv_lane8_kernel(
     const uint16_t* __restrict__ X, const int8_t* __restrict__ Acodes, const float* __restrict__ sx,
     const int8_t* __restrict__ Wq, const float* __restrict__ SW, const float* __restrict__ bias,
     void* y, int M, int N, int K, Epilogue ep, float* __restrict__ sx_out) {
   static_assert(kLSlices * NL <= 2 * kLMaxLines && MR >= 1 && MR <= kGemvLaneRows, "lane GEMV shape");
+  static_assert(WIN >= 1 && WIN <= NL, "line window");
   constexpr int kT = kLWaves * 64;
   constexpr int kMaxK = NL * 128 * kLSlices;                // K that the slices' lines cover
   constexpr int kHPT = (MR * kMaxK / 32 + kT - 1) / kT;     // 32-value units per thread
@@ -1045,10 +1079,13 @@ __global__ __launch_bounds__(kLWaves * 64) void gemv_lane8_kernel(
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(Wq + (int64_t)min(nw, N - 1) * K), 0, nrec, 0x00020000);
   const int voff = c8 * K + 128 * l0 + 16 * p;
+  auto load_line = [&](int i) {
+    return __builtin_bit_cast(
+        v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, i < nlw ? voff + 128 * i : 0x40000000, 0, 0));
+  };
   v4i wv[NL];
 #pragma unroll
-  for (int i = 0; i < NL; ++i)
-    wv[i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rw, i < nlw ? voff + 128 * i : 0x40000000, 0, 0));
+  for (int i = 0; i < WIN; ++i) wv[i] = load_line(i);  // the rest as lines are consumed
   __builtin_amdgcn_sched_barrier(0);
 
   // 3. row scales and codes into LDS (rows at a kMaxK-byte stride)
@@ -1132,6 +1169,7 @@ __global__ __launch_bounds__(kLWaves * 64) void gemv_lane8_kernel(
   const uint32_t* cbase = s_code + 32 * l0 + 4 * p;
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
+    if (i + WIN < NL) wv[i + WIN] = load_line(i + WIN);  // keep WIN lines in flight
     if (i >= nlw) continue;  // uniform
 #pragma unroll
     for (int rr = 0; rr < MR; ++rr) {
@@ -1180,19 +1218,32 @@ __global__ __launch_bounds__(kLWaves * 64) void gemv_lane8_kernel(
   }
 }
 
-template <bool XQ, int MR, int NL>
-void launch_lane8_out(const uint16_t* x, const int8_t* a, const float* sx, const void* q,
+template <bool XQ, int MR, int NL, int WIN>
+void launch_lane8_win(const uint16_t* x, const int8_t* a, const float* sx, const void* q,
                       const void* sw, const float* bias, void* y, int out, int M, int N, int K,
                       hipStream_t s, const Epilogue& ep, float* sx_out) {
   const dim3 grid((unsigned)((N + kLCols - 1) / kLCols)), block(kLWaves * 64);
   const int8_t* qw = reinterpret_cast<const int8_t*>(q);
   const float* swf = reinterpret_cast<const float*>(sw);
   if (out == kOutF32)
-    hipLaunchKernelGGL((gemv_lane8_kernel<kOutF32, XQ, MR, NL>), grid, block, 0, s, x, a, sx, qw, swf, bias, y, M, N, K, ep, sx_out);
+    hipLaunchKernelGGL((gemv_lane8_kernel<kOutF32, XQ, MR, NL, WIN>), grid, block, 0, s, x, a, sx, qw, swf, bias, y, M, N, K, ep, sx_out);
   else if (out == kOutBF16)
-    hipLaunchKernelGGL((gemv_lane8_kernel<kOutBF16, XQ, MR, NL>), grid, block, 0, s, x, a, sx, qw, swf, bias, y, M, N, K, ep, sx_out);
+    hipLaunchKernelGGL((gemv_lane8_kernel<kOutBF16, XQ, MR, NL, WIN>), grid, block, 0, s, x, a, sx, qw, swf, bias, y, M, N, K, ep, sx_out);
   else
-    hipLaunchKernelGGL((gemv_lane8_kernel<kOutI32, XQ, MR, NL>), grid, block, 0, s, x, a, sx, qw, swf, bias, y, M, N, K, ep, sx_out);
+    hipLaunchKernelGGL((gemv_lane8_kernel<kOutI32, XQ, MR, NL, WIN>), grid, block, 0, s, x, a, sx, qw, swf, bias, y, M, N, K, ep, sx_out);
+}
+
+template <bool XQ, int MR, int NL>
+void launch_lane8_out(const uint16_t* x, const int8_t* a, const float* sx, const void* q,
+                      const void* sw, const float* bias, void* y, int out, int M, int N, int K,
+                      hipStream_t s, const Epilogue& ep, float* sx_out) {
+  if constexpr (NL > kLaneWin8) {
+    if (lane_streams(N)) {
+      launch_lane8_win<XQ, MR, NL, kLaneWin8>(x, a, sx, q, sw, bias, y, out, M, N, K, s, ep, sx_out);
+      return;
+    }
+  }
+  launch_lane8_win<XQ, MR, NL, NL>(x, a, sx, q, sw, bias, y, out, M, N, K, s, ep, sx_out);
 }
 
 template <bool XQ, int MR>
