@@ -17,16 +17,21 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
+// fp32 -> bf16 rounds to nearest even in one v_cvt_pk_bf16_f32 (gfx950),
+// two values per instruction: the same result as adding 0x7fff plus the
+// kept bit's parity to the fp32 pattern and truncating, for every finite
+// input, in a fifth of the instructions.
+typedef __bf16 kq_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float kq_f32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 bits, round to nearest even.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float v) {
-  uint32_t u = __float_as_uint(v);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
 // Two fp32 -> packed bf16x2 (low half = a).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(kq_f32x2{a, b}, kq_bf16x2));
 }
 
 // Wave-wide reductions over all 64 lanes (result in every lane).
