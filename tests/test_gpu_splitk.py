@@ -176,3 +176,31 @@ def test_int4_split_with_gated_epilogue(kq_env):
     ref = oracle.gated_residual_exact(oracle.w4a8_linear_exact(xb, q, gs, gb, b), r, g, M)
     T = oracle.gated_magnitude(oracle.w4a8_magnitude(xb, q, gs, gb, b), r, g, M)
     check_bf16(host_bf16_bits(y), ref, T, "int4 split gated")
+
+
+# The 4-buffer ring (tiles up to 128x128 on grids of at most one workgroup
+# per CU, K/64 a multiple of 8 in every slice): the same sums and epilogue
+# as the 2-buffer ring, so every output bit agrees with KQ_DEEP_RING=0.
+@pytest.mark.parametrize("tile", ["128x128", "64x64"])
+@pytest.mark.parametrize("split", [None, "1", "2", "6"])
+@pytest.mark.parametrize("M,K,N", [(128, 12288, 3072), (100, 4096, 500), (256, 512, 129),
+                                   (64, 3584, 1000)])
+def test_deep_ring_matches_two_buffer_ring(M, K, N, tile, split, kq_env):
+    kq_env(KQ_FORCE_ROUTE="gemm", KQ_TILE=tile, KQ_SPLIT=split, KQ_DEEP_RING=None)
+    print(f"[splitk] deep ring {M}x{K}x{N} tile {tile} split {split}", flush=True)
+    xb, q8, sw, b = _problem(M, K, N, seed=3 * M + K + N)
+    args = (dev_bf16(xb), dev(q8), dev(sw), dev(b))
+    outs = {}
+    for deep in (None, "0"):
+        kq_env(KQ_DEEP_RING=deep)
+        outs[deep] = [kq.kq_w8a8_linear(*args, out_dtype=dt) for dt in (torch.float32, torch.bfloat16)]
+        outs[deep].append(kq.kq_w8a8_linear(*args[:3], out_dtype=torch.int32))
+    torch.cuda.synchronize()
+    for a, c in zip(outs[None], outs["0"]):
+        assert torch.equal(_bits(a), _bits(c))
+    a, _, _ = oracle.quantize_act(xb)
+    assert np.array_equal(host(outs[None][2]), oracle.w8a8_acc(a, q8))
+    y64 = oracle.w8a8_linear_exact(xb, q8, sw, b)
+    T = oracle.w8a8_magnitude(xb, q8, sw, b)
+    check_f32(host(outs[None][0]), y64, T, f"deep ring {M}x{K}x{N} f32")
+    check_bf16(host_bf16_bits(outs[None][1]), y64, T, f"deep ring {M}x{K}x{N} bf16")

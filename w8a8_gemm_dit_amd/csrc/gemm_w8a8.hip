@@ -158,16 +158,23 @@ __device__ __forceinline__ void store4(void* y, int64_t idx, const float v[4], c
 // kchunk)) of every row (K stays the row stride) and, with OUT == I32,
 // writes its int32 sums to slice y of y[splits][M][N]; kchunk = K and one
 // grid row otherwise.
-template <int BM, int BN, int WM, int WN, int OUT, bool REM, bool GATED>
+// NB: pair buffers in the ring (2, or 4 where a small tile runs one
+// workgroup per CU on a grid that does not fill the chip twice: the
+// kernel is then bound by the bytes it keeps in flight, and 4 buffers hold
+// three pairs in flight instead of one).  NB = 4 needs K/64 a multiple of
+// 8 in every slice and no REM.
+template <int BM, int BN, int WM, int WN, int OUT, bool REM, bool GATED, int NB = 2>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int8_t* __restrict__ W,
     const float* __restrict__ sw, const float* __restrict__ bias, void* y, int M,
     int N, int K, Epilogue ep, int kchunk) {
   using C = Cfg<BM, BN, WM, WN>;
-  // Two pair buffers (steps 4i, 4i+1 and 4i+2, 4i+3): each its own array,
-  // so the compiler's tracking of the asynchronous LDS writes never couples
-  // reads of one buffer to loads landing in the other.
+  static_assert(NB == 2 || (NB == 4 && !REM), "ring depth");
+  // NB pair buffers (pair p, steps 2p and 2p+1, in buffer p % NB): each its
+  // own array, so the compiler's tracking of the asynchronous LDS writes
+  // never couples reads of one buffer to loads landing in another.
   __shared__ int4 lds0[C::kPairSlots], lds1[C::kPairSlots];
+  __shared__ int4 lds2[NB > 2 ? C::kPairSlots : 1], lds3[NB > 2 ? C::kPairSlots : 1];
   // bf16 output: the staged epilogue's operands (token scales of the BM
   // rows, then channel scales and biases of the BN columns), moved into
   // LDS by DMA ahead of the first pair, so the epilogue waits for no load.
@@ -297,33 +304,51 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
   // One step kt: (1) wait until step kt+1 has landed and this wave's reads
   // of step kt's fragments are done, then barrier; (2) issue the reads of
   // step kt+1's fragments and, at odd kt, refill step kt's pair buffer
-  // (both of its steps are read by now) with steps kt+3 and kt+4,
-  // interleaved with (3) the MFMAs on step kt's fragments.  The refill of an
-  // odd step is the only one that can still be in flight at the next (even)
-  // step's wait; at an odd step the next step lies in the buffer refilled
-  // two steps earlier, so nothing may be outstanding.
+  // (both of its steps are read by now) with the pair NB ahead, interleaved
+  // with (3) the MFMAs on step kt's fragments.  VM: the loads that may
+  // still be in flight at the wait (vmcnt retires in issue order): at an
+  // even step the next step is in the pair waited for at the odd step
+  // before, so the NB - 1 youngest refills may fly; at an odd step the next
+  // step's pair was issued NB - 1 refills ago, so NB - 2 may (fewer in the
+  // last group, which issues no refills).
   // LAST: a step of the last group (no refill; at the last step no reads).
   auto step = [&](Frags& cur, Frags& nxt, int4* cur_buf, const int4* nxt_slot, int kt,
-                  auto odd_tag, auto last_tag, auto final_tag) {
+                  auto odd_tag, auto last_tag, auto final_tag, auto vm_tag) {
     constexpr bool kOdd = decltype(odd_tag)::value;
     constexpr bool kRefill = kOdd && !decltype(last_tag)::value;
     constexpr bool kReads = !decltype(final_tag)::value;
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm_lgkm0<kOdd ? 0 : C::kLPW>();
+    wait_vm_lgkm0<decltype(vm_tag)::value>();
     barrier_nofence();
     if (kReads) read_frags(nxt, nxt_slot);
-    if (kRefill) issue(cur_buf, (kt + 3) >> 1);
+    if (kRefill) issue(cur_buf, ((kt - 1) >> 1) + NB);
     mfmas(cur);
     interleave_step<C::kTM * C::kTN, kReads ? C::kTM + C::kTN : 0, kRefill ? C::kLPW : 0>();
   };
   using Even = std::integral_constant<bool, false>;
   using Odd = std::integral_constant<bool, true>;
-  // step j of an unrolled group of 4: buffer, next step's slot, parity
+  // pair buffer b of the ring
+  auto bufp = [&](auto b_tag) -> int4* {
+    constexpr int b = decltype(b_tag)::value;
+    if constexpr (b == 0) return lds0;
+    else if constexpr (b == 1) return lds1;
+    else if constexpr (b == 2) return lds2;
+    else return lds3;
+  };
+#define KQ_BUF(b) bufp(std::integral_constant<int, (b)>{})
+  // loads that may fly at step j of a group of 2*NB (steady state; in the
+  // last group an odd step j has (NB - 2 - (j - 1)/2) younger pairs at most)
+#define KQ_VM(j, LAST)                                                                   \
+  std::integral_constant<int, (j) % 2 == 0 ? (NB - 1) * C::kLPW                          \
+                              : (LAST ? (NB - 2 - ((j) - 1) / 2 > 0 ? NB - 2 - ((j) - 1) / 2 : 0) \
+                                      : NB - 2) * C::kLPW>{}
+  // step j of an unrolled group of 2*NB: pair buffer j/2, next step's slot
+  // (the pair's second half, or the next buffer's first), parity
 #define KQ_STEPX(j, LAST)                                                                \
-  step((j) % 2 ? f1 : f0, (j) % 2 ? f0 : f1, (j) < 2 ? lds0 : lds1,                     \
-       (j) == 0 ? lds0 + 32 : (j) == 1 ? lds1 : (j) == 2 ? lds1 + 32 : lds0, kt + (j),    \
+  step((j) % 2 ? f1 : f0, (j) % 2 ? f0 : f1, KQ_BUF((j) / 2),                           \
+       (j) % 2 == 0 ? KQ_BUF((j) / 2) + 32 : KQ_BUF(((j) / 2 + 1) % NB), kt + (j),       \
        std::conditional_t<(j) % 2 == 1, Odd, Even>{}, std::integral_constant<bool, LAST>{}, \
-       std::integral_constant<bool, LAST && (j) == 3>{})
+       std::integral_constant<bool, LAST && (j) == 2 * NB - 1>{}, KQ_VM(j, LAST))
 #define KQ_STEP(j) KQ_STEPX(j, false)
 #define KQ_LAST(j) KQ_STEPX(j, true)
 
@@ -347,11 +372,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
   }
   issue(lds0, 0);
   issue(lds1, 1);
-  wait_vm_lgkm0<C::kLPW>();
+  if constexpr (NB > 2) {
+    issue(lds2, 2);
+    issue(lds3, 3);
+  }
+  wait_vm_lgkm0<(NB - 1) * C::kLPW>();  // pair 0
   barrier_nofence();
   read_frags(f0, lds0);
   int kt = 0;
-  if constexpr (!REM) {
+  if constexpr (!REM && NB == 4) {
+    for (; kt + 8 < KT; kt += 8) {
+      KQ_STEP(0); KQ_STEP(1); KQ_STEP(2); KQ_STEP(3);
+      KQ_STEP(4); KQ_STEP(5); KQ_STEP(6); KQ_STEP(7);
+    }
+    // the last group: its pairs are in the buffers, so no refills (and no
+    // reads for a step past the end)
+    KQ_LAST(0); KQ_LAST(1); KQ_LAST(2); KQ_LAST(3);
+    KQ_LAST(4); KQ_LAST(5); KQ_LAST(6); KQ_LAST(7);
+  } else if constexpr (!REM) {
     for (; kt + 4 < KT; kt += 4) {
       KQ_STEP(0); KQ_STEP(1); KQ_STEP(2); KQ_STEP(3);
     }
@@ -370,6 +408,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_w8a8_kernel(
 #undef KQ_STEP
 #undef KQ_LAST
 #undef KQ_STEPX
+#undef KQ_VM
+#undef KQ_BUF
   __builtin_amdgcn_sched_barrier(0);
   wait_vm_lgkm0<0>();  // drain the dead loads of a tail before the workgroup exits
 
@@ -749,6 +789,12 @@ int device_cus() {
   return cache[dev];
 }
 
+// KQ_DEEP_RING=0 keeps the 2-buffer ring everywhere (A/B runs).
+bool deep_ring_enabled() {
+  const char* v = getenv("KQ_DEEP_RING");
+  return !(v && v[0] == '0');
+}
+
 // KQ_PERSIST=1 takes the persistent form where it applies (off by
 // default: measured slower at the 4K shape, the next tile's refills wait
 // behind the previous tile's output stores).
@@ -776,7 +822,7 @@ bool launch_persist(const int8_t* a, const float* sx, const int8_t* q, const flo
   return true;
 }
 
-template <int BM, int BN, int WM, int WN, bool REM>
+template <int BM, int BN, int WM, int WN, bool REM, int NB = 2>
 void launch_rem(const int8_t* a, const float* sx, const int8_t* q, const float* sw,
                 const float* bias, void* y, int out, int M, int N, int K, hipStream_t s,
                 const Epilogue& ep, int splits, int kchunk) {
@@ -784,15 +830,15 @@ void launch_rem(const int8_t* a, const float* sx, const int8_t* q, const float* 
   const dim3 grid((unsigned)tiles, (unsigned)splits), block(64 * WM * WN);
   const bool g = ep.active();
   if (out == kOutF32 && g)
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutF32, REM, true>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep, kchunk);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutF32, REM, true, NB>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep, kchunk);
   else if (out == kOutF32)
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutF32, REM, false>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep, kchunk);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutF32, REM, false, NB>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep, kchunk);
   else if (out == kOutBF16 && g)
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutBF16, REM, true>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep, kchunk);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutBF16, REM, true, NB>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep, kchunk);
   else if (out == kOutBF16)
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutBF16, REM, false>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep, kchunk);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutBF16, REM, false, NB>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep, kchunk);
   else
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutI32, REM, false>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep, kchunk);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, kOutI32, REM, false, NB>), grid, block, 0, s, a, sx, q, sw, bias, y, M, N, K, ep, kchunk);
 }
 
 template <int BM, int BN, int WM = 2, int WN = 2>
@@ -804,6 +850,18 @@ const char* launch_tile(const int8_t* a, const float* sx, const int8_t* q, const
   if constexpr (WM * WN == 8 && BN == 192) {  // (the 8-wave 256x256 tile would spill)
     if (splits == 1 && launch_persist<BM, BN, WM, WN>(a, sx, q, sw, bias, y, out, M, N, K, s, ep))
       return name;
+  }
+  // the 4-buffer ring: tiles of at most 128x128 (4 pairs fit the LDS),
+  // K steps a multiple of 8 in every slice, a grid of at most one
+  // workgroup per CU (the ring's LDS then costs no occupancy)
+  if constexpr (BM + BN <= 256) {
+    const int64_t wgs = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN) * splits;
+    if ((kchunk / 64) % 8 == 0 && (klast / 64) % 8 == 0 && wgs <= device_cus() &&
+        deep_ring_enabled()) {
+      launch_rem<BM, BN, WM, WN, false, 4>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, splits,
+                                           kchunk);
+      return name;
+    }
   }
   if ((kchunk / 64) % 4 == 0 && (klast / 64) % 4 == 0)
     launch_rem<BM, BN, WM, WN, false>(a, sx, q, sw, bias, y, out, M, N, K, s, ep, splits, kchunk);
