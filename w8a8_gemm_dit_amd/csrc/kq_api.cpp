@@ -16,6 +16,8 @@
 //   KQ_FUSE=0           no fused thin-N route (quantize kernel + GEMV instead)
 //   KQ_GEMV_LANE=0      GEMVs at M <= 2 on the MFMA GEMV kernel instead of
 //                       the lane-per-column ones
+//   KQ_DEEP_RING=0      the W8A8 GEMM keeps its 2-buffer pair ring on every
+//                       grid (A/B runs of the 4-buffer ring)
 #include <hip/hip_runtime.h>
 
 #include <climits>
