@@ -411,12 +411,15 @@ kq_status kq_sage_prepare(const void* q, const void* k, const void* v, int64_t B
 
 /* The attention alone, on a workspace kq_sage_prepare filled for the same
  * B, H, Lq and Lk.  k_block >= 64 asserts that every 64-key step shares one
- * key scale and takes the faster kernel for it; the kernel checks that
- * assertion against the key block the preparation recorded in the
- * workspace (meta) and, on a workspace prepared with a smaller k_block,
- * writes NaN to every output element instead of wrong values (the host
- * cannot read the workspace without synchronizing, so the mismatch cannot
- * be returned as a status).  A k_block below 64 is correct on any prepared
+ * key scale and takes the faster kernel for it.  The library keeps, per
+ * workspace address, the shape and key block of the last kq_sage_prepare
+ * this process issued on it, and returns KQ_ERR_INVALID_VALUE (nothing
+ * enqueued) when the call's B, H, Lq or Lk differ from it, or when k_block
+ * >= 64 meets a workspace prepared with a smaller k_block.  A workspace this
+ * process never prepared is not checked on the host; for it, the kernel
+ * compares the assertion with the key block the preparation wrote into the
+ * workspace (meta) and, on a mismatch, writes NaN to every output element
+ * instead of wrong values.  A k_block below 64 is correct on any prepared
  * workspace. */
 kq_status kq_sage_attend(const void* ws, size_t ws_bytes, void* out, int64_t B,
                          int64_t H, int64_t Lq, int64_t Lk, int64_t D,

@@ -258,17 +258,27 @@ def test_large_scores_are_one_hot():
         _check_out(out[0, h], qc, sq, kc, sk, v[0, h], 128 ** -0.5, f"one-hot h{h}")
 
 
-def test_key_block_mismatch_writes_nan_not_wrong_values():
+def test_key_block_mismatch_refused_or_nan_not_wrong_values():
     """A workspace prepared with per-token key scales (k_block 1) attended
-    with the uniform-step kernel (k_block 64): the kernel finds the recorded
-    key block and writes NaN everywhere; attended as prepared it is right."""
+    with the uniform-step kernel (k_block 64): the call is refused on the
+    host (the library recorded the preparation), a call for another shape
+    too; a copy of the workspace at an address the library never prepared
+    goes to the kernel, which finds the recorded key block and writes NaN
+    everywhere.  Attended as prepared, both are right."""
     rng = np.random.default_rng(77)
     q, k, v = (rng.standard_normal((1, 2, 130, 128)).astype(np.float16) for _ in range(3))
     ws = kq.kq_sage_prepare(_dev(q), _dev(k), _dev(v), 128, 1)
-    bad = kq.kq_sage_attend(ws, 1, 2, 130, 130, 0.1, k_block=64)
+    with pytest.raises(ValueError, match="prepared with k_block=1"):
+        kq.kq_sage_attend(ws, 1, 2, 130, 130, 0.1, k_block=64)
+    with pytest.raises(ValueError, match="was prepared for"):
+        kq.kq_sage_attend(ws, 1, 1, 130, 130, 0.1, k_block=1)
+    copy = ws.clone()
+    bad = kq.kq_sage_attend(copy, 1, 2, 130, 130, 0.1, k_block=64)
     good = kq.kq_sage_attend(ws, 1, 2, 130, 130, 0.1, k_block=1)
+    good_copy = kq.kq_sage_attend(copy, 1, 2, 130, 130, 0.1, k_block=1)
     torch.cuda.synchronize()
     assert torch.isnan(bad).all()
     assert not torch.isnan(good).any()
+    assert torch.equal(good, good_copy)
     qc, sq, kc, sk, _ = S.prepare(q[0, 1], k[0, 1], 128, 1)
     _check_out(good.cpu().numpy()[0, 1], qc, sq, kc, sk, v[0, 1], 0.1, "mismatch, attended as prepared")

@@ -25,7 +25,9 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <unordered_map>
 
 #include "kq.h"
 #include "kq_launch.hpp"
@@ -333,6 +335,32 @@ kq_status check_sage_ws(const char* op, const void* ws, size_t ws_bytes, const k
   return KQ_SUCCESS;
 }
 
+// The last preparation this process issued on each workspace address: its
+// shape and key block.  The attention checks a call against it on the host,
+// so a workspace prepared with per-token (or sub-step) key scales is refused
+// before anything is enqueued when the call asserts uniform 64-key steps.  A
+// workspace the process never prepared (filled by another process, or
+// copied) is not in the table; the kernel's own check of the key block the
+// preparation wrote into the workspace covers it.
+struct SagePrepRecord {
+  int64_t B, H, Lq, Lk, k_block;
+};
+std::mutex g_sage_mu;
+std::unordered_map<const void*, SagePrepRecord> g_sage_prep;
+
+void sage_record(const void* ws, const SagePrepRecord& r) {
+  std::lock_guard<std::mutex> lk(g_sage_mu);
+  g_sage_prep[ws] = r;
+}
+
+bool sage_lookup(const void* ws, SagePrepRecord* r) {
+  std::lock_guard<std::mutex> lk(g_sage_mu);
+  auto it = g_sage_prep.find(ws);
+  if (it == g_sage_prep.end()) return false;
+  *r = it->second;
+  return true;
+}
+
 kq_status sage_prepare_impl(const char* op, const void* q, const void* k, const void* v, int64_t B,
                             int64_t H, int64_t Lq, int64_t Lk, int64_t D, kq_layout layout,
                             int64_t q_block, int64_t k_block, void* ws, size_t ws_bytes,
@@ -356,6 +384,7 @@ kq_status sage_prepare_impl(const char* op, const void* q, const void* k, const 
       sage_strides(layout, H, Lk), B, H, Lq, Lk, (int)q_block, (int)k_block,
       reinterpret_cast<char*>(ws), L, reinterpret_cast<hipStream_t>(stream));
   st = check_launch(op);
+  if (st == KQ_SUCCESS) sage_record(ws, SagePrepRecord{B, H, Lq, Lk, k_block});
   if (st == KQ_SUCCESS && env_log())
     fprintf(stderr, "[kq] %s B=%lld H=%lld Lq=%lld Lk=%lld q_block=%lld k_block=%lld kernels=%s\n", op,
             (long long)B, (long long)H, (long long)Lq, (long long)Lk, (long long)q_block,
@@ -380,6 +409,20 @@ kq_status sage_attend_impl(const char* op, const void* ws, size_t ws_bytes, void
   const bool k_uniform = k_block >= kq::kSageKTile;
   st = check_sage_ws(op, ws, ws_bytes, L);
   if (st != KQ_SUCCESS) return st;
+  SagePrepRecord rec;
+  if (sage_lookup(ws, &rec)) {
+    if (rec.B != B || rec.H != H || rec.Lq != Lq || rec.Lk != Lk)
+      return fail(KQ_ERR_INVALID_VALUE,
+                  "[%s] workspace was prepared for B=%lld H=%lld Lq=%lld Lk=%lld, not B=%lld H=%lld "
+                  "Lq=%lld Lk=%lld",
+                  op, (long long)rec.B, (long long)rec.H, (long long)rec.Lq, (long long)rec.Lk,
+                  (long long)B, (long long)H, (long long)Lq, (long long)Lk);
+    if (k_uniform && rec.k_block < kq::kSageKTile)
+      return fail(KQ_ERR_INVALID_VALUE,
+                  "[%s] k_block=%lld asserts one key scale per %d-key step, but the workspace was "
+                  "prepared with k_block=%lld",
+                  op, (long long)k_block, kq::kSageKTile, (long long)rec.k_block);
+  }
   st = check_device(op);
   if (st != KQ_SUCCESS) return st;
   const char* name = kq::launch_sage_attend(reinterpret_cast<const char*>(ws), L,
