@@ -258,9 +258,16 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, (BM == 128 && BN == 1
       }
       const v4i fw = v4i{(int)u0, (int)u1, (int)u2, (int)u3};
       const float s = kScaled ? __half2float(__ushort_as_half((unsigned short)f.s[i])) : 0.f;
+      // the column block's MFMAs go out together, into separate registers,
+      // so each rescale finds its product ready instead of waiting out the
+      // latency of the MFMA just issued
+      v4i pp[C::kTM];
+#pragma unroll
+      for (int j = 0; j < C::kTM; ++j)
+        pp[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.a[j], fw, v4i{0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < C::kTM; ++j) {
-        const v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.a[j], fw, v4i{0, 0, 0, 0}, 0, 0, 0);
+        const v4i p = pp[j];
         if (kScaled) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(s, (float)p[r], acc[i][j][r]);
