@@ -192,6 +192,14 @@ def test_route_levers(kq_env):
     kq_env(KQ_TILE="128x256")
     r = kq.kq_route(4096, 3072, 3072, kq.KQ_W8_PER_CHANNEL)
     assert (r["tile_m"], r["tile_n"]) == (256, 128)     # int8: same area
+    # a tile the kernel has is taken as named, also where another tile has
+    # the same area (the 4- and 8-wavefront 256x256 tiles)
+    kq_env(KQ_TILE="256x256w8")
+    r = kq.kq_route(1024, 1536, 1024, kq.KQ_W8_PER_CHANNEL)
+    assert (r["tile_m"], r["tile_n"], r["threads"], r["grid"]) == (256, 256, 512, 24)
+    kq_env(KQ_TILE="256x256")
+    r = kq.kq_route(1024, 1536, 1024, kq.KQ_W8_PER_CHANNEL)
+    assert (r["tile_m"], r["tile_n"], r["threads"]) == (256, 256, 256)
 
 
 @pytest.mark.parametrize("K,msg", [

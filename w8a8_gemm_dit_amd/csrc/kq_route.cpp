@@ -160,7 +160,9 @@ kq_route_info choose_route(int64_t M, int64_t N, int64_t K, kq_wformat fmt,
   const int32_t* cand = w8 ? kW8Tiles : kW4Tiles;
   const int ncand = w8 ? 6 : 3;
   int32_t tile = -1;
-  if (tile_override >= 0 && tile_override < kNumTiles) {
+  for (int i = 0; i < ncand && tile_override >= 0; ++i)
+    if (cand[i] == tile_override) tile = tile_override;
+  if (tile < 0 && tile_override >= 0 && tile_override < kNumTiles) {
     // a tile this kernel lacks: the one nearest in area (larger on a tie)
     const TileShape want = tile_shape(tile_override);
     int64_t best_d = -1;
