@@ -84,7 +84,12 @@ __device__ __forceinline__ void store1(void* y, int64_t idx, float v) {
 // reordering.  Otherwise the codes are in natural order and the unpacked
 // nibbles are put back into it (two v_perm_b32 a dword).  The dot product
 // of a group is the same sum in another order, exact in int32.
-template <int BM, int BN, int WTM, int WTN, int OUT, bool GATED, bool EO>
+// TV: the tables come in with 16-byte loads: thread t stages 8 consecutive
+// groups of column t/2 (and of row t/2), groups 8*(t%2)..+7 of the chunk.
+// It needs the table rows 16-byte aligned (K/64 a multiple of 8, aligned
+// bases), so the slice's group count G is a multiple of 8 as well and an
+// 8-group unit lies wholly inside or wholly past the slice.
+template <int BM, int BN, int WTM, int WTN, int OUT, bool GATED, bool EO, bool TV>
 // (128x128: two workgroups per CU, so at most 256 registers per lane)
 __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, (BM == 128 && BN == 128) ? 2 : 1) void gemm_w4a8_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int32_t* __restrict__ gsum,
@@ -167,7 +172,56 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, (BM == 128 && BN == 1
   // they are written, not here: a select at the load lets the compiler sink
   // the load under a branch and wait for it (and for every ring load in
   // flight) on the spot.
+  static_assert(!TV || (BN * 2 == C::kThreads && BM * 2 <= C::kThreads), "vector table staging");
+  v4i st_sv = v4i{0, 0, 0, 0}, st_bv = v4i{0, 0, 0, 0}, st_av[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
+  const int tv_c = tid >> 1, tv_h = tid & 1;      // column (and row) and half of the chunk
+  const int tv_r = min(tv_c, BM - 1);             // rows past BM repeat row BM-1's unit
+  auto stage_load_v = [&](int chunk) {
+    // 8-group units wholly past the slice load the slice's last unit (the
+    // writes zero them); columns and rows past N / M load the last one
+    const int g = min(chunk * kSG + 8 * tv_h, G - 8);
+    const int64_t cn = (int64_t)min(n0 + tv_c, N - 1) * Gall + g;
+    st_sv = *reinterpret_cast<const v4i*>(GS + cn);
+    st_bv = *reinterpret_cast<const v4i*>(GB + cn);
+    const int32_t* ga = gsum + (int64_t)min(m0 + tv_r, M - 1) * Gall + g;
+    st_av[0] = *reinterpret_cast<const v4i*>(ga);
+    st_av[1] = *reinterpret_cast<const v4i*>(ga + 4);
+  };
+  auto stage_write_v = [&](int buf, int chunk) {
+    const bool inside = chunk * kSG + 8 * tv_h < G;
+    const bool okn = inside && n0 + tv_c < N;
+    const v4i z = v4i{0, 0, 0, 0};
+    // t_gs rows may be padded to 18 halves: 4-byte aligned words
+    uint32_t* ds = reinterpret_cast<uint32_t*>(&t_gs[buf][tv_c][8 * tv_h]);
+    const v4i vs = okn ? st_sv : z;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ds[i] = (uint32_t)vs[i];
+    *reinterpret_cast<v4i*>(&t_gb[buf][tv_c][8 * tv_h]) = okn ? st_bv : z;
+    const bool okm = inside && m0 + tv_r < M;
+    uint32_t hi2[4], lo2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t hv[2], lv[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int j = 2 * i + k;
+        const int v = okm ? st_av[j >> 2][j & 3] : 0;
+        const int hi = v >> 6;        // floor(v / 64)
+        const int lo = v - hi * 64;   // 0..63
+        hv[k] = __half_as_ushort(__float2half_rn((float)(hi * 64)));
+        lv[k] = __half_as_ushort(__float2half_rn((float)lo));
+      }
+      hi2[i] = hv[0] | (hv[1] << 16);
+      lo2[i] = lv[0] | (lv[1] << 16);
+    }
+    *reinterpret_cast<v4i*>(&t_as[buf][tv_r][8 * tv_h]) = v4i{(int)hi2[0], (int)hi2[1], (int)hi2[2], (int)hi2[3]};
+    *reinterpret_cast<v4i*>(&t_as[buf][tv_r][kSG + 8 * tv_h]) = v4i{(int)lo2[0], (int)lo2[1], (int)lo2[2], (int)lo2[3]};
+  };
   auto stage_load = [&](int chunk) {
+    if constexpr (TV) {
+      stage_load_v(chunk);
+      return;
+    }
     const int gbase = chunk * kSG;
 #pragma unroll
     for (int u = 0; u < C::kSBN; ++u) {
@@ -187,6 +241,10 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, (BM == 128 && BN == 1
     }
   };
   auto stage_write = [&](int buf, int chunk) {
+    if constexpr (TV) {
+      stage_write_v(buf, chunk);
+      return;
+    }
     const int gbase = chunk * kSG;
 #pragma unroll
     for (int u = 0; u < C::kSBN; ++u) {
@@ -323,7 +381,7 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, (BM == 128 && BN == 1
     }
   };
   using I0 = std::integral_constant<int, 0>;
-  constexpr int kStageOps = kScaled ? 2 * C::kSBN + C::kSBM : 0;
+  constexpr int kStageOps = !kScaled ? 0 : TV ? 4 : 2 * C::kSBN + C::kSBM;
   using IX = std::integral_constant<int, kStageOps>;
 
   // prologue: table chunk 0, ring steps 0..3
@@ -441,8 +499,8 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, (BM == 128 && BN == 1
   }
 }
 
-template <int BM, int BN, int WTM, int WTN, bool EO>
-const char* launch_tile4(const int8_t* a, const float* sx, const int32_t* gsum, const uint8_t* q4,
+template <int BM, int BN, int WTM, int WTN, bool EO, bool TV>
+const char* launch_tile4_tv(const int8_t* a, const float* sx, const int32_t* gsum, const uint8_t* q4,
                          const uint16_t* gs, const uint16_t* gb, const float* bias, void* y,
                          int out, int M, int N, int K, hipStream_t s, const Epilogue& ep,
                          const char* name, int splits, int gchunk) {
@@ -450,20 +508,37 @@ const char* launch_tile4(const int8_t* a, const float* sx, const int32_t* gsum, 
   const int64_t tiles = (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const dim3 grid((unsigned)tiles, (unsigned)splits), block(C::kThreads);
   if (out == kOutPart) {
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutPart, false, EO>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutPart, false, EO, TV>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
     return name;
   }
   if (ep.active() && out == kOutF32)
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutF32, true, EO>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutF32, true, EO, TV>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
   else if (ep.active() && out == kOutBF16)
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutBF16, true, EO>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutBF16, true, EO, TV>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
   else if (out == kOutF32)
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutF32, false, EO>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutF32, false, EO, TV>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
   else if (out == kOutBF16)
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutBF16, false, EO>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutBF16, false, EO, TV>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
   else
-    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutI32, false, EO>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
+    hipLaunchKernelGGL((gemm_w4a8_kernel<BM, BN, WTM, WTN, kOutI32, false, EO, false>), grid, block, 0, s, a, sx, gsum, q4, gs, gb, bias, y, M, N, K, ep, gchunk);
   return name;
+}
+
+// 16-byte table loads where the split-order (linear) kernels can take them:
+// table rows of a multiple of 8 groups on 16-byte aligned bases.
+template <int BM, int BN, int WTM, int WTN, bool EO>
+const char* launch_tile4(const int8_t* a, const float* sx, const int32_t* gsum, const uint8_t* q4,
+                         const uint16_t* gs, const uint16_t* gb, const float* bias, void* y,
+                         int out, int M, int N, int K, hipStream_t s, const Epilogue& ep,
+                         const char* name, int splits, int gchunk) {
+  auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  if constexpr (EO) {
+    if ((K / 64) % 8 == 0 && a16(gs) && a16(gb) && a16(gsum) && out != kOutI32)
+      return launch_tile4_tv<BM, BN, WTM, WTN, EO, true>(a, sx, gsum, q4, gs, gb, bias, y, out, M, N,
+                                                         K, s, ep, name, splits, gchunk);
+  }
+  return launch_tile4_tv<BM, BN, WTM, WTN, EO, false>(a, sx, gsum, q4, gs, gb, bias, y, out, M, N, K,
+                                                      s, ep, name, splits, gchunk);
 }
 
 // Fold of a split int4 GEMM: the fp32 slice sums added in slice order,
