@@ -301,31 +301,43 @@ __global__ __launch_bounds__((BM / WTM) * (BN / WTN) * 64, (BM == 128 && BN == 1
       for (int i = 0; i < C::kTN; ++i) f.s[i] = t_gs[buf][q_col0 + 16 * i][t];
     }
   };
+  auto weights = [&](const Frags& f, int i) {
+    uint32_t u0, u1, u2, u3;
+    if constexpr (EO) {
+      u0 = f.q[i].x & 0x0F0F0F0Fu;
+      u1 = (f.q[i].x >> 4) & 0x0F0F0F0Fu;
+      u2 = f.q[i].y & 0x0F0F0F0Fu;
+      u3 = (f.q[i].y >> 4) & 0x0F0F0F0Fu;
+    } else {
+      unpack8_u4(f.q[i].x, u0, u1);
+      unpack8_u4(f.q[i].y, u2, u3);
+    }
+    return v4i{(int)u0, (int)u1, (int)u2, (int)u3};
+  };
   auto compute = [&](const Frags& f, int kt) {
-#pragma unroll
-    for (int i = 0; i < C::kTN; ++i) {
-      uint32_t u0, u1, u2, u3;
-      if constexpr (EO) {
-        u0 = f.q[i].x & 0x0F0F0F0Fu;
-        u1 = (f.q[i].x >> 4) & 0x0F0F0F0Fu;
-        u2 = f.q[i].y & 0x0F0F0F0Fu;
-        u3 = (f.q[i].y >> 4) & 0x0F0F0F0Fu;
-      } else {
-        unpack8_u4(f.q[i].x, u0, u1);
-        unpack8_u4(f.q[i].y, u2, u3);
-      }
-      const v4i fw = v4i{(int)u0, (int)u1, (int)u2, (int)u3};
-      const float s = kScaled ? __half2float(__ushort_as_half((unsigned short)f.s[i])) : 0.f;
-      // the column block's MFMAs go out together, into separate registers,
-      // so each rescale finds its product ready instead of waiting out the
-      // latency of the MFMA just issued
-      v4i pp[C::kTM];
+    // A column block's MFMAs go out together, into separate registers, and
+    // the next block's go out before this block's rescale, so each rescale
+    // finds its products ready instead of waiting out the latency of an
+    // MFMA just issued.
+    v4i pp[2][C::kTM];
+    {
+      const v4i fw = weights(f, 0);
 #pragma unroll
       for (int j = 0; j < C::kTM; ++j)
-        pp[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.a[j], fw, v4i{0, 0, 0, 0}, 0, 0, 0);
+        pp[0][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.a[j], fw, v4i{0, 0, 0, 0}, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < C::kTN; ++i) {
+      if (i + 1 < C::kTN) {
+        const v4i fw = weights(f, i + 1);
+#pragma unroll
+        for (int j = 0; j < C::kTM; ++j)
+          pp[(i + 1) & 1][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.a[j], fw, v4i{0, 0, 0, 0}, 0, 0, 0);
+      }
+      const float s = kScaled ? __half2float(__ushort_as_half((unsigned short)f.s[i])) : 0.f;
 #pragma unroll
       for (int j = 0; j < C::kTM; ++j) {
-        const v4i p = pp[j];
+        const v4i p = pp[i & 1][j];
         if (kScaled) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(s, (float)p[r], acc[i][j][r]);
